@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark: q8_1 quantize + block-quantized int8 MMQ on one MI355X.
+
+One step = one pass of the whole path over one batch: quantize the fp32
+activations to q8_1, then the MMQ GEMM against the block-quantized weights.
+Inputs are seeded synthetic tensors resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is effective int8 TOPS of the whole step,
+2*M*N*K / (quantize + GEMM time); the roofline object reports the GEMM
+kernel alone against the MI355X dense int8 matrix-core peak, timed with HIP
+events on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective int8 MMQ TOPS at 7B prefill shapes (M=2048); % of MFMA int8 peak"
+PEAK_INT8_TOPS = 5000.0          # MI355X dense int8 matrix-core peak, TOP/s
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_quantized_int8_q8_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 PMC counters, if they were
+    taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def make_inputs(cfg: int):
+    from block_quantized_int8_q8_amd import inputs
+    fmt, M, N, K = inputs.CONFIGS[cfg]
+    x = inputs.activations(M, K, inputs.seed_for(cfg, 0))
+    w = (inputs.q8_0_weights(N, K, inputs.seed_for(cfg, 1)) if fmt == "q8_0"
+         else inputs.q4_K_weights(N, K, inputs.seed_for(cfg, 1)))
+    return fmt, M, N, K, x, w
+
+
+def time_config(cfg: int, steps: int, warmup: int, check: bool = True):
+    import torch
+    import block_quantized_int8_q8_amd as mmq
+
+    fmt, M, N, K, x, w = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    xd = torch.from_numpy(x).to(dev)
+    wd = torch.from_numpy(w).to(dev)
+    xq = torch.empty((M, K // 32, 36), dtype=torch.uint8, device=dev)
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+    gemm = mmq.gemm_q8_0 if fmt == "q8_0" else mmq.gemm_q4_K
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mmq.quantize_q8_1(xd, xq, stream=stream)
+        gemm(xq, wd, M, N, K, out, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    parity = None
+    if check:
+        parity = check_parity(fmt, M, N, K, x, w, xq, out)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        mmq.quantize_q8_1(xd, xq, stream=stream)
+        ev[i][1].record(stream)
+        gemm(xq, wd, M, N, K, out, stream=stream)
+        ev[i][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    q_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
+    g_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]
+    ops = 2.0 * M * N * K
+    step_ms = total_ms / steps
+    g_avg = float(np.mean(g_ms))
+    q_avg = float(np.mean(q_ms))
+    return {
+        "cfg": cfg, "fmt": fmt, "M": M, "N": N, "K": K,
+        "ms_per_step": step_ms,
+        "wall_s": wall,
+        "tops_step": ops / (step_ms * 1e-3) / 1e12,
+        "gemm_ms_avg": g_avg, "gemm_ms_min": float(np.min(g_ms)),
+        "gemm_tops": ops / (g_avg * 1e-3) / 1e12,
+        "quant_ms_avg": q_avg,
+        "quant_gbs": (4.0 + 36.0 / 32.0) * M * K / (q_avg * 1e-3) / 1e9,
+        "parity": parity,
+    }
+
+
+def check_parity(fmt, M, N, K, x, w, xq_dev, out_dev):
+    """The timed output, checked against the oracle on sampled rows."""
+    import oracle
+    from tests import metrics
+    xq = oracle.quantize_q8_1(x)
+    q_ok = bool(np.array_equal(xq_dev.cpu().numpy(), xq))
+    o = out_dev.cpu().numpy()
+    rows = sorted(set([0, M - 1, M // 2] + list(np.random.default_rng(0).integers(0, M, 5))))
+    f = oracle.gemm_q8_0 if fmt == "q8_0" else oracle.gemm_q4_K
+    ref = f(np.ascontiguousarray(xq[rows]), w, len(rows), N, K, nthreads=min(16, os.cpu_count() or 1))
+    rep = metrics.report(o[rows], ref)
+    return {
+        "quantize_bit_exact": q_ok,
+        "unwritten": int(np.isnan(o).sum()),
+        "rows_checked": len(rows),
+        "normalized_max_error": rep["normalized_max_error"],
+        "bit_identical_fraction": rep["bit_identical_fraction"],
+        "ok": bool(q_ok and not np.isnan(o).any() and rep["normalized_max_error"] <= metrics.TOL),
+    }
+
+
+def cpu_baseline(cfg: int, target_s: float = 15.0):
+    """The oracle (quantize + GEMM) on a bounded row sample of the same
+    workload, on the host cores; scaled to TOP/s of that sample."""
+    import oracle
+    fmt, M, N, K, x, w = make_inputs(cfg)
+    threads = min(16, os.cpu_count() or 1)
+    f = oracle.gemm_q8_0 if fmt == "q8_0" else oracle.gemm_q4_K
+    used = oracle.threads_used(threads)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        xq = oracle.quantize_q8_1(x[:rows])
+        f(xq, w, rows, N, K, nthreads=threads)
+        return time.perf_counter() - t0
+
+    probe = max(1, min(M, 2 * used))
+    t_probe = run(probe)
+    rows = int(max(probe, min(M, probe * target_s / max(t_probe, 1e-6))))
+    rows = max(used, rows - rows % used) if rows >= used else rows
+    t = run(rows)
+    return {
+        "value": 2.0 * rows * N * K / t / 1e12,
+        "unit": "TOP/s",
+        "cores": used,
+        "kind": "oracle",
+        "sample": f"{rows} of {M} activation rows (quantize + full-N GEMM), {t:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="benchmark shape (2: Q8_0 2048x3584x3584)")
+    ap.add_argument("--extra-configs", default="3,4", help="other shapes timed in the same run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by output columns with no reduction; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import block_quantized_int8_q8_amd as mmq
+    mmq.lib()   # fail loudly when the library is missing
+
+    main_rec = time_config(args.config, args.steps, args.warmup, check=not args.no_check)
+    extra = {}
+    for c in [int(v) for v in args.extra_configs.split(",") if v.strip()]:
+        if c != args.config:
+            r = time_config(c, max(5, args.steps // 5), 2, check=not args.no_check)
+            extra[f"config{c}"] = {k: r[k] for k in ("fmt", "M", "N", "K", "ms_per_step", "tops_step",
+                                                      "gemm_ms_avg", "gemm_tops", "quant_gbs", "parity")}
+            extra[f"config{c}"]["gemm_frac_of_int8_peak"] = r["gemm_tops"] / PEAK_INT8_TOPS
+
+    kname = "k_mmq<Q8_0>" if main_rec["fmt"] == "q8_0" else "k_mmq<Q4_K>"
+    achieved = main_rec["gemm_tops"]
+    roofline = {
+        "bound": "mfma",
+        "achieved": achieved,
+        "peak": PEAK_INT8_TOPS,
+        "unit": "TOP/s",
+        "frac": achieved / PEAK_INT8_TOPS,
+        "traffic": traffic_for(kname),
+        "kernel": kname,
+        "kernel_ms_avg": main_rec["gemm_ms_avg"],
+    }
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.config)
+    M, N, K = main_rec["M"], main_rec["N"], main_rec["K"]
+    line = {
+        "metric": METRIC,
+        "value": main_rec["tops_step"],
+        "unit": "TOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{main_rec['fmt'].upper()} x q8_1 MMQ M={M} N={N} K={K} (quantize + GEMM)",
+            "M": M, "N": N, "K": K, "format": main_rec["fmt"].upper(),
+            "parallelism": "single GPU",
+        },
+        "frac_of_int8_peak_step": main_rec["tops_step"] / PEAK_INT8_TOPS,
+        "gemm_tops": main_rec["gemm_tops"],
+        "quantize_gbs": main_rec["quant_gbs"],
+        "quantize_frac_of_hbm": main_rec["quant_gbs"] / PEAK_HBM_GBS,
+        "parity": main_rec["parity"],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,144 @@
-"""Block-quantized int8 MMQ for MI355X (gfx950)."""
+"""Block-quantized int8 MMQ for AMD MI355X (gfx950).
+
+Thin Python binding over ``libmmq.so`` (C ABI in ``include/mmq.h``): argument
+marshalling only.  Every step of the path runs in the library's HIP kernels;
+PyTorch supplies device memory and the stream.  There is no CPU fallback: if
+the library is missing or refuses a call, an exception says why.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmmq.so")
+
+FMT_Q8_0 = 0
+FMT_Q4_K = 1
+Q8_1_BYTES, Q8_0_BYTES, Q4_K_BYTES = 36, 34, 144
+
+EXPORTS = (
+    "mmq_quantize_q8_1", "mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_debug_block_dots",
+    "mmq_last_error", "mmq_plan_describe", "mmq_plan_for_limits",
+    "mmq_debug_set_extra_lds", "mmq_version",
+)
+
+
+class MMQError(RuntimeError):
+    """The library refused a call (nothing was launched)."""
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmmq.so (built by __graft_entry__.build()); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.mmq_quantize_q8_1.argtypes = [p, p, i64, i64, p]
+        L.mmq_quantize_q8_1.restype = i32
+        for name in ("mmq_gemm_q8_0", "mmq_gemm_q4_K"):
+            getattr(L, name).argtypes = [p, p, p, i64, i64, i64, p]
+            getattr(L, name).restype = i32
+        L.mmq_debug_block_dots.argtypes = [i32, p, p, p, i64, i64, i64, p]
+        L.mmq_debug_block_dots.restype = i32
+        L.mmq_last_error.argtypes = []
+        L.mmq_last_error.restype = ctypes.c_char_p
+        L.mmq_plan_describe.argtypes = [i32, i64, i64, i64, ctypes.c_char_p, i64]
+        L.mmq_plan_describe.restype = i32
+        L.mmq_plan_for_limits.argtypes = [i32, i64, i64, i64, i64, i32, ctypes.c_char_p, i64]
+        L.mmq_plan_for_limits.restype = i32
+        L.mmq_debug_set_extra_lds.argtypes = [i64]
+        L.mmq_debug_set_extra_lds.restype = None
+        L.mmq_version.argtypes = []
+        L.mmq_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().mmq_last_error().decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 1:
+        raise MMQError(f"{what}: {last_error()}")
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t, dtype=None):
+    if not t.is_cuda:
+        raise ValueError("tensor must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"expected {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def quantize_q8_1(x, y=None, stream=None):
+    """fp32 [M, K] -> q8_1 uint8 [M, K/32, 36] on the same device."""
+    import torch
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, K // 32, Q8_1_BYTES), dtype=torch.uint8, device=x.device)
+    _check(lib().mmq_quantize_q8_1(_ptr(x, torch.float32), _ptr(y, torch.uint8), M, K, _stream(stream)),
+           "mmq_quantize_q8_1")
+    return y
+
+
+def _gemm(fn, name, xq, w, M, N, K, out, stream):
+    import torch
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    _check(getattr(lib(), fn)(_ptr(xq), _ptr(w), _ptr(out, torch.float32), M, N, K, _stream(stream)), name)
+    return out
+
+
+def gemm_q8_0(xq, w, M, N, K, out=None, stream=None):
+    """q8_1 [M, K/32, 36] x Q8_0 [N, K/32, 34] -> fp32 [M, N]."""
+    return _gemm("mmq_gemm_q8_0", "mmq_gemm_q8_0", xq, w, M, N, K, out, stream)
+
+
+def gemm_q4_K(xq, w, M, N, K, out=None, stream=None):
+    """q8_1 [M, K/32, 36] x Q4_K [N, K/256, 144] -> fp32 [M, N]."""
+    return _gemm("mmq_gemm_q4_K", "mmq_gemm_q4_K", xq, w, M, N, K, out, stream)
+
+
+def debug_block_dots(fmt, xq, w, M, N, K, dots=None, stream=None):
+    """Exact int32 block dots [M, N, K/32] through the GEMM's own staging and MFMA code."""
+    import torch
+    if dots is None:
+        dots = torch.empty((M, N, K // 32), dtype=torch.int32, device=xq.device)
+    _check(lib().mmq_debug_block_dots(fmt, _ptr(xq), _ptr(w), _ptr(dots, torch.int32), M, N, K,
+                                      _stream(stream)), "mmq_debug_block_dots")
+    return dots
+
+
+def plan_describe(fmt, M, N, K) -> tuple[bool, str]:
+    buf = ctypes.create_string_buffer(512)
+    ok = lib().mmq_plan_describe(fmt, M, N, K, buf, 512)
+    return bool(ok), buf.value.decode()
+
+
+def plan_for_limits(fmt, M, N, K, lds_limit, cu_count) -> tuple[bool, str]:
+    buf = ctypes.create_string_buffer(512)
+    ok = lib().mmq_plan_for_limits(fmt, M, N, K, lds_limit, cu_count, buf, 512)
+    return bool(ok), buf.value.decode()
+
+
+def set_extra_lds(nbytes: int) -> None:
+    lib().mmq_debug_set_extra_lds(nbytes)
+
+
+def version() -> str:
+    return lib().mmq_version().decode()

@@ -1,0 +1,174 @@
+// mmq_api.hip -- the C ABI declared in include/mmq.h.
+//
+// Launch protocol ("13 . r7-r8 raw-byte MMQ kernel", sections 3.3 and 6):
+// every entry point returns 1 when the kernel was enqueued and 0 when it was
+// refused; a refusal is decided before any device work (so no output byte is
+// written), printed to stderr and kept in a thread-local string; launch
+// errors are read back with hipGetLastError() and reported the same way.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/mmq.h"
+#include "mmq_plan.hpp"
+
+namespace mmq {
+hipError_t launch_quantize(const float *x, void *y, int64_t M, int64_t K, int cu_count, hipStream_t stream);
+hipError_t launch_gemm(const Plan &p, const void *x, const void *w, void *out, int64_t M, int64_t N,
+                       int64_t K, bool dots, hipStream_t stream);
+}  // namespace mmq
+
+namespace {
+
+thread_local char g_err[512] = "";
+std::atomic<int64_t> g_extra_lds{0};
+
+int refuse(const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    std::fprintf(stderr, "mmq: refused: %s\n", g_err);
+    return 0;
+}
+
+struct DeviceLimits {
+    bool valid = false;
+    bool is_gfx950 = false;
+    int64_t lds_per_block = 0;
+    int cu_count = 0;
+    char arch[64] = "";
+};
+
+constexpr int kMaxDevices = 64;
+DeviceLimits g_limits[kMaxDevices];
+std::mutex g_limits_mu;
+
+// Current device's limits (cached per device). Returns false and sets the
+// error when there is no usable device.
+bool current_limits(DeviceLimits *out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        refuse("no HIP device available");
+        return false;
+    }
+    std::lock_guard<std::mutex> lock(g_limits_mu);
+    DeviceLimits &L = g_limits[dev];
+    if (!L.valid) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            refuse("hipGetDeviceProperties failed for device %d", dev);
+            return false;
+        }
+        int lds = 0, cus = 0;
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            refuse("hipDeviceGetAttribute failed for device %d", dev);
+            return false;
+        }
+        std::snprintf(L.arch, sizeof(L.arch), "%s", prop.gcnArchName);
+        L.is_gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        L.lds_per_block = lds;
+        L.cu_count = cus;
+        L.valid = true;
+    }
+    *out = L;
+    return true;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int gemm_common(int fmt, const void *x, const void *w, void *out, int64_t M, int64_t N, int64_t K,
+                bool dots, void *stream) {
+    g_err[0] = '\0';
+    if (!mmq::fmt_ok(fmt)) return refuse("unknown weight format %d", fmt);
+    if (!x || !w || !out) return refuse("null pointer argument");
+    if (!aligned(x, 16) || !aligned(w, 16)) return refuse("activation and weight pointers must be 16-byte aligned");
+    if (!aligned(out, 4)) return refuse("output pointer must be 4-byte aligned");
+    DeviceLimits L;
+    if (!current_limits(&L)) return 0;
+    if (!L.is_gfx950) return refuse("device is %s; this library is built for gfx950 only", L.arch);
+    mmq::Plan p;
+    char why[256];
+    if (!mmq::make_plan(fmt, M, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), &p, why, sizeof(why)))
+        return refuse("%s GEMM M=%lld N=%lld K=%lld: %s", mmq::fmt_name(fmt), (long long)M, (long long)N,
+                      (long long)K, why);
+    (void)hipGetLastError();   // a stale error must not be blamed on this launch
+    const hipError_t e = mmq::launch_gemm(p, x, w, out, M, N, K, dots, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return refuse("%s GEMM launch failed: %s", mmq::fmt_name(fmt), hipGetErrorString(e));
+    return 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mmq_quantize_q8_1(const float *x, void *y, int64_t M, int64_t K, void *stream) {
+    g_err[0] = '\0';
+    if (!x || !y) return refuse("null pointer argument");
+    if (!aligned(x, 16) || !aligned(y, 16)) return refuse("x and y must be 16-byte aligned");
+    if (const char *bad = mmq::check_quantize_shape(M, K))
+        return refuse("quantize M=%lld K=%lld: %s", (long long)M, (long long)K, bad);
+    DeviceLimits L;
+    if (!current_limits(&L)) return 0;
+    if (!L.is_gfx950) return refuse("device is %s; this library is built for gfx950 only", L.arch);
+    (void)hipGetLastError();
+    const hipError_t e = mmq::launch_quantize(x, y, M, K, L.cu_count, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return refuse("quantize launch failed: %s", hipGetErrorString(e));
+    return 1;
+}
+
+int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out, int64_t M, int64_t N, int64_t K,
+                  void *stream) {
+    return gemm_common(mmq::FMT_Q8_0, x_q8_1, w_q8_0, out, M, N, K, false, stream);
+}
+
+int mmq_gemm_q4_K(const void *x_q8_1, const void *w_q4_K, float *out, int64_t M, int64_t N, int64_t K,
+                  void *stream) {
+    return gemm_common(mmq::FMT_Q4_K, x_q8_1, w_q4_K, out, M, N, K, false, stream);
+}
+
+int mmq_debug_block_dots(int fmt, const void *x_q8_1, const void *w, int32_t *dots, int64_t M, int64_t N,
+                         int64_t K, void *stream) {
+    return gemm_common(fmt, x_q8_1, w, dots, M, N, K, true, stream);
+}
+
+const char *mmq_last_error(void) { return g_err; }
+
+int mmq_plan_for_limits(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limit_bytes, int cu_count,
+                        char *buf, int64_t len) {
+    mmq::Plan p;
+    char why[256];
+    const bool ok = mmq::make_plan(fmt, M, N, K, lds_limit_bytes, cu_count, g_extra_lds.load(), &p, why,
+                                   sizeof(why));
+    if (buf && len > 0) {
+        if (ok)
+            mmq::describe(p, buf, size_t(len));
+        else
+            std::snprintf(buf, size_t(len), "%s", why);
+    }
+    return ok ? 1 : 0;
+}
+
+int mmq_plan_describe(int fmt, int64_t M, int64_t N, int64_t K, char *buf, int64_t len) {
+    DeviceLimits L;
+    if (!current_limits(&L)) {
+        if (buf && len > 0) std::snprintf(buf, size_t(len), "%s", g_err);
+        return 0;
+    }
+    return mmq_plan_for_limits(fmt, M, N, K, L.lds_per_block, L.cu_count, buf, len);
+}
+
+void mmq_debug_set_extra_lds(int64_t extra_bytes) { g_extra_lds.store(extra_bytes < 0 ? 0 : extra_bytes); }
+
+const char *mmq_version(void) { return "mmq-gfx950 0.1"; }
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// mmq_plan.hpp -- launch planning and the capacity guard (pure host C++).
+//
+// "13 . r7-r8 raw-byte MMQ kernel", sections 3.3 and 6: a tile whose shared
+// memory exceeds the device's cap must be refused by the launcher before
+// launch, loudly, instead of failing silently and leaving the output
+// unwritten.  Every refusal decision of the library lives here, in code with
+// no HIP calls, so that it can be exercised without a GPU.
+#pragma once
+
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+namespace mmq {
+
+enum Fmt : int { FMT_Q8_0 = 0, FMT_Q4_K = 1 };
+
+// Geometry of the GEMM kernel (must match the kernel's compile-time tile).
+constexpr int kTileM = 128;        // output rows per workgroup
+constexpr int kTileN = 128;        // output columns per workgroup
+constexpr int kThreads = 256;      // four wave64s; wave w owns rows 32w..32w+31
+constexpr int kBlocksPerStage = 8; // 32-blocks staged per k-step (one Q4_K super-block)
+
+// LDS layout sizes in bytes for one k-step (see the kernel for the layouts).
+constexpr int64_t lds_bytes_for(int fmt) {
+    // activation codes [8][2][128][16] + activation scales [8][128] fp32
+    int64_t a = int64_t(kBlocksPerStage) * 2 * kTileM * 16 + int64_t(kBlocksPerStage) * kTileM * 4;
+    if (fmt == FMT_Q8_0) {
+        // weight codes [8][2][128][16] + weight scales [8][128] fp32
+        return a + int64_t(kBlocksPerStage) * 2 * kTileN * 16 + int64_t(kBlocksPerStage) * kTileN * 4;
+    }
+    // Q4_K: packed codes [4][2][128][16] + d*sc [8][128] fp32
+    //       + min-term operand [128][2][8] fp16 + activation sums [128][8] fp16
+    return a + int64_t(4) * 2 * kTileN * 16 + int64_t(kBlocksPerStage) * kTileN * 4 +
+           int64_t(kTileN) * 2 * 8 * 2 + int64_t(kTileM) * 8 * 2;
+}
+
+struct Plan {
+    int fmt = 0;
+    int tile_m = kTileM, tile_n = kTileN, threads = kThreads, blocks_per_stage = kBlocksPerStage;
+    int64_t lds_bytes = 0;
+    int64_t grid_x = 0, grid_y = 0;   // x: column tiles, y: row tiles
+    int64_t k_steps = 0;
+};
+
+inline bool fmt_ok(int fmt) { return fmt == FMT_Q8_0 || fmt == FMT_Q4_K; }
+inline const char *fmt_name(int fmt) { return fmt == FMT_Q8_0 ? "Q8_0" : fmt == FMT_Q4_K ? "Q4_K" : "?"; }
+
+// Shape checks shared by the quantize pass.  Returns nullptr when fine.
+inline const char *check_quantize_shape(int64_t M, int64_t K) {
+    if (M < 1 || K < 1) return "M and K must be >= 1";
+    if (K % 32 != 0) return "K must be a multiple of 32 (whole q8_1 blocks)";
+    if (M > (int64_t(1) << 40) / K) return "M*K too large";
+    return nullptr;
+}
+
+// Build the GEMM plan or explain the refusal.  `extra_lds` is the test hook.
+inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limit, int cu_count,
+                      int64_t extra_lds, Plan *p, char *why, size_t why_len) {
+    auto fail = [&](const char *msg) {
+        if (why && why_len) std::snprintf(why, why_len, "%s", msg);
+        return false;
+    };
+    if (!fmt_ok(fmt)) return fail("unknown weight format");
+    if (M < 1 || N < 1 || K < 1) return fail("M, N and K must be >= 1");
+    if (K % 256 != 0)
+        return fail(fmt == FMT_Q4_K ? "K must be a multiple of 256 (whole Q4_K super-blocks)"
+                                    : "K must be a multiple of 256 (whole 8-block k-steps)");
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail("M, N and K must fit in int32");
+    // Every byte offset the kernels form must fit in int64 comfortably.
+    if (M > (int64_t(1) << 50) / N || M > (int64_t(1) << 45) / (K / 32))
+        return fail("problem too large for 64-bit offsets");
+    if (cu_count < 1) return fail("device reports no compute units");
+    Plan q;
+    q.fmt = fmt;
+    q.lds_bytes = lds_bytes_for(fmt) + extra_lds;
+    q.grid_x = (N + kTileN - 1) / kTileN;
+    q.grid_y = (M + kTileM - 1) / kTileM;
+    q.k_steps = K / (32 * kBlocksPerStage);
+    if (q.grid_y > 65535) return fail("too many row tiles for the launch grid (M too large)");
+    if (q.grid_x > INT32_MAX) return fail("too many column tiles");
+    if (q.lds_bytes > lds_limit) {
+        if (why && why_len)
+            std::snprintf(why, why_len,
+                          "plan needs %lld B of LDS per workgroup, device allows %lld B: refused",
+                          (long long)q.lds_bytes, (long long)lds_limit);
+        return false;
+    }
+    *p = q;
+    return true;
+}
+
+inline void describe(const Plan &p, char *buf, size_t len) {
+    std::snprintf(buf, len,
+                  "fmt=%s tile=%dx%d threads=%d blocks_per_stage=%d lds=%lld grid=%lldx%lld k_steps=%lld",
+                  fmt_name(p.fmt), p.tile_m, p.tile_n, p.threads, p.blocks_per_stage,
+                  (long long)p.lds_bytes, (long long)p.grid_x, (long long)p.grid_y,
+                  (long long)p.k_steps);
+}
+
+}  // namespace mmq

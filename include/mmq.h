@@ -1,0 +1,126 @@
+/*
+ * mmq.h -- C ABI of the block-quantized int8 MMQ library for AMD MI355X
+ * (gfx950).
+ *
+ * The operation ("When the Product Won't Collapse: A Negative Result on int8
+ * Tensor-Core MMQ", section 2, the displayed contraction):
+ *
+ *     out[m,n] = sum over 32-element k-blocks b of
+ *                (activation scale[m,b] * weight scale[n,b]) * I[m,n,b],
+ *     I[m,n,b] = exact int32 dot of the 32 activation codes of row m and the
+ *                32 weight codes of row n inside block b.
+ *
+ * For Q4_K weights the block term is the affine identity of "When Does a
+ * Kernel Win Surface?" (section 6.2): d*sc * xs * I - dmin*m * xsum, with
+ * (sc, m) the 6-bit scale and min of the weight sub-block and xsum the
+ * activation block-sum field of q8_1.  Activations are quantized to q8_1 once
+ * per GEMM input by a separate pass ("13 . r7-r8 raw-byte MMQ kernel",
+ * section 3.2, quantize pass; the same page's section 1 keeps it a pass of
+ * its own).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or synchronises; work is enqueued on `stream`
+ *    (a hipStream_t passed as void*; NULL is the null stream) and runs
+ *    asynchronously.
+ *  - Return value: 1 = launched; 0 = refused.  A refusal enqueues nothing and
+ *    writes no output byte; the reason is returned by mmq_last_error() and
+ *    printed to stderr.  The library never falls back silently: a caller that
+ *    wants a fallback decides it ("13 . r7-r8 raw-byte MMQ kernel", section
+ *    3.3: a launch that fails must be reported, never mistaken for success).
+ *  - Refusal causes, all checked on the host before any device work: null
+ *    pointer, M/N/K < 1, K not a multiple of the format's block, a pointer not
+ *    16-byte aligned (4-byte for `out`/`dots`), sizes beyond int32 tile
+ *    indexing, no HIP device or a device that is not gfx950, a launch plan
+ *    whose LDS exceeds the device's per-workgroup maximum, and any launch
+ *    error reported by hipGetLastError().
+ *  - Faults that happen asynchronously on the device surface at the caller's
+ *    next synchronisation and are outside this contract.
+ *  - Inputs must be finite; non-finite activations give unspecified codes.
+ *  - Thread safety: entry points may be called from several host threads; the
+ *    only global state is a per-device limits cache and a thread-local error
+ *    string.
+ *
+ * Byte layouts (little-endian, blocks packed back to back, row-major over
+ * blocks):
+ *  - q8_1 activation block, 36 B per 32 values: fp16 d @0, fp16 s @2 where
+ *    s = fp16(d * sum of codes), 32 x int8 codes @4.
+ *  - Q8_0 weight block, 34 B per 32 values: fp16 d @0, 32 x int8 codes @2.
+ *  - Q4_K weight super-block, 144 B per 256 values: fp16 d @0, fp16 dmin @2,
+ *    12 B of packed 6-bit sub-block scales and mins @4 (GGUF K-quant packing),
+ *    128 B of 4-bit codes @16 where code byte 32*g + i holds element 64*g + i
+ *    in its low nibble and element 64*g + 32 + i in its high nibble.
+ */
+#ifndef MMQ_H
+#define MMQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MMQ_FMT_Q8_0 0
+#define MMQ_FMT_Q4_K 1
+
+/* Quantize fp32 activations to q8_1 ("13 . r7-r8 raw-byte MMQ kernel",
+ * section 3.2; q8_1 fields from "When Does a Kernel Win Surface?", 6.2).
+ *   x: M x K fp32, row-major (leading dimension K), 16-byte aligned.
+ *   y: M x (K/32) q8_1 blocks (36 B each), row-major, 16-byte aligned.
+ * Per block: amax = max |x|, d = amax/127 (fp32, correctly rounded),
+ * code = round-half-away(x * (1/d)) clamped to [-127, 127] (d = 0 gives all
+ * codes 0), s = fp16(d * sum of codes).  Requires K % 32 == 0. */
+int mmq_quantize_q8_1(const float *x, void *y, int64_t M, int64_t K, void *stream);
+
+/* q8_1 activations x Q8_0 weights -> fp32 ("When the Product Won't
+ * Collapse", section 2).
+ *   x_q8_1: M x (K/32) q8_1 blocks; w_q8_0: N x (K/32) Q8_0 blocks;
+ *   out: M x N fp32 row-major (leading dimension N), fully overwritten.
+ * Per block the weight scale multiplies the integer dot first (one
+ * rounding) and the activation scale is then fused into the fp32 running
+ * sum, blocks in ascending order from 0.  Requires K % 256 == 0. */
+int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out,
+                  int64_t M, int64_t N, int64_t K, void *stream);
+
+/* q8_1 activations x Q4_K weights -> fp32 ("When Does a Kernel Win
+ * Surface?", section 6.2, affine identity with the min term folded in
+ * through the q8_1 block-sum field).
+ *   x_q8_1: M x (K/32) q8_1 blocks; w_q4_K: N x (K/256) super-blocks;
+ *   out: M x N fp32 row-major, fully overwritten.  Requires K % 256 == 0. */
+int mmq_gemm_q4_K(const void *x_q8_1, const void *w_q4_K, float *out,
+                  int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Test entry: the exact int32 block dots I[m,n,b] through the same staging
+ * and matrix-core code as the GEMM of format `fmt` (MMQ_FMT_Q8_0 or
+ * MMQ_FMT_Q4_K), written to dots[(m*N + n)*(K/32) + b].  Same refusal rules
+ * as the GEMM. */
+int mmq_debug_block_dots(int fmt, const void *x_q8_1, const void *w, int32_t *dots,
+                         int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Reason for the calling thread's last refusal ("" if none). Static storage. */
+const char *mmq_last_error(void);
+
+/* Describe the launch plan the GEMM of `fmt` would use on the current device
+ * (tile, LDS bytes, grid) into buf (NUL-terminated).  Returns 1 if the plan
+ * would launch, 0 if it would be refused (reason in buf). */
+int mmq_plan_describe(int fmt, int64_t M, int64_t N, int64_t K, char *buf, int64_t len);
+
+/* Pure host planning with explicit device limits, so that the guard can be
+ * checked without a GPU.  Same return convention as mmq_plan_describe. */
+int mmq_plan_for_limits(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limit_bytes,
+                        int cu_count, char *buf, int64_t len);
+
+/* Test hook: add `extra_bytes` to the LDS every GEMM plan requests from now
+ * on (0 restores normal plans).  Used to check that an over-capacity plan is
+ * refused before launch.  Process-wide; not for production use. */
+void mmq_debug_set_extra_lds(int64_t extra_bytes);
+
+/* Library version string. */
+const char *mmq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MMQ_H */

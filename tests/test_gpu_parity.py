@@ -1,0 +1,233 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+Bars: q8_1 bytes and int32 block dots bit-exact; fp32 outputs within 1e-5 of
+the oracle by the normalized measure in tests/metrics.py (Q8_0 is also
+bit-identical by construction: same per-block arithmetic in the same order).
+Every output buffer is pre-filled with a NaN sentinel, so an element the
+kernel never wrote fails the test ("13 . r7-r8 raw-byte MMQ kernel",
+section 3.3: prove the kernel ran).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_int8_q8_amd as mmq
+import oracle
+from block_quantized_int8_q8_amd import inputs
+from tests import golden_cases, metrics
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _nan_out(M, N):
+    return torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+
+
+def _gpu_quantize(x: np.ndarray) -> np.ndarray:
+    M, K = x.shape
+    y = torch.full((M, K // 32, 36), 0xA5, dtype=torch.uint8, device=DEV)
+    mmq.quantize_q8_1(_to_dev(x), y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+# ------------------------------------------------------------------ quantize
+
+@pytest.mark.parametrize("M,K,seed", [(1, 32, 1), (3, 64, 2), (64, 512, 3), (129, 3584, 4),
+                                      (2048, 3584, inputs.seed_for(2, 0)), (7, 18944, 5)])
+def test_quantize_bit_exact(M, K, seed):
+    _say(f"quantize M={M} K={K} seed={seed}")
+    x = inputs.activations(M, K, seed)
+    assert np.array_equal(_gpu_quantize(x), oracle.quantize_q8_1(x))
+
+
+def test_quantize_special_blocks():
+    _say("quantize special blocks")
+    xs, d_bits, s_bits, codes = golden_cases.q8_1_blocks()
+    rows = [xs.reshape(1, -1)]
+    r = np.random.default_rng(0)
+    scale = np.float32(2.0 ** -3)
+    ties = np.zeros((1, 32), np.float32)
+    ties[0, :31] = (np.arange(31) + 0.5) * scale * np.where(np.arange(31) % 2, 1, -1)
+    ties[0, 31] = 127 * scale
+    tiny = (r.standard_normal((1, 64)) * 1e-39).astype(np.float32)   # fp32 subnormal inputs
+    huge = (r.standard_normal((1, 64)) * 1e37).astype(np.float32)
+    sparse = np.zeros((1, 96), np.float32)
+    sparse[0, 40] = -1e-3
+    for x in rows + [ties, tiny, huge, sparse]:
+        assert np.array_equal(_gpu_quantize(x), oracle.quantize_q8_1(x))
+    y = _gpu_quantize(xs.reshape(1, -1))[0]
+    assert np.array_equal(y[:, 0:2].copy().view("<u2")[:, 0], d_bits)
+    assert np.array_equal(y[:, 2:4].copy().view("<u2")[:, 0], s_bits)
+    assert np.array_equal(y[:, 4:].view(np.int8).astype(np.int64), codes)
+
+
+# ------------------------------------------------------------------ block dots
+
+def _weights(fmt, N, K, seed):
+    return inputs.q8_0_weights(N, K, seed) if fmt == mmq.FMT_Q8_0 else inputs.q4_K_weights(N, K, seed)
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (200, 300, 768), (128, 128, 512), (33, 517, 256)])
+def test_block_dots_bit_exact(fmt, M, N, K):
+    _say(f"dots fmt={fmt} M={M} N={N} K={K}")
+    x = inputs.q8_1_blocks(M, K, 10 + M)
+    w = _weights(fmt, N, K, 20 + N)
+    dots = torch.full((M, N, K // 32), -(2 ** 31), dtype=torch.int32, device=DEV)
+    mmq.debug_block_dots(fmt, _to_dev(x), _to_dev(w), M, N, K, dots)
+    torch.cuda.synchronize()
+    ref = (oracle.block_dots_q8_0 if fmt == mmq.FMT_Q8_0 else oracle.block_dots_q4_K)(x, w, M, N, K)
+    assert np.array_equal(dots.cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------ GEMMs
+
+def _run_gemm(fmt, xq, w, M, N, K):
+    out = _nan_out(M, N)
+    f = mmq.gemm_q8_0 if fmt == mmq.FMT_Q8_0 else mmq.gemm_q4_K
+    f(_to_dev(xq), _to_dev(w), M, N, K, out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert not np.isnan(o).any(), "output element left unwritten"
+    return o
+
+
+def _oracle_gemm(fmt, xq, w, M, N, K, rows=None):
+    f = oracle.gemm_q8_0 if fmt == mmq.FMT_Q8_0 else oracle.gemm_q4_K
+    return f(xq, w, M, N, K, nthreads=16, rows=rows)
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (64, 256, 512), (200, 300, 768), (129, 257, 1024),
+                                   (300, 130, 2048)])
+def test_gemm_matches_oracle(fmt, M, N, K):
+    _say(f"gemm fmt={fmt} M={M} N={N} K={K}")
+    x = inputs.activations(M, K, 30 + M)
+    xq = oracle.quantize_q8_1(x)
+    w = _weights(fmt, N, K, 40 + N)
+    got = _run_gemm(fmt, xq, w, M, N, K)
+    ref = _oracle_gemm(fmt, xq, w, M, N, K)
+    rep = metrics.report(got, ref)
+    _say(rep)
+    assert rep["normalized_max_error"] <= metrics.TOL
+    if fmt == mmq.FMT_Q8_0:
+        assert rep["bit_identical_fraction"] == 1.0
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+def test_gemm_on_random_q8_1_fields(fmt):
+    """Fields not tied to each other (s independent of the codes): the
+    contraction must read d, s and the codes exactly as stored."""
+    M, N, K = 150, 200, 512
+    _say(f"gemm random fields fmt={fmt}")
+    xq = inputs.q8_1_blocks(M, K, 77)
+    w = _weights(fmt, N, K, 78)
+    got = _run_gemm(fmt, xq, w, M, N, K)
+    ref = _oracle_gemm(fmt, xq, w, M, N, K)
+    assert metrics.normalized_max_error(got, ref) <= metrics.TOL
+
+
+def test_gemm_hand_cases():
+    _say("gemm hand cases")
+    x, w, K, expect = golden_cases.gemm_q8_0_case()
+    xq = _gpu_quantize(x)
+    assert _run_gemm(mmq.FMT_Q8_0, xq, w, 1, 1, K)[0, 0] == expect
+    x, w, K, expect = golden_cases.gemm_q4_K_case()
+    xq = _gpu_quantize(x)
+    assert _run_gemm(mmq.FMT_Q4_K, xq, w, 1, 1, K)[0, 0] == expect
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_full_size_configs_sampled_rows(cfg):
+    """Benchmark shapes, full launch: GPU quantize then GPU GEMM on device
+    (the benchmarked path); the oracle checks the quantized bytes in full and
+    the output on sampled rows (first, last, last row tile, random)."""
+    fmt_name, M, N, K = inputs.CONFIGS[cfg]
+    fmt = mmq.FMT_Q8_0 if fmt_name == "q8_0" else mmq.FMT_Q4_K
+    _say(f"full config {cfg}: {fmt_name} M={M} N={N} K={K}")
+    x = inputs.activations(M, K, inputs.seed_for(cfg, 0))
+    w = _weights(fmt, N, K, inputs.seed_for(cfg, 1))
+    xd = _to_dev(x)
+    xq_dev = mmq.quantize_q8_1(xd)
+    out = _nan_out(M, N)
+    (mmq.gemm_q8_0 if fmt == mmq.FMT_Q8_0 else mmq.gemm_q4_K)(xq_dev, _to_dev(w), M, N, K, out)
+    torch.cuda.synchronize()
+    xq = oracle.quantize_q8_1(x)
+    assert np.array_equal(xq_dev.cpu().numpy(), xq)
+    o = out.cpu().numpy()
+    assert not np.isnan(o).any()
+    rows = sorted(set([0, 1, M - 1, M - 128, M // 2] + list(np.random.default_rng(cfg).integers(0, M, 6))))
+    sub = np.ascontiguousarray(xq[rows])
+    ref = _oracle_gemm(fmt, sub, w, len(rows), N, K)
+    rep = metrics.report(o[rows], ref)
+    _say(rep)
+    assert rep["normalized_max_error"] <= metrics.TOL
+
+
+def test_nondefault_stream():
+    _say("non-default stream")
+    M, N, K = 96, 160, 512
+    x = inputs.activations(M, K, 5)
+    w = inputs.q4_K_weights(N, K, 6)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        xd = _to_dev(x)
+        wd = _to_dev(w)
+        xq = mmq.quantize_q8_1(xd, stream=s)
+        out = _nan_out(M, N)
+        mmq.gemm_q4_K(xq, wd, M, N, K, out, stream=s)
+    s.synchronize()
+    ref = oracle.gemm_q4_K(oracle.quantize_q8_1(x), w, M, N, K)
+    assert metrics.normalized_max_error(out.cpu().numpy(), ref) <= metrics.TOL
+
+
+# ------------------------------------------------------------------ refusals
+
+def test_refusals_leave_output_untouched():
+    _say("refusals")
+    M, N, K = 64, 128, 512
+    xq = _to_dev(inputs.q8_1_blocks(M, K, 1))
+    w = _to_dev(inputs.q8_0_weights(N, K, 2))
+    out = _nan_out(M, N)
+    try:
+        mmq.set_extra_lds(200 * 1024)
+        with pytest.raises(mmq.MMQError, match="LDS"):
+            mmq.gemm_q8_0(xq, w, M, N, K, out)
+        with pytest.raises(mmq.MMQError, match="LDS"):
+            mmq.debug_block_dots(mmq.FMT_Q8_0, xq, w, M, N, K)
+    finally:
+        mmq.set_extra_lds(0)
+    with pytest.raises(mmq.MMQError, match="multiple of 256"):
+        mmq.gemm_q8_0(xq, w, M, N, K - 32, out)
+    with pytest.raises(mmq.MMQError, match="aligned"):
+        mmq.gemm_q8_0(xq.view(-1)[4:4 + 36 * M * 15].view(M, 15, 36), w, M, N, 480 + 0 * K, out)
+    with pytest.raises(mmq.MMQError, match=">= 1"):
+        mmq.gemm_q8_0(xq, w, 0, N, K, out)
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
+    # a normal call afterwards works and writes everything
+    mmq.gemm_q8_0(xq, w, M, N, K, out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any()
+
+
+def test_quantize_refusals():
+    _say("quantize refusals")
+    x = torch.zeros((4, 48), dtype=torch.float32, device=DEV)
+    with pytest.raises(mmq.MMQError, match="multiple of 32"):
+        mmq.quantize_q8_1(x, torch.empty((4, 2, 36), dtype=torch.uint8, device=DEV))
+    ok, desc = mmq.plan_describe(mmq.FMT_Q4_K, 2048, 18944, 3584)
+    assert ok, desc

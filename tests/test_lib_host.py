@@ -1,0 +1,88 @@
+"""Host-side checks of the GPU library that need no GPU: every symbol the
+header declares is exported, and the launch guard (pure host planning)
+refuses what it must ("13 . r7-r8 raw-byte MMQ kernel", sections 3.3 and 6:
+an over-capacity plan is refused before launch, never run silently)."""
+import os
+import re
+
+import pytest
+
+import block_quantized_int8_q8_amd as mmq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LDS_GFX950 = 160 * 1024
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "mmq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mmq_[A-Za-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = mmq.lib()
+    syms = declared_symbols()
+    assert len(syms) >= 9
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(mmq.EXPORTS) == set(syms)
+
+
+def test_library_carries_gfx950_code_only():
+    blob = open(mmq.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+    for other in (b"gfx942", b"gfx90a", b"gfx1100"):
+        assert b"amdgcn-amd-amdhsa--" + other not in blob
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [
+    (mmq.FMT_Q8_0, 64, 256, 512), (mmq.FMT_Q8_0, 2048, 3584, 3584),
+    (mmq.FMT_Q4_K, 2048, 18944, 3584), (mmq.FMT_Q4_K, 2048, 3584, 18944),
+    (mmq.FMT_Q4_K, 8192, 512, 3584), (mmq.FMT_Q8_0, 1, 1, 256),
+])
+def test_plans_for_benchmark_shapes_fit(fmt, M, N, K):
+    ok, desc = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
+    assert ok, desc
+    lds = int(re.search(r"lds=(\d+)", desc).group(1))
+    assert lds <= 80 * 1024          # two workgroups fit in one CU's 160 KiB
+    gx, gy = map(int, re.search(r"grid=(\d+)x(\d+)", desc).groups())
+    assert gx == -(-N // 128) and gy == -(-M // 128)
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+def test_guard_refuses_over_capacity_lds(fmt):
+    ok, desc = mmq.plan_for_limits(fmt, 2048, 3584, 3584, LDS_GFX950, 256)
+    need = int(re.search(r"lds=(\d+)", desc).group(1))
+    assert mmq.plan_for_limits(fmt, 2048, 3584, 3584, need, 256)[0]
+    ok, why = mmq.plan_for_limits(fmt, 2048, 3584, 3584, need - 1, 256)
+    assert not ok and "LDS" in why and "refused" in why
+
+
+def test_extra_lds_hook_forces_refusal():
+    try:
+        mmq.set_extra_lds(LDS_GFX950)
+        ok, why = mmq.plan_for_limits(mmq.FMT_Q8_0, 64, 256, 512, LDS_GFX950, 256)
+        assert not ok and "LDS" in why
+    finally:
+        mmq.set_extra_lds(0)
+    assert mmq.plan_for_limits(mmq.FMT_Q8_0, 64, 256, 512, LDS_GFX950, 256)[0]
+
+
+@pytest.mark.parametrize("fmt,M,N,K,needle", [
+    (mmq.FMT_Q8_0, 64, 256, 288, "multiple of 256"),
+    (mmq.FMT_Q4_K, 64, 256, 512 + 32, "super-blocks"),
+    (mmq.FMT_Q8_0, 0, 256, 512, ">= 1"),
+    (mmq.FMT_Q8_0, 64, 0, 512, ">= 1"),
+    (mmq.FMT_Q8_0, 64, 256, 0, ">= 1"),
+    (7, 64, 256, 512, "format"),
+    (mmq.FMT_Q8_0, 1 << 31, 256, 512, "int32"),
+    (mmq.FMT_Q8_0, (65536 * 128), 256, 512, "row tiles"),
+])
+def test_guard_refuses_bad_shapes(fmt, M, N, K, needle):
+    ok, why = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
+    assert not ok and needle in why, why
+
+
+def test_guard_refuses_without_compute_units():
+    ok, why = mmq.plan_for_limits(mmq.FMT_Q8_0, 64, 256, 512, LDS_GFX950, 0)
+    assert not ok and "compute units" in why
