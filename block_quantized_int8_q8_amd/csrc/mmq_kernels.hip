@@ -50,7 +50,10 @@ __global__ __launch_bounds__(256) void k_quantize_q8_1(const float *__restrict__
         am = fmaxf(am, __shfl_xor(am, 2, 8));
         am = fmaxf(am, __shfl_xor(am, 4, 8));
         const float d = am / 127.0f;                    // correctly rounded fp32 divide
-        const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+        // id = 1/d; a zero block, or one so small that 1/d overflows fp32,
+        // quantizes to all-zero codes (its fp16 scale is 0 as well)
+        float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+        if (__builtin_isinf(id)) id = 0.0f;
         // round half away from zero (roundf), then clamp to the symmetric range
         int q0 = (int)roundf(v.x * id), q1 = (int)roundf(v.y * id);
         int q2 = (int)roundf(v.z * id), q3 = (int)roundf(v.w * id);

@@ -69,8 +69,9 @@ extern "C" {
  *   x: M x K fp32, row-major (leading dimension K), 16-byte aligned.
  *   y: M x (K/32) q8_1 blocks (36 B each), row-major, 16-byte aligned.
  * Per block: amax = max |x|, d = amax/127 (fp32, correctly rounded),
- * code = round-half-away(x * (1/d)) clamped to [-127, 127] (d = 0 gives all
- * codes 0), s = fp16(d * sum of codes).  Requires K % 32 == 0. */
+ * code = round-half-away(x * (1/d)) clamped to [-127, 127] (d = 0, or a d
+ * so small that 1/d overflows fp32, gives all codes 0), s = fp16(d * sum of
+ * codes).  Requires K % 32 == 0. */
 int mmq_quantize_q8_1(const float *x, void *y, int64_t M, int64_t K, void *stream);
 
 /* q8_1 activations x Q8_0 weights -> fp32 ("When the Product Won't

@@ -40,7 +40,9 @@
  *   R3  the fp32 d = amax/127 quantizes; fp16 is only the stored copy.
  *   R4  the q8_1 sum field is fp16(d * (float)sum of codes).
  *   R5  codes clamp to [-127, 127] (never binds for finite input).
- *   R6  amax == 0 gives d = id = 0, all codes 0, sum field +0.
+ *   R6  amax == 0 gives d = id = 0, all codes 0, sum field +0; so does a
+ *       block whose fp32 reciprocal 1/d overflows to infinity (amax below
+ *       about 3.7e-37, where fp16(d) is 0 as well): id = 0, codes 0.
  *   R7  non-finite input is rejected (the function returns an error).
  *   R8  byte layouts (little-endian):
  *         q8_1 block (36 B): [0,2) fp16 d, [2,4) fp16 s, [4,36) int8 codes
@@ -192,6 +194,8 @@ int oracle_quantize_block_q8_1(const float *x, uint8_t *y)
     }
     float d = amax / 127.0f;                        /* R3 */
     float id = (d != 0.0f) ? 1.0f / d : 0.0f;        /* R2, R6 */
+    if (isinf(id))                                   /* R6: 1/d overflows fp32 */
+        id = 0.0f;
     int32_t sum = 0;
     for (int i = 0; i < QK; i++) {
         float v = x[i] * id;

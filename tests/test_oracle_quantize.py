@@ -139,3 +139,19 @@ def test_block_independence_and_layout():
     for m in range(3):
         for b in range(3):
             assert np.array_equal(y[m, b], _q(x[m, 32 * b:32 * b + 32]))
+
+
+@pytest.mark.parametrize("amax", [1e-39, 1e-38, 3.0e-37])
+def test_reciprocal_overflow_block_is_zero(amax):
+    """amax/127 below 1/FLT_MAX makes 1/d overflow; such a block quantizes
+    like the zero block (codes 0, s = 0) and its fp16 d is 0."""
+    x = (np.linspace(-1, 1, 32) * amax).astype(np.float32)
+    assert np.isinf(np.float32(1) / (np.abs(x).max() / np.float32(127)))
+    y = _q(x)
+    assert not y.any()
+
+
+def test_just_above_reciprocal_overflow_has_codes():
+    x = (np.linspace(-1, 1, 32) * 1e-36).astype(np.float32)
+    d, s, q = _fields(_q(x))
+    assert d == 0.0 and q[0] == -127 and q[-1] == 127
