@@ -143,8 +143,14 @@ def test_gemm_on_random_q8_1_fields(fmt):
 def test_gemm_hand_cases():
     _say("gemm hand cases")
     x, w, K, expect = golden_cases.gemm_q8_0_case()
-    xq = _gpu_quantize(x)
-    assert _run_gemm(mmq.FMT_Q8_0, xq, w, 1, 1, K)[0, 0] == expect
+    # the kernel takes whole 8-block k-steps: pad with all-zero blocks, which
+    # quantize to d = 0 and add exactly +0
+    xp = np.zeros((1, 256), np.float32)
+    xp[:, :K] = x
+    wp = np.zeros((1, 8, 34), np.uint8)
+    wp[:, :K // 32] = w
+    xq = _gpu_quantize(xp)
+    assert _run_gemm(mmq.FMT_Q8_0, xq, wp, 1, 1, 256)[0, 0] == expect
     x, w, K, expect = golden_cases.gemm_q4_K_case()
     xq = _gpu_quantize(x)
     assert _run_gemm(mmq.FMT_Q4_K, xq, w, 1, 1, K)[0, 0] == expect
