@@ -181,6 +181,8 @@ def main():
     ap.add_argument("--extra-configs", default="3,4", help="other shapes timed in the same run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -195,6 +197,15 @@ def main():
         sys.exit(1)
     import block_quantized_int8_q8_amd as mmq
     mmq.lib()   # fail loudly when the library is missing
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     main_rec = time_config(args.config, args.steps, args.warmup, check=not args.no_check)
     extra = {}

@@ -86,7 +86,10 @@ __global__ __launch_bounds__(256) void k_quantize_q8_1(const float *__restrict__
 //
 // Workgroup: 256 threads (4 wave64s) compute a 128 x 128 output tile; wave w
 // owns rows 32w..32w+31 and all 128 columns as four 32x32 sub-tiles.  Each
-// k-step stages 8 consecutive 32-blocks (one Q4_K super-block) into LDS.
+// k-step stages 4 consecutive 32-blocks (half a Q4_K super-block) into LDS;
+// a step's LDS (36-44 KiB) lets three or four workgroups share a CU, so that
+// every SIMD has several waves to switch between while one waits on LDS,
+// the matrix core or a barrier.
 //
 // Matrix core: v_mfma_i32_32x32x32_i8 takes exactly one 32-block as its K,
 // so every MFMA result is one exact block dot I (the block-boundary rule of
@@ -103,14 +106,14 @@ __global__ __launch_bounds__(256) void k_quantize_q8_1(const float *__restrict__
 //         one value per lane: its column's scale; the product 1.5*2^23*ws is
 //         exact, so t is the singly-rounded ws*I)
 //   acc = fma(xs, t, acc)                                 (xs = activation
-//         scale of the element's row)
+//         scale of the element's row, fp16 widened exactly inside the FMA)
 // For Q8_0 this is the same arithmetic, in the same block order, as the
 // oracle, so the output is bit-identical.
 //
-// Q4_K ("When Does a Kernel Win Surface?", 6.2): ws = d*sc_j (exact in fp32),
-// the 4-bit codes are unpacked from the raw packed bytes in registers
-// (low nibbles = even sub-block, high nibbles = odd sub-block of a 32-byte
-// group), and the min term  -sum_j dmin*m_j * s_j  of a whole super-block is
+// Q4_K ("When Does a Kernel Win Surface?", 6.2): ws = d*sc_j (exact in fp32);
+// the packed 4-bit codes are unpacked once per workgroup while staging (low
+// nibbles = even sub-block, high nibbles = odd sub-block of a 32-byte
+// group); and the min term  -sum_j dmin*m_j * s_j  of a whole super-block is
 // added by one fp16 MFMA per 32x32 sub-tile that accumulates straight into
 // the fp32 accumulator: A = the eight activation block sums s_j (fp16, as
 // stored), B = -dmin*m_j split exactly into an fp16 high and low part
@@ -118,13 +121,39 @@ __global__ __launch_bounds__(256) void k_quantize_q8_1(const float *__restrict__
 // ---------------------------------------------------------------------------
 constexpr uint32_t kMagicBits = 0x4B400000u;   // 12582912.0f
 constexpr float kMagic = 12582912.0f;
+constexpr int KB = kBlocksPerStage;            // 32-blocks per k-step
+
+// LDS layouts.  Codes (activations, and weights of either format once
+// unpacked to one int8 code per byte) are row-major, 128 bytes per row = 8
+// chunks of 16 bytes (block b of the step, k-half g -> chunk 2b+g), with the
+// chunk index XOR-swizzled by row%8.  A fragment read (32 consecutive rows,
+// one chunk) then touches eight distinct 16-byte bank groups per 8-lane
+// phase, and staging writes are at worst 2-way conflicted, with no padding.
+//
+// Activation scales stay fp16 as stored in q8_1 and are consumed by
+// v_fma_mix_f32 (exact widening inside the FMA).  They are kept per block in
+// accumulator-fragment order: within each 32-row group, lane half g needs the
+// scales of rows 8q + 4g + i (q, i = 0..3) for its registers r = 4q + i, so
+// position 16g + 4q + i holds row 8q + 4g + i and a lane reads its 16 scales
+// as two contiguous 16-byte words.  Planes are 272 bytes apart (16-byte
+// aligned, 4 banks apart).  Weight scales are fp32 [block][column] planes of
+// 132 floats (staging writes of one column's blocks land on distinct banks);
+// Q4_K keeps all eight planes of a super-block, written at its first step.
+constexpr int kRowBytes = KB * 32;   // codes per row per step
+constexpr int kPlaneH = 136;         // halves per activation-scale plane
+constexpr int kPlane = 132;          // floats per weight-scale plane
+
+__device__ __forceinline__ int chunk_off(int row, int j) { return row * kRowBytes + ((j ^ (row & 7)) << 4); }
+__device__ __forceinline__ int xs_pos(int row) {
+    return (row & ~31) + (((row >> 2) & 1) << 4) + (((row >> 3) & 3) << 2) + (row & 3);
+}
 
 template <int FMT>
 struct Lds {
-    static constexpr int A_CODES = kBlocksPerStage * 2 * kTileM * 16;   // [b][g][row][16]
-    static constexpr int A_SCALE = kBlocksPerStage * kTileM * 4;        // [b][row] fp32
-    static constexpr int B_CODES = (FMT == FMT_Q8_0 ? kBlocksPerStage : 4) * 2 * kTileN * 16;
-    static constexpr int B_SCALE = kBlocksPerStage * kTileN * 4;        // [b][col] fp32
+    static constexpr int A_CODES = kTileM * kRowBytes;
+    static constexpr int A_SCALE = KB * kPlaneH * 2;
+    static constexpr int B_CODES = kTileN * kRowBytes;
+    static constexpr int B_SCALE = (FMT == FMT_Q8_0 ? KB : 8) * kPlane * 4;
     static constexpr int B_MIN = (FMT == FMT_Q4_K) ? kTileN * 2 * 8 * 2 : 0;   // [col][g][8] fp16
     static constexpr int A_SUM = (FMT == FMT_Q4_K) ? kTileM * 8 * 2 : 0;       // [row][8] fp16
     static constexpr int OFF_A_SCALE = A_CODES;
@@ -134,150 +163,231 @@ struct Lds {
     static constexpr int OFF_A_SUM = OFF_B_MIN + B_MIN;
     static constexpr int TOTAL = OFF_A_SUM + A_SUM;
 };
+static_assert(KB == 4, "the staging maps below assume 4 blocks per k-step");
 static_assert(Lds<FMT_Q8_0>::TOTAL == lds_bytes_for(FMT_Q8_0), "plan and kernel LDS disagree");
 static_assert(Lds<FMT_Q4_K>::TOTAL == lds_bytes_for(FMT_Q4_K), "plan and kernel LDS disagree");
+static_assert(Lds<FMT_Q4_K>::OFF_B_CODES % 16 == 0 && Lds<FMT_Q4_K>::OFF_B_MIN % 16 == 0 &&
+              Lds<FMT_Q4_K>::OFF_A_SUM % 16 == 0 && Lds<FMT_Q8_0>::OFF_B_SCALE % 16 == 0,
+              "LDS regions must stay 16-byte aligned");
 
-// Stage the 8 q8_1 blocks of k-step `ks` for the tile's 128 rows.
-// Unit u -> (row = u/8, block = u%8): eight consecutive threads read one
-// row's 288 contiguous bytes.  Rows past M are zero-filled (codes and scale 0,
-// so they add nothing and are never stored).
-template <int FMT>
-__device__ __forceinline__ void stage_activations(const uint8_t *__restrict__ xq, uint8_t *smem,
-                                                  int M, int kb, int m0, int ks, int tid) {
-    using L = Lds<FMT>;
-    float *sXd = reinterpret_cast<float *>(smem + L::OFF_A_SCALE);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int u = tid + kThreads * i;
-        const int row = u >> 3, b = u & 7;
-        const int m = m0 + row;
-        uint32_t w[9];
-        if (m < M) {
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(
-                xq + (int64_t(m) * kb + int64_t(ks) * kBlocksPerStage + b) * 36);
-#pragma unroll
-            for (int j = 0; j < 9; j++) w[j] = src[j];
-        } else {
-#pragma unroll
-            for (int j = 0; j < 9; j++) w[j] = 0;
-        }
-        *reinterpret_cast<uint4 *>(smem + ((b * 2 + 0) * kTileM + row) * 16) = make_uint4(w[1], w[2], w[3], w[4]);
-        *reinterpret_cast<uint4 *>(smem + ((b * 2 + 1) * kTileM + row) * 16) = make_uint4(w[5], w[6], w[7], w[8]);
-        sXd[b * kTileM + row] = h2f(w[0]);
-        if constexpr (FMT == FMT_Q4_K) {
-            unsigned short *sSum = reinterpret_cast<unsigned short *>(smem + L::OFF_A_SUM);
-            sSum[row * 8 + b] = (unsigned short)(w[0] >> 16);
-        }
-    }
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// A raw buffer over the rows of one tile: reads past `bytes` return zero in
+// hardware, which is how rows beyond M or N are zero-filled (codes 0,
+// scales 0: they add nothing and are never stored) without a single VALU
+// instruction.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base, int64_t bytes) {
+    const int n = bytes > 0x7fffffffLL ? 0x7fffffff : int(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, n, 0x00020000);
 }
 
-// Stage Q8_0: unit u -> (row = u/4, block pair p = u%4).  A pair of 34-byte
-// blocks is 68 bytes = 17 dwords starting on a 4-byte boundary (K % 256 == 0
-// makes every row an even number of blocks); the even block's codes sit two
-// bytes off the dword grid and are realigned with v_alignbyte.
-__device__ __forceinline__ void stage_q8_0(const uint8_t *__restrict__ wq, uint8_t *smem, int N,
-                                           int kb, int n0, int ks, int tid) {
-    using L = Lds<FMT_Q8_0>;
-    uint8_t *sB = smem + L::OFF_B_CODES;
-    float *sWd = reinterpret_cast<float *>(smem + L::OFF_B_SCALE);
+// Staging is split into a load half (global memory -> registers, issued one
+// k-step ahead so that its latency hides behind the current step's MFMAs)
+// and a store half (registers -> LDS after the step's barrier).
+
+// Activations: unit u -> (row = u/4, block = u%4): four consecutive threads
+// read one row's 144 contiguous bytes of this step.
+struct ActRegs {
+    uint32_t w0[2];
+    u32x4 lo[2], hi[2];
+};
+
+__device__ __forceinline__ void load_activations(__amdgpu_buffer_rsrc_t rx, int kb, int ks, int tid,
+                                                 ActRegs &r) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int u = tid + kThreads * i;
-        const int row = u >> 2, p = u & 3;
-        const int n = n0 + row;
-        uint32_t w[17];
-        if (n < N) {
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(
-                wq + (int64_t(n) * kb + int64_t(ks) * kBlocksPerStage + 2 * p) * 34);
+        const int row = u >> 2, b = u & 3;
+        const int off = (row * kb + ks * KB + b) * 36;
+        r.w0[i] = __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0);
+        r.lo[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 4, 0, 0);
+        r.hi[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 20, 0, 0);
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void store_activations(const ActRegs &r, uint8_t *smem, int ks, int tid) {
+    using L = Lds<FMT>;
+    unsigned short *sXh = reinterpret_cast<unsigned short *>(smem + L::OFF_A_SCALE);
 #pragma unroll
-            for (int j = 0; j < 17; j++) w[j] = src[j];
-        } else {
-#pragma unroll
-            for (int j = 0; j < 17; j++) w[j] = 0;
+    for (int i = 0; i < 2; i++) {
+        const int u = tid + kThreads * i;
+        const int row = u >> 2, b = u & 3;
+        *reinterpret_cast<u32x4 *>(smem + chunk_off(row, 2 * b)) = r.lo[i];
+        *reinterpret_cast<u32x4 *>(smem + chunk_off(row, 2 * b + 1)) = r.hi[i];
+        sXh[b * kPlaneH + xs_pos(row)] = (unsigned short)(r.w0[i] & 0xffffu);
+        if constexpr (FMT == FMT_Q4_K) {
+            unsigned short *sSum = reinterpret_cast<unsigned short *>(smem + L::OFF_A_SUM);
+            sSum[row * 8 + (ks & 1) * KB + b] = (unsigned short)(r.w0[i] >> 16);   // sub-block of its super-block
         }
-        uint32_t c[8];
+    }
+}
+
+// Q8_0: thread -> (row = tid/2, block pair p = tid%2).  A pair of 34-byte
+// blocks is 68 bytes = 17 dwords starting on a 4-byte boundary (K % 256 == 0
+// makes every row an even number of blocks); the even block's codes sit two
+// bytes off the dword grid and are realigned with v_alignbyte.
+struct Q80Regs {
+    u32x4 v[4];
+    uint32_t last;
+};
+
+__device__ __forceinline__ void load_q8_0(__amdgpu_buffer_rsrc_t rw, int kb, int ks, int tid, Q80Regs &r) {
+    const int row = tid >> 1, p = tid & 1;
+    const int off = (row * kb + ks * KB + 2 * p) * 34;
 #pragma unroll
-        for (int j = 0; j < 8; j++) c[j] = __builtin_amdgcn_alignbyte(w[j + 1], w[j], 2);
-        const int b0 = 2 * p, b1 = 2 * p + 1;
-        *reinterpret_cast<uint4 *>(sB + ((b0 * 2 + 0) * kTileN + row) * 16) = make_uint4(c[0], c[1], c[2], c[3]);
-        *reinterpret_cast<uint4 *>(sB + ((b0 * 2 + 1) * kTileN + row) * 16) = make_uint4(c[4], c[5], c[6], c[7]);
-        *reinterpret_cast<uint4 *>(sB + ((b1 * 2 + 0) * kTileN + row) * 16) = make_uint4(w[9], w[10], w[11], w[12]);
-        *reinterpret_cast<uint4 *>(sB + ((b1 * 2 + 1) * kTileN + row) * 16) = make_uint4(w[13], w[14], w[15], w[16]);
-        sWd[b0 * kTileN + row] = h2f(w[0]);
-        sWd[b1 * kTileN + row] = h2f(w[8] >> 16);
-    }
+    for (int q = 0; q < 4; q++) r.v[q] = __builtin_amdgcn_raw_buffer_load_b128(rw, off + 16 * q, 0, 0);
+    r.last = __builtin_amdgcn_raw_buffer_load_b32(rw, off + 64, 0, 0);
 }
 
-// Sub-block j (0..7) 6-bit scale and min from the 12 packed bytes (GGUF
-// K-quant packing): j < 4 uses the low six bits of bytes j and j+4; j >= 4
-// takes its low four bits from byte j+4 and its top two from the spare top
-// bits of bytes j-4 (scale) and j (min).
-__device__ __forceinline__ void q4k_scale_min(const uint8_t *s, int j, int &sc, int &mn) {
-    if (j < 4) {
-        sc = s[j] & 63;
-        mn = s[j + 4] & 63;
+__device__ __forceinline__ void store_q8_0(const Q80Regs &r, uint8_t *smem, int tid) {
+    using L = Lds<FMT_Q8_0>;
+    uint8_t *sB = smem + L::OFF_B_CODES;
+    float *sWd = reinterpret_cast<float *>(smem + L::OFF_B_SCALE);
+    const int row = tid >> 1, p = tid & 1;
+    const uint32_t w[17] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w, r.v[1].x, r.v[1].y,
+                            r.v[1].z, r.v[1].w, r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w,
+                            r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w, r.last};
+    u32x4 c0, c1;
+    c0.x = __builtin_amdgcn_alignbyte(w[1], w[0], 2);
+    c0.y = __builtin_amdgcn_alignbyte(w[2], w[1], 2);
+    c0.z = __builtin_amdgcn_alignbyte(w[3], w[2], 2);
+    c0.w = __builtin_amdgcn_alignbyte(w[4], w[3], 2);
+    c1.x = __builtin_amdgcn_alignbyte(w[5], w[4], 2);
+    c1.y = __builtin_amdgcn_alignbyte(w[6], w[5], 2);
+    c1.z = __builtin_amdgcn_alignbyte(w[7], w[6], 2);
+    c1.w = __builtin_amdgcn_alignbyte(w[8], w[7], 2);
+    *reinterpret_cast<u32x4 *>(sB + chunk_off(row, 4 * p + 0)) = c0;
+    *reinterpret_cast<u32x4 *>(sB + chunk_off(row, 4 * p + 1)) = c1;
+    *reinterpret_cast<u32x4 *>(sB + chunk_off(row, 4 * p + 2)) = u32x4{w[9], w[10], w[11], w[12]};
+    *reinterpret_cast<u32x4 *>(sB + chunk_off(row, 4 * p + 3)) = u32x4{w[13], w[14], w[15], w[16]};
+    sWd[(2 * p) * kPlane + row] = h2f(w[0]);
+    sWd[(2 * p + 1) * kPlane + row] = h2f(w[8] >> 16);
+}
+
+// Byte k (0..11) of the packed scale/min field held in three dwords.
+template <int k>
+__device__ __forceinline__ uint32_t sbyte(const u32x4 &h) {
+    const uint32_t w = k < 4 ? h.y : (k < 8 ? h.z : h.w);
+    return (w >> (8 * (k & 3))) & 0xffu;
+}
+
+// Sub-block J (0..7) of a Q4_K super-block: 6-bit scale and min from the 12
+// packed bytes (GGUF K-quant packing).  J < 4 uses the low six bits of bytes J
+// and J+4; J >= 4 takes its low four bits from byte J+4 (scale: low nibble,
+// min: high nibble) and its top two bits from the spare top bits of bytes J-4
+// (scale) and J (min).  Writes d*sc_J and -dmin*m_J split into fp16 high and
+// low parts.
+template <int J>
+__device__ __forceinline__ void q4k_subblock(const u32x4 &h, float d, float dmin, int row, float *sWd,
+                                             _Float16 *sMin) {
+    uint32_t sc, mn;
+    if constexpr (J < 4) {
+        sc = sbyte<J>(h) & 63u;
+        mn = sbyte<J + 4>(h) & 63u;
     } else {
-        sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
-        mn = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+        sc = (sbyte<J + 4>(h) & 15u) | ((sbyte<J - 4>(h) >> 6) << 4);
+        mn = (sbyte<J + 4>(h) >> 4) | ((sbyte<J>(h) >> 6) << 4);
     }
+    sWd[J * kPlane + row] = d * (float)sc;                 // exact: 11 x 6 bits
+    const float neg = -(dmin * (float)mn);                  // exact
+    const _Float16 hi = (_Float16)neg;
+    const _Float16 lo = (_Float16)(neg - (float)hi);        // exact remainder
+    sMin[(row * 2 + 0) * 8 + J] = hi;
+    sMin[(row * 2 + 1) * 8 + J] = lo;
 }
 
-// Stage Q4_K super-block `ks` for the tile's 128 columns: 9 units of 16 bytes
-// per row (one header, eight code chunks), consecutive threads on consecutive
-// 16-byte chunks.  The codes stay packed (two 4-bit codes per byte) in LDS;
-// the header is decoded once here into d*sc_j and the split min operand.
-__device__ __forceinline__ void stage_q4_K(const uint8_t *__restrict__ wq, uint8_t *smem, int N,
-                                           int nsb, int n0, int ks, int tid) {
+// Q4_K, half `ks & 1` of super-block `ks / 2`, for the tile's 128 columns.
+// Unit u -> (row = u/4, packed chunk c = 4*half + u%4): the 16 code bytes
+// 16c..16c+15 belong to 32-byte group c/2 and k-half c%2; their low nibbles
+// are codes of sub-block 2*(c/2), their high nibbles of sub-block 2*(c/2)+1
+// (the layout reading in the header).  They are unpacked at store time, once
+// per workgroup, into the same one-code-per-byte layout as Q8_0, so the MFMA
+// loop reads both formats alike.  At the first half the header is decoded
+// too: waves 0-1 turn sub-blocks 0..3 of row tid%128 into d*sc_j and the
+// split min operand, waves 2-3 sub-blocks 4..7 (a wave-uniform branch; every
+// sub-block index a compile-time constant).
+struct Q4KRegs {
+    u32x4 v[2];
+    u32x4 h;
+};
+
+__device__ __forceinline__ void load_q4_K(__amdgpu_buffer_rsrc_t rw, int nsb, int ks, int tid, Q4KRegs &r) {
+    const int sb = ks >> 1, half = ks & 1;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int u = tid + kThreads * i;
+        const int row = u >> 2, c = 4 * half + (u & 3);
+        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (row * nsb + sb) * 144 + 16 + 16 * c, 0, 0);
+    }
+    if (half == 0)
+        r.h = __builtin_amdgcn_raw_buffer_load_b128(rw, ((tid & (kTileN - 1)) * nsb + sb) * 144, 0, 0);
+}
+
+__device__ __forceinline__ void store_q4_K(const Q4KRegs &r, uint8_t *smem, int ks, int tid) {
     using L = Lds<FMT_Q4_K>;
     uint8_t *sB = smem + L::OFF_B_CODES;
     float *sWd = reinterpret_cast<float *>(smem + L::OFF_B_SCALE);
     _Float16 *sMin = reinterpret_cast<_Float16 *>(smem + L::OFF_B_MIN);
-    for (int u = tid; u < kTileN * 9; u += kThreads) {
-        const int row = u / 9, part = u - 9 * (u / 9);
-        const int n = n0 + row;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (n < N)
-            v = reinterpret_cast<const uint4 *>(wq + (int64_t(n) * nsb + ks) * 144)[part];
-        if (part == 0) {
-            const float d = h2f(v.x), dmin = h2f(v.x >> 16);
-            uint8_t s[12];
-            const uint32_t sw[3] = {v.y, v.z, v.w};
 #pragma unroll
-            for (int j = 0; j < 12; j++) s[j] = uint8_t(sw[j >> 2] >> (8 * (j & 3)));
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                int sc, mn;
-                q4k_scale_min(s, j, sc, mn);
-                sWd[j * kTileN + row] = d * (float)sc;               // exact: 11 x 6 bits
-                const float neg = -(dmin * (float)mn);               // exact
-                const _Float16 hi = (_Float16)neg;
-                const _Float16 lo = (_Float16)(neg - (float)hi);     // exact remainder
-                sMin[(row * 2 + 0) * 8 + j] = hi;
-                sMin[(row * 2 + 1) * 8 + j] = lo;
-            }
+    for (int i = 0; i < 2; i++) {
+        const int u = tid + kThreads * i;
+        const int row = u >> 2, cl = u & 3;          // cl: chunk within this half
+        const u32x4 lo = r.v[i] & 0x0F0F0F0Fu;
+        const u32x4 hi = (r.v[i] >> 4) & 0x0F0F0F0Fu;
+        // sub-blocks 2*(c/2) and 2*(c/2)+1 are blocks 2*(cl/2) and 2*(cl/2)+1 of this step
+        const int gl = cl >> 1, kh = cl & 1;
+        *reinterpret_cast<u32x4 *>(sB + chunk_off(row, 4 * gl + kh)) = lo;
+        *reinterpret_cast<u32x4 *>(sB + chunk_off(row, 4 * gl + 2 + kh)) = hi;
+    }
+    if ((ks & 1) == 0) {
+        const int row = tid & (kTileN - 1);
+        const float d = h2f(r.h.x), dmin = h2f(r.h.x >> 16);
+        if (tid < kTileN) {
+            q4k_subblock<0>(r.h, d, dmin, row, sWd, sMin);
+            q4k_subblock<1>(r.h, d, dmin, row, sWd, sMin);
+            q4k_subblock<2>(r.h, d, dmin, row, sWd, sMin);
+            q4k_subblock<3>(r.h, d, dmin, row, sWd, sMin);
         } else {
-            const int c = part - 1;                  // code bytes 16c .. 16c+15
-            const int grp = c >> 1, half = c & 1;    // 32-byte group, k-half within it
-            *reinterpret_cast<uint4 *>(sB + ((grp * 2 + half) * kTileN + row) * 16) = v;
+            q4k_subblock<4>(r.h, d, dmin, row, sWd, sMin);
+            q4k_subblock<5>(r.h, d, dmin, row, sWd, sMin);
+            q4k_subblock<6>(r.h, d, dmin, row, sWd, sMin);
+            q4k_subblock<7>(r.h, d, dmin, row, sWd, sMin);
         }
     }
 }
 
+template <int FMT>
+struct WRegs;
+template <>
+struct WRegs<FMT_Q8_0> { Q80Regs r; };
+template <>
+struct WRegs<FMT_Q4_K> { Q4KRegs r; };
+
 template <int FMT, bool DOTS>
-__global__ __launch_bounds__(kThreads) void k_mmq(const uint8_t *__restrict__ xq,
-                                                  const uint8_t *__restrict__ wq,
-                                                  void *__restrict__ outp, int M, int N, int K) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DOTS ? 1 : (FMT == FMT_Q8_0 ? 2 : 3))))
+void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void *__restrict__ outp,
+           int M, int N, int K) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using L = Lds<FMT>;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     const int n0 = blockIdx.x * kTileN, m0 = blockIdx.y * kTileM;
-    const int kb = K >> 5, nsteps = K >> 8;
+    const int kb = K >> 5, nsteps = kb / KB;
 
-    const float *sXd = reinterpret_cast<const float *>(smem + L::OFF_A_SCALE);
+    const _Float16 *sXh = reinterpret_cast<const _Float16 *>(smem + L::OFF_A_SCALE);
     const uint8_t *sB = smem + L::OFF_B_CODES;
     const float *sWd = reinterpret_cast<const float *>(smem + L::OFF_B_SCALE);
+
+    // Buffers over this tile's rows of x and w (reads past M / N return 0).
+    const int64_t xrow = int64_t(kb) * 36;
+    const int64_t wrow = FMT == FMT_Q8_0 ? int64_t(kb) * 34 : int64_t(K >> 8) * 144;
+    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq + int64_t(m0) * xrow, int64_t(M - m0) * xrow);
+    const __amdgpu_buffer_rsrc_t rw = tile_rsrc(wq + int64_t(n0) * wrow, int64_t(N - n0) * wrow);
+
+    const int a_row = (32 * wv + l32) * kRowBytes;   // this lane's A row (fragment row l32 of wave wv)
+    const int b_row = l32 * kRowBytes;                // this lane's B column within a 32-column sub-tile
 
     i32x16 srcC;
 #pragma unroll
@@ -289,66 +399,88 @@ __global__ __launch_bounds__(kThreads) void k_mmq(const uint8_t *__restrict__ xq
 #pragma unroll
         for (int r = 0; r < 16; r++) acc[c][r] = 0.0f;
 
-    for (int ks = 0; ks < nsteps; ks++) {
-        stage_activations<FMT>(xq, smem, M, kb, m0, ks, tid);
+    // Q8_0 software-pipelines its staging (the registers hold step ks+1 while
+    // step ks computes); Q4_K, held to 168 VGPRs for three waves per SIMD,
+    // has no room for the prefetch registers and loads each step just before
+    // storing it.
+    constexpr bool kPrefetch = FMT == FMT_Q8_0;
+    ActRegs ar;
+    WRegs<FMT> wr;
+    auto load_step = [&](int k) {
+        load_activations(rx, kb, k, tid, ar);
         if constexpr (FMT == FMT_Q8_0)
-            stage_q8_0(wq, smem, N, kb, n0, ks, tid);
+            load_q8_0(rw, kb, k, tid, wr.r);
         else
-            stage_q4_K(wq, smem, N, K >> 8, n0, ks, tid);
-        __syncthreads();
+            load_q4_K(rw, K >> 8, k, tid, wr.r);
+    };
+    if constexpr (kPrefetch) load_step(0);
 
+    for (int ks = 0; ks < nsteps; ks++) {
+        if constexpr (!kPrefetch) load_step(ks);
+        store_activations<FMT>(ar, smem, ks, tid);
+        if constexpr (FMT == FMT_Q8_0)
+            store_q8_0(wr.r, smem, tid);
+        else
+            store_q4_K(wr.r, smem, ks, tid);
+        __syncthreads();
+        if (kPrefetch && ks + 1 < nsteps) load_step(ks + 1);
+
+        // Q4_K weight-scale planes hold the whole super-block: this step's
+        // blocks are sub-blocks 4*(ks&1) .. 4*(ks&1)+3
+        const int wplane = FMT == FMT_Q8_0 ? 0 : (ks & 1) * KB;
 #pragma unroll
-        for (int b = 0; b < kBlocksPerStage; b++) {
-            const i32x4 a = *reinterpret_cast<const i32x4 *>(smem + ((b * 2 + g) * kTileM + 32 * wv + l32) * 16);
-            float xs[16];
+        for (int b = 0; b < KB; b++) {
+            // swizzled chunk of (block b, k-half g) for this lane's rows and
+            // columns: all of them are == l32 (mod 8)
+            const int sw = ((2 * b + g) ^ (l32 & 7)) << 4;
+            const i32x4 a = *reinterpret_cast<const i32x4 *>(smem + a_row + sw);
+            f16x8 xs0, xs1;   // activation scales of this lane's 16 accumulator rows
             if constexpr (!DOTS) {
-#pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const float4 t4 = *reinterpret_cast<const float4 *>(sXd + b * kTileM + 32 * wv + 8 * q + 4 * g);
-                    xs[4 * q + 0] = t4.x;
-                    xs[4 * q + 1] = t4.y;
-                    xs[4 * q + 2] = t4.z;
-                    xs[4 * q + 3] = t4.w;
-                }
+                xs0 = *reinterpret_cast<const f16x8 *>(sXh + b * kPlaneH + 32 * wv + 16 * g);
+                xs1 = *reinterpret_cast<const f16x8 *>(sXh + b * kPlaneH + 32 * wv + 16 * g + 8);
             }
 #pragma unroll
             for (int c = 0; c < 4; c++) {
-                i32x4 bq;
-                if constexpr (FMT == FMT_Q8_0) {
-                    bq = *reinterpret_cast<const i32x4 *>(sB + ((b * 2 + g) * kTileN + 32 * c + l32) * 16);
-                } else {
-                    const i32x4 raw = *reinterpret_cast<const i32x4 *>(sB + (((b >> 1) * 2 + g) * kTileN + 32 * c + l32) * 16);
-                    bq = (b & 1) ? ((raw >> 4) & 0x0F0F0F0F) : (raw & 0x0F0F0F0F);
-                }
+                const int col = 32 * c + l32;
+                const i32x4 bq = *reinterpret_cast<const i32x4 *>(sB + b_row + sw + c * 32 * kRowBytes);
                 const i32x16 D = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bq, srcC, 0, 0, 0);
                 if constexpr (DOTS) {
                     int32_t *dots = reinterpret_cast<int32_t *>(outp);
-                    const int n = n0 + 32 * c + l32;
+                    const int n = n0 + col;
 #pragma unroll
                     for (int r = 0; r < 16; r++) {
                         const int m = m0 + 32 * wv + 8 * (r >> 2) + 4 * g + (r & 3);
                         if (m < M && n < N)
-                            dots[(int64_t(m) * N + n) * kb + int64_t(ks) * kBlocksPerStage + b] = D[r];
+                            dots[(int64_t(m) * N + n) * kb + int64_t(ks) * KB + b] = D[r];
                     }
                 } else {
-                    const float ws = sWd[b * kTileN + 32 * c + l32];
+                    const float ws = sWd[(wplane + b) * kPlane + col];
                     const float cs = -kMagic * ws;   // exact
 #pragma unroll
                     for (int r = 0; r < 16; r++) {
                         const float t = __builtin_fmaf(__int_as_float(D[r]), ws, cs);
-                        acc[c][r] = __builtin_fmaf(xs[r], t, acc[c][r]);
+                        const float xr = (float)(r < 8 ? xs0[r & 7] : xs1[r & 7]);   // exact widening
+                        acc[c][r] = __builtin_fmaf(xr, t, acc[c][r]);
                     }
                 }
+                // One MFMA result in flight per wave: the matrix core and the
+                // VALU do not overlap within a SIMD here, so the other waves
+                // of the SIMD hide this wave's MFMA latency, and the register
+                // budget allows three (Q4_K) or four (Q8_0) waves per SIMD.
+                // Only LDS reads may be hoisted across.
+                __builtin_amdgcn_sched_barrier(0x0100);
             }
         }
         if constexpr (FMT == FMT_Q4_K && !DOTS) {
-            const unsigned short *sSum = reinterpret_cast<const unsigned short *>(smem + L::OFF_A_SUM);
-            const _Float16 *sMin = reinterpret_cast<const _Float16 *>(smem + L::OFF_B_MIN);
-            const f16x8 sa = *reinterpret_cast<const f16x8 *>(sSum + (32 * wv + l32) * 8);
+            if (ks & 1) {   // end of a super-block: its min term
+                const unsigned short *sSum = reinterpret_cast<const unsigned short *>(smem + L::OFF_A_SUM);
+                const _Float16 *sMin = reinterpret_cast<const _Float16 *>(smem + L::OFF_B_MIN);
+                const f16x8 sa = *reinterpret_cast<const f16x8 *>(sSum + (32 * wv + l32) * 8);
 #pragma unroll
-            for (int c = 0; c < 4; c++) {
-                const f16x8 mb = *reinterpret_cast<const f16x8 *>(sMin + ((32 * c + l32) * 2 + g) * 8);
-                acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa, mb, acc[c], 0, 0, 0);
+                for (int c = 0; c < 4; c++) {
+                    const f16x8 mb = *reinterpret_cast<const f16x8 *>(sMin + ((32 * c + l32) * 2 + g) * 8);
+                    acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa, mb, acc[c], 0, 0, 0);
+                }
             }
         }
         __syncthreads();

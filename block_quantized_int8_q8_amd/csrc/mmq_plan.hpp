@@ -19,20 +19,19 @@ enum Fmt : int { FMT_Q8_0 = 0, FMT_Q4_K = 1 };
 constexpr int kTileM = 128;        // output rows per workgroup
 constexpr int kTileN = 128;        // output columns per workgroup
 constexpr int kThreads = 256;      // four wave64s; wave w owns rows 32w..32w+31
-constexpr int kBlocksPerStage = 8; // 32-blocks staged per k-step (one Q4_K super-block)
+constexpr int kBlocksPerStage = 4; // 32-blocks staged per k-step (half a Q4_K super-block)
 
-// LDS layout sizes in bytes for one k-step (see the kernel for the layouts).
+// LDS bytes of one k-step for the kernel's layouts: codes row-major (32 B
+// per block per row, swizzled, no padding), activation scales fp16 in
+// 272-byte planes, weight scales fp32 in planes of 132 floats (Q4_K keeps the
+// eight planes of a whole super-block).
 constexpr int64_t lds_bytes_for(int fmt) {
-    // activation codes [8][2][128][16] + activation scales [8][128] fp32
-    int64_t a = int64_t(kBlocksPerStage) * 2 * kTileM * 16 + int64_t(kBlocksPerStage) * kTileM * 4;
-    if (fmt == FMT_Q8_0) {
-        // weight codes [8][2][128][16] + weight scales [8][128] fp32
-        return a + int64_t(kBlocksPerStage) * 2 * kTileN * 16 + int64_t(kBlocksPerStage) * kTileN * 4;
-    }
-    // Q4_K: packed codes [4][2][128][16] + d*sc [8][128] fp32
-    //       + min-term operand [128][2][8] fp16 + activation sums [128][8] fp16
-    return a + int64_t(4) * 2 * kTileN * 16 + int64_t(kBlocksPerStage) * kTileN * 4 +
-           int64_t(kTileN) * 2 * 8 * 2 + int64_t(kTileM) * 8 * 2;
+    const int64_t codes = int64_t(kTileM + kTileN) * 32 * kBlocksPerStage;
+    const int64_t ascale = int64_t(kBlocksPerStage) * 272;
+    if (fmt == FMT_Q8_0) return codes + ascale + int64_t(kBlocksPerStage) * 132 * 4;
+    // Q4_K: eight weight-scale planes, the split min operand [col][2][8] fp16
+    // and the activation block sums [row][8] fp16
+    return codes + ascale + int64_t(8) * 132 * 4 + int64_t(kTileN) * 2 * 8 * 2 + int64_t(kTileM) * 8 * 2;
 }
 
 struct Plan {
@@ -66,7 +65,9 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
     if (K % 256 != 0)
         return fail(fmt == FMT_Q4_K ? "K must be a multiple of 256 (whole Q4_K super-blocks)"
                                     : "K must be a multiple of 256 (whole 8-block k-steps)");
-    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail("M, N and K must fit in int32");
+    if (M > INT32_MAX || N > INT32_MAX) return fail("M and N must fit in int32");
+    // byte offsets inside one 128-row tile are 32-bit buffer offsets
+    if (K > (int64_t(1) << 23)) return fail("K must be at most 8388608 (32-bit offsets within a tile)");
     // Every byte offset the kernels form must fit in int64 comfortably.
     if (M > (int64_t(1) << 50) / N || M > (int64_t(1) << 45) / (K / 32))
         return fail("problem too large for 64-bit offsets");

@@ -76,6 +76,7 @@ def test_extra_lds_hook_forces_refusal():
     (mmq.FMT_Q8_0, 64, 256, 0, ">= 1"),
     (7, 64, 256, 512, "format"),
     (mmq.FMT_Q8_0, 1 << 31, 256, 512, "int32"),
+    (mmq.FMT_Q8_0, 64, 256, 1 << 24, "at most"),
     (mmq.FMT_Q8_0, (65536 * 128), 256, 512, "row tiles"),
 ])
 def test_guard_refuses_bad_shapes(fmt, M, N, K, needle):
