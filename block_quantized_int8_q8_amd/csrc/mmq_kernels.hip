@@ -84,12 +84,15 @@ __global__ __launch_bounds__(256) void k_quantize_q8_1(const float *__restrict__
 // ---------------------------------------------------------------------------
 // MMQ kernel.
 //
-// Workgroup: 256 threads (4 wave64s) compute a 128 x 128 output tile; wave w
-// owns rows 32w..32w+31 and all 128 columns as four 32x32 sub-tiles.  Each
-// k-step stages 4 consecutive 32-blocks (half a Q4_K super-block) into LDS;
-// a step's LDS (36-44 KiB) lets three or four workgroups share a CU, so that
-// every SIMD has several waves to switch between while one waits on LDS,
-// the matrix core or a barrier.
+// Workgroup: 512 threads (8 wave64s) compute a 128 x 128 output tile as a
+// 4 x 2 grid of 32 x 64 wave tiles; each wave holds two 32 x 32 sub-tiles.
+// Each k-step covers 4 consecutive 32-blocks (half a Q4_K super-block).
+// LDS holds two k-steps: while the waves compute step ks from one buffer,
+// step ks+1 is brought into the other (activations by DMA, weights through
+// registers), so a step costs one barrier.  The kernel is held to 128
+// VGPRs so that two workgroups -- four waves per SIMD -- share a CU: the
+// per-block scale epilogue is VALU work that only other waves can overlap
+// with a wave's MFMA and LDS latency.
 //
 // Matrix core: v_mfma_i32_32x32x32_i8 takes exactly one 32-block as its K,
 // so every MFMA result is one exact block dot I (the block-boundary rule of
@@ -106,71 +109,110 @@ __global__ __launch_bounds__(256) void k_quantize_q8_1(const float *__restrict__
 //         one value per lane: its column's scale; the product 1.5*2^23*ws is
 //         exact, so t is the singly-rounded ws*I)
 //   acc = fma(xs, t, acc)                                 (xs = activation
-//         scale of the element's row, fp16 widened exactly inside the FMA)
+//         scale of the element's row)
 // For Q8_0 this is the same arithmetic, in the same block order, as the
 // oracle, so the output is bit-identical.
 //
 // Q4_K ("When Does a Kernel Win Surface?", 6.2): ws = d*sc_j (exact in fp32);
 // the packed 4-bit codes are unpacked once per workgroup while staging (low
 // nibbles = even sub-block, high nibbles = odd sub-block of a 32-byte
-// group); and the min term  -sum_j dmin*m_j * s_j  of a whole super-block is
-// added by one fp16 MFMA per 32x32 sub-tile that accumulates straight into
-// the fp32 accumulator: A = the eight activation block sums s_j (fp16, as
-// stored), B = -dmin*m_j split exactly into an fp16 high and low part
-// (k = 0..7 high parts, k = 8..15 low parts, each multiplied by the same s_j).
+// group); and the min term  -sum_j dmin*m_j * s_j  of the step's four
+// sub-blocks is added by one fp16 MFMA per 32x32 sub-tile that accumulates
+// straight into the fp32 accumulator: A = the four activation block sums s_j
+// (fp16, as stored), B = -dmin*m_j split exactly into an fp16 high and low
+// part (k = 0..3 high parts, k = 4..7 low parts, each against the same s_j).
 // ---------------------------------------------------------------------------
 constexpr uint32_t kMagicBits = 0x4B400000u;   // 12582912.0f
 constexpr float kMagic = 12582912.0f;
 constexpr int KB = kBlocksPerStage;            // 32-blocks per k-step
 
-// LDS layouts.  Codes (activations, and weights of either format once
-// unpacked to one int8 code per byte) are row-major, 128 bytes per row = 8
-// chunks of 16 bytes (block b of the step, k-half g -> chunk 2b+g), with the
-// chunk index XOR-swizzled by row%8.  A fragment read (32 consecutive rows,
-// one chunk) then touches eight distinct 16-byte bank groups per 8-lane
+// LDS layout of one k-step buffer.  Codes (activations, and weights of either
+// format once unpacked to one int8 code per byte) are row-major, 128 bytes per
+// row = 8 chunks of 16 bytes (block b of the step, k-half g -> chunk 2b+g),
+// with the chunk index XOR-swizzled by row%8: a fragment read (32 consecutive
+// rows, one chunk) touches eight distinct 16-byte bank groups per 8-lane
 // phase, and staging writes are at worst 2-way conflicted, with no padding.
 //
-// Activation scales stay fp16 as stored in q8_1 and are consumed by
-// v_fma_mix_f32 (exact widening inside the FMA).  They are kept per block in
-// accumulator-fragment order: within each 32-row group, lane half g needs the
-// scales of rows 8q + 4g + i (q, i = 0..3) for its registers r = 4q + i, so
-// position 16g + 4q + i holds row 8q + 4g + i and a lane reads its 16 scales
-// as two contiguous 16-byte words.  Planes are 272 bytes apart (16-byte
-// aligned, 4 banks apart).  Weight scales are fp32 [block][column] planes of
-// 132 floats (staging writes of one column's blocks land on distinct banks);
-// Q4_K keeps all eight planes of a super-block, written at its first step.
+// Activation block headers (fp16 d and s) are copied as they are, [row][block]
+// as one dword each; a lane widens the one activation scale it needs per block
+// itself.  Weight scales are widened to fp32 at staging (v_fma_mix_f32, which
+// would take the fp16 form in the FMA, issues at half the rate of v_fmac_f32
+// on gfx950) and stored [block][column] in planes of 132 floats.
+//
+// An output register r of lane l needs the scale of row 8(r/4) + 4(l/32) +
+// r%4, so a lane needs 16 different row scales per block.  Instead of
+// reading them from LDS (4 KiB per wave and block) each lane reads one:
+// lane l holds the scale of row 8(k/4) + k%4 + 4(l/32), k = l%16, and the
+// DPP broadcast row_newbcast:r (every lane of a 16-lane row takes lane r of
+// that row) hands each lane the scale of its register r inside the FMA
+// itself (v_fmac_f32 with a DPP source): lanes 0-31 see rows with l/32 = 0
+// and lanes 32-63 rows with l/32 = 1, as needed.
 constexpr int kRowBytes = KB * 32;   // codes per row per step
-constexpr int kPlaneH = 136;         // halves per activation-scale plane
 constexpr int kPlane = 132;          // floats per weight-scale plane
+constexpr int kWavesN = 2;           // wave grid: 4 along rows x 2 along columns
+constexpr int kWaveN = kTileN / kWavesN;
+constexpr int kNSub = kWaveN / 32;   // 32-column sub-tiles per wave
 
 __device__ __forceinline__ int chunk_off(int row, int j) { return row * kRowBytes + ((j ^ (row & 7)) << 4); }
-__device__ __forceinline__ int xs_pos(int row) {
-    return (row & ~31) + (((row >> 2) & 1) << 4) + (((row >> 3) & 3) << 2) + (row & 3);
+
+// acc[R0+i] += (xsv of lane R0+i of this lane's 16-lane row) * t[R0+i], i =
+// 0..7, as v_fmac_f32_dpp row_newbcast (the compiler does not fold a
+// row_newbcast move into an FMA by itself).  DPP reads a VGPR at least two
+// wait states after a VALU write to it: the leading s_nop covers the VALU
+// instructions just before the block (the t values), and nothing inside the
+// block writes a register that a later DPP instruction of the block reads.
+#define MMQ_FMAC_BCAST(R, A, T) "v_fmac_f32_dpp %" #A ", %16, %" #T " row_newbcast:" #R " row_mask:0xf bank_mask:0xf\n"
+template <int R0>
+__device__ __forceinline__ void fmac_row_bcast8(f32x16 &acc, const f32x16 &t, float xsv) {
+    float a0 = acc[R0 + 0], a1 = acc[R0 + 1], a2 = acc[R0 + 2], a3 = acc[R0 + 3];
+    float a4 = acc[R0 + 4], a5 = acc[R0 + 5], a6 = acc[R0 + 6], a7 = acc[R0 + 7];
+    if constexpr (R0 == 0) {
+        asm volatile("s_nop 1\n"
+                     MMQ_FMAC_BCAST(0, 0, 8) MMQ_FMAC_BCAST(1, 1, 9) MMQ_FMAC_BCAST(2, 2, 10)
+                     MMQ_FMAC_BCAST(3, 3, 11) MMQ_FMAC_BCAST(4, 4, 12) MMQ_FMAC_BCAST(5, 5, 13)
+                     MMQ_FMAC_BCAST(6, 6, 14) MMQ_FMAC_BCAST(7, 7, 15)
+                     : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5), "+v"(a6), "+v"(a7)
+                     : "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]), "v"(t[4]), "v"(t[5]), "v"(t[6]),
+                       "v"(t[7]), "v"(xsv));
+    } else {
+        asm volatile("s_nop 1\n"
+                     MMQ_FMAC_BCAST(8, 0, 8) MMQ_FMAC_BCAST(9, 1, 9) MMQ_FMAC_BCAST(10, 2, 10)
+                     MMQ_FMAC_BCAST(11, 3, 11) MMQ_FMAC_BCAST(12, 4, 12) MMQ_FMAC_BCAST(13, 5, 13)
+                     MMQ_FMAC_BCAST(14, 6, 14) MMQ_FMAC_BCAST(15, 7, 15)
+                     : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5), "+v"(a6), "+v"(a7)
+                     : "v"(t[8]), "v"(t[9]), "v"(t[10]), "v"(t[11]), "v"(t[12]), "v"(t[13]), "v"(t[14]),
+                       "v"(t[15]), "v"(xsv));
+    }
+    acc[R0 + 0] = a0; acc[R0 + 1] = a1; acc[R0 + 2] = a2; acc[R0 + 3] = a3;
+    acc[R0 + 4] = a4; acc[R0 + 5] = a5; acc[R0 + 6] = a6; acc[R0 + 7] = a7;
 }
+#undef MMQ_FMAC_BCAST
 
 template <int FMT>
 struct Lds {
     static constexpr int A_CODES = kTileM * kRowBytes;
-    static constexpr int A_SCALE = KB * kPlaneH * 2;
+    static constexpr int A_HDR = kTileM * KB * 4;                               // [row][4] (d, s) fp16 pairs
     static constexpr int B_CODES = kTileN * kRowBytes;
-    static constexpr int B_SCALE = (FMT == FMT_Q8_0 ? KB : 8) * kPlane * 4;
-    static constexpr int B_MIN = (FMT == FMT_Q4_K) ? kTileN * 2 * 8 * 2 : 0;   // [col][g][8] fp16
-    static constexpr int A_SUM = (FMT == FMT_Q4_K) ? kTileM * 8 * 2 : 0;       // [row][8] fp16
-    static constexpr int OFF_A_SCALE = A_CODES;
-    static constexpr int OFF_B_CODES = OFF_A_SCALE + A_SCALE;
+    static constexpr int B_SCALE = KB * kPlane * 4;
+    static constexpr int B_MIN = (FMT == FMT_Q4_K) ? kTileN * 2 * KB * 2 : 0;   // [col][g][4] fp16
+    static constexpr int OFF_A_HDR = A_CODES;
+    static constexpr int OFF_B_CODES = OFF_A_HDR + A_HDR;
     static constexpr int OFF_B_SCALE = OFF_B_CODES + B_CODES;
     static constexpr int OFF_B_MIN = OFF_B_SCALE + B_SCALE;
-    static constexpr int OFF_A_SUM = OFF_B_MIN + B_MIN;
-    static constexpr int TOTAL = OFF_A_SUM + A_SUM;
+    static constexpr int STEP = OFF_B_MIN + B_MIN;     // one k-step buffer
+    static constexpr int TOTAL = 2 * STEP;
 };
-static_assert(KB == 4, "the staging maps below assume 4 blocks per k-step");
+static_assert(KB == 4 && kTileM == 128 && kTileN == 128 && kThreads == 512 && kNSub == 2,
+              "the staging maps below assume 4 blocks per k-step, a 128 x 128 tile and 512 threads");
 static_assert(Lds<FMT_Q8_0>::TOTAL == lds_bytes_for(FMT_Q8_0), "plan and kernel LDS disagree");
 static_assert(Lds<FMT_Q4_K>::TOTAL == lds_bytes_for(FMT_Q4_K), "plan and kernel LDS disagree");
 static_assert(Lds<FMT_Q4_K>::OFF_B_CODES % 16 == 0 && Lds<FMT_Q4_K>::OFF_B_MIN % 16 == 0 &&
-              Lds<FMT_Q4_K>::OFF_A_SUM % 16 == 0 && Lds<FMT_Q8_0>::OFF_B_SCALE % 16 == 0,
+              Lds<FMT_Q4_K>::STEP % 16 == 0 &&
+              Lds<FMT_Q8_0>::OFF_B_SCALE % 16 == 0 && Lds<FMT_Q8_0>::STEP % 16 == 0,
               "LDS regions must stay 16-byte aligned");
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // A raw buffer over the rows of one tile: reads past `bytes` return zero in
 // hardware, which is how rows beyond M or N are zero-filled (codes 0,
@@ -181,88 +223,98 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base,
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, n, 0x00020000);
 }
 
-// Staging is split into a load half (global memory -> registers, issued one
-// k-step ahead so that its latency hides behind the current step's MFMAs)
-// and a store half (registers -> LDS after the step's barrier).
+// Activations go from global memory to LDS by DMA (buffer_load ... lds): a
+// wave's DMA instruction writes 64 consecutive LDS slots of its size, slot i
+// from lane i's address, so choosing each lane's source realises any layout
+// of whole 16-byte (codes) or 4-byte (headers) units, including the swizzle,
+// with no registers and no VALU work.  A wave moves two 1 KiB slices of codes
+// (rows 16w..16w+15) and one 256-byte slice of headers (rows 16w..16w+15) per
+// k-step.  Each lane's offsets are fixed for the whole kernel; the k-step
+// enters as the scalar offset.
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Activations: unit u -> (row = u/4, block = u%4): four consecutive threads
-// read one row's 144 contiguous bytes of this step.
-struct ActRegs {
-    uint32_t w0[2];
-    u32x4 lo[2], hi[2];
+struct ActDma {
+    int code_off[2];   // per slice: byte offset in x of this lane's 16 code bytes at k-step 0
+    int hdr_off;       // byte offset of this lane's block header at k-step 0
 };
 
-__device__ __forceinline__ void load_activations(__amdgpu_buffer_rsrc_t rx, int kb, int ks, int tid,
-                                                 ActRegs &r) {
+__device__ __forceinline__ ActDma act_dma_offsets(int kb, int wv, int lane) {
+    ActDma o;
 #pragma unroll
     for (int i = 0; i < 2; i++) {
-        const int u = tid + kThreads * i;
-        const int row = u >> 2, b = u & 3;
-        const int off = (row * kb + ks * KB + b) * 36;
-        r.w0[i] = __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0);
-        r.lo[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 4, 0, 0);
-        r.hi[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 20, 0, 0);
+        const int row = 16 * wv + 8 * i + (lane >> 3);
+        const int j = (lane & 7) ^ (row & 7);          // chunk stored in slot lane%8 of this row
+        o.code_off[i] = row * kb * 36 + (j >> 1) * 36 + 4 + 16 * (j & 1);
     }
+    o.hdr_off = (16 * wv + (lane >> 2)) * kb * 36 + (lane & 3) * 36;
+    return o;
 }
 
 template <int FMT>
-__device__ __forceinline__ void store_activations(const ActRegs &r, uint8_t *smem, int ks, int tid) {
+__device__ __forceinline__ void dma_activations(__amdgpu_buffer_rsrc_t rx, const ActDma &o, int ks, uint8_t *buf,
+                                                int wv) {
     using L = Lds<FMT>;
-    unsigned short *sXh = reinterpret_cast<unsigned short *>(smem + L::OFF_A_SCALE);
+    const int soff = ks * KB * 36;
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int u = tid + kThreads * i;
-        const int row = u >> 2, b = u & 3;
-        *reinterpret_cast<u32x4 *>(smem + chunk_off(row, 2 * b)) = r.lo[i];
-        *reinterpret_cast<u32x4 *>(smem + chunk_off(row, 2 * b + 1)) = r.hi[i];
-        sXh[b * kPlaneH + xs_pos(row)] = (unsigned short)(r.w0[i] & 0xffffu);
-        if constexpr (FMT == FMT_Q4_K) {
-            unsigned short *sSum = reinterpret_cast<unsigned short *>(smem + L::OFF_A_SUM);
-            sSum[row * 8 + (ks & 1) * KB + b] = (unsigned short)(r.w0[i] >> 16);   // sub-block of its super-block
-        }
-    }
+    for (int i = 0; i < 2; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + (2 * wv + i) * 1024), 16, o.code_off[i], soff,
+                                                 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + L::OFF_A_HDR + wv * 256), 4, o.hdr_off, soff, 0, 0);
 }
 
-// Q8_0: thread -> (row = tid/2, block pair p = tid%2).  A pair of 34-byte
-// blocks is 68 bytes = 17 dwords starting on a 4-byte boundary (K % 256 == 0
-// makes every row an even number of blocks); the even block's codes sit two
-// bytes off the dword grid and are realigned with v_alignbyte.
+// Weights pass through registers instead (fetched one k-step ahead, stored
+// at the end of a step): Q8_0 codes sit two bytes off the dword grid and Q4_K
+// codes are unpacked, so neither can be copied as it is.  Each of the 512
+// threads moves one unit per step.
+//
+// Q8_0: a pair of 34-byte blocks is 68 bytes = 17 dwords starting on a
+// 4-byte boundary (K % 256 == 0 makes every row an even number of blocks).
+// Thread -> (column, pair q, half p) with p = wave%2 (wave-uniform): half 0
+// reads dwords 0..8 and realigns the even block's codes, which sit two bytes
+// off the dword grid, with v_alignbyte; half 1 reads dword 8 (the odd block's
+// scale in its high half) and the aligned dwords 9..16.
 struct Q80Regs {
-    u32x4 v[4];
+    u32x4 v0, v1;
     uint32_t last;
 };
 
+__device__ __forceinline__ int q80_unit(int tid) { return (tid >> 7) * 64 + (tid & 63); }
+
 __device__ __forceinline__ void load_q8_0(__amdgpu_buffer_rsrc_t rw, int kb, int ks, int tid, Q80Regs &r) {
-    const int row = tid >> 1, p = tid & 1;
-    const int off = (row * kb + ks * KB + 2 * p) * 34;
-#pragma unroll
-    for (int q = 0; q < 4; q++) r.v[q] = __builtin_amdgcn_raw_buffer_load_b128(rw, off + 16 * q, 0, 0);
-    r.last = __builtin_amdgcn_raw_buffer_load_b32(rw, off + 64, 0, 0);
+    const int u = q80_unit(tid), p = (tid >> 6) & 1;
+    const int col = u >> 1, q = u & 1;
+    const int off = (col * kb + ks * KB + 2 * q) * 34;
+    r.v0 = __builtin_amdgcn_raw_buffer_load_b128(rw, off + 36 * p, 0, 0);
+    r.v1 = __builtin_amdgcn_raw_buffer_load_b128(rw, off + 16 + 36 * p, 0, 0);
+    r.last = __builtin_amdgcn_raw_buffer_load_b32(rw, off + 32, 0, 0);
 }
 
-__device__ __forceinline__ void store_q8_0(const Q80Regs &r, uint8_t *smem, int tid) {
+__device__ __forceinline__ void store_q8_0(const Q80Regs &r, uint8_t *buf, int tid) {
     using L = Lds<FMT_Q8_0>;
-    uint8_t *sB = smem + L::OFF_B_CODES;
-    float *sWd = reinterpret_cast<float *>(smem + L::OFF_B_SCALE);
-    const int row = tid >> 1, p = tid & 1;
-    const uint32_t w[17] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w, r.v[1].x, r.v[1].y,
-                            r.v[1].z, r.v[1].w, r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w,
-                            r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w, r.last};
+    uint8_t *sB = buf + L::OFF_B_CODES;
+    float *sWd = reinterpret_cast<float *>(buf + L::OFF_B_SCALE);
+    const int u = q80_unit(tid), p = (tid >> 6) & 1;
+    const int col = u >> 1, b = 2 * (u & 1) + p;
     u32x4 c0, c1;
-    c0.x = __builtin_amdgcn_alignbyte(w[1], w[0], 2);
-    c0.y = __builtin_amdgcn_alignbyte(w[2], w[1], 2);
-    c0.z = __builtin_amdgcn_alignbyte(w[3], w[2], 2);
-    c0.w = __builtin_amdgcn_alignbyte(w[4], w[3], 2);
-    c1.x = __builtin_amdgcn_alignbyte(w[5], w[4], 2);
-    c1.y = __builtin_amdgcn_alignbyte(w[6], w[5], 2);
-    c1.z = __builtin_amdgcn_alignbyte(w[7], w[6], 2);
-    c1.w = __builtin_amdgcn_alignbyte(w[8], w[7], 2);
-    *reinterpret_cast<u32x4 *>(sB + chunk_off(row, 4 * p + 0)) = c0;
-    *reinterpret_cast<u32x4 *>(sB + chunk_off(row, 4 * p + 1)) = c1;
-    *reinterpret_cast<u32x4 *>(sB + chunk_off(row, 4 * p + 2)) = u32x4{w[9], w[10], w[11], w[12]};
-    *reinterpret_cast<u32x4 *>(sB + chunk_off(row, 4 * p + 3)) = u32x4{w[13], w[14], w[15], w[16]};
-    sWd[(2 * p) * kPlane + row] = h2f(w[0]);
-    sWd[(2 * p + 1) * kPlane + row] = h2f(w[8] >> 16);
+    uint32_t dbits;
+    if (p == 0) {   // wave-uniform
+        c0.x = __builtin_amdgcn_alignbyte(r.v0.y, r.v0.x, 2);
+        c0.y = __builtin_amdgcn_alignbyte(r.v0.z, r.v0.y, 2);
+        c0.z = __builtin_amdgcn_alignbyte(r.v0.w, r.v0.z, 2);
+        c0.w = __builtin_amdgcn_alignbyte(r.v1.x, r.v0.w, 2);
+        c1.x = __builtin_amdgcn_alignbyte(r.v1.y, r.v1.x, 2);
+        c1.y = __builtin_amdgcn_alignbyte(r.v1.z, r.v1.y, 2);
+        c1.z = __builtin_amdgcn_alignbyte(r.v1.w, r.v1.z, 2);
+        c1.w = __builtin_amdgcn_alignbyte(r.last, r.v1.w, 2);
+        dbits = r.v0.x;
+    } else {
+        c0 = r.v0;
+        c1 = r.v1;
+        dbits = r.last >> 16;
+    }
+    *reinterpret_cast<u32x4 *>(sB + chunk_off(col, 2 * b)) = c0;
+    *reinterpret_cast<u32x4 *>(sB + chunk_off(col, 2 * b + 1)) = c1;
+    sWd[b * kPlane + col] = h2f(dbits);
 }
 
 // Byte k (0..11) of the packed scale/min field held in three dwords.
@@ -277,10 +329,9 @@ __device__ __forceinline__ uint32_t sbyte(const u32x4 &h) {
 // and J+4; J >= 4 takes its low four bits from byte J+4 (scale: low nibble,
 // min: high nibble) and its top two bits from the spare top bits of bytes J-4
 // (scale) and J (min).  Writes d*sc_J and -dmin*m_J split into fp16 high and
-// low parts.
+// low parts, for block J%4 of the step.
 template <int J>
-__device__ __forceinline__ void q4k_subblock(const u32x4 &h, float d, float dmin, int row, float *sWd,
-                                             _Float16 *sMin) {
+__device__ __forceinline__ void q4k_subblock(const u32x4 &h, int col, float *sWd, _Float16 *sMin) {
     uint32_t sc, mn;
     if constexpr (J < 4) {
         sc = sbyte<J>(h) & 63u;
@@ -289,71 +340,62 @@ __device__ __forceinline__ void q4k_subblock(const u32x4 &h, float d, float dmin
         sc = (sbyte<J + 4>(h) & 15u) | ((sbyte<J - 4>(h) >> 6) << 4);
         mn = (sbyte<J + 4>(h) >> 4) | ((sbyte<J>(h) >> 6) << 4);
     }
-    sWd[J * kPlane + row] = d * (float)sc;                 // exact: 11 x 6 bits
+    const float d = h2f(h.x), dmin = h2f(h.x >> 16);
+    constexpr int jb = J % KB;                              // block of the step
+    sWd[jb * kPlane + col] = d * (float)sc;                 // exact: 11 x 6 bits
     const float neg = -(dmin * (float)mn);                  // exact
     const _Float16 hi = (_Float16)neg;
     const _Float16 lo = (_Float16)(neg - (float)hi);        // exact remainder
-    sMin[(row * 2 + 0) * 8 + J] = hi;
-    sMin[(row * 2 + 1) * 8 + J] = lo;
+    sMin[(col * 2 + 0) * KB + jb] = hi;
+    sMin[(col * 2 + 1) * KB + jb] = lo;
 }
 
-// Q4_K, half `ks & 1` of super-block `ks / 2`, for the tile's 128 columns.
-// Unit u -> (row = u/4, packed chunk c = 4*half + u%4): the 16 code bytes
-// 16c..16c+15 belong to 32-byte group c/2 and k-half c%2; their low nibbles
-// are codes of sub-block 2*(c/2), their high nibbles of sub-block 2*(c/2)+1
-// (the layout reading in the header).  They are unpacked at store time, once
-// per workgroup, into the same one-code-per-byte layout as Q8_0, so the MFMA
-// loop reads both formats alike.  At the first half the header is decoded
-// too: waves 0-1 turn sub-blocks 0..3 of row tid%128 into d*sc_j and the
-// split min operand, waves 2-3 sub-blocks 4..7 (a wave-uniform branch; every
-// sub-block index a compile-time constant).
+// Q4_K, half `ks & 1` of super-block `ks / 2`.  Codes: thread -> (column =
+// tid/4, packed chunk c = 4*half + tid%4): the 16 code bytes 16c..16c+15
+// belong to 32-byte group c/2 and k-half c%2; their low nibbles are codes of
+// sub-block 2*(c/2), their high nibbles of sub-block 2*(c/2)+1 (the layout
+// reading in the header).  They are unpacked at store time, once per
+// workgroup, into the same one-code-per-byte layout as Q8_0, so the MFMA loop
+// reads both formats alike.  Header: thread -> (column = 64*(wave/4) + lane,
+// sub-block 4*half + wave%4), so the sub-block index is wave-uniform and a
+// compile-time constant inside each case of the switch.
 struct Q4KRegs {
-    u32x4 v[2];
+    u32x4 v;
     u32x4 h;
 };
 
 __device__ __forceinline__ void load_q4_K(__amdgpu_buffer_rsrc_t rw, int nsb, int ks, int tid, Q4KRegs &r) {
     const int sb = ks >> 1, half = ks & 1;
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int u = tid + kThreads * i;
-        const int row = u >> 2, c = 4 * half + (u & 3);
-        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (row * nsb + sb) * 144 + 16 + 16 * c, 0, 0);
-    }
-    if (half == 0)
-        r.h = __builtin_amdgcn_raw_buffer_load_b128(rw, ((tid & (kTileN - 1)) * nsb + sb) * 144, 0, 0);
+    const int col = tid >> 2, c = 4 * half + (tid & 3);
+    r.v = __builtin_amdgcn_raw_buffer_load_b128(rw, (col * nsb + sb) * 144 + 16 + 16 * c, 0, 0);
+    const int hcol = (tid >> 8) * 64 + (tid & 63);
+    r.h = __builtin_amdgcn_raw_buffer_load_b128(rw, (hcol * nsb + sb) * 144, 0, 0);
 }
 
-__device__ __forceinline__ void store_q4_K(const Q4KRegs &r, uint8_t *smem, int ks, int tid) {
+__device__ __forceinline__ void store_q4_K(const Q4KRegs &r, uint8_t *buf, int ks, int tid) {
     using L = Lds<FMT_Q4_K>;
-    uint8_t *sB = smem + L::OFF_B_CODES;
-    float *sWd = reinterpret_cast<float *>(smem + L::OFF_B_SCALE);
-    _Float16 *sMin = reinterpret_cast<_Float16 *>(smem + L::OFF_B_MIN);
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int u = tid + kThreads * i;
-        const int row = u >> 2, cl = u & 3;          // cl: chunk within this half
-        const u32x4 lo = r.v[i] & 0x0F0F0F0Fu;
-        const u32x4 hi = (r.v[i] >> 4) & 0x0F0F0F0Fu;
+    uint8_t *sB = buf + L::OFF_B_CODES;
+    float *sWd = reinterpret_cast<float *>(buf + L::OFF_B_SCALE);
+    _Float16 *sMin = reinterpret_cast<_Float16 *>(buf + L::OFF_B_MIN);
+    {
+        const int col = tid >> 2, cl = tid & 3;      // cl: chunk within this half
+        const u32x4 lo = r.v & 0x0F0F0F0Fu;
+        const u32x4 hi = (r.v >> 4) & 0x0F0F0F0Fu;
         // sub-blocks 2*(c/2) and 2*(c/2)+1 are blocks 2*(cl/2) and 2*(cl/2)+1 of this step
         const int gl = cl >> 1, kh = cl & 1;
-        *reinterpret_cast<u32x4 *>(sB + chunk_off(row, 4 * gl + kh)) = lo;
-        *reinterpret_cast<u32x4 *>(sB + chunk_off(row, 4 * gl + 2 + kh)) = hi;
+        *reinterpret_cast<u32x4 *>(sB + chunk_off(col, 4 * gl + kh)) = lo;
+        *reinterpret_cast<u32x4 *>(sB + chunk_off(col, 4 * gl + 2 + kh)) = hi;
     }
-    if ((ks & 1) == 0) {
-        const int row = tid & (kTileN - 1);
-        const float d = h2f(r.h.x), dmin = h2f(r.h.x >> 16);
-        if (tid < kTileN) {
-            q4k_subblock<0>(r.h, d, dmin, row, sWd, sMin);
-            q4k_subblock<1>(r.h, d, dmin, row, sWd, sMin);
-            q4k_subblock<2>(r.h, d, dmin, row, sWd, sMin);
-            q4k_subblock<3>(r.h, d, dmin, row, sWd, sMin);
-        } else {
-            q4k_subblock<4>(r.h, d, dmin, row, sWd, sMin);
-            q4k_subblock<5>(r.h, d, dmin, row, sWd, sMin);
-            q4k_subblock<6>(r.h, d, dmin, row, sWd, sMin);
-            q4k_subblock<7>(r.h, d, dmin, row, sWd, sMin);
-        }
+    const int hcol = (tid >> 8) * 64 + (tid & 63);
+    switch ((ks & 1) * 4 + ((tid >> 6) & 3)) {   // wave-uniform
+    case 0: q4k_subblock<0>(r.h, hcol, sWd, sMin); break;
+    case 1: q4k_subblock<1>(r.h, hcol, sWd, sMin); break;
+    case 2: q4k_subblock<2>(r.h, hcol, sWd, sMin); break;
+    case 3: q4k_subblock<3>(r.h, hcol, sWd, sMin); break;
+    case 4: q4k_subblock<4>(r.h, hcol, sWd, sMin); break;
+    case 5: q4k_subblock<5>(r.h, hcol, sWd, sMin); break;
+    case 6: q4k_subblock<6>(r.h, hcol, sWd, sMin); break;
+    default: q4k_subblock<7>(r.h, hcol, sWd, sMin); break;
     }
 }
 
@@ -364,21 +406,41 @@ struct WRegs<FMT_Q8_0> { Q80Regs r; };
 template <>
 struct WRegs<FMT_Q4_K> { Q4KRegs r; };
 
+// One int8 MFMA at this point of the program.  The empty asm statements
+// redefine the operands just before it and its result just after it, so the
+// MFMA can move neither above nor below its neighbours in the software
+// pipeline (left free, the compiler may hoist all of a k-step's MFMAs ahead
+// of their epilogues and run out of registers).
+__device__ __forceinline__ i32x16 mfma_at(i32x4 &a, i32x4 &b, const i32x16 &c) {
+    asm volatile("" : "+v"(a), "+v"(b));
+    i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+    asm volatile("" : "+v"(d));
+    return d;
+}
+
+// acc[r] += xs(row of register r) * round(ws * I[r]) for the 16 registers:
+// all sixteen t first (compiler-visible, so the MFMA-to-VALU wait states are
+// the compiler's), then the row-broadcast FMAs.
+__device__ __forceinline__ void scale_epilogue(f32x16 &acc, const i32x16 &D, float ws, float cs, float xsv) {
+    f32x16 t;
+#pragma unroll
+    for (int r = 0; r < 16; r++) t[r] = __builtin_fmaf(__int_as_float(D[r]), ws, cs);
+    fmac_row_bcast8<0>(acc, t, xsv);
+    fmac_row_bcast8<8>(acc, t, xsv);
+}
+
 template <int FMT, bool DOTS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DOTS ? 1 : (FMT == FMT_Q8_0 ? 2 : 3))))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DOTS ? 2 : 4)))
 void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void *__restrict__ outp,
            int M, int N, int K) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using L = Lds<FMT>;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
+    const int wr = wv >> 1, wc = wv & 1;          // wave tile: rows 32*wr.., columns 64*wc..
     const int g = lane >> 5, l32 = lane & 31;
     const int n0 = blockIdx.x * kTileN, m0 = blockIdx.y * kTileM;
     const int kb = K >> 5, nsteps = kb / KB;
-
-    const _Float16 *sXh = reinterpret_cast<const _Float16 *>(smem + L::OFF_A_SCALE);
-    const uint8_t *sB = smem + L::OFF_B_CODES;
-    const float *sWd = reinterpret_cast<const float *>(smem + L::OFF_B_SCALE);
 
     // Buffers over this tile's rows of x and w (reads past M / N return 0).
     const int64_t xrow = int64_t(kb) * 36;
@@ -386,114 +448,139 @@ void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void 
     const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq + int64_t(m0) * xrow, int64_t(M - m0) * xrow);
     const __amdgpu_buffer_rsrc_t rw = tile_rsrc(wq + int64_t(n0) * wrow, int64_t(N - n0) * wrow);
 
-    const int a_row = (32 * wv + l32) * kRowBytes;   // this lane's A row (fragment row l32 of wave wv)
-    const int b_row = l32 * kRowBytes;                // this lane's B column within a 32-column sub-tile
+    const int a_row = (32 * wr + l32) * kRowBytes;   // this lane's A row
+    const int b_col0 = kWaveN * wc + l32;            // this lane's B column in sub-tile 0
+    // the activation row whose scale this lane holds for the row broadcasts
+    const int xs_row = 32 * wr + 8 * ((lane & 15) >> 2) + (lane & 3) + 4 * g;
+    const ActDma adma = act_dma_offsets(kb, wv, lane);
 
     i32x16 srcC;
 #pragma unroll
     for (int r = 0; r < 16; r++) srcC[r] = DOTS ? 0 : int(kMagicBits);
+    // an opaque value: kept in registers instead of being rebuilt from
+    // scalar registers before every MFMA
+    asm volatile("" : "+v"(srcC));
 
-    f32x16 acc[4];
+    f32x16 acc[kNSub];
 #pragma unroll
-    for (int c = 0; c < 4; c++)
+    for (int c = 0; c < kNSub; c++)
 #pragma unroll
         for (int r = 0; r < 16; r++) acc[c][r] = 0.0f;
 
-    // Q8_0 software-pipelines its staging (the registers hold step ks+1 while
-    // step ks computes); Q4_K, held to 168 VGPRs for three waves per SIMD,
-    // has no room for the prefetch registers and loads each step just before
-    // storing it.
-    constexpr bool kPrefetch = FMT == FMT_Q8_0;
-    ActRegs ar;
-    WRegs<FMT> wr;
-    auto load_step = [&](int k) {
-        load_activations(rx, kb, k, tid, ar);
+    WRegs<FMT> wr_;
+    auto load_w = [&](int k) {
         if constexpr (FMT == FMT_Q8_0)
-            load_q8_0(rw, kb, k, tid, wr.r);
+            load_q8_0(rw, kb, k, tid, wr_.r);
         else
-            load_q4_K(rw, K >> 8, k, tid, wr.r);
+            load_q4_K(rw, K >> 8, k, tid, wr_.r);
     };
-    if constexpr (kPrefetch) load_step(0);
+    auto store_w = [&](int k) {
+        uint8_t *buf = smem + (k & 1) * L::STEP;
+        if constexpr (FMT == FMT_Q8_0)
+            store_q8_0(wr_.r, buf, tid);
+        else
+            store_q4_K(wr_.r, buf, k, tid);
+    };
+
+    // Pipeline: step ks computes from buffer ks%2.  Meanwhile the DMA fills
+    // the other buffer with step ks+1's activations (issued at the top of the
+    // step), and the weight registers, fetched one step earlier, are stored
+    // into it at the end of the step; after the barrier they fetch step ks+2.
+    // Buffer (ks+1)%2 was last read by step ks-1, which every wave finished
+    // before the previous barrier.
+    dma_activations<FMT>(rx, adma, 0, smem, wv);
+    load_w(0);
+    store_w(0);
+    if (nsteps > 1) load_w(1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the DMA has landed in LDS
+    __syncthreads();
 
     for (int ks = 0; ks < nsteps; ks++) {
-        if constexpr (!kPrefetch) load_step(ks);
-        store_activations<FMT>(ar, smem, ks, tid);
-        if constexpr (FMT == FMT_Q8_0)
-            store_q8_0(wr.r, smem, tid);
-        else
-            store_q4_K(wr.r, smem, ks, tid);
-        __syncthreads();
-        if (kPrefetch && ks + 1 < nsteps) load_step(ks + 1);
+        if (ks + 1 < nsteps) dma_activations<FMT>(rx, adma, ks + 1, smem + ((ks + 1) & 1) * L::STEP, wv);
+        const uint8_t *buf = smem + (ks & 1) * L::STEP;
+        const unsigned short *sHdr = reinterpret_cast<const unsigned short *>(buf + L::OFF_A_HDR);
+        const uint8_t *sB = buf + L::OFF_B_CODES;
+        const float *sWd = reinterpret_cast<const float *>(buf + L::OFF_B_SCALE);
 
-        // Q4_K weight-scale planes hold the whole super-block: this step's
-        // blocks are sub-blocks 4*(ks&1) .. 4*(ks&1)+3
-        const int wplane = FMT == FMT_Q8_0 ? 0 : (ks & 1) * KB;
-#pragma unroll
-        for (int b = 0; b < KB; b++) {
-            // swizzled chunk of (block b, k-half g) for this lane's rows and
-            // columns: all of them are == l32 (mod 8)
+        // Sub-step st = (block b = st/2, sub-tile c = st%2).  Fragments of
+        // sub-step st+1 are read from LDS while st computes.
+        constexpr int kSteps = KB * kNSub;
+        i32x4 fa[2];
+        float xsv[2];
+        i32x4 fb[2];
+        float fw[2];
+        auto load_a = [&](int b) {
             const int sw = ((2 * b + g) ^ (l32 & 7)) << 4;
-            const i32x4 a = *reinterpret_cast<const i32x4 *>(smem + a_row + sw);
-            f16x8 xs0, xs1;   // activation scales of this lane's 16 accumulator rows
-            if constexpr (!DOTS) {
-                xs0 = *reinterpret_cast<const f16x8 *>(sXh + b * kPlaneH + 32 * wv + 16 * g);
-                xs1 = *reinterpret_cast<const f16x8 *>(sXh + b * kPlaneH + 32 * wv + 16 * g + 8);
+            fa[b & 1] = *reinterpret_cast<const i32x4 *>(buf + a_row + sw);
+            if constexpr (!DOTS) xsv[b & 1] = h2f(sHdr[(xs_row * KB + b) * 2]);
+        };
+        auto load_b = [&](int st) {
+            const int b = st / kNSub, c = st % kNSub;
+            const int col = b_col0 + 32 * c;
+            const int sw = ((2 * b + g) ^ (col & 7)) << 4;
+            fb[st & 1] = *reinterpret_cast<const i32x4 *>(sB + col * kRowBytes + sw);
+            if constexpr (!DOTS) fw[st & 1] = sWd[b * kPlane + col];
+        };
+        load_a(0);
+        load_b(0);
+#pragma unroll
+        for (int st = 0; st < kSteps; st++) {
+            const int b = st / kNSub, c = st % kNSub;
+            if (st + 1 < kSteps) {
+                load_b(st + 1);
+                if ((st + 1) % kNSub == 0) load_a(b + 1);
             }
+            const i32x16 D = mfma_at(fa[b & 1], fb[st & 1], srcC);
+            const int col = b_col0 + 32 * c;
+            if constexpr (DOTS) {
+                int32_t *dots = reinterpret_cast<int32_t *>(outp);
+                const int n = n0 + col;
 #pragma unroll
-            for (int c = 0; c < 4; c++) {
-                const int col = 32 * c + l32;
-                const i32x4 bq = *reinterpret_cast<const i32x4 *>(sB + b_row + sw + c * 32 * kRowBytes);
-                const i32x16 D = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bq, srcC, 0, 0, 0);
-                if constexpr (DOTS) {
-                    int32_t *dots = reinterpret_cast<int32_t *>(outp);
-                    const int n = n0 + col;
-#pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int m = m0 + 32 * wv + 8 * (r >> 2) + 4 * g + (r & 3);
-                        if (m < M && n < N)
-                            dots[(int64_t(m) * N + n) * kb + int64_t(ks) * KB + b] = D[r];
-                    }
-                } else {
-                    const float ws = sWd[(wplane + b) * kPlane + col];
-                    const float cs = -kMagic * ws;   // exact
-#pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const float t = __builtin_fmaf(__int_as_float(D[r]), ws, cs);
-                        const float xr = (float)(r < 8 ? xs0[r & 7] : xs1[r & 7]);   // exact widening
-                        acc[c][r] = __builtin_fmaf(xr, t, acc[c][r]);
-                    }
+                for (int r = 0; r < 16; r++) {
+                    const int m = m0 + 32 * wr + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if (m < M && n < N)
+                        dots[(int64_t(m) * N + n) * kb + int64_t(ks) * KB + b] = D[r];
                 }
-                // One MFMA result in flight per wave: the matrix core and the
-                // VALU do not overlap within a SIMD here, so the other waves
-                // of the SIMD hide this wave's MFMA latency, and the register
-                // budget allows three (Q4_K) or four (Q8_0) waves per SIMD.
-                // Only LDS reads may be hoisted across.
-                __builtin_amdgcn_sched_barrier(0x0100);
+            } else {
+                const float ws = fw[st & 1];
+                const float cs = -kMagic * ws;   // exact
+                scale_epilogue(acc[c], D, ws, cs, xsv[b & 1]);
+                // the epilogue happens here, not sunk to the end of the step
+                asm volatile("" : "+v"(acc[c]));
             }
         }
         if constexpr (FMT == FMT_Q4_K && !DOTS) {
-            if (ks & 1) {   // end of a super-block: its min term
-                const unsigned short *sSum = reinterpret_cast<const unsigned short *>(smem + L::OFF_A_SUM);
-                const _Float16 *sMin = reinterpret_cast<const _Float16 *>(smem + L::OFF_B_MIN);
-                const f16x8 sa = *reinterpret_cast<const f16x8 *>(sSum + (32 * wv + l32) * 8);
+            // the min term of this step's four sub-blocks
+            const _Float16 *sMin = reinterpret_cast<const _Float16 *>(buf + L::OFF_B_MIN);
+            // A = the four block sums s (high halves of the row's headers)
+            const u32x4 h = *reinterpret_cast<const u32x4 *>(buf + L::OFF_A_HDR + (32 * wr + l32) * KB * 4);
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 sp = {__builtin_amdgcn_perm(h.y, h.x, 0x07060302u), __builtin_amdgcn_perm(h.w, h.z, 0x07060302u)};
+            const f16x4 sa = __builtin_bit_cast(f16x4, sp);
+            // the accumulators were last written by the asm FMAs, which the
+            // compiler's hazard tracking does not see: wait states before an
+            // MFMA reads them as its C operand
+            asm volatile("s_nop 4" ::: "memory");
 #pragma unroll
-                for (int c = 0; c < 4; c++) {
-                    const f16x8 mb = *reinterpret_cast<const f16x8 *>(sMin + ((32 * c + l32) * 2 + g) * 8);
-                    acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa, mb, acc[c], 0, 0, 0);
-                }
+            for (int c = 0; c < kNSub; c++) {
+                const f16x4 mb = *reinterpret_cast<const f16x4 *>(sMin + ((b_col0 + 32 * c) * 2 + g) * KB);
+                acc[c] = __builtin_amdgcn_mfma_f32_32x32x8f16(sa, mb, acc[c], 0, 0, 0);
             }
         }
+        if (ks + 1 < nsteps) store_w(ks + 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // step ks+1's DMA has landed
         __syncthreads();
+        if (ks + 2 < nsteps) load_w(ks + 2);
     }
 
     if constexpr (!DOTS) {
         float *out = reinterpret_cast<float *>(outp);
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-            const int n = n0 + 32 * c + l32;
+        for (int c = 0; c < kNSub; c++) {
+            const int n = n0 + b_col0 + 32 * c;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int m = m0 + 32 * wv + 8 * (r >> 2) + 4 * g + (r & 3);
+                const int m = m0 + 32 * wr + 8 * (r >> 2) + 4 * g + (r & 3);
                 if (m < M && n < N) out[int64_t(m) * N + n] = acc[c][r];
             }
         }

@@ -18,20 +18,18 @@ enum Fmt : int { FMT_Q8_0 = 0, FMT_Q4_K = 1 };
 // Geometry of the GEMM kernel (must match the kernel's compile-time tile).
 constexpr int kTileM = 128;        // output rows per workgroup
 constexpr int kTileN = 128;        // output columns per workgroup
-constexpr int kThreads = 256;      // four wave64s; wave w owns rows 32w..32w+31
+constexpr int kThreads = 512;      // eight wave64s, a 4 x 2 grid of 32 x 64 wave tiles
 constexpr int kBlocksPerStage = 4; // 32-blocks staged per k-step (half a Q4_K super-block)
 
-// LDS bytes of one k-step for the kernel's layouts: codes row-major (32 B
-// per block per row, swizzled, no padding), activation scales fp16 in
-// 272-byte planes, weight scales fp32 in planes of 132 floats (Q4_K keeps the
-// eight planes of a whole super-block).
+// LDS bytes for the kernel's layouts: two k-step buffers, each with codes
+// row-major (32 B per block per row, swizzled, no padding), the activation
+// block headers [row][4] as dwords, and the weight scales fp32 in planes of
+// 132 floats; Q4_K adds the split min operand [col][2][4] fp16.
 constexpr int64_t lds_bytes_for(int fmt) {
-    const int64_t codes = int64_t(kTileM + kTileN) * 32 * kBlocksPerStage;
-    const int64_t ascale = int64_t(kBlocksPerStage) * 272;
-    if (fmt == FMT_Q8_0) return codes + ascale + int64_t(kBlocksPerStage) * 132 * 4;
-    // Q4_K: eight weight-scale planes, the split min operand [col][2][8] fp16
-    // and the activation block sums [row][8] fp16
-    return codes + ascale + int64_t(8) * 132 * 4 + int64_t(kTileN) * 2 * 8 * 2 + int64_t(kTileM) * 8 * 2;
+    int64_t step = int64_t(kTileM + kTileN) * 32 * kBlocksPerStage + int64_t(kTileM) * kBlocksPerStage * 4 +
+                   int64_t(kBlocksPerStage) * 132 * 4;
+    if (fmt == FMT_Q4_K) step += int64_t(kTileN) * 2 * kBlocksPerStage * 2;
+    return 2 * step;
 }
 
 struct Plan {
