@@ -143,6 +143,83 @@ def check_parity(fmt, M, N, K, x, w, xq_dev, out_dev):
     }
 
 
+def time_layer(M: int, steps: int, warmup: int, check: bool = True):
+    """The seven Q4_K projection GEMMs of one 7B layer at M tokens, with one
+    quantize pass per distinct input; one step is the whole set in order on
+    one stream."""
+    import torch
+    import block_quantized_int8_q8_amd as mmq
+    from block_quantized_int8_q8_amd import inputs
+
+    dev = torch.device("cuda:0")
+    shapes = {g: (n, k) for g, n, k in inputs.LAYER_7B}
+    stream = torch.cuda.current_stream()
+    host_x, xs, xqs, ws, outs, w_host = {}, {}, {}, {}, {}, {}
+    for name, K, gemms in inputs.LAYER_INPUTS:
+        host_x[name] = inputs.activations(M, K, inputs.layer_activation_seed(M, name))
+        xs[name] = torch.from_numpy(host_x[name]).to(dev)
+        xqs[name] = torch.empty((M, K // 32, 36), dtype=torch.uint8, device=dev)
+        for g in gemms:
+            N, _ = shapes[g]
+            w_host[g] = inputs.q4_K_weights(N, K, inputs.layer_weight_seed(g))
+            ws[g] = torch.from_numpy(w_host[g]).to(dev)
+            outs[g] = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        i = 0
+        for name, K, gemms in inputs.LAYER_INPUTS:
+            mmq.quantize_q8_1(xs[name], xqs[name], stream=stream)
+            for g in gemms:
+                if ev is not None:
+                    ev[i][0].record(stream)
+                N, _ = shapes[g]
+                mmq.gemm_q4_K(xqs[name], ws[g], M, N, K, outs[g], stream=stream)
+                if ev is not None:
+                    ev[i][1].record(stream)
+                i += 1
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    parity = None
+    if check:
+        import oracle
+        from tests import metrics
+        worst, unwritten = 0.0, 0
+        for name, K, gemms in inputs.LAYER_INPUTS:
+            rows = [0, M // 2, M - 1]
+            xq = oracle.quantize_q8_1(host_x[name][rows])
+            for g in gemms:
+                N, _ = shapes[g]
+                o = outs[g].cpu().numpy()
+                unwritten += int(np.isnan(o).sum())
+                worst = max(worst, metrics.normalized_max_error(
+                    o[rows], oracle.gemm_q4_K(xq, w_host[g], len(rows), N, K)))
+        parity = {"rows_checked_per_gemm": 3, "unwritten": unwritten,
+                  "normalized_max_error": worst, "ok": bool(unwritten == 0 and worst <= metrics.TOL)}
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(7)] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        step(ev[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(end) / steps
+    names = [g for _, _, gemms in inputs.LAYER_INPUTS for g in gemms]
+    gemm_ms = {g: float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)]))
+               for j, g in enumerate(names)}
+    ops = sum(2.0 * M * n * k for _, n, k in inputs.LAYER_7B)
+    return {
+        "M": M, "ms_per_layer": step_ms,
+        "tops_layer": ops / (step_ms * 1e-3) / 1e12,
+        "gemm_tops": ops / (sum(gemm_ms.values()) * 1e-3) / 1e12,
+        "gemm_ms": gemm_ms,
+        "parity": parity,
+    }
+
+
 def cpu_baseline(cfg: int, target_s: float = 15.0):
     """The oracle (quantize + GEMM) on a bounded row sample of the same
     workload, on the host cores; scaled to TOP/s of that sample."""
@@ -179,6 +256,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="benchmark shape (2: Q8_0 2048x3584x3584)")
     ap.add_argument("--extra-configs", default="3,4", help="other shapes timed in the same run")
+    ap.add_argument("--layer-m", default="512,2048,8192",
+                    help="token counts at which the 7B layer GEMM set is timed ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -215,6 +294,9 @@ def main():
             extra[f"config{c}"] = {k: r[k] for k in ("fmt", "M", "N", "K", "ms_per_step", "tops_step",
                                                       "gemm_ms_avg", "gemm_tops", "quant_gbs", "parity")}
             extra[f"config{c}"]["gemm_frac_of_int8_peak"] = r["gemm_tops"] / PEAK_INT8_TOPS
+
+    for m in [int(v) for v in args.layer_m.split(",") if v.strip()]:
+        extra[f"layer_M{m}"] = time_layer(m, max(3, args.steps // 10), 1, check=not args.no_check)
 
     kname = "k_mmq<Q8_0>" if main_rec["fmt"] == "q8_0" else "k_mmq<Q4_K>"
     achieved = main_rec["gemm_tops"]

@@ -127,17 +127,20 @@ constexpr float kMagic = 12582912.0f;
 constexpr int KB = kBlocksPerStage;            // 32-blocks per k-step
 
 // LDS layout of one k-step buffer.  Codes (activations, and weights of either
-// format once unpacked to one int8 code per byte) are row-major, 128 bytes per
-// row = 8 chunks of 16 bytes (block b of the step, k-half g -> chunk 2b+g),
-// with the chunk index XOR-swizzled by row%8: a fragment read (32 consecutive
-// rows, one chunk) touches eight distinct 16-byte bank groups per 8-lane
-// phase, and staging writes are at worst 2-way conflicted, with no padding.
+// format once unpacked to one int8 code per byte) are block-major: [block of
+// the step][row][32 bytes].  A fragment read (32 consecutive rows, one
+// 16-byte k-half) covers 16 bytes of every 32 in a 1 KiB span, and every
+// fragment address is a per-lane base plus a compile-time offset for the
+// block and sub-tile.  (Swapping the k-halves of every other group of four
+// rows, which would spread an 8-lane phase over 128 contiguous bytes, was
+// measured slower on gfx950.)
 //
 // Activation block headers (fp16 d and s) are copied as they are, [row][block]
 // as one dword each; a lane widens the one activation scale it needs per block
 // itself.  Weight scales are widened to fp32 at staging (v_fma_mix_f32, which
 // would take the fp16 form in the FMA, issues at half the rate of v_fmac_f32
-// on gfx950) and stored [block][column] in planes of 132 floats.
+// on gfx950) and stored [block][column] as the pair (ws, -1.5*2^23*ws), so
+// the epilogue's two constants arrive in one LDS read.
 //
 // An output register r of lane l needs the scale of row 8(r/4) + 4(l/32) +
 // r%4, so a lane needs 16 different row scales per block.  Instead of
@@ -147,13 +150,16 @@ constexpr int KB = kBlocksPerStage;            // 32-blocks per k-step
 // that row) hands each lane the scale of its register r inside the FMA
 // itself (v_fmac_f32 with a DPP source): lanes 0-31 see rows with l/32 = 0
 // and lanes 32-63 rows with l/32 = 1, as needed.
-constexpr int kRowBytes = KB * 32;   // codes per row per step
-constexpr int kPlane = 132;          // floats per weight-scale plane
+constexpr int kBlockBytes = kTileM * 32;   // one block of codes for the tile's 128 rows
 constexpr int kWavesN = 2;           // wave grid: 4 along rows x 2 along columns
 constexpr int kWaveN = kTileN / kWavesN;
 constexpr int kNSub = kWaveN / 32;   // 32-column sub-tiles per wave
+#ifndef MMQ_PREFETCH_B
+#define MMQ_PREFETCH_B 1
+#endif
+constexpr int kPfB = MMQ_PREFETCH_B; // sub-steps of B-fragment prefetch
 
-__device__ __forceinline__ int chunk_off(int row, int j) { return row * kRowBytes + ((j ^ (row & 7)) << 4); }
+__device__ __forceinline__ int code_off(int b, int row, int half) { return b * kBlockBytes + row * 32 + 16 * half; }
 
 // acc[R0+i] += (xsv of lane R0+i of this lane's 16-lane row) * t[R0+i], i =
 // 0..7, as v_fmac_f32_dpp row_newbcast (the compiler does not fold a
@@ -190,10 +196,10 @@ __device__ __forceinline__ void fmac_row_bcast8(f32x16 &acc, const f32x16 &t, fl
 
 template <int FMT>
 struct Lds {
-    static constexpr int A_CODES = kTileM * kRowBytes;
+    static constexpr int A_CODES = KB * kBlockBytes;
     static constexpr int A_HDR = kTileM * KB * 4;                               // [row][4] (d, s) fp16 pairs
-    static constexpr int B_CODES = kTileN * kRowBytes;
-    static constexpr int B_SCALE = KB * kPlane * 4;
+    static constexpr int B_CODES = KB * kBlockBytes;
+    static constexpr int B_SCALE = KB * kTileN * 8;                             // [4][col] (ws, cs) fp32
     static constexpr int B_MIN = (FMT == FMT_Q4_K) ? kTileN * 2 * KB * 2 : 0;   // [col][g][4] fp16
     static constexpr int OFF_A_HDR = A_CODES;
     static constexpr int OFF_B_CODES = OFF_A_HDR + A_HDR;
@@ -202,7 +208,7 @@ struct Lds {
     static constexpr int STEP = OFF_B_MIN + B_MIN;     // one k-step buffer
     static constexpr int TOTAL = 2 * STEP;
 };
-static_assert(KB == 4 && kTileM == 128 && kTileN == 128 && kThreads == 512 && kNSub == 2,
+static_assert(KB == 4 && kTileM == 128 && kTileN == 128 && kThreads == 512 && kNSub == 2 && kBlockBytes == 4096,
               "the staging maps below assume 4 blocks per k-step, a 128 x 128 tile and 512 threads");
 static_assert(Lds<FMT_Q8_0>::TOTAL == lds_bytes_for(FMT_Q8_0), "plan and kernel LDS disagree");
 static_assert(Lds<FMT_Q4_K>::TOTAL == lds_bytes_for(FMT_Q4_K), "plan and kernel LDS disagree");
@@ -226,10 +232,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base,
 // Activations go from global memory to LDS by DMA (buffer_load ... lds): a
 // wave's DMA instruction writes 64 consecutive LDS slots of its size, slot i
 // from lane i's address, so choosing each lane's source realises any layout
-// of whole 16-byte (codes) or 4-byte (headers) units, including the swizzle,
-// with no registers and no VALU work.  A wave moves two 1 KiB slices of codes
-// (rows 16w..16w+15) and one 256-byte slice of headers (rows 16w..16w+15) per
-// k-step.  Each lane's offsets are fixed for the whole kernel; the k-step
+// of whole 16-byte (codes) or 4-byte (headers) units with no registers and no
+// VALU work.  A wave moves two 1 KiB slices of codes (slice s = block s/4,
+// rows 32(s%4)..32(s%4)+31) and one 256-byte slice of headers (rows
+// 16w..16w+15) per k-step.  Each lane's offsets are fixed for the whole kernel; the k-step
 // enters as the scalar offset.
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -242,9 +248,9 @@ __device__ __forceinline__ ActDma act_dma_offsets(int kb, int wv, int lane) {
     ActDma o;
 #pragma unroll
     for (int i = 0; i < 2; i++) {
-        const int row = 16 * wv + 8 * i + (lane >> 3);
-        const int j = (lane & 7) ^ (row & 7);          // chunk stored in slot lane%8 of this row
-        o.code_off[i] = row * kb * 36 + (j >> 1) * 36 + 4 + 16 * (j & 1);
+        const int s = 2 * wv + i, b = s >> 2;
+        const int row = 32 * (s & 3) + (lane >> 1), half = lane & 1;   // slot = code_off(b, row, half)
+        o.code_off[i] = row * kb * 36 + b * 36 + 4 + 16 * half;
     }
     o.hdr_off = (16 * wv + (lane >> 2)) * kb * 36 + (lane & 3) * 36;
     return o;
@@ -292,7 +298,7 @@ __device__ __forceinline__ void load_q8_0(__amdgpu_buffer_rsrc_t rw, int kb, int
 __device__ __forceinline__ void store_q8_0(const Q80Regs &r, uint8_t *buf, int tid) {
     using L = Lds<FMT_Q8_0>;
     uint8_t *sB = buf + L::OFF_B_CODES;
-    float *sWd = reinterpret_cast<float *>(buf + L::OFF_B_SCALE);
+    float2 *sW = reinterpret_cast<float2 *>(buf + L::OFF_B_SCALE);
     const int u = q80_unit(tid), p = (tid >> 6) & 1;
     const int col = u >> 1, b = 2 * (u & 1) + p;
     u32x4 c0, c1;
@@ -312,9 +318,10 @@ __device__ __forceinline__ void store_q8_0(const Q80Regs &r, uint8_t *buf, int t
         c1 = r.v1;
         dbits = r.last >> 16;
     }
-    *reinterpret_cast<u32x4 *>(sB + chunk_off(col, 2 * b)) = c0;
-    *reinterpret_cast<u32x4 *>(sB + chunk_off(col, 2 * b + 1)) = c1;
-    sWd[b * kPlane + col] = h2f(dbits);
+    *reinterpret_cast<u32x4 *>(sB + code_off(b, col, 0)) = c0;
+    *reinterpret_cast<u32x4 *>(sB + code_off(b, col, 1)) = c1;
+    const float ws = h2f(dbits);
+    sW[b * kTileN + col] = make_float2(ws, -kMagic * ws);   // exact: 11 x 2 bits
 }
 
 // Byte k (0..11) of the packed scale/min field held in three dwords.
@@ -331,7 +338,7 @@ __device__ __forceinline__ uint32_t sbyte(const u32x4 &h) {
 // (scale) and J (min).  Writes d*sc_J and -dmin*m_J split into fp16 high and
 // low parts, for block J%4 of the step.
 template <int J>
-__device__ __forceinline__ void q4k_subblock(const u32x4 &h, int col, float *sWd, _Float16 *sMin) {
+__device__ __forceinline__ void q4k_subblock(const u32x4 &h, int col, float2 *sW, _Float16 *sMin) {
     uint32_t sc, mn;
     if constexpr (J < 4) {
         sc = sbyte<J>(h) & 63u;
@@ -342,7 +349,8 @@ __device__ __forceinline__ void q4k_subblock(const u32x4 &h, int col, float *sWd
     }
     const float d = h2f(h.x), dmin = h2f(h.x >> 16);
     constexpr int jb = J % KB;                              // block of the step
-    sWd[jb * kPlane + col] = d * (float)sc;                 // exact: 11 x 6 bits
+    const float ws = d * (float)sc;                         // exact: 11 x 6 bits
+    sW[jb * kTileN + col] = make_float2(ws, -kMagic * ws);  // exact: 17 x 2 bits
     const float neg = -(dmin * (float)mn);                  // exact
     const _Float16 hi = (_Float16)neg;
     const _Float16 lo = (_Float16)(neg - (float)hi);        // exact remainder
@@ -375,7 +383,7 @@ __device__ __forceinline__ void load_q4_K(__amdgpu_buffer_rsrc_t rw, int nsb, in
 __device__ __forceinline__ void store_q4_K(const Q4KRegs &r, uint8_t *buf, int ks, int tid) {
     using L = Lds<FMT_Q4_K>;
     uint8_t *sB = buf + L::OFF_B_CODES;
-    float *sWd = reinterpret_cast<float *>(buf + L::OFF_B_SCALE);
+    float2 *sW = reinterpret_cast<float2 *>(buf + L::OFF_B_SCALE);
     _Float16 *sMin = reinterpret_cast<_Float16 *>(buf + L::OFF_B_MIN);
     {
         const int col = tid >> 2, cl = tid & 3;      // cl: chunk within this half
@@ -383,19 +391,19 @@ __device__ __forceinline__ void store_q4_K(const Q4KRegs &r, uint8_t *buf, int k
         const u32x4 hi = (r.v >> 4) & 0x0F0F0F0Fu;
         // sub-blocks 2*(c/2) and 2*(c/2)+1 are blocks 2*(cl/2) and 2*(cl/2)+1 of this step
         const int gl = cl >> 1, kh = cl & 1;
-        *reinterpret_cast<u32x4 *>(sB + chunk_off(col, 4 * gl + kh)) = lo;
-        *reinterpret_cast<u32x4 *>(sB + chunk_off(col, 4 * gl + 2 + kh)) = hi;
+        *reinterpret_cast<u32x4 *>(sB + code_off(2 * gl, col, kh)) = lo;
+        *reinterpret_cast<u32x4 *>(sB + code_off(2 * gl + 1, col, kh)) = hi;
     }
     const int hcol = (tid >> 8) * 64 + (tid & 63);
     switch ((ks & 1) * 4 + ((tid >> 6) & 3)) {   // wave-uniform
-    case 0: q4k_subblock<0>(r.h, hcol, sWd, sMin); break;
-    case 1: q4k_subblock<1>(r.h, hcol, sWd, sMin); break;
-    case 2: q4k_subblock<2>(r.h, hcol, sWd, sMin); break;
-    case 3: q4k_subblock<3>(r.h, hcol, sWd, sMin); break;
-    case 4: q4k_subblock<4>(r.h, hcol, sWd, sMin); break;
-    case 5: q4k_subblock<5>(r.h, hcol, sWd, sMin); break;
-    case 6: q4k_subblock<6>(r.h, hcol, sWd, sMin); break;
-    default: q4k_subblock<7>(r.h, hcol, sWd, sMin); break;
+    case 0: q4k_subblock<0>(r.h, hcol, sW, sMin); break;
+    case 1: q4k_subblock<1>(r.h, hcol, sW, sMin); break;
+    case 2: q4k_subblock<2>(r.h, hcol, sW, sMin); break;
+    case 3: q4k_subblock<3>(r.h, hcol, sW, sMin); break;
+    case 4: q4k_subblock<4>(r.h, hcol, sW, sMin); break;
+    case 5: q4k_subblock<5>(r.h, hcol, sW, sMin); break;
+    case 6: q4k_subblock<6>(r.h, hcol, sW, sMin); break;
+    default: q4k_subblock<7>(r.h, hcol, sW, sMin); break;
     }
 }
 
@@ -429,12 +437,23 @@ __device__ __forceinline__ void scale_epilogue(f32x16 &acc, const i32x16 &D, flo
     fmac_row_bcast8<8>(acc, t, xsv);
 }
 
+template <int P>
+struct Parity {
+    static constexpr int value = P;
+};
+
 template <int FMT, bool DOTS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DOTS ? 2 : 4)))
 void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void *__restrict__ outp,
            int M, int N, int K) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using L = Lds<FMT>;
+    // The two k-step buffers are two LDS variables, not offsets into one
+    // array: the compiler then knows that the DMA into one buffer cannot
+    // write what the fragment reads of the other return, and does not make
+    // every LDS read wait for the DMA in flight.  The step loop is unrolled
+    // by two so that each copy names its buffers at compile time.
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[L::STEP];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[L::STEP];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const int wr = wv >> 1, wc = wv & 1;          // wave tile: rows 32*wr.., columns 64*wc..
@@ -448,8 +467,9 @@ void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void 
     const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq + int64_t(m0) * xrow, int64_t(M - m0) * xrow);
     const __amdgpu_buffer_rsrc_t rw = tile_rsrc(wq + int64_t(n0) * wrow, int64_t(N - n0) * wrow);
 
-    const int a_row = (32 * wr + l32) * kRowBytes;   // this lane's A row
     const int b_col0 = kWaveN * wc + l32;            // this lane's B column in sub-tile 0
+    const int a_lane = code_off(0, 32 * wr + l32, g); // fragment bases; blocks and sub-tiles
+    const int b_lane = code_off(0, b_col0, g);        // are compile-time offsets from here
     // the activation row whose scale this lane holds for the row broadcasts
     const int xs_row = 32 * wr + 8 * ((lane & 15) >> 2) + (lane & 3) + 4 * g;
     const ActDma adma = act_dma_offsets(kb, wv, lane);
@@ -474,63 +494,61 @@ void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void 
         else
             load_q4_K(rw, K >> 8, k, tid, wr_.r);
     };
-    auto store_w = [&](int k) {
-        uint8_t *buf = smem + (k & 1) * L::STEP;
+    auto store_w = [&](int k, uint8_t *buf) {
         if constexpr (FMT == FMT_Q8_0)
             store_q8_0(wr_.r, buf, tid);
         else
             store_q4_K(wr_.r, buf, k, tid);
     };
 
-    // Pipeline: step ks computes from buffer ks%2.  Meanwhile the DMA fills
+    // Pipeline: step ks computes from buffer ks%2 (lds0 or lds1).  Meanwhile the DMA fills
     // the other buffer with step ks+1's activations (issued at the top of the
     // step), and the weight registers, fetched one step earlier, are stored
     // into it at the end of the step; after the barrier they fetch step ks+2.
     // Buffer (ks+1)%2 was last read by step ks-1, which every wave finished
     // before the previous barrier.
-    dma_activations<FMT>(rx, adma, 0, smem, wv);
+    dma_activations<FMT>(rx, adma, 0, lds0, wv);
     load_w(0);
-    store_w(0);
+    store_w(0, lds0);
     if (nsteps > 1) load_w(1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the DMA has landed in LDS
     __syncthreads();
 
-    for (int ks = 0; ks < nsteps; ks++) {
-        if (ks + 1 < nsteps) dma_activations<FMT>(rx, adma, ks + 1, smem + ((ks + 1) & 1) * L::STEP, wv);
-        const uint8_t *buf = smem + (ks & 1) * L::STEP;
+    auto step = [&](auto parity, int ks) {
+        constexpr int P = decltype(parity)::value;
+        uint8_t *const buf = P ? lds1 : lds0;     // step ks (ks % 2 == P)
+        uint8_t *const nxt = P ? lds0 : lds1;     // step ks + 1
+        if (ks + 1 < nsteps) dma_activations<FMT>(rx, adma, ks + 1, nxt, wv);
         const unsigned short *sHdr = reinterpret_cast<const unsigned short *>(buf + L::OFF_A_HDR);
         const uint8_t *sB = buf + L::OFF_B_CODES;
-        const float *sWd = reinterpret_cast<const float *>(buf + L::OFF_B_SCALE);
+        const float2 *sW = reinterpret_cast<const float2 *>(buf + L::OFF_B_SCALE);
 
-        // Sub-step st = (block b = st/2, sub-tile c = st%2).  Fragments of
-        // sub-step st+1 are read from LDS while st computes.
+        // Sub-step st = (block b = st/2, sub-tile c = st%2).  B fragments are
+        // read from LDS kPfB sub-steps ahead, A fragments one block ahead.
         constexpr int kSteps = KB * kNSub;
+        constexpr int kRing = kPfB + 1;
         i32x4 fa[2];
         float xsv[2];
-        i32x4 fb[2];
-        float fw[2];
+        i32x4 fb[kRing];
+        float2 fw[kRing];
         auto load_a = [&](int b) {
-            const int sw = ((2 * b + g) ^ (l32 & 7)) << 4;
-            fa[b & 1] = *reinterpret_cast<const i32x4 *>(buf + a_row + sw);
+            fa[b & 1] = *reinterpret_cast<const i32x4 *>(buf + a_lane + b * kBlockBytes);
             if constexpr (!DOTS) xsv[b & 1] = h2f(sHdr[(xs_row * KB + b) * 2]);
         };
         auto load_b = [&](int st) {
             const int b = st / kNSub, c = st % kNSub;
-            const int col = b_col0 + 32 * c;
-            const int sw = ((2 * b + g) ^ (col & 7)) << 4;
-            fb[st & 1] = *reinterpret_cast<const i32x4 *>(sB + col * kRowBytes + sw);
-            if constexpr (!DOTS) fw[st & 1] = sWd[b * kPlane + col];
+            fb[st % kRing] = *reinterpret_cast<const i32x4 *>(sB + b_lane + b * kBlockBytes + c * 32 * 32);
+            if constexpr (!DOTS) fw[st % kRing] = sW[b * kTileN + b_col0 + 32 * c];
         };
         load_a(0);
-        load_b(0);
+#pragma unroll
+        for (int st = 0; st < kPfB; st++) load_b(st);
 #pragma unroll
         for (int st = 0; st < kSteps; st++) {
             const int b = st / kNSub, c = st % kNSub;
-            if (st + 1 < kSteps) {
-                load_b(st + 1);
-                if ((st + 1) % kNSub == 0) load_a(b + 1);
-            }
-            const i32x16 D = mfma_at(fa[b & 1], fb[st & 1], srcC);
+            if (st + kPfB < kSteps) load_b(st + kPfB);
+            if (c == 0 && b + 1 < KB) load_a(b + 1);
+            const i32x16 D = mfma_at(fa[b & 1], fb[st % kRing], srcC);
             const int col = b_col0 + 32 * c;
             if constexpr (DOTS) {
                 int32_t *dots = reinterpret_cast<int32_t *>(outp);
@@ -542,9 +560,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void 
                         dots[(int64_t(m) * N + n) * kb + int64_t(ks) * KB + b] = D[r];
                 }
             } else {
-                const float ws = fw[st & 1];
-                const float cs = -kMagic * ws;   // exact
-                scale_epilogue(acc[c], D, ws, cs, xsv[b & 1]);
+                scale_epilogue(acc[c], D, fw[st % kRing].x, fw[st % kRing].y, xsv[b & 1]);
                 // the epilogue happens here, not sunk to the end of the step
                 asm volatile("" : "+v"(acc[c]));
             }
@@ -567,10 +583,14 @@ void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void 
                 acc[c] = __builtin_amdgcn_mfma_f32_32x32x8f16(sa, mb, acc[c], 0, 0, 0);
             }
         }
-        if (ks + 1 < nsteps) store_w(ks + 1);
+        if (ks + 1 < nsteps) store_w(ks + 1, nxt);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // step ks+1's DMA has landed
         __syncthreads();
         if (ks + 2 < nsteps) load_w(ks + 2);
+    };
+    for (int ks = 0; ks < nsteps; ks += 2) {   // nsteps = K / 128 is even
+        step(Parity<0>{}, ks);
+        if (ks + 1 < nsteps) step(Parity<1>{}, ks + 1);
     }
 
     if constexpr (!DOTS) {
@@ -606,7 +626,9 @@ hipError_t launch_gemm(const Plan &p, const void *x, const void *w, void *out, i
     const dim3 block(p.threads);
     const auto *xb = reinterpret_cast<const uint8_t *>(x);
     const auto *wb = reinterpret_cast<const uint8_t *>(w);
-    const size_t lds = size_t(p.lds_bytes);
+    // The GEMM kernel's LDS is static (its two k-step buffers, lds_bytes_for()
+    // bytes, which the plan checked against the device); nothing dynamic.
+    const size_t lds = 0;
     if (p.fmt == FMT_Q8_0) {
         if (dots)
             hipLaunchKernelGGL((k_mmq<FMT_Q8_0, true>), grid, block, lds, stream, xb, wb, out, int(M), int(N), int(K));

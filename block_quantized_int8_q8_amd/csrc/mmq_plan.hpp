@@ -22,12 +22,13 @@ constexpr int kThreads = 512;      // eight wave64s, a 4 x 2 grid of 32 x 64 wav
 constexpr int kBlocksPerStage = 4; // 32-blocks staged per k-step (half a Q4_K super-block)
 
 // LDS bytes for the kernel's layouts: two k-step buffers, each with codes
-// row-major (32 B per block per row, swizzled, no padding), the activation
-// block headers [row][4] as dwords, and the weight scales fp32 in planes of
-// 132 floats; Q4_K adds the split min operand [col][2][4] fp16.
+// block-major (32 B per block per row, no padding), the activation block
+// headers [row][4] as dwords, and the weight scale pairs [4][col] as two fp32;
+// Q4_K adds the split min operand [col][2][4] fp16.  Q4_K comes to exactly
+// 80 KiB, so two workgroups share a CU's 160 KiB.
 constexpr int64_t lds_bytes_for(int fmt) {
     int64_t step = int64_t(kTileM + kTileN) * 32 * kBlocksPerStage + int64_t(kTileM) * kBlocksPerStage * 4 +
-                   int64_t(kBlocksPerStage) * 132 * 4;
+                   int64_t(kBlocksPerStage) * kTileN * 8;
     if (fmt == FMT_Q4_K) step += int64_t(kTileN) * 2 * kBlocksPerStage * 2;
     return 2 * step;
 }

@@ -128,3 +128,23 @@ LAYER_7B = [  # (name, N, K) -- hidden 3584, 28 q heads / 4 kv heads of 128, ffn
     ("up", 18944, 3584),
     ("down", 3584, 18944),
 ]
+
+# Config 5: the layer's GEMMs at these token counts, Q4_K weights.  GEMMs that
+# read the same activations share one q8_1 quantize pass: q, k and v read the
+# attention input, gate and up the FFN input.
+LAYER_M = (512, 2048, 8192)
+LAYER_INPUTS = [  # (input name, K, GEMMs reading it)
+    ("attn_in", 3584, ("q", "k", "v")),
+    ("o_in", 3584, ("o",)),
+    ("ffn_in", 3584, ("gate", "up")),
+    ("down_in", 18944, ("down",)),
+]
+
+
+def layer_weight_seed(gemm: str) -> int:
+    """One weight tensor per projection, the same at every token count."""
+    return seed_for(5, 10 + [g for g, _, _ in LAYER_7B].index(gemm))
+
+
+def layer_activation_seed(M: int, input_name: str) -> int:
+    return seed_for(5, 100 + 4 * LAYER_M.index(M) + [n for n, _, _ in LAYER_INPUTS].index(input_name))

@@ -183,6 +183,40 @@ def test_full_size_configs_sampled_rows(cfg):
     assert rep["normalized_max_error"] <= metrics.TOL
 
 
+@pytest.mark.parametrize("M", inputs.LAYER_M)
+def test_layer_gemm_set_sampled_rows(M):
+    """The seven Q4_K projection GEMMs of one 7B layer at M tokens, with one
+    GPU quantize pass per distinct input: the q8_1 bytes in full, and every
+    output on sampled rows (first, last, last row tile, random)."""
+    shapes = {g: (n, k) for g, n, k in inputs.LAYER_7B}
+    for name, K, gemms in inputs.LAYER_INPUTS:
+        _say(f"layer M={M}: input {name} K={K}")
+        x = inputs.activations(M, K, inputs.layer_activation_seed(M, name))
+        xq_dev = mmq.quantize_q8_1(_to_dev(x))
+        torch.cuda.synchronize()
+        xq = oracle.quantize_q8_1(x)
+        assert np.array_equal(xq_dev.cpu().numpy(), xq)
+        del x
+        rows = sorted(set([0, M - 1, M - 128, M // 2] + list(np.random.default_rng(M).integers(0, M, 4))))
+        sub = np.ascontiguousarray(xq[rows])
+        for g in gemms:
+            N, Kg = shapes[g]
+            assert Kg == K
+            _say(f"layer M={M}: gemm {g} N={N} K={K}")
+            w = inputs.q4_K_weights(N, K, inputs.layer_weight_seed(g))
+            out = _nan_out(M, N)
+            mmq.gemm_q4_K(xq_dev, _to_dev(w), M, N, K, out)
+            torch.cuda.synchronize()
+            o = out.cpu().numpy()
+            del out
+            assert not np.isnan(o).any()
+            rep = metrics.report(o[rows], oracle.gemm_q4_K(sub, w, len(rows), N, K))
+            _say(rep)
+            assert rep["normalized_max_error"] <= metrics.TOL
+        del xq_dev
+        torch.cuda.empty_cache()
+
+
 def test_nondefault_stream():
     _say("non-default stream")
     M, N, K = 96, 160, 512
