@@ -16,6 +16,8 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "mmq_plan.hpp"
 
 namespace mmq {
@@ -445,7 +447,7 @@ struct Parity {
 template <int FMT, bool DOTS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DOTS ? 2 : 4)))
 void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void *__restrict__ outp,
-           int M, int N, int K) {
+           int M, int N, int K, int steps_per_split) {
     using L = Lds<FMT>;
     // The two k-step buffers are two LDS variables, not offsets into one
     // array: the compiler then knows that the DMA into one buffer cannot
@@ -460,6 +462,9 @@ void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void 
     const int g = lane >> 5, l32 = lane & 31;
     const int n0 = blockIdx.x * kTileN, m0 = blockIdx.y * kTileM;
     const int kb = K >> 5, nsteps = kb / KB;
+    // this workgroup's k-steps: [ks0, ks0 + nloc) (all of them unless K is split)
+    const int ks0 = blockIdx.z * steps_per_split;
+    const int nloc = min(steps_per_split, nsteps - ks0);
 
     // Buffers over this tile's rows of x and w (reads past M / N return 0).
     const int64_t xrow = int64_t(kb) * 36;
@@ -507,18 +512,19 @@ void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void 
     // into it at the end of the step; after the barrier they fetch step ks+2.
     // Buffer (ks+1)%2 was last read by step ks-1, which every wave finished
     // before the previous barrier.
-    dma_activations<FMT>(rx, adma, 0, lds0, wv);
-    load_w(0);
-    store_w(0, lds0);
-    if (nsteps > 1) load_w(1);
+    dma_activations<FMT>(rx, adma, ks0, lds0, wv);
+    load_w(ks0);
+    store_w(ks0, lds0);
+    if (nloc > 1) load_w(ks0 + 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the DMA has landed in LDS
     __syncthreads();
 
-    auto step = [&](auto parity, int ks) {
+    auto step = [&](auto parity, int j) {
         constexpr int P = decltype(parity)::value;
-        uint8_t *const buf = P ? lds1 : lds0;     // step ks (ks % 2 == P)
-        uint8_t *const nxt = P ? lds0 : lds1;     // step ks + 1
-        if (ks + 1 < nsteps) dma_activations<FMT>(rx, adma, ks + 1, nxt, wv);
+        const int ks = ks0 + j;                   // the k-step; j is its place in this workgroup's range
+        uint8_t *const buf = P ? lds1 : lds0;     // local step j (j % 2 == P)
+        uint8_t *const nxt = P ? lds0 : lds1;     // local step j + 1
+        if (j + 1 < nloc) dma_activations<FMT>(rx, adma, ks + 1, nxt, wv);
         const unsigned short *sHdr = reinterpret_cast<const unsigned short *>(buf + L::OFF_A_HDR);
         const uint8_t *sB = buf + L::OFF_B_CODES;
         const float2 *sW = reinterpret_cast<const float2 *>(buf + L::OFF_B_SCALE);
@@ -583,28 +589,41 @@ void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void 
                 acc[c] = __builtin_amdgcn_mfma_f32_32x32x8f16(sa, mb, acc[c], 0, 0, 0);
             }
         }
-        if (ks + 1 < nsteps) store_w(ks + 1, nxt);
+        if (j + 1 < nloc) store_w(ks + 1, nxt);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // step ks+1's DMA has landed
         __syncthreads();
-        if (ks + 2 < nsteps) load_w(ks + 2);
+        if (j + 2 < nloc) load_w(ks + 2);
     };
-    for (int ks = 0; ks < nsteps; ks += 2) {   // nsteps = K / 128 is even
-        step(Parity<0>{}, ks);
-        if (ks + 1 < nsteps) step(Parity<1>{}, ks + 1);
+    for (int j = 0; j < nloc; j += 2) {
+        step(Parity<0>{}, j);
+        if (j + 1 < nloc) step(Parity<1>{}, j + 1);
     }
 
     if constexpr (!DOTS) {
         float *out = reinterpret_cast<float *>(outp);
+        const bool split = gridDim.z > 1;   // partial sums: added into the zeroed output
 #pragma unroll
         for (int c = 0; c < kNSub; c++) {
             const int n = n0 + b_col0 + 32 * c;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int m = m0 + 32 * wr + 8 * (r >> 2) + 4 * g + (r & 3);
-                if (m < M && n < N) out[int64_t(m) * N + n] = acc[c][r];
+                if (m < M && n < N) {
+                    if (split)
+                        unsafeAtomicAdd(out + int64_t(m) * N + n, acc[c][r]);
+                    else
+                        out[int64_t(m) * N + n] = acc[c][r];
+                }
             }
         }
     }
+}
+
+// Zero an fp32 array (the output of a split-K launch, before the slices add
+// into it).  A kernel rather than a memset node, so that the launch sequence
+// stays capturable as plain kernels.
+__global__ __launch_bounds__(256) void k_zero_fill(float *__restrict__ p, int64_t n) {
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) p[i] = 0.0f;
 }
 
 // Host-side launchers (declared in mmq_launch.hpp).
@@ -622,7 +641,13 @@ hipError_t launch_quantize(const float *x, void *y, int64_t M, int64_t K, int cu
 
 hipError_t launch_gemm(const Plan &p, const void *x, const void *w, void *out, int64_t M, int64_t N,
                        int64_t K, bool dots, hipStream_t stream) {
-    const dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y);
+    const dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.split_k);
+    if (p.split_k > 1 && !dots) {
+        const int64_t n = M * N;
+        const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
+        hipLaunchKernelGGL(k_zero_fill, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<float *>(out), n);
+    }
+    const int sps = int(p.steps_per_split);
     const dim3 block(p.threads);
     const auto *xb = reinterpret_cast<const uint8_t *>(x);
     const auto *wb = reinterpret_cast<const uint8_t *>(w);
@@ -631,14 +656,14 @@ hipError_t launch_gemm(const Plan &p, const void *x, const void *w, void *out, i
     const size_t lds = 0;
     if (p.fmt == FMT_Q8_0) {
         if (dots)
-            hipLaunchKernelGGL((k_mmq<FMT_Q8_0, true>), grid, block, lds, stream, xb, wb, out, int(M), int(N), int(K));
+            hipLaunchKernelGGL((k_mmq<FMT_Q8_0, true>), grid, block, lds, stream, xb, wb, out, int(M), int(N), int(K), sps);
         else
-            hipLaunchKernelGGL((k_mmq<FMT_Q8_0, false>), grid, block, lds, stream, xb, wb, out, int(M), int(N), int(K));
+            hipLaunchKernelGGL((k_mmq<FMT_Q8_0, false>), grid, block, lds, stream, xb, wb, out, int(M), int(N), int(K), sps);
     } else {
         if (dots)
-            hipLaunchKernelGGL((k_mmq<FMT_Q4_K, true>), grid, block, lds, stream, xb, wb, out, int(M), int(N), int(K));
+            hipLaunchKernelGGL((k_mmq<FMT_Q4_K, true>), grid, block, lds, stream, xb, wb, out, int(M), int(N), int(K), sps);
         else
-            hipLaunchKernelGGL((k_mmq<FMT_Q4_K, false>), grid, block, lds, stream, xb, wb, out, int(M), int(N), int(K));
+            hipLaunchKernelGGL((k_mmq<FMT_Q4_K, false>), grid, block, lds, stream, xb, wb, out, int(M), int(N), int(K), sps);
     }
     return hipGetLastError();
 }

@@ -20,6 +20,14 @@ constexpr int kTileM = 128;        // output rows per workgroup
 constexpr int kTileN = 128;        // output columns per workgroup
 constexpr int kThreads = 512;      // eight wave64s, a 4 x 2 grid of 32 x 64 wave tiles
 constexpr int kBlocksPerStage = 4; // 32-blocks staged per k-step (half a Q4_K super-block)
+constexpr int kWgPerCu = 2;        // workgroups resident per CU (LDS and VGPR budget)
+// Split-K policy, measured on the 7B layer shapes: split only when the output
+// tiles fill at most half of the resident workgroup slots, and then into
+// about one workgroup per CU (more slices cost more in fp32 atomics than
+// they gain), each slice keeping at least four k-steps.
+constexpr int kMinStepsPerSplit = 4;   // k-steps a split-K slice keeps at least
+constexpr int kSplitBelow = 2;         // split when tiles * kSplitBelow <= resident slots
+constexpr int kSplitSlots = 1;         // workgroups per CU a split aims for
 
 // LDS bytes for the kernel's layouts: two k-step buffers, each with codes
 // block-major (32 B per block per row, no padding), the activation block
@@ -39,6 +47,9 @@ struct Plan {
     int64_t lds_bytes = 0;
     int64_t grid_x = 0, grid_y = 0;   // x: column tiles, y: row tiles
     int64_t k_steps = 0;
+    // Split K: grid z = split_k slices of steps_per_split k-steps each (the
+    // last may be shorter), summed into a zeroed output with fp32 atomics.
+    int64_t split_k = 1, steps_per_split = 0;
 };
 
 inline bool fmt_ok(int fmt) { return fmt == FMT_Q8_0 || fmt == FMT_Q4_K; }
@@ -78,6 +89,19 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
     q.grid_y = (M + kTileM - 1) / kTileM;
     q.k_steps = K / (32 * kBlocksPerStage);
     if (q.grid_y > 65535) return fail("too many row tiles for the launch grid (M too large)");
+    // Too few output tiles to occupy the device (at most half of the
+    // resident workgroup slots): split K into slices of at least
+    // kMinStepsPerSplit k-steps, about one workgroup per CU in all.
+    q.steps_per_split = q.k_steps;
+    const int64_t tiles = q.grid_x * q.grid_y, slots = int64_t(kWgPerCu) * cu_count;
+    if (tiles * kSplitBelow <= slots) {
+        int64_t s = (int64_t(kSplitSlots) * cu_count + tiles - 1) / tiles;
+        if (s > q.k_steps / kMinStepsPerSplit) s = q.k_steps / kMinStepsPerSplit;
+        if (s > 1) {
+            q.steps_per_split = (q.k_steps + s - 1) / s;
+            q.split_k = (q.k_steps + q.steps_per_split - 1) / q.steps_per_split;
+        }
+    }
     if (q.grid_x > INT32_MAX) return fail("too many column tiles");
     if (q.lds_bytes > lds_limit) {
         if (why && why_len)
@@ -92,10 +116,11 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
 
 inline void describe(const Plan &p, char *buf, size_t len) {
     std::snprintf(buf, len,
-                  "fmt=%s tile=%dx%d threads=%d blocks_per_stage=%d lds=%lld grid=%lldx%lld k_steps=%lld",
+                  "fmt=%s tile=%dx%d threads=%d blocks_per_stage=%d lds=%lld grid=%lldx%lld k_steps=%lld "
+                  "split_k=%lld steps_per_split=%lld",
                   fmt_name(p.fmt), p.tile_m, p.tile_n, p.threads, p.blocks_per_stage,
                   (long long)p.lds_bytes, (long long)p.grid_x, (long long)p.grid_y,
-                  (long long)p.k_steps);
+                  (long long)p.k_steps, (long long)p.split_k, (long long)p.steps_per_split);
 }
 
 }  // namespace mmq

@@ -49,6 +49,27 @@ def test_plans_for_benchmark_shapes_fit(fmt, M, N, K):
     assert gx == -(-N // 128) and gy == -(-M // 128)
 
 
+@pytest.mark.parametrize("M,N,K,split,steps", [
+    (2048, 3584, 3584, 1, 28),      # 448 tiles: enough to occupy 256 CUs x 2
+    (2048, 18944, 3584, 1, 28),
+    (512, 512, 3584, 7, 4),         # 16 tiles: 7 slices of 4 k-steps (the minimum)
+    (512, 3584, 3584, 3, 10),       # 112 tiles: ~one workgroup per CU
+    (512, 3584, 18944, 3, 50),
+    (2048, 512, 3584, 4, 7),        # 64 tiles
+    (8192, 512, 3584, 1, 28),       # 256 tiles: one per CU already
+    (64, 256, 512, 1, 4),           # 4 k-steps: too short to split
+    (100, 100, 18944, 37, 4),       # one tile, 148 k-steps
+])
+def test_split_k_planning(M, N, K, split, steps):
+    for fmt in (mmq.FMT_Q8_0, mmq.FMT_Q4_K):
+        ok, desc = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
+        assert ok, desc
+        got = tuple(int(v) for v in re.search(r"split_k=(\d+) steps_per_split=(\d+)", desc).groups())
+        assert got == (split, steps), desc
+        k_steps = K // 128
+        assert (split - 1) * steps < k_steps <= split * steps   # no empty slice
+
+
 @pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
 def test_guard_refuses_over_capacity_lds(fmt):
     ok, desc = mmq.plan_for_limits(fmt, 2048, 3584, 3584, LDS_GFX950, 256)
