@@ -80,7 +80,12 @@ int mmq_quantize_q8_1(const float *x, void *y, int64_t M, int64_t K, void *strea
  *   out: M x N fp32 row-major (leading dimension N), fully overwritten.
  * Per block the weight scale multiplies the integer dot first (one
  * rounding) and the activation scale is then fused into the fp32 running
- * sum, blocks in ascending order from 0.  Requires K % 256 == 0. */
+ * sum, blocks in ascending order from 0.  Requires K % 256 == 0.
+ * Shapes with too few 128 x 128 output tiles to occupy the device are split
+ * along K (mmq_plan_describe reports split_k): the library first zeroes
+ * `out` with a kernel on `stream`, then each K slice adds its partial sums
+ * with fp32 atomics, so for those shapes the summation order, and the last
+ * bits of the result, can differ from run to run. */
 int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out,
                   int64_t M, int64_t N, int64_t K, void *stream);
 
@@ -88,7 +93,8 @@ int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out,
  * Surface?", section 6.2, affine identity with the min term folded in
  * through the q8_1 block-sum field).
  *   x_q8_1: M x (K/32) q8_1 blocks; w_q4_K: N x (K/256) super-blocks;
- *   out: M x N fp32 row-major, fully overwritten.  Requires K % 256 == 0. */
+ *   out: M x N fp32 row-major, fully overwritten.  Requires K % 256 == 0.
+ * Split-K shapes behave as for mmq_gemm_q8_0. */
 int mmq_gemm_q4_K(const void *x_q8_1, const void *w_q4_K, float *out,
                   int64_t M, int64_t N, int64_t K, void *stream);
 
