@@ -144,9 +144,10 @@ def check_parity(fmt, M, N, K, x, w, xq_dev, out_dev):
 
 
 def time_layer(M: int, steps: int, warmup: int, check: bool = True):
-    """The seven Q4_K projection GEMMs of one 7B layer at M tokens, with one
-    quantize pass per distinct input; one step is the whole set in order on
-    one stream."""
+    """The seven Q4_K projection GEMMs of one 7B layer at M tokens: one
+    quantize pass per distinct input, and the GEMMs that share it (q, k, v;
+    gate, up) in one launch; one step is the whole set in order on one
+    stream.  `gemm_ms` is per input group."""
     import torch
     import block_quantized_int8_q8_amd as mmq
     from block_quantized_int8_q8_amd import inputs
@@ -165,18 +166,22 @@ def time_layer(M: int, steps: int, warmup: int, check: bool = True):
             ws[g] = torch.from_numpy(w_host[g]).to(dev)
             outs[g] = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
 
+    groups = [(name, K, gemms) for name, K, gemms in inputs.LAYER_INPUTS]
+
     def step(ev=None):
-        i = 0
-        for name, K, gemms in inputs.LAYER_INPUTS:
+        # one quantize per distinct input, then its GEMMs in one launch
+        for i, (name, K, gemms) in enumerate(groups):
             mmq.quantize_q8_1(xs[name], xqs[name], stream=stream)
-            for g in gemms:
-                if ev is not None:
-                    ev[i][0].record(stream)
-                N, _ = shapes[g]
-                mmq.gemm_q4_K(xqs[name], ws[g], M, N, K, outs[g], stream=stream)
-                if ev is not None:
-                    ev[i][1].record(stream)
-                i += 1
+            if ev is not None:
+                ev[i][0].record(stream)
+            if len(gemms) == 1:
+                g = gemms[0]
+                mmq.gemm_q4_K(xqs[name], ws[g], M, shapes[g][0], K, outs[g], stream=stream)
+            else:
+                mmq.gemm_multi(mmq.FMT_Q4_K, xqs[name], [ws[g] for g in gemms], [shapes[g][0] for g in gemms],
+                               M, K, [outs[g] for g in gemms], stream=stream)
+            if ev is not None:
+                ev[i][1].record(stream)
 
     for _ in range(warmup):
         step()
@@ -197,7 +202,7 @@ def time_layer(M: int, steps: int, warmup: int, check: bool = True):
                     o[rows], oracle.gemm_q4_K(xq, w_host[g], len(rows), N, K)))
         parity = {"rows_checked_per_gemm": 3, "unwritten": unwritten,
                   "normalized_max_error": worst, "ok": bool(unwritten == 0 and worst <= metrics.TOL)}
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(7)] for _ in range(steps)]
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in groups] for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -207,9 +212,8 @@ def time_layer(M: int, steps: int, warmup: int, check: bool = True):
     end.record(stream)
     torch.cuda.synchronize()
     step_ms = start.elapsed_time(end) / steps
-    names = [g for _, _, gemms in inputs.LAYER_INPUTS for g in gemms]
-    gemm_ms = {g: float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)]))
-               for j, g in enumerate(names)}
+    gemm_ms = {"+".join(gemms): float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)]))
+               for j, (_, _, gemms) in enumerate(groups)}
     ops = sum(2.0 * M * n * k for _, n, k in inputs.LAYER_7B)
     return {
         "M": M, "ms_per_layer": step_ms,

@@ -18,7 +18,7 @@ FMT_Q4_K = 1
 Q8_1_BYTES, Q8_0_BYTES, Q4_K_BYTES = 36, 34, 144
 
 EXPORTS = (
-    "mmq_quantize_q8_1", "mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_debug_block_dots",
+    "mmq_quantize_q8_1", "mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_multi", "mmq_debug_block_dots",
     "mmq_last_error", "mmq_plan_describe", "mmq_plan_for_limits",
     "mmq_debug_set_extra_lds", "mmq_version",
 )
@@ -44,6 +44,8 @@ def lib() -> ctypes.CDLL:
         for name in ("mmq_gemm_q8_0", "mmq_gemm_q4_K"):
             getattr(L, name).argtypes = [p, p, p, i64, i64, i64, p]
             getattr(L, name).restype = i32
+        L.mmq_gemm_multi.argtypes = [i32, p, i32, p, p, p, i64, i64, p]
+        L.mmq_gemm_multi.restype = i32
         L.mmq_debug_block_dots.argtypes = [i32, p, p, p, i64, i64, i64, p]
         L.mmq_debug_block_dots.restype = i32
         L.mmq_last_error.argtypes = []
@@ -112,6 +114,22 @@ def gemm_q8_0(xq, w, M, N, K, out=None, stream=None):
 def gemm_q4_K(xq, w, M, N, K, out=None, stream=None):
     """q8_1 [M, K/32, 36] x Q4_K [N, K/256, 144] -> fp32 [M, N]."""
     return _gemm("mmq_gemm_q4_K", "mmq_gemm_q4_K", xq, w, M, N, K, out, stream)
+
+
+def gemm_multi(fmt, xq, ws, Ns, M, K, outs=None, stream=None):
+    """One launch of several GEMMs sharing the q8_1 activations:
+    q8_1 [M, K/32, 36] x ws[g] [N[g], ...] -> outs[g] fp32 [M, N[g]]."""
+    import torch
+    count = len(ws)
+    if len(Ns) != count or (outs is not None and len(outs) != count):
+        raise ValueError("ws, Ns and outs must have the same length")
+    if outs is None:
+        outs = [torch.empty((M, n), dtype=torch.float32, device=xq.device) for n in Ns]
+    wp = (ctypes.c_void_p * count)(*[_ptr(w).value for w in ws])
+    op = (ctypes.c_void_p * count)(*[_ptr(o, torch.float32).value for o in outs])
+    npv = (ctypes.c_int64 * count)(*[int(n) for n in Ns])
+    _check(lib().mmq_gemm_multi(fmt, _ptr(xq), count, wp, op, npv, M, K, _stream(stream)), "mmq_gemm_multi")
+    return outs
 
 
 def debug_block_dots(fmt, xq, w, M, N, K, dots=None, stream=None):

@@ -19,8 +19,8 @@
 
 namespace mmq {
 hipError_t launch_quantize(const float *x, void *y, int64_t M, int64_t K, int cu_count, hipStream_t stream);
-hipError_t launch_gemm(const Plan &p, const void *x, const void *w, void *out, int64_t M, int64_t N,
-                       int64_t K, bool dots, hipStream_t stream);
+hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const void *x, const void *const *w,
+                       void *const *out, const int64_t *N, int64_t M, int64_t K, bool dots, hipStream_t stream);
 }  // namespace mmq
 
 namespace {
@@ -86,25 +86,38 @@ bool current_limits(DeviceLimits *out) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int gemm_common(int fmt, const void *x, const void *w, void *out, int64_t M, int64_t N, int64_t K,
-                bool dots, void *stream) {
+int gemm_set(int fmt, const void *x, int count, const void *const *w, void *const *out, const int64_t *N,
+             int64_t M, int64_t K, bool dots, void *stream) {
     g_err[0] = '\0';
     if (!mmq::fmt_ok(fmt)) return refuse("unknown weight format %d", fmt);
-    if (!x || !w || !out) return refuse("null pointer argument");
-    if (!aligned(x, 16) || !aligned(w, 16)) return refuse("activation and weight pointers must be 16-byte aligned");
-    if (!aligned(out, 4)) return refuse("output pointer must be 4-byte aligned");
+    if (count < 1 || count > mmq::kMaxGemms) return refuse("count must be 1..%d GEMMs", mmq::kMaxGemms);
+    if (!x || !w || !out || !N) return refuse("null pointer argument");
+    if (!aligned(x, 16)) return refuse("activation and weight pointers must be 16-byte aligned");
+    for (int g = 0; g < count; g++) {
+        if (!w[g] || !out[g]) return refuse("null pointer argument");
+        if (!aligned(w[g], 16)) return refuse("activation and weight pointers must be 16-byte aligned");
+        if (!aligned(out[g], 4)) return refuse("output pointer must be 4-byte aligned");
+    }
     DeviceLimits L;
     if (!current_limits(&L)) return 0;
     if (!L.is_gfx950) return refuse("device is %s; this library is built for gfx950 only", L.arch);
     mmq::Plan p;
+    int tile_start[mmq::kMaxGemms + 1];
     char why[256];
-    if (!mmq::make_plan(fmt, M, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), &p, why, sizeof(why)))
-        return refuse("%s GEMM M=%lld N=%lld K=%lld: %s", mmq::fmt_name(fmt), (long long)M, (long long)N,
-                      (long long)K, why);
+    if (!mmq::make_plan_multi(fmt, M, count, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), &p, tile_start,
+                              why, sizeof(why)))
+        return refuse("%s GEMM M=%lld N=%lld K=%lld%s: %s", mmq::fmt_name(fmt), (long long)M, (long long)N[0],
+                      (long long)K, count > 1 ? " (first of a set)" : "", why);
     (void)hipGetLastError();   // a stale error must not be blamed on this launch
-    const hipError_t e = mmq::launch_gemm(p, x, w, out, M, N, K, dots, static_cast<hipStream_t>(stream));
+    const hipError_t e = mmq::launch_gemm(p, tile_start, count, x, w, out, N, M, K, dots,
+                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return refuse("%s GEMM launch failed: %s", mmq::fmt_name(fmt), hipGetErrorString(e));
     return 1;
+}
+
+int gemm_common(int fmt, const void *x, const void *w, void *out, int64_t M, int64_t N, int64_t K,
+                bool dots, void *stream) {
+    return gemm_set(fmt, x, 1, &w, &out, &N, M, K, dots, stream);
 }
 
 }  // namespace
@@ -134,6 +147,11 @@ int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out, int64_t M,
 int mmq_gemm_q4_K(const void *x_q8_1, const void *w_q4_K, float *out, int64_t M, int64_t N, int64_t K,
                   void *stream) {
     return gemm_common(mmq::FMT_Q4_K, x_q8_1, w_q4_K, out, M, N, K, false, stream);
+}
+
+int mmq_gemm_multi(int fmt, const void *x_q8_1, int count, const void *const *w, float *const *out,
+                   const int64_t *N, int64_t M, int64_t K, void *stream) {
+    return gemm_set(fmt, x_q8_1, count, w, reinterpret_cast<void *const *>(out), N, M, K, false, stream);
 }
 
 int mmq_debug_block_dots(int fmt, const void *x_q8_1, const void *w, int32_t *dots, int64_t M, int64_t N,

@@ -17,6 +17,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "mmq_plan.hpp"
 
@@ -444,10 +445,20 @@ struct Parity {
     static constexpr int value = P;
 };
 
+// The GEMMs of one launch (a single GEMM is a set of one): they share the
+// activations and K; GEMM g owns column tiles [tile_start[g], tile_start[g+1])
+// of the grid's x dimension.  Passed by value in the kernel arguments.
+struct GemmSet {
+    int count;
+    int tile_start[kMaxGemms + 1];
+    int N[kMaxGemms];
+    const uint8_t *w[kMaxGemms];
+    void *out[kMaxGemms];
+};
+
 template <int FMT, bool DOTS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DOTS ? 2 : 4)))
-void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void *__restrict__ outp,
-           int M, int N, int K, int steps_per_split) {
+void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int steps_per_split) {
     using L = Lds<FMT>;
     // The two k-step buffers are two LDS variables, not offsets into one
     // array: the compiler then knows that the DMA into one buffer cannot
@@ -460,7 +471,14 @@ void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void 
     const int lane = tid & 63, wv = tid >> 6;
     const int wr = wv >> 1, wc = wv & 1;          // wave tile: rows 32*wr.., columns 64*wc..
     const int g = lane >> 5, l32 = lane & 31;
-    const int n0 = blockIdx.x * kTileN, m0 = blockIdx.y * kTileM;
+    // which GEMM of the set this column tile belongs to (workgroup-uniform)
+    int gi = 0;
+    for (int i = 1; i < set.count; i++)
+        if (int(blockIdx.x) >= set.tile_start[i]) gi = i;
+    const uint8_t *__restrict__ wq = set.w[gi];
+    void *__restrict__ outp = set.out[gi];
+    const int N = set.N[gi];
+    const int n0 = (int(blockIdx.x) - set.tile_start[gi]) * kTileN, m0 = blockIdx.y * kTileM;
     const int kb = K >> 5, nsteps = kb / KB;
     // this workgroup's k-steps: [ks0, ks0 + nloc) (all of them unless K is split)
     const int ks0 = blockIdx.z * steps_per_split;
@@ -536,7 +554,10 @@ void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void 
         i32x4 fa[2];
         float xsv[2];
         i32x4 fb[kRing];
-        float2 fw[kRing];
+        // Q8_0 reads the (ws, cs) pair; Q4_K, short of registers, reads ws
+        // alone and forms cs with one multiply (exact)
+        using WsT = typename std::conditional<FMT == FMT_Q8_0, float2, float>::type;
+        WsT fw[kRing];
         auto load_a = [&](int b) {
             fa[b & 1] = *reinterpret_cast<const i32x4 *>(buf + a_lane + b * kBlockBytes);
             if constexpr (!DOTS) xsv[b & 1] = h2f(sHdr[(xs_row * KB + b) * 2]);
@@ -544,7 +565,12 @@ void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void 
         auto load_b = [&](int st) {
             const int b = st / kNSub, c = st % kNSub;
             fb[st % kRing] = *reinterpret_cast<const i32x4 *>(sB + b_lane + b * kBlockBytes + c * 32 * 32);
-            if constexpr (!DOTS) fw[st % kRing] = sW[b * kTileN + b_col0 + 32 * c];
+            if constexpr (!DOTS) {
+                if constexpr (FMT == FMT_Q8_0)
+                    fw[st % kRing] = sW[b * kTileN + b_col0 + 32 * c];
+                else
+                    fw[st % kRing] = sW[b * kTileN + b_col0 + 32 * c].x;
+            }
         };
         load_a(0);
 #pragma unroll
@@ -566,7 +592,10 @@ void k_mmq(const uint8_t *__restrict__ xq, const uint8_t *__restrict__ wq, void 
                         dots[(int64_t(m) * N + n) * kb + int64_t(ks) * KB + b] = D[r];
                 }
             } else {
-                scale_epilogue(acc[c], D, fw[st % kRing].x, fw[st % kRing].y, xsv[b & 1]);
+                if constexpr (FMT == FMT_Q8_0)
+                    scale_epilogue(acc[c], D, fw[st % kRing].x, fw[st % kRing].y, xsv[b & 1]);
+                else
+                    scale_epilogue(acc[c], D, fw[st % kRing], -kMagic * fw[st % kRing], xsv[b & 1]);
                 // the epilogue happens here, not sunk to the end of the step
                 asm volatile("" : "+v"(acc[c]));
             }
@@ -639,31 +668,42 @@ hipError_t launch_quantize(const float *x, void *y, int64_t M, int64_t K, int cu
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(const Plan &p, const void *x, const void *w, void *out, int64_t M, int64_t N,
-                       int64_t K, bool dots, hipStream_t stream) {
-    const dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.split_k);
-    if (p.split_k > 1 && !dots) {
-        const int64_t n = M * N;
-        const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
-        hipLaunchKernelGGL(k_zero_fill, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<float *>(out), n);
+hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const void *x, const void *const *w,
+                       void *const *out, const int64_t *N, int64_t M, int64_t K, bool dots, hipStream_t stream) {
+    GemmSet set{};
+    set.count = count;
+    for (int g = 0; g < count; g++) {
+        set.tile_start[g] = tile_start[g];
+        set.N[g] = int(N[g]);
+        set.w[g] = reinterpret_cast<const uint8_t *>(w[g]);
+        set.out[g] = out[g];
     }
+    set.tile_start[count] = tile_start[count];
+    if (p.split_k > 1 && !dots) {
+        for (int g = 0; g < count; g++) {
+            const int64_t n = M * N[g];
+            const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
+            hipLaunchKernelGGL(k_zero_fill, dim3((unsigned)blocks), dim3(256), 0, stream,
+                               reinterpret_cast<float *>(out[g]), n);
+        }
+    }
+    const dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.split_k);
     const int sps = int(p.steps_per_split);
     const dim3 block(p.threads);
     const auto *xb = reinterpret_cast<const uint8_t *>(x);
-    const auto *wb = reinterpret_cast<const uint8_t *>(w);
     // The GEMM kernel's LDS is static (its two k-step buffers, lds_bytes_for()
     // bytes, which the plan checked against the device); nothing dynamic.
     const size_t lds = 0;
     if (p.fmt == FMT_Q8_0) {
         if (dots)
-            hipLaunchKernelGGL((k_mmq<FMT_Q8_0, true>), grid, block, lds, stream, xb, wb, out, int(M), int(N), int(K), sps);
+            hipLaunchKernelGGL((k_mmq<FMT_Q8_0, true>), grid, block, lds, stream, xb, set, int(M), int(K), sps);
         else
-            hipLaunchKernelGGL((k_mmq<FMT_Q8_0, false>), grid, block, lds, stream, xb, wb, out, int(M), int(N), int(K), sps);
+            hipLaunchKernelGGL((k_mmq<FMT_Q8_0, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps);
     } else {
         if (dots)
-            hipLaunchKernelGGL((k_mmq<FMT_Q4_K, true>), grid, block, lds, stream, xb, wb, out, int(M), int(N), int(K), sps);
+            hipLaunchKernelGGL((k_mmq<FMT_Q4_K, true>), grid, block, lds, stream, xb, set, int(M), int(K), sps);
         else
-            hipLaunchKernelGGL((k_mmq<FMT_Q4_K, false>), grid, block, lds, stream, xb, wb, out, int(M), int(N), int(K), sps);
+            hipLaunchKernelGGL((k_mmq<FMT_Q4_K, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps);
     }
     return hipGetLastError();
 }

@@ -114,6 +114,33 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
     return true;
 }
 
+// Several GEMMs of one format that read the same activations (M x K), one
+// launch: the column tiles of all of them form one grid row, GEMM g owning
+// tiles [tile_start[g], tile_start[g+1]).  Planned as one GEMM of
+// N = 128 * (total column tiles); every N[g] must itself plan.
+constexpr int kMaxGemms = 8;
+
+inline bool make_plan_multi(int fmt, int64_t M, int count, const int64_t *Ns, int64_t K, int64_t lds_limit,
+                            int cu_count, int64_t extra_lds, Plan *p, int *tile_start, char *why,
+                            size_t why_len) {
+    auto fail = [&](const char *msg) {
+        if (why && why_len) std::snprintf(why, why_len, "%s", msg);
+        return false;
+    };
+    if (count < 1 || count > kMaxGemms) return fail("count must be 1..8 GEMMs");
+    if (!Ns) return fail("null N array");
+    int64_t tiles = 0;
+    for (int g = 0; g < count; g++) {
+        Plan one;
+        if (!make_plan(fmt, M, Ns[g], K, lds_limit, cu_count, extra_lds, &one, why, why_len)) return false;
+        tile_start[g] = int(tiles);
+        tiles += one.grid_x;
+        if (tiles > (int64_t(1) << 24)) return fail("too many column tiles in the GEMM set");
+    }
+    tile_start[count] = int(tiles);
+    return make_plan(fmt, M, tiles * kTileN, K, lds_limit, cu_count, extra_lds, p, why, why_len);
+}
+
 inline void describe(const Plan &p, char *buf, size_t len) {
     std::snprintf(buf, len,
                   "fmt=%s tile=%dx%d threads=%d blocks_per_stage=%d lds=%lld grid=%lldx%lld k_steps=%lld "

@@ -98,6 +98,21 @@ int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out,
 int mmq_gemm_q4_K(const void *x_q8_1, const void *w_q4_K, float *out,
                   int64_t M, int64_t N, int64_t K, void *stream);
 
+/* Several GEMMs of one format that read the same q8_1 activations (the
+ * layer pipeline of "13 . r7-r8 raw-byte MMQ kernel": quantize once per
+ * distinct input, e.g. the q, k and v projections, or gate and up), computed
+ * by one launch whose grid covers the column tiles of all of them.
+ *   fmt: MMQ_FMT_Q8_0 or MMQ_FMT_Q4_K; count: 1..8;
+ *   x_q8_1: M x (K/32) q8_1 blocks, shared;
+ *   w[g]: N[g] x K weights of format fmt; out[g]: M x N[g] fp32 row-major,
+ *   fully overwritten; the arrays w, out and N are host memory (read during
+ *   the call), the tensors device memory.
+ * Each out[g] equals what mmq_gemm_q8_0 / mmq_gemm_q4_K would write for
+ * (x, w[g], N[g]), except that split-K is decided for the set as a whole.
+ * Refused (nothing launched) when any member would be refused. */
+int mmq_gemm_multi(int fmt, const void *x_q8_1, int count, const void *const *w, float *const *out,
+                   const int64_t *N, int64_t M, int64_t K, void *stream);
+
 /* Test entry: the exact int32 block dots I[m,n,b] through the same staging
  * and matrix-core code as the GEMM of format `fmt` (MMQ_FMT_Q8_0 or
  * MMQ_FMT_Q4_K), written to dots[(m*N + n)*(K/32) + b].  Same refusal rules

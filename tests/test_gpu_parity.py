@@ -243,6 +243,63 @@ def test_layer_gemm_set_sampled_rows(M):
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+@pytest.mark.parametrize("M,Ns,K", [(200, (384, 128, 130), 1024), (129, (257,), 512),
+                                     (2048, (3584, 512, 512), 3584), (512, (18944, 18944), 3584)])
+def test_gemm_multi_matches_oracle(fmt, M, Ns, K):
+    """One launch over several weight matrices sharing the q8_1 input: every
+    output within tolerance of the oracle (sampled rows at the large shapes),
+    every element written."""
+    _say(f"gemm multi fmt={fmt} M={M} Ns={Ns} K={K}")
+    x = inputs.activations(M, K, 70 + M)
+    xq = oracle.quantize_q8_1(x)
+    ws = [_weights(fmt, n, K, 80 + g) for g, n in enumerate(Ns)]
+    outs = [_nan_out(M, n) for n in Ns]
+    mmq.gemm_multi(fmt, _to_dev(xq), [_to_dev(w) for w in ws], list(Ns), M, K, outs)
+    torch.cuda.synchronize()
+    rows = list(range(M)) if M <= 256 else sorted({0, 1, M // 2, M - 128, M - 1})
+    sub = np.ascontiguousarray(xq[rows])
+    for g, (n, w) in enumerate(zip(Ns, ws)):
+        o = outs[g].cpu().numpy()
+        assert not np.isnan(o).any(), f"GEMM {g}: output element left unwritten"
+        rep = metrics.report(o[rows], _oracle_gemm(fmt, sub, w, len(rows), n, K))
+        _say(g, rep)
+        assert rep["normalized_max_error"] <= metrics.TOL
+
+
+def test_gemm_multi_unsplit_member_equals_single_launch():
+    """Without split-K a member of a set computes exactly what its own launch
+    computes (same tiles, same arithmetic)."""
+    M, K = 2048, 3584
+    Ns = (3584, 1024)
+    _say(f"gemm multi vs single M={M} Ns={Ns}")
+    assert _split_k(mmq.FMT_Q8_0, M, Ns[0], K) == 1
+    x = inputs.activations(M, K, 90)
+    xq = _to_dev(oracle.quantize_q8_1(x))
+    ws = [_to_dev(_weights(mmq.FMT_Q8_0, n, K, 91 + g)) for g, n in enumerate(Ns)]
+    outs = mmq.gemm_multi(mmq.FMT_Q8_0, xq, ws, list(Ns), M, K)
+    single = mmq.gemm_q8_0(xq, ws[0], M, Ns[0], K)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], single)
+
+
+def test_gemm_multi_refusals_leave_outputs_untouched():
+    _say("gemm multi refusals")
+    M, K = 64, 512
+    xq = _to_dev(oracle.quantize_q8_1(inputs.activations(M, K, 95)))
+    w = _to_dev(_weights(mmq.FMT_Q8_0, 256, K, 96))
+    outs = [_nan_out(M, 256), _nan_out(M, 256)]
+    with pytest.raises(mmq.MMQError, match="count"):
+        mmq.gemm_multi(mmq.FMT_Q8_0, xq, [w] * 9, [256] * 9, M, K, [_nan_out(M, 256) for _ in range(9)])
+    with pytest.raises(mmq.MMQError, match="multiple of 256"):
+        mmq.gemm_multi(mmq.FMT_Q8_0, xq, [w, w], [256, 256], M, K + 32, outs)
+    with pytest.raises(mmq.MMQError, match=">= 1"):
+        mmq.gemm_multi(mmq.FMT_Q8_0, xq, [w, w], [256, 0], M, K, outs)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.isnan(o).all()
+
+
 def test_nondefault_stream():
     _say("non-default stream")
     M, N, K = 96, 160, 512
