@@ -261,14 +261,18 @@ __device__ __forceinline__ ActDma act_dma_offsets(int kb, int wv, int lane) {
 
 template <int FMT>
 __device__ __forceinline__ void dma_activations(__amdgpu_buffer_rsrc_t rx, const ActDma &o, int ks, uint8_t *buf,
-                                                int wv) {
+                                                int wv, int piece) {
+    // piece 0, 1: the wave's two code slices; 2: its header slice; -1: all
     using L = Lds<FMT>;
     const int soff = ks * KB * 36;
 #pragma unroll
     for (int i = 0; i < 2; i++)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + (2 * wv + i) * 1024), 16, o.code_off[i], soff,
+        if (piece < 0 || piece == i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + (2 * wv + i) * 1024), 16, o.code_off[i],
+                                                     soff, 0, 0);
+    if (piece < 0 || piece == 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + L::OFF_A_HDR + wv * 256), 4, o.hdr_off, soff,
                                                  0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + L::OFF_A_HDR + wv * 256), 4, o.hdr_off, soff, 0, 0);
 }
 
 // Weights pass through registers instead (fetched one k-step ahead, stored
@@ -525,12 +529,12 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     };
 
     // Pipeline: step ks computes from buffer ks%2 (lds0 or lds1).  Meanwhile the DMA fills
-    // the other buffer with step ks+1's activations (issued at the top of the
-    // step), and the weight registers, fetched one step earlier, are stored
-    // into it at the end of the step; after the barrier they fetch step ks+2.
+    // the other buffer with step ks+1's activations, and the weight
+    // registers, fetched one step earlier, are stored into it; after the
+    // barrier they fetch step ks+2.
     // Buffer (ks+1)%2 was last read by step ks-1, which every wave finished
     // before the previous barrier.
-    dma_activations<FMT>(rx, adma, ks0, lds0, wv);
+    dma_activations<FMT>(rx, adma, ks0, lds0, wv, -1);
     load_w(ks0);
     store_w(ks0, lds0);
     if (nloc > 1) load_w(ks0 + 1);
@@ -542,7 +546,6 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
         const int ks = ks0 + j;                   // the k-step; j is its place in this workgroup's range
         uint8_t *const buf = P ? lds1 : lds0;     // local step j (j % 2 == P)
         uint8_t *const nxt = P ? lds0 : lds1;     // local step j + 1
-        if (j + 1 < nloc) dma_activations<FMT>(rx, adma, ks + 1, nxt, wv);
         const unsigned short *sHdr = reinterpret_cast<const unsigned short *>(buf + L::OFF_A_HDR);
         const uint8_t *sB = buf + L::OFF_B_CODES;
         const float2 *sW = reinterpret_cast<const float2 *>(buf + L::OFF_B_SCALE);
@@ -580,6 +583,14 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
             const int b = st / kNSub, c = st % kNSub;
             if (st + kPfB < kSteps) load_b(st + kPfB);
             if (c == 0 && b + 1 < KB) load_a(b + 1);
+            // The LDS writes for step ks+1 are spread over the sub-steps (the
+            // three DMA pieces at 1, 3 and 5, the weight stores at 6): issued
+            // together at the top or bottom of the step they were measured to
+            // cost 8-10 % more.
+            if (j + 1 < nloc) {
+                if ((st & 1) && st < 6) dma_activations<FMT>(rx, adma, ks + 1, nxt, wv, st >> 1);
+                if (st == 6) store_w(ks + 1, nxt);
+            }
             const i32x16 D = mfma_at(fa[b & 1], fb[st % kRing], srcC);
             const int col = b_col0 + 32 * c;
             if constexpr (DOTS) {
@@ -618,7 +629,6 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
                 acc[c] = __builtin_amdgcn_mfma_f32_32x32x8f16(sa, mb, acc[c], 0, 0, 0);
             }
         }
-        if (j + 1 < nloc) store_w(ks + 1, nxt);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // step ks+1's DMA has landed
         __syncthreads();
         if (j + 2 < nloc) load_w(ks + 2);
