@@ -444,6 +444,35 @@ __device__ __forceinline__ void scale_epilogue(f32x16 &acc, const i32x16 &D, flo
     fmac_row_bcast8<8>(acc, t, xsv);
 }
 
+// Output tile of this workgroup.  Workgroups reach the eight XCDs (each with
+// its own L2) round-robin by linear id, so neighbouring ids share no L2.
+// XCD k is therefore given a contiguous run of the tile sequence (k-th
+// eighth, linear id = 8q + k -> run position q), and the sequence walks
+// groups of kGroupRows row tiles column by column: an XCD's run is a compact
+// rectangle of tiles (4 x 14 at 2048 x 3584) whose A rows and B columns its
+// L2 serves to all of them.  Measured: Q4_K 2-3 % faster with it, Q8_0 2-3 %
+// slower (its weight stream is a third of Q4_K's per tile), so only Q4_K
+// remaps.
+constexpr int kXcds = 8, kGroupRows = 4;
+template <bool REMAP>
+__device__ __forceinline__ void tile_of_workgroup(int &tx, int &ty) {
+    if constexpr (!REMAP) {
+        tx = blockIdx.x;
+        ty = blockIdx.y;
+        return;
+    }
+    const int gx = gridDim.x, gy = gridDim.y, T = gx * gy;
+    const int L = blockIdx.y * gx + blockIdx.x;
+    const int k = L % kXcds, q = L / kXcds;
+    const int base = T / kXcds, rem = T % kXcds;
+    const int n = k * base + min(k, rem) + q;          // bijective on [0, T)
+    const int group = n / (kGroupRows * gx);
+    const int rows = min(kGroupRows, gy - group * kGroupRows);
+    const int idx = n - group * kGroupRows * gx;
+    ty = group * kGroupRows + idx % rows;
+    tx = idx / rows;
+}
+
 template <int P>
 struct Parity {
     static constexpr int value = P;
@@ -475,14 +504,16 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     const int lane = tid & 63, wv = tid >> 6;
     const int wr = wv >> 1, wc = wv & 1;          // wave tile: rows 32*wr.., columns 64*wc..
     const int g = lane >> 5, l32 = lane & 31;
+    int tx, ty;
+    tile_of_workgroup<FMT == FMT_Q4_K>(tx, ty);
     // which GEMM of the set this column tile belongs to (workgroup-uniform)
     int gi = 0;
     for (int i = 1; i < set.count; i++)
-        if (int(blockIdx.x) >= set.tile_start[i]) gi = i;
+        if (tx >= set.tile_start[i]) gi = i;
     const uint8_t *__restrict__ wq = set.w[gi];
     void *__restrict__ outp = set.out[gi];
     const int N = set.N[gi];
-    const int n0 = (int(blockIdx.x) - set.tile_start[gi]) * kTileN, m0 = blockIdx.y * kTileM;
+    const int n0 = (tx - set.tile_start[gi]) * kTileN, m0 = ty * kTileM;
     const int kb = K >> 5, nsteps = kb / KB;
     // this workgroup's k-steps: [ks0, ks0 + nloc) (all of them unless K is split)
     const int ks0 = blockIdx.z * steps_per_split;
