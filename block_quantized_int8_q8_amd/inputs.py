@@ -148,3 +148,22 @@ def layer_weight_seed(gemm: str) -> int:
 
 def layer_activation_seed(M: int, input_name: str) -> int:
     return seed_for(5, 100 + 4 * LAYER_M.index(M) + [n for n, _, _ in LAYER_INPUTS].index(input_name))
+
+
+# Indexed MoE (a Qwen3-30B-A3B-shaped layer: 128 experts, 8 per token,
+# hidden 2048, expert FFN 768).
+MOE_SHAPE = {"n_experts": 128, "topk": 8, "hidden": 2048, "ffn": 768}
+
+
+def moe_ids(T: int, n_experts: int, topk: int, seed: int, skew: float = 0.0) -> np.ndarray:
+    """int32 [T, topk]: topk distinct experts per token.  Expert e is drawn
+    with probability proportional to (e + 1) ** -skew (skew 0: uniform), by
+    Gumbel top-k sampling without replacement."""
+    if not 1 <= topk <= n_experts:
+        raise ValueError("need 1 <= topk <= n_experts")
+    r = np.random.default_rng(seed)
+    logp = -skew * np.log(np.arange(1, n_experts + 1, dtype=np.float64))
+    scores = logp[None, :] + r.gumbel(size=(T, n_experts))
+    ids = np.argpartition(-scores, topk - 1, axis=1)[:, :topk]
+    return ids.astype(np.int32)
+

@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_f32_to_f16.restype = ctypes.c_uint16
         L.oracle_f32_to_f16_array.argtypes = [p, p, i64]
         L.oracle_f16_to_f32_array.argtypes = [p, p, i64]
+        L.oracle_moe_gemm.argtypes = [i32, p, p, p, i32, p, i64, i64, i64, i32, i64, i64, i32]
+        L.oracle_moe_gemm.restype = i32
         L.oracle_quantize_q8_1.argtypes = [p, p, i64, i64]
         L.oracle_quantize_q8_1.restype = i32
         L.oracle_q4k_scale_min.argtypes = [p, i32, p, p]
@@ -189,6 +191,26 @@ def gemm_q4_K(x, w, M, N, K, nthreads: int = 0, rows=None) -> np.ndarray:
     if rc < 0:
         raise ValueError(f"bad shape ({rc})")
     return out
+
+
+def moe_gemm(fmt: int, x: np.ndarray, w: np.ndarray, ids: np.ndarray, topk: int, T: int, N: int, K: int,
+             n_experts: int, nthreads: int = 0, rows=None) -> np.ndarray:
+    """Indexed MoE (``oracle_moe_gemm``): out[r] = x[r // topk] times the
+    weights of expert ids[r] (experts stored one after another in ``w``).
+    ``rows`` selects routed rows (sorted); the result then holds only those."""
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)
+    R = T * topk
+    assert ids.size == R
+    out = np.zeros((R, N), dtype=np.float32)
+    spans = [(0, R)] if rows is None else [(int(r), int(r) + 1) for r in rows]
+    for r0, r1 in spans:
+        rc = lib().oracle_moe_gemm(fmt, _ptr(x), _ptr(w), _ptr(ids), topk, _ptr(out), T, N, K, n_experts,
+                                   r0, r1, nthreads)
+        if rc < 0:
+            raise ValueError(f"oracle_moe_gemm rejected the input ({rc})")
+    return out if rows is None else out[np.asarray(rows)]
 
 
 def threads_used(nthreads: int = 0) -> int:

@@ -439,3 +439,35 @@ int oracle_gemm_q4_K(const uint8_t *x, const uint8_t *w, float *out,
 {
     return oracle_gemm_q4_K_rows(x, w, out, M, N, K, 0, M, nthreads);
 }
+
+/* Indexed MoE ("13 . r7-r8 raw-byte MMQ kernel", the fused indexed-MoE
+ * prefill GEMM): routed row r = t*topk + j of out is token t's q8_1 row
+ * times the weights of expert ids[r], i.e. the dense GEMM row above with
+ * that expert's N x K matrix; experts are stored one after another.
+ * fmt 0 = Q8_0, 1 = Q4_K.  Rows [r0, r1) of out (T*topk x N) are written.
+ * Returns the thread count used, -2 on a bad shape, -3 on an expert id out
+ * of range. */
+int oracle_moe_gemm(int fmt, const uint8_t *x, const uint8_t *w, const int32_t *ids, int topk,
+                    float *out, int64_t T, int64_t N, int64_t K, int n_experts,
+                    int64_t r0, int64_t r1, int nthreads)
+{
+    if ((fmt != 0 && fmt != 1) || topk < 1 || n_experts < 1 || T < 0 || N < 0 || K < 0 ||
+        K % (fmt == 0 ? QK : QK_K) != 0 || r0 < 0 || r1 > T * topk || r0 > r1)
+        return -2;
+    for (int64_t r = r0; r < r1; r++)
+        if (ids[r] < 0 || ids[r] >= n_experts) return -3;
+    const int64_t kb = K / QK;
+    const int64_t wrow = fmt == 0 ? kb * Q8_0_BYTES : (K / QK_K) * Q4_K_BYTES;
+    int used = set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = r0; r < r1; r++) {
+        const uint8_t *xr = x + (r / topk) * kb * Q8_1_BYTES;
+        const uint8_t *we = w + (int64_t)ids[r] * N * wrow;
+        if (fmt == 0)
+            oracle_gemm_q8_0_rows(xr, we, out + r * N, 1, N, K, 0, 1, 1);
+        else
+            oracle_gemm_q4_K_rows(xr, we, out + r * N, 1, N, K, 0, 1, 1);
+    }
+    return used;
+}
+
