@@ -18,7 +18,8 @@ FMT_Q4_K = 1
 Q8_1_BYTES, Q8_0_BYTES, Q4_K_BYTES = 36, 34, 144
 
 EXPORTS = (
-    "mmq_quantize_q8_1", "mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_multi", "mmq_debug_block_dots",
+    "mmq_quantize_q8_1", "mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_multi", "mmq_moe_workspace_bytes",
+    "mmq_moe_gemm", "mmq_debug_block_dots",
     "mmq_last_error", "mmq_plan_describe", "mmq_plan_for_limits",
     "mmq_debug_set_extra_lds", "mmq_version",
 )
@@ -46,6 +47,10 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).restype = i32
         L.mmq_gemm_multi.argtypes = [i32, p, i32, p, p, p, i64, i64, p]
         L.mmq_gemm_multi.restype = i32
+        L.mmq_moe_workspace_bytes.argtypes = [i64, i32, i32]
+        L.mmq_moe_workspace_bytes.restype = i64
+        L.mmq_moe_gemm.argtypes = [i32, p, p, i32, p, i32, p, i64, i64, i64, p, i64, p]
+        L.mmq_moe_gemm.restype = i32
         L.mmq_debug_block_dots.argtypes = [i32, p, p, p, i64, i64, i64, p]
         L.mmq_debug_block_dots.restype = i32
         L.mmq_last_error.argtypes = []
@@ -130,6 +135,27 @@ def gemm_multi(fmt, xq, ws, Ns, M, K, outs=None, stream=None):
     npv = (ctypes.c_int64 * count)(*[int(n) for n in Ns])
     _check(lib().mmq_gemm_multi(fmt, _ptr(xq), count, wp, op, npv, M, K, _stream(stream)), "mmq_gemm_multi")
     return outs
+
+
+def moe_workspace_bytes(T, topk, n_experts) -> int:
+    """Device workspace bytes mmq_moe_gemm needs (-1 for arguments it refuses)."""
+    return int(lib().mmq_moe_workspace_bytes(T, topk, n_experts))
+
+
+def moe_gemm(fmt, xq, w, n_experts, ids, topk, T, N, K, out=None, workspace=None, stream=None):
+    """Indexed MoE: q8_1 [T, K/32, 36] x expert weights [E, N, ...] routed by
+    int32 ids [T, topk] -> fp32 [T*topk, N] (row t*topk + j = token t times
+    expert ids[t, j])."""
+    import torch
+    if out is None:
+        out = torch.empty((T * topk, N), dtype=torch.float32, device=xq.device)
+    need = moe_workspace_bytes(T, topk, n_experts)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=xq.device)
+    _check(lib().mmq_moe_gemm(fmt, _ptr(xq), _ptr(w), n_experts, _ptr(ids, torch.int32), topk,
+                              _ptr(out, torch.float32), T, N, K, _ptr(workspace, torch.uint8),
+                              workspace.numel(), _stream(stream)), "mmq_moe_gemm")
+    return out
 
 
 def debug_block_dots(fmt, xq, w, M, N, K, dots=None, stream=None):

@@ -21,6 +21,8 @@ namespace mmq {
 hipError_t launch_quantize(const float *x, void *y, int64_t M, int64_t K, int cu_count, hipStream_t stream);
 hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const void *x, const void *const *w,
                        void *const *out, const int64_t *N, int64_t M, int64_t K, bool dots, hipStream_t stream);
+hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t *ids, int topk, int n_experts,
+                      float *out, int64_t T, int64_t N, int64_t K, void *workspace, hipStream_t stream);
 }  // namespace mmq
 
 namespace {
@@ -152,6 +154,41 @@ int mmq_gemm_q4_K(const void *x_q8_1, const void *w_q4_K, float *out, int64_t M,
 int mmq_gemm_multi(int fmt, const void *x_q8_1, int count, const void *const *w, float *const *out,
                    const int64_t *N, int64_t M, int64_t K, void *stream) {
     return gemm_set(fmt, x_q8_1, count, w, reinterpret_cast<void *const *>(out), N, M, K, false, stream);
+}
+
+int64_t mmq_moe_workspace_bytes(int64_t T, int topk, int n_experts) {
+    if (T < 0 || topk < 1 || topk > mmq::kMoeMaxTopk || n_experts < 1 || n_experts > mmq::kMoeMaxExperts ||
+        T > INT32_MAX / topk)
+        return -1;
+    return mmq::moe_workspace_bytes(T * topk, n_experts);
+}
+
+int mmq_moe_gemm(int fmt, const void *x_q8_1, const void *w, int n_experts, const int32_t *ids, int topk,
+                 float *out, int64_t T, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,
+                 void *stream) {
+    g_err[0] = '\0';
+    if (!mmq::fmt_ok(fmt)) return refuse("unknown weight format %d", fmt);
+    if (!x_q8_1 || !w || !ids || !out || !workspace) return refuse("null pointer argument");
+    if (!aligned(x_q8_1, 16) || !aligned(w, 16)) return refuse("activation and weight pointers must be 16-byte aligned");
+    if (!aligned(ids, 4) || !aligned(out, 4)) return refuse("ids and output pointers must be 4-byte aligned");
+    if (!aligned(workspace, 16)) return refuse("workspace must be 16-byte aligned");
+    DeviceLimits L;
+    if (!current_limits(&L)) return 0;
+    if (!L.is_gfx950) return refuse("device is %s; this library is built for gfx950 only", L.arch);
+    mmq::Plan p;
+    char why[256];
+    if (!mmq::make_plan_moe(fmt, T, topk, n_experts, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), &p,
+                            why, sizeof(why)))
+        return refuse("%s MoE GEMM T=%lld topk=%d E=%d N=%lld K=%lld: %s", mmq::fmt_name(fmt), (long long)T, topk,
+                      n_experts, (long long)N, (long long)K, why);
+    const int64_t need = mmq::moe_workspace_bytes(T * topk, n_experts);
+    if (workspace_bytes < need)
+        return refuse("MoE workspace of %lld B given, %lld B needed", (long long)workspace_bytes, (long long)need);
+    (void)hipGetLastError();
+    const hipError_t e = mmq::launch_moe(p, x_q8_1, w, ids, topk, n_experts, out, T, N, K, workspace,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return refuse("%s MoE GEMM launch failed: %s", mmq::fmt_name(fmt), hipGetErrorString(e));
+    return 1;
 }
 
 int mmq_debug_block_dots(int fmt, const void *x_q8_1, const void *w, int32_t *dots, int64_t M, int64_t N,

@@ -1,9 +1,12 @@
 // mmq_kernels.hip -- gfx950 kernels of the block-quantized int8 MMQ library.
 //
 //   k_quantize_q8_1   fp32 -> q8_1, one pass over the activations (HBM-bound)
-//   k_mmq<FMT, DOTS>  q8_1 x {Q8_0, Q4_K} -> fp32 (or the raw int32 block
+//   k_mmq<FMT, DOTS, MOE>
+//                     q8_1 x {Q8_0, Q4_K} -> fp32 (or the raw int32 block
 //                     dots when DOTS), int8 MFMA with the per-block scale
-//                     applied in registers on the MFMA accumulator layout.
+//                     applied in registers on the MFMA accumulator layout;
+//                     MOE gathers the rows of each expert's routed tokens
+//   k_moe_route       expert routing for the MOE launch (counts, scan, scatter)
 //
 // The operation is the block-scaled contraction of "When the Product Won't
 // Collapse" (section 2) and, for Q4_K, the affine identity of "When Does a
@@ -259,6 +262,31 @@ __device__ __forceinline__ ActDma act_dma_offsets(int kb, int wv, int lane) {
     return o;
 }
 
+// The same slots for a gathered tile (indexed MoE): tile row i is sorted
+// routed row rbeg + i, whose activations are those of its token
+// (routed row / topk).  Rows at or past rend belong to no routed row: they
+// read token 0, which is in bounds, and are never stored.  Offsets stay
+// 32-bit: the launcher refuses activations of 2 GiB or more.
+__device__ __forceinline__ int gathered_row(const int32_t *__restrict__ sorted, int rbeg, int rend, int topk,
+                                            int i) {
+    const int p = rbeg + i;
+    return p < rend ? sorted[p] / topk : 0;
+}
+
+__device__ __forceinline__ ActDma act_dma_offsets_gather(int kb, int wv, int lane, const int32_t *__restrict__ sorted,
+                                                         int rbeg, int rend, int topk) {
+    ActDma o;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int s = 2 * wv + i, b = s >> 2;
+        const int tok = gathered_row(sorted, rbeg, rend, topk, 32 * (s & 3) + (lane >> 1));
+        o.code_off[i] = tok * kb * 36 + b * 36 + 4 + 16 * (lane & 1);
+    }
+    const int tok = gathered_row(sorted, rbeg, rend, topk, 16 * wv + (lane >> 2));
+    o.hdr_off = tok * kb * 36 + (lane & 3) * 36;
+    return o;
+}
+
 template <int FMT>
 __device__ __forceinline__ void dma_activations(__amdgpu_buffer_rsrc_t rx, const ActDma &o, int ks, uint8_t *buf,
                                                 int wv, int piece) {
@@ -489,9 +517,23 @@ struct GemmSet {
     void *out[kMaxGemms];
 };
 
-template <int FMT, bool DOTS>
+// Indexed MoE: the row tiles come from the routing kernel's table instead of
+// from blockIdx.y alone (row tile y = tiles[y]: expert, first sorted row, end
+// of the expert's sorted rows; expert -1 marks a spare tile), the activation
+// rows are gathered through the sorted routed-row ids, the weights are those
+// of the tile's expert (expert_bytes apart) and output row i of the tile is
+// routed row sorted[first + i].
+struct MoeArgs {
+    const int4 *tiles;
+    const int32_t *sorted;
+    int topk;
+    int64_t expert_bytes;
+};
+
+template <int FMT, bool DOTS, bool MOE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DOTS ? 2 : 4)))
-void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int steps_per_split) {
+void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int steps_per_split, const MoeArgs moe) {
+    static_assert(!(MOE && DOTS), "the block-dot output exists for plain GEMMs only");
     using L = Lds<FMT>;
     // The two k-step buffers are two LDS variables, not offsets into one
     // array: the compiler then knows that the DMA into one buffer cannot
@@ -505,7 +547,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     const int wr = wv >> 1, wc = wv & 1;          // wave tile: rows 32*wr.., columns 64*wc..
     const int g = lane >> 5, l32 = lane & 31;
     int tx, ty;
-    tile_of_workgroup<FMT == FMT_Q4_K>(tx, ty);
+    tile_of_workgroup<FMT == FMT_Q4_K && !MOE>(tx, ty);
     // which GEMM of the set this column tile belongs to (workgroup-uniform)
     int gi = 0;
     for (int i = 1; i < set.count; i++)
@@ -513,7 +555,13 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     const uint8_t *__restrict__ wq = set.w[gi];
     void *__restrict__ outp = set.out[gi];
     const int N = set.N[gi];
-    const int n0 = (tx - set.tile_start[gi]) * kTileN, m0 = ty * kTileM;
+    int4 mt = {0, 0, 0, 0};   // MoE row tile: expert, first sorted row, end of the expert's rows
+    if constexpr (MOE) {
+        mt = moe.tiles[ty];
+        if (mt.x < 0) return;   // a spare row tile (workgroup-uniform)
+        wq += int64_t(mt.x) * moe.expert_bytes;
+    }
+    const int n0 = (tx - set.tile_start[gi]) * kTileN, m0 = MOE ? 0 : ty * kTileM;
     const int kb = K >> 5, nsteps = kb / KB;
     // this workgroup's k-steps: [ks0, ks0 + nloc) (all of them unless K is split)
     const int ks0 = blockIdx.z * steps_per_split;
@@ -530,7 +578,8 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     const int b_lane = code_off(0, b_col0, g);        // are compile-time offsets from here
     // the activation row whose scale this lane holds for the row broadcasts
     const int xs_row = 32 * wr + 8 * ((lane & 15) >> 2) + (lane & 3) + 4 * g;
-    const ActDma adma = act_dma_offsets(kb, wv, lane);
+    const ActDma adma = MOE ? act_dma_offsets_gather(kb, wv, lane, moe.sorted, mt.y, mt.z, moe.topk)
+                            : act_dma_offsets(kb, wv, lane);
 
     i32x16 srcC;
 #pragma unroll
@@ -669,7 +718,23 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
         if (j + 1 < nloc) step(Parity<1>{}, j + 1);
     }
 
-    if constexpr (!DOTS) {
+    if constexpr (MOE) {
+        // scatter: tile row i -> routed row sorted[first + i]
+        float *out = reinterpret_cast<float *>(outp);
+        int64_t orow[16];
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int p = mt.y + 32 * wr + 8 * (r >> 2) + 4 * g + (r & 3);
+            orow[r] = p < mt.z ? int64_t(moe.sorted[p]) * N : -1;
+        }
+#pragma unroll
+        for (int c = 0; c < kNSub; c++) {
+            const int n = n0 + b_col0 + 32 * c;
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                if (orow[r] >= 0 && n < N) out[orow[r] + n] = acc[c][r];
+        }
+    } else if constexpr (!DOTS) {
         float *out = reinterpret_cast<float *>(outp);
         const bool split = gridDim.z > 1;   // partial sums: added into the zeroed output
 #pragma unroll
@@ -687,6 +752,80 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
             }
         }
     }
+}
+
+// Routing of the indexed MoE GEMM, one workgroup: count the routed rows of
+// each expert, scan the counts into row and tile offsets, scatter the routed
+// row ids into expert order and write the tile table (spare tiles: expert
+// -1).  Rows with an id outside [0, E) join no expert.  Within an expert the
+// order of rows depends on atomic timing; the GEMM's result does not (every
+// output row is computed on its own, in the same arithmetic wherever it sits).
+constexpr int kRouteThreads = 1024;
+static_assert(kMoeMaxExperts <= 2 * kRouteThreads, "each routing thread owns two experts");
+
+__global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__restrict__ ids, int R, int E,
+                                                             int max_tiles, int4 *__restrict__ tiles,
+                                                             int32_t *__restrict__ sorted) {
+    __shared__ int cnt[kMoeMaxExperts];
+    __shared__ int cursor[kMoeMaxExperts];
+    __shared__ int row_off[kMoeMaxExperts + 1];
+    __shared__ int tile_off[kMoeMaxExperts + 1];
+    __shared__ long long scan[kRouteThreads];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kRouteThreads) cnt[e] = 0;
+    __syncthreads();
+    for (int i = tid; i < R; i += kRouteThreads) {
+        const int e = ids[i];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    // exclusive scan of (rows, tiles) per expert, packed as rows + tiles * 2^32
+    // (rows <= R < 2^31, so the low half never carries); thread t owns
+    // experts 2t and 2t + 1
+    long long own[2], v = 0;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int e = 2 * tid + j;
+        const int c = e < E ? cnt[e] : 0;
+        own[j] = (long long)c + ((long long)((c + kTileM - 1) / kTileM) << 32);
+        v += own[j];
+    }
+    scan[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kRouteThreads; off <<= 1) {
+        const long long a = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += a;
+        __syncthreads();
+    }
+    long long ex = scan[tid] - v;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int e = 2 * tid + j;
+        if (e < E) {
+            row_off[e] = int(ex & 0xffffffffLL);
+            tile_off[e] = int(ex >> 32);
+            cursor[e] = row_off[e];
+        }
+        ex += own[j];
+    }
+    if (tid == kRouteThreads - 1) {
+        row_off[E] = int(scan[tid] & 0xffffffffLL);
+        tile_off[E] = int(scan[tid] >> 32);
+    }
+    __syncthreads();
+    for (int i = tid; i < R; i += kRouteThreads) {
+        const int e = ids[i];
+        if (e >= 0 && e < E) sorted[atomicAdd(&cursor[e], 1)] = i;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int e = 2 * tid + j;
+        if (e < E)
+            for (int t = tile_off[e]; t < tile_off[e + 1]; t++)
+                tiles[t] = make_int4(e, row_off[e] + kTileM * (t - tile_off[e]), row_off[e + 1], 0);
+    }
+    for (int t = tile_off[E] + tid; t < max_tiles; t += kRouteThreads) tiles[t] = make_int4(-1, 0, 0, 0);
 }
 
 // Zero an fp32 array (the output of a split-K launch, before the slices add
@@ -737,15 +876,50 @@ hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const vo
     const size_t lds = 0;
     if (p.fmt == FMT_Q8_0) {
         if (dots)
-            hipLaunchKernelGGL((k_mmq<FMT_Q8_0, true>), grid, block, lds, stream, xb, set, int(M), int(K), sps);
+            hipLaunchKernelGGL((k_mmq<FMT_Q8_0, true, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps,
+                               MoeArgs{});
         else
-            hipLaunchKernelGGL((k_mmq<FMT_Q8_0, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps);
+            hipLaunchKernelGGL((k_mmq<FMT_Q8_0, false, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps,
+                               MoeArgs{});
     } else {
         if (dots)
-            hipLaunchKernelGGL((k_mmq<FMT_Q4_K, true>), grid, block, lds, stream, xb, set, int(M), int(K), sps);
+            hipLaunchKernelGGL((k_mmq<FMT_Q4_K, true, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps,
+                               MoeArgs{});
         else
-            hipLaunchKernelGGL((k_mmq<FMT_Q4_K, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps);
+            hipLaunchKernelGGL((k_mmq<FMT_Q4_K, false, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps,
+                               MoeArgs{});
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t *ids, int topk, int n_experts,
+                      float *out, int64_t T, int64_t N, int64_t K, void *workspace, hipStream_t stream) {
+    const int64_t R = T * topk;
+    const int max_tiles = int(p.grid_y);
+    int4 *tiles = reinterpret_cast<int4 *>(workspace);
+    int32_t *sorted = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(workspace) + 16 * int64_t(max_tiles));
+    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(kRouteThreads), 0, stream, ids, int(R), n_experts, max_tiles,
+                       tiles, sorted);
+    GemmSet set{};
+    set.count = 1;
+    set.tile_start[0] = 0;
+    set.tile_start[1] = int(p.grid_x);
+    set.N[0] = int(N);
+    set.w[0] = reinterpret_cast<const uint8_t *>(w);
+    set.out[0] = out;
+    MoeArgs moe;
+    moe.tiles = tiles;
+    moe.sorted = sorted;
+    moe.topk = topk;
+    moe.expert_bytes = N * (p.fmt == FMT_Q8_0 ? (K / 32) * 34 : (K / 256) * 144);
+    const dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, 1);
+    const dim3 block(p.threads);
+    const auto *xb = reinterpret_cast<const uint8_t *>(x);
+    const int sps = int(p.steps_per_split);
+    if (p.fmt == FMT_Q8_0)
+        hipLaunchKernelGGL((k_mmq<FMT_Q8_0, false, true>), grid, block, 0, stream, xb, set, int(T), int(K), sps, moe);
+    else
+        hipLaunchKernelGGL((k_mmq<FMT_Q4_K, false, true>), grid, block, 0, stream, xb, set, int(T), int(K), sps, moe);
     return hipGetLastError();
 }
 

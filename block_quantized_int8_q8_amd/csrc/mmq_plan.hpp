@@ -141,6 +141,48 @@ inline bool make_plan_multi(int fmt, int64_t M, int count, const int64_t *Ns, in
     return make_plan(fmt, M, tiles * kTileN, K, lds_limit, cu_count, extra_lds, p, why, why_len);
 }
 
+// Indexed MoE ("When Does a Kernel Win Surface?", section 4.5, the fused
+// indexed-MoE prefill GEMM): routed row r = t * topk + j multiplies token t's activations
+// by the weights of expert ids[r].  The routed rows are grouped by expert
+// into 128-row tiles; every non-empty expert leaves at most one partial tile,
+// so floor(R / 128) + min(E, R) row tiles always suffice, and that is the
+// launch's grid y.  The workspace holds the tile table (one int4 per row
+// tile: expert, first sorted row, end of the expert's sorted rows, unused)
+// followed by the routed-row ids sorted by expert (int32 [R]).
+constexpr int kMoeMaxExperts = 2048;   // the routing kernel keeps its per-expert tables in LDS
+constexpr int kMoeMaxTopk = 64;
+
+inline int64_t moe_max_tiles(int64_t R, int64_t E) { return R / kTileM + (E < R ? E : R); }
+
+inline int64_t moe_workspace_bytes(int64_t R, int64_t E) {
+    if (R < 0 || E < 0) return -1;
+    return 16 * moe_max_tiles(R, E) + ((4 * R + 15) / 16) * 16;
+}
+
+inline bool make_plan_moe(int fmt, int64_t T, int topk, int n_experts, int64_t N, int64_t K, int64_t lds_limit,
+                          int cu_count, int64_t extra_lds, Plan *p, char *why, size_t why_len) {
+    auto fail = [&](const char *msg) {
+        if (why && why_len) std::snprintf(why, why_len, "%s", msg);
+        return false;
+    };
+    if (n_experts < 1 || n_experts > kMoeMaxExperts) return fail("n_experts must be 1..2048");
+    if (topk < 1 || topk > kMoeMaxTopk) return fail("topk must be 1..64");
+    if (T < 1) return fail("T (tokens) must be >= 1");
+    if (T > INT32_MAX / topk) return fail("T * topk (routed rows) must fit in int32");
+    Plan q;
+    if (!make_plan(fmt, T, N, K, lds_limit, cu_count, extra_lds, &q, why, why_len)) return false;
+    // the gathered activation rows are addressed by 32-bit byte offsets
+    // from the start of x
+    if (T * (K / 32) * 36 > int64_t(0x7fffffff)) return fail("activations must be under 2 GiB (32-bit offsets)");
+    const int64_t R = T * topk;
+    q.grid_y = moe_max_tiles(R, n_experts);
+    if (q.grid_y > 65535) return fail("too many row tiles for the launch grid (T * topk too large)");
+    q.split_k = 1;
+    q.steps_per_split = q.k_steps;
+    *p = q;
+    return true;
+}
+
 inline void describe(const Plan &p, char *buf, size_t len) {
     std::snprintf(buf, len,
                   "fmt=%s tile=%dx%d threads=%d blocks_per_stage=%d lds=%lld grid=%lldx%lld k_steps=%lld "

@@ -153,6 +153,19 @@ def layer_activation_seed(M: int, input_name: str) -> int:
 # Indexed MoE (a Qwen3-30B-A3B-shaped layer: 128 experts, 8 per token,
 # hidden 2048, expert FFN 768).
 MOE_SHAPE = {"n_experts": 128, "topk": 8, "hidden": 2048, "ffn": 768}
+MOE_T = 2048   # prefill tokens
+# The two expert GEMMs of the layer: gate and up fused into one N = 2 * ffn
+# matrix per expert, reading the T token rows (topk routed rows per token);
+# down reading the T * topk routed rows (one expert each, topk = 1).
+MOE_GEMMS = [  # (name, N, K, rows read per routed row: "token" or "routed")
+    ("gate_up", 2 * MOE_SHAPE["ffn"], MOE_SHAPE["hidden"], "token"),
+    ("down", MOE_SHAPE["hidden"], MOE_SHAPE["ffn"], "routed"),
+]
+
+
+def moe_seed(name: str) -> int:
+    """Seeds of the MoE layer's tensors: expert weights, activations, routing."""
+    return seed_for(6, ["ids", "gate_up_w", "down_w", "gate_up_x", "down_x"].index(name))
 
 
 def moe_ids(T: int, n_experts: int, topk: int, seed: int, skew: float = 0.0) -> np.ndarray:

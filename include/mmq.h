@@ -113,6 +113,39 @@ int mmq_gemm_q4_K(const void *x_q8_1, const void *w_q4_K, float *out,
 int mmq_gemm_multi(int fmt, const void *x_q8_1, int count, const void *const *w, float *const *out,
                    const int64_t *N, int64_t M, int64_t K, void *stream);
 
+/* Bytes of device workspace mmq_moe_gemm needs for T tokens routed to topk
+ * experts each among n_experts: a tile table (16 B per possible 128-row
+ * tile, floor(T*topk/128) + min(n_experts, T*topk) of them) and the routed
+ * row ids sorted by expert (4 B each).  -1 for arguments mmq_moe_gemm
+ * refuses outright (topk outside 1..64, n_experts outside 1..2048, T < 0). */
+int64_t mmq_moe_workspace_bytes(int64_t T, int topk, int n_experts);
+
+/* Indexed-MoE GEMM ("When Does a Kernel Win Surface?", section 4.5, the fused
+ * indexed-MoE prefill GEMM): each token's q8_1 activation row is multiplied
+ * by the weights of each of the topk experts it was routed to, all in one
+ * launch, with every 128-row tile holding rows of a single expert.
+ *   x_q8_1: T x (K/32) q8_1 blocks (device);
+ *   w: n_experts weight matrices of format fmt stored one after another,
+ *      each N x K (N rows of K/32 Q8_0 blocks or K/256 Q4_K super-blocks,
+ *      the layout mmq_gemm_q8_0 / mmq_gemm_q4_K take) (device);
+ *   ids: int32 [T][topk] expert ids (device); routed row r = t*topk + j is
+ *      token t times expert ids[r];
+ *   out: (T*topk) x N fp32 row-major (device); row r is routed row r.
+ *   workspace: at least mmq_moe_workspace_bytes(T, topk, n_experts) bytes of
+ *      16-byte aligned device memory, caller-owned; its contents on entry do
+ *      not matter and on return are the routing tables.
+ * Row r of out equals mmq_gemm_q8_0 / mmq_gemm_q4_K's row for token t and
+ * expert ids[r]'s matrix (bit-identical for Q8_0: the same arithmetic in the
+ * same order).  A routed row whose id is outside [0, n_experts) is not
+ * computed and its row of out is left as it was.  The routing runs on the
+ * device (a kernel on `stream` before the GEMM): the ids never visit the
+ * host.  Requires K % 256 == 0, 1 <= topk <= 64, 1 <= n_experts <= 2048,
+ * T*topk < 2^31 and x under 2 GiB.  Two calls on one stream may share a
+ * workspace; calls that overlap in time may not. */
+int mmq_moe_gemm(int fmt, const void *x_q8_1, const void *w, int n_experts, const int32_t *ids, int topk,
+                 float *out, int64_t T, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,
+                 void *stream);
+
 /* Test entry: the exact int32 block dots I[m,n,b] through the same staging
  * and matrix-core code as the GEMM of format `fmt` (MMQ_FMT_Q8_0 or
  * MMQ_FMT_Q4_K), written to dots[(m*N + n)*(K/32) + b].  Same refusal rules

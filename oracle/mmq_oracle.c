@@ -440,8 +440,8 @@ int oracle_gemm_q4_K(const uint8_t *x, const uint8_t *w, float *out,
     return oracle_gemm_q4_K_rows(x, w, out, M, N, K, 0, M, nthreads);
 }
 
-/* Indexed MoE ("13 . r7-r8 raw-byte MMQ kernel", the fused indexed-MoE
- * prefill GEMM): routed row r = t*topk + j of out is token t's q8_1 row
+/* Indexed MoE ("When Does a Kernel Win Surface?", section 4.5, the fused
+ * indexed-MoE prefill GEMM): routed row r = t*topk + j of out is token t's q8_1 row
  * times the weights of expert ids[r], i.e. the dense GEMM row above with
  * that expert's N x K matrix; experts are stored one after another.
  * fmt 0 = Q8_0, 1 = Q4_K.  Rows [r0, r1) of out (T*topk x N) are written.

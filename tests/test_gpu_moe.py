@@ -1,0 +1,152 @@
+"""GPU parity of the indexed-MoE GEMM ("When Does a Kernel Win Surface?",
+section 4.5): mmq_moe_gemm against the oracle's oracle_moe_gemm on the same
+seeded inputs.
+
+Bars as for the dense GEMM: normalized error <= 1e-5, and Q8_0 bit-identical
+(every routed row is computed by the dense kernel's arithmetic in its order,
+wherever the routing places it).  Outputs start as a NaN sentinel, so a
+routed row the kernel never wrote fails."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_int8_q8_amd as mmq
+import oracle
+from block_quantized_int8_q8_amd import inputs
+from tests import metrics
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _weights(fmt, E, N, K, seed):
+    f = inputs.q8_0_weights if fmt == mmq.FMT_Q8_0 else inputs.q4_K_weights
+    return f(E * N, K, seed)   # E matrices of N rows, one after another
+
+
+def _run(fmt, xq, w, E, ids, topk, T, N, K, out=None):
+    if out is None:
+        out = torch.full((T * topk, N), float("nan"), dtype=torch.float32, device=DEV)
+    mmq.moe_gemm(fmt, _dev(xq), _dev(w), E, _dev(ids.astype(np.int32)), topk, T, N, K, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _check(fmt, got, ref):
+    assert not np.isnan(got).any(), "routed row left unwritten"
+    rep = metrics.report(got, ref)
+    _say(rep)
+    assert rep["normalized_max_error"] <= metrics.TOL
+    if fmt == mmq.FMT_Q8_0:
+        assert rep["bit_identical_fraction"] == 1.0
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+@pytest.mark.parametrize("T,E,topk,N,K,skew", [
+    (37, 8, 3, 200, 512, 0.0),      # ragged N, several experts per tile row
+    (300, 16, 4, 130, 1024, 2.0),   # skewed: popular experts span several 128-row tiles
+    (1, 8, 2, 256, 256, 0.0),       # one token (decode-sized)
+    (129, 4, 4, 257, 768, 0.0),     # every token routed to every expert
+    (700, 3, 1, 384, 256, 0.0),     # topk 1: plain row gather
+])
+def test_moe_matches_oracle(fmt, T, E, topk, N, K, skew):
+    _say(f"moe fmt={fmt} T={T} E={E} topk={topk} N={N} K={K} skew={skew}")
+    xq = oracle.quantize_q8_1(inputs.activations(T, K, 50 + T))
+    w = _weights(fmt, E, N, K, 60 + N)
+    ids = inputs.moe_ids(T, E, topk, 70 + T, skew=skew)
+    got = _run(fmt, xq, w, E, ids, topk, T, N, K)
+    _check(fmt, got, oracle.moe_gemm(fmt, xq, w, ids, topk, T, N, K, E, nthreads=16))
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+def test_moe_one_expert_takes_all(fmt):
+    """All 300 routed rows on expert 2 of 5 (three row tiles, one partial);
+    the other experts empty."""
+    T, E, topk, N, K = 300, 5, 1, 192, 512
+    _say(f"moe one expert fmt={fmt}")
+    xq = oracle.quantize_q8_1(inputs.activations(T, K, 81))
+    w = _weights(fmt, E, N, K, 82)
+    ids = np.full((T, topk), 2, np.int32)
+    got = _run(fmt, xq, w, E, ids, topk, T, N, K)
+    _check(fmt, got, oracle.moe_gemm(fmt, xq, w, ids, topk, T, N, K, E, nthreads=16))
+    # equal to the dense GEMM with expert 2's matrix
+    wrow = w.reshape(E, N, *w.shape[1:])[2]
+    dense = (mmq.gemm_q8_0 if fmt == mmq.FMT_Q8_0 else mmq.gemm_q4_K)(_dev(xq), _dev(wrow), T, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.view(np.uint32), dense.cpu().numpy().view(np.uint32))
+
+
+def test_moe_out_of_range_ids_leave_rows_untouched():
+    fmt, T, E, topk, N, K = mmq.FMT_Q8_0, 90, 6, 2, 160, 256
+    _say("moe out-of-range ids")
+    xq = oracle.quantize_q8_1(inputs.activations(T, K, 91))
+    w = _weights(fmt, E, N, K, 92)
+    ids = inputs.moe_ids(T, E, topk, 93)
+    bad = np.zeros(T * topk, bool)
+    bad[[0, 5, 17, 179]] = True
+    ids_bad = ids.reshape(-1).copy()
+    ids_bad[[0, 5]] = -1
+    ids_bad[[17, 179]] = E
+    got = _run(fmt, xq, w, E, ids_bad.reshape(T, topk), topk, T, N, K)
+    assert np.isnan(got[bad]).all()
+    ref = oracle.moe_gemm(fmt, xq, w, ids, topk, T, N, K, E, nthreads=16)
+    _check(fmt, got[~bad], ref[~bad])
+
+
+def test_moe_workspace_reuse_and_refusals():
+    fmt, E, N, K = mmq.FMT_Q8_0, 8, 128, 256
+    _say("moe workspace reuse / refusals")
+    big_T, small_T, topk = 400, 33, 2
+    ws = torch.empty((mmq.moe_workspace_bytes(big_T, topk, E),), dtype=torch.uint8, device=DEV)
+    w = _weights(fmt, E, N, K, 101)
+    for T in (big_T, small_T):   # the second call reuses the first call's routing tables
+        xq = oracle.quantize_q8_1(inputs.activations(T, K, 102 + T))
+        ids = inputs.moe_ids(T, E, topk, 103 + T)
+        out = torch.full((T * topk, N), float("nan"), dtype=torch.float32, device=DEV)
+        mmq.moe_gemm(fmt, _dev(xq), _dev(w), E, _dev(ids), topk, T, N, K, out, workspace=ws)
+        torch.cuda.synchronize()
+        _check(fmt, out.cpu().numpy(), oracle.moe_gemm(fmt, xq, w, ids, topk, T, N, K, E, nthreads=16))
+    # refusals launch nothing
+    T = small_T
+    xq = _dev(oracle.quantize_q8_1(inputs.activations(T, K, 104)))
+    ids = _dev(inputs.moe_ids(T, E, topk, 105))
+    out = torch.full((T * topk, N), float("nan"), dtype=torch.float32, device=DEV)
+    short = torch.empty((mmq.moe_workspace_bytes(T, topk, E) - 16,), dtype=torch.uint8, device=DEV)
+    for kw, args in [({"workspace": short}, (E, topk, K)), ({}, (0, topk, K)), ({}, (E, 0, K)),
+                     ({}, (E, topk, 320)), ({}, (4096, topk, K))]:
+        e, k_top, kk = args
+        with pytest.raises(mmq.MMQError):
+            mmq.moe_gemm(fmt, xq, _dev(w), e, ids, k_top, T, N, kk, out, **kw)
+    torch.cuda.synchronize()
+    assert np.isnan(out.cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+@pytest.mark.parametrize("gemm", [g[0] for g in inputs.MOE_GEMMS])
+def test_moe_full_size_sampled_rows(fmt, gemm):
+    """The Qwen3-30B-A3B-shaped layer (128 experts, 8 per token, 2048
+    tokens) at full size, on routed rows sampled across the output."""
+    name, N, K, rows_from = next(g for g in inputs.MOE_GEMMS if g[0] == gemm)
+    E, topk, T = inputs.MOE_SHAPE["n_experts"], inputs.MOE_SHAPE["topk"], inputs.MOE_T
+    ids = inputs.moe_ids(T, E, topk, inputs.moe_seed("ids"))
+    if rows_from == "routed":   # down: one activation row per routed row, topk 1
+        T, topk, ids = T * topk, 1, ids.reshape(-1, 1)
+    _say(f"moe full size fmt={fmt} {name} T={T} topk={topk} N={N} K={K}")
+    xq = oracle.quantize_q8_1(inputs.activations(T, K, inputs.moe_seed(f"{name}_x")))
+    w = _weights(fmt, E, N, K, inputs.moe_seed(f"{name}_w"))
+    got = _run(fmt, xq, w, E, ids, topk, T, N, K)
+    assert not np.isnan(got).any(), "routed row left unwritten"
+    rows = np.unique(np.random.default_rng(7).integers(0, T * topk, size=48))
+    ref = oracle.moe_gemm(fmt, xq, w, ids, topk, T, N, K, E, nthreads=16, rows=rows)
+    _check(fmt, got[rows], ref)

@@ -1,5 +1,5 @@
-"""Pins of the oracle's indexed-MoE GEMM ("13 . r7-r8 raw-byte MMQ kernel",
-fused indexed-MoE prefill GEMM: each routed row is its token's activations
+"""Pins of the oracle's indexed-MoE GEMM ("When Does a Kernel Win Surface?",
+section 4.5, fused indexed-MoE prefill GEMM: each routed row is its token's activations
 times the weights of the expert it was routed to).
 
 The MoE-specific part of the oracle is indexing (token = r // topk, expert =
