@@ -224,6 +224,95 @@ def time_layer(M: int, steps: int, warmup: int, check: bool = True):
     }
 
 
+def time_moe(fmt_name: str, steps: int, warmup: int, check: bool = True):
+    """The expert GEMMs of one Qwen3-30B-A3B-shaped MoE layer (128 experts,
+    8 per token) at 2048 prefill tokens, in one format: quantize the token
+    rows, the gate+up indexed GEMM (routing included), quantize the routed
+    rows' down-projection input, the down indexed GEMM.  The routing is
+    seeded top-8 over uniform expert scores; the down input is synthetic
+    (the activation function between the two GEMMs is not part of the
+    path).  `moe_ms` is per indexed GEMM, routing kernel included."""
+    import torch
+    import block_quantized_int8_q8_amd as mmq
+    from block_quantized_int8_q8_amd import inputs
+
+    dev = torch.device("cuda:0")
+    fmt = mmq.FMT_Q8_0 if fmt_name == "q8_0" else mmq.FMT_Q4_K
+    wgen = inputs.q8_0_weights if fmt == mmq.FMT_Q8_0 else inputs.q4_K_weights
+    E, topk0, T0 = inputs.MOE_SHAPE["n_experts"], inputs.MOE_SHAPE["topk"], inputs.MOE_T
+    ids0 = inputs.moe_ids(T0, E, topk0, inputs.moe_seed("ids"))
+    stream = torch.cuda.current_stream()
+    legs = []
+    for name, N, K, rows_from in inputs.MOE_GEMMS:
+        T, topk, ids = (T0, topk0, ids0) if rows_from == "token" else (T0 * topk0, 1, ids0.reshape(-1, 1))
+        x = inputs.activations(T, K, inputs.moe_seed(f"{name}_x"))
+        w = wgen(E * N, K, inputs.moe_seed(f"{name}_w"))
+        legs.append({
+            "name": name, "T": T, "topk": topk, "N": N, "K": K, "x_host": x, "w_host": w, "ids_host": ids,
+            "x": torch.from_numpy(x).to(dev), "xq": torch.empty((T, K // 32, 36), dtype=torch.uint8, device=dev),
+            "w": torch.from_numpy(w).to(dev), "ids": torch.from_numpy(np.ascontiguousarray(ids)).to(dev),
+            "out": torch.full((T * topk, N), float("nan"), dtype=torch.float32, device=dev),
+            "ws": torch.empty((mmq.moe_workspace_bytes(T, topk, E),), dtype=torch.uint8, device=dev),
+        })
+
+    def step(ev=None):
+        for i, g in enumerate(legs):
+            mmq.quantize_q8_1(g["x"], g["xq"], stream=stream)
+            if ev is not None:
+                ev[i][0].record(stream)
+            mmq.moe_gemm(fmt, g["xq"], g["w"], E, g["ids"], g["topk"], g["T"], g["N"], g["K"], g["out"],
+                         workspace=g["ws"], stream=stream)
+            if ev is not None:
+                ev[i][1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    parity = None
+    if check:
+        import oracle
+        from tests import metrics
+        worst, unwritten = 0.0, 0
+        for g in legs:
+            o = g["out"].cpu().numpy()
+            unwritten += int(np.isnan(o).sum())
+            R = g["T"] * g["topk"]
+            rows = [0, R // 3, R // 2, R - 1]
+            toks = sorted({r // g["topk"] for r in rows})
+            xq = oracle.quantize_q8_1(g["x_host"][toks])
+            # the sampled tokens re-indexed 0..len(toks)-1 with all their routed rows
+            sub_ids = g["ids_host"][toks]
+            ref = oracle.moe_gemm(fmt, xq, g["w_host"], sub_ids, g["topk"], len(toks), g["N"], g["K"], E)
+            got = np.concatenate([o[t * g["topk"]:(t + 1) * g["topk"]] for t in toks])
+            worst = max(worst, metrics.normalized_max_error(got, ref))
+        parity = {"tokens_checked_per_gemm": 4, "unwritten": unwritten, "normalized_max_error": worst,
+                  "ok": bool(unwritten == 0 and worst <= metrics.TOL)}
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in legs] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        step(ev[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(end) / steps
+    moe_ms = {g["name"]: float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)]))
+              for j, g in enumerate(legs)}
+    ops = {g["name"]: 2.0 * g["T"] * g["topk"] * g["N"] * g["K"] for g in legs}
+    wbytes = {g["name"]: float(g["w_host"].nbytes) for g in legs}
+    return {
+        "format": fmt_name.upper(), "tokens": T0, "experts": E, "topk": topk0,
+        "ms_per_layer": step_ms,
+        "tops_layer": sum(ops.values()) / (step_ms * 1e-3) / 1e12,
+        "moe_ms": moe_ms,
+        "moe_tops": {k: ops[k] / (moe_ms[k] * 1e-3) / 1e12 for k in moe_ms},
+        # every expert's weights are read at least once per launch
+        "expert_weight_gbs": {k: wbytes[k] / (moe_ms[k] * 1e-3) / 1e9 for k in moe_ms},
+        "parity": parity,
+    }
+
+
 def cpu_baseline(cfg: int, target_s: float = 15.0):
     """The oracle (quantize + GEMM) on a bounded row sample of the same
     workload, on the host cores; scaled to TOP/s of that sample."""
@@ -262,6 +351,8 @@ def main():
     ap.add_argument("--extra-configs", default="3,4", help="other shapes timed in the same run")
     ap.add_argument("--layer-m", default="512,2048,8192",
                     help="token counts at which the 7B layer GEMM set is timed ('' for none)")
+    ap.add_argument("--moe", default="q4_K,q8_0",
+                    help="weight formats of the timed 128-expert MoE layer ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -301,6 +392,9 @@ def main():
 
     for m in [int(v) for v in args.layer_m.split(",") if v.strip()]:
         extra[f"layer_M{m}"] = time_layer(m, max(3, args.steps // 10), 1, check=not args.no_check)
+
+    for f in [v.strip() for v in args.moe.split(",") if v.strip()]:
+        extra[f"moe_{f}"] = time_moe(f, max(3, args.steps // 5), 1, check=not args.no_check)
 
     kname = "k_mmq<Q8_0>" if main_rec["fmt"] == "q8_0" else "k_mmq<Q4_K>"
     achieved = main_rec["gemm_tops"]

@@ -760,8 +760,28 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
 // -1).  Rows with an id outside [0, E) join no expert.  Within an expert the
 // order of rows depends on atomic timing; the GEMM's result does not (every
 // output row is computed on its own, in the same arithmetic wherever it sits).
-constexpr int kRouteThreads = 1024;
+//
+// The kernel is latency-bound (16 K ids are 64 KiB): each thread loads its
+// kRouteIds ids of a chunk with independent loads before it uses any, so a
+// chunk costs one memory latency, and the scan runs in registers within each
+// wave (row broadcasts by shuffle) with one LDS exchange of wave totals.
+constexpr int kRouteThreads = 1024, kRouteWaves = kRouteThreads / 64, kRouteIds = 16;
 static_assert(kMoeMaxExperts <= 2 * kRouteThreads, "each routing thread owns two experts");
+
+template <typename F>
+__device__ __forceinline__ void for_each_routed_row(const int32_t *__restrict__ ids, int R, int E, F &&f) {
+    for (int base = 0; base < R; base += kRouteThreads * kRouteIds) {
+        int e[kRouteIds];
+#pragma unroll
+        for (int j = 0; j < kRouteIds; j++) {
+            const int i = base + j * kRouteThreads + int(threadIdx.x);
+            e[j] = i < R ? ids[i] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < kRouteIds; j++)
+            if (e[j] >= 0 && e[j] < E) f(base + j * kRouteThreads + int(threadIdx.x), e[j]);
+    }
+}
 
 __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__restrict__ ids, int R, int E,
                                                              int max_tiles, int4 *__restrict__ tiles,
@@ -770,14 +790,11 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__re
     __shared__ int cursor[kMoeMaxExperts];
     __shared__ int row_off[kMoeMaxExperts + 1];
     __shared__ int tile_off[kMoeMaxExperts + 1];
-    __shared__ long long scan[kRouteThreads];
-    const int tid = threadIdx.x;
+    __shared__ long long wave_sum[kRouteWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     for (int e = tid; e < E; e += kRouteThreads) cnt[e] = 0;
     __syncthreads();
-    for (int i = tid; i < R; i += kRouteThreads) {
-        const int e = ids[i];
-        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-    }
+    for_each_routed_row(ids, R, E, [&](int, int e) { atomicAdd(&cnt[e], 1); });
     __syncthreads();
     // exclusive scan of (rows, tiles) per expert, packed as rows + tiles * 2^32
     // (rows <= R < 2^31, so the low half never carries); thread t owns
@@ -790,15 +807,16 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__re
         own[j] = (long long)c + ((long long)((c + kTileM - 1) / kTileM) << 32);
         v += own[j];
     }
-    scan[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kRouteThreads; off <<= 1) {
-        const long long a = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += a;
-        __syncthreads();
+    long long inc = v;   // inclusive scan within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const long long a = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += a;
     }
-    long long ex = scan[tid] - v;
+    if (lane == 63) wave_sum[wv] = inc;
+    __syncthreads();
+    long long ex = inc - v;
+    for (int w = 0; w < wv; w++) ex += wave_sum[w];
 #pragma unroll
     for (int j = 0; j < 2; j++) {
         const int e = 2 * tid + j;
@@ -809,15 +827,12 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__re
         }
         ex += own[j];
     }
-    if (tid == kRouteThreads - 1) {
-        row_off[E] = int(scan[tid] & 0xffffffffLL);
-        tile_off[E] = int(scan[tid] >> 32);
+    if (tid == kRouteThreads - 1) {   // ex is now the total over all experts
+        row_off[E] = int(ex & 0xffffffffLL);
+        tile_off[E] = int(ex >> 32);
     }
     __syncthreads();
-    for (int i = tid; i < R; i += kRouteThreads) {
-        const int e = ids[i];
-        if (e >= 0 && e < E) sorted[atomicAdd(&cursor[e], 1)] = i;
-    }
+    for_each_routed_row(ids, R, E, [&](int i, int e) { sorted[atomicAdd(&cursor[e], 1)] = i; });
 #pragma unroll
     for (int j = 0; j < 2; j++) {
         const int e = 2 * tid + j;
