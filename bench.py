@@ -224,6 +224,80 @@ def time_layer(M: int, steps: int, warmup: int, check: bool = True):
     }
 
 
+def time_decode(M: int, fmt_name: str, steps: int, warmup: int, check: bool = True):
+    """The 7B layer's projections at decode size (M <= 8 tokens), one format:
+    one quantize per distinct input and one matvec launch per input group
+    (q+k+v, o, gate+up, down).  The matvec streams every weight byte once,
+    so its roofline is HBM: `weight_gbs` is weight bytes / GEMM time."""
+    import torch
+    import block_quantized_int8_q8_amd as mmq
+    from block_quantized_int8_q8_amd import inputs
+
+    dev = torch.device("cuda:0")
+    fmt = mmq.FMT_Q8_0 if fmt_name == "q8_0" else mmq.FMT_Q4_K
+    wgen = inputs.q8_0_weights if fmt == mmq.FMT_Q8_0 else inputs.q4_K_weights
+    shapes = {g: (n, k) for g, n, k in inputs.LAYER_7B}
+    stream = torch.cuda.current_stream()
+    groups = []
+    for name, K, gemms in inputs.LAYER_INPUTS:
+        x = inputs.activations(M, K, inputs.layer_activation_seed(2048, name))
+        ws_host = [wgen(shapes[g][0], K, inputs.layer_weight_seed(g)) for g in gemms]
+        groups.append({
+            "gemms": gemms, "K": K, "Ns": [shapes[g][0] for g in gemms], "x_host": x, "w_host": ws_host,
+            "x": torch.from_numpy(x).to(dev), "xq": torch.empty((M, K // 32, 36), dtype=torch.uint8, device=dev),
+            "w": [torch.from_numpy(w).to(dev) for w in ws_host],
+            "out": [torch.full((M, shapes[g][0]), float("nan"), dtype=torch.float32, device=dev) for g in gemms],
+        })
+
+    def step(ev=None):
+        for i, g in enumerate(groups):
+            mmq.quantize_q8_1(g["x"], g["xq"], stream=stream)
+            if ev is not None:
+                ev[i][0].record(stream)
+            mmq.gemm_multi(fmt, g["xq"], g["w"], g["Ns"], M, g["K"], g["out"], stream=stream)
+            if ev is not None:
+                ev[i][1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    parity = None
+    if check:
+        import oracle
+        from tests import metrics
+        worst, unwritten = 0.0, 0
+        f = oracle.gemm_q8_0 if fmt == mmq.FMT_Q8_0 else oracle.gemm_q4_K
+        for g in groups:
+            xq = oracle.quantize_q8_1(g["x_host"])
+            for n, w, o in zip(g["Ns"], g["w_host"], g["out"]):
+                o = o.cpu().numpy()
+                unwritten += int(np.isnan(o).sum())
+                worst = max(worst, metrics.normalized_max_error(o, f(xq, w, M, n, g["K"], nthreads=16)))
+        parity = {"outputs_checked": "all", "unwritten": unwritten, "normalized_max_error": worst,
+                  "ok": bool(unwritten == 0 and worst <= metrics.TOL)}
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in groups] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        step(ev[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(end) / steps
+    gemm_ms = {"+".join(g["gemms"]): float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)]))
+               for j, g in enumerate(groups)}
+    wbytes = {"+".join(g["gemms"]): float(sum(w.nbytes for w in g["w_host"])) for g in groups}
+    return {
+        "format": fmt_name.upper(), "M": M, "ms_per_layer": step_ms,
+        "weight_bytes": sum(wbytes.values()),
+        "gemm_ms": gemm_ms,
+        "weight_gbs": {k: wbytes[k] / (gemm_ms[k] * 1e-3) / 1e9 for k in gemm_ms},
+        "weight_gbs_all_gemms": sum(wbytes.values()) / (sum(gemm_ms.values()) * 1e-3) / 1e9,
+        "parity": parity,
+    }
+
+
 def time_moe(fmt_name: str, steps: int, warmup: int, check: bool = True):
     """The expert GEMMs of one Qwen3-30B-A3B-shaped MoE layer (128 experts,
     8 per token) at 2048 prefill tokens, in one format: quantize the token
@@ -351,6 +425,8 @@ def main():
     ap.add_argument("--extra-configs", default="3,4", help="other shapes timed in the same run")
     ap.add_argument("--layer-m", default="512,2048,8192",
                     help="token counts at which the 7B layer GEMM set is timed ('' for none)")
+    ap.add_argument("--decode", default="q4_K:1,q8_0:1,q4_K:8",
+                    help="format:M pairs of the timed decode-size layer ('' for none)")
     ap.add_argument("--moe", default="q4_K,q8_0",
                     help="weight formats of the timed 128-expert MoE layer ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -392,6 +468,10 @@ def main():
 
     for m in [int(v) for v in args.layer_m.split(",") if v.strip()]:
         extra[f"layer_M{m}"] = time_layer(m, max(3, args.steps // 10), 1, check=not args.no_check)
+
+    for spec in [v.strip() for v in args.decode.split(",") if v.strip()]:
+        f, m = spec.split(":")
+        extra[f"decode_{f}_M{m}"] = time_decode(int(m), f, max(10, args.steps), 2, check=not args.no_check)
 
     for f in [v.strip() for v in args.moe.split(",") if v.strip()]:
         extra[f"moe_{f}"] = time_moe(f, max(3, args.steps // 5), 1, check=not args.no_check)

@@ -106,8 +106,9 @@ int gemm_set(int fmt, const void *x, int count, const void *const *w, void *cons
     mmq::Plan p;
     int tile_start[mmq::kMaxGemms + 1];
     char why[256];
+    // the block-dot output exists for the MMQ kernel only
     if (!mmq::make_plan_multi(fmt, M, count, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), &p, tile_start,
-                              why, sizeof(why)))
+                              why, sizeof(why), !dots))
         return refuse("%s GEMM M=%lld N=%lld K=%lld%s: %s", mmq::fmt_name(fmt), (long long)M, (long long)N[0],
                       (long long)K, count > 1 ? " (first of a set)" : "", why);
     (void)hipGetLastError();   // a stale error must not be blamed on this launch

@@ -7,6 +7,8 @@
 //                     applied in registers on the MFMA accumulator layout;
 //                     MOE gathers the rows of each expert's routed tokens
 //   k_moe_route       expert routing for the MOE launch (counts, scan, scatter)
+//   k_mmv<FMT>        the same contraction for a few activation rows
+//                     (decode): VALU int8 dot products at the HBM roofline
 //
 // The operation is the block-scaled contraction of "When the Product Won't
 // Collapse" (section 2) and, for Q4_K, the affine identity of "When Does a
@@ -754,6 +756,186 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-vector kernel for a few activation rows (decode, M <= kMvMaxM): the
+// matvec contraction of "When Does a Kernel Win Surface?" (section 2; its
+// section 8 puts decode at the HBM roofline).  Every weight byte is read
+// once from HBM and used for all M rows, so the kernel is bound by the
+// weight stream, and its arithmetic is VALU int8 dot products
+// (v_dot4_i32_i8), not a matrix core: a wave computes one output row (all M
+// rows of x against one weight row) at a time.  The lanes of the wave stride
+// over the row in units of two 32-blocks (Q8_0: a 68-byte block pair, 17
+// dwords; Q4_K: one 32-byte code group of a super-block, i.e. two sub-blocks,
+// plus the super-block's 16-byte header), each lane keeping one fp32 partial
+// sum per activation row in ascending unit order; the 64 partials are then
+// summed by a butterfly.  The q8_1 activations (at most 8 x 21 KiB here) are
+// read per unit straight from the caches.  The per-block arithmetic is the
+// oracle's (t = fl(ws * I), then fma(xs, t, acc); Q4_K with its min term
+// per sub-block); only the order of the sum over blocks differs.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int dot8(const uint32_t *a, const uint32_t *b) {
+    int acc = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc = __builtin_amdgcn_sdot4(int(a[i]), int(b[i]), acc, false);
+    return acc;
+}
+
+// The q8_1 block pair starting at block b of activation row m: headers and codes.
+struct XPair {
+    uint32_t h0, h1;
+    uint32_t c0[8], c1[8];
+};
+
+__device__ __forceinline__ XPair load_x_pair(__amdgpu_buffer_rsrc_t rx, int off) {
+    XPair x;
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0);
+    const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 32, 0, 0);
+    const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 48, 0, 0);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 e = __builtin_amdgcn_raw_buffer_load_b64(rx, off + 64, 0, 0);
+    // dwords 0..17: [h0][c0 x 8][h1][c1 x 8]
+    x.h0 = a.x;
+    x.c0[0] = a.y; x.c0[1] = a.z; x.c0[2] = a.w; x.c0[3] = b.x;
+    x.c0[4] = b.y; x.c0[5] = b.z; x.c0[6] = b.w; x.c0[7] = c.x;
+    x.h1 = c.y;
+    x.c1[0] = c.z; x.c1[1] = c.w; x.c1[2] = d.x; x.c1[3] = d.y;
+    x.c1[4] = d.z; x.c1[5] = d.w; x.c1[6] = e.x; x.c1[7] = e.y;
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Unit u's two blocks (codes w0 / w1, weight scales ws0 / ws1, Q4_K min
+// terms dm0 / dm1) against the matching q8_1 block pair of every activation row.
+template <int FMT, int MR>
+__device__ __forceinline__ void mv_unit_terms(__amdgpu_buffer_rsrc_t rx, int M, int kb, int u, const uint32_t *w0,
+                                              const uint32_t *w1, float ws0, float ws1, float dm0, float dm1,
+                                              float *acc) {
+#pragma unroll
+    for (int m = 0; m < MR; m++) {
+        if (m < M) {
+            const XPair x = load_x_pair(rx, (m * kb + 2 * u) * 36);
+            const float t0 = ws0 * (float)dot8(w0, x.c0);
+            const float t1 = ws1 * (float)dot8(w1, x.c1);
+            acc[m] = __builtin_fmaf(h2f(x.h0), t0, acc[m]);
+            if constexpr (FMT == FMT_Q4_K) acc[m] = __builtin_fmaf(-dm0, h2f(x.h0 >> 16), acc[m]);
+            acc[m] = __builtin_fmaf(h2f(x.h1), t1, acc[m]);
+            if constexpr (FMT == FMT_Q4_K) acc[m] = __builtin_fmaf(-dm1, h2f(x.h1 >> 16), acc[m]);
+        }
+    }
+}
+
+template <int FMT, int MR>   // MR: activation rows compiled for (M <= MR)
+__global__ __launch_bounds__(kMvThreads) void k_mmv(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K) {
+    const int lane = threadIdx.x & 63;
+    // the output row of this wave over all GEMMs of the set; read as a
+    // wave-uniform (scalar) value, so that the weight row's buffer descriptor
+    // lives in scalar registers (a descriptor in vector registers makes
+    // every load a loop over the lanes' distinct values)
+    const int row = blockIdx.x * kMvRowsPerWg + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= set.tile_start[set.count]) return;
+    int gi = 0;
+    for (int i = 1; i < set.count; i++)
+        if (row >= set.tile_start[i]) gi = i;
+    const int n = row - set.tile_start[gi], N = set.N[gi];
+    const int kb = K >> 5;
+    const int64_t wrow = FMT == FMT_Q8_0 ? int64_t(kb) * 34 : int64_t(K >> 8) * 144;
+    const __amdgpu_buffer_rsrc_t rw = tile_rsrc(set.w[gi] + int64_t(n) * wrow, wrow);
+    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq, int64_t(M) * kb * 36);
+    const int units = kb >> 1;   // block pairs (Q8_0) / sub-block pairs (Q4_K) in the row
+
+    float acc[MR];
+#pragma unroll
+    for (int m = 0; m < MR; m++) acc[m] = 0.0f;
+
+    // Q8_0 rows are read in 64-unit chunks (4352 bytes) with contiguous
+    // 16-byte pieces per lane (each load instruction covers 1 KiB) into this
+    // wave's own LDS area, and each lane then takes its 68-byte unit from
+    // there: 68-byte units loaded straight by each lane touch ~34 cache lines
+    // per instruction, and were measured 15-30 % slower.  Q4_K units (a
+    // 16-byte header and 32 code bytes, both 16-byte aligned) load straight:
+    // the staged form was 10-13 % slower there.
+    constexpr int kQ8Chunk = 64 * 68;
+    for (int u0 = 0; u0 < units; u0 += 64) {
+        const int u = u0 + lane;
+        if constexpr (FMT == FMT_Q8_0) {
+            __shared__ __attribute__((aligned(16))) uint8_t stage[kMvRowsPerWg][kQ8Chunk];
+            uint8_t *my = stage[threadIdx.x >> 6];
+            // pieces past the row end read as zero
+#pragma unroll
+            for (int i = 0; i < (kQ8Chunk / 16 + 63) / 64; i++) {
+                const int piece = lane + 64 * i;
+                if (piece < kQ8Chunk / 16)
+                    *reinterpret_cast<u32x4 *>(my + 16 * piece) =
+                        __builtin_amdgcn_raw_buffer_load_b128(rw, u0 * 68 + 16 * piece, 0, 0);
+            }
+            // the area is this wave's alone and LDS serves a wave's accesses
+            // in order; the barrier only keeps the compiler from moving the
+            // unit reads above the other lanes' piece writes (or the next
+            // chunk's writes above these reads)
+            __builtin_amdgcn_wave_barrier();
+            if (u < units) {
+                const uint32_t *src = reinterpret_cast<const uint32_t *>(my + 68 * lane);
+                uint32_t v[17];
+#pragma unroll
+                for (int i = 0; i < 17; i++) v[i] = src[i];
+                uint32_t w0[8], w1[8];
+                // block 0: scale in bytes 0-1, codes two bytes off the dword
+                // grid; block 1: scale in bytes 34-35, codes on dwords 9..16
+#pragma unroll
+                for (int i = 0; i < 8; i++) w0[i] = __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2);
+#pragma unroll
+                for (int i = 0; i < 8; i++) w1[i] = v[i + 9];
+                mv_unit_terms<FMT, MR>(rx, M, kb, u, w0, w1, h2f(v[0]), h2f(v[8] >> 16), 0.0f, 0.0f, acc);
+            }
+            __builtin_amdgcn_wave_barrier();
+        } else if (u < units) {
+            uint32_t w0[8], w1[8];
+            const int sb = u >> 2, grp = u & 3;   // super-block, 32-byte code group
+            const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(rw, 144 * sb, 0, 0);
+            const u32x4 q0 = __builtin_amdgcn_raw_buffer_load_b128(rw, 144 * sb + 16 + 32 * grp, 0, 0);
+            const u32x4 q1 = __builtin_amdgcn_raw_buffer_load_b128(rw, 144 * sb + 32 + 32 * grp, 0, 0);
+            const uint32_t q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+            // low nibbles: sub-block 2*grp; high nibbles: sub-block 2*grp+1
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                w0[i] = q[i] & 0x0f0f0f0fu;
+                w1[i] = (q[i] >> 4) & 0x0f0f0f0fu;
+            }
+            // 6-bit scale and min of sub-blocks j = 2*grp + {0, 1} (the
+            // K-quant packing: j < 4 in the low six bits of bytes j and j+4;
+            // j >= 4 low four bits from byte j+4, top two bits from the spare
+            // top bits of bytes j-4 and j)
+            const float d = h2f(h.x), dmin = h2f(h.x >> 16);
+            float sc[2], mn[2];
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const int j = 2 * grp + t, sh = 8 * (j & 3);
+                const uint32_t b0 = (h.y >> sh) & 0xffu, b1 = (h.z >> sh) & 0xffu, b2 = (h.w >> sh) & 0xffu;
+                const uint32_t s = j < 4 ? (b0 & 63u) : ((b2 & 15u) | ((b0 >> 6) << 4));
+                const uint32_t mm = j < 4 ? (b1 & 63u) : ((b2 >> 4) | ((b1 >> 6) << 4));
+                sc[t] = (float)s;
+                mn[t] = (float)mm;
+            }
+            mv_unit_terms<FMT, MR>(rx, M, kb, u, w0, w1, d * sc[0], d * sc[1],   // d * sc: exact (11 x 6 bits)
+                                   dmin * mn[0], dmin * mn[1], acc);                 // exact
+        }
+    }
+    float *out = reinterpret_cast<float *>(set.out[gi]);
+#pragma unroll
+    for (int m = 0; m < MR; m++) {
+        if (m < M) {
+            const float v = wave_sum(acc[m]);
+            if (lane == 0) out[int64_t(m) * N + n] = v;
+        }
+    }
+}
+
 // Routing of the indexed MoE GEMM, one workgroup: count the routed rows of
 // each expert, scan the counts into row and tile offsets, scatter the routed
 // row ids into expert order and write the tile table (spare tiles: expert
@@ -863,6 +1045,28 @@ hipError_t launch_quantize(const float *x, void *y, int64_t M, int64_t K, int cu
     return hipGetLastError();
 }
 
+static hipError_t launch_mv(const Plan &p, const GemmSet &set, const uint8_t *xb, int64_t M, int64_t K,
+                            hipStream_t stream) {
+    const dim3 grid((unsigned)p.grid_x), block(kMvThreads);
+    static_assert(kMvMaxM == 8, "the matvec launches below cover M = 1, 2, 3-4, 5-8");
+    auto go = [&](auto mr) {
+        constexpr int MR = decltype(mr)::value;
+        if (p.fmt == FMT_Q8_0)
+            hipLaunchKernelGGL((k_mmv<FMT_Q8_0, MR>), grid, block, 0, stream, xb, set, int(M), int(K));
+        else
+            hipLaunchKernelGGL((k_mmv<FMT_Q4_K, MR>), grid, block, 0, stream, xb, set, int(M), int(K));
+    };
+    if (M == 1)
+        go(std::integral_constant<int, 1>{});
+    else if (M == 2)
+        go(std::integral_constant<int, 2>{});
+    else if (M <= 4)
+        go(std::integral_constant<int, 4>{});
+    else
+        go(std::integral_constant<int, 8>{});
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const void *x, const void *const *w,
                        void *const *out, const int64_t *N, int64_t M, int64_t K, bool dots, hipStream_t stream) {
     GemmSet set{};
@@ -874,6 +1078,7 @@ hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const vo
         set.out[g] = out[g];
     }
     set.tile_start[count] = tile_start[count];
+    if (p.kernel == KERNEL_MV) return launch_mv(p, set, reinterpret_cast<const uint8_t *>(x), M, K, stream);
     if (p.split_k > 1 && !dots) {
         for (int g = 0; g < count; g++) {
             const int64_t n = M * N[g];

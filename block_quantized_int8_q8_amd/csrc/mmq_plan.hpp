@@ -41,8 +41,17 @@ constexpr int64_t lds_bytes_for(int fmt) {
     return 2 * step;
 }
 
+// Few activation rows (decode): a matrix-vector kernel streams each weight
+// row once for all of them (one wave per output row, kMvRowsPerWg rows per
+// workgroup) instead of a 128-row tile that would be almost empty.
+enum Kernel : int { KERNEL_MMQ = 0, KERNEL_MV = 1 };
+constexpr int kMvMaxM = 8;          // activation rows the matvec kernel takes at most
+constexpr int kMvThreads = 256;
+constexpr int kMvRowsPerWg = kMvThreads / 64;
+
 struct Plan {
     int fmt = 0;
+    int kernel = KERNEL_MMQ;
     int tile_m = kTileM, tile_n = kTileN, threads = kThreads, blocks_per_stage = kBlocksPerStage;
     int64_t lds_bytes = 0;
     int64_t grid_x = 0, grid_y = 0;   // x: column tiles, y: row tiles
@@ -65,7 +74,7 @@ inline const char *check_quantize_shape(int64_t M, int64_t K) {
 
 // Build the GEMM plan or explain the refusal.  `extra_lds` is the test hook.
 inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limit, int cu_count,
-                      int64_t extra_lds, Plan *p, char *why, size_t why_len) {
+                      int64_t extra_lds, Plan *p, char *why, size_t why_len, bool allow_mv = true) {
     auto fail = [&](const char *msg) {
         if (why && why_len) std::snprintf(why, why_len, "%s", msg);
         return false;
@@ -84,6 +93,22 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
     if (cu_count < 1) return fail("device reports no compute units");
     Plan q;
     q.fmt = fmt;
+    if (allow_mv && M <= kMvMaxM) {
+        q.kernel = KERNEL_MV;
+        q.tile_m = int(M);
+        q.tile_n = 1;
+        q.threads = kMvThreads;
+        q.blocks_per_stage = 2;
+        q.lds_bytes = extra_lds;
+        q.grid_x = (N + kMvRowsPerWg - 1) / kMvRowsPerWg;
+        q.grid_y = 1;
+        q.k_steps = K / 64;
+        q.steps_per_split = q.k_steps;
+        if (q.grid_x > INT32_MAX) return fail("too many output rows");
+        if (q.lds_bytes > lds_limit) return fail("plan needs more LDS per workgroup than the device allows: refused");
+        *p = q;
+        return true;
+    }
     q.lds_bytes = lds_bytes_for(fmt) + extra_lds;
     q.grid_x = (N + kTileN - 1) / kTileN;
     q.grid_y = (M + kTileM - 1) / kTileM;
@@ -122,23 +147,27 @@ constexpr int kMaxGemms = 8;
 
 inline bool make_plan_multi(int fmt, int64_t M, int count, const int64_t *Ns, int64_t K, int64_t lds_limit,
                             int cu_count, int64_t extra_lds, Plan *p, int *tile_start, char *why,
-                            size_t why_len) {
+                            size_t why_len, bool allow_mv = true) {
     auto fail = [&](const char *msg) {
         if (why && why_len) std::snprintf(why, why_len, "%s", msg);
         return false;
     };
     if (count < 1 || count > kMaxGemms) return fail("count must be 1..8 GEMMs");
     if (!Ns) return fail("null N array");
+    // tile units: 128-column tiles for the MMQ kernel, single rows for the matvec kernel
+    const bool mv = allow_mv && M >= 1 && M <= kMvMaxM;
     int64_t tiles = 0;
     for (int g = 0; g < count; g++) {
         Plan one;
-        if (!make_plan(fmt, M, Ns[g], K, lds_limit, cu_count, extra_lds, &one, why, why_len)) return false;
+        if (!make_plan(fmt, M, Ns[g], K, lds_limit, cu_count, extra_lds, &one, why, why_len, allow_mv))
+            return false;
         tile_start[g] = int(tiles);
-        tiles += one.grid_x;
-        if (tiles > (int64_t(1) << 24)) return fail("too many column tiles in the GEMM set");
+        tiles += mv ? Ns[g] : one.grid_x;
+        if (tiles > (int64_t(1) << 30)) return fail("too many output columns in the GEMM set");
     }
     tile_start[count] = int(tiles);
-    return make_plan(fmt, M, tiles * kTileN, K, lds_limit, cu_count, extra_lds, p, why, why_len);
+    return make_plan(fmt, M, mv ? tiles : tiles * kTileN, K, lds_limit, cu_count, extra_lds, p, why, why_len,
+                     allow_mv);
 }
 
 // Indexed MoE ("When Does a Kernel Win Surface?", section 4.5, the fused
@@ -170,7 +199,7 @@ inline bool make_plan_moe(int fmt, int64_t T, int topk, int n_experts, int64_t N
     if (T < 1) return fail("T (tokens) must be >= 1");
     if (T > INT32_MAX / topk) return fail("T * topk (routed rows) must fit in int32");
     Plan q;
-    if (!make_plan(fmt, T, N, K, lds_limit, cu_count, extra_lds, &q, why, why_len)) return false;
+    if (!make_plan(fmt, T, N, K, lds_limit, cu_count, extra_lds, &q, why, why_len, false)) return false;
     // the gathered activation rows are addressed by 32-bit byte offsets
     // from the start of x
     if (T * (K / 32) * 36 > int64_t(0x7fffffff)) return fail("activations must be under 2 GiB (32-bit offsets)");
@@ -185,9 +214,9 @@ inline bool make_plan_moe(int fmt, int64_t T, int topk, int n_experts, int64_t N
 
 inline void describe(const Plan &p, char *buf, size_t len) {
     std::snprintf(buf, len,
-                  "fmt=%s tile=%dx%d threads=%d blocks_per_stage=%d lds=%lld grid=%lldx%lld k_steps=%lld "
-                  "split_k=%lld steps_per_split=%lld",
-                  fmt_name(p.fmt), p.tile_m, p.tile_n, p.threads, p.blocks_per_stage,
+                  "kernel=%s fmt=%s tile=%dx%d threads=%d blocks_per_stage=%d lds=%lld grid=%lldx%lld "
+                  "k_steps=%lld split_k=%lld steps_per_split=%lld",
+                  p.kernel == KERNEL_MV ? "mv" : "mmq", fmt_name(p.fmt), p.tile_m, p.tile_n, p.threads, p.blocks_per_stage,
                   (long long)p.lds_bytes, (long long)p.grid_x, (long long)p.grid_y,
                   (long long)p.k_steps, (long long)p.split_k, (long long)p.steps_per_split);
 }

@@ -85,7 +85,13 @@ int mmq_quantize_q8_1(const float *x, void *y, int64_t M, int64_t K, void *strea
  * along K (mmq_plan_describe reports split_k): the library first zeroes
  * `out` with a kernel on `stream`, then each K slice adds its partial sums
  * with fp32 atomics, so for those shapes the summation order, and the last
- * bits of the result, can differ from run to run. */
+ * bits of the result, can differ from run to run.
+ * M <= 8 (decode; "When Does a Kernel Win Surface?", sections 2 and 8: the
+ * matvec contraction, bound by the weight stream) runs a matrix-vector
+ * kernel instead: each weight row is read once for all M activation rows
+ * and its blocks are summed per lane and then across the 64 lanes of a
+ * wave, a fixed order (the same on every run) other than ascending.
+ * mmq_plan_describe reports kernel=mv for such shapes. */
 int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out,
                   int64_t M, int64_t N, int64_t K, void *stream);
 
@@ -94,7 +100,7 @@ int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out,
  * through the q8_1 block-sum field).
  *   x_q8_1: M x (K/32) q8_1 blocks; w_q4_K: N x (K/256) super-blocks;
  *   out: M x N fp32 row-major, fully overwritten.  Requires K % 256 == 0.
- * Split-K shapes behave as for mmq_gemm_q8_0. */
+ * Split-K and M <= 8 shapes behave as for mmq_gemm_q8_0. */
 int mmq_gemm_q4_K(const void *x_q8_1, const void *w_q4_K, float *out,
                   int64_t M, int64_t N, int64_t K, void *stream);
 

@@ -16,7 +16,7 @@ import torch
 import block_quantized_int8_q8_amd as mmq
 import oracle
 from block_quantized_int8_q8_amd import inputs
-from tests import golden_cases, metrics
+from tests import golden_cases, metrics, npdecode
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -120,12 +120,60 @@ def test_gemm_matches_oracle(fmt, M, N, K):
     w = _weights(fmt, N, K, 40 + N)
     got = _run_gemm(fmt, xq, w, M, N, K)
     ref = _oracle_gemm(fmt, xq, w, M, N, K)
+    if _kernel(fmt, M, N, K) == "mv":
+        _check_reordered(fmt, got, ref, xq, w, M, N, K)
+        return
     rep = metrics.report(got, ref)
     _say(rep)
     assert rep["normalized_max_error"] <= metrics.TOL
     if fmt == mmq.FMT_Q8_0 and _split_k(fmt, M, N, K) == 1:
         # one workgroup per output tile: the oracle's arithmetic in its order
         assert rep["bit_identical_fraction"] == 1.0
+
+
+U = 2.0 ** -24
+
+
+def _exact_and_scale(fmt, xq, w, M, N, K):
+    """The exact value of every output (block terms summed in fp64) and the
+    sum of the absolute block terms, from the independent numpy decoders."""
+    kb = K // 32
+    xd, xs, xc = npdecode.q8_1_fields(xq.reshape(M, kb, 36))
+    if fmt == mmq.FMT_Q8_0:
+        wd, wc = npdecode.q8_0_fields(w.reshape(N, kb, 34))
+    else:
+        d, dmin, sc, mn, codes = npdecode.q4_K_fields(w.reshape(N, K // 256, 144))
+        wc = codes.reshape(N, kb, 32)
+        wd = (d[..., None] * sc).reshape(N, kb)
+    # exact int block dots as fp64 matrix products, one per block
+    I = np.matmul(xc.transpose(1, 0, 2).astype(np.float64), wc.transpose(1, 2, 0).astype(np.float64))
+    main = xd.T[:, :, None] * wd.T[:, None, :] * I          # [kb, M, N]
+    if fmt == mmq.FMT_Q8_0:
+        return main.sum(0), np.abs(main).sum(0)
+    dm = (dmin[..., None] * mn).reshape(N, kb)
+    mins = xs.T[:, :, None] * dm.T[:, None, :]
+    return (main - mins).sum(0), (np.abs(main) + np.abs(mins)).sum(0)
+
+
+def _check_reordered(fmt, got, ref, xq, w, M, N, K):
+    """A result summed in another order than the oracle's: every element
+    within the fp32 accumulation bound of the exact value (the bound the
+    oracle itself is pinned to), and the 1e-5 normalized error against the
+    oracle wherever the output has enough elements for its rms to set the
+    scale (a single cancellation-dominated sum can differ from the oracle's
+    by more than 1e-5 of itself in any order but the oracle's)."""
+    exact, absterm = _exact_and_scale(fmt, xq, w, M, N, K)
+    err = np.abs(got.astype(np.float64) - exact)
+    assert (err <= (K // 32 + 2) * U * absterm + 1e-300).all()
+    rep = metrics.report(got, ref)
+    _say(rep)
+    if M * N >= 64:
+        assert rep["normalized_max_error"] <= metrics.TOL
+
+
+def _kernel(fmt, M, N, K):
+    import re
+    return re.search(r"kernel=(\w+)", mmq.plan_describe(fmt, M, N, K)[1]).group(1)
 
 
 def _split_k(fmt, M, N, K):
@@ -281,6 +329,59 @@ def test_gemm_multi_unsplit_member_equals_single_launch():
     single = mmq.gemm_q8_0(xq, ws[0], M, Ns[0], K)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], single)
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+@pytest.mark.parametrize("M", [1, 2, 3, 8])
+@pytest.mark.parametrize("N,K", [(1, 256), (300, 768), (3584, 3584), (129, 18944)])
+def test_matvec_matches_oracle(fmt, M, N, K):
+    """Decode-sized inputs (M <= 8) run the matrix-vector kernel: every
+    element written and checked as a reordered sum (the blocks of a row are
+    split over 64 lanes, so bit identity is not expected)."""
+    assert _kernel(fmt, M, N, K) == "mv"
+    _say(f"matvec fmt={fmt} M={M} N={N} K={K}")
+    x = inputs.activations(M, K, 110 + M)
+    xq = oracle.quantize_q8_1(x)
+    w = _weights(fmt, N, K, 120 + N)
+    got = _run_gemm(fmt, xq, w, M, N, K)
+    _check_reordered(fmt, got, _oracle_gemm(fmt, xq, w, M, N, K), xq, w, M, N, K)
+
+
+def test_matvec_boundary_m8_m9():
+    """M = 8 is the last matvec size and M = 9 the first tiled one; both agree
+    with the oracle on the same weights."""
+    fmt, N, K = mmq.FMT_Q4_K, 640, 2048
+    w = _weights(fmt, N, K, 130)
+    for M, kern in ((8, "mv"), (9, "mmq")):
+        assert _kernel(fmt, M, N, K) == kern
+        xq = oracle.quantize_q8_1(inputs.activations(M, K, 131))
+        rep = metrics.report(_run_gemm(fmt, xq, w, M, N, K), _oracle_gemm(fmt, xq, w, M, N, K))
+        _say(M, kern, rep)
+        assert rep["normalized_max_error"] <= metrics.TOL
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+def test_matvec_layer_set_decode(fmt):
+    """The 7B layer's projections at one token: q+k+v and gate+up through
+    one matvec launch each, o and down alone; each member equal to its own
+    launch, all within tolerance of the oracle."""
+    M = 1
+    shapes = {g: (n, k) for g, n, k in inputs.LAYER_7B}
+    for name, K, gemms in inputs.LAYER_INPUTS:
+        _say(f"matvec layer fmt={fmt} {name} {gemms}")
+        xq = oracle.quantize_q8_1(inputs.activations(M, K, inputs.layer_activation_seed(2048, name)))
+        ws = [_weights(fmt, shapes[g][0], K, inputs.layer_weight_seed(g)) for g in gemms]
+        Ns = [shapes[g][0] for g in gemms]
+        outs = mmq.gemm_multi(fmt, _to_dev(xq), [_to_dev(w) for w in ws], Ns, M, K)
+        torch.cuda.synchronize()
+        for g, (n, w) in enumerate(zip(Ns, ws)):
+            o = outs[g].cpu().numpy()
+            single = (mmq.gemm_q8_0 if fmt == mmq.FMT_Q8_0 else mmq.gemm_q4_K)(_to_dev(xq), _to_dev(w), M, n, K)
+            torch.cuda.synchronize()
+            assert np.array_equal(o.view(np.uint32), single.cpu().numpy().view(np.uint32))
+            rep = metrics.report(o, _oracle_gemm(fmt, xq, w, M, n, K))
+            _say(gemms[g], rep)
+            assert rep["normalized_max_error"] <= metrics.TOL
 
 
 def test_gemm_multi_refusals_leave_outputs_untouched():

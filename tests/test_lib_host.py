@@ -38,11 +38,12 @@ def test_library_carries_gfx950_code_only():
 @pytest.mark.parametrize("fmt,M,N,K", [
     (mmq.FMT_Q8_0, 64, 256, 512), (mmq.FMT_Q8_0, 2048, 3584, 3584),
     (mmq.FMT_Q4_K, 2048, 18944, 3584), (mmq.FMT_Q4_K, 2048, 3584, 18944),
-    (mmq.FMT_Q4_K, 8192, 512, 3584), (mmq.FMT_Q8_0, 1, 1, 256),
+    (mmq.FMT_Q4_K, 8192, 512, 3584), (mmq.FMT_Q8_0, 9, 1, 256),
 ])
 def test_plans_for_benchmark_shapes_fit(fmt, M, N, K):
     ok, desc = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
     assert ok, desc
+    assert "kernel=mmq" in desc
     lds = int(re.search(r"lds=(\d+)", desc).group(1))
     assert lds <= 80 * 1024          # two workgroups fit in one CU's 160 KiB
     gx, gy = map(int, re.search(r"grid=(\d+)x(\d+)", desc).groups())
@@ -123,3 +124,17 @@ def test_moe_workspace_bytes(T, topk, E, tiles):
                                       (2 ** 31, 1, 4)])
 def test_moe_workspace_bytes_refuses(T, topk, E):
     assert mmq.moe_workspace_bytes(T, topk, E) == -1
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (1, 3584, 3584), (8, 18944, 3584), (3, 5, 18944)])
+def test_decode_sizes_plan_the_matvec_kernel(fmt, M, N, K):
+    """M <= 8: one wave per output row, four rows per 256-thread workgroup,
+    no LDS, no split."""
+    ok, desc = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
+    assert ok and "kernel=mv" in desc, desc
+    gx, gy = map(int, re.search(r"grid=(\d+)x(\d+)", desc).groups())
+    assert (gx, gy) == (-(-N // 4), 1)
+    assert "threads=256" in desc and "lds=0" in desc and "split_k=1" in desc
+    # the same shape with one more row is tiled
+    assert "kernel=mmq" in mmq.plan_for_limits(fmt, 9, N, K, LDS_GFX950, 256)[1]
