@@ -228,7 +228,10 @@ def time_decode(M: int, fmt_name: str, steps: int, warmup: int, check: bool = Tr
     """The 7B layer's projections at decode size (M <= 8 tokens), one format:
     one quantize per distinct input and one matvec launch per input group
     (q+k+v, o, gate+up, down).  The matvec streams every weight byte once,
-    so its roofline is HBM: `weight_gbs` is weight bytes / GEMM time."""
+    so its roofline is HBM: `weight_gbs` is weight bytes / GEMM time.  The
+    step runs `layers` copies of the layer's weights (more bytes than the
+    256 MB last-level cache holds twice over), as a model's layers would,
+    so that every weight byte comes from HBM."""
     import torch
     import block_quantized_int8_q8_amd as mmq
     from block_quantized_int8_q8_amd import inputs
@@ -237,7 +240,6 @@ def time_decode(M: int, fmt_name: str, steps: int, warmup: int, check: bool = Tr
     fmt = mmq.FMT_Q8_0 if fmt_name == "q8_0" else mmq.FMT_Q4_K
     wgen = inputs.q8_0_weights if fmt == mmq.FMT_Q8_0 else inputs.q4_K_weights
     shapes = {g: (n, k) for g, n, k in inputs.LAYER_7B}
-    stream = torch.cuda.current_stream()
     groups = []
     for name, K, gemms in inputs.LAYER_INPUTS:
         x = inputs.activations(M, K, inputs.layer_activation_seed(2048, name))
@@ -245,18 +247,18 @@ def time_decode(M: int, fmt_name: str, steps: int, warmup: int, check: bool = Tr
         groups.append({
             "gemms": gemms, "K": K, "Ns": [shapes[g][0] for g in gemms], "x_host": x, "w_host": ws_host,
             "x": torch.from_numpy(x).to(dev), "xq": torch.empty((M, K // 32, 36), dtype=torch.uint8, device=dev),
-            "w": [torch.from_numpy(w).to(dev) for w in ws_host],
             "out": [torch.full((M, shapes[g][0]), float("nan"), dtype=torch.float32, device=dev) for g in gemms],
         })
+    layer_bytes = sum(w.nbytes for g in groups for w in g["w_host"])
+    layers = max(2, -(-2 * 256 * 2 ** 20 // layer_bytes))
+    for g in groups:   # per layer, its own device copy of the weights
+        g["w"] = [[torch.from_numpy(w).to(dev) for w in g["w_host"]] for _ in range(layers)]
 
-    def step(ev=None):
-        for i, g in enumerate(groups):
-            mmq.quantize_q8_1(g["x"], g["xq"], stream=stream)
-            if ev is not None:
-                ev[i][0].record(stream)
-            mmq.gemm_multi(fmt, g["xq"], g["w"], g["Ns"], M, g["K"], g["out"], stream=stream)
-            if ev is not None:
-                ev[i][1].record(stream)
+    def step():
+        for layer in range(layers):
+            for g in groups:
+                mmq.quantize_q8_1(g["x"], g["xq"])
+                mmq.gemm_multi(fmt, g["xq"], g["w"][layer], g["Ns"], M, g["K"], g["out"])
 
     for _ in range(warmup):
         step()
@@ -275,25 +277,55 @@ def time_decode(M: int, fmt_name: str, steps: int, warmup: int, check: bool = Tr
                 worst = max(worst, metrics.normalized_max_error(o, f(xq, w, M, n, g["K"], nthreads=16)))
         parity = {"outputs_checked": "all", "unwritten": unwritten, "normalized_max_error": worst,
                   "ok": bool(unwritten == 0 and worst <= metrics.TOL)}
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in groups] for _ in range(steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    # A decode step is a few microseconds of GPU work per launch, less than
+    # the host needs to issue a launch, so it is timed as HIP graph replays
+    # (the launches captured once): the whole step, and each group's GEMM
+    # launch over the layer copies.
+    ref_out = [[o.clone() for o in g["out"]] for g in groups]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(step_graph, stream=side):
+            step()
+        group_graphs = []
+        for g in groups:
+            gg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gg, stream=side):
+                for layer in range(layers):
+                    mmq.gemm_multi(fmt, g["xq"], g["w"][layer], g["Ns"], M, g["K"], g["out"])
+            group_graphs.append(gg)
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(steps):
-        step(ev[i])
-    end.record(stream)
-    torch.cuda.synchronize()
-    step_ms = start.elapsed_time(end) / steps
-    gemm_ms = {"+".join(g["gemms"]): float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)]))
-               for j, g in enumerate(groups)}
+
+    def timed(graph):
+        graph.replay()   # warm
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (steps * layers)
+
+    layer_ms = timed(step_graph)
+    gemm_ms = {"+".join(g["gemms"]): timed(gg) for g, gg in zip(groups, group_graphs)}
+    # replays recompute the same outputs: they must equal the eager ones
+    replay_ok = all(torch.equal(o, r) for g, rs in zip(groups, ref_out) for o, r in zip(g["out"], rs))
+    if parity is not None:
+        parity["graph_replays_equal_eager"] = bool(replay_ok)
+        parity["ok"] = bool(parity["ok"] and replay_ok)
     wbytes = {"+".join(g["gemms"]): float(sum(w.nbytes for w in g["w_host"])) for g in groups}
     return {
-        "format": fmt_name.upper(), "M": M, "ms_per_layer": step_ms,
+        "format": fmt_name.upper(), "M": M, "ms_per_layer": layer_ms, "timing": "HIP graph replay",
+        "layer_copies": layers,
         "weight_bytes": sum(wbytes.values()),
         "gemm_ms": gemm_ms,
         "weight_gbs": {k: wbytes[k] / (gemm_ms[k] * 1e-3) / 1e9 for k in gemm_ms},
         "weight_gbs_all_gemms": sum(wbytes.values()) / (sum(gemm_ms.values()) * 1e-3) / 1e9,
+        "weight_gbs_layer": sum(wbytes.values()) / (layer_ms * 1e-3) / 1e9,
         "parity": parity,
     }
 
@@ -471,7 +503,7 @@ def main():
 
     for spec in [v.strip() for v in args.decode.split(",") if v.strip()]:
         f, m = spec.split(":")
-        extra[f"decode_{f}_M{m}"] = time_decode(int(m), f, max(10, args.steps), 2, check=not args.no_check)
+        extra[f"decode_{f}_M{m}"] = time_decode(int(m), f, max(10, args.steps // 2), 2, check=not args.no_check)
 
     for f in [v.strip() for v in args.moe.split(",") if v.strip()]:
         extra[f"moe_{f}"] = time_moe(f, max(3, args.steps // 5), 1, check=not args.no_check)
