@@ -14,12 +14,16 @@ Distributions follow the 7B prefill workloads the library is measured on:
     the 12-byte field feeds exactly one 6-bit value, so uniform bytes give
     uniform values), fp16 d uniform on [1e-3, 1e-2], fp16 dmin uniform on
     [0, 1e-2].
+  * Q5_K weights: as Q4_K, plus 32 uniformly random high-bit bytes (each
+    code's fifth bit uniform).
 Seeds are ``1000 * config + tensor_id`` with numpy's PCG64.
 
 Block layouts (little-endian):
   q8_1 (36 B):  fp16 d @0, fp16 s @2, 32 x int8 @4
   Q8_0 (34 B):  fp16 d @0, 32 x int8 @2
   Q4_K (144 B): fp16 d @0, fp16 dmin @2, 12 B scales/mins @4, 128 B codes @16
+  Q5_K (176 B): fp16 d @0, fp16 dmin @2, 12 B scales/mins @4, 32 B high bits
+                @16, 128 B low nibbles @48
 """
 from __future__ import annotations
 
@@ -28,6 +32,7 @@ import numpy as np
 Q8_1_BYTES = 36
 Q8_0_BYTES = 34
 Q4_K_BYTES = 144
+Q5_K_BYTES = 176
 
 
 def seed_for(config: int, tensor_id: int) -> int:
@@ -87,6 +92,38 @@ def q4_K_weights(N: int, K: int, seed: int, d_range=(1e-3, 1e-2), dmin_range=(0.
     out[..., 2:4] = _f16_bytes(dmin)
     out[..., 4:16] = sc
     out[..., 16:144] = qs
+    return out
+
+
+def q5_K_weights(N: int, K: int, seed: int, d_range=(1e-3, 1e-2), dmin_range=(0.0, 1e-2),
+                 d_value: float | None = None, dmin_value: float | None = None,
+                 scale_bytes: np.ndarray | None = None, code_byte: int | None = None,
+                 high_byte: int | None = None) -> np.ndarray:
+    """uint8 N x (K/256) x 176: fp16 d, fp16 dmin, 12 scale/min bytes, 32
+    high-bit bytes, 128 low-nibble bytes.  ``high_byte`` fixes every high-bit
+    byte; the other keywords as for ``q4_K_weights``."""
+    if K % 256:
+        raise ValueError("K must be a multiple of 256")
+    nsb = K // 256
+    r = np.random.default_rng(seed)
+    d = np.full((N, nsb), d_value) if d_value is not None else r.uniform(*d_range, size=(N, nsb))
+    dmin = (np.full((N, nsb), dmin_value) if dmin_value is not None
+            else r.uniform(*dmin_range, size=(N, nsb)))
+    sc = r.integers(0, 255, size=(N, nsb, 12), endpoint=True, dtype=np.uint8)
+    qh = r.integers(0, 255, size=(N, nsb, 32), endpoint=True, dtype=np.uint8)
+    qs = r.integers(0, 255, size=(N, nsb, 128), endpoint=True, dtype=np.uint8)
+    if scale_bytes is not None:
+        sc[...] = np.asarray(scale_bytes, dtype=np.uint8).reshape(12)
+    if code_byte is not None:
+        qs[...] = np.uint8(code_byte)
+    if high_byte is not None:
+        qh[...] = np.uint8(high_byte)
+    out = np.empty((N, nsb, Q5_K_BYTES), dtype=np.uint8)
+    out[..., 0:2] = _f16_bytes(d)
+    out[..., 2:4] = _f16_bytes(dmin)
+    out[..., 4:16] = sc
+    out[..., 16:48] = qh
+    out[..., 48:176] = qs
     return out
 
 

@@ -24,6 +24,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 Q8_1_BYTES = 36
 Q8_0_BYTES = 34
 Q4_K_BYTES = 144
+Q5_K_BYTES = 176
 
 
 def build(force: bool = True) -> str:
@@ -66,13 +67,15 @@ def lib() -> ctypes.CDLL:
         L.oracle_q4k_code.argtypes = [p, i32]
         L.oracle_q4k_code.restype = i32
         L.oracle_dequant_q4_K_block.argtypes = [p, p]
-        for name in ("oracle_block_dots_q8_0", "oracle_block_dots_q4_K"):
+        L.oracle_q5k_code.argtypes = [p, i32]
+        L.oracle_q5k_code.restype = i32
+        for name in ("oracle_block_dots_q8_0", "oracle_block_dots_q4_K", "oracle_block_dots_q5_K"):
             getattr(L, name).argtypes = [p, p, p, i64, i64, i64]
             getattr(L, name).restype = i32
-        for name in ("oracle_gemm_q8_0", "oracle_gemm_q4_K"):
+        for name in ("oracle_gemm_q8_0", "oracle_gemm_q4_K", "oracle_gemm_q5_K"):
             getattr(L, name).argtypes = [p, p, p, i64, i64, i64, i32]
             getattr(L, name).restype = i32
-        for name in ("oracle_gemm_q8_0_rows", "oracle_gemm_q4_K_rows"):
+        for name in ("oracle_gemm_q8_0_rows", "oracle_gemm_q4_K_rows", "oracle_gemm_q5_K_rows"):
             getattr(L, name).argtypes = [p, p, p, i64, i64, i64, i64, i64, i32]
             getattr(L, name).restype = i32
         _lib = L
@@ -140,6 +143,13 @@ def q4k_code(superblock: np.ndarray, e: int) -> int:
     return lib().oracle_q4k_code(_ptr(superblock), e)
 
 
+def q5k_code(superblock: np.ndarray, e: int) -> int:
+    """5-bit code of element e of a Q5_K super-block (reading R21 in the C source)."""
+    superblock = np.ascontiguousarray(superblock, dtype=np.uint8)
+    assert superblock.size == Q5_K_BYTES
+    return lib().oracle_q5k_code(_ptr(superblock), e)
+
+
 def dequant_q4_K_block(superblock: np.ndarray) -> np.ndarray:
     superblock = np.ascontiguousarray(superblock, dtype=np.uint8)
     out = np.empty(256, dtype=np.float32)
@@ -169,6 +179,16 @@ def block_dots_q4_K(x, w, M, N, K) -> np.ndarray:
     return out
 
 
+def block_dots_q5_K(x, w, M, N, K) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    out = np.zeros((M, N, K // 32), dtype=np.int32)
+    rc = lib().oracle_block_dots_q5_K(_ptr(x), _ptr(w), _ptr(out), M, N, K)
+    if rc != 0:
+        raise ValueError(f"bad shape ({rc})")
+    return out
+
+
 def gemm_q8_0(x, w, M, N, K, nthreads: int = 0, rows=None) -> np.ndarray:
     """q8_1 activations x Q8_0 weights -> fp32 M x N (or the row range ``rows``)."""
     x = np.ascontiguousarray(x, dtype=np.uint8)
@@ -188,6 +208,18 @@ def gemm_q4_K(x, w, M, N, K, nthreads: int = 0, rows=None) -> np.ndarray:
     out = np.zeros((M, N), dtype=np.float32)
     m0, m1 = (0, M) if rows is None else rows
     rc = lib().oracle_gemm_q4_K_rows(_ptr(x), _ptr(w), _ptr(out), M, N, K, m0, m1, nthreads)
+    if rc < 0:
+        raise ValueError(f"bad shape ({rc})")
+    return out
+
+
+def gemm_q5_K(x, w, M, N, K, nthreads: int = 0, rows=None) -> np.ndarray:
+    """q8_1 activations x Q5_K weights -> fp32 M x N (or the row range ``rows``)."""
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    out = np.zeros((M, N), dtype=np.float32)
+    m0, m1 = (0, M) if rows is None else rows
+    rc = lib().oracle_gemm_q5_K_rows(_ptr(x), _ptr(w), _ptr(out), M, N, K, m0, m1, nthreads)
     if rc < 0:
         raise ValueError(f"bad shape ({rc})")
     return out

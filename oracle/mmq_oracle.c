@@ -52,6 +52,13 @@
  *   R9  Q4_K 6-bit packing and nibble order: the GGUF K-quant packing (see
  *       q4k_scale_min below); element e of a super-block lives in byte
  *       32*(e/64) + (e%32) of the code area, low nibble when (e%64) < 32.
+ *   R21 Q5_K (a format the pages name in their list of K-quants without a
+ *       layout; the GGUF K-quant layout is taken): super-block (176 B, 256
+ *       values): [0,2) fp16 d, [2,4) fp16 dmin, [4,16) the Q4_K 6-bit
+ *       scale/min packing, [16,48) high bits, [48,176) low nibbles in the
+ *       Q4_K order; the 5-bit code of element e is its nibble plus 16 times
+ *       bit e/32 of high-bit byte e%32.  Its block term is the Q4_K affine
+ *       identity with 5-bit codes (0..31), computed as in R10-R11.
  *   R10 per block: t = weight_scale * (float)I (one rounding), then
  *       acc = fmaf(activation_scale, t, acc).
  *   R11 the Q4_K min term is acc = fmaf(-(dmin*m), f32(s16), acc), using
@@ -71,6 +78,7 @@
 #define Q8_1_BYTES 36
 #define Q8_0_BYTES 34
 #define Q4_K_BYTES 144
+#define Q5_K_BYTES 176
 
 /* ------------------------------------------------------------------ */
 /* IEEE binary16 <-> binary32, written from the format definition.      */
@@ -273,6 +281,16 @@ static int q4k_code(const uint8_t *qs, int e)
 /* Public forms for the layout tests. */
 int oracle_q4k_code(const uint8_t *superblock, int e) { return q4k_code(superblock + 16, e); }
 
+/* 5-bit code of element e (0..255) of a Q5_K super-block (reading R21). */
+static int q5k_code(const uint8_t *blk, int e)
+{
+    int lo = q4k_code(blk + 48, e);
+    int hi = (blk[16 + (e % 32)] >> (e / 32)) & 1;
+    return lo | (hi << 4);
+}
+
+int oracle_q5k_code(const uint8_t *superblock, int e) { return q5k_code(superblock, e); }
+
 /* Dequantize one Q4_K super-block into 256 fp32 values (w = d*sc*q - dmin*m). */
 void oracle_dequant_q4_K_block(const uint8_t *blk, float *w)
 {
@@ -335,6 +353,26 @@ int oracle_block_dots_q4_K(const uint8_t *x, const uint8_t *w, int32_t *dots,
                 int32_t s = 0;
                 for (int i = 0; i < QK; i++)
                     s += (int32_t)xq[i] * q4k_code(blk + 16, (int)(b % 8) * QK + i);
+                dots[(m * N + n) * kb + b] = s;
+            }
+    return 0;
+}
+
+/* Same for Q5_K weights: the 5-bit codes (0..31) of sub-block b%8. */
+int oracle_block_dots_q5_K(const uint8_t *x, const uint8_t *w, int32_t *dots,
+                           int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0 || K % QK_K != 0)
+        return -2;
+    int64_t kb = K / QK, nsb = K / QK_K;
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++)
+            for (int64_t b = 0; b < kb; b++) {
+                const int8_t *xq = (const int8_t *)(x + (m * kb + b) * Q8_1_BYTES + 4);
+                const uint8_t *blk = w + (n * nsb + b / 8) * Q5_K_BYTES;
+                int32_t s = 0;
+                for (int i = 0; i < QK; i++)
+                    s += (int32_t)xq[i] * q5k_code(blk, (int)(b % 8) * QK + i);
                 dots[(m * N + n) * kb + b] = s;
             }
     return 0;
@@ -440,24 +478,73 @@ int oracle_gemm_q4_K(const uint8_t *x, const uint8_t *w, float *out,
     return oracle_gemm_q4_K_rows(x, w, out, M, N, K, 0, M, nthreads);
 }
 
+/* x: M x kb q8_1 blocks; w: N x (K/256) Q5_K super-blocks; out: M x N fp32.
+ * The Q4_K contraction above with 5-bit codes (reading R21). */
+int oracle_gemm_q5_K_rows(const uint8_t *x, const uint8_t *w, float *out,
+                          int64_t M, int64_t N, int64_t K, int64_t m0, int64_t m1,
+                          int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || K % QK_K != 0 || m0 < 0 || m1 > M || m0 > m1)
+        return -2;
+    int used = set_threads(nthreads);
+    int64_t kb = K / QK, nsb = K / QK_K;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = m0; m < m1; m++) {
+        for (int64_t n = 0; n < N; n++) {
+            float acc = 0.0f;
+            for (int64_t sb = 0; sb < nsb; sb++) {
+                const uint8_t *blk = w + (n * nsb + sb) * Q5_K_BYTES;
+                float d = oracle_f16_to_f32(rd16(blk));
+                float dmin = oracle_f16_to_f32(rd16(blk + 2));
+                for (int j = 0; j < 8; j++) {
+                    int64_t b = sb * 8 + j;
+                    const uint8_t *xb = x + (m * kb + b) * Q8_1_BYTES;
+                    const int8_t *xq = (const int8_t *)(xb + 4);
+                    uint8_t sc, mn;
+                    oracle_q4k_scale_min(blk + 4, j, &sc, &mn);
+                    int32_t I = 0;
+                    for (int i = 0; i < QK; i++)
+                        I += (int32_t)xq[i] * q5k_code(blk, j * QK + i);
+                    float ds = d * (float)sc;       /* exact: 11 x 6 bits */
+                    float dm = dmin * (float)mn;    /* exact */
+                    float xd = oracle_f16_to_f32(rd16(xb));
+                    float xs = oracle_f16_to_f32(rd16(xb + 2));
+                    float t = ds * (float)I;
+                    acc = fmaf(xd, t, acc);
+                    acc = fmaf(-dm, xs, acc);
+                }
+            }
+            out[m * N + n] = acc;
+        }
+    }
+    return used;
+}
+
+int oracle_gemm_q5_K(const uint8_t *x, const uint8_t *w, float *out,
+                     int64_t M, int64_t N, int64_t K, int nthreads)
+{
+    return oracle_gemm_q5_K_rows(x, w, out, M, N, K, 0, M, nthreads);
+}
+
 /* Indexed MoE ("When Does a Kernel Win Surface?", section 4.5, the fused
  * indexed-MoE prefill GEMM): routed row r = t*topk + j of out is token t's q8_1 row
  * times the weights of expert ids[r], i.e. the dense GEMM row above with
  * that expert's N x K matrix; experts are stored one after another.
- * fmt 0 = Q8_0, 1 = Q4_K.  Rows [r0, r1) of out (T*topk x N) are written.
+ * fmt 0 = Q8_0, 1 = Q4_K, 2 = Q5_K.  Rows [r0, r1) of out (T*topk x N) are
+ * written.
  * Returns the thread count used, -2 on a bad shape, -3 on an expert id out
  * of range. */
 int oracle_moe_gemm(int fmt, const uint8_t *x, const uint8_t *w, const int32_t *ids, int topk,
                     float *out, int64_t T, int64_t N, int64_t K, int n_experts,
                     int64_t r0, int64_t r1, int nthreads)
 {
-    if ((fmt != 0 && fmt != 1) || topk < 1 || n_experts < 1 || T < 0 || N < 0 || K < 0 ||
+    if ((fmt != 0 && fmt != 1 && fmt != 2) || topk < 1 || n_experts < 1 || T < 0 || N < 0 || K < 0 ||
         K % (fmt == 0 ? QK : QK_K) != 0 || r0 < 0 || r1 > T * topk || r0 > r1)
         return -2;
     for (int64_t r = r0; r < r1; r++)
         if (ids[r] < 0 || ids[r] >= n_experts) return -3;
     const int64_t kb = K / QK;
-    const int64_t wrow = fmt == 0 ? kb * Q8_0_BYTES : (K / QK_K) * Q4_K_BYTES;
+    const int64_t wrow = fmt == 0 ? kb * Q8_0_BYTES : (K / QK_K) * (fmt == 1 ? Q4_K_BYTES : Q5_K_BYTES);
     int used = set_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t r = r0; r < r1; r++) {
@@ -465,8 +552,10 @@ int oracle_moe_gemm(int fmt, const uint8_t *x, const uint8_t *w, const int32_t *
         const uint8_t *we = w + (int64_t)ids[r] * N * wrow;
         if (fmt == 0)
             oracle_gemm_q8_0_rows(xr, we, out + r * N, 1, N, K, 0, 1, 1);
-        else
+        else if (fmt == 1)
             oracle_gemm_q4_K_rows(xr, we, out + r * N, 1, N, K, 0, 1, 1);
+        else
+            oracle_gemm_q5_K_rows(xr, we, out + r * N, 1, N, K, 0, 1, 1);
     }
     return used;
 }

@@ -43,6 +43,34 @@ def q4_K_fields(w):
     return d, dmin, sc, mn, codes
 
 
+def q5_K_fields(w):
+    """-> (d, dmin, sc, mn, codes 0..31 [N,nsb,256]): the Q4_K fields of bytes
+    0..15 and 48..175, plus 16 x bit (e // 32) of high-bit byte e % 32."""
+    d = f16(w[..., 0:2])
+    dmin = f16(w[..., 2:4])
+    s = w[..., 4:16].astype(np.int64)
+    sc = np.empty(s.shape[:-1] + (8,), np.int64)
+    mn = np.empty_like(sc)
+    sc[..., 0:4] = s[..., 0:4] & 63
+    mn[..., 0:4] = s[..., 4:8] & 63
+    sc[..., 4:8] = (s[..., 8:12] & 15) | ((s[..., 0:4] >> 6) << 4)
+    mn[..., 4:8] = (s[..., 8:12] >> 4) | ((s[..., 4:8] >> 6) << 4)
+    q = w[..., 48:176].astype(np.int64).reshape(w.shape[:-1] + (4, 32))
+    low = np.stack([q & 15, q >> 4], axis=-2).reshape(w.shape[:-1] + (256,))
+    qh = w[..., 16:48].astype(np.int64)                                   # [..., 32]
+    high = (qh[..., None, :] >> np.arange(8)[:, None]) & 1               # [..., 8 (bit j), 32 (byte l)]
+    return d, dmin, sc, mn, low + 16 * high.reshape(w.shape[:-1] + (256,))
+
+
+def dequant_q5_K(w) -> np.ndarray:
+    """-> f64 N x K: d*sc*q - dmin*m with 5-bit q."""
+    d, dmin, sc, mn, codes = q5_K_fields(w)
+    N, nsb = d.shape
+    c = codes.reshape(N, nsb, 8, 32)
+    val = (d[..., None, None] * sc[..., None]) * c - (dmin[..., None] * mn)[..., None]
+    return val.reshape(N, -1)
+
+
 def dequant_q8_0(w) -> np.ndarray:
     """-> f64 N x K (exact: fp16 x int8)."""
     d, q = q8_0_fields(w)
