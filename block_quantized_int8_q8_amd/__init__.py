@@ -15,10 +15,11 @@ LIB_PATH = os.path.join(PKG, "libmmq.so")
 
 FMT_Q8_0 = 0
 FMT_Q4_K = 1
-Q8_1_BYTES, Q8_0_BYTES, Q4_K_BYTES = 36, 34, 144
+FMT_Q5_K = 2
+Q8_1_BYTES, Q8_0_BYTES, Q4_K_BYTES, Q5_K_BYTES = 36, 34, 144, 176
 
 EXPORTS = (
-    "mmq_quantize_q8_1", "mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_multi", "mmq_moe_workspace_bytes",
+    "mmq_quantize_q8_1", "mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_q5_K", "mmq_gemm_multi", "mmq_moe_workspace_bytes",
     "mmq_moe_gemm", "mmq_debug_block_dots",
     "mmq_last_error", "mmq_plan_describe", "mmq_plan_for_limits",
     "mmq_debug_set_extra_lds", "mmq_version",
@@ -42,7 +43,7 @@ def lib() -> ctypes.CDLL:
         p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.mmq_quantize_q8_1.argtypes = [p, p, i64, i64, p]
         L.mmq_quantize_q8_1.restype = i32
-        for name in ("mmq_gemm_q8_0", "mmq_gemm_q4_K"):
+        for name in ("mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_q5_K"):
             getattr(L, name).argtypes = [p, p, p, i64, i64, i64, p]
             getattr(L, name).restype = i32
         L.mmq_gemm_multi.argtypes = [i32, p, i32, p, p, p, i64, i64, p]
@@ -119,6 +120,17 @@ def gemm_q8_0(xq, w, M, N, K, out=None, stream=None):
 def gemm_q4_K(xq, w, M, N, K, out=None, stream=None):
     """q8_1 [M, K/32, 36] x Q4_K [N, K/256, 144] -> fp32 [M, N]."""
     return _gemm("mmq_gemm_q4_K", "mmq_gemm_q4_K", xq, w, M, N, K, out, stream)
+
+
+def gemm_q5_K(xq, w, M, N, K, out=None, stream=None):
+    """q8_1 [M, K/32, 36] x Q5_K [N, K/256, 176] -> fp32 [M, N]."""
+    return _gemm("mmq_gemm_q5_K", "mmq_gemm_q5_K", xq, w, M, N, K, out, stream)
+
+
+def gemm(fmt, xq, w, M, N, K, out=None, stream=None):
+    """The GEMM of weight format ``fmt`` (FMT_Q8_0, FMT_Q4_K or FMT_Q5_K)."""
+    f = {FMT_Q8_0: gemm_q8_0, FMT_Q4_K: gemm_q4_K, FMT_Q5_K: gemm_q5_K}[fmt]
+    return f(xq, w, M, N, K, out, stream)
 
 
 def gemm_multi(fmt, xq, ws, Ns, M, K, outs=None, stream=None):

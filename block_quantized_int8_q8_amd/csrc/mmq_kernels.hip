@@ -2,7 +2,7 @@
 //
 //   k_quantize_q8_1   fp32 -> q8_1, one pass over the activations (HBM-bound)
 //   k_mmq<FMT, DOTS, MOE>
-//                     q8_1 x {Q8_0, Q4_K} -> fp32 (or the raw int32 block
+//                     q8_1 x {Q8_0, Q4_K, Q5_K} -> fp32 (or the raw int32 block
 //                     dots when DOTS), int8 MFMA with the per-block scale
 //                     applied in registers on the MFMA accumulator layout;
 //                     MOE gathers the rows of each expert's routed tokens
@@ -208,7 +208,7 @@ struct Lds {
     static constexpr int A_HDR = kTileM * KB * 4;                               // [row][4] (d, s) fp16 pairs
     static constexpr int B_CODES = KB * kBlockBytes;
     static constexpr int B_SCALE = KB * kTileN * 8;                             // [4][col] (ws, cs) fp32
-    static constexpr int B_MIN = (FMT == FMT_Q4_K) ? kTileN * 2 * KB * 2 : 0;   // [col][g][4] fp16
+    static constexpr int B_MIN = (FMT != FMT_Q8_0) ? kTileN * 2 * KB * 2 : 0;   // [col][g][4] fp16
     static constexpr int OFF_A_HDR = A_CODES;
     static constexpr int OFF_B_CODES = OFF_A_HDR + A_HDR;
     static constexpr int OFF_B_SCALE = OFF_B_CODES + B_CODES;
@@ -220,6 +220,7 @@ static_assert(KB == 4 && kTileM == 128 && kTileN == 128 && kThreads == 512 && kN
               "the staging maps below assume 4 blocks per k-step, a 128 x 128 tile and 512 threads");
 static_assert(Lds<FMT_Q8_0>::TOTAL == lds_bytes_for(FMT_Q8_0), "plan and kernel LDS disagree");
 static_assert(Lds<FMT_Q4_K>::TOTAL == lds_bytes_for(FMT_Q4_K), "plan and kernel LDS disagree");
+static_assert(Lds<FMT_Q5_K>::TOTAL == lds_bytes_for(FMT_Q5_K), "plan and kernel LDS disagree");
 static_assert(Lds<FMT_Q4_K>::OFF_B_CODES % 16 == 0 && Lds<FMT_Q4_K>::OFF_B_MIN % 16 == 0 &&
               Lds<FMT_Q4_K>::STEP % 16 == 0 &&
               Lds<FMT_Q8_0>::OFF_B_SCALE % 16 == 0 && Lds<FMT_Q8_0>::STEP % 16 == 0,
@@ -409,6 +410,17 @@ struct Q4KRegs {
     u32x4 h;
 };
 
+// Q5_K: the same chunks and header as Q4_K (its scales use the same packing),
+// plus the 16 high-bit bytes of the chunk's k-half: byte l of the high-bit
+// plane carries the fifth bit of element l of every sub-block j in bit j, so
+// the chunk's codes take bits 2g (low nibbles, sub-block 2g) and 2g+1 (high
+// nibbles) of the same 16 bytes.
+struct Q5KRegs {
+    u32x4 v;
+    u32x4 h;
+    u32x4 qh;
+};
+
 __device__ __forceinline__ void load_q4_K(__amdgpu_buffer_rsrc_t rw, int nsb, int ks, int tid, Q4KRegs &r) {
     const int sb = ks >> 1, half = ks & 1;
     const int col = tid >> 2, c = 4 * half + (tid & 3);
@@ -417,15 +429,30 @@ __device__ __forceinline__ void load_q4_K(__amdgpu_buffer_rsrc_t rw, int nsb, in
     r.h = __builtin_amdgcn_raw_buffer_load_b128(rw, (hcol * nsb + sb) * 144, 0, 0);
 }
 
-__device__ __forceinline__ void store_q4_K(const Q4KRegs &r, uint8_t *buf, int ks, int tid) {
-    using L = Lds<FMT_Q4_K>;
+__device__ __forceinline__ void load_q5_K(__amdgpu_buffer_rsrc_t rw, int nsb, int ks, int tid, Q5KRegs &r) {
+    const int sb = ks >> 1, half = ks & 1;
+    const int col = tid >> 2, c = 4 * half + (tid & 3);
+    r.v = __builtin_amdgcn_raw_buffer_load_b128(rw, (col * nsb + sb) * 176 + 48 + 16 * c, 0, 0);
+    r.qh = __builtin_amdgcn_raw_buffer_load_b128(rw, (col * nsb + sb) * 176 + 16 + 16 * (c & 1), 0, 0);
+    const int hcol = (tid >> 8) * 64 + (tid & 63);
+    r.h = __builtin_amdgcn_raw_buffer_load_b128(rw, (hcol * nsb + sb) * 176, 0, 0);
+}
+
+template <int FMT, typename Regs>
+__device__ __forceinline__ void store_kquant(const Regs &r, uint8_t *buf, int ks, int tid) {
+    using L = Lds<FMT>;
     uint8_t *sB = buf + L::OFF_B_CODES;
     float2 *sW = reinterpret_cast<float2 *>(buf + L::OFF_B_SCALE);
     _Float16 *sMin = reinterpret_cast<_Float16 *>(buf + L::OFF_B_MIN);
     {
         const int col = tid >> 2, cl = tid & 3;      // cl: chunk within this half
-        const u32x4 lo = r.v & 0x0F0F0F0Fu;
-        const u32x4 hi = (r.v >> 4) & 0x0F0F0F0Fu;
+        u32x4 lo = r.v & 0x0F0F0F0Fu;
+        u32x4 hi = (r.v >> 4) & 0x0F0F0F0Fu;
+        if constexpr (FMT == FMT_Q5_K) {
+            const int g = 2 * (ks & 1) + (cl >> 1);   // 32-byte group of the super-block
+            lo |= ((r.qh >> (2 * g)) & 0x01010101u) << 4;
+            hi |= ((r.qh >> (2 * g + 1)) & 0x01010101u) << 4;
+        }
         // sub-blocks 2*(c/2) and 2*(c/2)+1 are blocks 2*(cl/2) and 2*(cl/2)+1 of this step
         const int gl = cl >> 1, kh = cl & 1;
         *reinterpret_cast<u32x4 *>(sB + code_off(2 * gl, col, kh)) = lo;
@@ -450,6 +477,8 @@ template <>
 struct WRegs<FMT_Q8_0> { Q80Regs r; };
 template <>
 struct WRegs<FMT_Q4_K> { Q4KRegs r; };
+template <>
+struct WRegs<FMT_Q5_K> { Q5KRegs r; };
 
 // One int8 MFMA at this point of the program.  The empty asm statements
 // redefine the operands just before it and its result just after it, so the
@@ -549,7 +578,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     const int wr = wv >> 1, wc = wv & 1;          // wave tile: rows 32*wr.., columns 64*wc..
     const int g = lane >> 5, l32 = lane & 31;
     int tx, ty;
-    tile_of_workgroup<FMT == FMT_Q4_K && !MOE>(tx, ty);
+    tile_of_workgroup<FMT != FMT_Q8_0 && !MOE>(tx, ty);
     // which GEMM of the set this column tile belongs to (workgroup-uniform)
     int gi = 0;
     for (int i = 1; i < set.count; i++)
@@ -571,7 +600,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
 
     // Buffers over this tile's rows of x and w (reads past M / N return 0).
     const int64_t xrow = int64_t(kb) * 36;
-    const int64_t wrow = FMT == FMT_Q8_0 ? int64_t(kb) * 34 : int64_t(K >> 8) * 144;
+    const int64_t wrow = weight_row_bytes(FMT, K);
     const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq + int64_t(m0) * xrow, int64_t(M - m0) * xrow);
     const __amdgpu_buffer_rsrc_t rw = tile_rsrc(wq + int64_t(n0) * wrow, int64_t(N - n0) * wrow);
 
@@ -600,14 +629,16 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     auto load_w = [&](int k) {
         if constexpr (FMT == FMT_Q8_0)
             load_q8_0(rw, kb, k, tid, wr_.r);
-        else
+        else if constexpr (FMT == FMT_Q4_K)
             load_q4_K(rw, K >> 8, k, tid, wr_.r);
+        else
+            load_q5_K(rw, K >> 8, k, tid, wr_.r);
     };
     auto store_w = [&](int k, uint8_t *buf) {
         if constexpr (FMT == FMT_Q8_0)
             store_q8_0(wr_.r, buf, tid);
         else
-            store_q4_K(wr_.r, buf, k, tid);
+            store_kquant<FMT>(wr_.r, buf, k, tid);
     };
 
     // Pipeline: step ks computes from buffer ks%2 (lds0 or lds1).  Meanwhile the DMA fills
@@ -693,7 +724,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
                 asm volatile("" : "+v"(acc[c]));
             }
         }
-        if constexpr (FMT == FMT_Q4_K && !DOTS) {
+        if constexpr (FMT != FMT_Q8_0 && !DOTS) {
             // the min term of this step's four sub-blocks
             const _Float16 *sMin = reinterpret_cast<const _Float16 *>(buf + L::OFF_B_MIN);
             // A = the four block sums s (high halves of the row's headers)
@@ -823,9 +854,9 @@ __device__ __forceinline__ void mv_unit_terms(__amdgpu_buffer_rsrc_t rx, int M, 
             const float t0 = ws0 * (float)dot8(w0, x.c0);
             const float t1 = ws1 * (float)dot8(w1, x.c1);
             acc[m] = __builtin_fmaf(h2f(x.h0), t0, acc[m]);
-            if constexpr (FMT == FMT_Q4_K) acc[m] = __builtin_fmaf(-dm0, h2f(x.h0 >> 16), acc[m]);
+            if constexpr (FMT != FMT_Q8_0) acc[m] = __builtin_fmaf(-dm0, h2f(x.h0 >> 16), acc[m]);
             acc[m] = __builtin_fmaf(h2f(x.h1), t1, acc[m]);
-            if constexpr (FMT == FMT_Q4_K) acc[m] = __builtin_fmaf(-dm1, h2f(x.h1 >> 16), acc[m]);
+            if constexpr (FMT != FMT_Q8_0) acc[m] = __builtin_fmaf(-dm1, h2f(x.h1 >> 16), acc[m]);
         }
     }
 }
@@ -844,7 +875,7 @@ __global__ __launch_bounds__(kMvThreads) void k_mmv(const uint8_t *__restrict__ 
         if (row >= set.tile_start[i]) gi = i;
     const int n = row - set.tile_start[gi], N = set.N[gi];
     const int kb = K >> 5;
-    const int64_t wrow = FMT == FMT_Q8_0 ? int64_t(kb) * 34 : int64_t(K >> 8) * 144;
+    const int64_t wrow = weight_row_bytes(FMT, K);
     const __amdgpu_buffer_rsrc_t rw = tile_rsrc(set.w[gi] + int64_t(n) * wrow, wrow);
     const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq, int64_t(M) * kb * 36);
     const int units = kb >> 1;   // block pairs (Q8_0) / sub-block pairs (Q4_K) in the row
@@ -897,15 +928,28 @@ __global__ __launch_bounds__(kMvThreads) void k_mmv(const uint8_t *__restrict__ 
         } else if (u < units) {
             uint32_t w0[8], w1[8];
             const int sb = u >> 2, grp = u & 3;   // super-block, 32-byte code group
-            const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(rw, 144 * sb, 0, 0);
-            const u32x4 q0 = __builtin_amdgcn_raw_buffer_load_b128(rw, 144 * sb + 16 + 32 * grp, 0, 0);
-            const u32x4 q1 = __builtin_amdgcn_raw_buffer_load_b128(rw, 144 * sb + 32 + 32 * grp, 0, 0);
+            constexpr int SB = FMT == FMT_Q4_K ? 144 : 176, QS = FMT == FMT_Q4_K ? 16 : 48;
+            const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(rw, SB * sb, 0, 0);
+            const u32x4 q0 = __builtin_amdgcn_raw_buffer_load_b128(rw, SB * sb + QS + 32 * grp, 0, 0);
+            const u32x4 q1 = __builtin_amdgcn_raw_buffer_load_b128(rw, SB * sb + QS + 16 + 32 * grp, 0, 0);
             const uint32_t q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
             // low nibbles: sub-block 2*grp; high nibbles: sub-block 2*grp+1
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 w0[i] = q[i] & 0x0f0f0f0fu;
                 w1[i] = (q[i] >> 4) & 0x0f0f0f0fu;
+            }
+            if constexpr (FMT == FMT_Q5_K) {
+                // fifth bits: byte l of the high-bit plane holds element l of
+                // sub-block j in bit j (here j = 2*grp and 2*grp+1)
+                const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rw, SB * sb + 16, 0, 0);
+                const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rw, SB * sb + 32, 0, 0);
+                const uint32_t qh[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    w0[i] |= ((qh[i] >> (2 * grp)) & 0x01010101u) << 4;
+                    w1[i] |= ((qh[i] >> (2 * grp + 1)) & 0x01010101u) << 4;
+                }
             }
             // 6-bit scale and min of sub-blocks j = 2*grp + {0, 1} (the
             // K-quant packing: j < 4 in the low six bits of bytes j and j+4;
@@ -1053,8 +1097,10 @@ static hipError_t launch_mv(const Plan &p, const GemmSet &set, const uint8_t *xb
         constexpr int MR = decltype(mr)::value;
         if (p.fmt == FMT_Q8_0)
             hipLaunchKernelGGL((k_mmv<FMT_Q8_0, MR>), grid, block, 0, stream, xb, set, int(M), int(K));
-        else
+        else if (p.fmt == FMT_Q4_K)
             hipLaunchKernelGGL((k_mmv<FMT_Q4_K, MR>), grid, block, 0, stream, xb, set, int(M), int(K));
+        else
+            hipLaunchKernelGGL((k_mmv<FMT_Q5_K, MR>), grid, block, 0, stream, xb, set, int(M), int(K));
     };
     if (M == 1)
         go(std::integral_constant<int, 1>{});
@@ -1094,21 +1140,21 @@ hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const vo
     // The GEMM kernel's LDS is static (its two k-step buffers, lds_bytes_for()
     // bytes, which the plan checked against the device); nothing dynamic.
     const size_t lds = 0;
-    if (p.fmt == FMT_Q8_0) {
+    auto go = [&](auto fmt) {
+        constexpr int F = decltype(fmt)::value;
         if (dots)
-            hipLaunchKernelGGL((k_mmq<FMT_Q8_0, true, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps,
+            hipLaunchKernelGGL((k_mmq<F, true, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps,
                                MoeArgs{});
         else
-            hipLaunchKernelGGL((k_mmq<FMT_Q8_0, false, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps,
+            hipLaunchKernelGGL((k_mmq<F, false, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps,
                                MoeArgs{});
-    } else {
-        if (dots)
-            hipLaunchKernelGGL((k_mmq<FMT_Q4_K, true, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps,
-                               MoeArgs{});
-        else
-            hipLaunchKernelGGL((k_mmq<FMT_Q4_K, false, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps,
-                               MoeArgs{});
-    }
+    };
+    if (p.fmt == FMT_Q8_0)
+        go(std::integral_constant<int, FMT_Q8_0>{});
+    else if (p.fmt == FMT_Q4_K)
+        go(std::integral_constant<int, FMT_Q4_K>{});
+    else
+        go(std::integral_constant<int, FMT_Q5_K>{});
     return hipGetLastError();
 }
 
@@ -1131,15 +1177,17 @@ hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t
     moe.tiles = tiles;
     moe.sorted = sorted;
     moe.topk = topk;
-    moe.expert_bytes = N * (p.fmt == FMT_Q8_0 ? (K / 32) * 34 : (K / 256) * 144);
+    moe.expert_bytes = N * weight_row_bytes(p.fmt, K);
     const dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, 1);
     const dim3 block(p.threads);
     const auto *xb = reinterpret_cast<const uint8_t *>(x);
     const int sps = int(p.steps_per_split);
     if (p.fmt == FMT_Q8_0)
         hipLaunchKernelGGL((k_mmq<FMT_Q8_0, false, true>), grid, block, 0, stream, xb, set, int(T), int(K), sps, moe);
-    else
+    else if (p.fmt == FMT_Q4_K)
         hipLaunchKernelGGL((k_mmq<FMT_Q4_K, false, true>), grid, block, 0, stream, xb, set, int(T), int(K), sps, moe);
+    else
+        hipLaunchKernelGGL((k_mmq<FMT_Q5_K, false, true>), grid, block, 0, stream, xb, set, int(T), int(K), sps, moe);
     return hipGetLastError();
 }
 

@@ -13,7 +13,13 @@
 
 namespace mmq {
 
-enum Fmt : int { FMT_Q8_0 = 0, FMT_Q4_K = 1 };
+enum Fmt : int { FMT_Q8_0 = 0, FMT_Q4_K = 1, FMT_Q5_K = 2 };
+
+// Bytes of one weight row of K values (Q8_0: 34-byte blocks of 32; Q4_K /
+// Q5_K: 144- / 176-byte super-blocks of 256).
+constexpr int64_t weight_row_bytes(int fmt, int64_t K) {
+    return fmt == FMT_Q8_0 ? (K / 32) * 34 : (K / 256) * (fmt == FMT_Q4_K ? 144 : 176);
+}
 
 // Geometry of the GEMM kernel (must match the kernel's compile-time tile).
 constexpr int kTileM = 128;        // output rows per workgroup
@@ -32,12 +38,12 @@ constexpr int kSplitSlots = 1;         // workgroups per CU a split aims for
 // LDS bytes for the kernel's layouts: two k-step buffers, each with codes
 // block-major (32 B per block per row, no padding), the activation block
 // headers [row][4] as dwords, and the weight scale pairs [4][col] as two fp32;
-// Q4_K adds the split min operand [col][2][4] fp16.  Q4_K comes to exactly
-// 80 KiB, so two workgroups share a CU's 160 KiB.
+// the K-quants (Q4_K, Q5_K) add the split min operand [col][2][4] fp16 and
+// come to exactly 80 KiB, so two workgroups share a CU's 160 KiB.
 constexpr int64_t lds_bytes_for(int fmt) {
     int64_t step = int64_t(kTileM + kTileN) * 32 * kBlocksPerStage + int64_t(kTileM) * kBlocksPerStage * 4 +
                    int64_t(kBlocksPerStage) * kTileN * 8;
-    if (fmt == FMT_Q4_K) step += int64_t(kTileN) * 2 * kBlocksPerStage * 2;
+    if (fmt != FMT_Q8_0) step += int64_t(kTileN) * 2 * kBlocksPerStage * 2;
     return 2 * step;
 }
 
@@ -61,8 +67,10 @@ struct Plan {
     int64_t split_k = 1, steps_per_split = 0;
 };
 
-inline bool fmt_ok(int fmt) { return fmt == FMT_Q8_0 || fmt == FMT_Q4_K; }
-inline const char *fmt_name(int fmt) { return fmt == FMT_Q8_0 ? "Q8_0" : fmt == FMT_Q4_K ? "Q4_K" : "?"; }
+inline bool fmt_ok(int fmt) { return fmt == FMT_Q8_0 || fmt == FMT_Q4_K || fmt == FMT_Q5_K; }
+inline const char *fmt_name(int fmt) {
+    return fmt == FMT_Q8_0 ? "Q8_0" : fmt == FMT_Q4_K ? "Q4_K" : fmt == FMT_Q5_K ? "Q5_K" : "?";
+}
 
 // Shape checks shared by the quantize pass.  Returns nullptr when fine.
 inline const char *check_quantize_shape(int64_t M, int64_t K) {
@@ -82,7 +90,7 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
     if (!fmt_ok(fmt)) return fail("unknown weight format");
     if (M < 1 || N < 1 || K < 1) return fail("M, N and K must be >= 1");
     if (K % 256 != 0)
-        return fail(fmt == FMT_Q4_K ? "K must be a multiple of 256 (whole Q4_K super-blocks)"
+        return fail(fmt != FMT_Q8_0 ? "K must be a multiple of 256 (whole K-quant super-blocks)"
                                     : "K must be a multiple of 256 (whole 8-block k-steps)");
     if (M > INT32_MAX || N > INT32_MAX) return fail("M and N must fit in int32");
     // byte offsets inside one 128-row tile are 32-bit buffer offsets

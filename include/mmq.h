@@ -63,6 +63,7 @@ extern "C" {
 
 #define MMQ_FMT_Q8_0 0
 #define MMQ_FMT_Q4_K 1
+#define MMQ_FMT_Q5_K 2
 
 /* Quantize fp32 activations to q8_1 ("13 . r7-r8 raw-byte MMQ kernel",
  * section 3.2; q8_1 fields from "When Does a Kernel Win Surface?", 6.2).
@@ -104,11 +105,24 @@ int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out,
 int mmq_gemm_q4_K(const void *x_q8_1, const void *w_q4_K, float *out,
                   int64_t M, int64_t N, int64_t K, void *stream);
 
+/* q8_1 activations x Q5_K weights -> fp32 (a K-quant family "When Does a
+ * Kernel Win Surface?" names in section 2; block term: the Q4_K affine
+ * identity of its section 6.2 with 5-bit codes).
+ *   x_q8_1: M x (K/32) q8_1 blocks; w_q5_K: N x (K/256) super-blocks of
+ *   176 B (fp16 d @0, fp16 dmin @2, 12 B of 6-bit scales/mins @4 packed as
+ *   for Q4_K, 32 B of high bits @16, 128 B of low nibbles @48 in the Q4_K
+ *   order; the code of element e is its nibble + 16 * bit (e/32) of
+ *   high-bit byte e%32); out: M x N fp32 row-major, fully overwritten.
+ *   Requires K % 256 == 0.  Split-K and M <= 8 shapes behave as for
+ *   mmq_gemm_q8_0. */
+int mmq_gemm_q5_K(const void *x_q8_1, const void *w_q5_K, float *out,
+                  int64_t M, int64_t N, int64_t K, void *stream);
+
 /* Several GEMMs of one format that read the same q8_1 activations (the
  * layer pipeline of "13 . r7-r8 raw-byte MMQ kernel": quantize once per
  * distinct input, e.g. the q, k and v projections, or gate and up), computed
  * by one launch whose grid covers the column tiles of all of them.
- *   fmt: MMQ_FMT_Q8_0 or MMQ_FMT_Q4_K; count: 1..8;
+ *   fmt: MMQ_FMT_Q8_0, MMQ_FMT_Q4_K or MMQ_FMT_Q5_K; count: 1..8;
  *   x_q8_1: M x (K/32) q8_1 blocks, shared;
  *   w[g]: N[g] x K weights of format fmt; out[g]: M x N[g] fp32 row-major,
  *   fully overwritten; the arrays w, out and N are host memory (read during
@@ -153,8 +167,8 @@ int mmq_moe_gemm(int fmt, const void *x_q8_1, const void *w, int n_experts, cons
                  void *stream);
 
 /* Test entry: the exact int32 block dots I[m,n,b] through the same staging
- * and matrix-core code as the GEMM of format `fmt` (MMQ_FMT_Q8_0 or
- * MMQ_FMT_Q4_K), written to dots[(m*N + n)*(K/32) + b].  Same refusal rules
+ * and matrix-core code as the GEMM of format `fmt` (MMQ_FMT_Q8_0,
+ * MMQ_FMT_Q4_K or MMQ_FMT_Q5_K), written to dots[(m*N + n)*(K/32) + b].  Same refusal rules
  * as the GEMM. */
 int mmq_debug_block_dots(int fmt, const void *x_q8_1, const void *w, int32_t *dots,
                          int64_t M, int64_t N, int64_t K, void *stream);

@@ -31,7 +31,8 @@ def _dev(a):
 
 
 def _weights(fmt, E, N, K, seed):
-    f = inputs.q8_0_weights if fmt == mmq.FMT_Q8_0 else inputs.q4_K_weights
+    f = {mmq.FMT_Q8_0: inputs.q8_0_weights, mmq.FMT_Q4_K: inputs.q4_K_weights,
+         mmq.FMT_Q5_K: inputs.q5_K_weights}[fmt]
     return f(E * N, K, seed)   # E matrices of N rows, one after another
 
 
@@ -52,7 +53,7 @@ def _check(fmt, got, ref):
         assert rep["bit_identical_fraction"] == 1.0
 
 
-@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K, mmq.FMT_Q5_K])
 @pytest.mark.parametrize("T,E,topk,N,K,skew", [
     (37, 8, 3, 200, 512, 0.0),      # ragged N, several experts per tile row
     (300, 16, 4, 130, 1024, 2.0),   # skewed: popular experts span several 128-row tiles
@@ -82,7 +83,7 @@ def test_moe_one_expert_takes_all(fmt):
     _check(fmt, got, oracle.moe_gemm(fmt, xq, w, ids, topk, T, N, K, E, nthreads=16))
     # equal to the dense GEMM with expert 2's matrix
     wrow = w.reshape(E, N, *w.shape[1:])[2]
-    dense = (mmq.gemm_q8_0 if fmt == mmq.FMT_Q8_0 else mmq.gemm_q4_K)(_dev(xq), _dev(wrow), T, N, K)
+    dense = mmq.gemm(fmt, _dev(xq), _dev(wrow), T, N, K)
     torch.cuda.synchronize()
     assert np.array_equal(got.view(np.uint32), dense.cpu().numpy().view(np.uint32))
 

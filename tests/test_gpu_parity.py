@@ -77,10 +77,14 @@ def test_quantize_special_blocks():
 # ------------------------------------------------------------------ block dots
 
 def _weights(fmt, N, K, seed):
-    return inputs.q8_0_weights(N, K, seed) if fmt == mmq.FMT_Q8_0 else inputs.q4_K_weights(N, K, seed)
+    gen = {mmq.FMT_Q8_0: inputs.q8_0_weights, mmq.FMT_Q4_K: inputs.q4_K_weights, mmq.FMT_Q5_K: inputs.q5_K_weights}
+    return gen[fmt](N, K, seed)
 
 
-@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+FMTS = [mmq.FMT_Q8_0, mmq.FMT_Q4_K, mmq.FMT_Q5_K]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (200, 300, 768), (128, 128, 512), (33, 517, 256)])
 def test_block_dots_bit_exact(fmt, M, N, K):
     _say(f"dots fmt={fmt} M={M} N={N} K={K}")
@@ -89,7 +93,8 @@ def test_block_dots_bit_exact(fmt, M, N, K):
     dots = torch.full((M, N, K // 32), -(2 ** 31), dtype=torch.int32, device=DEV)
     mmq.debug_block_dots(fmt, _to_dev(x), _to_dev(w), M, N, K, dots)
     torch.cuda.synchronize()
-    ref = (oracle.block_dots_q8_0 if fmt == mmq.FMT_Q8_0 else oracle.block_dots_q4_K)(x, w, M, N, K)
+    ref = {mmq.FMT_Q8_0: oracle.block_dots_q8_0, mmq.FMT_Q4_K: oracle.block_dots_q4_K,
+           mmq.FMT_Q5_K: oracle.block_dots_q5_K}[fmt](x, w, M, N, K)
     assert np.array_equal(dots.cpu().numpy(), ref)
 
 
@@ -97,8 +102,7 @@ def test_block_dots_bit_exact(fmt, M, N, K):
 
 def _run_gemm(fmt, xq, w, M, N, K):
     out = _nan_out(M, N)
-    f = mmq.gemm_q8_0 if fmt == mmq.FMT_Q8_0 else mmq.gemm_q4_K
-    f(_to_dev(xq), _to_dev(w), M, N, K, out)
+    mmq.gemm(fmt, _to_dev(xq), _to_dev(w), M, N, K, out)
     torch.cuda.synchronize()
     o = out.cpu().numpy()
     assert not np.isnan(o).any(), "output element left unwritten"
@@ -106,11 +110,11 @@ def _run_gemm(fmt, xq, w, M, N, K):
 
 
 def _oracle_gemm(fmt, xq, w, M, N, K, rows=None):
-    f = oracle.gemm_q8_0 if fmt == mmq.FMT_Q8_0 else oracle.gemm_q4_K
+    f = {mmq.FMT_Q8_0: oracle.gemm_q8_0, mmq.FMT_Q4_K: oracle.gemm_q4_K, mmq.FMT_Q5_K: oracle.gemm_q5_K}[fmt]
     return f(xq, w, M, N, K, nthreads=16, rows=rows)
 
 
-@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (64, 256, 512), (200, 300, 768), (129, 257, 1024),
                                    (300, 130, 2048)])
 def test_gemm_matches_oracle(fmt, M, N, K):
@@ -142,7 +146,8 @@ def _exact_and_scale(fmt, xq, w, M, N, K):
     if fmt == mmq.FMT_Q8_0:
         wd, wc = npdecode.q8_0_fields(w.reshape(N, kb, 34))
     else:
-        d, dmin, sc, mn, codes = npdecode.q4_K_fields(w.reshape(N, K // 256, 144))
+        fields = npdecode.q4_K_fields if fmt == mmq.FMT_Q4_K else npdecode.q5_K_fields
+        d, dmin, sc, mn, codes = fields(w.reshape(N, K // 256, -1))
         wc = codes.reshape(N, kb, 32)
         wd = (d[..., None] * sc).reshape(N, kb)
     # exact int block dots as fp64 matrix products, one per block
@@ -181,7 +186,7 @@ def _split_k(fmt, M, N, K):
     return int(re.search(r"split_k=(\d+)", mmq.plan_describe(fmt, M, N, K)[1]).group(1))
 
 
-@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,N,K", [(64, 64, 3584), (129, 257, 1024), (200, 300, 2048), (100, 100, 18944),
                                    (512, 512, 3584)])
 def test_split_k_gemm_matches_oracle(fmt, M, N, K):
@@ -201,7 +206,7 @@ def test_split_k_gemm_matches_oracle(fmt, M, N, K):
     assert rep["normalized_max_error"] <= metrics.TOL
 
 
-@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_gemm_on_random_q8_1_fields(fmt):
     """Fields not tied to each other (s independent of the codes): the
     contraction must read d, s and the codes exactly as stored."""
@@ -257,6 +262,26 @@ def test_full_size_configs_sampled_rows(cfg):
     assert rep["normalized_max_error"] <= metrics.TOL
 
 
+def test_q5_K_full_size_sampled_rows():
+    """Q5_K at the 7B gate/up shape (M=2048 N=18944 K=3584), full launch,
+    sampled output rows against the oracle."""
+    fmt, M, N, K = mmq.FMT_Q5_K, 2048, 18944, 3584
+    _say(f"Q5_K full size M={M} N={N} K={K}")
+    x = inputs.activations(M, K, 7001)
+    w = _weights(fmt, N, K, 7002)
+    xq_dev = mmq.quantize_q8_1(_to_dev(x))
+    out = _nan_out(M, N)
+    mmq.gemm_q5_K(xq_dev, _to_dev(w), M, N, K, out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert not np.isnan(o).any()
+    xq = xq_dev.cpu().numpy()
+    rows = [0, 1, 1000, M - 128, M - 1]
+    rep = metrics.report(o[rows], _oracle_gemm(fmt, np.ascontiguousarray(xq[rows]), w, len(rows), N, K))
+    _say(rep)
+    assert rep["normalized_max_error"] <= metrics.TOL
+
+
 @pytest.mark.parametrize("M", inputs.LAYER_M)
 def test_layer_gemm_set_sampled_rows(M):
     """The seven Q4_K projection GEMMs of one 7B layer at M tokens, with one
@@ -291,7 +316,7 @@ def test_layer_gemm_set_sampled_rows(M):
         torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,Ns,K", [(200, (384, 128, 130), 1024), (129, (257,), 512),
                                      (2048, (3584, 512, 512), 3584), (512, (18944, 18944), 3584)])
 def test_gemm_multi_matches_oracle(fmt, M, Ns, K):
@@ -331,7 +356,7 @@ def test_gemm_multi_unsplit_member_equals_single_launch():
     assert torch.equal(outs[0], single)
 
 
-@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M", [1, 2, 3, 8])
 @pytest.mark.parametrize("N,K", [(1, 256), (300, 768), (3584, 3584), (129, 18944)])
 def test_matvec_matches_oracle(fmt, M, N, K):
@@ -360,7 +385,7 @@ def test_matvec_boundary_m8_m9():
         assert rep["normalized_max_error"] <= metrics.TOL
 
 
-@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_matvec_layer_set_decode(fmt):
     """The 7B layer's projections at one token: q+k+v and gate+up through
     one matvec launch each, o and down alone; each member equal to its own
@@ -376,7 +401,7 @@ def test_matvec_layer_set_decode(fmt):
         torch.cuda.synchronize()
         for g, (n, w) in enumerate(zip(Ns, ws)):
             o = outs[g].cpu().numpy()
-            single = (mmq.gemm_q8_0 if fmt == mmq.FMT_Q8_0 else mmq.gemm_q4_K)(_to_dev(xq), _to_dev(w), M, n, K)
+            single = mmq.gemm(fmt, _to_dev(xq), _to_dev(w), M, n, K)
             torch.cuda.synchronize()
             assert np.array_equal(o.view(np.uint32), single.cpu().numpy().view(np.uint32))
             rep = metrics.report(o, _oracle_gemm(fmt, xq, w, M, n, K))
