@@ -53,13 +53,24 @@ def traffic_for(kernel: str):
     return rec.get("bytes_per_launch")
 
 
-def make_inputs(cfg: int):
+def make_inputs(cfg):
+    """`cfg`: a numbered configuration, or "fmt:MxNxK" (seeds 7000 + 1, 2)."""
     from block_quantized_int8_q8_amd import inputs
-    fmt, M, N, K = inputs.CONFIGS[cfg]
-    x = inputs.activations(M, K, inputs.seed_for(cfg, 0))
-    w = (inputs.q8_0_weights(N, K, inputs.seed_for(cfg, 1)) if fmt == "q8_0"
-         else inputs.q4_K_weights(N, K, inputs.seed_for(cfg, 1)))
-    return fmt, M, N, K, x, w
+    if isinstance(cfg, int):
+        fmt, M, N, K = inputs.CONFIGS[cfg]
+        sx, sw = inputs.seed_for(cfg, 0), inputs.seed_for(cfg, 1)
+    else:
+        fmt, shape = cfg.split(":")
+        M, N, K = (int(v) for v in shape.split("x"))
+        sx, sw = inputs.seed_for(7, 1), inputs.seed_for(7, 2)
+    x = inputs.activations(M, K, sx)
+    gen = {"q8_0": inputs.q8_0_weights, "q4_K": inputs.q4_K_weights, "q5_K": inputs.q5_K_weights}[fmt]
+    return fmt, M, N, K, x, gen(N, K, sw)
+
+
+def _fmt_code(fmt: str) -> int:
+    import block_quantized_int8_q8_amd as mmq
+    return {"q8_0": mmq.FMT_Q8_0, "q4_K": mmq.FMT_Q4_K, "q5_K": mmq.FMT_Q5_K}[fmt]
 
 
 def time_config(cfg: int, steps: int, warmup: int, check: bool = True):
@@ -72,7 +83,11 @@ def time_config(cfg: int, steps: int, warmup: int, check: bool = True):
     wd = torch.from_numpy(w).to(dev)
     xq = torch.empty((M, K // 32, 36), dtype=torch.uint8, device=dev)
     out = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
-    gemm = mmq.gemm_q8_0 if fmt == "q8_0" else mmq.gemm_q4_K
+    code = _fmt_code(fmt)
+
+    def gemm(*a, **k):
+        return mmq.gemm(code, *a, **k)
+
     stream = torch.cuda.current_stream()
 
     def step():
@@ -130,7 +145,7 @@ def check_parity(fmt, M, N, K, x, w, xq_dev, out_dev):
     q_ok = bool(np.array_equal(xq_dev.cpu().numpy(), xq))
     o = out_dev.cpu().numpy()
     rows = sorted(set([0, M - 1, M // 2] + list(np.random.default_rng(0).integers(0, M, 5))))
-    f = oracle.gemm_q8_0 if fmt == "q8_0" else oracle.gemm_q4_K
+    f = {"q8_0": oracle.gemm_q8_0, "q4_K": oracle.gemm_q4_K, "q5_K": oracle.gemm_q5_K}[fmt]
     ref = f(np.ascontiguousarray(xq[rows]), w, len(rows), N, K, nthreads=min(16, os.cpu_count() or 1))
     rep = metrics.report(o[rows], ref)
     return {
@@ -237,8 +252,8 @@ def time_decode(M: int, fmt_name: str, steps: int, warmup: int, check: bool = Tr
     from block_quantized_int8_q8_amd import inputs
 
     dev = torch.device("cuda:0")
-    fmt = mmq.FMT_Q8_0 if fmt_name == "q8_0" else mmq.FMT_Q4_K
-    wgen = inputs.q8_0_weights if fmt == mmq.FMT_Q8_0 else inputs.q4_K_weights
+    fmt = _fmt_code(fmt_name)
+    wgen = {"q8_0": inputs.q8_0_weights, "q4_K": inputs.q4_K_weights, "q5_K": inputs.q5_K_weights}[fmt_name]
     shapes = {g: (n, k) for g, n, k in inputs.LAYER_7B}
     groups = []
     for name, K, gemms in inputs.LAYER_INPUTS:
@@ -268,7 +283,7 @@ def time_decode(M: int, fmt_name: str, steps: int, warmup: int, check: bool = Tr
         import oracle
         from tests import metrics
         worst, unwritten = 0.0, 0
-        f = oracle.gemm_q8_0 if fmt == mmq.FMT_Q8_0 else oracle.gemm_q4_K
+        f = {mmq.FMT_Q8_0: oracle.gemm_q8_0, mmq.FMT_Q4_K: oracle.gemm_q4_K, mmq.FMT_Q5_K: oracle.gemm_q5_K}[fmt]
         for g in groups:
             xq = oracle.quantize_q8_1(g["x_host"])
             for n, w, o in zip(g["Ns"], g["w_host"], g["out"]):
@@ -343,8 +358,8 @@ def time_moe(fmt_name: str, steps: int, warmup: int, check: bool = True):
     from block_quantized_int8_q8_amd import inputs
 
     dev = torch.device("cuda:0")
-    fmt = mmq.FMT_Q8_0 if fmt_name == "q8_0" else mmq.FMT_Q4_K
-    wgen = inputs.q8_0_weights if fmt == mmq.FMT_Q8_0 else inputs.q4_K_weights
+    fmt = _fmt_code(fmt_name)
+    wgen = {"q8_0": inputs.q8_0_weights, "q4_K": inputs.q4_K_weights, "q5_K": inputs.q5_K_weights}[fmt_name]
     E, topk0, T0 = inputs.MOE_SHAPE["n_experts"], inputs.MOE_SHAPE["topk"], inputs.MOE_T
     ids0 = inputs.moe_ids(T0, E, topk0, inputs.moe_seed("ids"))
     stream = torch.cuda.current_stream()
@@ -455,6 +470,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="benchmark shape (2: Q8_0 2048x3584x3584)")
     ap.add_argument("--extra-configs", default="3,4", help="other shapes timed in the same run")
+    ap.add_argument("--extra-shapes", default="q5_K:2048x18944x3584",
+                    help="fmt:MxNxK GEMMs timed in the same run ('' for none)")
     ap.add_argument("--layer-m", default="512,2048,8192",
                     help="token counts at which the 7B layer GEMM set is timed ('' for none)")
     ap.add_argument("--decode", default="q4_K:1,q8_0:1,q4_K:8",
@@ -497,6 +514,12 @@ def main():
             extra[f"config{c}"] = {k: r[k] for k in ("fmt", "M", "N", "K", "ms_per_step", "tops_step",
                                                       "gemm_ms_avg", "gemm_tops", "quant_gbs", "parity")}
             extra[f"config{c}"]["gemm_frac_of_int8_peak"] = r["gemm_tops"] / PEAK_INT8_TOPS
+
+    for spec in [v.strip() for v in args.extra_shapes.split(",") if v.strip()]:
+        r = time_config(spec, max(5, args.steps // 5), 2, check=not args.no_check)
+        extra[spec] = {k: r[k] for k in ("fmt", "M", "N", "K", "ms_per_step", "tops_step", "gemm_ms_avg",
+                                         "gemm_tops", "quant_gbs", "parity")}
+        extra[spec]["gemm_frac_of_int8_peak"] = r["gemm_tops"] / PEAK_INT8_TOPS
 
     for m in [int(v) for v in args.layer_m.split(",") if v.strip()]:
         extra[f"layer_M{m}"] = time_layer(m, max(3, args.steps // 10), 1, check=not args.no_check)

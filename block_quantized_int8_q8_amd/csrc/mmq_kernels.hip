@@ -410,15 +410,17 @@ struct Q4KRegs {
     u32x4 h;
 };
 
-// Q5_K: the same chunks and header as Q4_K (its scales use the same packing),
-// plus the 16 high-bit bytes of the chunk's k-half: byte l of the high-bit
-// plane carries the fifth bit of element l of every sub-block j in bit j, so
-// the chunk's codes take bits 2g (low nibbles, sub-block 2g) and 2g+1 (high
-// nibbles) of the same 16 bytes.
+// Q5_K: the header as for Q4_K (its scales use the same packing).  Codes:
+// byte l of the high-bit plane carries the fifth bit of element l of every
+// sub-block j in bit j, so a thread takes the same 8 byte positions
+// l = 8*cl .. 8*cl+7 (cl = tid % 4) of both 32-byte code groups of the step
+// and the 8 high-bit bytes at those positions, which serve both groups:
+// 6 registers of codes and high bits where 16-byte chunks per group would
+// need 8 (the kernel is at its register limit).
 struct Q5KRegs {
-    u32x4 v;
+    uint2 v0, v1;   // code bytes 8cl.. of groups 2*half and 2*half+1
+    uint2 qh;       // high-bit bytes 8cl..
     u32x4 h;
-    u32x4 qh;
 };
 
 __device__ __forceinline__ void load_q4_K(__amdgpu_buffer_rsrc_t rw, int nsb, int ks, int tid, Q4KRegs &r) {
@@ -431,9 +433,15 @@ __device__ __forceinline__ void load_q4_K(__amdgpu_buffer_rsrc_t rw, int nsb, in
 
 __device__ __forceinline__ void load_q5_K(__amdgpu_buffer_rsrc_t rw, int nsb, int ks, int tid, Q5KRegs &r) {
     const int sb = ks >> 1, half = ks & 1;
-    const int col = tid >> 2, c = 4 * half + (tid & 3);
-    r.v = __builtin_amdgcn_raw_buffer_load_b128(rw, (col * nsb + sb) * 176 + 48 + 16 * c, 0, 0);
-    r.qh = __builtin_amdgcn_raw_buffer_load_b128(rw, (col * nsb + sb) * 176 + 16 + 16 * (c & 1), 0, 0);
+    const int col = tid >> 2, cl = tid & 3;
+    const int base = (col * nsb + sb) * 176;
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(rw, base + 48 + 64 * half + 8 * cl, 0, 0);
+    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(rw, base + 48 + 64 * half + 32 + 8 * cl, 0, 0);
+    const u32x2 q = __builtin_amdgcn_raw_buffer_load_b64(rw, base + 16 + 8 * cl, 0, 0);
+    r.v0 = make_uint2(a.x, a.y);
+    r.v1 = make_uint2(b.x, b.y);
+    r.qh = make_uint2(q.x, q.y);
     const int hcol = (tid >> 8) * 64 + (tid & 63);
     r.h = __builtin_amdgcn_raw_buffer_load_b128(rw, (hcol * nsb + sb) * 176, 0, 0);
 }
@@ -444,15 +452,28 @@ __device__ __forceinline__ void store_kquant(const Regs &r, uint8_t *buf, int ks
     uint8_t *sB = buf + L::OFF_B_CODES;
     float2 *sW = reinterpret_cast<float2 *>(buf + L::OFF_B_SCALE);
     _Float16 *sMin = reinterpret_cast<_Float16 *>(buf + L::OFF_B_MIN);
-    {
-        const int col = tid >> 2, cl = tid & 3;      // cl: chunk within this half
-        u32x4 lo = r.v & 0x0F0F0F0Fu;
-        u32x4 hi = (r.v >> 4) & 0x0F0F0F0Fu;
-        if constexpr (FMT == FMT_Q5_K) {
-            const int g = 2 * (ks & 1) + (cl >> 1);   // 32-byte group of the super-block
-            lo |= ((r.qh >> (2 * g)) & 0x01010101u) << 4;
-            hi |= ((r.qh >> (2 * g + 1)) & 0x01010101u) << 4;
+    if constexpr (FMT == FMT_Q5_K) {
+        const int col = tid >> 2, cl = tid & 3;
+        // element positions 8cl..8cl+7: k-half cl/2 of each block, bytes 8*(cl%2).. of it
+        const int off = code_off(0, col, cl >> 1) + 8 * (cl & 1);
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const uint2 v = i ? r.v1 : r.v0;
+            const int g = 2 * (ks & 1) + i;             // group of the super-block
+            uint2 lo = make_uint2(v.x & 0x0F0F0F0Fu, v.y & 0x0F0F0F0Fu);
+            uint2 hi = make_uint2((v.x >> 4) & 0x0F0F0F0Fu, (v.y >> 4) & 0x0F0F0F0Fu);
+            lo.x |= ((r.qh.x >> (2 * g)) & 0x01010101u) << 4;
+            lo.y |= ((r.qh.y >> (2 * g)) & 0x01010101u) << 4;
+            hi.x |= ((r.qh.x >> (2 * g + 1)) & 0x01010101u) << 4;
+            hi.y |= ((r.qh.y >> (2 * g + 1)) & 0x01010101u) << 4;
+            // sub-blocks 2g and 2g+1 are blocks 2i and 2i+1 of this step
+            *reinterpret_cast<uint2 *>(sB + off + (2 * i) * kBlockBytes) = lo;
+            *reinterpret_cast<uint2 *>(sB + off + (2 * i + 1) * kBlockBytes) = hi;
         }
+    } else {
+        const int col = tid >> 2, cl = tid & 3;      // cl: chunk within this half
+        const u32x4 lo = r.v & 0x0F0F0F0Fu;
+        const u32x4 hi = (r.v >> 4) & 0x0F0F0F0Fu;
         // sub-blocks 2*(c/2) and 2*(c/2)+1 are blocks 2*(cl/2) and 2*(cl/2)+1 of this step
         const int gl = cl >> 1, kh = cl & 1;
         *reinterpret_cast<u32x4 *>(sB + code_off(2 * gl, col, kh)) = lo;
