@@ -675,11 +675,30 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the DMA has landed in LDS
     __syncthreads();
 
+    // MoE: a wave whose 32 rows lie past its expert's last routed row (the
+    // partial last tile of an expert) has nothing to compute; it only takes
+    // its part in staging, which leaves the SIMD's VALU to the other waves.
+    bool wave_live = true;
+    if constexpr (MOE) wave_live = __builtin_amdgcn_readfirstlane(int(mt.y + 32 * wr < mt.z)) != 0;
+
     auto step = [&](auto parity, int j) {
         constexpr int P = decltype(parity)::value;
         const int ks = ks0 + j;                   // the k-step; j is its place in this workgroup's range
         uint8_t *const buf = P ? lds1 : lds0;     // local step j (j % 2 == P)
         uint8_t *const nxt = P ? lds0 : lds1;     // local step j + 1
+        if constexpr (MOE) {
+            if (!wave_live) {
+                if (j + 1 < nloc) {
+#pragma unroll
+                    for (int piece = 0; piece < 3; piece++) dma_activations<FMT>(rx, adma, ks + 1, nxt, wv, piece);
+                    store_w(ks + 1, nxt);
+                }
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+                if (j + 2 < nloc) load_w(ks + 2);
+                return;
+            }
+        }
         const unsigned short *sHdr = reinterpret_cast<const unsigned short *>(buf + L::OFF_A_HDR);
         const uint8_t *sB = buf + L::OFF_B_CODES;
         const float2 *sW = reinterpret_cast<const float2 *>(buf + L::OFF_B_SCALE);

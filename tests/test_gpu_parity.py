@@ -480,3 +480,44 @@ def test_quantize_refusals():
         mmq.quantize_q8_1(x, torch.empty((4, 2, 36), dtype=torch.uint8, device=DEV))
     ok, desc = mmq.plan_describe(mmq.FMT_Q4_K, 2048, 18944, 3584)
     assert ok, desc
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [(mmq.FMT_Q4_K, 1, 4608, 3584),      # matvec
+                                       (mmq.FMT_Q8_0, 512, 512, 3584),     # split-K: zero fill + atomics
+                                       (mmq.FMT_Q5_K, 300, 640, 1024)])    # tiled
+def test_graph_capture_replays_match_eager(fmt, M, N, K):
+    """The library's launches captured in a HIP graph (quantize + GEMM on the
+    capture stream): every replay, with eager work and synchronizations in
+    between, reproduces the eager output (split-K replays within the
+    tolerance, since their atomics add in any order)."""
+    _say(f"graph capture fmt={fmt} M={M} N={N} K={K}")
+    x = _to_dev(inputs.activations(M, K, 140 + M))
+    w = _to_dev(_weights(fmt, N, K, 141))
+    xq = torch.empty((M, K // 32, 36), dtype=torch.uint8, device=DEV)
+    out = _nan_out(M, N)
+    mmq.quantize_q8_1(x, xq)
+    mmq.gemm(fmt, xq, w, M, N, K, out)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    split = _kernel(fmt, M, N, K) == "mmq" and _split_k(fmt, M, N, K) > 1
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            mmq.quantize_q8_1(x, xq)
+            mmq.gemm(fmt, xq, w, M, N, K, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        xq.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert not np.isnan(got).any(), f"replay {rep}: output left unwritten"
+        if split:
+            assert metrics.normalized_max_error(got, eager.cpu().numpy()) <= metrics.TOL
+        else:
+            assert torch.equal(out, eager), f"replay {rep} differs from the eager output"
