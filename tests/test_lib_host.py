@@ -138,3 +138,16 @@ def test_decode_sizes_plan_the_matvec_kernel(fmt, M, N, K):
     assert "threads=256" in desc and "lds=0" in desc and "split_k=1" in desc
     # the same shape with one more row is tiled
     assert "kernel=mmq" in mmq.plan_for_limits(fmt, 9, N, K, LDS_GFX950, 256)[1]
+
+
+def test_q5_K_plans_like_q4_K():
+    """Q5_K stages the same LDS layout as Q4_K (codes unpacked to one byte,
+    scales, split min operand): 80 KiB, two workgroups per CU."""
+    for M, N, K in [(2048, 18944, 3584), (512, 512, 3584), (1, 3584, 3584)]:
+        a = mmq.plan_for_limits(mmq.FMT_Q5_K, M, N, K, LDS_GFX950, 256)
+        b = mmq.plan_for_limits(mmq.FMT_Q4_K, M, N, K, LDS_GFX950, 256)
+        assert a[0] and b[0]
+        assert a[1].replace("Q5_K", "Q4_K") == b[1]
+    assert "lds=81920" in mmq.plan_for_limits(mmq.FMT_Q5_K, 2048, 18944, 3584, LDS_GFX950, 256)[1]
+    ok, why = mmq.plan_for_limits(mmq.FMT_Q5_K, 64, 256, 512 + 32, LDS_GFX950, 256)
+    assert not ok and "super-blocks" in why
