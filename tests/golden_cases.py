@@ -68,3 +68,21 @@ def gemm_q4_K_case(pack_scale_min=None):
     w[0, 0, 12:16] = g["sc"] | (g["m"] << 4)
     w[0, 0, 16:] = g["code"] | (g["code"] << 4)
     return x, w, K, g["out"]
+
+
+def gemm_q5_K_case():
+    """-> (x fp32 [1, K], w Q5_K bytes [1, 1, 176], K, expected out): the
+    Q4_K case's fields plus a high-bit plane with only byte 0 non-zero."""
+    g = json.load(open(os.path.join(HERE, "gemm_hand.json")))["q5_K"]
+    K = g["K"]
+    x = np.zeros((1, K), np.float32)
+    x[0, ::32] = g["x_first_of_each_block"]
+    w = np.zeros((1, 1, 176), np.uint8)
+    w[0, 0, 0:2] = np.array([g["d"]], "<f2").view(np.uint8)
+    w[0, 0, 2:4] = np.array([g["dmin"]], "<f2").view(np.uint8)
+    w[0, 0, 4:8] = g["sc"]
+    w[0, 0, 8:12] = g["m"]
+    w[0, 0, 12:16] = g["sc"] | (g["m"] << 4)
+    w[0, 0, 16] = g["high_byte_0"]
+    w[0, 0, 48:] = g["code"] | (g["code"] << 4)
+    return x, w, K, g["out"]

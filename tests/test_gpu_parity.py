@@ -230,9 +230,19 @@ def test_gemm_hand_cases():
     wp[:, :K // 32] = w
     xq = _gpu_quantize(xp)
     assert _run_gemm(mmq.FMT_Q8_0, xq, wp, 1, 1, 256)[0, 0] == expect
+    xp9 = np.repeat(xp, 9, axis=0)   # the tiled kernel (M > 8) as well
+    assert (_run_gemm(mmq.FMT_Q8_0, _gpu_quantize(xp9), wp, 9, 1, 256)[:, 0] == expect).all()
     x, w, K, expect = golden_cases.gemm_q4_K_case()
     xq = _gpu_quantize(x)
     assert _run_gemm(mmq.FMT_Q4_K, xq, w, 1, 1, K)[0, 0] == expect
+    x9 = np.repeat(x, 9, axis=0)
+    assert (_run_gemm(mmq.FMT_Q4_K, _gpu_quantize(x9), w, 9, 1, K)[:, 0] == expect).all()
+    x, w, K, expect = golden_cases.gemm_q5_K_case()
+    xq = _gpu_quantize(x)
+    assert _run_gemm(mmq.FMT_Q5_K, xq, w, 1, 1, K)[0, 0] == expect
+    # the tiled kernel too: the same row in a 9-row input (M > 8)
+    x9 = np.repeat(x, 9, axis=0)
+    assert (_run_gemm(mmq.FMT_Q5_K, _gpu_quantize(x9), w, 9, 1, K)[:, 0] == expect).all()
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4])

@@ -20,3 +20,7 @@ def test_gemm_hand_cases():
     _, _, sc, mn, codes = npdecode.q4_K_fields(w)
     assert (sc == 2).all() and (mn == 3).all() and (codes == 5).all()
     assert oracle.gemm_q4_K(oracle.quantize_q8_1(x), w, 1, 1, K)[0, 0] == expect
+    x, w, K, expect = golden_cases.gemm_q5_K_case()
+    codes = npdecode.q5_K_fields(w)[4].reshape(8, 32)
+    assert (codes[0::2, 0] == 5).all() and (codes[1::2, 0] == 21).all()
+    assert oracle.gemm_q5_K(oracle.quantize_q8_1(x), w, 1, 1, K)[0, 0] == expect
