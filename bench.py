@@ -540,8 +540,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by output columns with no reduction; see the design notes)",
+        print(f"bench.py: the library and this benchmark run on one GPU; --gpus {args.gpus} is not "
+              "supported (the path would shard by output columns, with no reduction between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
