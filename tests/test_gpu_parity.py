@@ -531,3 +531,42 @@ def test_graph_capture_replays_match_eager(fmt, M, N, K):
             assert metrics.normalized_max_error(got, eager.cpu().numpy()) <= metrics.TOL
         else:
             assert torch.equal(out, eager), f"replay {rep} differs from the eager output"
+
+
+def test_two_host_threads_two_streams():
+    """Two host threads, each with its own stream, launch quantize + GEMM
+    (tiled and matvec) concurrently; each result equals the same call made
+    alone."""
+    import threading
+    _say("two threads, two streams")
+    cases = [(mmq.FMT_Q4_K, 256, 640, 1024, 150), (mmq.FMT_Q8_0, 3, 1000, 2048, 151)]
+    data = []
+    for fmt, M, N, K, seed in cases:
+        x = _to_dev(inputs.activations(M, K, seed))
+        w = _to_dev(_weights(fmt, N, K, seed + 1))
+        ref = mmq.gemm(fmt, mmq.quantize_q8_1(x), w, M, N, K)
+        data.append((fmt, M, N, K, x, w, ref))
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            fmt, M, N, K, x, w, ref = data[i]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(20):
+                    xq = mmq.quantize_q8_1(x, stream=s)
+                    out = mmq.gemm(fmt, xq, w, M, N, K, stream=s)
+                s.synchronize()
+                if not torch.equal(out, ref):
+                    errors.append(f"case {i}: result differs")
+        except Exception as e:   # reported below, in the main thread
+            errors.append(f"case {i}: {e!r}")
+
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(len(data))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors

@@ -151,3 +151,25 @@ def test_q5_K_plans_like_q4_K():
     assert "lds=81920" in mmq.plan_for_limits(mmq.FMT_Q5_K, 2048, 18944, 3584, LDS_GFX950, 256)[1]
     ok, why = mmq.plan_for_limits(mmq.FMT_Q5_K, 64, 256, 512 + 32, LDS_GFX950, 256)
     assert not ok and "super-blocks" in why
+
+
+def test_refusal_reasons_are_per_thread():
+    """A refusal decided before any device call (here a null pointer or an
+    unknown format) leaves its reason in a thread-local string: two threads
+    refusing for different reasons each read their own."""
+    import ctypes
+    import threading
+    L = mmq.lib()
+    seen = {}
+
+    def worker(name, fmt):
+        for _ in range(200):
+            rc = L.mmq_gemm_multi(fmt, None, 1, None, None, None, 64, 256, None)
+            assert rc == 0
+            seen.setdefault(name, set()).add(mmq.last_error())
+
+    a = threading.Thread(target=worker, args=("null", mmq.FMT_Q8_0))
+    b = threading.Thread(target=worker, args=("fmt", 7))
+    a.start(); b.start(); a.join(); b.join()
+    assert seen["null"] == {"null pointer argument"}
+    assert seen["fmt"] == {"unknown weight format 7"}
