@@ -121,13 +121,14 @@ int mmq_gemm_q5_K(const void *x_q8_1, const void *w_q5_K, float *out,
 /* Several GEMMs of one format that read the same q8_1 activations (the
  * layer pipeline of "13 . r7-r8 raw-byte MMQ kernel": quantize once per
  * distinct input, e.g. the q, k and v projections, or gate and up), computed
- * by one launch whose grid covers the column tiles of all of them.
+ * by one launch whose grid covers the column tiles of all of them (for
+ * M <= 8, the output rows of all of them, in the matrix-vector kernel).
  *   fmt: MMQ_FMT_Q8_0, MMQ_FMT_Q4_K or MMQ_FMT_Q5_K; count: 1..8;
  *   x_q8_1: M x (K/32) q8_1 blocks, shared;
  *   w[g]: N[g] x K weights of format fmt; out[g]: M x N[g] fp32 row-major,
  *   fully overwritten; the arrays w, out and N are host memory (read during
  *   the call), the tensors device memory.
- * Each out[g] equals what mmq_gemm_q8_0 / mmq_gemm_q4_K would write for
+ * Each out[g] equals what mmq_gemm_q8_0 / _q4_K / _q5_K would write for
  * (x, w[g], N[g]), except that split-K is decided for the set as a whole.
  * Refused (nothing launched) when any member would be refused. */
 int mmq_gemm_multi(int fmt, const void *x_q8_1, int count, const void *const *w, float *const *out,
@@ -145,18 +146,19 @@ int64_t mmq_moe_workspace_bytes(int64_t T, int topk, int n_experts);
  * by the weights of each of the topk experts it was routed to, all in one
  * launch, with every 128-row tile holding rows of a single expert.
  *   x_q8_1: T x (K/32) q8_1 blocks (device);
+ *   fmt: MMQ_FMT_Q8_0, MMQ_FMT_Q4_K or MMQ_FMT_Q5_K;
  *   w: n_experts weight matrices of format fmt stored one after another,
- *      each N x K (N rows of K/32 Q8_0 blocks or K/256 Q4_K super-blocks,
- *      the layout mmq_gemm_q8_0 / mmq_gemm_q4_K take) (device);
+ *      each N x K (N rows of K/32 Q8_0 blocks or K/256 Q4_K / Q5_K
+ *      super-blocks, the layout the dense GEMMs take) (device);
  *   ids: int32 [T][topk] expert ids (device); routed row r = t*topk + j is
  *      token t times expert ids[r];
  *   out: (T*topk) x N fp32 row-major (device); row r is routed row r.
  *   workspace: at least mmq_moe_workspace_bytes(T, topk, n_experts) bytes of
  *      16-byte aligned device memory, caller-owned; its contents on entry do
  *      not matter and on return are the routing tables.
- * Row r of out equals mmq_gemm_q8_0 / mmq_gemm_q4_K's row for token t and
- * expert ids[r]'s matrix (bit-identical for Q8_0: the same arithmetic in the
- * same order).  A routed row whose id is outside [0, n_experts) is not
+ * Row r of out equals the tiled dense GEMM's row for token t and expert
+ * ids[r]'s matrix (bit-identical for Q8_0: the same arithmetic in the same
+ * order; the MoE launch always uses the 128 x 128 tile kernel, whatever T).  A routed row whose id is outside [0, n_experts) is not
  * computed and its row of out is left as it was.  The routing runs on the
  * device (a kernel on `stream` before the GEMM): the ids never visit the
  * host.  Requires K % 256 == 0, 1 <= topk <= 64, 1 <= n_experts <= 2048,
@@ -167,9 +169,9 @@ int mmq_moe_gemm(int fmt, const void *x_q8_1, const void *w, int n_experts, cons
                  void *stream);
 
 /* Test entry: the exact int32 block dots I[m,n,b] through the same staging
- * and matrix-core code as the GEMM of format `fmt` (MMQ_FMT_Q8_0,
- * MMQ_FMT_Q4_K or MMQ_FMT_Q5_K), written to dots[(m*N + n)*(K/32) + b].  Same refusal rules
- * as the GEMM. */
+ * and matrix-core code as the tiled GEMM of format `fmt` (MMQ_FMT_Q8_0,
+ * MMQ_FMT_Q4_K or MMQ_FMT_Q5_K; always the tile kernel, whatever M),
+ * written to dots[(m*N + n)*(K/32) + b].  Same refusal rules as the GEMM. */
 int mmq_debug_block_dots(int fmt, const void *x_q8_1, const void *w, int32_t *dots,
                          int64_t M, int64_t N, int64_t K, void *stream);
 
@@ -177,7 +179,9 @@ int mmq_debug_block_dots(int fmt, const void *x_q8_1, const void *w, int32_t *do
 const char *mmq_last_error(void);
 
 /* Describe the launch plan the GEMM of `fmt` would use on the current device
- * (tile, LDS bytes, grid) into buf (NUL-terminated).  Returns 1 if the plan
+ * (kernel=mmq for the 128 x 128 tile kernel or kernel=mv for the M <= 8
+ * matrix-vector kernel, tile, LDS bytes, grid, split-K) into buf
+ * (NUL-terminated).  Returns 1 if the plan
  * would launch, 0 if it would be refused (reason in buf). */
 int mmq_plan_describe(int fmt, int64_t M, int64_t N, int64_t K, char *buf, int64_t len);
 
