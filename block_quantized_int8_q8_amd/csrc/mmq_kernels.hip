@@ -1034,18 +1034,13 @@ __global__ __launch_bounds__(kMvThreads) void k_mmv(const uint8_t *__restrict__ 
 constexpr int kRouteThreads = 1024, kRouteWaves = kRouteThreads / 64, kRouteIds = 16;
 static_assert(kMoeMaxExperts <= 2 * kRouteThreads, "each routing thread owns two experts");
 
-template <typename F>
-__device__ __forceinline__ void for_each_routed_row(const int32_t *__restrict__ ids, int R, int E, F &&f) {
-    for (int base = 0; base < R; base += kRouteThreads * kRouteIds) {
-        int e[kRouteIds];
+// Ids of one chunk of routed rows (kRouteIds per thread, strided by the
+// block size so that the loads coalesce); -1 past the end.
+__device__ __forceinline__ void load_ids(const int32_t *__restrict__ ids, int R, int base, int *e) {
 #pragma unroll
-        for (int j = 0; j < kRouteIds; j++) {
-            const int i = base + j * kRouteThreads + int(threadIdx.x);
-            e[j] = i < R ? ids[i] : -1;
-        }
-#pragma unroll
-        for (int j = 0; j < kRouteIds; j++)
-            if (e[j] >= 0 && e[j] < E) f(base + j * kRouteThreads + int(threadIdx.x), e[j]);
+    for (int j = 0; j < kRouteIds; j++) {
+        const int i = base + j * kRouteThreads + int(threadIdx.x);
+        e[j] = i < R ? ids[i] : -1;
     }
 }
 
@@ -1058,9 +1053,25 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__re
     __shared__ int tile_off[kMoeMaxExperts + 1];
     __shared__ long long wave_sum[kRouteWaves];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    constexpr int kChunk = kRouteThreads * kRouteIds;
+    // the first chunk's ids stay in registers for both passes (all of them
+    // when R <= 16 Ki, the usual case); they are requested before anything
+    // else so that their latency overlaps the clearing of the counters
+    int e0[kRouteIds];
+    load_ids(ids, R, 0, e0);
     for (int e = tid; e < E; e += kRouteThreads) cnt[e] = 0;
     __syncthreads();
-    for_each_routed_row(ids, R, E, [&](int, int e) { atomicAdd(&cnt[e], 1); });
+    auto valid = [&](int e) { return e >= 0 && e < E; };
+#pragma unroll
+    for (int j = 0; j < kRouteIds; j++)
+        if (valid(e0[j])) atomicAdd(&cnt[e0[j]], 1);
+    for (int base = kChunk; base < R; base += kChunk) {
+        int e[kRouteIds];
+        load_ids(ids, R, base, e);
+#pragma unroll
+        for (int j = 0; j < kRouteIds; j++)
+            if (valid(e[j])) atomicAdd(&cnt[e[j]], 1);
+    }
     __syncthreads();
     // exclusive scan of (rows, tiles) per expert, packed as rows + tiles * 2^32
     // (rows <= R < 2^31, so the low half never carries); thread t owns
@@ -1083,13 +1094,16 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__re
     __syncthreads();
     long long ex = inc - v;
     for (int w = 0; w < wv; w++) ex += wave_sum[w];
+    int my_row[2], my_tile[2];
 #pragma unroll
     for (int j = 0; j < 2; j++) {
         const int e = 2 * tid + j;
+        my_row[j] = int(ex & 0xffffffffLL);
+        my_tile[j] = int(ex >> 32);
         if (e < E) {
-            row_off[e] = int(ex & 0xffffffffLL);
-            tile_off[e] = int(ex >> 32);
-            cursor[e] = row_off[e];
+            row_off[e] = my_row[j];
+            tile_off[e] = my_tile[j];
+            cursor[e] = my_row[j];
         }
         ex += own[j];
     }
@@ -1097,16 +1111,27 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__re
         row_off[E] = int(ex & 0xffffffffLL);
         tile_off[E] = int(ex >> 32);
     }
-    __syncthreads();
-    for_each_routed_row(ids, R, E, [&](int i, int e) { sorted[atomicAdd(&cursor[e], 1)] = i; });
+    // the tile table needs only this thread's own offsets and counts
 #pragma unroll
     for (int j = 0; j < 2; j++) {
         const int e = 2 * tid + j;
+        const int c = int(own[j] & 0xffffffffLL), nt = int(own[j] >> 32);
         if (e < E)
-            for (int t = tile_off[e]; t < tile_off[e + 1]; t++)
-                tiles[t] = make_int4(e, row_off[e] + kTileM * (t - tile_off[e]), row_off[e + 1], 0);
+            for (int t = 0; t < nt; t++)
+                tiles[my_tile[j] + t] = make_int4(e, my_row[j] + kTileM * t, my_row[j] + c, 0);
     }
+    __syncthreads();
     for (int t = tile_off[E] + tid; t < max_tiles; t += kRouteThreads) tiles[t] = make_int4(-1, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kRouteIds; j++)
+        if (valid(e0[j])) sorted[atomicAdd(&cursor[e0[j]], 1)] = j * kRouteThreads + tid;
+    for (int base = kChunk; base < R; base += kChunk) {
+        int e[kRouteIds];
+        load_ids(ids, R, base, e);
+#pragma unroll
+        for (int j = 0; j < kRouteIds; j++)
+            if (valid(e[j])) sorted[atomicAdd(&cursor[e[j]], 1)] = base + j * kRouteThreads + tid;
+    }
 }
 
 // Zero an fp32 array (the output of a split-K launch, before the slices add
