@@ -376,7 +376,8 @@ def time_moe(fmt_name: str, steps: int, warmup: int, check: bool = True):
     rows' down-projection input, the down indexed GEMM.  The routing is
     seeded top-8 over uniform expert scores; the down input is synthetic
     (the activation function between the two GEMMs is not part of the
-    path).  `moe_ms` is per indexed GEMM, routing kernel included."""
+    path).  `moe_ms` is per indexed GEMM, gate+up's including the routing
+    kernel, which down reuses."""
     import torch
     import block_quantized_int8_q8_amd as mmq
     from block_quantized_int8_q8_amd import inputs
@@ -401,12 +402,18 @@ def time_moe(fmt_name: str, steps: int, warmup: int, check: bool = True):
         })
 
     def step(ev=None):
+        # down reuses gate+up's routing tables (same routed rows, one input
+        # row each): one routing kernel per layer
         for i, g in enumerate(legs):
             mmq.quantize_q8_1(g["x"], g["xq"], stream=stream)
             if ev is not None:
                 ev[i][0].record(stream)
-            mmq.moe_gemm(fmt, g["xq"], g["w"], E, g["ids"], g["topk"], g["T"], g["N"], g["K"], g["out"],
-                         workspace=g["ws"], stream=stream)
+            if i == 0:
+                mmq.moe_gemm(fmt, g["xq"], g["w"], E, g["ids"], g["topk"], g["T"], g["N"], g["K"], g["out"],
+                             workspace=legs[0]["ws"], stream=stream)
+            else:
+                mmq.moe_gemm_routed(fmt, g["xq"], g["w"], E, g["topk"], g["T"], g["N"], g["K"], legs[0]["ws"],
+                                    g["out"], stream=stream)
             if ev is not None:
                 ev[i][1].record(stream)
 

@@ -20,7 +20,7 @@ Q8_1_BYTES, Q8_0_BYTES, Q4_K_BYTES, Q5_K_BYTES = 36, 34, 144, 176
 
 EXPORTS = (
     "mmq_quantize_q8_1", "mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_q5_K", "mmq_gemm_multi", "mmq_moe_workspace_bytes",
-    "mmq_moe_gemm", "mmq_debug_block_dots",
+    "mmq_moe_gemm", "mmq_moe_gemm_routed", "mmq_debug_block_dots",
     "mmq_last_error", "mmq_plan_describe", "mmq_plan_for_limits",
     "mmq_debug_set_extra_lds", "mmq_version",
 )
@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.mmq_moe_workspace_bytes.restype = i64
         L.mmq_moe_gemm.argtypes = [i32, p, p, i32, p, i32, p, i64, i64, i64, p, i64, p]
         L.mmq_moe_gemm.restype = i32
+        L.mmq_moe_gemm_routed.argtypes = [i32, p, p, i32, i32, p, i64, i64, i64, p, i64, p]
+        L.mmq_moe_gemm_routed.restype = i32
         L.mmq_debug_block_dots.argtypes = [i32, p, p, p, i64, i64, i64, p]
         L.mmq_debug_block_dots.restype = i32
         L.mmq_last_error.argtypes = []
@@ -167,6 +169,19 @@ def moe_gemm(fmt, xq, w, n_experts, ids, topk, T, N, K, out=None, workspace=None
     _check(lib().mmq_moe_gemm(fmt, _ptr(xq), _ptr(w), n_experts, _ptr(ids, torch.int32), topk,
                               _ptr(out, torch.float32), T, N, K, _ptr(workspace, torch.uint8),
                               workspace.numel(), _stream(stream)), "mmq_moe_gemm")
+    return out
+
+
+def moe_gemm_routed(fmt, xq, w, n_experts, topk, T, N, K, workspace, out=None, stream=None):
+    """Indexed MoE on the routing tables an earlier ``moe_gemm`` left in
+    ``workspace`` (same T*topk routed rows and experts; e.g. the down
+    projection: T*topk input rows, topk 1)."""
+    import torch
+    if out is None:
+        out = torch.empty((T * topk, N), dtype=torch.float32, device=xq.device)
+    _check(lib().mmq_moe_gemm_routed(fmt, _ptr(xq), _ptr(w), n_experts, topk, _ptr(out, torch.float32), T, N, K,
+                                     _ptr(workspace, torch.uint8), workspace.numel(), _stream(stream)),
+           "mmq_moe_gemm_routed")
     return out
 
 

@@ -169,12 +169,16 @@ int64_t mmq_moe_workspace_bytes(int64_t T, int topk, int n_experts) {
     return mmq::moe_workspace_bytes(T * topk, n_experts);
 }
 
-int mmq_moe_gemm(int fmt, const void *x_q8_1, const void *w, int n_experts, const int32_t *ids, int topk,
-                 float *out, int64_t T, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,
-                 void *stream) {
+}  // extern "C"
+
+namespace {
+
+int moe_common(int fmt, const void *x_q8_1, const void *w, int n_experts, const int32_t *ids, int topk, float *out,
+               int64_t T, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes, void *stream,
+               const char *name) {
     g_err[0] = '\0';
     if (!mmq::fmt_ok(fmt)) return refuse("unknown weight format %d", fmt);
-    if (!x_q8_1 || !w || !ids || !out || !workspace) return refuse("null pointer argument");
+    if (!x_q8_1 || !w || !out || !workspace) return refuse("null pointer argument");
     if (!aligned(x_q8_1, 16) || !aligned(w, 16)) return refuse("activation and weight pointers must be 16-byte aligned");
     if (!aligned(ids, 4) || !aligned(out, 4)) return refuse("ids and output pointers must be 4-byte aligned");
     if (!aligned(workspace, 16)) return refuse("workspace must be 16-byte aligned");
@@ -185,7 +189,7 @@ int mmq_moe_gemm(int fmt, const void *x_q8_1, const void *w, int n_experts, cons
     char why[256];
     if (!mmq::make_plan_moe(fmt, T, topk, n_experts, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), &p,
                             why, sizeof(why)))
-        return refuse("%s MoE GEMM T=%lld topk=%d E=%d N=%lld K=%lld: %s", mmq::fmt_name(fmt), (long long)T, topk,
+        return refuse("%s %s T=%lld topk=%d E=%d N=%lld K=%lld: %s", mmq::fmt_name(fmt), name, (long long)T, topk,
                       n_experts, (long long)N, (long long)K, why);
     const int64_t need = mmq::moe_workspace_bytes(T * topk, n_experts);
     if (workspace_bytes < need)
@@ -193,8 +197,29 @@ int mmq_moe_gemm(int fmt, const void *x_q8_1, const void *w, int n_experts, cons
     (void)hipGetLastError();
     const hipError_t e = mmq::launch_moe(p, x_q8_1, w, ids, topk, n_experts, out, T, N, K, workspace,
                                          static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return refuse("%s MoE GEMM launch failed: %s", mmq::fmt_name(fmt), hipGetErrorString(e));
+    if (e != hipSuccess) return refuse("%s %s launch failed: %s", mmq::fmt_name(fmt), name, hipGetErrorString(e));
     return 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mmq_moe_gemm(int fmt, const void *x_q8_1, const void *w, int n_experts, const int32_t *ids, int topk,
+                 float *out, int64_t T, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,
+                 void *stream) {
+    if (!ids) {
+        g_err[0] = '\0';
+        return refuse("null pointer argument");
+    }
+    return moe_common(fmt, x_q8_1, w, n_experts, ids, topk, out, T, N, K, workspace, workspace_bytes, stream,
+                      "MoE GEMM");
+}
+
+int mmq_moe_gemm_routed(int fmt, const void *x_q8_1, const void *w, int n_experts, int topk, float *out,
+                        int64_t T, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes, void *stream) {
+    return moe_common(fmt, x_q8_1, w, n_experts, nullptr, topk, out, T, N, K, workspace, workspace_bytes, stream,
+                      "MoE GEMM (reused routing)");
 }
 
 int mmq_debug_block_dots(int fmt, const void *x_q8_1, const void *w, int32_t *dots, int64_t M, int64_t N,

@@ -576,9 +576,11 @@ struct GemmSet {
 // of the tile's expert (expert_bytes apart) and output row i of the tile is
 // routed row sorted[first + i].
 struct MoeArgs {
+    const int4 *header;   // (kMoeMagic, R, E, 0) when the tables below are this launch's
     const int4 *tiles;
     const int32_t *sorted;
     int topk;
+    int R, E;
     int64_t expert_bytes;
 };
 
@@ -609,6 +611,10 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     const int N = set.N[gi];
     int4 mt = {0, 0, 0, 0};   // MoE row tile: expert, first sorted row, end of the expert's rows
     if constexpr (MOE) {
+        // tables built for other routed rows or experts (or never built):
+        // nothing is computed and nothing written
+        const int4 h = *moe.header;
+        if (h.x != kMoeMagic || h.y != moe.R || h.z != moe.E) return;
         mt = moe.tiles[ty];
         if (mt.x < 0) return;   // a spare row tile (workgroup-uniform)
         wq += int64_t(mt.x) * moe.expert_bytes;
@@ -1045,8 +1051,8 @@ __device__ __forceinline__ void load_ids(const int32_t *__restrict__ ids, int R,
 }
 
 __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__restrict__ ids, int R, int E,
-                                                             int max_tiles, int4 *__restrict__ tiles,
-                                                             int32_t *__restrict__ sorted) {
+                                                             int max_tiles, int4 *__restrict__ header,
+                                                             int4 *__restrict__ tiles, int32_t *__restrict__ sorted) {
     __shared__ int cnt[kMoeMaxExperts];
     __shared__ int cursor[kMoeMaxExperts];
     __shared__ int row_off[kMoeMaxExperts + 1];
@@ -1132,6 +1138,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__re
         for (int j = 0; j < kRouteIds; j++)
             if (valid(e[j])) sorted[atomicAdd(&cursor[e[j]], 1)] = base + j * kRouteThreads + tid;
     }
+    if (tid == 0) *header = make_int4(kMoeMagic, R, E, 0);
 }
 
 // Zero an fp32 array (the output of a split-K launch, before the slices add
@@ -1227,10 +1234,12 @@ hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t
                       float *out, int64_t T, int64_t N, int64_t K, void *workspace, hipStream_t stream) {
     const int64_t R = T * topk;
     const int max_tiles = int(p.grid_y);
-    int4 *tiles = reinterpret_cast<int4 *>(workspace);
-    int32_t *sorted = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(workspace) + 16 * int64_t(max_tiles));
-    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(kRouteThreads), 0, stream, ids, int(R), n_experts, max_tiles,
-                       tiles, sorted);
+    int4 *header = reinterpret_cast<int4 *>(workspace);
+    int4 *tiles = reinterpret_cast<int4 *>(reinterpret_cast<uint8_t *>(workspace) + kMoeHeaderBytes);
+    int32_t *sorted = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(tiles) + 16 * int64_t(max_tiles));
+    if (ids)   // else: the tables a previous launch left in the workspace
+        hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(kRouteThreads), 0, stream, ids, int(R), n_experts, max_tiles,
+                           header, tiles, sorted);
     GemmSet set{};
     set.count = 1;
     set.tile_start[0] = 0;
@@ -1239,9 +1248,12 @@ hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t
     set.w[0] = reinterpret_cast<const uint8_t *>(w);
     set.out[0] = out;
     MoeArgs moe;
+    moe.header = header;
     moe.tiles = tiles;
     moe.sorted = sorted;
     moe.topk = topk;
+    moe.R = int(R);
+    moe.E = n_experts;
     moe.expert_bytes = N * weight_row_bytes(p.fmt, K);
     const dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, 1);
     const dim3 block(p.threads);

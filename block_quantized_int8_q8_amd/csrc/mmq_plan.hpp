@@ -183,17 +183,24 @@ inline bool make_plan_multi(int fmt, int64_t M, int count, const int64_t *Ns, in
 // by the weights of expert ids[r].  The routed rows are grouped by expert
 // into 128-row tiles; every non-empty expert leaves at most one partial tile,
 // so floor(R / 128) + min(E, R) row tiles always suffice, and that is the
-// launch's grid y.  The workspace holds the tile table (one int4 per row
-// tile: expert, first sorted row, end of the expert's sorted rows, unused)
-// followed by the routed-row ids sorted by expert (int32 [R]).
+// launch's grid y.  The workspace holds a header, the tile table (one int4
+// per row tile: expert, first sorted row, end of the expert's sorted rows,
+// unused) and the routed-row ids sorted by expert (int32 [R]).
 constexpr int kMoeMaxExperts = 2048;   // the routing kernel keeps its per-expert tables in LDS
 constexpr int kMoeMaxTopk = 64;
 
 inline int64_t moe_max_tiles(int64_t R, int64_t E) { return R / kTileM + (E < R ? E : R); }
 
+// Workspace: a 16-byte header (kMoeMagic, R, E, 0) that the routing kernel
+// writes last, so that a later launch can check that the tables it reuses
+// were built for the same routed rows and experts; then the tile table; then
+// the sorted routed-row ids.
+constexpr int kMoeMagic = 0x4d6f4531;   // "MoE1"
+constexpr int64_t kMoeHeaderBytes = 16;
+
 inline int64_t moe_workspace_bytes(int64_t R, int64_t E) {
     if (R < 0 || E < 0) return -1;
-    return 16 * moe_max_tiles(R, E) + ((4 * R + 15) / 16) * 16;
+    return kMoeHeaderBytes + 16 * moe_max_tiles(R, E) + ((4 * R + 15) / 16) * 16;
 }
 
 inline bool make_plan_moe(int fmt, int64_t T, int topk, int n_experts, int64_t N, int64_t K, int64_t lds_limit,

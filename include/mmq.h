@@ -135,9 +135,9 @@ int mmq_gemm_multi(int fmt, const void *x_q8_1, int count, const void *const *w,
                    const int64_t *N, int64_t M, int64_t K, void *stream);
 
 /* Bytes of device workspace mmq_moe_gemm needs for T tokens routed to topk
- * experts each among n_experts: a tile table (16 B per possible 128-row
- * tile, floor(T*topk/128) + min(n_experts, T*topk) of them) and the routed
- * row ids sorted by expert (4 B each).  -1 for arguments mmq_moe_gemm
+ * experts each among n_experts: a 16-byte header, a tile table (16 B per
+ * possible 128-row tile, floor(T*topk/128) + min(n_experts, T*topk) of
+ * them) and the routed row ids sorted by expert (4 B each).  -1 for arguments mmq_moe_gemm
  * refuses outright (topk outside 1..64, n_experts outside 1..2048, T < 0). */
 int64_t mmq_moe_workspace_bytes(int64_t T, int topk, int n_experts);
 
@@ -167,6 +167,20 @@ int64_t mmq_moe_workspace_bytes(int64_t T, int topk, int n_experts);
 int mmq_moe_gemm(int fmt, const void *x_q8_1, const void *w, int n_experts, const int32_t *ids, int topk,
                  float *out, int64_t T, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,
                  void *stream);
+
+/* The indexed-MoE GEMM on the routing tables an earlier mmq_moe_gemm left in
+ * `workspace` (no ids, no routing kernel): for a second expert GEMM of the
+ * same routed rows, e.g. the down projection after gate/up, whose input has
+ * one row per routed row (pass T' = T*topk, topk' = 1: routed row r is then
+ * input row r, grouped into the same expert tiles).  Arguments as for
+ * mmq_moe_gemm.  The tables are used only if their header records the same
+ * number of routed rows (T*topk) and n_experts; otherwise nothing is
+ * computed and `out` is left as it was (a workspace never routed, or routed
+ * for other rows, writes nothing).  Tables routed for other ids of the same
+ * sizes are used as they are: keeping the ids and the workspace together is
+ * the caller's part. */
+int mmq_moe_gemm_routed(int fmt, const void *x_q8_1, const void *w, int n_experts, int topk, float *out,
+                        int64_t T, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Test entry: the exact int32 block dots I[m,n,b] through the same staging
  * and matrix-core code as the tiled GEMM of format `fmt` (MMQ_FMT_Q8_0,

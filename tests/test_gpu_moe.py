@@ -151,3 +151,49 @@ def test_moe_full_size_sampled_rows(fmt, gemm):
     rows = np.unique(np.random.default_rng(7).integers(0, T * topk, size=48))
     ref = oracle.moe_gemm(fmt, xq, w, ids, topk, T, N, K, E, nthreads=16, rows=rows)
     _check(fmt, got[rows], ref)
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
+def test_moe_routed_reuse_for_down_projection(fmt):
+    """gate/up routes T tokens to topk experts; the down projection then
+    reuses those tables with one input row per routed row (T*topk rows,
+    topk 1) and equals a fresh routing of the flattened ids."""
+    T, E, topk, K1, N1, K2, N2 = 150, 8, 2, 512, 256, 256, 384
+    _say(f"moe routed reuse fmt={fmt}")
+    ids = inputs.moe_ids(T, E, topk, 160, skew=1.0)
+    x1 = oracle.quantize_q8_1(inputs.activations(T, K1, 161))
+    w1 = _weights(fmt, E, N1, K1, 162)
+    ws = torch.empty((mmq.moe_workspace_bytes(T, topk, E),), dtype=torch.uint8, device=DEV)
+    up = torch.full((T * topk, N1), float("nan"), dtype=torch.float32, device=DEV)
+    mmq.moe_gemm(fmt, _dev(x1), _dev(w1), E, _dev(ids), topk, T, N1, K1, up, workspace=ws)
+    x2 = oracle.quantize_q8_1(inputs.activations(T * topk, K2, 163))
+    w2 = _weights(fmt, E, N2, K2, 164)
+    down = torch.full((T * topk, N2), float("nan"), dtype=torch.float32, device=DEV)
+    mmq.moe_gemm_routed(fmt, _dev(x2), _dev(w2), E, 1, T * topk, N2, K2, ws, down)
+    fresh = _run(fmt, x2, w2, E, ids.reshape(-1, 1), 1, T * topk, N2, K2)
+    torch.cuda.synchronize()
+    got = down.cpu().numpy()
+    assert not np.isnan(got).any()
+    assert np.array_equal(got.view(np.uint32), fresh.view(np.uint32))
+    _check(fmt, got, oracle.moe_gemm(fmt, x2, w2, ids.reshape(-1, 1), 1, T * topk, N2, K2, E, nthreads=16))
+
+
+def test_moe_routed_without_matching_tables_writes_nothing():
+    fmt, T, E, topk, N, K = mmq.FMT_Q8_0, 64, 4, 2, 128, 256
+    _say("moe routed: no matching tables")
+    xq = _dev(oracle.quantize_q8_1(inputs.activations(T, K, 170)))
+    w = _dev(_weights(fmt, E, N, K, 171))
+    ws = torch.zeros((mmq.moe_workspace_bytes(T, topk, E) + 256,), dtype=torch.uint8, device=DEV)
+    out = torch.full((T * topk, N), float("nan"), dtype=torch.float32, device=DEV)
+    mmq.moe_gemm_routed(fmt, xq, w, E, topk, T, N, K, ws, out)      # never routed
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
+    ids = _dev(inputs.moe_ids(T, E, topk, 172))
+    mmq.moe_gemm(fmt, xq, w, E, ids, topk, T, N, K, out, workspace=ws)  # routed for 128 rows, 4 experts
+    out2 = torch.full((T * topk // 2, N), float("nan"), dtype=torch.float32, device=DEV)
+    mmq.moe_gemm_routed(fmt, xq, w, E, 1, T, N, K, ws, out2)          # 64 routed rows: no match
+    out3 = torch.full((T * topk, N), float("nan"), dtype=torch.float32, device=DEV)
+    mmq.moe_gemm_routed(fmt, xq, w, E + 1, topk, T, N, K, ws, out3)   # 5 experts: no match
+    torch.cuda.synchronize()
+    assert torch.isnan(out2).all() and torch.isnan(out3).all()
+    assert not torch.isnan(out).any()
