@@ -98,10 +98,8 @@ def time_config(cfg, steps: int, warmup: int, check: bool = True, cold: bool = F
         step()
     torch.cuda.synchronize()
 
-    parity = None
-    if check:
-        parity = check_parity(fmt, M, N, K, x, w, xq, out)
-
+    # timed right after the warm-up (a pause for the parity check first would
+    # let the clocks drop); the check reads the last timed launch's output
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -134,6 +132,7 @@ def time_config(cfg, steps: int, warmup: int, check: bool = True, cold: bool = F
     ops = 2.0 * M * N * K
     step_ms = total_ms / steps
     g_avg = a.elapsed_time(b) / steps
+    parity = check_parity(fmt, M, N, K, x, w, xq, out) if check else None
     cold_ms = None
     if cold:
         # one launch after writing 512 MB elsewhere: the weights and the q8_1
@@ -186,7 +185,9 @@ def time_layer(M: int, steps: int, warmup: int, check: bool = True):
     """The seven Q4_K projection GEMMs of one 7B layer at M tokens: one
     quantize pass per distinct input, and the GEMMs that share it (q, k, v;
     gate, up) in one launch; one step is the whole set in order on one
-    stream.  `gemm_ms` is per input group."""
+    stream.  Timed as HIP graph replays (the step, and each input group's
+    GEMM launch: `gemm_ms`); `ms_per_layer_eager` is the same step issued
+    launch by launch from the host."""
     import torch
     import block_quantized_int8_q8_amd as mmq
     from block_quantized_int8_q8_amd import inputs
@@ -241,26 +242,72 @@ def time_layer(M: int, steps: int, warmup: int, check: bool = True):
                     o[rows], oracle.gemm_q4_K(xq, w_host[g], len(rows), N, K)))
         parity = {"rows_checked_per_gemm": 3, "unwritten": unwritten,
                   "normalized_max_error": worst, "ok": bool(unwritten == 0 and worst <= metrics.TOL)}
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in groups] for _ in range(steps)]
+    # eager: launches issued by the host as the step runs (host issue time
+    # shows up as idle gaps at small M)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(steps):
-        step(ev[i])
+        step()
     end.record(stream)
     torch.cuda.synchronize()
-    step_ms = start.elapsed_time(end) / steps
-    gemm_ms = {"+".join(gemms): float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)]))
-               for j, (_, _, gemms) in enumerate(groups)}
+    eager_ms = start.elapsed_time(end) / steps
+
+    # the GPU time: the step, and each group's GEMM launch, as HIP graph replays
+    def group_call(name, K, gemms):
+        return lambda: step_group(name, K, gemms)
+
+    def step_group(name, K, gemms):
+        if len(gemms) == 1:
+            g = gemms[0]
+            mmq.gemm_q4_K(xqs[name], ws[g], M, shapes[g][0], K, outs[g])
+        else:
+            mmq.gemm_multi(mmq.FMT_Q4_K, xqs[name], [ws[g] for g in gemms], [shapes[g][0] for g in gemms],
+                           M, K, [outs[g] for g in gemms])
+
+    def eager_step():
+        for name, K, gemms in groups:
+            mmq.quantize_q8_1(xs[name], xqs[name])
+            step_group(name, K, gemms)
+
+    step_ms = graph_time(eager_step, steps)
+    gemm_ms = {"+".join(gemms): graph_time(group_call(name, K, gemms), steps) for name, K, gemms in groups}
     ops = sum(2.0 * M * n * k for _, n, k in inputs.LAYER_7B)
     return {
-        "M": M, "ms_per_layer": step_ms,
+        "M": M, "ms_per_layer": step_ms, "ms_per_layer_eager": eager_ms, "timing": "HIP graph replay",
         "tops_layer": ops / (step_ms * 1e-3) / 1e12,
         "gemm_tops": ops / (sum(gemm_ms.values()) * 1e-3) / 1e12,
         "gemm_ms": gemm_ms,
         "parity": parity,
     }
+
+
+def graph_time(fn, n: int, reps: int = 4) -> float:
+    """ms per call of `fn` (launches on the current stream): `reps` calls
+    captured once in a HIP graph, the graph replayed `n` times between two
+    events (host launch cost kept out of the figure)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(reps):
+                fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(3):   # warm
+        g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(max(1, n)):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (max(1, n) * reps)
 
 
 def time_decode(M: int, fmt_name: str, steps: int, warmup: int, check: bool = True):
@@ -338,7 +385,8 @@ def time_decode(M: int, fmt_name: str, steps: int, warmup: int, check: bool = Tr
     torch.cuda.synchronize()
 
     def timed(graph):
-        graph.replay()   # warm
+        for _ in range(3):   # warm
+            graph.replay()
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
