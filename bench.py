@@ -99,39 +99,40 @@ def time_config(cfg, steps: int, warmup: int, check: bool = True, cold: bool = F
     torch.cuda.synchronize()
 
     # timed right after the warm-up (a pause for the parity check first would
-    # let the clocks drop); the check reads the last timed launch's output
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # let the clocks drop); the check reads the last timed launch's output.
+    # The step (quantize then GEMM on one stream) is timed with two events
+    # around all the steps, with nothing recorded in between; the GEMM and
+    # the quantize pass alone the same way, back to back (these are the
+    # kernels' own durations: an event recorded before each launch leaves a
+    # gap the kernel trace does not show).
+    def span(fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
     t0 = time.perf_counter()
-    start.record(stream)
+    step_ms = span(step)
+    wall = time.perf_counter() - t0
+    g_avg = span(lambda: gemm(xq, wd, M, N, K, out, stream=stream))
+    q_avg = span(lambda: mmq.quantize_q8_1(xd, xq, stream=stream))
+    # per launch, evented (median and minimum; each includes the record gap)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
     for i in range(steps):
         ev[i][0].record(stream)
-        mmq.quantize_q8_1(xd, xq, stream=stream)
-        ev[i][1].record(stream)
         gemm(xq, wd, M, N, K, out, stream=stream)
-        ev[i][2].record(stream)
-    end.record(stream)
+        ev[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    q_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
-    g_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]
-    # The GEMM kernel's own duration: the same launches back to back between
-    # two events, so that the gap an event record leaves before each launch
-    # is not counted (the figure the roofline uses; the per-step events above
-    # include that gap).
+    g_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
+    ops = 2.0 * M * N * K
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
-        gemm(xq, wd, M, N, K, out, stream=stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    ops = 2.0 * M * N * K
-    step_ms = total_ms / steps
-    g_avg = a.elapsed_time(b) / steps
     parity = check_parity(fmt, M, N, K, x, w, xq, out) if check else None
     cold_ms = None
     if cold:
@@ -145,7 +146,6 @@ def time_config(cfg, steps: int, warmup: int, check: bool = True, cold: bool = F
         torch.cuda.synchronize()
         cold_ms = a.elapsed_time(b)
         del scrub
-    q_avg = float(np.mean(q_ms))
     return {
         "cfg": cfg, "fmt": fmt, "M": M, "N": N, "K": K,
         "ms_per_step": step_ms,
