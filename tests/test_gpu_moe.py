@@ -197,3 +197,16 @@ def test_moe_routed_without_matching_tables_writes_nothing():
     torch.cuda.synchronize()
     assert torch.isnan(out2).all() and torch.isnan(out3).all()
     assert not torch.isnan(out).any()
+
+
+@pytest.mark.parametrize("fmt,T,E,topk", [(mmq.FMT_Q8_0, 300, 2048, 1),   # the most experts: most of them empty
+                                          (mmq.FMT_Q4_K, 20, 64, 64),     # the largest topk: every expert per token
+                                          (mmq.FMT_Q8_0, 129, 1, 1)])     # one expert: a plain gathered GEMM
+def test_moe_extreme_expert_counts(fmt, T, E, topk):
+    N, K = 160, 256
+    _say(f"moe extremes fmt={fmt} T={T} E={E} topk={topk}")
+    xq = oracle.quantize_q8_1(inputs.activations(T, K, 180 + E))
+    w = _weights(fmt, E, N, K, 181 + topk)
+    ids = inputs.moe_ids(T, E, topk, 182)
+    got = _run(fmt, xq, w, E, ids, topk, T, N, K)
+    _check(fmt, got, oracle.moe_gemm(fmt, xq, w, ids, topk, T, N, K, E, nthreads=16))
