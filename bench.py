@@ -279,11 +279,21 @@ def time_layer(M: int, steps: int, warmup: int, check: bool = True):
             mmq.quantize_q8_1(xs[name], xqs[name])
             step_group(name, K, gemms)
 
+    def separate_step():
+        # the variant without sharing: every GEMM quantizes its own input and
+        # runs in a launch of its own (7 quantize passes, 7 GEMM launches)
+        for name, K, gemms in groups:
+            for g in gemms:
+                mmq.quantize_q8_1(xs[name], xqs[name])
+                mmq.gemm_q4_K(xqs[name], ws[g], M, shapes[g][0], K, outs[g])
+
     step_ms = graph_time(eager_step, steps)
+    separate_ms = graph_time(separate_step, steps)
     gemm_ms = {"+".join(gemms): graph_time(group_call(name, K, gemms), steps) for name, K, gemms in groups}
     ops = sum(2.0 * M * n * k for _, n, k in inputs.LAYER_7B)
     return {
         "M": M, "ms_per_layer": step_ms, "ms_per_layer_eager": eager_ms, "timing": "HIP graph replay",
+        "ms_per_layer_7_passes_7_launches": separate_ms,
         "tops_layer": ops / (step_ms * 1e-3) / 1e12,
         "gemm_tops": ops / (sum(gemm_ms.values()) * 1e-3) / 1e12,
         "gemm_ms": gemm_ms,
