@@ -50,6 +50,16 @@ def activations(M: int, K: int, seed: int) -> np.ndarray:
     return np.random.default_rng(seed).standard_normal((M, K), dtype=np.float32)
 
 
+def activations_device(M: int, K: int, seed: int, device) -> "torch.Tensor":
+    """fp32 M x K, standard normal, drawn on the device by torch's seeded
+    generator: for sizes (several GB) the host would take too long to draw.
+    The tests read back the rows they check and hand those to the oracle."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn((M, K), generator=g, dtype=torch.float32, device=device)
+
+
 def q8_0_weights(N: int, K: int, seed: int, d_range=(1e-3, 1e-2),
                  d_value: float | None = None) -> np.ndarray:
     """uint8 N x (K/32) x 34.  ``d_value`` fixes every scale (e.g. 1.0)."""
