@@ -1,11 +1,12 @@
 // mmq_kernels.hip -- gfx950 kernels of the block-quantized int8 MMQ library.
 //
 //   k_quantize_q8_1   fp32 -> q8_1, one pass over the activations (HBM-bound)
-//   k_mmq<FMT, DOTS, MOE>
+//   k_mmq<FMT, DOTS, MOE, SKIP>
 //                     q8_1 x {Q8_0, Q4_K, Q5_K} -> fp32 (or the raw int32 block
 //                     dots when DOTS), int8 MFMA with the per-block scale
 //                     applied in registers on the MFMA accumulator layout;
-//                     MOE gathers the rows of each expert's routed tokens
+//                     MOE gathers the rows of each expert's routed tokens;
+//                     SKIP lets waves with no rows left skip their compute
 //   k_moe_route       expert routing for the MOE launch (counts, scan, scatter)
 //   k_mmv<FMT>        the same contraction for a few activation rows
 //                     (decode): VALU int8 dot products at the HBM roofline
@@ -584,10 +585,17 @@ struct MoeArgs {
     int64_t expert_bytes;
 };
 
-template <int FMT, bool DOTS, bool MOE>
+// SKIP: waves whose 32 rows all lie past the tile's last row skip their
+// MFMAs and epilogues (see wave_live below).  The MoE launch always skips;
+// so does the dense Q8_0 kernel, where the branch costs nothing measurable.
+// For the K-quants the branch costs 1-2 % on full tiles (register
+// allocation), so the launcher uses that instantiation only when the plan
+// marks enough of the launch's waves as idle.
+template <int FMT, bool DOTS, bool MOE, bool SKIP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DOTS ? 2 : 4)))
 void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int steps_per_split, const MoeArgs moe) {
     static_assert(!(MOE && DOTS), "the block-dot output exists for plain GEMMs only");
+    static_assert(!(DOTS && SKIP) && (!MOE || SKIP), "block dots never skip; the MoE launch always does");
     using L = Lds<FMT>;
     // The two k-step buffers are two LDS variables, not offsets into one
     // array: the compiler then knows that the DMA into one buffer cannot
@@ -681,18 +689,26 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the DMA has landed in LDS
     __syncthreads();
 
-    // MoE: a wave whose 32 rows lie past its expert's last routed row (the
-    // partial last tile of an expert) has nothing to compute; it only takes
-    // its part in staging, which leaves the SIMD's VALU to the other waves.
+    // A wave whose 32 rows lie past the tile's last row (rows at or past M in
+    // the last row tile of a GEMM; past its expert's last routed row in a MoE
+    // tile) has nothing to compute: it only takes its part in staging, which
+    // leaves the SIMD's VALU to the other waves.
     bool wave_live = true;
-    if constexpr (MOE) wave_live = __builtin_amdgcn_readfirstlane(int(mt.y + 32 * wr < mt.z)) != 0;
+    if constexpr (MOE)
+        wave_live = __builtin_amdgcn_readfirstlane(int(mt.y + 32 * wr < mt.z)) != 0;
+    else if constexpr (SKIP)
+        wave_live = __builtin_amdgcn_readfirstlane(int(m0 + 32 * wr < M)) != 0;
 
     auto step = [&](auto parity, int j) {
         constexpr int P = decltype(parity)::value;
         const int ks = ks0 + j;                   // the k-step; j is its place in this workgroup's range
         uint8_t *const buf = P ? lds1 : lds0;     // local step j (j % 2 == P)
         uint8_t *const nxt = P ? lds0 : lds1;     // local step j + 1
-        if constexpr (MOE) {
+        // Q8_0: an idle wave takes this path of its own (staging only).  The
+        // K-quants skip the same work by guarding the fragment reads, MFMAs
+        // and epilogues below instead: with a second copy of the staging code
+        // their register allocation spilled inside the k-loop.
+        if constexpr (SKIP && FMT == FMT_Q8_0) {
             if (!wave_live) {
                 if (j + 1 < nloc) {
 #pragma unroll
@@ -734,14 +750,19 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
                     fw[st % kRing] = sW[b * kTileN + b_col0 + 32 * c].x;
             }
         };
-        load_a(0);
+        const bool live = !SKIP || FMT == FMT_Q8_0 || wave_live;   // wave-uniform
+        if (live) {
+            load_a(0);
 #pragma unroll
-        for (int st = 0; st < kPfB; st++) load_b(st);
+            for (int st = 0; st < kPfB; st++) load_b(st);
+        }
 #pragma unroll
         for (int st = 0; st < kSteps; st++) {
             const int b = st / kNSub, c = st % kNSub;
-            if (st + kPfB < kSteps) load_b(st + kPfB);
-            if (c == 0 && b + 1 < KB) load_a(b + 1);
+            if (live) {
+                if (st + kPfB < kSteps) load_b(st + kPfB);
+                if (c == 0 && b + 1 < KB) load_a(b + 1);
+            }
             // The LDS writes for step ks+1 are spread over the sub-steps (the
             // three DMA pieces at 1, 3 and 5, the weight stores at 6): issued
             // together at the top or bottom of the step they were measured to
@@ -750,6 +771,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
                 if ((st & 1) && st < 6) dma_activations<FMT>(rx, adma, ks + 1, nxt, wv, st >> 1);
                 if (st == 6) store_w(ks + 1, nxt);
             }
+            if (!live) continue;
             const i32x16 D = mfma_at(fa[b & 1], fb[st % kRing], srcC);
             const int col = b_col0 + 32 * c;
             if constexpr (DOTS) {
@@ -770,7 +792,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
                 asm volatile("" : "+v"(acc[c]));
             }
         }
-        if constexpr (FMT != FMT_Q8_0 && !DOTS) {
+        if constexpr (FMT != FMT_Q8_0 && !DOTS) if (live) {
             // the min term of this step's four sub-blocks
             const _Float16 *sMin = reinterpret_cast<const _Float16 *>(buf + L::OFF_B_MIN);
             // A = the four block sums s (high halves of the row's headers)
@@ -1215,11 +1237,14 @@ hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const vo
     auto go = [&](auto fmt) {
         constexpr int F = decltype(fmt)::value;
         if (dots)
-            hipLaunchKernelGGL((k_mmq<F, true, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps,
-                               MoeArgs{});
+            hipLaunchKernelGGL((k_mmq<F, true, false, false>), grid, block, lds, stream, xb, set, int(M), int(K),
+                               sps, MoeArgs{});
+        else if (F == FMT_Q8_0 || p.skip_idle_waves)
+            hipLaunchKernelGGL((k_mmq<F, false, false, true>), grid, block, lds, stream, xb, set, int(M), int(K),
+                               sps, MoeArgs{});
         else
-            hipLaunchKernelGGL((k_mmq<F, false, false>), grid, block, lds, stream, xb, set, int(M), int(K), sps,
-                               MoeArgs{});
+            hipLaunchKernelGGL((k_mmq<F, false, false, (F == FMT_Q8_0)>), grid, block, lds, stream, xb, set,
+                               int(M), int(K), sps, MoeArgs{});
     };
     if (p.fmt == FMT_Q8_0)
         go(std::integral_constant<int, FMT_Q8_0>{});
@@ -1260,11 +1285,11 @@ hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t
     const auto *xb = reinterpret_cast<const uint8_t *>(x);
     const int sps = int(p.steps_per_split);
     if (p.fmt == FMT_Q8_0)
-        hipLaunchKernelGGL((k_mmq<FMT_Q8_0, false, true>), grid, block, 0, stream, xb, set, int(T), int(K), sps, moe);
+        hipLaunchKernelGGL((k_mmq<FMT_Q8_0, false, true, true>), grid, block, 0, stream, xb, set, int(T), int(K), sps, moe);
     else if (p.fmt == FMT_Q4_K)
-        hipLaunchKernelGGL((k_mmq<FMT_Q4_K, false, true>), grid, block, 0, stream, xb, set, int(T), int(K), sps, moe);
+        hipLaunchKernelGGL((k_mmq<FMT_Q4_K, false, true, true>), grid, block, 0, stream, xb, set, int(T), int(K), sps, moe);
     else
-        hipLaunchKernelGGL((k_mmq<FMT_Q5_K, false, true>), grid, block, 0, stream, xb, set, int(T), int(K), sps, moe);
+        hipLaunchKernelGGL((k_mmq<FMT_Q5_K, false, true, true>), grid, block, 0, stream, xb, set, int(T), int(K), sps, moe);
     return hipGetLastError();
 }
 

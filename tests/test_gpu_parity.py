@@ -116,7 +116,10 @@ def _oracle_gemm(fmt, xq, w, M, N, K, rows=None):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (64, 256, 512), (200, 300, 768), (129, 257, 1024),
-                                   (300, 130, 2048)])
+                                   (300, 130, 2048),
+                                   # K-quants: M=96 runs the idle-wave skipping kernel (one wave
+                                   # row of four idle), M=2000 the full-tile one with a ragged tile
+                                   (96, 300, 512), (2000, 300, 512)])
 def test_gemm_matches_oracle(fmt, M, N, K):
     _say(f"gemm fmt={fmt} M={M} N={N} K={K}")
     x = inputs.activations(M, K, 30 + M)

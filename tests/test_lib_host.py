@@ -141,6 +141,21 @@ def test_decode_sizes_plan_the_matvec_kernel(fmt, M, N, K):
     assert "kernel=mmq" in mmq.plan_for_limits(fmt, 9, N, K, LDS_GFX950, 256)[1]
 
 
+@pytest.mark.parametrize("M,kquant_skips", [
+    (9, True), (64, True), (96, True),      # one row tile, 1-3 of its 4 wave rows past M
+    (97, False), (128, False),              # every wave row holds rows
+    (192, True),                            # 2 of 8 wave rows idle: the 1/4 share
+    (200, False), (2000, False), (2048, False), (8192, False)])
+def test_idle_wave_skip_planning(M, kquant_skips):
+    """Waves whose 32 rows all lie past M skip their MFMAs and epilogues:
+    always for Q8_0, and for the K-quants only when idle wave rows make up
+    at least 1/4 of the launch's (their skipping kernel runs full tiles a
+    little slower).  The matvec kernel (M <= 8) has no row tiles."""
+    for fmt, want in [(mmq.FMT_Q8_0, True), (mmq.FMT_Q4_K, kquant_skips), (mmq.FMT_Q5_K, kquant_skips)]:
+        ok, desc = mmq.plan_for_limits(fmt, M, 3584, 3584, LDS_GFX950, 256)
+        assert ok and f"skip_idle_waves={int(want)}" in desc, desc
+
+
 def test_q5_K_plans_like_q4_K():
     """Q5_K stages the same LDS layout as Q4_K (codes unpacked to one byte,
     scales, split min operand): 80 KiB, two workgroups per CU."""
