@@ -909,141 +909,199 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// Unit u's two blocks (codes w0 / w1, weight scales ws0 / ws1, Q4_K min
-// terms dm0 / dm1) against the matching q8_1 block pair of every activation row.
-template <int FMT, int MR>
-__device__ __forceinline__ void mv_unit_terms(__amdgpu_buffer_rsrc_t rx, int M, int kb, int u, const uint32_t *w0,
-                                              const uint32_t *w1, float ws0, float ws1, float dm0, float dm1,
-                                              float *acc) {
+// One weight unit (two 32-blocks) of one output row, ready for the dot
+// products: one int8 code per byte, the weight scales and (K-quants) the
+// min terms dmin * m of its two sub-blocks.
+struct WUnit {
+    uint32_t w0[8], w1[8];
+    float ws0, ws1, dm0, dm1;
+};
+
+// K-quant unit u of a row: one 32-byte code group of super-block u/4 (low
+// nibbles: sub-block 2*grp, high nibbles: sub-block 2*grp+1) and the
+// super-block's header; Q5_K adds the fifth bits from its high-bit plane.
+template <int FMT>
+__device__ __forceinline__ WUnit mv_load_kquant(__amdgpu_buffer_rsrc_t rw, int u) {
+    WUnit r;
+    const int sb = u >> 2, grp = u & 3;   // super-block, 32-byte code group
+    constexpr int SB = FMT == FMT_Q4_K ? 144 : 176, QS = FMT == FMT_Q4_K ? 16 : 48;
+    const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(rw, SB * sb, 0, 0);
+    const u32x4 q0 = __builtin_amdgcn_raw_buffer_load_b128(rw, SB * sb + QS + 32 * grp, 0, 0);
+    const u32x4 q1 = __builtin_amdgcn_raw_buffer_load_b128(rw, SB * sb + QS + 16 + 32 * grp, 0, 0);
+    const uint32_t q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        r.w0[i] = q[i] & 0x0f0f0f0fu;
+        r.w1[i] = (q[i] >> 4) & 0x0f0f0f0fu;
+    }
+    if constexpr (FMT == FMT_Q5_K) {
+        // fifth bits: byte l of the high-bit plane holds element l of
+        // sub-block j in bit j (here j = 2*grp and 2*grp+1)
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rw, SB * sb + 16, 0, 0);
+        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rw, SB * sb + 32, 0, 0);
+        const uint32_t qh[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            r.w0[i] |= ((qh[i] >> (2 * grp)) & 0x01010101u) << 4;
+            r.w1[i] |= ((qh[i] >> (2 * grp + 1)) & 0x01010101u) << 4;
+        }
+    }
+    // 6-bit scale and min of sub-blocks j = 2*grp + {0, 1} (the K-quant
+    // packing: j < 4 in the low six bits of bytes j and j+4; j >= 4 low four
+    // bits from byte j+4, top two bits from the spare top bits of bytes j-4
+    // and j)
+    const float d = h2f(h.x), dmin = h2f(h.x >> 16);
+    float sc[2], mn[2];
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+        const int j = 2 * grp + t, sh = 8 * (j & 3);
+        const uint32_t b0 = (h.y >> sh) & 0xffu, b1 = (h.z >> sh) & 0xffu, b2 = (h.w >> sh) & 0xffu;
+        const uint32_t sv = j < 4 ? (b0 & 63u) : ((b2 & 15u) | ((b0 >> 6) << 4));
+        const uint32_t mv = j < 4 ? (b1 & 63u) : ((b2 >> 4) | ((b1 >> 6) << 4));
+        sc[t] = (float)sv;
+        mn[t] = (float)mv;
+    }
+    r.ws0 = d * sc[0];     // exact (11 x 6 bits)
+    r.ws1 = d * sc[1];
+    r.dm0 = dmin * mn[0];  // exact
+    r.dm1 = dmin * mn[1];
+    return r;
+}
+
+// Q8_0 unit from its 68 bytes (17 dwords) in LDS: block 0's scale in bytes
+// 0-1 and codes two bytes off the dword grid; block 1's scale in bytes 34-35
+// and codes on dwords 9..16.
+__device__ __forceinline__ WUnit mv_unit_q8_0(const uint32_t *src) {
+    WUnit r;
+    uint32_t v[17];
+#pragma unroll
+    for (int i = 0; i < 17; i++) v[i] = src[i];
+#pragma unroll
+    for (int i = 0; i < 8; i++) r.w0[i] = __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2);
+#pragma unroll
+    for (int i = 0; i < 8; i++) r.w1[i] = v[i + 9];
+    r.ws0 = h2f(v[0]);
+    r.ws1 = h2f(v[8] >> 16);
+    r.dm0 = r.dm1 = 0.0f;
+    return r;
+}
+
+// Unit u of RW weight rows against the matching q8_1 block pair of every
+// activation row: each pair is loaded once and serves all RW rows.  The
+// arithmetic of one (weight row, activation row) is the oracle's per-block
+// order: acc += xs * fl(ws * I), then (K-quants) acc -= dmin*m * s.
+template <int FMT, int MR, int RW>
+__device__ __forceinline__ void mv_unit_terms(__amdgpu_buffer_rsrc_t rx, int M, int kb, int u, const WUnit *wu,
+                                              float (*acc)[MR]) {
 #pragma unroll
     for (int m = 0; m < MR; m++) {
         if (m < M) {
             const XPair x = load_x_pair(rx, (m * kb + 2 * u) * 36);
-            const float t0 = ws0 * (float)dot8(w0, x.c0);
-            const float t1 = ws1 * (float)dot8(w1, x.c1);
-            acc[m] = __builtin_fmaf(h2f(x.h0), t0, acc[m]);
-            if constexpr (FMT != FMT_Q8_0) acc[m] = __builtin_fmaf(-dm0, h2f(x.h0 >> 16), acc[m]);
-            acc[m] = __builtin_fmaf(h2f(x.h1), t1, acc[m]);
-            if constexpr (FMT != FMT_Q8_0) acc[m] = __builtin_fmaf(-dm1, h2f(x.h1 >> 16), acc[m]);
+            const float xs0 = h2f(x.h0), xs1 = h2f(x.h1);
+#pragma unroll
+            for (int r = 0; r < RW; r++) {
+                const float t0 = wu[r].ws0 * (float)dot8(wu[r].w0, x.c0);
+                const float t1 = wu[r].ws1 * (float)dot8(wu[r].w1, x.c1);
+                acc[r][m] = __builtin_fmaf(xs0, t0, acc[r][m]);
+                if constexpr (FMT != FMT_Q8_0) acc[r][m] = __builtin_fmaf(-wu[r].dm0, h2f(x.h0 >> 16), acc[r][m]);
+                acc[r][m] = __builtin_fmaf(xs1, t1, acc[r][m]);
+                if constexpr (FMT != FMT_Q8_0) acc[r][m] = __builtin_fmaf(-wu[r].dm1, h2f(x.h1 >> 16), acc[r][m]);
+            }
         }
     }
 }
 
-template <int FMT, int MR>   // MR: activation rows compiled for (M <= MR)
+// MR: activation rows compiled for (M <= MR).  RW: output rows per wave
+// (mv_rows_per_wave(M), the planner's choice): with several activation rows
+// the activation loads, served from the caches, cost more than the weight
+// stream, and RW rows per wave divide them by RW.
+template <int FMT, int MR>
 __global__ __launch_bounds__(kMvThreads) void k_mmv(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K) {
+    constexpr int RW = mv_rows_per_wave(MR);
     const int lane = threadIdx.x & 63;
-    // the output row of this wave over all GEMMs of the set; read as a
-    // wave-uniform (scalar) value, so that the weight row's buffer descriptor
-    // lives in scalar registers (a descriptor in vector registers makes
-    // every load a loop over the lanes' distinct values)
-    const int row = blockIdx.x * kMvRowsPerWg + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (row >= set.tile_start[set.count]) return;
-    int gi = 0;
-    for (int i = 1; i < set.count; i++)
-        if (row >= set.tile_start[i]) gi = i;
-    const int n = row - set.tile_start[gi], N = set.N[gi];
+    // this wave's first output row over all GEMMs of the set; read as a
+    // wave-uniform (scalar) value, so that the weight rows' buffer
+    // descriptors live in scalar registers (a descriptor in vector registers
+    // makes every load a loop over the lanes' distinct values)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row0 = (blockIdx.x * kMvWaves + wave) * RW;
+    const int total = set.tile_start[set.count];
+    if (row0 >= total) return;
     const int kb = K >> 5;
     const int64_t wrow = weight_row_bytes(FMT, K);
-    const __amdgpu_buffer_rsrc_t rw = tile_rsrc(set.w[gi] + int64_t(n) * wrow, wrow);
-    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq, int64_t(M) * kb * 36);
-    const int units = kb >> 1;   // block pairs (Q8_0) / sub-block pairs (Q4_K) in the row
-
-    float acc[MR];
+    // row r of the wave: GEMM gi[r] of the set, its row n[r]; a row past the
+    // last one reads through an empty buffer (zeros) and is not stored
+    __amdgpu_buffer_rsrc_t rw[RW];
+    int gi[RW], n[RW];
 #pragma unroll
-    for (int m = 0; m < MR; m++) acc[m] = 0.0f;
+    for (int r = 0; r < RW; r++) {
+        const int row = row0 + r;
+        int g = 0;
+        for (int i = 1; i < set.count; i++)
+            if (row >= set.tile_start[i]) g = i;
+        gi[r] = g;
+        n[r] = row - set.tile_start[g];
+        rw[r] = tile_rsrc(set.w[g] + int64_t(n[r]) * wrow, row < total ? wrow : 0);
+    }
+    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq, int64_t(M) * kb * 36);
+    const int units = kb >> 1;   // block pairs (Q8_0) / sub-block pairs (K-quants) in a row
+
+    float acc[RW][MR];
+#pragma unroll
+    for (int r = 0; r < RW; r++)
+#pragma unroll
+        for (int m = 0; m < MR; m++) acc[r][m] = 0.0f;
 
     // Q8_0 rows are read in 64-unit chunks (4352 bytes) with contiguous
     // 16-byte pieces per lane (each load instruction covers 1 KiB) into this
     // wave's own LDS area, and each lane then takes its 68-byte unit from
     // there: 68-byte units loaded straight by each lane touch ~34 cache lines
-    // per instruction, and were measured 15-30 % slower.  Q4_K units (a
+    // per instruction, and were measured 15-30 % slower.  K-quant units (a
     // 16-byte header and 32 code bytes, both 16-byte aligned) load straight:
     // the staged form was 10-13 % slower there.
     constexpr int kQ8Chunk = 64 * 68;
     for (int u0 = 0; u0 < units; u0 += 64) {
         const int u = u0 + lane;
+        WUnit wu[RW];
         if constexpr (FMT == FMT_Q8_0) {
-            __shared__ __attribute__((aligned(16))) uint8_t stage[kMvRowsPerWg][kQ8Chunk];
-            uint8_t *my = stage[threadIdx.x >> 6];
-            // pieces past the row end read as zero
+            __shared__ __attribute__((aligned(16))) uint8_t stage[kMvWaves][kQ8Chunk];
+            uint8_t *my = stage[wave];
 #pragma unroll
-            for (int i = 0; i < (kQ8Chunk / 16 + 63) / 64; i++) {
-                const int piece = lane + 64 * i;
-                if (piece < kQ8Chunk / 16)
-                    *reinterpret_cast<u32x4 *>(my + 16 * piece) =
-                        __builtin_amdgcn_raw_buffer_load_b128(rw, u0 * 68 + 16 * piece, 0, 0);
+            for (int r = 0; r < RW; r++) {
+                // pieces past the row end read as zero
+#pragma unroll
+                for (int i = 0; i < (kQ8Chunk / 16 + 63) / 64; i++) {
+                    const int piece = lane + 64 * i;
+                    if (piece < kQ8Chunk / 16)
+                        *reinterpret_cast<u32x4 *>(my + 16 * piece) =
+                            __builtin_amdgcn_raw_buffer_load_b128(rw[r], u0 * 68 + 16 * piece, 0, 0);
+                }
+                // the area is this wave's alone and LDS serves a wave's
+                // accesses in order; the barriers only keep the compiler from
+                // moving the unit reads above the other lanes' piece writes
+                // (or the next row's writes above these reads)
+                __builtin_amdgcn_wave_barrier();
+                if (u < units) wu[r] = mv_unit_q8_0(reinterpret_cast<const uint32_t *>(my + 68 * lane));
+                __builtin_amdgcn_wave_barrier();
             }
-            // the area is this wave's alone and LDS serves a wave's accesses
-            // in order; the barrier only keeps the compiler from moving the
-            // unit reads above the other lanes' piece writes (or the next
-            // chunk's writes above these reads)
-            __builtin_amdgcn_wave_barrier();
-            if (u < units) {
-                const uint32_t *src = reinterpret_cast<const uint32_t *>(my + 68 * lane);
-                uint32_t v[17];
-#pragma unroll
-                for (int i = 0; i < 17; i++) v[i] = src[i];
-                uint32_t w0[8], w1[8];
-                // block 0: scale in bytes 0-1, codes two bytes off the dword
-                // grid; block 1: scale in bytes 34-35, codes on dwords 9..16
-#pragma unroll
-                for (int i = 0; i < 8; i++) w0[i] = __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2);
-#pragma unroll
-                for (int i = 0; i < 8; i++) w1[i] = v[i + 9];
-                mv_unit_terms<FMT, MR>(rx, M, kb, u, w0, w1, h2f(v[0]), h2f(v[8] >> 16), 0.0f, 0.0f, acc);
-            }
-            __builtin_amdgcn_wave_barrier();
         } else if (u < units) {
-            uint32_t w0[8], w1[8];
-            const int sb = u >> 2, grp = u & 3;   // super-block, 32-byte code group
-            constexpr int SB = FMT == FMT_Q4_K ? 144 : 176, QS = FMT == FMT_Q4_K ? 16 : 48;
-            const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(rw, SB * sb, 0, 0);
-            const u32x4 q0 = __builtin_amdgcn_raw_buffer_load_b128(rw, SB * sb + QS + 32 * grp, 0, 0);
-            const u32x4 q1 = __builtin_amdgcn_raw_buffer_load_b128(rw, SB * sb + QS + 16 + 32 * grp, 0, 0);
-            const uint32_t q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-            // low nibbles: sub-block 2*grp; high nibbles: sub-block 2*grp+1
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                w0[i] = q[i] & 0x0f0f0f0fu;
-                w1[i] = (q[i] >> 4) & 0x0f0f0f0fu;
-            }
-            if constexpr (FMT == FMT_Q5_K) {
-                // fifth bits: byte l of the high-bit plane holds element l of
-                // sub-block j in bit j (here j = 2*grp and 2*grp+1)
-                const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rw, SB * sb + 16, 0, 0);
-                const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rw, SB * sb + 32, 0, 0);
-                const uint32_t qh[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            for (int r = 0; r < RW; r++) wu[r] = mv_load_kquant<FMT>(rw[r], u);
+        }
+        if (u < units) mv_unit_terms<FMT, MR, RW>(rx, M, kb, u, wu, acc);
+    }
 #pragma unroll
-                for (int i = 0; i < 8; i++) {
-                    w0[i] |= ((qh[i] >> (2 * grp)) & 0x01010101u) << 4;
-                    w1[i] |= ((qh[i] >> (2 * grp + 1)) & 0x01010101u) << 4;
+    for (int r = 0; r < RW; r++) {
+        if (row0 + r < total) {
+            float *out = reinterpret_cast<float *>(set.out[gi[r]]);
+            const int N = set.N[gi[r]];
+#pragma unroll
+            for (int m = 0; m < MR; m++) {
+                if (m < M) {
+                    const float v = wave_sum(acc[r][m]);
+                    if (lane == 0) out[int64_t(m) * N + n[r]] = v;
                 }
             }
-            // 6-bit scale and min of sub-blocks j = 2*grp + {0, 1} (the
-            // K-quant packing: j < 4 in the low six bits of bytes j and j+4;
-            // j >= 4 low four bits from byte j+4, top two bits from the spare
-            // top bits of bytes j-4 and j)
-            const float d = h2f(h.x), dmin = h2f(h.x >> 16);
-            float sc[2], mn[2];
-#pragma unroll
-            for (int t = 0; t < 2; t++) {
-                const int j = 2 * grp + t, sh = 8 * (j & 3);
-                const uint32_t b0 = (h.y >> sh) & 0xffu, b1 = (h.z >> sh) & 0xffu, b2 = (h.w >> sh) & 0xffu;
-                const uint32_t s = j < 4 ? (b0 & 63u) : ((b2 & 15u) | ((b0 >> 6) << 4));
-                const uint32_t mm = j < 4 ? (b1 & 63u) : ((b2 >> 4) | ((b1 >> 6) << 4));
-                sc[t] = (float)s;
-                mn[t] = (float)mm;
-            }
-            mv_unit_terms<FMT, MR>(rx, M, kb, u, w0, w1, d * sc[0], d * sc[1],   // d * sc: exact (11 x 6 bits)
-                                   dmin * mn[0], dmin * mn[1], acc);                 // exact
-        }
-    }
-    float *out = reinterpret_cast<float *>(set.out[gi]);
-#pragma unroll
-    for (int m = 0; m < MR; m++) {
-        if (m < M) {
-            const float v = wave_sum(acc[m]);
-            if (lane == 0) out[int64_t(m) * N + n] = v;
         }
     }
 }

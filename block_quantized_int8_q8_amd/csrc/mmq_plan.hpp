@@ -48,12 +48,19 @@ constexpr int64_t lds_bytes_for(int fmt) {
 }
 
 // Few activation rows (decode): a matrix-vector kernel streams each weight
-// row once for all of them (one wave per output row, kMvRowsPerWg rows per
-// workgroup) instead of a 128-row tile that would be almost empty.
+// row once for all of them (mv_rows_per_wave(M) output rows per wave, four
+// waves per workgroup) instead of a 128-row tile that would be almost empty.
 enum Kernel : int { KERNEL_MMQ = 0, KERNEL_MV = 1 };
 constexpr int kMvMaxM = 8;          // activation rows the matvec kernel takes at most
 constexpr int kMvThreads = 256;
-constexpr int kMvRowsPerWg = kMvThreads / 64;
+constexpr int kMvWaves = kMvThreads / 64;
+// Output rows per wave: two for M >= 5, where the activation loads (one
+// 72-byte block pair per unit, activation row and output row, served from
+// the caches) weigh most and a wave's rows share each of them; one below.
+// Measured on the 7B decode layer at M = 8: Q4_K 150 -> 119 us, Q5_K 157 ->
+// 128 us, Q8_0 168 -> 159 us; four or eight rows per wave were slower than
+// one (fewer resident waves), and at M = 3-4 two rows gained nothing.
+constexpr int mv_rows_per_wave(int64_t M) { return M >= 5 ? 2 : 1; }
 
 struct Plan {
     int fmt = 0;
@@ -71,6 +78,7 @@ struct Plan {
     // instantiation runs full tiles 1-2 % slower (measured: a gain of 11-17 %
     // with 1-3 of 4 wave rows idle, a small loss with 1 of 8).
     bool skip_idle_waves = false;
+    int mv_rows_per_wave = 0;   // matvec kernel: output rows per wave
 };
 constexpr int kSkipShare = 4;   // K-quants skip when idle wave rows >= 1/kSkipShare of all
 
@@ -115,7 +123,9 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
         q.threads = kMvThreads;
         q.blocks_per_stage = 2;
         q.lds_bytes = extra_lds;
-        q.grid_x = (N + kMvRowsPerWg - 1) / kMvRowsPerWg;
+        const int64_t rows_per_wg = int64_t(kMvWaves) * mv_rows_per_wave(M);
+        q.grid_x = (N + rows_per_wg - 1) / rows_per_wg;
+        q.mv_rows_per_wave = mv_rows_per_wave(M);
         q.grid_y = 1;
         q.k_steps = K / 64;
         q.steps_per_split = q.k_steps;
@@ -241,10 +251,11 @@ inline bool make_plan_moe(int fmt, int64_t T, int topk, int n_experts, int64_t N
 inline void describe(const Plan &p, char *buf, size_t len) {
     std::snprintf(buf, len,
                   "kernel=%s fmt=%s tile=%dx%d threads=%d blocks_per_stage=%d lds=%lld grid=%lldx%lld "
-                  "k_steps=%lld split_k=%lld steps_per_split=%lld skip_idle_waves=%d",
+                  "k_steps=%lld split_k=%lld steps_per_split=%lld skip_idle_waves=%d mv_rows_per_wave=%d",
                   p.kernel == KERNEL_MV ? "mv" : "mmq", fmt_name(p.fmt), p.tile_m, p.tile_n, p.threads, p.blocks_per_stage,
                   (long long)p.lds_bytes, (long long)p.grid_x, (long long)p.grid_y,
-                  (long long)p.k_steps, (long long)p.split_k, (long long)p.steps_per_split, int(p.skip_idle_waves));
+                  (long long)p.k_steps, (long long)p.split_k, (long long)p.steps_per_split, int(p.skip_idle_waves),
+                  p.mv_rows_per_wave);
 }
 
 }  // namespace mmq

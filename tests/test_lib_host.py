@@ -128,14 +128,17 @@ def test_moe_workspace_bytes_refuses(T, topk, E):
 
 
 @pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
-@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (1, 3584, 3584), (8, 18944, 3584), (3, 5, 18944)])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (1, 3584, 3584), (2, 4608, 3584), (5, 7, 512), (8, 18944, 3584), (3, 5, 18944)])
 def test_decode_sizes_plan_the_matvec_kernel(fmt, M, N, K):
-    """M <= 8: one wave per output row, four rows per 256-thread workgroup,
-    no LDS, no split."""
+    """M <= 8: the matvec kernel, four waves per 256-thread workgroup, one
+    output row per wave for M <= 4 and two for M >= 5 (the wave's rows share
+    each activation load), no LDS, no split."""
     ok, desc = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
     assert ok and "kernel=mv" in desc, desc
+    rows = 1 if M <= 4 else 2
+    assert f"mv_rows_per_wave={rows}" in desc, desc
     gx, gy = map(int, re.search(r"grid=(\d+)x(\d+)", desc).groups())
-    assert (gx, gy) == (-(-N // 4), 1)
+    assert (gx, gy) == (-(-N // (4 * rows)), 1)
     assert "threads=256" in desc and "lds=0" in desc and "split_k=1" in desc
     # the same shape with one more row is tiled
     assert "kernel=mmq" in mmq.plan_for_limits(fmt, 9, N, K, LDS_GFX950, 256)[1]
