@@ -30,10 +30,16 @@ constexpr int kWgPerCu = 2;        // workgroups resident per CU (LDS and VGPR b
 // Split-K policy, measured on the 7B layer shapes: split only when the output
 // tiles fill at most half of the resident workgroup slots, and then into
 // about one workgroup per CU (more slices cost more in fp32 atomics than
-// they gain), each slice keeping at least four k-steps.
+// they gain), each slice keeping at least four k-steps; with fewer tiles
+// than CUs, into up to two per CU when each slice keeps eight k-steps.
 constexpr int kMinStepsPerSplit = 4;   // k-steps a split-K slice keeps at least
 constexpr int kSplitBelow = 2;         // split when tiles * kSplitBelow <= resident slots
-constexpr int kSplitSlots = 1;         // workgroups per CU a split aims for
+constexpr int kSplitSlots = 1;         // workgroups per CU a split aims for ...
+constexpr int kMinStepsPerSplit2 = 8;  // ... or two per CU, for slices this long
+// (measured at M = 512: the down projection, 112 tiles of 148 k-steps, 143 ->
+// 123 us with 4 slices instead of 3; the q+k+v set, 144 tiles of 28, 62 -> 55
+// us with 3 instead of 2; o, 112 tiles of 28, slower with 4 slices of 7; 256
+// tiles of 28 split in two, slower than one per CU)
 
 // LDS bytes for the kernel's layouts: two k-step buffers, each with codes
 // block-major (32 B per block per row, no padding), the activation block
@@ -141,12 +147,21 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
     if (q.grid_y > 65535) return fail("too many row tiles for the launch grid (M too large)");
     // Too few output tiles to occupy the device (at most half of the
     // resident workgroup slots): split K into slices of at least
-    // kMinStepsPerSplit k-steps, about one workgroup per CU in all.
+    // kMinStepsPerSplit k-steps, about one workgroup per CU in all, or into
+    // up to two per CU when the slices still keep kMinStepsPerSplit2.
     q.steps_per_split = q.k_steps;
     const int64_t tiles = q.grid_x * q.grid_y, slots = int64_t(kWgPerCu) * cu_count;
     if (tiles * kSplitBelow <= slots) {
+        // about one workgroup per CU, slices of at least kMinStepsPerSplit ...
         int64_t s = (int64_t(kSplitSlots) * cu_count + tiles - 1) / tiles;
         if (s > q.k_steps / kMinStepsPerSplit) s = q.k_steps / kMinStepsPerSplit;
+        // ... or, with fewer tiles than CUs, up to two per CU where the
+        // slices keep kMinStepsPerSplit2
+        if (tiles < cu_count) {
+            int64_t s2 = (2 * int64_t(cu_count)) / tiles;
+            if (s2 > q.k_steps / kMinStepsPerSplit2) s2 = q.k_steps / kMinStepsPerSplit2;
+            if (s2 > s) s = s2;
+        }
         if (s > 1) {
             q.steps_per_split = (q.k_steps + s - 1) / s;
             q.split_k = (q.k_steps + q.steps_per_split - 1) / q.steps_per_split;

@@ -55,7 +55,8 @@ def test_plans_for_benchmark_shapes_fit(fmt, M, N, K):
     (2048, 18944, 3584, 1, 28),
     (512, 512, 3584, 7, 4),         # 16 tiles: 7 slices of 4 k-steps (the minimum)
     (512, 3584, 3584, 3, 10),       # 112 tiles: ~one workgroup per CU
-    (512, 3584, 18944, 3, 50),
+    (512, 3584, 18944, 4, 37),      # 112 tiles of 148 k-steps: two per CU, 4 slices
+    (512, 4608, 3584, 3, 10),       # the q+k+v set (144 tiles): 3 slices of >= 8 k-steps
     (2048, 512, 3584, 4, 7),        # 64 tiles
     (8192, 512, 3584, 1, 28),       # 256 tiles: one per CU already
     (64, 256, 512, 1, 4),           # 4 k-steps: too short to split
