@@ -399,6 +399,29 @@ def test_matvec_boundary_m8_m9():
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M,Ns,K", [(8, (257, 130, 33), 512), (5, (3, 1, 2), 256), (6, (1, 129), 18944)])
+def test_matvec_set_rows_straddling_members(fmt, M, Ns, K):
+    """M >= 5 runs two output rows per wave, so with odd member widths a
+    wave's two rows belong to different GEMMs of the set (and the last wave
+    may have one row past the end): every member equals its own launch bit
+    for bit and passes the reordered-sum check against the oracle."""
+    assert _kernel(fmt, M, Ns[0], K) == "mv"
+    _say(f"matvec set fmt={fmt} M={M} Ns={Ns} K={K}")
+    xq = oracle.quantize_q8_1(inputs.activations(M, K, 140 + M))
+    ws = [_weights(fmt, n, K, 150 + g) for g, n in enumerate(Ns)]
+    outs = [_nan_out(M, n) for n in Ns]
+    mmq.gemm_multi(fmt, _to_dev(xq), [_to_dev(w) for w in ws], list(Ns), M, K, outs)
+    torch.cuda.synchronize()
+    for g, (n, w) in enumerate(zip(Ns, ws)):
+        o = outs[g].cpu().numpy()
+        assert not np.isnan(o).any(), f"GEMM {g}: output element left unwritten"
+        single = mmq.gemm(fmt, _to_dev(xq), _to_dev(w), M, n, K)
+        torch.cuda.synchronize()
+        assert np.array_equal(o.view(np.uint32), single.cpu().numpy().view(np.uint32))
+        _check_reordered(fmt, o, _oracle_gemm(fmt, xq, w, M, n, K), xq, w, M, n, K)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_matvec_layer_set_decode(fmt):
     """The 7B layer's projections at one token: q+k+v and gate+up through
     one matvec launch each, o and down alone; each member equal to its own
