@@ -194,8 +194,10 @@ const char *mmq_last_error(void);
 
 /* Describe the launch plan the GEMM of `fmt` would use on the current device
  * (kernel=mmq for the 128 x 128 tile kernel or kernel=mv for the M <= 8
- * matrix-vector kernel, tile, LDS bytes, grid, split-K, and skip_idle_waves:
- * whether waves whose 32 rows all lie past M skip their MFMAs) into buf
+ * matrix-vector kernel, tile, LDS bytes, grid, split-K, skip_idle_waves:
+ * whether waves whose 32 rows all lie past M skip their MFMAs, and
+ * mv_rows_per_wave: the matrix-vector kernel's output rows per wave, 0 for
+ * the tiled kernel) into buf
  * (NUL-terminated).  Returns 1 if the plan
  * would launch, 0 if it would be refused (reason in buf). */
 int mmq_plan_describe(int fmt, int64_t M, int64_t N, int64_t K, char *buf, int64_t len);
