@@ -29,12 +29,25 @@ PEAK_INT8_TOPS = 5000.0          # MI355X dense int8 matrix-core peak, TOP/s
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and blank space, so that the hash
+    below follows the code the compiler sees, not its prose (string literals
+    in the kernel sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash() -> str:
+    """Hash of the kernel sources' code (comments and layout ignored): the
+    committed HBM-traffic counters are reported only while it matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_quantized_int8_q8_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, name), "rb").read())
+            h.update(name.encode())
+            h.update(_code_only(open(os.path.join(csrc, name)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -863,7 +863,8 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
 // once from HBM and used for all M rows, so the kernel is bound by the
 // weight stream, and its arithmetic is VALU int8 dot products
 // (v_dot4_i32_i8), not a matrix core: a wave computes one output row (all M
-// rows of x against one weight row) at a time.  The lanes of the wave stride
+// rows of x against one weight row), or two for M >= 5 (see
+// mv_rows_per_wave), at a time.  The lanes of the wave stride
 // over the row in units of two 32-blocks (Q8_0: a 68-byte block pair, 17
 // dwords; Q4_K: one 32-byte code group of a super-block, i.e. two sub-blocks,
 // plus the super-block's 16-byte header), each lane keeping one fp32 partial
