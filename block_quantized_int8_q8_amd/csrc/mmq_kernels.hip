@@ -606,7 +606,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     __shared__ __attribute__((aligned(16))) uint8_t lds0[L::STEP];
     __shared__ __attribute__((aligned(16))) uint8_t lds1[L::STEP];
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6;
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wr = wv >> 1, wc = wv & 1;          // wave tile: rows 32*wr.., columns 64*wc..
     const int g = lane >> 5, l32 = lane & 31;
     int tx, ty;
