@@ -410,8 +410,8 @@ __device__ __forceinline__ void q4k_subblock(const u32x4 &h, int col, float2 *sW
     sMin[(col * 2 + 1) * KB + jb] = lo;
 }
 
-// Q4_K, half `ks & 1` of super-block `ks / 2`.  Codes: thread -> (column =
-// tid/4, packed chunk c = 4*half + tid%4): the 16 code bytes 16c..16c+15
+// Q4_K, half `ks & 1` of super-block `ks / 2`.  Codes: thread -> (column,
+// packed chunk c = 4*half + cl) by q4k_code_unit: the 16 code bytes 16c..16c+15
 // belong to 32-byte group c/2 and k-half c%2; their low nibbles are codes of
 // sub-block 2*(c/2), their high nibbles of sub-block 2*(c/2)+1 (the layout
 // reading in the header).  They are unpacked at store time, once per
@@ -437,9 +437,24 @@ struct Q5KRegs {
     u32x4 h;
 };
 
+// Q4_K codes: thread -> (column 16*wave + lane%16, chunk lane/16 of the
+// half), so 16 consecutive lanes store 16 consecutive columns of one block
+// and k-half, which the swizzled code rows spread over distinct banks (four
+// lanes per column wrote four blocks, 4 KiB apart, into the same banks).  A
+// wave instruction still reads 16 columns x 64 contiguous bytes.  Measured
+// 1-2 % faster on Q4_K, output unchanged; Q5_K keeps four lanes per column,
+// since its 8-byte loads lose more coalescing than its stores gain (6 %
+// slower).
+__device__ __forceinline__ void q4k_code_unit(int tid, int &col, int &cl) {
+    col = 16 * (tid >> 6) + (tid & 15);
+    cl = (tid >> 4) & 3;
+}
+
 __device__ __forceinline__ void load_q4_K(__amdgpu_buffer_rsrc_t rw, int nsb, int ks, int tid, Q4KRegs &r) {
     const int sb = ks >> 1, half = ks & 1;
-    const int col = tid >> 2, c = 4 * half + (tid & 3);
+    int col, cl;
+    q4k_code_unit(tid, col, cl);
+    const int c = 4 * half + cl;
     r.v = __builtin_amdgcn_raw_buffer_load_b128(rw, (col * nsb + sb) * 144 + 16 + 16 * c, 0, 0);
     const int hcol = (tid >> 8) * 64 + (tid & 63);
     r.h = __builtin_amdgcn_raw_buffer_load_b128(rw, (hcol * nsb + sb) * 144, 0, 0);
@@ -485,7 +500,8 @@ __device__ __forceinline__ void store_kquant(const Regs &r, uint8_t *buf, int ks
             *reinterpret_cast<uint2 *>(sB + off + (2 * i + 1) * kBlockBytes) = hi;
         }
     } else {
-        const int col = tid >> 2, cl = tid & 3;      // cl: chunk within this half
+        int col, cl;                                 // cl: chunk within this half
+        q4k_code_unit(tid, col, cl);
         const u32x4 lo = r.v & 0x0F0F0F0Fu;
         const u32x4 hi = (r.v >> 4) & 0x0F0F0F0Fu;
         // sub-blocks 2*(c/2) and 2*(c/2)+1 are blocks 2*(cl/2) and 2*(cl/2)+1 of this step
