@@ -28,6 +28,9 @@ def q8_1_blocks():
         elif b["x"] == "onehot":
             x[5] = -2.0
             c[5] = -127
+        elif b["x"] == "recip":
+            x[0], x[1] = 9.0, 4.5
+            c[0], c[1] = 127, 64
         xs.append(x)
         d.append(b["d_bits"])
         s.append(b["s_bits"])
