@@ -181,24 +181,38 @@ def time_config(cfg, steps: int, warmup: int, check: bool = True, cold: bool = F
     }
 
 
-def check_parity(fmt, M, N, K, x, w, xq_dev, out_dev):
-    """The timed output, checked against the oracle on sampled rows."""
+def check_parity(fmt, M, N, K, x, w, xq_dev, out_dev, full_rows: int = 2048):
+    """The timed output against the oracle: every row when M <= full_rows
+    (all the M=2048 configurations), else sampled rows.  The oracle run is
+    timed (quantize + GEMM, all host cores): for the configurations other
+    than the headline it is their one-run CPU baseline."""
     import oracle
     from tests import metrics
+    threads = min(16, os.cpu_count() or 1)
+    t0 = time.perf_counter()
     xq = oracle.quantize_q8_1(x)
     q_ok = bool(np.array_equal(xq_dev.cpu().numpy(), xq))
     o = out_dev.cpu().numpy()
-    rows = sorted(set([0, M - 1, M // 2] + list(np.random.default_rng(0).integers(0, M, 5))))
+    rows = list(range(M)) if M <= full_rows else \
+        sorted(set([0, M - 1, M // 2] + list(np.random.default_rng(0).integers(0, M, 5))))
     f = {"q8_0": oracle.gemm_q8_0, "q4_K": oracle.gemm_q4_K, "q5_K": oracle.gemm_q5_K}[fmt]
-    ref = f(np.ascontiguousarray(xq[rows]), w, len(rows), N, K, nthreads=min(16, os.cpu_count() or 1))
-    rep = metrics.report(o[rows], ref)
+    t1 = time.perf_counter()
+    ref = f(xq if len(rows) == M else np.ascontiguousarray(xq[rows]), w, len(rows), N, K, nthreads=threads)
+    t2 = time.perf_counter()
+    rep = metrics.report(o if len(rows) == M else o[rows], ref)
+    oracle_s = (t1 - t0) + (t2 - t1) if len(rows) == M else None
     return {
         "quantize_bit_exact": q_ok,
         "unwritten": int(np.isnan(o).sum()),
         "rows_checked": len(rows),
         "normalized_max_error": rep["normalized_max_error"],
+        "elementwise_max_rel": rep["elementwise_max_rel"],
+        "count_over_tol_elementwise": rep["count_over_tol_elementwise"],
         "bit_identical_fraction": rep["bit_identical_fraction"],
         "ok": bool(q_ok and not np.isnan(o).any() and rep["normalized_max_error"] <= metrics.TOL),
+        # the oracle's quantize (including its byte comparison) and full GEMM, one run
+        "oracle_s": oracle_s,
+        "oracle_threads": oracle.threads_used(threads),
     }
 
 
@@ -544,6 +558,19 @@ def time_moe(fmt_name: str, steps: int, warmup: int, check: bool = True):
     }
 
 
+def oracle_baseline(rec):
+    """The one full oracle run of a configuration's parity check (quantize +
+    GEMM over every row, all host cores) as its CPU baseline; None when the
+    check was skipped or sampled rows only."""
+    par = rec.get("parity") or {}
+    if not par.get("oracle_s"):
+        return None
+    M, N, K = rec["M"], rec["N"], rec["K"]
+    return {"value": 2.0 * M * N * K / par["oracle_s"] / 1e12, "unit": "TOP/s", "cores": par["oracle_threads"],
+            "kind": "oracle", "sample": f"all {M} rows (quantize + full GEMM), one run, {par['oracle_s']:.2f} s",
+            "vs_gpu_gemm": rec["gemm_tops"] / (2.0 * M * N * K / par["oracle_s"] / 1e12)}
+
+
 def _cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -648,7 +675,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    def progress(what):
+        print(f"bench.py: {what} done", file=sys.stderr, flush=True)
+
     main_rec = time_config(args.config, args.steps, args.warmup, check=not args.no_check, cold=True)
+    progress(f"config {args.config}")
     extra = {}
     for c in [int(v) for v in args.extra_configs.split(",") if v.strip()]:
         if c != args.config:
@@ -656,22 +687,29 @@ def main():
             extra[f"config{c}"] = {k: r[k] for k in ("fmt", "M", "N", "K", "ms_per_step", "tops_step",
                                                       "gemm_ms_avg", "gemm_tops", "quant_gbs", "parity")}
             extra[f"config{c}"]["gemm_frac_of_int8_peak"] = r["gemm_tops"] / PEAK_INT8_TOPS
+            extra[f"config{c}"]["cpu_baseline"] = oracle_baseline(r)
+            progress(f"config {c}")
 
     for spec in [v.strip() for v in args.extra_shapes.split(",") if v.strip()]:
         r = time_config(spec, max(5, args.steps // 5), 2, check=not args.no_check)
         extra[spec] = {k: r[k] for k in ("fmt", "M", "N", "K", "ms_per_step", "tops_step", "gemm_ms_avg",
                                          "gemm_tops", "quant_gbs", "parity")}
         extra[spec]["gemm_frac_of_int8_peak"] = r["gemm_tops"] / PEAK_INT8_TOPS
+        extra[spec]["cpu_baseline"] = oracle_baseline(r)
+        progress(spec)
 
     for m in [int(v) for v in args.layer_m.split(",") if v.strip()]:
         extra[f"layer_M{m}"] = time_layer(m, max(3, args.steps // 10), 1, check=not args.no_check)
+        progress(f"layer M={m}")
 
     for spec in [v.strip() for v in args.decode.split(",") if v.strip()]:
         f, m = spec.split(":")
         extra[f"decode_{f}_M{m}"] = time_decode(int(m), f, max(10, args.steps // 2), 2, check=not args.no_check)
+        progress(f"decode {spec}")
 
     for f in [v.strip() for v in args.moe.split(",") if v.strip()]:
         extra[f"moe_{f}"] = time_moe(f, max(3, args.steps // 5), 1, check=not args.no_check)
+        progress(f"moe {f}")
 
     kname = "k_mmq<Q8_0>" if main_rec["fmt"] == "q8_0" else "k_mmq<Q4_K>"
     achieved = main_rec["gemm_tops"]
@@ -691,6 +729,7 @@ def main():
         "kernel_ms_avg": main_rec["gemm_ms_avg"],
     }
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.config)
+    progress("cpu baseline")
     M, N, K = main_rec["M"], main_rec["N"], main_rec["K"]
     line = {
         "metric": METRIC,

@@ -60,7 +60,7 @@ def lib() -> ctypes.CDLL:
         L.mmq_last_error.restype = ctypes.c_char_p
         L.mmq_plan_describe.argtypes = [i32, i64, i64, i64, ctypes.c_char_p, i64]
         L.mmq_plan_describe.restype = i32
-        L.mmq_plan_for_limits.argtypes = [i32, i64, i64, i64, i64, i32, ctypes.c_char_p, i64]
+        L.mmq_plan_for_limits.argtypes = [i32, i64, i64, i64, i64, i32, i32, i64, ctypes.c_char_p, i64]
         L.mmq_plan_for_limits.restype = i32
         L.mmq_debug_set_extra_lds.argtypes = [i64]
         L.mmq_debug_set_extra_lds.restype = None
@@ -85,6 +85,31 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def row_bytes(fmt, K) -> int:
+    """Bytes of one weight row of K values in format ``fmt``."""
+    if fmt == FMT_Q8_0:
+        return (K // 32) * Q8_0_BYTES
+    if fmt in (FMT_Q4_K, FMT_Q5_K):
+        return (K // 256) * (Q4_K_BYTES if fmt == FMT_Q4_K else Q5_K_BYTES)
+    raise ValueError(f"unknown weight format {fmt}")
+
+
+def _need(t, dtype, count, what):
+    """``t`` must be a ``dtype`` tensor holding at least ``count`` elements:
+    the library receives bare pointers and trusts the sizes it is given, so a
+    short buffer would be read or written past its end on the device."""
+    if t.dtype != dtype:
+        raise ValueError(f"{what}: expected {dtype}, got {t.dtype}")
+    if count > 0 and t.numel() < count:
+        raise ValueError(f"{what} holds {t.numel()} elements; the shape needs {count}")
+
+
+def _dims_ok(*dims) -> bool:
+    # sizes are checked only for shapes the library could accept; it refuses
+    # the others itself, with its own reason
+    return all(int(d) >= 1 for d in dims)
+
+
 def _ptr(t, dtype=None):
     if not t.is_cuda:
         raise ValueError("tensor must be on a GPU device")
@@ -101,17 +126,32 @@ def quantize_q8_1(x, y=None, stream=None):
     M, K = x.shape
     if y is None:
         y = torch.empty((M, K // 32, Q8_1_BYTES), dtype=torch.uint8, device=x.device)
+    if _dims_ok(M, K):
+        _need(x, torch.float32, M * K, "x")
+        _need(y, torch.uint8, M * (K // 32) * Q8_1_BYTES, "y (q8_1)")
     _check(lib().mmq_quantize_q8_1(_ptr(x, torch.float32), _ptr(y, torch.uint8), M, K, _stream(stream)),
            "mmq_quantize_q8_1")
     return y
+
+
+def _check_gemm_sizes(fmt, xq, w, out, M, N, K):
+    import torch
+    if _dims_ok(M, N, K):
+        _need(xq, torch.uint8, M * (K // 32) * Q8_1_BYTES, "xq (q8_1 activations)")
+        _need(w, torch.uint8, N * row_bytes(fmt, K), "w (weights)")
+        _need(out, torch.float32, M * N, "out")
 
 
 def _gemm(fn, name, xq, w, M, N, K, out, stream):
     import torch
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    _check_gemm_sizes(_FN_FMT[fn], xq, w, out, M, N, K)
     _check(getattr(lib(), fn)(_ptr(xq), _ptr(w), _ptr(out, torch.float32), M, N, K, _stream(stream)), name)
     return out
+
+
+_FN_FMT = {"mmq_gemm_q8_0": FMT_Q8_0, "mmq_gemm_q4_K": FMT_Q4_K, "mmq_gemm_q5_K": FMT_Q5_K}
 
 
 def gemm_q8_0(xq, w, M, N, K, out=None, stream=None):
@@ -144,6 +184,8 @@ def gemm_multi(fmt, xq, ws, Ns, M, K, outs=None, stream=None):
         raise ValueError("ws, Ns and outs must have the same length")
     if outs is None:
         outs = [torch.empty((M, n), dtype=torch.float32, device=xq.device) for n in Ns]
+    for w, o, n in zip(ws, outs, Ns):
+        _check_gemm_sizes(fmt, xq, w, o, M, n, K)
     wp = (ctypes.c_void_p * count)(*[_ptr(w).value for w in ws])
     op = (ctypes.c_void_p * count)(*[_ptr(o, torch.float32).value for o in outs])
     npv = (ctypes.c_int64 * count)(*[int(n) for n in Ns])
@@ -156,6 +198,15 @@ def moe_workspace_bytes(T, topk, n_experts) -> int:
     return int(lib().mmq_moe_workspace_bytes(T, topk, n_experts))
 
 
+def _check_moe_sizes(fmt, xq, w, n_experts, topk, T, N, K, out, workspace):
+    import torch
+    if _dims_ok(T, topk, n_experts, N, K):
+        _need(xq, torch.uint8, T * (K // 32) * Q8_1_BYTES, "xq (q8_1 activations)")
+        _need(w, torch.uint8, n_experts * N * row_bytes(fmt, K), "w (expert weights)")
+        _need(out, torch.float32, T * topk * N, "out")
+    _need(workspace, torch.uint8, 0, "workspace")
+
+
 def moe_gemm(fmt, xq, w, n_experts, ids, topk, T, N, K, out=None, workspace=None, stream=None):
     """Indexed MoE: q8_1 [T, K/32, 36] x expert weights [E, N, ...] routed by
     int32 ids [T, topk] -> fp32 [T*topk, N] (row t*topk + j = token t times
@@ -166,6 +217,9 @@ def moe_gemm(fmt, xq, w, n_experts, ids, topk, T, N, K, out=None, workspace=None
     need = moe_workspace_bytes(T, topk, n_experts)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=xq.device)
+    _check_moe_sizes(fmt, xq, w, n_experts, topk, T, N, K, out, workspace)
+    if _dims_ok(T, topk):
+        _need(ids, torch.int32, T * topk, "ids")
     _check(lib().mmq_moe_gemm(fmt, _ptr(xq), _ptr(w), n_experts, _ptr(ids, torch.int32), topk,
                               _ptr(out, torch.float32), T, N, K, _ptr(workspace, torch.uint8),
                               workspace.numel(), _stream(stream)), "mmq_moe_gemm")
@@ -179,6 +233,7 @@ def moe_gemm_routed(fmt, xq, w, n_experts, topk, T, N, K, workspace, out=None, s
     import torch
     if out is None:
         out = torch.empty((T * topk, N), dtype=torch.float32, device=xq.device)
+    _check_moe_sizes(fmt, xq, w, n_experts, topk, T, N, K, out, workspace)
     _check(lib().mmq_moe_gemm_routed(fmt, _ptr(xq), _ptr(w), n_experts, topk, _ptr(out, torch.float32), T, N, K,
                                      _ptr(workspace, torch.uint8), workspace.numel(), _stream(stream)),
            "mmq_moe_gemm_routed")
@@ -190,6 +245,10 @@ def debug_block_dots(fmt, xq, w, M, N, K, dots=None, stream=None):
     import torch
     if dots is None:
         dots = torch.empty((M, N, K // 32), dtype=torch.int32, device=xq.device)
+    if _dims_ok(M, N, K):
+        _need(xq, torch.uint8, M * (K // 32) * Q8_1_BYTES, "xq (q8_1 activations)")
+        _need(w, torch.uint8, N * row_bytes(fmt, K), "w (weights)")
+        _need(dots, torch.int32, M * N * (K // 32), "dots")
     _check(lib().mmq_debug_block_dots(fmt, _ptr(xq), _ptr(w), _ptr(dots, torch.int32), M, N, K,
                                       _stream(stream)), "mmq_debug_block_dots")
     return dots
@@ -201,9 +260,11 @@ def plan_describe(fmt, M, N, K) -> tuple[bool, str]:
     return bool(ok), buf.value.decode()
 
 
-def plan_for_limits(fmt, M, N, K, lds_limit, cu_count) -> tuple[bool, str]:
+def plan_for_limits(fmt, M, N, K, lds_limit, cu_count, vgprs=0, scratch=0) -> tuple[bool, str]:
+    """Pure host planning; ``vgprs``/``scratch``: the launched kernel's
+    registers and scratch bytes per lane (0 registers: the built budget)."""
     buf = ctypes.create_string_buffer(512)
-    ok = lib().mmq_plan_for_limits(fmt, M, N, K, lds_limit, cu_count, buf, 512)
+    ok = lib().mmq_plan_for_limits(fmt, M, N, K, lds_limit, cu_count, vgprs, scratch, buf, 512)
     return bool(ok), buf.value.decode()
 
 

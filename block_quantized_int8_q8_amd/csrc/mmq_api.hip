@@ -12,7 +12,10 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <deque>
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "../../include/mmq.h"
 #include "mmq_plan.hpp"
@@ -23,6 +26,7 @@ hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const vo
                        void *const *out, const int64_t *N, int64_t M, int64_t K, bool dots, hipStream_t stream);
 hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t *ids, int topk, int n_experts,
                       float *out, int64_t T, int64_t N, int64_t K, void *workspace, hipStream_t stream);
+const void *plan_kernel(const Plan &p, bool dots, bool moe);
 }  // namespace mmq
 
 namespace {
@@ -88,6 +92,51 @@ bool current_limits(DeviceLimits *out) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Registers and scratch of a kernel on the current device
+// (hipFuncGetAttributes), cached per (device, kernel).
+std::mutex g_fit_mu;
+std::map<std::pair<int, const void *>, mmq::KernelFit> g_fit;
+
+bool kernel_fit(const void *fn, mmq::KernelFit *fit) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        refuse("no HIP device available");
+        return false;
+    }
+    const auto key = std::make_pair(dev, fn);
+    std::lock_guard<std::mutex> lock(g_fit_mu);
+    auto it = g_fit.find(key);
+    if (it == g_fit.end()) {
+        hipFuncAttributes a;
+        if (hipFuncGetAttributes(&a, fn) != hipSuccess) {
+            (void)hipGetLastError();
+            refuse("hipFuncGetAttributes failed for a kernel on device %d", dev);
+            return false;
+        }
+        mmq::KernelFit f;
+        f.vgprs = a.numRegs;
+        f.scratch = int64_t(a.localSizeBytes);
+        it = g_fit.emplace(key, f).first;
+    }
+    *fit = it->second;
+    return true;
+}
+
+// Plan with the nominal kernel, read the attributes of the kernel that plan
+// launches, and plan again with them (the kernel choice depends on the
+// shape only, so the second plan launches the same kernel).
+template <typename MakePlan>
+bool plan_with_kernel_fit(MakePlan make, bool dots, bool moe, mmq::Plan *p, char *why, size_t why_len) {
+    if (!make(mmq::KernelFit(), p, why, why_len)) return false;
+    mmq::KernelFit fit;
+    if (!kernel_fit(mmq::plan_kernel(*p, dots, moe), &fit)) {
+        std::snprintf(why, why_len, "%s", g_err);
+        return false;
+    }
+    return make(fit, p, why, why_len);
+}
+
 int gemm_set(int fmt, const void *x, int count, const void *const *w, void *const *out, const int64_t *N,
              int64_t M, int64_t K, bool dots, void *stream) {
     g_err[0] = '\0';
@@ -107,8 +156,11 @@ int gemm_set(int fmt, const void *x, int count, const void *const *w, void *cons
     int tile_start[mmq::kMaxGemms + 1];
     char why[256];
     // the block-dot output exists for the MMQ kernel only
-    if (!mmq::make_plan_multi(fmt, M, count, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), &p, tile_start,
-                              why, sizeof(why), !dots))
+    auto make = [&](const mmq::KernelFit &fit, mmq::Plan *q, char *w, size_t wl) {
+        return mmq::make_plan_multi(fmt, M, count, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), q,
+                                    tile_start, w, wl, !dots, fit);
+    };
+    if (!plan_with_kernel_fit(make, dots, false, &p, why, sizeof(why)))
         return refuse("%s GEMM M=%lld N=%lld K=%lld%s: %s", mmq::fmt_name(fmt), (long long)M, (long long)N[0],
                       (long long)K, count > 1 ? " (first of a set)" : "", why);
     (void)hipGetLastError();   // a stale error must not be blamed on this launch
@@ -173,6 +225,49 @@ int64_t mmq_moe_workspace_bytes(int64_t T, int topk, int n_experts) {
 
 namespace {
 
+// Which routing each MoE workspace holds: (device, workspace) -> (routed
+// rows, experts) of the last mmq_moe_gemm enqueued with it.  A routed call
+// is refused on the host unless its sizes match, so it never launches over
+// tables built for other sizes (or never built).  The GEMM kernel keeps its
+// own check of the header the routing kernel writes, for a workspace whose
+// contents the caller changed after routing.  At most kMaxRoutes
+// workspaces are remembered (the oldest is forgotten first; a routed call
+// on a forgotten workspace is refused, never run on stale tables).
+constexpr size_t kMaxRoutes = 1024;
+std::mutex g_routes_mu;
+std::map<std::pair<int, const void *>, std::pair<int64_t, int>> g_routes;
+std::deque<std::pair<int, const void *>> g_route_order;
+
+void record_route(const void *workspace, int64_t R, int E) {
+    int dev = -1;
+    (void)hipGetDevice(&dev);
+    const auto key = std::make_pair(dev, workspace);
+    std::lock_guard<std::mutex> lock(g_routes_mu);
+    if (g_routes.find(key) == g_routes.end()) {
+        g_route_order.push_back(key);
+        if (g_route_order.size() > kMaxRoutes) {
+            g_routes.erase(g_route_order.front());
+            g_route_order.pop_front();
+        }
+    }
+    g_routes[key] = std::make_pair(R, E);
+}
+
+// Returns nullptr when `workspace` holds a routing of R rows and E experts.
+const char *route_mismatch(const void *workspace, int64_t R, int E, char *buf, size_t len) {
+    int dev = -1;
+    (void)hipGetDevice(&dev);
+    std::lock_guard<std::mutex> lock(g_routes_mu);
+    const auto it = g_routes.find(std::make_pair(dev, workspace));
+    if (it == g_routes.end()) return "the workspace holds no routing from mmq_moe_gemm on this device";
+    if (it->second.first != R || it->second.second != E) {
+        std::snprintf(buf, len, "the workspace was routed for %lld rows and %d experts, not %lld and %d",
+                      (long long)it->second.first, it->second.second, (long long)R, E);
+        return buf;
+    }
+    return nullptr;
+}
+
 int moe_common(int fmt, const void *x_q8_1, const void *w, int n_experts, const int32_t *ids, int topk, float *out,
                int64_t T, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes, void *stream,
                const char *name) {
@@ -187,17 +282,27 @@ int moe_common(int fmt, const void *x_q8_1, const void *w, int n_experts, const 
     if (!L.is_gfx950) return refuse("device is %s; this library is built for gfx950 only", L.arch);
     mmq::Plan p;
     char why[256];
-    if (!mmq::make_plan_moe(fmt, T, topk, n_experts, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), &p,
-                            why, sizeof(why)))
+    auto make = [&](const mmq::KernelFit &fit, mmq::Plan *q, char *w, size_t wl) {
+        return mmq::make_plan_moe(fmt, T, topk, n_experts, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), q,
+                                  w, wl, fit);
+    };
+    if (!plan_with_kernel_fit(make, false, true, &p, why, sizeof(why)))
         return refuse("%s %s T=%lld topk=%d E=%d N=%lld K=%lld: %s", mmq::fmt_name(fmt), name, (long long)T, topk,
                       n_experts, (long long)N, (long long)K, why);
     const int64_t need = mmq::moe_workspace_bytes(T * topk, n_experts);
     if (workspace_bytes < need)
         return refuse("MoE workspace of %lld B given, %lld B needed", (long long)workspace_bytes, (long long)need);
+    if (!ids) {
+        char buf[160];
+        if (const char *bad = route_mismatch(workspace, T * topk, n_experts, buf, sizeof(buf)))
+            return refuse("%s %s T=%lld topk=%d E=%d: %s", mmq::fmt_name(fmt), name, (long long)T, topk, n_experts,
+                          bad);
+    }
     (void)hipGetLastError();
     const hipError_t e = mmq::launch_moe(p, x_q8_1, w, ids, topk, n_experts, out, T, N, K, workspace,
                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return refuse("%s %s launch failed: %s", mmq::fmt_name(fmt), name, hipGetErrorString(e));
+    if (ids) record_route(workspace, T * topk, n_experts);
     return 1;
 }
 
@@ -230,11 +335,14 @@ int mmq_debug_block_dots(int fmt, const void *x_q8_1, const void *w, int32_t *do
 const char *mmq_last_error(void) { return g_err; }
 
 int mmq_plan_for_limits(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limit_bytes, int cu_count,
-                        char *buf, int64_t len) {
+                        int kernel_vgprs, int64_t kernel_scratch_bytes, char *buf, int64_t len) {
     mmq::Plan p;
     char why[256];
+    mmq::KernelFit fit;
+    if (kernel_vgprs > 0) fit.vgprs = kernel_vgprs;
+    fit.scratch = kernel_scratch_bytes;
     const bool ok = mmq::make_plan(fmt, M, N, K, lds_limit_bytes, cu_count, g_extra_lds.load(), &p, why,
-                                   sizeof(why));
+                                   sizeof(why), true, fit);
     if (buf && len > 0) {
         if (ok)
             mmq::describe(p, buf, size_t(len));
@@ -250,7 +358,20 @@ int mmq_plan_describe(int fmt, int64_t M, int64_t N, int64_t K, char *buf, int64
         if (buf && len > 0) std::snprintf(buf, size_t(len), "%s", g_err);
         return 0;
     }
-    return mmq_plan_for_limits(fmt, M, N, K, L.lds_per_block, L.cu_count, buf, len);
+    mmq::Plan p;
+    char why[256];
+    auto make = [&](const mmq::KernelFit &fit, mmq::Plan *q, char *w, size_t wl) {
+        return mmq::make_plan(fmt, M, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), q, w, wl, true, fit);
+    };
+    const bool ok = mmq::fmt_ok(fmt) && plan_with_kernel_fit(make, false, false, &p, why, sizeof(why));
+    if (!mmq::fmt_ok(fmt)) std::snprintf(why, sizeof(why), "unknown weight format");
+    if (buf && len > 0) {
+        if (ok)
+            mmq::describe(p, buf, size_t(len));
+        else
+            std::snprintf(buf, size_t(len), "%s", why);
+    }
+    return ok ? 1 : 0;
 }
 
 void mmq_debug_set_extra_lds(int64_t extra_bytes) { g_extra_lds.store(extra_bytes < 0 ? 0 : extra_bytes); }

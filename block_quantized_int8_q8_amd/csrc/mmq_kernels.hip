@@ -250,6 +250,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base,
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, n, 0x00020000);
 }
 
+// A raw buffer over weight bytes that may start 2 bytes off the dword grid
+// (Q8_0 rows, or MoE experts' matrices, when K/32 is odd): the descriptor
+// starts at the dword below the first byte, `shift` (0 or 2) is added to
+// every offset, and the length is rounded up to whole dwords.  The range
+// check is per dword, so a last dword the exact length covered only in part
+// would read as zero; the <= 3 bytes added share a dword with the last byte
+// of the range, so they never reach another page.
+struct WBuf {
+    __amdgpu_buffer_rsrc_t r;
+    int shift;
+};
+
+__device__ __forceinline__ WBuf weight_rsrc(const uint8_t *base, int64_t bytes) {
+    WBuf w;
+    w.shift = int(reinterpret_cast<uintptr_t>(base) & 3);
+    w.r = tile_rsrc(base - w.shift, bytes > 0 ? (bytes + w.shift + 3) & ~int64_t(3) : 0);
+    return w;
+}
+
 // Activations go from global memory to LDS by DMA (buffer_load ... lds): a
 // wave's DMA instruction writes 64 consecutive LDS slots of its size, slot i
 // from lane i's address, so choosing each lane's source realises any layout
@@ -325,54 +344,62 @@ __device__ __forceinline__ void dma_activations(__amdgpu_buffer_rsrc_t rx, const
 // codes are unpacked, so neither can be copied as it is.  Each of the 512
 // threads moves one unit per step.
 //
-// Q8_0: a pair of 34-byte blocks is 68 bytes = 17 dwords starting on a
-// 4-byte boundary (K % 256 == 0 makes every row an even number of blocks).
-// Thread -> (column, pair q, half p) with p = wave%2 (wave-uniform): half 0
-// reads dwords 0..8 and realigns the even block's codes, which sit two bytes
-// off the dword grid, with v_alignbyte; half 1 reads dword 8 (the odd block's
-// scale in its high half) and the aligned dwords 9..16.
+// Q8_0: thread -> (column, block b of the step), b = 2*(u%2) + wave%2, so a
+// lane pair covers four consecutive blocks of one column.  A 34-byte block
+// starts on a 2-byte boundary: at byte 4j of the dword grid when its index
+// (column * kb + block) is even, at 4j + 2 when it is odd (every row starts
+// on a 4-byte boundary when kb is even, every other row when kb is odd).  The
+// thread loads the 9 dwords [4j, 4j + 36) that hold it and realigns the codes
+// with v_perm, whose byte selector takes the lane's own offset.  Blocks past
+// the row's last one (the partial last k-step when K % 128 != 0) are staged
+// with weight scale 0, so whatever codes the load returned add nothing.
 struct Q80Regs {
-    u32x4 v0, v1;
-    uint32_t last;
+    uint32_t first;   // dword 0 of the window: the scale, in its low or high half
+    u32x4 v0, v1;     // dwords 1..8
 };
 
-__device__ __forceinline__ int q80_unit(int tid) { return (tid >> 7) * 64 + (tid & 63); }
-
-__device__ __forceinline__ void load_q8_0(__amdgpu_buffer_rsrc_t rw, int kb, int ks, int tid, Q80Regs &r) {
-    const int u = q80_unit(tid), p = (tid >> 6) & 1;
-    const int col = u >> 1, q = u & 1;
-    const int off = (col * kb + ks * KB + 2 * q) * 34;
-    r.v0 = __builtin_amdgcn_raw_buffer_load_b128(rw, off + 36 * p, 0, 0);
-    r.v1 = __builtin_amdgcn_raw_buffer_load_b128(rw, off + 16 + 36 * p, 0, 0);
-    r.last = __builtin_amdgcn_raw_buffer_load_b32(rw, off + 32, 0, 0);
+__device__ __forceinline__ void q80_unit(int tid, int &col, int &b) {
+    const int u = (tid >> 7) * 64 + (tid & 63);
+    col = u >> 1;
+    b = 2 * (u & 1) + ((tid >> 6) & 1);
 }
 
-__device__ __forceinline__ void store_q8_0(const Q80Regs &r, uint8_t *buf, int tid) {
+// Byte offset of block blk of tile column col in the tile's weight buffer.
+__device__ __forceinline__ int q80_off(int wshift, int kb, int col, int blk) { return wshift + (col * kb + blk) * 34; }
+
+__device__ __forceinline__ void load_q8_0(__amdgpu_buffer_rsrc_t rw, int wshift, int kb, int ks, int tid,
+                                          Q80Regs &r) {
+    int col, b;
+    q80_unit(tid, col, b);
+    const int a = q80_off(wshift, kb, col, ks * KB + b) & ~3;   // the dword holding the block's first byte
+    r.first = __builtin_amdgcn_raw_buffer_load_b32(rw, a, 0, 0);
+    r.v0 = __builtin_amdgcn_raw_buffer_load_b128(rw, a + 4, 0, 0);
+    r.v1 = __builtin_amdgcn_raw_buffer_load_b128(rw, a + 20, 0, 0);
+}
+
+__device__ __forceinline__ void store_q8_0(const Q80Regs &r, uint8_t *buf, int wshift, int kb, int ks, int tid) {
     using L = Lds<FMT_Q8_0>;
     uint8_t *sB = buf + L::OFF_B_CODES;
     float2 *sW = reinterpret_cast<float2 *>(buf + L::OFF_B_SCALE);
-    const int u = q80_unit(tid), p = (tid >> 6) & 1;
-    const int col = u >> 1, b = 2 * (u & 1) + p;
+    int col, b;
+    q80_unit(tid, col, b);
+    const int blk = ks * KB + b;
+    const bool odd = q80_off(wshift, kb, col, blk) & 2;   // block starts 2 bytes into its first dword
+    // bytes 2..5 of (dword i+1 : dword i), or all of dword i+1
+    const uint32_t sel = odd ? 0x07060504u : 0x05040302u;
+    const uint32_t w[9] = {r.first, r.v0.x, r.v0.y, r.v0.z, r.v0.w, r.v1.x, r.v1.y, r.v1.z, r.v1.w};
     u32x4 c0, c1;
-    uint32_t dbits;
-    if (p == 0) {   // wave-uniform
-        c0.x = __builtin_amdgcn_alignbyte(r.v0.y, r.v0.x, 2);
-        c0.y = __builtin_amdgcn_alignbyte(r.v0.z, r.v0.y, 2);
-        c0.z = __builtin_amdgcn_alignbyte(r.v0.w, r.v0.z, 2);
-        c0.w = __builtin_amdgcn_alignbyte(r.v1.x, r.v0.w, 2);
-        c1.x = __builtin_amdgcn_alignbyte(r.v1.y, r.v1.x, 2);
-        c1.y = __builtin_amdgcn_alignbyte(r.v1.z, r.v1.y, 2);
-        c1.z = __builtin_amdgcn_alignbyte(r.v1.w, r.v1.z, 2);
-        c1.w = __builtin_amdgcn_alignbyte(r.last, r.v1.w, 2);
-        dbits = r.v0.x;
-    } else {
-        c0 = r.v0;
-        c1 = r.v1;
-        dbits = r.last >> 16;
-    }
+    c0.x = __builtin_amdgcn_perm(w[1], w[0], sel);
+    c0.y = __builtin_amdgcn_perm(w[2], w[1], sel);
+    c0.z = __builtin_amdgcn_perm(w[3], w[2], sel);
+    c0.w = __builtin_amdgcn_perm(w[4], w[3], sel);
+    c1.x = __builtin_amdgcn_perm(w[5], w[4], sel);
+    c1.y = __builtin_amdgcn_perm(w[6], w[5], sel);
+    c1.z = __builtin_amdgcn_perm(w[7], w[6], sel);
+    c1.w = __builtin_amdgcn_perm(w[8], w[7], sel);
     *reinterpret_cast<u32x4 *>(sB + code_off(b, col, 0)) = c0;
     *reinterpret_cast<u32x4 *>(sB + code_off(b, col, 1)) = c1;
-    const float ws = h2f(dbits);
+    const float ws = blk < kb ? h2f(odd ? r.first >> 16 : r.first) : 0.0f;
     sW[b * kTileN + col] = make_float2(ws, -kMagic * ws);   // exact: 11 x 2 bits
 }
 
@@ -658,7 +685,9 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
         wq += int64_t(mt.x) * moe.expert_bytes;
     }
     const int n0 = (tx - set.tile_start[gi]) * kTileN, m0 = MOE ? 0 : ty * kTileM;
-    const int kb = K >> 5, nsteps = kb / KB;
+    // K-quants: whole super-blocks, so whole k-steps; Q8_0: the last k-step
+    // may hold fewer than KB blocks (see nvalid below)
+    const int kb = K >> 5, nsteps = (kb + KB - 1) / KB;
     // this workgroup's k-steps: [ks0, ks0 + nloc) (all of them unless K is split)
     const int ks0 = blockIdx.z * steps_per_split;
     const int nloc = min(steps_per_split, nsteps - ks0);
@@ -667,7 +696,8 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     const int64_t xrow = int64_t(kb) * 36;
     const int64_t wrow = weight_row_bytes(FMT, K);
     const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq + int64_t(m0) * xrow, int64_t(M - m0) * xrow);
-    const __amdgpu_buffer_rsrc_t rw = tile_rsrc(wq + int64_t(n0) * wrow, int64_t(N - n0) * wrow);
+    const WBuf rwb = weight_rsrc(wq + int64_t(n0) * wrow, int64_t(N - n0) * wrow);
+    const __amdgpu_buffer_rsrc_t rw = rwb.r;
 
     const int b_col0 = kWaveN * wc + l32;            // this lane's B column in sub-tile 0
     const int a_lane = code_off(0, 32 * wr + l32, g); // fragment bases; blocks and sub-tiles
@@ -693,7 +723,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     WRegs<FMT> wr_;
     auto load_w = [&](int k) {
         if constexpr (FMT == FMT_Q8_0)
-            load_q8_0(rw, kb, k, tid, wr_.r);
+            load_q8_0(rw, rwb.shift, kb, k, tid, wr_.r);
         else if constexpr (FMT == FMT_Q4_K)
             load_q4_K(rw, K >> 8, k, tid, wr_.r);
         else
@@ -701,7 +731,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     };
     auto store_w = [&](int k, uint8_t *buf) {
         if constexpr (FMT == FMT_Q8_0)
-            store_q8_0(wr_.r, buf, tid);
+            store_q8_0(wr_.r, buf, rwb.shift, kb, k, tid);
         else
             store_kquant<FMT>(wr_.r, buf, k, tid);
     };
@@ -766,9 +796,21 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
         // alone and forms cs with one multiply (exact)
         using WsT = typename std::conditional<FMT == FMT_Q8_0, float2, float>::type;
         WsT fw[kRing];
+        // Blocks of this step that exist (Q8_0 with K % 128 != 0: the last
+        // step has 1-3).  A block past the row's end holds whatever the loads
+        // returned; its weight scale was staged as 0, so t = 0, and its
+        // activation scale is taken as 0 here, so the epilogue adds
+        // fma(0, 0, acc) = acc whatever those bytes were.
+        const int nvalid = kb - ks * KB;   // wave-uniform, >= KB except in that last step
         auto load_a = [&](int b) {
             fa[b & 1] = *reinterpret_cast<const i32x4 *>(buf + a_lane + b * kBlockBytes);
-            if constexpr (!DOTS) xsv[b & 1] = h2f(sHdr[(xs_row * KB + b) * 2]);
+            if constexpr (!DOTS) {
+                const float xs = h2f(sHdr[(xs_row * KB + b) * 2]);
+                if constexpr (FMT == FMT_Q8_0)
+                    xsv[b & 1] = (b == 0 || b < nvalid) ? xs : 0.0f;
+                else
+                    xsv[b & 1] = xs;
+            }
         };
         auto load_b = [&](int st) {
             const int b = st / kNSub, c = st % kNSub;
@@ -810,7 +852,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int m = m0 + 32 * wr + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (m < M && n < N)
+                    if (m < M && n < N && b < nvalid)
                         dots[(int64_t(m) * N + n) * kb + int64_t(ks) * KB + b] = D[r];
                 }
             } else {
@@ -999,31 +1041,39 @@ __device__ __forceinline__ WUnit mv_load_kquant(__amdgpu_buffer_rsrc_t rw, int u
     return r;
 }
 
-// Q8_0 unit from its 68 bytes (17 dwords) in LDS: block 0's scale in bytes
-// 0-1 and codes two bytes off the dword grid; block 1's scale in bytes 34-35
-// and codes on dwords 9..16.
-__device__ __forceinline__ WUnit mv_unit_q8_0(const uint32_t *src) {
+// One Q8_0 block from the 9 dwords at src, starting `off` (0 or 2) bytes in:
+// scale in the low or high half of dword 0, codes realigned by v_perm (bytes
+// 2..5 of each dword pair, or the upper dword whole).
+__device__ __forceinline__ float mv_block_q8_0(const uint32_t *src, int off, uint32_t *w) {
+    uint32_t v[9];
+#pragma unroll
+    for (int i = 0; i < 9; i++) v[i] = src[i];
+    const uint32_t sel = off ? 0x07060504u : 0x05040302u;
+#pragma unroll
+    for (int i = 0; i < 8; i++) w[i] = __builtin_amdgcn_perm(v[i + 1], v[i], sel);
+    return h2f(off ? v[0] >> 16 : v[0]);
+}
+
+// Q8_0 unit from LDS: its 68 bytes start `sh` bytes (0 or 2, the row's
+// offset from the dword grid) past src.  Block 0 is read from dwords 0..8 at
+// byte offset sh, block 1 from dwords 8 + sh/2 .. 16 + sh/2 at byte offset
+// 2 - sh.  `pair` false: the row's odd last block, alone in its unit (block
+// 1 gets scale 0 and is skipped by the caller).
+__device__ __forceinline__ WUnit mv_unit_q8_0(const uint32_t *src, int sh, bool pair) {
     WUnit r;
-    uint32_t v[17];
-#pragma unroll
-    for (int i = 0; i < 17; i++) v[i] = src[i];
-#pragma unroll
-    for (int i = 0; i < 8; i++) r.w0[i] = __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2);
-#pragma unroll
-    for (int i = 0; i < 8; i++) r.w1[i] = v[i + 9];
-    r.ws0 = h2f(v[0]);
-    r.ws1 = h2f(v[8] >> 16);
+    r.ws0 = mv_block_q8_0(src, sh, r.w0);
+    r.ws1 = mv_block_q8_0(src + 8 + (sh >> 1), 2 - sh, r.w1);
+    if (!pair) r.ws1 = 0.0f;
     r.dm0 = r.dm1 = 0.0f;
     return r;
 }
 
-// Unit u of RW weight rows against the matching q8_1 block pair of every
-// activation row: each pair is loaded once and serves all RW rows.  The
-// arithmetic of one (weight row, activation row) is the oracle's per-block
-// order: acc += xs * fl(ws * I), then (K-quants) acc -= dmin*m * s.
+// `pair` false (Q8_0 with an odd number of blocks, the row's last unit):
+// only block 0 exists; the activation pair's second block is the next row's
+// first (or zeros past the end) and is not added.
 template <int FMT, int MR, int RW>
 __device__ __forceinline__ void mv_unit_terms(__amdgpu_buffer_rsrc_t rx, int M, int kb, int u, const WUnit *wu,
-                                              float (*acc)[MR]) {
+                                              float (*acc)[MR], bool pair) {
 #pragma unroll
     for (int m = 0; m < MR; m++) {
         if (m < M) {
@@ -1035,7 +1085,7 @@ __device__ __forceinline__ void mv_unit_terms(__amdgpu_buffer_rsrc_t rx, int M, 
                 const float t1 = wu[r].ws1 * (float)dot8(wu[r].w1, x.c1);
                 acc[r][m] = __builtin_fmaf(xs0, t0, acc[r][m]);
                 if constexpr (FMT != FMT_Q8_0) acc[r][m] = __builtin_fmaf(-wu[r].dm0, h2f(x.h0 >> 16), acc[r][m]);
-                acc[r][m] = __builtin_fmaf(xs1, t1, acc[r][m]);
+                if (FMT != FMT_Q8_0 || pair) acc[r][m] = __builtin_fmaf(xs1, t1, acc[r][m]);
                 if constexpr (FMT != FMT_Q8_0) acc[r][m] = __builtin_fmaf(-wu[r].dm1, h2f(x.h1 >> 16), acc[r][m]);
             }
         }
@@ -1062,8 +1112,10 @@ __global__ __launch_bounds__(kMvThreads) void k_mmv(const uint8_t *__restrict__ 
     const int64_t wrow = weight_row_bytes(FMT, K);
     // row r of the wave: GEMM gi[r] of the set, its row n[r]; a row past the
     // last one reads through an empty buffer (zeros) and is not stored
+    // (a Q8_0 row starts 2 bytes off the dword grid when its first block
+    // index n*kb is odd: sh[r] = 2)
     __amdgpu_buffer_rsrc_t rw[RW];
-    int gi[RW], n[RW];
+    int gi[RW], n[RW], sh[RW];
 #pragma unroll
     for (int r = 0; r < RW; r++) {
         const int row = row0 + r;
@@ -1072,10 +1124,14 @@ __global__ __launch_bounds__(kMvThreads) void k_mmv(const uint8_t *__restrict__ 
             if (row >= set.tile_start[i]) g = i;
         gi[r] = g;
         n[r] = row - set.tile_start[g];
-        rw[r] = tile_rsrc(set.w[g] + int64_t(n[r]) * wrow, row < total ? wrow : 0);
+        const WBuf b = weight_rsrc(set.w[g] + int64_t(n[r]) * wrow, row < total ? wrow : 0);
+        rw[r] = b.r;
+        sh[r] = b.shift;
     }
     const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq, int64_t(M) * kb * 36);
-    const int units = kb >> 1;   // block pairs (Q8_0) / sub-block pairs (K-quants) in a row
+    // block pairs (Q8_0) / sub-block pairs (K-quants) in a row; a Q8_0 row of
+    // an odd number of blocks ends with a unit of one block
+    const int units = (kb + 1) >> 1;
 
     float acc[RW][MR];
 #pragma unroll
@@ -1091,19 +1147,21 @@ __global__ __launch_bounds__(kMvThreads) void k_mmv(const uint8_t *__restrict__ 
     // 16-byte header and 32 code bytes, both 16-byte aligned) load straight:
     // the staged form was 10-13 % slower there.
     constexpr int kQ8Chunk = 64 * 68;
+    constexpr int kQ8Pieces = kQ8Chunk / 16 + 1;   // one more for a row 2 bytes off the grid
     for (int u0 = 0; u0 < units; u0 += 64) {
         const int u = u0 + lane;
+        const bool pair = 2 * u + 1 < kb;
         WUnit wu[RW];
         if constexpr (FMT == FMT_Q8_0) {
-            __shared__ __attribute__((aligned(16))) uint8_t stage[kMvWaves][kQ8Chunk];
+            __shared__ __attribute__((aligned(16))) uint8_t stage[kMvWaves][kQ8Pieces * 16];
             uint8_t *my = stage[wave];
 #pragma unroll
             for (int r = 0; r < RW; r++) {
                 // pieces past the row end read as zero
 #pragma unroll
-                for (int i = 0; i < (kQ8Chunk / 16 + 63) / 64; i++) {
+                for (int i = 0; i < (kQ8Pieces + 63) / 64; i++) {
                     const int piece = lane + 64 * i;
-                    if (piece < kQ8Chunk / 16)
+                    if (piece < kQ8Pieces)
                         *reinterpret_cast<u32x4 *>(my + 16 * piece) =
                             __builtin_amdgcn_raw_buffer_load_b128(rw[r], u0 * 68 + 16 * piece, 0, 0);
                 }
@@ -1112,14 +1170,14 @@ __global__ __launch_bounds__(kMvThreads) void k_mmv(const uint8_t *__restrict__ 
                 // moving the unit reads above the other lanes' piece writes
                 // (or the next row's writes above these reads)
                 __builtin_amdgcn_wave_barrier();
-                if (u < units) wu[r] = mv_unit_q8_0(reinterpret_cast<const uint32_t *>(my + 68 * lane));
+                if (u < units) wu[r] = mv_unit_q8_0(reinterpret_cast<const uint32_t *>(my + 68 * lane), sh[r], pair);
                 __builtin_amdgcn_wave_barrier();
             }
         } else if (u < units) {
 #pragma unroll
             for (int r = 0; r < RW; r++) wu[r] = mv_load_kquant<FMT>(rw[r], u);
         }
-        if (u < units) mv_unit_terms<FMT, MR, RW>(rx, M, kb, u, wu, acc);
+        if (u < units) mv_unit_terms<FMT, MR, RW>(rx, M, kb, u, wu, acc, pair);
     }
 #pragma unroll
     for (int r = 0; r < RW; r++) {
@@ -1294,6 +1352,27 @@ static hipError_t launch_mv(const Plan &p, const GemmSet &set, const uint8_t *xb
     else
         go(std::integral_constant<int, 8>{});
     return hipGetLastError();
+}
+
+// The kernel a plan launches (the same choice as launch_gemm / launch_moe
+// below), for the capacity guard's attribute query.
+const void *plan_kernel(const Plan &p, bool dots, bool moe) {
+    auto pick = [&](auto fmt) -> const void * {
+        constexpr int F = decltype(fmt)::value;
+        if (p.kernel == KERNEL_MV) {
+            if (p.tile_m == 1) return reinterpret_cast<const void *>(&k_mmv<F, 1>);
+            if (p.tile_m == 2) return reinterpret_cast<const void *>(&k_mmv<F, 2>);
+            if (p.tile_m <= 4) return reinterpret_cast<const void *>(&k_mmv<F, 4>);
+            return reinterpret_cast<const void *>(&k_mmv<F, 8>);
+        }
+        if (moe) return reinterpret_cast<const void *>(&k_mmq<F, false, true, true>);
+        if (dots) return reinterpret_cast<const void *>(&k_mmq<F, true, false, false>);
+        if (F == FMT_Q8_0 || p.skip_idle_waves) return reinterpret_cast<const void *>(&k_mmq<F, false, false, true>);
+        return reinterpret_cast<const void *>(&k_mmq<F, false, false, (F == FMT_Q8_0)>);
+    };
+    if (p.fmt == FMT_Q8_0) return pick(std::integral_constant<int, FMT_Q8_0>{});
+    if (p.fmt == FMT_Q4_K) return pick(std::integral_constant<int, FMT_Q4_K>{});
+    return pick(std::integral_constant<int, FMT_Q5_K>{});
 }
 
 hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const void *x, const void *const *w,

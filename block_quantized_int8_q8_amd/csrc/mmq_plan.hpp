@@ -26,7 +26,10 @@ constexpr int kTileM = 128;        // output rows per workgroup
 constexpr int kTileN = 128;        // output columns per workgroup
 constexpr int kThreads = 512;      // eight wave64s, a 4 x 2 grid of 32 x 64 wave tiles
 constexpr int kBlocksPerStage = 4; // 32-blocks staged per k-step (half a Q4_K super-block)
-constexpr int kWgPerCu = 2;        // workgroups resident per CU (LDS and VGPR budget)
+// Workgroups resident per CU are derived from the launched kernel's own
+// register and LDS use (kernel_wg_per_cu below); the kernels are built for
+// two (at most 128 VGPRs, four waves per SIMD).
+constexpr int kBuiltVgprs = 128;
 // Split-K policy, measured on the 7B layer shapes: split only when the output
 // tiles fill at most half of the resident workgroup slots, and then into
 // about one workgroup per CU (more slices cost more in fp32 atomics than
@@ -68,6 +71,34 @@ constexpr int kMvWaves = kMvThreads / 64;
 // one (fewer resident waves), and at M = 3-4 two rows gained nothing.
 constexpr int mv_rows_per_wave(int64_t M) { return M >= 5 ? 2 : 1; }
 
+// gfx950 register file: 512 registers per lane per SIMD (arch and
+// accumulation VGPRs together), allocated in granules of 8; at most 8 waves
+// per SIMD; 4 SIMDs per CU.
+constexpr int kRegsPerSimdLane = 512, kVgprGranule = 8, kMaxWavesPerSimd = 8, kSimdsPerCu = 4;
+
+// What the capacity guard needs to know of the kernel a plan launches (read
+// from the device with hipFuncGetAttributes; a pure-host caller passes it).
+struct KernelFit {
+    int vgprs = kBuiltVgprs;     // registers per lane
+    int64_t scratch = 0;         // private (scratch) bytes per lane: register spills
+};
+
+// Workgroups of `threads` threads using `vgprs` registers per lane and
+// `lds` bytes of LDS that fit one CU at once (0: none fits).
+inline int kernel_wg_per_cu(int vgprs, int64_t lds, int64_t lds_per_cu, int threads) {
+    const int waves = (threads + 63) / 64;
+    const int per_simd = (waves + kSimdsPerCu - 1) / kSimdsPerCu;
+    const int regs = ((vgprs < 1 ? 1 : vgprs) + kVgprGranule - 1) / kVgprGranule * kVgprGranule;
+    int waves_per_simd = kRegsPerSimdLane / regs;
+    if (waves_per_simd > kMaxWavesPerSimd) waves_per_simd = kMaxWavesPerSimd;
+    int wg = waves_per_simd / per_simd;
+    if (lds > 0) {
+        const int64_t by_lds = lds_per_cu / lds;
+        if (by_lds < wg) wg = int(by_lds);
+    }
+    return wg;
+}
+
 struct Plan {
     int fmt = 0;
     int kernel = KERNEL_MMQ;
@@ -85,6 +116,8 @@ struct Plan {
     // with 1-3 of 4 wave rows idle, a small loss with 1 of 8).
     bool skip_idle_waves = false;
     int mv_rows_per_wave = 0;   // matvec kernel: output rows per wave
+    int wg_per_cu = 0;          // workgroups of the launched kernel resident per CU
+    int kernel_vgprs = 0;       // its registers per lane
 };
 constexpr int kSkipShare = 4;   // K-quants skip when idle wave rows >= 1/kSkipShare of all
 
@@ -101,18 +134,45 @@ inline const char *check_quantize_shape(int64_t M, int64_t K) {
     return nullptr;
 }
 
-// Build the GEMM plan or explain the refusal.  `extra_lds` is the test hook.
+// Build the GEMM plan or explain the refusal.  `extra_lds` is the test hook;
+// `fit` describes the kernel the plan launches (registers, scratch), and
+// `lds_limit` is both the per-workgroup LDS limit and the CU's LDS (the same
+// 160 KiB on gfx950).  A kernel that spills to scratch is refused (the
+// kernels are built to need none, so a spill means a build that misses its
+// register budget), and the resident workgroups per CU that split-K plans
+// with come from the kernel's own registers and LDS.
 inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limit, int cu_count,
-                      int64_t extra_lds, Plan *p, char *why, size_t why_len, bool allow_mv = true) {
+                      int64_t extra_lds, Plan *p, char *why, size_t why_len, bool allow_mv = true,
+                      const KernelFit &fit = KernelFit()) {
     auto fail = [&](const char *msg) {
         if (why && why_len) std::snprintf(why, why_len, "%s", msg);
         return false;
     };
+    auto check_fit = [&](Plan &q) {
+        q.kernel_vgprs = fit.vgprs;
+        q.wg_per_cu = kernel_wg_per_cu(fit.vgprs, q.lds_bytes, lds_limit, q.threads);
+        if (fit.scratch > 0) {
+            if (why && why_len)
+                std::snprintf(why, why_len, "the %s kernel uses %lld B of scratch per lane (register spills): refused",
+                              q.kernel == KERNEL_MV ? "matvec" : "GEMM", (long long)fit.scratch);
+            return false;
+        }
+        if (q.wg_per_cu < 1) {
+            if (why && why_len)
+                std::snprintf(why, why_len, "no workgroup of the kernel fits a CU (%d VGPRs per lane, %lld B of LDS): refused",
+                              fit.vgprs, (long long)q.lds_bytes);
+            return false;
+        }
+        return true;
+    };
     if (!fmt_ok(fmt)) return fail("unknown weight format");
     if (M < 1 || N < 1 || K < 1) return fail("M, N and K must be >= 1");
-    if (K % 256 != 0)
+    // Q8_0: any whole number of 32-blocks (the last k-step of the tile kernel
+    // may hold fewer than kBlocksPerStage of them); K-quants: whole 256-value
+    // super-blocks
+    if (fmt == FMT_Q8_0 ? K % 32 != 0 : K % 256 != 0)
         return fail(fmt != FMT_Q8_0 ? "K must be a multiple of 256 (whole K-quant super-blocks)"
-                                    : "K must be a multiple of 256 (whole 8-block k-steps)");
+                                    : "K must be a multiple of 32 (whole Q8_0 blocks)");
     if (M > INT32_MAX || N > INT32_MAX) return fail("M and N must fit in int32");
     // byte offsets inside one 128-row tile are 32-bit buffer offsets
     if (K > (int64_t(1) << 23)) return fail("K must be at most 8388608 (32-bit offsets within a tile)");
@@ -133,24 +193,33 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
         q.grid_x = (N + rows_per_wg - 1) / rows_per_wg;
         q.mv_rows_per_wave = mv_rows_per_wave(M);
         q.grid_y = 1;
-        q.k_steps = K / 64;
+        q.k_steps = (K / 32 + 1) / 2;   // block pairs per row (an odd last block is a unit of its own)
         q.steps_per_split = q.k_steps;
         if (q.grid_x > INT32_MAX) return fail("too many output rows");
         if (q.lds_bytes > lds_limit) return fail("plan needs more LDS per workgroup than the device allows: refused");
+        if (!check_fit(q)) return false;
         *p = q;
         return true;
     }
     q.lds_bytes = lds_bytes_for(fmt) + extra_lds;
     q.grid_x = (N + kTileN - 1) / kTileN;
     q.grid_y = (M + kTileM - 1) / kTileM;
-    q.k_steps = K / (32 * kBlocksPerStage);
+    q.k_steps = (K / 32 + kBlocksPerStage - 1) / kBlocksPerStage;   // the last one may be partial (Q8_0)
     if (q.grid_y > 65535) return fail("too many row tiles for the launch grid (M too large)");
     // Too few output tiles to occupy the device (at most half of the
     // resident workgroup slots): split K into slices of at least
     // kMinStepsPerSplit k-steps, about one workgroup per CU in all, or into
     // up to two per CU when the slices still keep kMinStepsPerSplit2.
     q.steps_per_split = q.k_steps;
-    const int64_t tiles = q.grid_x * q.grid_y, slots = int64_t(kWgPerCu) * cu_count;
+    if (q.lds_bytes > lds_limit) {
+        if (why && why_len)
+            std::snprintf(why, why_len,
+                          "plan needs %lld B of LDS per workgroup, device allows %lld B: refused",
+                          (long long)q.lds_bytes, (long long)lds_limit);
+        return false;
+    }
+    if (!check_fit(q)) return false;
+    const int64_t tiles = q.grid_x * q.grid_y, slots = int64_t(q.wg_per_cu) * cu_count;
     if (tiles * kSplitBelow <= slots) {
         // about one workgroup per CU, slices of at least kMinStepsPerSplit ...
         int64_t s = (int64_t(kSplitSlots) * cu_count + tiles - 1) / tiles;
@@ -172,13 +241,6 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
         q.skip_idle_waves = fmt == FMT_Q8_0 || idle_wave_rows * 32 * kSkipShare >= rows;
     }
     if (q.grid_x > INT32_MAX) return fail("too many column tiles");
-    if (q.lds_bytes > lds_limit) {
-        if (why && why_len)
-            std::snprintf(why, why_len,
-                          "plan needs %lld B of LDS per workgroup, device allows %lld B: refused",
-                          (long long)q.lds_bytes, (long long)lds_limit);
-        return false;
-    }
     *p = q;
     return true;
 }
@@ -191,7 +253,7 @@ constexpr int kMaxGemms = 8;
 
 inline bool make_plan_multi(int fmt, int64_t M, int count, const int64_t *Ns, int64_t K, int64_t lds_limit,
                             int cu_count, int64_t extra_lds, Plan *p, int *tile_start, char *why,
-                            size_t why_len, bool allow_mv = true) {
+                            size_t why_len, bool allow_mv = true, const KernelFit &fit = KernelFit()) {
     auto fail = [&](const char *msg) {
         if (why && why_len) std::snprintf(why, why_len, "%s", msg);
         return false;
@@ -203,7 +265,7 @@ inline bool make_plan_multi(int fmt, int64_t M, int count, const int64_t *Ns, in
     int64_t tiles = 0;
     for (int g = 0; g < count; g++) {
         Plan one;
-        if (!make_plan(fmt, M, Ns[g], K, lds_limit, cu_count, extra_lds, &one, why, why_len, allow_mv))
+        if (!make_plan(fmt, M, Ns[g], K, lds_limit, cu_count, extra_lds, &one, why, why_len, allow_mv, fit))
             return false;
         tile_start[g] = int(tiles);
         tiles += mv ? Ns[g] : one.grid_x;
@@ -211,7 +273,7 @@ inline bool make_plan_multi(int fmt, int64_t M, int count, const int64_t *Ns, in
     }
     tile_start[count] = int(tiles);
     return make_plan(fmt, M, mv ? tiles : tiles * kTileN, K, lds_limit, cu_count, extra_lds, p, why, why_len,
-                     allow_mv);
+                     allow_mv, fit);
 }
 
 // Indexed MoE ("When Does a Kernel Win Surface?", section 4.5, the fused
@@ -240,7 +302,8 @@ inline int64_t moe_workspace_bytes(int64_t R, int64_t E) {
 }
 
 inline bool make_plan_moe(int fmt, int64_t T, int topk, int n_experts, int64_t N, int64_t K, int64_t lds_limit,
-                          int cu_count, int64_t extra_lds, Plan *p, char *why, size_t why_len) {
+                          int cu_count, int64_t extra_lds, Plan *p, char *why, size_t why_len,
+                          const KernelFit &fit = KernelFit()) {
     auto fail = [&](const char *msg) {
         if (why && why_len) std::snprintf(why, why_len, "%s", msg);
         return false;
@@ -250,7 +313,7 @@ inline bool make_plan_moe(int fmt, int64_t T, int topk, int n_experts, int64_t N
     if (T < 1) return fail("T (tokens) must be >= 1");
     if (T > INT32_MAX / topk) return fail("T * topk (routed rows) must fit in int32");
     Plan q;
-    if (!make_plan(fmt, T, N, K, lds_limit, cu_count, extra_lds, &q, why, why_len, false)) return false;
+    if (!make_plan(fmt, T, N, K, lds_limit, cu_count, extra_lds, &q, why, why_len, false, fit)) return false;
     // the gathered activation rows are addressed by 32-bit byte offsets
     // from the start of x
     if (T * (K / 32) * 36 > int64_t(0x7fffffff)) return fail("activations must be under 2 GiB (32-bit offsets)");
@@ -266,11 +329,12 @@ inline bool make_plan_moe(int fmt, int64_t T, int topk, int n_experts, int64_t N
 inline void describe(const Plan &p, char *buf, size_t len) {
     std::snprintf(buf, len,
                   "kernel=%s fmt=%s tile=%dx%d threads=%d blocks_per_stage=%d lds=%lld grid=%lldx%lld "
-                  "k_steps=%lld split_k=%lld steps_per_split=%lld skip_idle_waves=%d mv_rows_per_wave=%d",
+                  "k_steps=%lld split_k=%lld steps_per_split=%lld skip_idle_waves=%d mv_rows_per_wave=%d "
+                  "wg_per_cu=%d vgprs=%d",
                   p.kernel == KERNEL_MV ? "mv" : "mmq", fmt_name(p.fmt), p.tile_m, p.tile_n, p.threads, p.blocks_per_stage,
                   (long long)p.lds_bytes, (long long)p.grid_x, (long long)p.grid_y,
                   (long long)p.k_steps, (long long)p.split_k, (long long)p.steps_per_split, int(p.skip_idle_waves),
-                  p.mv_rows_per_wave);
+                  p.mv_rows_per_wave, p.wg_per_cu, p.kernel_vgprs);
 }
 
 }  // namespace mmq

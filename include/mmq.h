@@ -173,12 +173,15 @@ int mmq_moe_gemm(int fmt, const void *x_q8_1, const void *w, int n_experts, cons
  * same routed rows, e.g. the down projection after gate/up, whose input has
  * one row per routed row (pass T' = T*topk, topk' = 1: routed row r is then
  * input row r, grouped into the same expert tiles).  Arguments as for
- * mmq_moe_gemm.  The tables are used only if their header records the same
- * number of routed rows (T*topk) and n_experts; otherwise nothing is
- * computed and `out` is left as it was (a workspace never routed, or routed
- * for other rows, writes nothing).  Tables routed for other ids of the same
- * sizes are used as they are: keeping the ids and the workspace together is
- * the caller's part. */
+ * mmq_moe_gemm.  Refused (nothing launched) unless the last mmq_moe_gemm
+ * call of this process that was given this workspace on the current device
+ * routed the same number of routed rows (T*topk) and n_experts; the library
+ * remembers the last 1024 workspaces it routed.  As a second guard the GEMM
+ * kernel uses the tables only if the header the routing kernel wrote
+ * records the same sizes, so a workspace the caller overwrote after routing
+ * computes nothing and leaves `out` as it was.  Tables routed for other ids
+ * of the same sizes are used as they are: keeping the ids and the workspace
+ * together is the caller's part. */
 int mmq_moe_gemm_routed(int fmt, const void *x_q8_1, const void *w, int n_experts, int topk, float *out,
                         int64_t T, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes, void *stream);
 
@@ -197,15 +200,26 @@ const char *mmq_last_error(void);
  * matrix-vector kernel, tile, LDS bytes, grid, split-K, skip_idle_waves:
  * whether waves whose 32 rows all lie past M skip their MFMAs, and
  * mv_rows_per_wave: the matrix-vector kernel's output rows per wave, 0 for
- * the tiled kernel) into buf
- * (NUL-terminated).  Returns 1 if the plan
+ * the tiled kernel; wg_per_cu and vgprs: the launched kernel's resident
+ * workgroups per CU and registers per lane, read from the device with
+ * hipFuncGetAttributes) into buf (NUL-terminated).  Returns 1 if the plan
  * would launch, 0 if it would be refused (reason in buf). */
 int mmq_plan_describe(int fmt, int64_t M, int64_t N, int64_t K, char *buf, int64_t len);
 
-/* Pure host planning with explicit device limits, so that the guard can be
- * checked without a GPU.  Same return convention as mmq_plan_describe. */
+/* Pure host planning with explicit device limits and kernel attributes, so
+ * that the guard can be checked without a GPU ("13 . r7-r8 raw-byte MMQ
+ * kernel", sections 3.3 and 6: every capacity a launch depends on is checked
+ * before it).  lds_limit_bytes: the per-workgroup LDS limit, taken as the
+ * CU's LDS as well (both 160 KiB on gfx950).  kernel_vgprs: registers per
+ * lane of the kernel the plan launches (<= 0: the 128 the kernels are built
+ * for); kernel_scratch_bytes: its scratch bytes per lane.  On a device the
+ * library reads both with hipFuncGetAttributes before planning: the
+ * workgroups resident per CU (reported as wg_per_cu, and used by the split-K
+ * decision) follow from them and the plan's LDS, and a kernel that needs
+ * scratch (a register spill) or fits no workgroup per CU is refused.  Same
+ * return convention as mmq_plan_describe. */
 int mmq_plan_for_limits(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limit_bytes,
-                        int cu_count, char *buf, int64_t len);
+                        int cu_count, int kernel_vgprs, int64_t kernel_scratch_bytes, char *buf, int64_t len);
 
 /* Test hook: add `extra_bytes` to the LDS every GEMM plan requests from now
  * on (0 restores normal plans).  Used to check that an over-capacity plan is

@@ -62,6 +62,17 @@ def _check(fmt, got, ref):
     (700, 3, 1, 384, 256, 0.0),     # topk 1: plain row gather
 ])
 def test_moe_matches_oracle(fmt, T, E, topk, N, K, skew):
+    _moe_case(fmt, T, E, topk, N, K, skew)
+
+
+@pytest.mark.parametrize("T,E,topk,N,K", [(37, 5, 3, 201, 288), (150, 4, 2, 131, 3616)])
+def test_moe_q8_0_any_whole_blocks(T, E, topk, N, K):
+    """Q8_0 with K/32 odd and N odd: every other expert's matrix starts 2
+    bytes off the dword grid, and the last k-step holds fewer than 4 blocks."""
+    _moe_case(mmq.FMT_Q8_0, T, E, topk, N, K, 0.0)
+
+
+def _moe_case(fmt, T, E, topk, N, K, skew):
     _say(f"moe fmt={fmt} T={T} E={E} topk={topk} N={N} K={K} skew={skew}")
     xq = oracle.quantize_q8_1(inputs.activations(T, K, 50 + T))
     w = _weights(fmt, E, N, K, 60 + N)
@@ -178,25 +189,35 @@ def test_moe_routed_reuse_for_down_projection(fmt):
     _check(fmt, got, oracle.moe_gemm(fmt, x2, w2, ids.reshape(-1, 1), 1, T * topk, N2, K2, E, nthreads=16))
 
 
-def test_moe_routed_without_matching_tables_writes_nothing():
+def test_moe_routed_without_matching_tables_is_refused():
+    """A routed call on a workspace that holds no routing of its sizes is
+    refused on the host (nothing launched); a workspace whose tables the
+    caller overwrote after routing passes that check but computes nothing
+    (the kernel checks the header the routing kernel wrote)."""
     fmt, T, E, topk, N, K = mmq.FMT_Q8_0, 64, 4, 2, 128, 256
     _say("moe routed: no matching tables")
     xq = _dev(oracle.quantize_q8_1(inputs.activations(T, K, 170)))
     w = _dev(_weights(fmt, E, N, K, 171))
     ws = torch.zeros((mmq.moe_workspace_bytes(T, topk, E) + 256,), dtype=torch.uint8, device=DEV)
     out = torch.full((T * topk, N), float("nan"), dtype=torch.float32, device=DEV)
-    mmq.moe_gemm_routed(fmt, xq, w, E, topk, T, N, K, ws, out)      # never routed
-    torch.cuda.synchronize()
-    assert torch.isnan(out).all()
+    with pytest.raises(mmq.MMQError, match="no routing"):
+        mmq.moe_gemm_routed(fmt, xq, w, E, topk, T, N, K, ws, out)      # never routed
     ids = _dev(inputs.moe_ids(T, E, topk, 172))
     mmq.moe_gemm(fmt, xq, w, E, ids, topk, T, N, K, out, workspace=ws)  # routed for 128 rows, 4 experts
     out2 = torch.full((T * topk // 2, N), float("nan"), dtype=torch.float32, device=DEV)
-    mmq.moe_gemm_routed(fmt, xq, w, E, 1, T, N, K, ws, out2)          # 64 routed rows: no match
+    with pytest.raises(mmq.MMQError, match="routed for 128 rows"):
+        mmq.moe_gemm_routed(fmt, xq, w, E, 1, T, N, K, ws, out2)      # 64 routed rows
     out3 = torch.full((T * topk, N), float("nan"), dtype=torch.float32, device=DEV)
-    mmq.moe_gemm_routed(fmt, xq, w, E + 1, topk, T, N, K, ws, out3)   # 5 experts: no match
+    with pytest.raises(mmq.MMQError, match="routed for 128 rows"):
+        mmq.moe_gemm_routed(fmt, xq, w, E + 1, topk, T, N, K, ws, out3)   # 5 experts
     torch.cuda.synchronize()
     assert torch.isnan(out2).all() and torch.isnan(out3).all()
     assert not torch.isnan(out).any()
+    ws.zero_()                                                           # the header is gone
+    out4 = torch.full((T * topk, N), float("nan"), dtype=torch.float32, device=DEV)
+    mmq.moe_gemm_routed(fmt, xq, w, E, topk, T, N, K, ws, out4)
+    torch.cuda.synchronize()
+    assert torch.isnan(out4).all()
 
 
 @pytest.mark.parametrize("fmt,T,E,topk", [(mmq.FMT_Q8_0, 300, 2048, 1),   # the most experts: most of them empty

@@ -225,16 +225,11 @@ def test_gemm_on_random_q8_1_fields(fmt):
 def test_gemm_hand_cases():
     _say("gemm hand cases")
     x, w, K, expect = golden_cases.gemm_q8_0_case()
-    # the kernel takes whole 8-block k-steps: pad with all-zero blocks, which
-    # quantize to d = 0 and add exactly +0
-    xp = np.zeros((1, 256), np.float32)
-    xp[:, :K] = x
-    wp = np.zeros((1, 8, 34), np.uint8)
-    wp[:, :K // 32] = w
-    xq = _gpu_quantize(xp)
-    assert _run_gemm(mmq.FMT_Q8_0, xq, wp, 1, 1, 256)[0, 0] == expect
-    xp9 = np.repeat(xp, 9, axis=0)   # the tiled kernel (M > 8) as well
-    assert (_run_gemm(mmq.FMT_Q8_0, _gpu_quantize(xp9), wp, 9, 1, 256)[:, 0] == expect).all()
+    # K = 64: two blocks, half a k-step of the tile kernel
+    xq = _gpu_quantize(x)
+    assert _run_gemm(mmq.FMT_Q8_0, xq, w, 1, 1, K)[0, 0] == expect
+    x9 = np.repeat(x, 9, axis=0)   # the tiled kernel (M > 8) as well
+    assert (_run_gemm(mmq.FMT_Q8_0, _gpu_quantize(x9), w, 9, 1, K)[:, 0] == expect).all()
     x, w, K, expect = golden_cases.gemm_q4_K_case()
     xq = _gpu_quantize(x)
     assert _run_gemm(mmq.FMT_Q4_K, xq, w, 1, 1, K)[0, 0] == expect
@@ -249,10 +244,11 @@ def test_gemm_hand_cases():
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_full_size_configs_sampled_rows(cfg):
+def test_full_size_configs_full_output(cfg):
     """Benchmark shapes, full launch: GPU quantize then GPU GEMM on device
-    (the benchmarked path); the oracle checks the quantized bytes in full and
-    the output on sampled rows (first, last, last row tile, random)."""
+    (the benchmarked path); the oracle checks the quantized bytes and every
+    output element ("13 . r7-r8 raw-byte MMQ kernel", section 4: every cell
+    against the host reference)."""
     fmt_name, M, N, K = inputs.CONFIGS[cfg]
     fmt = mmq.FMT_Q8_0 if fmt_name == "q8_0" else mmq.FMT_Q4_K
     _say(f"full config {cfg}: {fmt_name} M={M} N={N} K={K}")
@@ -265,14 +261,15 @@ def test_full_size_configs_sampled_rows(cfg):
     torch.cuda.synchronize()
     xq = oracle.quantize_q8_1(x)
     assert np.array_equal(xq_dev.cpu().numpy(), xq)
+    del xq_dev, xd
     o = out.cpu().numpy()
+    del out
     assert not np.isnan(o).any()
-    rows = sorted(set([0, 1, M - 1, M - 128, M // 2] + list(np.random.default_rng(cfg).integers(0, M, 6))))
-    sub = np.ascontiguousarray(xq[rows])
-    ref = _oracle_gemm(fmt, sub, w, len(rows), N, K)
-    rep = metrics.report(o[rows], ref)
+    rep = metrics.report(o, _oracle_gemm(fmt, xq, w, M, N, K))
     _say(rep)
     assert rep["normalized_max_error"] <= metrics.TOL
+    if fmt == mmq.FMT_Q8_0:
+        assert rep["bit_identical_fraction"] == 1.0
 
 
 def test_q5_K_full_size_sampled_rows():
@@ -296,10 +293,12 @@ def test_q5_K_full_size_sampled_rows():
 
 
 @pytest.mark.parametrize("M", inputs.LAYER_M)
-def test_layer_gemm_set_sampled_rows(M):
-    """The seven Q4_K projection GEMMs of one 7B layer at M tokens, with one
-    GPU quantize pass per distinct input: the q8_1 bytes in full, and every
-    output on sampled rows (first, last, last row tile, random)."""
+def test_layer_gemm_set(M):
+    """The seven Q4_K projection GEMMs of one 7B layer at M tokens, run as
+    the benchmark runs them: one GPU quantize pass per distinct input and one
+    mmq_gemm_multi launch per input group (q+k+v, o, gate+up, down).  The
+    q8_1 bytes in full; every output element at M <= 2048, sampled rows
+    (first, last, last row tile, random) at M = 8192."""
     shapes = {g: (n, k) for g, n, k in inputs.LAYER_7B}
     for name, K, gemms in inputs.LAYER_INPUTS:
         _say(f"layer M={M}: input {name} K={K}")
@@ -309,23 +308,25 @@ def test_layer_gemm_set_sampled_rows(M):
         xq = oracle.quantize_q8_1(x)
         assert np.array_equal(xq_dev.cpu().numpy(), xq)
         del x
-        rows = sorted(set([0, M - 1, M - 128, M // 2] + list(np.random.default_rng(M).integers(0, M, 4))))
-        sub = np.ascontiguousarray(xq[rows])
-        for g in gemms:
-            N, Kg = shapes[g]
-            assert Kg == K
-            _say(f"layer M={M}: gemm {g} N={N} K={K}")
-            w = inputs.q4_K_weights(N, K, inputs.layer_weight_seed(g))
-            out = _nan_out(M, N)
-            mmq.gemm_q4_K(xq_dev, _to_dev(w), M, N, K, out)
-            torch.cuda.synchronize()
+        if M <= 2048:
+            rows = list(range(M))
+        else:
+            rows = sorted(set([0, M - 1, M - 128, M // 2] + list(np.random.default_rng(M).integers(0, M, 4))))
+        sub = xq if len(rows) == M else np.ascontiguousarray(xq[rows])
+        ws = [inputs.q4_K_weights(shapes[g][0], K, inputs.layer_weight_seed(g)) for g in gemms]
+        Ns = [shapes[g][0] for g in gemms]
+        assert all(shapes[g][1] == K for g in gemms)
+        outs = [_nan_out(M, n) for n in Ns]
+        _say(f"layer M={M}: gemm set {'+'.join(gemms)} N={Ns} K={K}")
+        mmq.gemm_multi(mmq.FMT_Q4_K, xq_dev, [_to_dev(w) for w in ws], Ns, M, K, outs)
+        torch.cuda.synchronize()
+        for g, n, w, out in zip(gemms, Ns, ws, outs):
             o = out.cpu().numpy()
-            del out
-            assert not np.isnan(o).any()
-            rep = metrics.report(o[rows], oracle.gemm_q4_K(sub, w, len(rows), N, K))
-            _say(rep)
+            assert not np.isnan(o).any(), f"{g}: output element left unwritten"
+            rep = metrics.report(o[rows] if len(rows) < M else o, oracle.gemm_q4_K(sub, w, len(rows), n, K, nthreads=16))
+            _say(g, rep)
             assert rep["normalized_max_error"] <= metrics.TOL
-        del xq_dev
+        del xq_dev, outs
         torch.cuda.empty_cache()
 
 
@@ -495,8 +496,10 @@ def test_refusals_leave_output_untouched():
             mmq.debug_block_dots(mmq.FMT_Q8_0, xq, w, M, N, K)
     finally:
         mmq.set_extra_lds(0)
+    with pytest.raises(mmq.MMQError, match="multiple of 32"):
+        mmq.gemm_q8_0(xq, w, M, N, K - 16, out)
     with pytest.raises(mmq.MMQError, match="multiple of 256"):
-        mmq.gemm_q8_0(xq, w, M, N, K - 32, out)
+        mmq.gemm_q4_K(xq, w, M, N // 4, K - 32, out)
     with pytest.raises(mmq.MMQError, match="aligned"):
         mmq.gemm_q8_0(xq.view(-1)[4:4 + 36 * M * 15].view(M, 15, 36), w, M, N, 480 + 0 * K, out)
     with pytest.raises(mmq.MMQError, match=">= 1"):
@@ -507,6 +510,22 @@ def test_refusals_leave_output_untouched():
     mmq.gemm_q8_0(xq, w, M, N, K, out)
     torch.cuda.synchronize()
     assert not torch.isnan(out).any()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_device_plans_read_the_kernels_attributes(fmt):
+    """On the device the guard reads each launched kernel's registers and
+    scratch (hipFuncGetAttributes) before planning: the tile kernels fit two
+    workgroups per CU (<= 128 VGPRs, no scratch, or they would be refused),
+    the matvec kernels at least one."""
+    import re
+    for M, N, K, kern in [(2048, 3584, 3584, "mmq"), (2048, 18944, 3584, "mmq"), (96, 300, 512, "mmq"),
+                          (1, 3584, 3584, "mv"), (8, 4608, 3584, "mv")]:
+        ok, desc = mmq.plan_describe(fmt, M, N, K)
+        _say(desc)
+        assert ok and f"kernel={kern}" in desc, desc
+        wg, vg = (int(v) for v in re.search(r"wg_per_cu=(\d+) vgprs=(\d+)", desc).groups())
+        assert vg > 0 and (wg == 2 and vg <= 128 if kern == "mmq" else wg >= 1), desc
 
 
 def test_quantize_refusals():
@@ -596,3 +615,77 @@ def test_two_host_threads_two_streams():
         t.join()
     torch.cuda.synchronize()
     assert not errors, errors
+
+
+# ------------------------------------------------------- Q8_0 at any whole number of 32-blocks
+#
+# "When the Product Won't Collapse" (section 2) sums over 32-element blocks,
+# so Q8_0 takes any K % 32 == 0.  With K/32 odd, every other weight row (and
+# every other MoE expert matrix) starts 2 bytes off the dword grid, and the
+# tile kernel's last k-step holds 1-3 blocks.
+
+ODD_K = [32, 96, 288, 3616]
+
+
+@pytest.mark.parametrize("K", ODD_K)
+@pytest.mark.parametrize("M,N", [(33, 65), (200, 301)])
+def test_q8_0_block_dots_any_whole_blocks(M, N, K):
+    _say(f"q8_0 dots any K: M={M} N={N} K={K}")
+    x = inputs.q8_1_blocks(M, K, 200 + M)
+    w = inputs.q8_0_weights(N, K, 210 + N)
+    dots = torch.full((M, N, K // 32), -(2 ** 31), dtype=torch.int32, device=DEV)
+    mmq.debug_block_dots(mmq.FMT_Q8_0, _to_dev(x), _to_dev(w), M, N, K, dots)
+    torch.cuda.synchronize()
+    assert np.array_equal(dots.cpu().numpy(), oracle.block_dots_q8_0(x, w, M, N, K))
+
+
+@pytest.mark.parametrize("K", [96, 288, 3616])
+def test_q8_0_gemm_any_whole_blocks_bit_identical(K):
+    """320 output tiles (no split): the whole output equals the oracle bit
+    for bit, with ragged rows and columns."""
+    M, N = 1200, 4000
+    assert _split_k(mmq.FMT_Q8_0, M, N, K) == 1 and _kernel(mmq.FMT_Q8_0, M, N, K) == "mmq"
+    _say(f"q8_0 gemm any K: M={M} N={N} K={K}")
+    xq = oracle.quantize_q8_1(inputs.activations(M, K, 220 + K))
+    w = inputs.q8_0_weights(N, K, 230 + K)
+    got = _run_gemm(mmq.FMT_Q8_0, xq, w, M, N, K)
+    rep = metrics.report(got, _oracle_gemm(mmq.FMT_Q8_0, xq, w, M, N, K))
+    _say(rep)
+    assert rep["bit_identical_fraction"] == 1.0
+
+
+@pytest.mark.parametrize("M,N,K", [(100, 100, 3616), (64, 130, 2080)])
+def test_q8_0_split_k_any_whole_blocks(M, N, K):
+    assert _split_k(mmq.FMT_Q8_0, M, N, K) > 1
+    _say(f"q8_0 split-K any K: M={M} N={N} K={K}")
+    xq = oracle.quantize_q8_1(inputs.activations(M, K, 240 + M))
+    w = inputs.q8_0_weights(N, K, 250 + N)
+    rep = metrics.report(_run_gemm(mmq.FMT_Q8_0, xq, w, M, N, K), _oracle_gemm(mmq.FMT_Q8_0, xq, w, M, N, K))
+    _say(rep)
+    assert rep["normalized_max_error"] <= metrics.TOL
+
+
+@pytest.mark.parametrize("K", [32, 288, 3616])
+@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("N", [1, 130])
+def test_q8_0_matvec_any_whole_blocks(M, N, K):
+    assert _kernel(mmq.FMT_Q8_0, M, N, K) == "mv"
+    _say(f"q8_0 matvec any K: M={M} N={N} K={K}")
+    xq = oracle.quantize_q8_1(inputs.activations(M, K, 260 + M))
+    w = inputs.q8_0_weights(N, K, 270 + N)
+    got = _run_gemm(mmq.FMT_Q8_0, xq, w, M, N, K)
+    _check_reordered(mmq.FMT_Q8_0, got, _oracle_gemm(mmq.FMT_Q8_0, xq, w, M, N, K), xq, w, M, N, K)
+
+
+def test_q8_0_gemm_multi_any_whole_blocks():
+    M, Ns, K = 129, (257, 130), 288
+    _say(f"q8_0 gemm multi any K: M={M} Ns={Ns} K={K}")
+    xq = oracle.quantize_q8_1(inputs.activations(M, K, 280))
+    ws = [inputs.q8_0_weights(n, K, 281 + g) for g, n in enumerate(Ns)]
+    outs = mmq.gemm_multi(mmq.FMT_Q8_0, _to_dev(xq), [_to_dev(w) for w in ws], list(Ns), M, K,
+                          [_nan_out(M, n) for n in Ns])
+    torch.cuda.synchronize()
+    for n, w, o in zip(Ns, ws, outs):
+        rep = metrics.report(o.cpu().numpy(), _oracle_gemm(mmq.FMT_Q8_0, xq, w, M, n, K))
+        _say(rep)
+        assert rep["bit_identical_fraction"] == 1.0

@@ -92,7 +92,7 @@ def test_extra_lds_hook_forces_refusal():
 
 
 @pytest.mark.parametrize("fmt,M,N,K,needle", [
-    (mmq.FMT_Q8_0, 64, 256, 288, "multiple of 256"),
+    (mmq.FMT_Q8_0, 64, 256, 272, "multiple of 32"),
     (mmq.FMT_Q4_K, 64, 256, 512 + 32, "super-blocks"),
     (mmq.FMT_Q8_0, 0, 256, 512, ">= 1"),
     (mmq.FMT_Q8_0, 64, 0, 512, ">= 1"),
@@ -105,6 +105,25 @@ def test_extra_lds_hook_forces_refusal():
 def test_guard_refuses_bad_shapes(fmt, M, N, K, needle):
     ok, why = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
     assert not ok and needle in why, why
+
+
+@pytest.mark.parametrize("M,K", [(64, 32), (200, 96), (2048, 288), (2048, 3616), (5, 3616), (100, 3616)])
+def test_q8_0_plans_any_whole_number_of_blocks(M, K):
+    """Q8_0 contracts over any whole number of 32-blocks ("When the Product
+    Won't Collapse", section 2): the tile kernel's last k-step may hold 1-3
+    blocks, the matvec's last unit one block.  The K-quants keep whole
+    super-blocks."""
+    ok, desc = mmq.plan_for_limits(mmq.FMT_Q8_0, M, 300, K, LDS_GFX950, 256)
+    assert ok, desc
+    kb = K // 32
+    steps = int(re.search(r"k_steps=(\d+)", desc).group(1))
+    if M <= 8:
+        assert "kernel=mv" in desc and steps == (kb + 1) // 2
+    else:
+        assert "kernel=mmq" in desc and steps == -(-kb // 4)
+        split, sps = (int(v) for v in re.search(r"split_k=(\d+) steps_per_split=(\d+)", desc).groups())
+        assert (split - 1) * sps < steps <= split * sps
+    assert not mmq.plan_for_limits(mmq.FMT_Q4_K, M, 300, K, LDS_GFX950, 256)[0]
 
 
 def test_guard_refuses_without_compute_units():
@@ -193,3 +212,89 @@ def test_refusal_reasons_are_per_thread():
     a.start(); b.start(); a.join(); b.join()
     assert seen["null"] == {"null pointer argument"}
     assert seen["fmt"] == {"unknown weight format 7"}
+
+
+def _t(dtype, n):
+    import torch
+    return torch.zeros(n, dtype=dtype)
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K, mmq.FMT_Q5_K])
+def test_binding_refuses_short_buffers(fmt):
+    """The C ABI takes bare pointers, so the binding checks every buffer
+    against the shape before the call: a short activation, weight, output,
+    id or block-dot buffer is a ValueError naming it (here on CPU tensors,
+    which the same check reaches before the device check)."""
+    import torch
+    u8, f32, i32 = torch.uint8, torch.float32, torch.int32
+    M, N, K = 9, 5, 512
+    xq_n, w_n, o_n = M * (K // 32) * 36, N * mmq.row_bytes(fmt, K), M * N
+    good = dict(xq=_t(u8, xq_n), w=_t(u8, w_n), out=_t(f32, o_n))
+    cases = [("xq", _t(u8, xq_n - 1)), ("w", _t(u8, w_n - 1)), ("out", _t(f32, o_n - 1)),
+             ("xq", _t(torch.int8, xq_n)), ("out", _t(torch.float16, o_n))]
+    for name, bad in cases:
+        args = dict(good, **{name: bad})
+        with pytest.raises(ValueError, match=name):
+            mmq.gemm(fmt, args["xq"], args["w"], M, N, K, args["out"])
+    with pytest.raises(ValueError, match="GPU"):   # sizes fine: the device check is next
+        mmq.gemm(fmt, good["xq"], good["w"], M, N, K, good["out"])
+    with pytest.raises(ValueError, match="w"):
+        mmq.gemm_multi(fmt, good["xq"], [good["w"], _t(u8, 3 * mmq.row_bytes(fmt, K))], [N, 4], M, K,
+                       [good["out"], _t(f32, M * 4)])
+    with pytest.raises(ValueError, match="dots"):
+        mmq.debug_block_dots(fmt, good["xq"], good["w"], M, N, K, _t(i32, M * N * (K // 32) - 1))
+    T, topk, E = 6, 2, 3
+    mw = _t(u8, E * N * mmq.row_bytes(fmt, K))
+    mo = _t(f32, T * topk * N)
+    ws = _t(u8, 1024)
+    ids = _t(i32, T * topk)
+    mx = _t(u8, T * (K // 32) * 36)
+    with pytest.raises(ValueError, match="ids"):
+        mmq.moe_gemm(fmt, mx, mw, E, _t(i32, T * topk - 1), topk, T, N, K, mo, ws)
+    with pytest.raises(ValueError, match="expert weights"):
+        mmq.moe_gemm(fmt, mx, _t(u8, (E - 1) * N * mmq.row_bytes(fmt, K)), E, ids, topk, T, N, K, mo, ws)
+    with pytest.raises(ValueError, match="out"):
+        mmq.moe_gemm_routed(fmt, mx, mw, E, topk, T, N, K, ws, _t(f32, T * topk * N - 1))
+
+
+def test_binding_refuses_short_quantize_buffers():
+    import torch
+    M, K = 3, 96
+    with pytest.raises(ValueError, match="x"):
+        mmq.quantize_q8_1(torch.zeros(M, K, dtype=torch.float64))
+    with pytest.raises(ValueError, match="q8_1"):
+        mmq.quantize_q8_1(torch.zeros(M, K), _t(torch.uint8, M * 3 * 36 - 1))
+
+
+def _split(desc):
+    return int(re.search(r"split_k=(\d+)", desc).group(1))
+
+
+def test_guard_plans_with_the_kernels_registers():
+    """The resident workgroups per CU come from the launched kernel's own
+    registers (read from the device with hipFuncGetAttributes; injected
+    here): 128 VGPRs give four waves per SIMD, two 8-wave workgroups per CU;
+    129-168 give one, which changes the split-K decision; more than 256 fit
+    no workgroup and are refused ("13 . r7-r8 raw-byte MMQ kernel", 3.3 and
+    6: every capacity the launch depends on is checked before it)."""
+    shape = (mmq.FMT_Q8_0, 1280, 2560, 3584)   # 200 output tiles
+    ok, desc = mmq.plan_for_limits(*shape, LDS_GFX950, 256)
+    assert ok and "wg_per_cu=2 vgprs=128" in desc and _split(desc) == 2, desc
+    ok, desc = mmq.plan_for_limits(*shape, LDS_GFX950, 256, vgprs=129)
+    assert ok and "wg_per_cu=1 vgprs=129" in desc and _split(desc) == 1, desc
+    ok, desc = mmq.plan_for_limits(*shape, LDS_GFX950, 256, vgprs=256)
+    assert ok and "wg_per_cu=1" in desc, desc
+    ok, why = mmq.plan_for_limits(*shape, LDS_GFX950, 256, vgprs=257)
+    assert not ok and "no workgroup" in why and "refused" in why, why
+    # LDS bounds residency too: a 100 KiB limit leaves one 76 KiB workgroup per CU
+    ok, desc = mmq.plan_for_limits(*shape, 100 * 1024, 256)
+    assert ok and "wg_per_cu=1" in desc, desc
+
+
+@pytest.mark.parametrize("M", [1, 8, 9, 2048])
+def test_guard_refuses_kernels_that_spill(M):
+    """A kernel that needs scratch missed its register budget: refused
+    before launch, for the tile and the matvec kernel alike."""
+    ok, why = mmq.plan_for_limits(mmq.FMT_Q4_K, M, 3584, 3584, LDS_GFX950, 256, vgprs=128, scratch=16)
+    assert not ok and "scratch" in why and "refused" in why, why
+    assert ("matvec" in why) == (M <= 8)
