@@ -135,11 +135,15 @@ def test_moe_workspace_reuse_and_refusals():
     ids = _dev(inputs.moe_ids(T, E, topk, 105))
     out = torch.full((T * topk, N), float("nan"), dtype=torch.float32, device=DEV)
     short = torch.empty((mmq.moe_workspace_bytes(T, topk, E) - 16,), dtype=torch.uint8, device=DEV)
+    # (the expert weights are sized for each call: the binding checks sizes
+    # before the library sees the call)
     for kw, args in [({"workspace": short}, (E, topk, K)), ({}, (0, topk, K)), ({}, (E, 0, K)),
-                     ({}, (E, topk, 320)), ({}, (4096, topk, K))]:
+                     ({}, (E, topk, 240)), ({}, (2049, topk, K))]:
         e, k_top, kk = args
+        we = _dev(w) if e <= E else torch.zeros((e * N * mmq.row_bytes(fmt, kk),), dtype=torch.uint8, device=DEV)
         with pytest.raises(mmq.MMQError):
-            mmq.moe_gemm(fmt, xq, _dev(w), e, ids, k_top, T, N, kk, out, **kw)
+            mmq.moe_gemm(fmt, xq, we, e, ids, k_top, T, N, kk, out, **kw)
+        del we
     torch.cuda.synchronize()
     assert np.isnan(out.cpu().numpy()).all()
 
@@ -208,8 +212,9 @@ def test_moe_routed_without_matching_tables_is_refused():
     with pytest.raises(mmq.MMQError, match="routed for 128 rows"):
         mmq.moe_gemm_routed(fmt, xq, w, E, 1, T, N, K, ws, out2)      # 64 routed rows
     out3 = torch.full((T * topk, N), float("nan"), dtype=torch.float32, device=DEV)
+    w5 = torch.zeros(((E + 1) * N * mmq.row_bytes(fmt, K),), dtype=torch.uint8, device=DEV)
     with pytest.raises(mmq.MMQError, match="routed for 128 rows"):
-        mmq.moe_gemm_routed(fmt, xq, w, E + 1, topk, T, N, K, ws, out3)   # 5 experts
+        mmq.moe_gemm_routed(fmt, xq, w5, E + 1, topk, T, N, K, ws, out3)  # 5 experts
     torch.cuda.synchronize()
     assert torch.isnan(out2).all() and torch.isnan(out3).all()
     assert not torch.isnan(out).any()
