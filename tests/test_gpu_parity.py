@@ -454,8 +454,8 @@ def test_gemm_multi_refusals_leave_outputs_untouched():
     outs = [_nan_out(M, 256), _nan_out(M, 256)]
     with pytest.raises(mmq.MMQError, match="count"):
         mmq.gemm_multi(mmq.FMT_Q8_0, xq, [w] * 9, [256] * 9, M, K, [_nan_out(M, 256) for _ in range(9)])
-    with pytest.raises(mmq.MMQError, match="multiple of 256"):
-        mmq.gemm_multi(mmq.FMT_Q8_0, xq, [w, w], [256, 256], M, K + 32, outs)
+    with pytest.raises(mmq.MMQError, match="multiple of 32"):
+        mmq.gemm_multi(mmq.FMT_Q8_0, xq, [w, w], [256, 256], M, K - 16, outs)
     with pytest.raises(mmq.MMQError, match=">= 1"):
         mmq.gemm_multi(mmq.FMT_Q8_0, xq, [w, w], [256, 0], M, K, outs)
     torch.cuda.synchronize()
