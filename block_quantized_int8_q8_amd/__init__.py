@@ -20,7 +20,7 @@ Q8_1_BYTES, Q8_0_BYTES, Q4_K_BYTES, Q5_K_BYTES = 36, 34, 144, 176
 
 EXPORTS = (
     "mmq_quantize_q8_1", "mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_q5_K", "mmq_gemm_multi", "mmq_moe_workspace_bytes",
-    "mmq_moe_gemm", "mmq_moe_gemm_routed", "mmq_debug_block_dots",
+    "mmq_moe_gemm", "mmq_moe_gemm_routed", "mmq_moe_gemm_noalloc", "mmq_debug_block_dots",
     "mmq_last_error", "mmq_plan_describe", "mmq_plan_for_limits",
     "mmq_debug_set_extra_lds", "mmq_version",
 )
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L.mmq_moe_gemm.restype = i32
         L.mmq_moe_gemm_routed.argtypes = [i32, p, p, i32, i32, p, i64, i64, i64, p, i64, p]
         L.mmq_moe_gemm_routed.restype = i32
+        L.mmq_moe_gemm_noalloc.argtypes = [i32, p, p, i32, p, i32, p, i64, i64, i64, p]
+        L.mmq_moe_gemm_noalloc.restype = i32
         L.mmq_debug_block_dots.argtypes = [i32, p, p, p, i64, i64, i64, p]
         L.mmq_debug_block_dots.restype = i32
         L.mmq_last_error.argtypes = []
@@ -204,7 +206,8 @@ def _check_moe_sizes(fmt, xq, w, n_experts, topk, T, N, K, out, workspace):
         _need(xq, torch.uint8, T * (K // 32) * Q8_1_BYTES, "xq (q8_1 activations)")
         _need(w, torch.uint8, n_experts * N * row_bytes(fmt, K), "w (expert weights)")
         _need(out, torch.float32, T * topk * N, "out")
-    _need(workspace, torch.uint8, 0, "workspace")
+    if workspace is not None:
+        _need(workspace, torch.uint8, 0, "workspace")
 
 
 def moe_gemm(fmt, xq, w, n_experts, ids, topk, T, N, K, out=None, workspace=None, stream=None):
@@ -237,6 +240,23 @@ def moe_gemm_routed(fmt, xq, w, n_experts, topk, T, N, K, workspace, out=None, s
     _check(lib().mmq_moe_gemm_routed(fmt, _ptr(xq), _ptr(w), n_experts, topk, _ptr(out, torch.float32), T, N, K,
                                      _ptr(workspace, torch.uint8), workspace.numel(), _stream(stream)),
            "mmq_moe_gemm_routed")
+    return out
+
+
+MOE_NOALLOC_MAX_ROUTED = 131072   # T * topk the allocation-free MoE entry point takes at most
+
+
+def moe_gemm_noalloc(fmt, xq, w, n_experts, ids, topk, T, N, K, out, stream=None):
+    """Indexed MoE as ``moe_gemm``, with the routing tables in the library's
+    static device scratch instead of a workspace: nothing is allocated,
+    here or in the library (``out`` must be given).  Calls that overlap in
+    time on one GPU race on that scratch.  T * topk <= MOE_NOALLOC_MAX_ROUTED."""
+    import torch
+    _check_moe_sizes(fmt, xq, w, n_experts, topk, T, N, K, out, None)
+    if _dims_ok(T, topk):
+        _need(ids, torch.int32, T * topk, "ids")
+    _check(lib().mmq_moe_gemm_noalloc(fmt, _ptr(xq), _ptr(w), n_experts, _ptr(ids, torch.int32), topk,
+                                      _ptr(out, torch.float32), T, N, K, _stream(stream)), "mmq_moe_gemm_noalloc")
     return out
 
 

@@ -20,6 +20,8 @@
 #include "../../include/mmq.h"
 #include "mmq_plan.hpp"
 
+static_assert(mmq::kNoAllocMaxRouted == MMQ_MOE_NOALLOC_MAX_ROUTED, "header and library disagree");
+
 namespace mmq {
 hipError_t launch_quantize(const float *x, void *y, int64_t M, int64_t K, int cu_count, hipStream_t stream);
 hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const void *x, const void *const *w,
@@ -27,6 +29,7 @@ hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const vo
 hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t *ids, int topk, int n_experts,
                       float *out, int64_t T, int64_t N, int64_t K, void *workspace, hipStream_t stream);
 const void *plan_kernel(const Plan &p, bool dots, bool moe);
+hipError_t noalloc_scratch(void **ptr);
 }  // namespace mmq
 
 namespace {
@@ -270,7 +273,7 @@ const char *route_mismatch(const void *workspace, int64_t R, int E, char *buf, s
 
 int moe_common(int fmt, const void *x_q8_1, const void *w, int n_experts, const int32_t *ids, int topk, float *out,
                int64_t T, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes, void *stream,
-               const char *name) {
+               const char *name, bool record = true) {
     g_err[0] = '\0';
     if (!mmq::fmt_ok(fmt)) return refuse("unknown weight format %d", fmt);
     if (!x_q8_1 || !w || !out || !workspace) return refuse("null pointer argument");
@@ -302,7 +305,7 @@ int moe_common(int fmt, const void *x_q8_1, const void *w, int n_experts, const 
     const hipError_t e = mmq::launch_moe(p, x_q8_1, w, ids, topk, n_experts, out, T, N, K, workspace,
                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return refuse("%s %s launch failed: %s", mmq::fmt_name(fmt), name, hipGetErrorString(e));
-    if (ids) record_route(workspace, T * topk, n_experts);
+    if (ids && record) record_route(workspace, T * topk, n_experts);
     return 1;
 }
 
@@ -325,6 +328,25 @@ int mmq_moe_gemm_routed(int fmt, const void *x_q8_1, const void *w, int n_expert
                         int64_t T, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes, void *stream) {
     return moe_common(fmt, x_q8_1, w, n_experts, nullptr, topk, out, T, N, K, workspace, workspace_bytes, stream,
                       "MoE GEMM (reused routing)");
+}
+
+int mmq_moe_gemm_noalloc(int fmt, const void *x_q8_1, const void *w, int n_experts, const int32_t *ids, int topk,
+                         float *out, int64_t T, int64_t N, int64_t K, void *stream) {
+    g_err[0] = '\0';
+    if (!ids) return refuse("null pointer argument");
+    if (topk >= 1 && T > mmq::kNoAllocMaxRouted / topk)
+        return refuse("MoE GEMM (no allocation): T*topk = %lld routed rows exceeds the static scratch's limit of %lld",
+                      (long long)T * topk, (long long)mmq::kNoAllocMaxRouted);
+    void *scratch = nullptr;
+    const hipError_t e = mmq::noalloc_scratch(&scratch);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return refuse("MoE GEMM (no allocation): device address of the static scratch: %s", hipGetErrorString(e));
+    }
+    // the scratch's tables are never offered to mmq_moe_gemm_routed (its
+    // address is not the caller's), so the routing is not recorded
+    return moe_common(fmt, x_q8_1, w, n_experts, ids, topk, out, T, N, K, scratch, mmq::kNoAllocScratchBytes, stream,
+                      "MoE GEMM (no allocation)", false);
 }
 
 int mmq_debug_block_dots(int fmt, const void *x_q8_1, const void *w, int32_t *dots, int64_t M, int64_t N,

@@ -23,6 +23,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "mmq_plan.hpp"
@@ -1315,6 +1316,41 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__re
 // stays capturable as plain kernels.
 __global__ __launch_bounds__(256) void k_zero_fill(float *__restrict__ p, int64_t n) {
     for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) p[i] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free MoE entry point: the routing tables of one
+// call (header, tile table, sorted routed-row ids: kNoAllocScratchBytes for
+// up to kNoAllocMaxRouted routed rows and kMoeMaxExperts experts) in a
+// file-scope device array instead of a caller workspace.  Each device holds
+// its own copy for the life of the process; every call on a device shares
+// it, so calls that overlap in time on one device race.  The routing kernel
+// rewrites everything the GEMM reads (header last) on every call, so
+// nothing needs clearing between calls.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+static_assert(kNoAllocScratchBytes % 16 == 0, "the tables are read as 16-byte units");
+
+// The device address of this device's copy of `scratch`, looked up once per
+// device with that device current (in host code the array's name is only a
+// stand-in for the symbol, never a device address).
+hipError_t noalloc_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static void *addr[kMaxDevices] = {};
+    static std::mutex mu;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 // Host-side launchers (declared in mmq_launch.hpp).

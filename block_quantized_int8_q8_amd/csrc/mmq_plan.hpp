@@ -287,7 +287,7 @@ inline bool make_plan_multi(int fmt, int64_t M, int count, const int64_t *Ns, in
 constexpr int kMoeMaxExperts = 2048;   // the routing kernel keeps its per-expert tables in LDS
 constexpr int kMoeMaxTopk = 64;
 
-inline int64_t moe_max_tiles(int64_t R, int64_t E) { return R / kTileM + (E < R ? E : R); }
+constexpr int64_t moe_max_tiles(int64_t R, int64_t E) { return R / kTileM + (E < R ? E : R); }
 
 // Workspace: a 16-byte header (kMoeMagic, R, E, 0) that the routing kernel
 // writes last, so that a later launch can check that the tables it reuses
@@ -296,10 +296,16 @@ inline int64_t moe_max_tiles(int64_t R, int64_t E) { return R / kTileM + (E < R 
 constexpr int kMoeMagic = 0x4d6f4531;   // "MoE1"
 constexpr int64_t kMoeHeaderBytes = 16;
 
-inline int64_t moe_workspace_bytes(int64_t R, int64_t E) {
+constexpr int64_t moe_workspace_bytes(int64_t R, int64_t E) {
     if (R < 0 || E < 0) return -1;
     return kMoeHeaderBytes + 16 * moe_max_tiles(R, E) + ((4 * R + 15) / 16) * 16;
 }
+
+// The allocation-free MoE entry point keeps its routing tables in a static
+// device array sized for this many routed rows (T * topk) and the most
+// experts: 576 KiB per device.
+constexpr int64_t kNoAllocMaxRouted = 131072;
+constexpr int64_t kNoAllocScratchBytes = moe_workspace_bytes(kNoAllocMaxRouted, kMoeMaxExperts);
 
 inline bool make_plan_moe(int fmt, int64_t T, int topk, int n_experts, int64_t N, int64_t K, int64_t lds_limit,
                           int cu_count, int64_t extra_lds, Plan *p, char *why, size_t why_len,

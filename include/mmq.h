@@ -185,6 +185,22 @@ int mmq_moe_gemm(int fmt, const void *x_q8_1, const void *w, int n_experts, cons
 int mmq_moe_gemm_routed(int fmt, const void *x_q8_1, const void *w, int n_experts, int topk, float *out,
                         int64_t T, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes, void *stream);
 
+/* The indexed-MoE GEMM of mmq_moe_gemm for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same routing and GEMM kernels, with the
+ * routing tables in a static device array of the library (576 KiB per
+ * device, held until the process ends) instead of a caller workspace.
+ * Arguments, layouts and results as for mmq_moe_gemm, without the workspace.
+ * Refused when T*topk exceeds MMQ_MOE_NOALLOC_MAX_ROUTED.  Calls no
+ * allocating routine.  Every call on a device shares that device's array,
+ * which keeps the last call's tables: calls that overlap in time on one
+ * device (several streams or host threads) race and must not be made;
+ * calls in order on one stream are safe.  The tables are not offered to
+ * mmq_moe_gemm_routed. */
+#define MMQ_MOE_NOALLOC_MAX_ROUTED 131072
+int mmq_moe_gemm_noalloc(int fmt, const void *x_q8_1, const void *w, int n_experts, const int32_t *ids, int topk,
+                         float *out, int64_t T, int64_t N, int64_t K, void *stream);
+
 /* Test entry: the exact int32 block dots I[m,n,b] through the same staging
  * and matrix-core code as the tiled GEMM of format `fmt` (MMQ_FMT_Q8_0,
  * MMQ_FMT_Q4_K or MMQ_FMT_Q5_K; always the tile kernel, whatever M),
