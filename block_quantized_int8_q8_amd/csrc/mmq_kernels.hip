@@ -1,12 +1,13 @@
 // mmq_kernels.hip -- gfx950 kernels of the block-quantized int8 MMQ library.
 //
 //   k_quantize_q8_1   fp32 -> q8_1, one pass over the activations (HBM-bound)
-//   k_mmq<FMT, DOTS, MOE, SKIP>
+//   k_mmq<FMT, DOTS, MOE, SKIP, TAIL>
 //                     q8_1 x {Q8_0, Q4_K, Q5_K} -> fp32 (or the raw int32 block
 //                     dots when DOTS), int8 MFMA with the per-block scale
 //                     applied in registers on the MFMA accumulator layout;
 //                     MOE gathers the rows of each expert's routed tokens;
-//                     SKIP lets waves with no rows left skip their compute
+//                     SKIP lets waves with no rows left skip their compute;
+//                     TAIL handles a last k-step of fewer than 4 blocks
 //   k_moe_route       expert routing for the MOE launch (counts, scan, scatter)
 //   k_mmv<FMT>        the same contraction for a few activation rows
 //                     (decode): VALU int8 dot products at the HBM roofline
@@ -644,16 +645,24 @@ struct MoeArgs {
 };
 
 // SKIP: waves whose 32 rows all lie past the tile's last row skip their
-// MFMAs and epilogues (see wave_live below).  The MoE launch always skips;
-// so does the dense Q8_0 kernel, where the branch costs nothing measurable.
-// For the K-quants the branch costs 1-2 % on full tiles (register
-// allocation), so the launcher uses that instantiation only when the plan
-// marks enough of the launch's waves as idle.
-template <int FMT, bool DOTS, bool MOE, bool SKIP>
+// MFMAs and epilogues (see wave_live below).  The MoE launch always skips.
+// On full tiles the branch costs 1-2 % (measured on both formats), so the
+// launcher uses the skipping instantiation only when the plan marks waves
+// as idle (Q8_0: any; K-quants: at least a quarter of the wave rows).
+// TAIL: the last k-step may hold fewer than KB blocks (Q8_0 with
+// K % 128 != 0); without it the per-block check of that case (2 % of the
+// step) is compiled out.
+// Q8_0 runs each k-step's last epilogue after the step's barrier (DEFER
+// below): the next step's first fragment reads are issued first, so their
+// LDS latency is spent on that epilogue instead of stalling the step's
+// first MFMA, and the last MFMA's latency is spent at the barrier.
+template <int FMT, bool DOTS, bool MOE, bool SKIP, bool TAIL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DOTS ? 2 : 4)))
 void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int steps_per_split, const MoeArgs moe) {
     static_assert(!(MOE && DOTS), "the block-dot output exists for plain GEMMs only");
     static_assert(!(DOTS && SKIP) && (!MOE || SKIP), "block dots never skip; the MoE launch always does");
+    static_assert(!TAIL || FMT == FMT_Q8_0, "only Q8_0 k-steps can be partial");
+    constexpr bool DEFER = FMT == FMT_Q8_0 && !DOTS;
     using L = Lds<FMT>;
     // The two k-step buffers are two LDS variables, not offsets into one
     // array: the compiler then knows that the DMA into one buffer cannot
@@ -720,6 +729,21 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     for (int c = 0; c < kNSub; c++)
 #pragma unroll
         for (int r = 0; r < 16; r++) acc[c][r] = 0.0f;
+    // DEFER: the last MFMA of the previous k-step and the scales of its
+    // epilogue (sub-tile kNSub-1 of block KB-1)
+    i32x16 pendD;
+    float2 pendW = make_float2(0.0f, 0.0f);
+    float pendX = 0.0f;
+    bool pending = false;   // wave-uniform
+    auto run_pending = [&]() {
+        if constexpr (DEFER) {
+            if (pending) {
+                scale_epilogue(acc[kNSub - 1], pendD, pendW.x, pendW.y, pendX);
+                asm volatile("" : "+v"(acc[kNSub - 1]));
+                pending = false;
+            }
+        }
+    };
 
     WRegs<FMT> wr_;
     auto load_w = [&](int k) {
@@ -807,7 +831,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
             fa[b & 1] = *reinterpret_cast<const i32x4 *>(buf + a_lane + b * kBlockBytes);
             if constexpr (!DOTS) {
                 const float xs = h2f(sHdr[(xs_row * KB + b) * 2]);
-                if constexpr (FMT == FMT_Q8_0)
+                if constexpr (TAIL)
                     xsv[b & 1] = (b == 0 || b < nvalid) ? xs : 0.0f;
                 else
                     xsv[b & 1] = xs;
@@ -829,6 +853,8 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
 #pragma unroll
             for (int st = 0; st < kPfB; st++) load_b(st);
         }
+        // the previous step's last epilogue, while those reads are in flight
+        run_pending();
 #pragma unroll
         for (int st = 0; st < kSteps; st++) {
             const int b = st / kNSub, c = st % kNSub;
@@ -847,6 +873,15 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
             if (!live) continue;
             const i32x16 D = mfma_at(fa[b & 1], fb[st % kRing], srcC);
             const int col = b_col0 + 32 * c;
+            if constexpr (DEFER) {
+                if (st == kSteps - 1) {   // its epilogue runs after the barrier
+                    pendD = D;
+                    pendW = fw[st % kRing];
+                    pendX = xsv[b & 1];
+                    pending = true;
+                    continue;
+                }
+            }
             if constexpr (DOTS) {
                 int32_t *dots = reinterpret_cast<int32_t *>(outp);
                 const int n = n0 + col;
@@ -891,6 +926,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
         step(Parity<0>{}, j);
         if (j + 1 < nloc) step(Parity<1>{}, j + 1);
     }
+    run_pending();
 
     if constexpr (MOE) {
         // scatter: tile row i -> routed row sorted[first + i]
@@ -1390,8 +1426,13 @@ static hipError_t launch_mv(const Plan &p, const GemmSet &set, const uint8_t *xb
     return hipGetLastError();
 }
 
-// The kernel a plan launches (the same choice as launch_gemm / launch_moe
-// below), for the capacity guard's attribute query.
+// The kernel a plan launches: launch_gemm and launch_moe below launch
+// exactly this one, and the capacity guard reads its attributes.
+template <int F, bool DOTS, bool MOE, bool SKIP, bool TAIL>
+static const void *kmmq() {
+    return reinterpret_cast<const void *>(&k_mmq<F, DOTS, MOE, SKIP, TAIL>);
+}
+
 const void *plan_kernel(const Plan &p, bool dots, bool moe) {
     auto pick = [&](auto fmt) -> const void * {
         constexpr int F = decltype(fmt)::value;
@@ -1401,10 +1442,16 @@ const void *plan_kernel(const Plan &p, bool dots, bool moe) {
             if (p.tile_m <= 4) return reinterpret_cast<const void *>(&k_mmv<F, 4>);
             return reinterpret_cast<const void *>(&k_mmv<F, 8>);
         }
-        if (moe) return reinterpret_cast<const void *>(&k_mmq<F, false, true, true>);
-        if (dots) return reinterpret_cast<const void *>(&k_mmq<F, true, false, false>);
-        if (F == FMT_Q8_0 || p.skip_idle_waves) return reinterpret_cast<const void *>(&k_mmq<F, false, false, true>);
-        return reinterpret_cast<const void *>(&k_mmq<F, false, false, (F == FMT_Q8_0)>);
+        if (dots) return kmmq<F, true, false, false, false>();   // partial steps: the store mask
+        if constexpr (F == FMT_Q8_0) {
+            if (moe) return p.tail ? kmmq<F, false, true, true, true>() : kmmq<F, false, true, true, false>();
+            if (p.skip_idle_waves)
+                return p.tail ? kmmq<F, false, false, true, true>() : kmmq<F, false, false, true, false>();
+            return p.tail ? kmmq<F, false, false, false, true>() : kmmq<F, false, false, false, false>();
+        } else {
+            if (moe) return kmmq<F, false, true, true, false>();
+            return p.skip_idle_waves ? kmmq<F, false, false, true, false>() : kmmq<F, false, false, false, false>();
+        }
     };
     if (p.fmt == FMT_Q8_0) return pick(std::integral_constant<int, FMT_Q8_0>{});
     if (p.fmt == FMT_Q4_K) return pick(std::integral_constant<int, FMT_Q4_K>{});
@@ -1432,30 +1479,15 @@ hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const vo
         }
     }
     const dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.split_k);
-    const int sps = int(p.steps_per_split);
     const dim3 block(p.threads);
-    const auto *xb = reinterpret_cast<const uint8_t *>(x);
-    // The GEMM kernel's LDS is static (its two k-step buffers, lds_bytes_for()
-    // bytes, which the plan checked against the device); nothing dynamic.
-    const size_t lds = 0;
-    auto go = [&](auto fmt) {
-        constexpr int F = decltype(fmt)::value;
-        if (dots)
-            hipLaunchKernelGGL((k_mmq<F, true, false, false>), grid, block, lds, stream, xb, set, int(M), int(K),
-                               sps, MoeArgs{});
-        else if (F == FMT_Q8_0 || p.skip_idle_waves)
-            hipLaunchKernelGGL((k_mmq<F, false, false, true>), grid, block, lds, stream, xb, set, int(M), int(K),
-                               sps, MoeArgs{});
-        else
-            hipLaunchKernelGGL((k_mmq<F, false, false, (F == FMT_Q8_0)>), grid, block, lds, stream, xb, set,
-                               int(M), int(K), sps, MoeArgs{});
-    };
-    if (p.fmt == FMT_Q8_0)
-        go(std::integral_constant<int, FMT_Q8_0>{});
-    else if (p.fmt == FMT_Q4_K)
-        go(std::integral_constant<int, FMT_Q4_K>{});
-    else
-        go(std::integral_constant<int, FMT_Q5_K>{});
+    // the kernel the plan names (the one whose attributes the guard read);
+    // its LDS is static (lds_bytes_for() bytes, checked by the plan)
+    const uint8_t *xb = reinterpret_cast<const uint8_t *>(x);
+    int Mi = int(M), Ki = int(K), sps = int(p.steps_per_split);
+    MoeArgs noMoe{};
+    void *args[] = {&xb, &set, &Mi, &Ki, &sps, &noMoe};
+    const hipError_t e = hipLaunchKernel(plan_kernel(p, dots, false), grid, block, args, 0, stream);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 
@@ -1486,14 +1518,11 @@ hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t
     moe.expert_bytes = N * weight_row_bytes(p.fmt, K);
     const dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, 1);
     const dim3 block(p.threads);
-    const auto *xb = reinterpret_cast<const uint8_t *>(x);
-    const int sps = int(p.steps_per_split);
-    if (p.fmt == FMT_Q8_0)
-        hipLaunchKernelGGL((k_mmq<FMT_Q8_0, false, true, true>), grid, block, 0, stream, xb, set, int(T), int(K), sps, moe);
-    else if (p.fmt == FMT_Q4_K)
-        hipLaunchKernelGGL((k_mmq<FMT_Q4_K, false, true, true>), grid, block, 0, stream, xb, set, int(T), int(K), sps, moe);
-    else
-        hipLaunchKernelGGL((k_mmq<FMT_Q5_K, false, true, true>), grid, block, 0, stream, xb, set, int(T), int(K), sps, moe);
+    const uint8_t *xb = reinterpret_cast<const uint8_t *>(x);
+    int Ti = int(T), Ki = int(K), sps = int(p.steps_per_split);
+    void *args[] = {&xb, &set, &Ti, &Ki, &sps, &moe};
+    const hipError_t e = hipLaunchKernel(plan_kernel(p, false, true), grid, block, args, 0, stream);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -110,11 +110,14 @@ struct Plan {
     // last may be shorter), summed into a zeroed output with fp32 atomics.
     int64_t split_k = 1, steps_per_split = 0;
     // Waves whose 32 rows all lie past M skip their MFMAs and epilogues.
-    // Always for Q8_0 (free there); for the K-quants only when at least
-    // 1/kSkipShare of the launch's wave rows are idle, since their skipping
-    // instantiation runs full tiles 1-2 % slower (measured: a gain of 11-17 %
-    // with 1-3 of 4 wave rows idle, a small loss with 1 of 8).
+    // Q8_0 whenever any wave row is idle; the K-quants only when at least
+    // 1/kSkipShare of the launch's wave rows are idle (measured: a gain of
+    // 11-17 % with 1-3 of 4 wave rows idle, a small loss with 1 of 8).  The
+    // skipping instantiation runs full tiles 1-2 % slower in both formats.
     bool skip_idle_waves = false;
+    // Q8_0 with K % 128 != 0: the last k-step holds fewer than
+    // kBlocksPerStage blocks (a kernel variant of its own)
+    bool tail = false;
     int mv_rows_per_wave = 0;   // matvec kernel: output rows per wave
     int wg_per_cu = 0;          // workgroups of the launched kernel resident per CU
     int kernel_vgprs = 0;       // its registers per lane
@@ -237,9 +240,12 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
         }
     }
     {
+        // the skipping kernel costs 1-2 % on full tiles (both formats): Q8_0
+        // takes it whenever a wave row is idle, the K-quants from a quarter on
         const int64_t rows = q.grid_y * kTileM, idle_wave_rows = (rows - M) / 32;
-        q.skip_idle_waves = fmt == FMT_Q8_0 || idle_wave_rows * 32 * kSkipShare >= rows;
+        q.skip_idle_waves = fmt == FMT_Q8_0 ? idle_wave_rows > 0 : idle_wave_rows * 32 * kSkipShare >= rows;
     }
+    q.tail = fmt == FMT_Q8_0 && (K / 32) % kBlocksPerStage != 0;
     if (q.grid_x > INT32_MAX) return fail("too many column tiles");
     *p = q;
     return true;
@@ -336,11 +342,11 @@ inline void describe(const Plan &p, char *buf, size_t len) {
     std::snprintf(buf, len,
                   "kernel=%s fmt=%s tile=%dx%d threads=%d blocks_per_stage=%d lds=%lld grid=%lldx%lld "
                   "k_steps=%lld split_k=%lld steps_per_split=%lld skip_idle_waves=%d mv_rows_per_wave=%d "
-                  "wg_per_cu=%d vgprs=%d",
+                  "wg_per_cu=%d vgprs=%d tail=%d",
                   p.kernel == KERNEL_MV ? "mv" : "mmq", fmt_name(p.fmt), p.tile_m, p.tile_n, p.threads, p.blocks_per_stage,
                   (long long)p.lds_bytes, (long long)p.grid_x, (long long)p.grid_y,
                   (long long)p.k_steps, (long long)p.split_k, (long long)p.steps_per_split, int(p.skip_idle_waves),
-                  p.mv_rows_per_wave, p.wg_per_cu, p.kernel_vgprs);
+                  p.mv_rows_per_wave, p.wg_per_cu, p.kernel_vgprs, int(p.tail));
 }
 
 }  // namespace mmq

@@ -116,6 +116,7 @@ def test_q8_0_plans_any_whole_number_of_blocks(M, K):
     ok, desc = mmq.plan_for_limits(mmq.FMT_Q8_0, M, 300, K, LDS_GFX950, 256)
     assert ok, desc
     kb = K // 32
+    assert f"tail={int(kb % 4 != 0 and M > 8)}" in desc, desc
     steps = int(re.search(r"k_steps=(\d+)", desc).group(1))
     if M <= 8:
         assert "kernel=mv" in desc and steps == (kb + 1) // 2
@@ -164,17 +165,19 @@ def test_decode_sizes_plan_the_matvec_kernel(fmt, M, N, K):
     assert "kernel=mmq" in mmq.plan_for_limits(fmt, 9, N, K, LDS_GFX950, 256)[1]
 
 
-@pytest.mark.parametrize("M,kquant_skips", [
-    (9, True), (64, True), (96, True),      # one row tile, 1-3 of its 4 wave rows past M
-    (97, False), (128, False),              # every wave row holds rows
-    (192, True),                            # 2 of 8 wave rows idle: the 1/4 share
-    (200, False), (2000, False), (2048, False), (8192, False)])
-def test_idle_wave_skip_planning(M, kquant_skips):
-    """Waves whose 32 rows all lie past M skip their MFMAs and epilogues:
-    always for Q8_0, and for the K-quants only when idle wave rows make up
-    at least 1/4 of the launch's (their skipping kernel runs full tiles a
-    little slower).  The matvec kernel (M <= 8) has no row tiles."""
-    for fmt, want in [(mmq.FMT_Q8_0, True), (mmq.FMT_Q4_K, kquant_skips), (mmq.FMT_Q5_K, kquant_skips)]:
+@pytest.mark.parametrize("M,q8_skips,kquant_skips", [
+    (9, True, True), (64, True, True), (96, True, True),   # one row tile, 1-3 of its 4 wave rows past M
+    (97, False, False), (128, False, False),               # every wave row holds rows
+    (192, True, True),                                     # 2 of 8 wave rows idle: the 1/4 share
+    (200, True, False), (2000, True, False),               # 1 idle wave row
+    (2048, False, False), (8192, False, False)])
+def test_idle_wave_skip_planning(M, q8_skips, kquant_skips):
+    """Waves whose 32 rows all lie past M skip their MFMAs and epilogues.
+    The skipping kernel runs full tiles 1-2 % slower, so it is chosen for
+    Q8_0 whenever a wave row is idle, and for the K-quants only when idle
+    wave rows make up at least 1/4 of the launch's.  The matvec kernel
+    (M <= 8) has no row tiles."""
+    for fmt, want in [(mmq.FMT_Q8_0, q8_skips), (mmq.FMT_Q4_K, kquant_skips), (mmq.FMT_Q5_K, kquant_skips)]:
         ok, desc = mmq.plan_for_limits(fmt, M, 3584, 3584, LDS_GFX950, 256)
         assert ok and f"skip_idle_waves={int(want)}" in desc, desc
 
