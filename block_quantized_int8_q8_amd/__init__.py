@@ -19,7 +19,8 @@ FMT_Q5_K = 2
 Q8_1_BYTES, Q8_0_BYTES, Q4_K_BYTES, Q5_K_BYTES = 36, 34, 144, 176
 
 EXPORTS = (
-    "mmq_quantize_q8_1", "mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_q5_K", "mmq_gemm_multi", "mmq_moe_workspace_bytes",
+    "mmq_quantize_q8_1", "mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_q5_K", "mmq_gemm_multi", "mmq_gemm_workspace_bytes",
+    "mmq_gemm_multi_ws", "mmq_moe_workspace_bytes",
     "mmq_moe_gemm", "mmq_moe_gemm_routed", "mmq_moe_gemm_noalloc", "mmq_debug_block_dots",
     "mmq_last_error", "mmq_plan_describe", "mmq_plan_for_limits",
     "mmq_debug_set_extra_lds", "mmq_version",
@@ -48,6 +49,10 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).restype = i32
         L.mmq_gemm_multi.argtypes = [i32, p, i32, p, p, p, i64, i64, p]
         L.mmq_gemm_multi.restype = i32
+        L.mmq_gemm_workspace_bytes.argtypes = [i32, i32, p, i64, i64]
+        L.mmq_gemm_workspace_bytes.restype = i64
+        L.mmq_gemm_multi_ws.argtypes = [i32, p, i32, p, p, p, i64, i64, p, i64, p]
+        L.mmq_gemm_multi_ws.restype = i32
         L.mmq_moe_workspace_bytes.argtypes = [i64, i32, i32]
         L.mmq_moe_workspace_bytes.restype = i64
         L.mmq_moe_gemm.argtypes = [i32, p, p, i32, p, i32, p, i64, i64, i64, p, i64, p]
@@ -177,9 +182,20 @@ def gemm(fmt, xq, w, M, N, K, out=None, stream=None):
     return f(xq, w, M, N, K, out, stream)
 
 
-def gemm_multi(fmt, xq, ws, Ns, M, K, outs=None, stream=None):
+def gemm_workspace_bytes(fmt, Ns, M, K) -> int:
+    """Split-K workspace bytes gemm_multi(..., workspace=...) needs on the
+    current device (0: the set does not split; -1: it would be refused)."""
+    count = len(Ns)
+    npv = (ctypes.c_int64 * max(count, 1))(*[int(n) for n in Ns])
+    return int(lib().mmq_gemm_workspace_bytes(fmt, count, npv, M, K))
+
+
+def gemm_multi(fmt, xq, ws, Ns, M, K, outs=None, stream=None, workspace=None):
     """One launch of several GEMMs sharing the q8_1 activations:
-    q8_1 [M, K/32, 36] x ws[g] [N[g], ...] -> outs[g] fp32 [M, N[g]]."""
+    q8_1 [M, K/32, 36] x ws[g] [N[g], ...] -> outs[g] fp32 [M, N[g]].
+    ``workspace``: a uint8 device tensor of at least gemm_workspace_bytes
+    bytes, which lets a shape with few output tiles split K further
+    (mmq_gemm_multi_ws); None: mmq_gemm_multi."""
     import torch
     count = len(ws)
     if len(Ns) != count or (outs is not None and len(outs) != count):
@@ -191,7 +207,12 @@ def gemm_multi(fmt, xq, ws, Ns, M, K, outs=None, stream=None):
     wp = (ctypes.c_void_p * count)(*[_ptr(w).value for w in ws])
     op = (ctypes.c_void_p * count)(*[_ptr(o, torch.float32).value for o in outs])
     npv = (ctypes.c_int64 * count)(*[int(n) for n in Ns])
-    _check(lib().mmq_gemm_multi(fmt, _ptr(xq), count, wp, op, npv, M, K, _stream(stream)), "mmq_gemm_multi")
+    if workspace is None:
+        _check(lib().mmq_gemm_multi(fmt, _ptr(xq), count, wp, op, npv, M, K, _stream(stream)), "mmq_gemm_multi")
+    else:
+        _need(workspace, torch.uint8, 0, "workspace")
+        _check(lib().mmq_gemm_multi_ws(fmt, _ptr(xq), count, wp, op, npv, M, K, _ptr(workspace),
+                                       workspace.numel(), _stream(stream)), "mmq_gemm_multi_ws")
     return outs
 
 

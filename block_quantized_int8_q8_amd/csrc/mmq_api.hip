@@ -25,7 +25,8 @@ static_assert(mmq::kNoAllocMaxRouted == MMQ_MOE_NOALLOC_MAX_ROUTED, "header and 
 namespace mmq {
 hipError_t launch_quantize(const float *x, void *y, int64_t M, int64_t K, int cu_count, hipStream_t stream);
 hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const void *x, const void *const *w,
-                       void *const *out, const int64_t *N, int64_t M, int64_t K, bool dots, hipStream_t stream);
+                       void *const *out, const int64_t *N, int64_t M, int64_t K, bool dots, void *workspace,
+                       hipStream_t stream);
 hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t *ids, int topk, int n_experts,
                       float *out, int64_t T, int64_t N, int64_t K, void *workspace, hipStream_t stream);
 const void *plan_kernel(const Plan &p, bool dots, bool moe);
@@ -140,12 +141,27 @@ bool plan_with_kernel_fit(MakePlan make, bool dots, bool moe, mmq::Plan *p, char
     return make(fit, p, why, why_len);
 }
 
+// Plan a GEMM set on the current device (with the launched kernel's
+// attributes); `workspace`: plan for a split-K workspace.
+bool plan_set(int fmt, int count, const int64_t *N, int64_t M, int64_t K, bool dots, bool workspace,
+              const DeviceLimits &L, mmq::Plan *p, int *tile_start, char *why, size_t why_len) {
+    auto make = [&](const mmq::KernelFit &fit, mmq::Plan *q, char *w, size_t wl) {
+        return mmq::make_plan_multi(fmt, M, count, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), q,
+                                    tile_start, w, wl, !dots, fit, workspace);
+    };
+    return plan_with_kernel_fit(make, dots, false, p, why, why_len);
+}
+
+// `workspace`: null, or `workspace_bytes` bytes of device memory for a
+// split-K plan (mmq_gemm_multi_ws).
 int gemm_set(int fmt, const void *x, int count, const void *const *w, void *const *out, const int64_t *N,
-             int64_t M, int64_t K, bool dots, void *stream) {
+             int64_t M, int64_t K, bool dots, void *workspace, int64_t workspace_bytes, void *stream) {
     g_err[0] = '\0';
     if (!mmq::fmt_ok(fmt)) return refuse("unknown weight format %d", fmt);
     if (count < 1 || count > mmq::kMaxGemms) return refuse("count must be 1..%d GEMMs", mmq::kMaxGemms);
     if (!x || !w || !out || !N) return refuse("null pointer argument");
+    if (workspace && !aligned(workspace, 16)) return refuse("workspace must be 16-byte aligned");
+    if (workspace && workspace_bytes < 0) return refuse("workspace_bytes must be >= 0");
     if (!aligned(x, 16)) return refuse("activation and weight pointers must be 16-byte aligned");
     for (int g = 0; g < count; g++) {
         if (!w[g] || !out[g]) return refuse("null pointer argument");
@@ -158,16 +174,18 @@ int gemm_set(int fmt, const void *x, int count, const void *const *w, void *cons
     mmq::Plan p;
     int tile_start[mmq::kMaxGemms + 1];
     char why[256];
-    // the block-dot output exists for the MMQ kernel only
-    auto make = [&](const mmq::KernelFit &fit, mmq::Plan *q, char *w, size_t wl) {
-        return mmq::make_plan_multi(fmt, M, count, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), q,
-                                    tile_start, w, wl, !dots, fit);
-    };
-    if (!plan_with_kernel_fit(make, dots, false, &p, why, sizeof(why)))
+    // the block-dot output exists for the MMQ kernel only (planned without
+    // a workspace: it never splits)
+    if (!plan_set(fmt, count, N, M, K, dots, workspace != nullptr && !dots, L, &p, tile_start, why, sizeof(why)))
         return refuse("%s GEMM M=%lld N=%lld K=%lld%s: %s", mmq::fmt_name(fmt), (long long)M, (long long)N[0],
                       (long long)K, count > 1 ? " (first of a set)" : "", why);
+    const int64_t need = mmq::split_workspace_bytes(p);
+    if (need > workspace_bytes)
+        return refuse("%s GEMM M=%lld N=%lld K=%lld: the split-K workspace holds %lld bytes, the plan needs %lld",
+                      mmq::fmt_name(fmt), (long long)M, (long long)N[0], (long long)K, (long long)workspace_bytes,
+                      (long long)need);
     (void)hipGetLastError();   // a stale error must not be blamed on this launch
-    const hipError_t e = mmq::launch_gemm(p, tile_start, count, x, w, out, N, M, K, dots,
+    const hipError_t e = mmq::launch_gemm(p, tile_start, count, x, w, out, N, M, K, dots, workspace,
                                           static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return refuse("%s GEMM launch failed: %s", mmq::fmt_name(fmt), hipGetErrorString(e));
     return 1;
@@ -175,7 +193,7 @@ int gemm_set(int fmt, const void *x, int count, const void *const *w, void *cons
 
 int gemm_common(int fmt, const void *x, const void *w, void *out, int64_t M, int64_t N, int64_t K,
                 bool dots, void *stream) {
-    return gemm_set(fmt, x, 1, &w, &out, &N, M, K, dots, stream);
+    return gemm_set(fmt, x, 1, &w, &out, &N, M, K, dots, nullptr, 0, stream);
 }
 
 }  // namespace
@@ -214,7 +232,31 @@ int mmq_gemm_q5_K(const void *x_q8_1, const void *w_q5_K, float *out, int64_t M,
 
 int mmq_gemm_multi(int fmt, const void *x_q8_1, int count, const void *const *w, float *const *out,
                    const int64_t *N, int64_t M, int64_t K, void *stream) {
-    return gemm_set(fmt, x_q8_1, count, w, reinterpret_cast<void *const *>(out), N, M, K, false, stream);
+    return gemm_set(fmt, x_q8_1, count, w, reinterpret_cast<void *const *>(out), N, M, K, false, nullptr, 0,
+                    stream);
+}
+
+int64_t mmq_gemm_workspace_bytes(int fmt, int count, const int64_t *N, int64_t M, int64_t K) {
+    g_err[0] = '\0';
+    if (!mmq::fmt_ok(fmt)) return refuse("unknown weight format %d", fmt), -1;
+    if (count < 1 || count > mmq::kMaxGemms) return refuse("count must be 1..%d GEMMs", mmq::kMaxGemms), -1;
+    if (!N) return refuse("null pointer argument"), -1;
+    DeviceLimits L;
+    if (!current_limits(&L)) return -1;
+    mmq::Plan p;
+    int tile_start[mmq::kMaxGemms + 1];
+    char why[256];
+    if (!plan_set(fmt, count, N, M, K, false, true, L, &p, tile_start, why, sizeof(why)))
+        return refuse("%s GEMM M=%lld N=%lld K=%lld: %s", mmq::fmt_name(fmt), (long long)M, (long long)N[0],
+                      (long long)K, why), -1;
+    return mmq::split_workspace_bytes(p);
+}
+
+int mmq_gemm_multi_ws(int fmt, const void *x_q8_1, int count, const void *const *w, float *const *out,
+                      const int64_t *N, int64_t M, int64_t K, void *workspace, int64_t workspace_bytes,
+                      void *stream) {
+    return gemm_set(fmt, x_q8_1, count, w, reinterpret_cast<void *const *>(out), N, M, K, false, workspace,
+                    workspace_bytes, stream);
 }
 
 int64_t mmq_moe_workspace_bytes(int64_t T, int topk, int n_experts) {
@@ -365,9 +407,12 @@ int mmq_plan_for_limits(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_li
     fit.scratch = kernel_scratch_bytes;
     const bool ok = mmq::make_plan(fmt, M, N, K, lds_limit_bytes, cu_count, g_extra_lds.load(), &p, why,
                                    sizeof(why), true, fit);
+    mmq::Plan pw;
+    const bool okw = ok && mmq::make_plan(fmt, M, N, K, lds_limit_bytes, cu_count, g_extra_lds.load(), &pw,
+                                          nullptr, 0, true, fit, true);
     if (buf && len > 0) {
         if (ok)
-            mmq::describe(p, buf, size_t(len));
+            mmq::describe(p, okw ? &pw : nullptr, buf, size_t(len));
         else
             std::snprintf(buf, size_t(len), "%s", why);
     }
@@ -380,16 +425,16 @@ int mmq_plan_describe(int fmt, int64_t M, int64_t N, int64_t K, char *buf, int64
         if (buf && len > 0) std::snprintf(buf, size_t(len), "%s", g_err);
         return 0;
     }
-    mmq::Plan p;
+    mmq::Plan p, pw;
     char why[256];
-    auto make = [&](const mmq::KernelFit &fit, mmq::Plan *q, char *w, size_t wl) {
-        return mmq::make_plan(fmt, M, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), q, w, wl, true, fit);
-    };
-    const bool ok = mmq::fmt_ok(fmt) && plan_with_kernel_fit(make, false, false, &p, why, sizeof(why));
+    int tile_start[mmq::kMaxGemms + 1];
+    const bool ok = mmq::fmt_ok(fmt) && plan_set(fmt, 1, &N, M, K, false, false, L, &p, tile_start, why, sizeof(why));
     if (!mmq::fmt_ok(fmt)) std::snprintf(why, sizeof(why), "unknown weight format");
+    char why2[256];
+    const bool okw = ok && plan_set(fmt, 1, &N, M, K, false, true, L, &pw, tile_start, why2, sizeof(why2));
     if (buf && len > 0) {
         if (ok)
-            mmq::describe(p, buf, size_t(len));
+            mmq::describe(p, okw ? &pw : nullptr, buf, size_t(len));
         else
             std::snprintf(buf, size_t(len), "%s", why);
     }

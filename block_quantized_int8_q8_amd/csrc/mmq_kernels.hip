@@ -643,6 +643,11 @@ struct GemmSet {
     int N[kMaxGemms];
     const uint8_t *w[kMaxGemms];
     void *out[kMaxGemms];
+    // split K through a workspace (null otherwise): the slices' partial
+    // tiles, [tile][slice][8][512 threads] float4, and one arrival counter
+    // per tile, zeroed before the launch
+    float *part;
+    uint32_t *cnt;
 };
 
 // Indexed MoE: the row tiles come from the routing kernel's table instead of
@@ -962,7 +967,69 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
         }
     } else if constexpr (!DOTS) {
         float *out = reinterpret_cast<float *>(outp);
-        const bool split = gridDim.z > 1;   // partial sums: added into the zeroed output
+        bool split = gridDim.z > 1;   // partial sums: added into the zeroed output
+        if (split && set.cnt) {
+            // Split through the workspace: every slice stores its partial
+            // tile; the slice that finds the tile's counter at S-1 on arrival
+            // is the last, and it sums the S partials in slice order 0..S-1
+            // (its own from registers) and stores the result.  No slice waits
+            // for another, and the sum's order does not depend on which one
+            // finishes last.
+            // Coherence across the XCDs' separate L2 caches: the partials
+            // are written and read with agent-scope coherent accesses (cache
+            // policy sc1, what an agent-scope atomic load or store uses), and
+            // each wave waits for its stores to complete before the
+            // workgroup's arrival is counted; the counter is a relaxed
+            // agent-scope atomic.  An agent-scope release/acquire fence pair
+            // would do the same by writing back and invalidating the whole
+            // L2, which slowed the concurrent workgroups' weight reads
+            // (measured: the 512-token layer 0.48 -> 0.70 ms).
+            constexpr int kCoherent = 16;   // sc1
+            const int S = gridDim.z, me = blockIdx.z;
+            const int64_t t = int64_t(ty) * gridDim.x + tx;
+            const __amdgpu_buffer_rsrc_t rp = tile_rsrc(reinterpret_cast<const uint8_t *>(set.part) + t * S * 65536,
+                                                        int64_t(S) * 65536);
+            // float4 i of this thread in slice sl: byte ((sl * 8 + i) * 512 + tid) * 16
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int c = i >> 2, r = (i & 3) * 4;
+                const u32x4 v = {__float_as_uint(acc[c][r]), __float_as_uint(acc[c][r + 1]),
+                                 __float_as_uint(acc[c][r + 2]), __float_as_uint(acc[c][r + 3])};
+                __builtin_amdgcn_raw_buffer_store_b128(v, rp, ((me * 8 + i) * kThreads + tid) * 16, 0, kCoherent);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial is in place
+            __syncthreads();   // also: no wave reads either LDS buffer any more
+            int *last = reinterpret_cast<int *>(lds0);
+            if (tid == 0)
+                *last = __hip_atomic_fetch_add(set.cnt + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                        uint32_t(S - 1);
+            __syncthreads();
+            if (!*last) return;   // workgroup-uniform
+            f32x16 sum[kNSub];
+            for (int sl = 0; sl < S; sl++) {
+                f32x16 v[kNSub];
+                if (sl == me) {
+#pragma unroll
+                    for (int c = 0; c < kNSub; c++) v[c] = acc[c];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; i++) {
+                        const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(
+                            rp, ((sl * 8 + i) * kThreads + tid) * 16, 0, kCoherent);
+                        const int c = i >> 2, r = (i & 3) * 4;
+                        v[c][r] = __uint_as_float(q.x);
+                        v[c][r + 1] = __uint_as_float(q.y);
+                        v[c][r + 2] = __uint_as_float(q.z);
+                        v[c][r + 3] = __uint_as_float(q.w);
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < kNSub; c++) sum[c] = sl == 0 ? v[c] : sum[c] + v[c];
+            }
+#pragma unroll
+            for (int c = 0; c < kNSub; c++) acc[c] = sum[c];
+            split = false;
+        }
 #pragma unroll
         for (int c = 0; c < kNSub; c++) {
             const int n = n0 + b_col0 + 32 * c;
@@ -1364,8 +1431,9 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__re
 }
 
 // Zero an fp32 array (the output of a split-K launch, before the slices add
-// into it).  A kernel rather than a memset node, so that the launch sequence
-// stays capturable as plain kernels.
+// into it; or, as 32-bit words, the arrival counters of a split through a
+// workspace).  A kernel rather than a memset node, so that the launch
+// sequence stays capturable as plain kernels.
 __global__ __launch_bounds__(256) void k_zero_fill(float *__restrict__ p, int64_t n) {
     for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) p[i] = 0.0f;
 }
@@ -1474,7 +1542,8 @@ const void *plan_kernel(const Plan &p, bool dots, bool moe) {
 }
 
 hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const void *x, const void *const *w,
-                       void *const *out, const int64_t *N, int64_t M, int64_t K, bool dots, hipStream_t stream) {
+                       void *const *out, const int64_t *N, int64_t M, int64_t K, bool dots, void *workspace,
+                       hipStream_t stream) {
     GemmSet set{};
     set.count = count;
     for (int g = 0; g < count; g++) {
@@ -1485,7 +1554,17 @@ hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const vo
     }
     set.tile_start[count] = tile_start[count];
     if (p.kernel == KERNEL_MV) return launch_mv(p, set, reinterpret_cast<const uint8_t *>(x), M, K, stream);
-    if (p.split_k > 1 && !dots) {
+    set.part = nullptr;
+    set.cnt = nullptr;
+    if (p.split_k > 1 && !dots && p.split_ws) {
+        // the arrival counters start at zero (a kernel, not a memset: the
+        // launch may be captured into a graph)
+        set.cnt = reinterpret_cast<uint32_t *>(workspace);
+        set.part = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(workspace) + split_counter_bytes(p));
+        const int64_t words = split_counter_bytes(p) / 4;
+        hipLaunchKernelGGL(k_zero_fill, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                           reinterpret_cast<float *>(workspace), words);
+    } else if (p.split_k > 1 && !dots) {
         for (int g = 0; g < count; g++) {
             const int64_t n = M * N[g];
             const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
@@ -1523,6 +1602,8 @@ hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t
     set.N[0] = int(N);
     set.w[0] = reinterpret_cast<const uint8_t *>(w);
     set.out[0] = out;
+    set.part = nullptr;
+    set.cnt = nullptr;
     MoeArgs moe;
     moe.header = header;
     moe.tiles = tiles;

@@ -39,6 +39,13 @@ constexpr int kMinStepsPerSplit = 4;   // k-steps a split-K slice keeps at least
 constexpr int kSplitBelow = 2;         // split when tiles * kSplitBelow <= resident slots
 constexpr int kSplitSlots = 1;         // workgroups per CU a split aims for ...
 constexpr int kMinStepsPerSplit2 = 8;  // ... or two per CU, for slices this long
+// Without a workspace the slices add into a zeroed output with fp32 atomics,
+// and only two of them: a sum of two terms onto an exact zero rounds the
+// same in either order, so the result does not change from run to run.  With
+// a caller workspace any number of slices store their partial tiles there and
+// the last slice of a tile to finish sums them in slice order (also the same
+// on every run).
+constexpr int kMaxSplitAtomic = 2;
 // (measured at M = 512: the down projection, 112 tiles of 148 k-steps, 143 ->
 // 123 us with 4 slices instead of 3; the q+k+v set, 144 tiles of 28, 62 -> 55
 // us with 3 instead of 2; o, 112 tiles of 28, slower with 4 slices of 7; 256
@@ -107,8 +114,12 @@ struct Plan {
     int64_t grid_x = 0, grid_y = 0;   // x: column tiles, y: row tiles
     int64_t k_steps = 0;
     // Split K: grid z = split_k slices of steps_per_split k-steps each (the
-    // last may be shorter), summed into a zeroed output with fp32 atomics.
+    // last may be shorter).  split_ws: the slices' partial tiles go to the
+    // caller's workspace and are summed there in slice order; otherwise
+    // (split_k <= kMaxSplitAtomic) they are added into a zeroed output with
+    // fp32 atomics.
     int64_t split_k = 1, steps_per_split = 0;
+    bool split_ws = false;
     // Waves whose 32 rows all lie past M skip their MFMAs and epilogues.
     // Q8_0 whenever any wave row is idle; the K-quants only when at least
     // 1/kSkipShare of the launch's wave rows are idle (measured: a gain of
@@ -146,7 +157,7 @@ inline const char *check_quantize_shape(int64_t M, int64_t K) {
 // with come from the kernel's own registers and LDS.
 inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limit, int cu_count,
                       int64_t extra_lds, Plan *p, char *why, size_t why_len, bool allow_mv = true,
-                      const KernelFit &fit = KernelFit()) {
+                      const KernelFit &fit = KernelFit(), bool workspace = false) {
     auto fail = [&](const char *msg) {
         if (why && why_len) std::snprintf(why, why_len, "%s", msg);
         return false;
@@ -234,9 +245,11 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
             if (s2 > q.k_steps / kMinStepsPerSplit2) s2 = q.k_steps / kMinStepsPerSplit2;
             if (s2 > s) s = s2;
         }
+        if (!workspace && s > kMaxSplitAtomic) s = kMaxSplitAtomic;
         if (s > 1) {
             q.steps_per_split = (q.k_steps + s - 1) / s;
             q.split_k = (q.k_steps + q.steps_per_split - 1) / q.steps_per_split;
+            q.split_ws = workspace && q.split_k > 1;
         }
     }
     {
@@ -259,7 +272,8 @@ constexpr int kMaxGemms = 8;
 
 inline bool make_plan_multi(int fmt, int64_t M, int count, const int64_t *Ns, int64_t K, int64_t lds_limit,
                             int cu_count, int64_t extra_lds, Plan *p, int *tile_start, char *why,
-                            size_t why_len, bool allow_mv = true, const KernelFit &fit = KernelFit()) {
+                            size_t why_len, bool allow_mv = true, const KernelFit &fit = KernelFit(),
+                            bool workspace = false) {
     auto fail = [&](const char *msg) {
         if (why && why_len) std::snprintf(why, why_len, "%s", msg);
         return false;
@@ -279,7 +293,20 @@ inline bool make_plan_multi(int fmt, int64_t M, int count, const int64_t *Ns, in
     }
     tile_start[count] = int(tiles);
     return make_plan(fmt, M, mv ? tiles : tiles * kTileN, K, lds_limit, cu_count, extra_lds, p, why, why_len,
-                     allow_mv, fit);
+                     allow_mv, fit, workspace);
+}
+
+// Split-K workspace of a plan: one 32-bit arrival counter per output tile
+// (padded to kSplitCountBytesAlign), then every slice's fp32 partial tile,
+// [tile][slice][128 x 128 values in the kernel's register order].
+constexpr int64_t kSplitCountBytesAlign = 256;
+inline int64_t split_counter_bytes(const Plan &p) {
+    const int64_t tiles = p.grid_x * p.grid_y;
+    return (4 * tiles + kSplitCountBytesAlign - 1) / kSplitCountBytesAlign * kSplitCountBytesAlign;
+}
+inline int64_t split_workspace_bytes(const Plan &p) {
+    if (p.kernel != KERNEL_MMQ || !p.split_ws) return 0;
+    return split_counter_bytes(p) + p.grid_x * p.grid_y * p.split_k * int64_t(kTileM) * kTileN * 4;
 }
 
 // Indexed MoE ("When Does a Kernel Win Surface?", section 4.5, the fused
@@ -338,15 +365,21 @@ inline bool make_plan_moe(int fmt, int64_t T, int topk, int n_experts, int64_t N
     return true;
 }
 
-inline void describe(const Plan &p, char *buf, size_t len) {
-    std::snprintf(buf, len,
-                  "kernel=%s fmt=%s tile=%dx%d threads=%d blocks_per_stage=%d lds=%lld grid=%lldx%lld "
-                  "k_steps=%lld split_k=%lld steps_per_split=%lld skip_idle_waves=%d mv_rows_per_wave=%d "
-                  "wg_per_cu=%d vgprs=%d tail=%d",
-                  p.kernel == KERNEL_MV ? "mv" : "mmq", fmt_name(p.fmt), p.tile_m, p.tile_n, p.threads, p.blocks_per_stage,
-                  (long long)p.lds_bytes, (long long)p.grid_x, (long long)p.grid_y,
-                  (long long)p.k_steps, (long long)p.split_k, (long long)p.steps_per_split, int(p.skip_idle_waves),
-                  p.mv_rows_per_wave, p.wg_per_cu, p.kernel_vgprs, int(p.tail));
+// `ws`: the plan of the same call given a split-K workspace (appended as
+// ws_split_k, ws_steps_per_split and ws_bytes), or null.
+inline void describe(const Plan &p, const Plan *ws, char *buf, size_t len) {
+    int n = std::snprintf(buf, len,
+                          "kernel=%s fmt=%s tile=%dx%d threads=%d blocks_per_stage=%d lds=%lld grid=%lldx%lld "
+                          "k_steps=%lld split_k=%lld steps_per_split=%lld skip_idle_waves=%d mv_rows_per_wave=%d "
+                          "wg_per_cu=%d vgprs=%d tail=%d split_ws=%d",
+                          p.kernel == KERNEL_MV ? "mv" : "mmq", fmt_name(p.fmt), p.tile_m, p.tile_n, p.threads,
+                          p.blocks_per_stage, (long long)p.lds_bytes, (long long)p.grid_x, (long long)p.grid_y,
+                          (long long)p.k_steps, (long long)p.split_k, (long long)p.steps_per_split,
+                          int(p.skip_idle_waves), p.mv_rows_per_wave, p.wg_per_cu, p.kernel_vgprs, int(p.tail),
+                          int(p.split_ws));
+    if (ws && n > 0 && size_t(n) < len)
+        std::snprintf(buf + n, len - size_t(n), " ws_split_k=%lld ws_steps_per_split=%lld ws_bytes=%lld",
+                      (long long)ws->split_k, (long long)ws->steps_per_split, (long long)split_workspace_bytes(*ws));
 }
 
 }  // namespace mmq

@@ -81,12 +81,16 @@ int mmq_quantize_q8_1(const float *x, void *y, int64_t M, int64_t K, void *strea
  *   out: M x N fp32 row-major (leading dimension N), fully overwritten.
  * Per block the weight scale multiplies the integer dot first (one
  * rounding) and the activation scale is then fused into the fp32 running
- * sum, blocks in ascending order from 0.  Requires K % 256 == 0.
+ * sum, blocks in ascending order from 0.  Requires K % 32 == 0 (any whole
+ * number of Q8_0 blocks).
  * Shapes with too few 128 x 128 output tiles to occupy the device are split
- * along K (mmq_plan_describe reports split_k): the library first zeroes
- * `out` with a kernel on `stream`, then each K slice adds its partial sums
- * with fp32 atomics, so for those shapes the summation order, and the last
- * bits of the result, can differ from run to run.
+ * along K into two slices (mmq_plan_describe reports split_k): the library
+ * first zeroes `out` with a kernel on `stream`, then each slice adds its
+ * partial sums with fp32 atomics.  A two-term sum onto an exact zero rounds
+ * the same in either order, so the result is the same on every run, but it
+ * is not the single ascending-order sum (a few ulp apart; Q8_0 is then not
+ * bit-identical to the one-pass order).  mmq_gemm_multi_ws splits such
+ * shapes further through a caller workspace, also reproducibly.
  * M <= 8 (decode; "When Does a Kernel Win Surface?", sections 2 and 8: the
  * matvec contraction, bound by the weight stream) runs a matrix-vector
  * kernel instead: each weight row is read once for all M activation rows
@@ -133,6 +137,36 @@ int mmq_gemm_q5_K(const void *x_q8_1, const void *w_q5_K, float *out,
  * Refused (nothing launched) when any member would be refused. */
 int mmq_gemm_multi(int fmt, const void *x_q8_1, int count, const void *const *w, float *const *out,
                    const int64_t *N, int64_t M, int64_t K, void *stream);
+
+/* Bytes of device workspace mmq_gemm_multi_ws needs for this GEMM set on the
+ * current device: 0 when its plan does not split K (then the workspace may be
+ * NULL), else 4 bytes per output tile of arrival counters (padded to 256 B)
+ * plus split_k x 64 KiB of fp32 partial sums per 128 x 128 output tile: at
+ * most 2 x (compute units) x 64 KiB plus the counters (32 MiB on MI355X,
+ * whose 256 CUs hold two workgroups each).  -1 when the
+ * set would be refused (reason in mmq_last_error()).  The size depends on the
+ * device (its compute-unit count), so query it on the device that runs the
+ * GEMMs. */
+int64_t mmq_gemm_workspace_bytes(int fmt, int count, const int64_t *N, int64_t M, int64_t K);
+
+/* mmq_gemm_multi with a split-K workspace ("When Does a Kernel Win Surface?",
+ * section 4.5, on occupying the device when the output has few tiles): the
+ * same GEMMs, but shapes with few output tiles may be split into more than
+ * two K slices.  Each slice stores its partial tile in the workspace; the
+ * last slice of a tile to finish (an arrival counter per tile, zeroed by a
+ * kernel on `stream` before the GEMM) sums the partials in slice order
+ * 0, 1, ... and writes the tile, so the result is the same on every run.
+ * mmq_plan_describe reports the split as ws_split_k.
+ *   workspace: device memory of workspace_bytes >= mmq_gemm_workspace_bytes
+ *   for the same arguments, 16-byte aligned, owned by the caller; its
+ *   contents need no preparation and are clobbered.  NULL with 0 bytes
+ *   behaves as mmq_gemm_multi.  Two calls that run at the same time must not
+ *   share a workspace.
+ * Refused, in addition to mmq_gemm_multi's causes, when the workspace is
+ * smaller than the plan needs or misaligned. */
+int mmq_gemm_multi_ws(int fmt, const void *x_q8_1, int count, const void *const *w, float *const *out,
+                      const int64_t *N, int64_t M, int64_t K, void *workspace, int64_t workspace_bytes,
+                      void *stream);
 
 /* Bytes of device workspace mmq_moe_gemm needs for T tokens routed to topk
  * experts each among n_experts: a 16-byte header, a tile table (16 B per

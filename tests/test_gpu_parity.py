@@ -193,13 +193,15 @@ def _split_k(fmt, M, N, K):
 @pytest.mark.parametrize("M,N,K", [(64, 64, 3584), (129, 257, 1024), (200, 300, 2048), (100, 100, 18944),
                                    (512, 512, 3584)])
 def test_split_k_gemm_matches_oracle(fmt, M, N, K):
-    """Shapes with too few output tiles for the device run split-K: the
-    slices add their partial sums into the zeroed output with fp32 atomics
-    (the summation order differs from the oracle's, so the tolerance applies
-    and bit identity does not).  Every element must still be written."""
+    """Shapes with too few output tiles for the device run split-K: without
+    a workspace, two slices add their partial sums into the zeroed output
+    with fp32 atomics (the summation order differs from the oracle's, so the
+    tolerance applies and bit identity does not).  Every element must still
+    be written, and a second run gives the same bits (a two-term sum onto
+    zero does not depend on which slice lands first)."""
     splits = _split_k(fmt, M, N, K)
     _say(f"split-K gemm fmt={fmt} M={M} N={N} K={K} split_k={splits}")
-    assert splits > 1
+    assert splits == 2
     x = inputs.activations(M, K, 50 + M)
     xq = oracle.quantize_q8_1(x)
     w = _weights(fmt, N, K, 60 + N)
@@ -207,6 +209,85 @@ def test_split_k_gemm_matches_oracle(fmt, M, N, K):
     rep = metrics.report(got, _oracle_gemm(fmt, xq, w, M, N, K))
     _say(rep)
     assert rep["normalized_max_error"] <= metrics.TOL
+    assert np.array_equal(_run_gemm(fmt, xq, w, M, N, K).view(np.uint32), got.view(np.uint32))
+
+
+def _ws_split_k(fmt, M, N, K):
+    import re
+    return int(re.search(r"ws_split_k=(\d+)", mmq.plan_describe(fmt, M, N, K)[1]).group(1))
+
+
+def _run_multi(fmt, xq_dev, w_dev, Ns, M, K, workspace=None):
+    outs = [_nan_out(M, n) for n in Ns]
+    mmq.gemm_multi(fmt, xq_dev, w_dev, list(Ns), M, K, outs, workspace=workspace)
+    torch.cuda.synchronize()
+    res = [o.cpu().numpy() for o in outs]
+    assert not any(np.isnan(o).any() for o in res), "output element left unwritten"
+    return res
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M,Ns,K", [(64, (64,), 3584), (100, (100,), 18944), (200, (300,), 2048),
+                                    (512, (512,), 3584), (512, (3584,), 18944), (512, (3584, 512, 512), 3584),
+                                    (300, (600,), 3616)])
+def test_split_workspace_matches_oracle_and_repeats(fmt, M, Ns, K):
+    """Split-K through a caller workspace (more than two slices): the slices
+    store their partial tiles and the last one of each tile sums them in
+    slice order.  Every output element within tolerance of the oracle; the
+    same bits again on a second call whose workspace was first filled with
+    0xFF (garbage counters and partials: the launch zeroes its counters),
+    and on a third; the call without a workspace (at most two slices) also
+    repeats bit for bit."""
+    if fmt != mmq.FMT_Q8_0 and K % 256:
+        pytest.skip("K-quants need whole super-blocks")
+    if len(Ns) == 1:
+        assert _ws_split_k(fmt, M, Ns[0], K) > 2
+    need = mmq.gemm_workspace_bytes(fmt, list(Ns), M, K)
+    _say(f"split workspace fmt={fmt} M={M} Ns={Ns} K={K} bytes={need}")
+    assert need > 0
+    x = inputs.activations(M, K, 150 + M)
+    xq = oracle.quantize_q8_1(x)
+    ws = [_weights(fmt, n, K, 160 + g) for g, n in enumerate(Ns)]
+    xq_dev, w_dev = _to_dev(xq), [_to_dev(w) for w in ws]
+    work = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    first = _run_multi(fmt, xq_dev, w_dev, Ns, M, K, work)
+    for g, (n, w) in enumerate(zip(Ns, ws)):
+        rep = metrics.report(first[g], _oracle_gemm(fmt, xq, w, M, n, K))
+        _say(g, rep)
+        assert rep["normalized_max_error"] <= metrics.TOL
+    for _ in range(2):
+        work.fill_(0xFF)
+        again = _run_multi(fmt, xq_dev, w_dev, Ns, M, K, work)
+        assert all(np.array_equal(a.view(np.uint32), b.view(np.uint32)) for a, b in zip(first, again))
+    plain = _run_multi(fmt, xq_dev, w_dev, Ns, M, K)
+    assert all(np.array_equal(a.view(np.uint32), b.view(np.uint32))
+               for a, b in zip(plain, _run_multi(fmt, xq_dev, w_dev, Ns, M, K)))
+
+
+def test_split_workspace_refusals():
+    """A workspace smaller than the plan needs, or not 16-byte aligned, is
+    refused before anything is launched (the outputs keep their NaN
+    sentinel); a shape that does not split needs none and computes exactly
+    what the call without a workspace computes."""
+    fmt, M, N, K = mmq.FMT_Q4_K, 512, 3584, 3584
+    need = mmq.gemm_workspace_bytes(fmt, [N], M, K)
+    assert need > 0
+    x = inputs.activations(M, K, 170)
+    xq_dev = _to_dev(oracle.quantize_q8_1(x))
+    w_dev = [_to_dev(_weights(fmt, N, K, 171))]
+    for work, why in ((torch.zeros(need - 1, dtype=torch.uint8, device=DEV), "workspace holds"),
+                      (torch.zeros(need + 16, dtype=torch.uint8, device=DEV)[1:], "aligned")):
+        out = _nan_out(M, N)
+        with pytest.raises(mmq.MMQError, match=why):
+            mmq.gemm_multi(fmt, xq_dev, w_dev, [N], M, K, [out], workspace=work)
+        torch.cuda.synchronize()
+        assert torch.isnan(out).all()
+    M2 = 2048
+    assert mmq.gemm_workspace_bytes(fmt, [N], M2, K) == 0
+    xq2 = _to_dev(oracle.quantize_q8_1(inputs.activations(M2, K, 172)))
+    a = _run_multi(fmt, xq2, w_dev, [N], M2, K, torch.zeros(0, dtype=torch.uint8, device=DEV))
+    b = _run_multi(fmt, xq2, w_dev, [N], M2, K)
+    assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -317,8 +398,10 @@ def test_layer_gemm_set(M):
         Ns = [shapes[g][0] for g in gemms]
         assert all(shapes[g][1] == K for g in gemms)
         outs = [_nan_out(M, n) for n in Ns]
-        _say(f"layer M={M}: gemm set {'+'.join(gemms)} N={Ns} K={K}")
-        mmq.gemm_multi(mmq.FMT_Q4_K, xq_dev, [_to_dev(w) for w in ws], Ns, M, K, outs)
+        need = mmq.gemm_workspace_bytes(mmq.FMT_Q4_K, Ns, M, K)
+        work = torch.empty(need, dtype=torch.uint8, device=DEV) if need > 0 else None
+        _say(f"layer M={M}: gemm set {'+'.join(gemms)} N={Ns} K={K} workspace={need}")
+        mmq.gemm_multi(mmq.FMT_Q4_K, xq_dev, [_to_dev(w) for w in ws], Ns, M, K, outs, workspace=work)
         torch.cuda.synchronize()
         for g, n, w, out in zip(gemms, Ns, ws, outs):
             o = out.cpu().numpy()

@@ -63,13 +63,33 @@ def test_plans_for_benchmark_shapes_fit(fmt, M, N, K):
     (100, 100, 18944, 37, 4),       # one tile, 148 k-steps
 ])
 def test_split_k_planning(M, N, K, split, steps):
+    """With a workspace (ws_*) the split follows the occupancy rule; without
+    one the same shapes split into at most two slices (fp32 atomics onto a
+    zeroed output, reproducible only for two terms)."""
     for fmt in (mmq.FMT_Q8_0, mmq.FMT_Q4_K):
         ok, desc = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
         assert ok, desc
-        got = tuple(int(v) for v in re.search(r"split_k=(\d+) steps_per_split=(\d+)", desc).groups())
-        assert got == (split, steps), desc
         k_steps = K // 128
+        got = tuple(int(v) for v in re.search(r" ws_split_k=(\d+) ws_steps_per_split=(\d+)", desc).groups())
+        assert got == (split, steps), desc
         assert (split - 1) * steps < k_steps <= split * steps   # no empty slice
+        tiles = -(-M // 128) * -(-N // 128)
+        ws = int(re.search(r"ws_bytes=(\d+)", desc).group(1))
+        assert ws == (0 if split == 1 else -(-4 * tiles // 256) * 256 + tiles * split * 128 * 128 * 4), desc
+        plain = (2, -(-k_steps // 2)) if split > 1 else (1, k_steps)
+        got = tuple(int(v) for v in re.search(r" split_k=(\d+) steps_per_split=(\d+)", desc).groups())
+        assert got == plain, desc
+        assert f"split_ws=0" in desc
+
+
+def test_split_workspace_bound():
+    """The workspace a split plan needs stays under 2 x CUs x 64 KiB plus the
+    counters, over tile counts from 1 to past the split threshold."""
+    for n_tiles in range(1, 300):
+        ok, desc = mmq.plan_for_limits(mmq.FMT_Q4_K, 128, 128 * n_tiles, 1 << 20, LDS_GFX950, 256)
+        assert ok, desc
+        ws = int(re.search(r"ws_bytes=(\d+)", desc).group(1))
+        assert ws <= 2 * 256 * 65536 + 4096, (n_tiles, desc)
 
 
 @pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
