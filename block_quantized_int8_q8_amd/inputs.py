@@ -16,6 +16,9 @@ Distributions follow the 7B prefill workloads the library is measured on:
     [0, 1e-2].
   * Q5_K weights: as Q4_K, plus 32 uniformly random high-bit bytes (each
     code's fifth bit uniform).
+  * Q6_K weights: 128 low-bit and 64 high-bit bytes uniformly random (each
+    6-bit code uniform on 0..63), the sixteen int8 scales uniform on
+    -128..127, fp16 d uniform on [1e-4, 1e-3].
 Seeds are ``1000 * config + tensor_id`` with numpy's PCG64.
 
 Block layouts (little-endian):
@@ -24,6 +27,8 @@ Block layouts (little-endian):
   Q4_K (144 B): fp16 d @0, fp16 dmin @2, 12 B scales/mins @4, 128 B codes @16
   Q5_K (176 B): fp16 d @0, fp16 dmin @2, 12 B scales/mins @4, 32 B high bits
                 @16, 128 B low nibbles @48
+  Q6_K (210 B): 128 B low four bits @0, 64 B high two bits @128, 16 x int8
+                scales @192, fp16 d @208
 """
 from __future__ import annotations
 
@@ -33,6 +38,7 @@ Q8_1_BYTES = 36
 Q8_0_BYTES = 34
 Q4_K_BYTES = 144
 Q5_K_BYTES = 176
+Q6_K_BYTES = 210
 
 
 def seed_for(config: int, tensor_id: int) -> int:
@@ -134,6 +140,33 @@ def q5_K_weights(N: int, K: int, seed: int, d_range=(1e-3, 1e-2), dmin_range=(0.
     out[..., 4:16] = sc
     out[..., 16:48] = qh
     out[..., 48:176] = qs
+    return out
+
+
+def q6_K_weights(N: int, K: int, seed: int, d_range=(1e-4, 1e-3), d_value: float | None = None,
+                 scale_value: int | None = None, low_byte: int | None = None,
+                 high_byte: int | None = None) -> np.ndarray:
+    """uint8 N x (K/256) x 210.  ``scale_value`` fixes all sixteen int8
+    scales, ``low_byte`` / ``high_byte`` every low-bit / high-bit byte."""
+    if K % 256:
+        raise ValueError("K must be a multiple of 256")
+    nsb = K // 256
+    r = np.random.default_rng(seed)
+    d = np.full((N, nsb), d_value) if d_value is not None else r.uniform(*d_range, size=(N, nsb))
+    ql = r.integers(0, 255, size=(N, nsb, 128), endpoint=True, dtype=np.uint8)
+    qh = r.integers(0, 255, size=(N, nsb, 64), endpoint=True, dtype=np.uint8)
+    sc = r.integers(-128, 127, size=(N, nsb, 16), endpoint=True, dtype=np.int8)
+    if scale_value is not None:
+        sc[...] = np.int8(scale_value)
+    if low_byte is not None:
+        ql[...] = np.uint8(low_byte)
+    if high_byte is not None:
+        qh[...] = np.uint8(high_byte)
+    out = np.empty((N, nsb, Q6_K_BYTES), dtype=np.uint8)
+    out[..., 0:128] = ql
+    out[..., 128:192] = qh
+    out[..., 192:208] = sc.view(np.uint8)
+    out[..., 208:210] = _f16_bytes(d)
     return out
 
 

@@ -25,6 +25,7 @@ Q8_1_BYTES = 36
 Q8_0_BYTES = 34
 Q4_K_BYTES = 144
 Q5_K_BYTES = 176
+Q6_K_BYTES = 210
 
 
 def build(force: bool = True) -> str:
@@ -69,13 +70,20 @@ def lib() -> ctypes.CDLL:
         L.oracle_dequant_q4_K_block.argtypes = [p, p]
         L.oracle_q5k_code.argtypes = [p, i32]
         L.oracle_q5k_code.restype = i32
+        for name in ("oracle_q6k_code", "oracle_q6k_scale"):
+            getattr(L, name).argtypes = [p, i32]
+            getattr(L, name).restype = i32
+        L.oracle_dequant_q6_K_block.argtypes = [p, p]
+        L.oracle_group_dots_q6_K.argtypes = [p, p, p, i64, i64, i64]
+        L.oracle_group_dots_q6_K.restype = i32
         for name in ("oracle_block_dots_q8_0", "oracle_block_dots_q4_K", "oracle_block_dots_q5_K"):
             getattr(L, name).argtypes = [p, p, p, i64, i64, i64]
             getattr(L, name).restype = i32
-        for name in ("oracle_gemm_q8_0", "oracle_gemm_q4_K", "oracle_gemm_q5_K"):
+        for name in ("oracle_gemm_q8_0", "oracle_gemm_q4_K", "oracle_gemm_q5_K", "oracle_gemm_q6_K"):
             getattr(L, name).argtypes = [p, p, p, i64, i64, i64, i32]
             getattr(L, name).restype = i32
-        for name in ("oracle_gemm_q8_0_rows", "oracle_gemm_q4_K_rows", "oracle_gemm_q5_K_rows"):
+        for name in ("oracle_gemm_q8_0_rows", "oracle_gemm_q4_K_rows", "oracle_gemm_q5_K_rows",
+                     "oracle_gemm_q6_K_rows"):
             getattr(L, name).argtypes = [p, p, p, i64, i64, i64, i64, i64, i32]
             getattr(L, name).restype = i32
         _lib = L
@@ -150,6 +158,28 @@ def q5k_code(superblock: np.ndarray, e: int) -> int:
     return lib().oracle_q5k_code(_ptr(superblock), e)
 
 
+def q6k_code(superblock: np.ndarray, e: int) -> int:
+    """6-bit code (0..63) of element e of a Q6_K super-block (reading R22 in the C source)."""
+    superblock = np.ascontiguousarray(superblock, dtype=np.uint8)
+    assert superblock.size == Q6_K_BYTES
+    return lib().oracle_q6k_code(_ptr(superblock), e)
+
+
+def q6k_scale(superblock: np.ndarray, g: int) -> int:
+    """int8 scale of 16-element group g of a Q6_K super-block (reading R22)."""
+    superblock = np.ascontiguousarray(superblock, dtype=np.uint8)
+    assert superblock.size == Q6_K_BYTES
+    return lib().oracle_q6k_scale(_ptr(superblock), g)
+
+
+def dequant_q6_K_block(superblock: np.ndarray) -> np.ndarray:
+    superblock = np.ascontiguousarray(superblock, dtype=np.uint8)
+    assert superblock.size == Q6_K_BYTES
+    out = np.empty(256, dtype=np.float32)
+    lib().oracle_dequant_q6_K_block(_ptr(superblock), _ptr(out))
+    return out
+
+
 def dequant_q4_K_block(superblock: np.ndarray) -> np.ndarray:
     superblock = np.ascontiguousarray(superblock, dtype=np.uint8)
     out = np.empty(256, dtype=np.float32)
@@ -189,6 +219,17 @@ def block_dots_q5_K(x, w, M, N, K) -> np.ndarray:
     return out
 
 
+def group_dots_q6_K(x, w, M, N, K) -> np.ndarray:
+    """Q6_K: the exact dot of each 16-element scale group, codes centred (R23)."""
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    out = np.zeros((M, N, K // 16), dtype=np.int32)
+    rc = lib().oracle_group_dots_q6_K(_ptr(x), _ptr(w), _ptr(out), M, N, K)
+    if rc != 0:
+        raise ValueError(f"bad shape ({rc})")
+    return out
+
+
 def gemm_q8_0(x, w, M, N, K, nthreads: int = 0, rows=None) -> np.ndarray:
     """q8_1 activations x Q8_0 weights -> fp32 M x N (or the row range ``rows``)."""
     x = np.ascontiguousarray(x, dtype=np.uint8)
@@ -220,6 +261,18 @@ def gemm_q5_K(x, w, M, N, K, nthreads: int = 0, rows=None) -> np.ndarray:
     out = np.zeros((M, N), dtype=np.float32)
     m0, m1 = (0, M) if rows is None else rows
     rc = lib().oracle_gemm_q5_K_rows(_ptr(x), _ptr(w), _ptr(out), M, N, K, m0, m1, nthreads)
+    if rc < 0:
+        raise ValueError(f"bad shape ({rc})")
+    return out
+
+
+def gemm_q6_K(x, w, M, N, K, nthreads: int = 0, rows=None) -> np.ndarray:
+    """q8_1 activations x Q6_K weights -> fp32 M x N (or the row range ``rows``)."""
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    out = np.zeros((M, N), dtype=np.float32)
+    m0, m1 = (0, M) if rows is None else rows
+    rc = lib().oracle_gemm_q6_K_rows(_ptr(x), _ptr(w), _ptr(out), M, N, K, m0, m1, nthreads)
     if rc < 0:
         raise ValueError(f"bad shape ({rc})")
     return out

@@ -59,6 +59,19 @@
  *       Q4_K order; the 5-bit code of element e is its nibble plus 16 times
  *       bit e/32 of high-bit byte e%32.  Its block term is the Q4_K affine
  *       identity with 5-bit codes (0..31), computed as in R10-R11.
+ *   R22 Q6_K (a format the pages name among the K-quants; "When Does a
+ *       Kernel Win Surface?", section 4.1, reads its 16-element scale
+ *       groups and centres its 6-bit codes at 32; the GGUF layout is taken):
+ *       super-block (210 B, 256 values): [0,128) low four bits, [128,192)
+ *       high two bits, [192,208) int8 scales, [208,210) fp16 d.  Element e
+ *       (half h = e/128, quarter q = (e%128)/32, l = e%32) takes nibble q/2
+ *       (low nibble when q < 2) of byte 64h + 32(q%2) + l and bits 2q, 2q+1
+ *       of byte 128 + 32h + l; its 6-bit code c is low | high << 4, its
+ *       signed weight code c - 32, its scale the int8 byte 192 + e/16.
+ *   R23 Q6_K term per 16-element scale group g (two per 32-block, in
+ *       ascending order): I_g = exact dot of the 16 activation codes with
+ *       the codes c - 32, t = (d * sc_g) * (float)I_g (d * sc_g exact, one
+ *       rounding), acc = fmaf(activation_scale of the block, t, acc).
  *   R10 per block: t = weight_scale * (float)I (one rounding), then
  *       acc = fmaf(activation_scale, t, acc).
  *   R11 the Q4_K min term is acc = fmaf(-(dmin*m), f32(s16), acc), using
@@ -79,6 +92,8 @@
 #define Q8_0_BYTES 34
 #define Q4_K_BYTES 144
 #define Q5_K_BYTES 176
+#define Q6_K_BYTES 210
+#define QG 16            /* values per Q6_K scale group     */
 
 /* ------------------------------------------------------------------ */
 /* IEEE binary16 <-> binary32, written from the format definition.      */
@@ -291,6 +306,30 @@ static int q5k_code(const uint8_t *blk, int e)
 
 int oracle_q5k_code(const uint8_t *superblock, int e) { return q5k_code(superblock, e); }
 
+/* 6-bit code (0..63) of element e (0..255) of a Q6_K super-block (R22). */
+static int q6k_code(const uint8_t *blk, int e)
+{
+    int h = e / 128, q = (e % 128) / 32, l = e % 32;
+    uint8_t lb = blk[64 * h + 32 * (q % 2) + l];
+    int lo = (q < 2) ? (lb & 0x0f) : (lb >> 4);
+    int hi = (blk[128 + 32 * h + l] >> (2 * q)) & 3;
+    return lo | (hi << 4);
+}
+
+/* Scale (int8) of 16-element group g (0..15) of a Q6_K super-block. */
+static int q6k_scale(const uint8_t *blk, int g) { return (int)(int8_t)blk[192 + g]; }
+
+int oracle_q6k_code(const uint8_t *superblock, int e) { return q6k_code(superblock, e); }
+int oracle_q6k_scale(const uint8_t *superblock, int g) { return q6k_scale(superblock, g); }
+
+/* Dequantize one Q6_K super-block into 256 fp32 values (w = d*sc*(c-32)). */
+void oracle_dequant_q6_K_block(const uint8_t *blk, float *w)
+{
+    float d = oracle_f16_to_f32(rd16(blk + 208));
+    for (int e = 0; e < QK_K; e++)
+        w[e] = (d * (float)q6k_scale(blk, e / QG)) * (float)(q6k_code(blk, e) - 32);
+}
+
 /* Dequantize one Q4_K super-block into 256 fp32 values (w = d*sc*q - dmin*m). */
 void oracle_dequant_q4_K_block(const uint8_t *blk, float *w)
 {
@@ -374,6 +413,27 @@ int oracle_block_dots_q5_K(const uint8_t *x, const uint8_t *w, int32_t *dots,
                 for (int i = 0; i < QK; i++)
                     s += (int32_t)xq[i] * q5k_code(blk, (int)(b % 8) * QK + i);
                 dots[(m * N + n) * kb + b] = s;
+            }
+    return 0;
+}
+
+/* Q6_K: one dot per 16-element scale group (R23), the codes centred:
+ * dots[(m*N + n)*(K/16) + g] = sum_i xq[m, 16g+i] * (c[n, 16g+i] - 32). */
+int oracle_group_dots_q6_K(const uint8_t *x, const uint8_t *w, int32_t *dots,
+                           int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0 || K % QK_K != 0)
+        return -2;
+    int64_t kb = K / QK, nsb = K / QK_K, ng = K / QG;
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++)
+            for (int64_t g = 0; g < ng; g++) {
+                const int8_t *xq = (const int8_t *)(x + (m * kb + g / 2) * Q8_1_BYTES + 4) + QG * (g % 2);
+                const uint8_t *blk = w + (n * nsb + g / 16) * Q6_K_BYTES;
+                int32_t s = 0;
+                for (int i = 0; i < QG; i++)
+                    s += (int32_t)xq[i] * (q6k_code(blk, (int)(g % 16) * QG + i) - 32);
+                dots[(m * N + n) * ng + g] = s;
             }
     return 0;
 }
@@ -526,11 +586,55 @@ int oracle_gemm_q5_K(const uint8_t *x, const uint8_t *w, float *out,
     return oracle_gemm_q5_K_rows(x, w, out, M, N, K, 0, M, nthreads);
 }
 
+/* x: M x kb q8_1 blocks; w: N x (K/256) Q6_K super-blocks; out: M x N fp32.
+ * Per 32-block, its two 16-element scale groups in order (R22-R23). */
+int oracle_gemm_q6_K_rows(const uint8_t *x, const uint8_t *w, float *out,
+                          int64_t M, int64_t N, int64_t K, int64_t m0, int64_t m1,
+                          int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || K % QK_K != 0 || m0 < 0 || m1 > M || m0 > m1)
+        return -2;
+    int used = set_threads(nthreads);
+    int64_t kb = K / QK, nsb = K / QK_K;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = m0; m < m1; m++) {
+        for (int64_t n = 0; n < N; n++) {
+            float acc = 0.0f;
+            for (int64_t sb = 0; sb < nsb; sb++) {
+                const uint8_t *blk = w + (n * nsb + sb) * Q6_K_BYTES;
+                float d = oracle_f16_to_f32(rd16(blk + 208));
+                for (int j = 0; j < 8; j++) {
+                    const uint8_t *xb = x + (m * kb + sb * 8 + j) * Q8_1_BYTES;
+                    const int8_t *xq = (const int8_t *)(xb + 4);
+                    float xd = oracle_f16_to_f32(rd16(xb));
+                    for (int h = 0; h < 2; h++) {
+                        int g = 2 * j + h;
+                        int32_t I = 0;
+                        for (int i = 0; i < QG; i++)
+                            I += (int32_t)xq[QG * h + i] * (q6k_code(blk, g * QG + i) - 32);
+                        float ws = d * (float)q6k_scale(blk, g);   /* exact: 11 x 8 bits */
+                        float t = ws * (float)I;
+                        acc = fmaf(xd, t, acc);
+                    }
+                }
+            }
+            out[m * N + n] = acc;
+        }
+    }
+    return used;
+}
+
+int oracle_gemm_q6_K(const uint8_t *x, const uint8_t *w, float *out,
+                     int64_t M, int64_t N, int64_t K, int nthreads)
+{
+    return oracle_gemm_q6_K_rows(x, w, out, M, N, K, 0, M, nthreads);
+}
+
 /* Indexed MoE ("When Does a Kernel Win Surface?", section 4.5, the fused
  * indexed-MoE prefill GEMM): routed row r = t*topk + j of out is token t's q8_1 row
  * times the weights of expert ids[r], i.e. the dense GEMM row above with
  * that expert's N x K matrix; experts are stored one after another.
- * fmt 0 = Q8_0, 1 = Q4_K, 2 = Q5_K.  Rows [r0, r1) of out (T*topk x N) are
+ * fmt 0 = Q8_0, 1 = Q4_K, 2 = Q5_K, 3 = Q6_K.  Rows [r0, r1) of out (T*topk x N) are
  * written.
  * Returns the thread count used, -2 on a bad shape, -3 on an expert id out
  * of range. */
@@ -538,13 +642,14 @@ int oracle_moe_gemm(int fmt, const uint8_t *x, const uint8_t *w, const int32_t *
                     float *out, int64_t T, int64_t N, int64_t K, int n_experts,
                     int64_t r0, int64_t r1, int nthreads)
 {
-    if ((fmt != 0 && fmt != 1 && fmt != 2) || topk < 1 || n_experts < 1 || T < 0 || N < 0 || K < 0 ||
+    if (fmt < 0 || fmt > 3 || topk < 1 || n_experts < 1 || T < 0 || N < 0 || K < 0 ||
         K % (fmt == 0 ? QK : QK_K) != 0 || r0 < 0 || r1 > T * topk || r0 > r1)
         return -2;
     for (int64_t r = r0; r < r1; r++)
         if (ids[r] < 0 || ids[r] >= n_experts) return -3;
     const int64_t kb = K / QK;
-    const int64_t wrow = fmt == 0 ? kb * Q8_0_BYTES : (K / QK_K) * (fmt == 1 ? Q4_K_BYTES : Q5_K_BYTES);
+    const int64_t wrow = fmt == 0 ? kb * Q8_0_BYTES
+                       : (K / QK_K) * (fmt == 1 ? Q4_K_BYTES : fmt == 2 ? Q5_K_BYTES : Q6_K_BYTES);
     int used = set_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t r = r0; r < r1; r++) {
@@ -554,8 +659,10 @@ int oracle_moe_gemm(int fmt, const uint8_t *x, const uint8_t *w, const int32_t *
             oracle_gemm_q8_0_rows(xr, we, out + r * N, 1, N, K, 0, 1, 1);
         else if (fmt == 1)
             oracle_gemm_q4_K_rows(xr, we, out + r * N, 1, N, K, 0, 1, 1);
-        else
+        else if (fmt == 2)
             oracle_gemm_q5_K_rows(xr, we, out + r * N, 1, N, K, 0, 1, 1);
+        else
+            oracle_gemm_q6_K_rows(xr, we, out + r * N, 1, N, K, 0, 1, 1);
     }
     return used;
 }

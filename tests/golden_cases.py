@@ -89,3 +89,18 @@ def gemm_q5_K_case():
     w[0, 0, 16] = g["high_byte_0"]
     w[0, 0, 48:] = g["code"] | (g["code"] << 4)
     return x, w, K, g["out"]
+
+
+def gemm_q6_K_case():
+    """-> (x fp32 [1, K], w Q6_K bytes [1, 1, 210], K, expected out): uniform
+    low-bit and high-bit bytes, sixteen listed int8 scales, fp16 d."""
+    g = json.load(open(os.path.join(HERE, "gemm_hand.json")))["q6_K"]
+    K = g["K"]
+    x = np.zeros((1, K), np.float32)
+    x[0, ::16] = g["x_at_0_and_16_of_each_block"]
+    w = np.zeros((1, 1, 210), np.uint8)
+    w[0, 0, 0:128] = g["low_byte"]
+    w[0, 0, 128:192] = g["high_byte"]
+    w[0, 0, 192:208] = np.array(g["scales"], np.int8).view(np.uint8)
+    w[0, 0, 208:210] = np.array([g["d"]], "<f2").view(np.uint8)
+    return x, w, K, g["out"]

@@ -89,3 +89,26 @@ def dequant_q4_K(w) -> np.ndarray:
 def dequant_q8_1(x) -> np.ndarray:
     d, _, q = q8_1_fields(x)
     return (d[..., None] * q).reshape(x.shape[0], -1)
+
+
+def q6_K_fields(w):
+    """-> (d f64 [N,nsb], sc int64 [N,nsb,16], codes 0..63 int64 [N,nsb,256]).
+    Low bits: the 128 bytes @0 as [half 2][row 2][32]; quarter q of a half
+    takes row q%2, low nibble for q < 2 and high nibble for q >= 2.  High
+    bits: the 64 bytes @128 as [half 2][32]; quarter q takes bits 2q, 2q+1.
+    Scales: 16 int8 @192 (one per 16 elements); d: fp16 @208."""
+    ql = w[..., 0:128].astype(np.int64).reshape(w.shape[:-1] + (2, 2, 32))
+    qh = w[..., 128:192].astype(np.int64).reshape(w.shape[:-1] + (2, 32))
+    low = np.stack([ql[..., 0, :] & 15, ql[..., 1, :] & 15, ql[..., 0, :] >> 4, ql[..., 1, :] >> 4], axis=-2)
+    high = np.stack([(qh >> (2 * q)) & 3 for q in range(4)], axis=-2)        # [..., half, quarter, 32]
+    codes = (low + 16 * high).reshape(w.shape[:-1] + (256,))
+    sc = w[..., 192:208].view(np.int8).astype(np.int64)
+    return f16(w[..., 208:210]), sc, codes
+
+
+def dequant_q6_K(w) -> np.ndarray:
+    """-> f64 N x K: d*sc*(code - 32) (exact in fp64)."""
+    d, sc, codes = q6_K_fields(w)
+    N, nsb = d.shape
+    c = (codes - 32).reshape(N, nsb, 16, 16)
+    return ((d[..., None, None] * sc[..., None]) * c).reshape(N, -1)
