@@ -77,13 +77,14 @@ def make_inputs(cfg):
         M, N, K = (int(v) for v in shape.split("x"))
         sx, sw = inputs.seed_for(7, 1), inputs.seed_for(7, 2)
     x = inputs.activations(M, K, sx)
-    gen = {"q8_0": inputs.q8_0_weights, "q4_K": inputs.q4_K_weights, "q5_K": inputs.q5_K_weights}[fmt]
+    gen = {"q8_0": inputs.q8_0_weights, "q4_K": inputs.q4_K_weights, "q5_K": inputs.q5_K_weights,
+           "q6_K": inputs.q6_K_weights}[fmt]
     return fmt, M, N, K, x, gen(N, K, sw)
 
 
 def _fmt_code(fmt: str) -> int:
     import block_quantized_int8_q8_amd as mmq
-    return {"q8_0": mmq.FMT_Q8_0, "q4_K": mmq.FMT_Q4_K, "q5_K": mmq.FMT_Q5_K}[fmt]
+    return {"q8_0": mmq.FMT_Q8_0, "q4_K": mmq.FMT_Q4_K, "q5_K": mmq.FMT_Q5_K, "q6_K": mmq.FMT_Q6_K}[fmt]
 
 
 def time_config(cfg, steps: int, warmup: int, check: bool = True, cold: bool = False):
@@ -195,7 +196,7 @@ def check_parity(fmt, M, N, K, x, w, xq_dev, out_dev, full_rows: int = 2048):
     o = out_dev.cpu().numpy()
     rows = list(range(M)) if M <= full_rows else \
         sorted(set([0, M - 1, M // 2] + list(np.random.default_rng(0).integers(0, M, 5))))
-    f = {"q8_0": oracle.gemm_q8_0, "q4_K": oracle.gemm_q4_K, "q5_K": oracle.gemm_q5_K}[fmt]
+    f = {"q8_0": oracle.gemm_q8_0, "q4_K": oracle.gemm_q4_K, "q5_K": oracle.gemm_q5_K, "q6_K": oracle.gemm_q6_K}[fmt]
     t1 = time.perf_counter()
     ref = f(xq if len(rows) == M else np.ascontiguousarray(xq[rows]), w, len(rows), N, K, nthreads=threads)
     t2 = time.perf_counter()
@@ -376,7 +377,8 @@ def time_decode(M: int, fmt_name: str, steps: int, warmup: int, check: bool = Tr
 
     dev = torch.device("cuda:0")
     fmt = _fmt_code(fmt_name)
-    wgen = {"q8_0": inputs.q8_0_weights, "q4_K": inputs.q4_K_weights, "q5_K": inputs.q5_K_weights}[fmt_name]
+    wgen = {"q8_0": inputs.q8_0_weights, "q4_K": inputs.q4_K_weights, "q5_K": inputs.q5_K_weights,
+           "q6_K": inputs.q6_K_weights}[fmt_name]
     shapes = {g: (n, k) for g, n, k in inputs.LAYER_7B}
     groups = []
     for name, K, gemms in inputs.LAYER_INPUTS:
@@ -406,7 +408,8 @@ def time_decode(M: int, fmt_name: str, steps: int, warmup: int, check: bool = Tr
         import oracle
         from tests import metrics
         worst, unwritten = 0.0, 0
-        f = {mmq.FMT_Q8_0: oracle.gemm_q8_0, mmq.FMT_Q4_K: oracle.gemm_q4_K, mmq.FMT_Q5_K: oracle.gemm_q5_K}[fmt]
+        f = {mmq.FMT_Q8_0: oracle.gemm_q8_0, mmq.FMT_Q4_K: oracle.gemm_q4_K, mmq.FMT_Q5_K: oracle.gemm_q5_K,
+             mmq.FMT_Q6_K: oracle.gemm_q6_K}[fmt]
         for g in groups:
             xq = oracle.quantize_q8_1(g["x_host"])
             for n, w, o in zip(g["Ns"], g["w_host"], g["out"]):
@@ -484,7 +487,8 @@ def time_moe(fmt_name: str, steps: int, warmup: int, check: bool = True):
 
     dev = torch.device("cuda:0")
     fmt = _fmt_code(fmt_name)
-    wgen = {"q8_0": inputs.q8_0_weights, "q4_K": inputs.q4_K_weights, "q5_K": inputs.q5_K_weights}[fmt_name]
+    wgen = {"q8_0": inputs.q8_0_weights, "q4_K": inputs.q4_K_weights, "q5_K": inputs.q5_K_weights,
+           "q6_K": inputs.q6_K_weights}[fmt_name]
     E, topk0, T0 = inputs.MOE_SHAPE["n_experts"], inputs.MOE_SHAPE["topk"], inputs.MOE_T
     ids0 = inputs.moe_ids(T0, E, topk0, inputs.moe_seed("ids"))
     stream = torch.cuda.current_stream()
@@ -597,7 +601,7 @@ def cpu_baseline(cfg: int, target_s: float = 15.0):
     import oracle
     fmt, M, N, K, x, w = make_inputs(cfg)
     threads = min(16, os.cpu_count() or 1)
-    f = {"q8_0": oracle.gemm_q8_0, "q4_K": oracle.gemm_q4_K, "q5_K": oracle.gemm_q5_K}[fmt]
+    f = {"q8_0": oracle.gemm_q8_0, "q4_K": oracle.gemm_q4_K, "q5_K": oracle.gemm_q5_K, "q6_K": oracle.gemm_q6_K}[fmt]
     used = oracle.threads_used(threads)
 
     def run(rows, nthreads):
@@ -646,7 +650,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="benchmark shape (2: Q8_0 2048x3584x3584)")
     ap.add_argument("--extra-configs", default="3,4", help="other shapes timed in the same run")
-    ap.add_argument("--extra-shapes", default="q5_K:2048x18944x3584",
+    ap.add_argument("--extra-shapes", default="q5_K:2048x18944x3584,q6_K:2048x18944x3584",
                     help="fmt:MxNxK GEMMs timed in the same run ('' for none)")
     ap.add_argument("--layer-m", default="512,2048,8192",
                     help="token counts at which the 7B layer GEMM set is timed ('' for none)")

@@ -16,10 +16,11 @@ LIB_PATH = os.path.join(PKG, "libmmq.so")
 FMT_Q8_0 = 0
 FMT_Q4_K = 1
 FMT_Q5_K = 2
-Q8_1_BYTES, Q8_0_BYTES, Q4_K_BYTES, Q5_K_BYTES = 36, 34, 144, 176
+FMT_Q6_K = 3
+Q8_1_BYTES, Q8_0_BYTES, Q4_K_BYTES, Q5_K_BYTES, Q6_K_BYTES = 36, 34, 144, 176, 210
 
 EXPORTS = (
-    "mmq_quantize_q8_1", "mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_q5_K", "mmq_gemm_multi", "mmq_gemm_workspace_bytes",
+    "mmq_quantize_q8_1", "mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_q5_K", "mmq_gemm_q6_K", "mmq_gemm_multi", "mmq_gemm_workspace_bytes",
     "mmq_gemm_multi_ws", "mmq_moe_workspace_bytes",
     "mmq_moe_gemm", "mmq_moe_gemm_routed", "mmq_moe_gemm_noalloc", "mmq_debug_block_dots",
     "mmq_last_error", "mmq_plan_describe", "mmq_plan_for_limits",
@@ -44,7 +45,7 @@ def lib() -> ctypes.CDLL:
         p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.mmq_quantize_q8_1.argtypes = [p, p, i64, i64, p]
         L.mmq_quantize_q8_1.restype = i32
-        for name in ("mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_q5_K"):
+        for name in ("mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_q5_K", "mmq_gemm_q6_K"):
             getattr(L, name).argtypes = [p, p, p, i64, i64, i64, p]
             getattr(L, name).restype = i32
         L.mmq_gemm_multi.argtypes = [i32, p, i32, p, p, p, i64, i64, p]
@@ -96,8 +97,8 @@ def row_bytes(fmt, K) -> int:
     """Bytes of one weight row of K values in format ``fmt``."""
     if fmt == FMT_Q8_0:
         return (K // 32) * Q8_0_BYTES
-    if fmt in (FMT_Q4_K, FMT_Q5_K):
-        return (K // 256) * (Q4_K_BYTES if fmt == FMT_Q4_K else Q5_K_BYTES)
+    if fmt in (FMT_Q4_K, FMT_Q5_K, FMT_Q6_K):
+        return (K // 256) * {FMT_Q4_K: Q4_K_BYTES, FMT_Q5_K: Q5_K_BYTES, FMT_Q6_K: Q6_K_BYTES}[fmt]
     raise ValueError(f"unknown weight format {fmt}")
 
 
@@ -158,7 +159,8 @@ def _gemm(fn, name, xq, w, M, N, K, out, stream):
     return out
 
 
-_FN_FMT = {"mmq_gemm_q8_0": FMT_Q8_0, "mmq_gemm_q4_K": FMT_Q4_K, "mmq_gemm_q5_K": FMT_Q5_K}
+_FN_FMT = {"mmq_gemm_q8_0": FMT_Q8_0, "mmq_gemm_q4_K": FMT_Q4_K, "mmq_gemm_q5_K": FMT_Q5_K,
+           "mmq_gemm_q6_K": FMT_Q6_K}
 
 
 def gemm_q8_0(xq, w, M, N, K, out=None, stream=None):
@@ -176,9 +178,14 @@ def gemm_q5_K(xq, w, M, N, K, out=None, stream=None):
     return _gemm("mmq_gemm_q5_K", "mmq_gemm_q5_K", xq, w, M, N, K, out, stream)
 
 
+def gemm_q6_K(xq, w, M, N, K, out=None, stream=None):
+    """q8_1 [M, K/32, 36] x Q6_K [N, K/256, 210] -> fp32 [M, N]."""
+    return _gemm("mmq_gemm_q6_K", "mmq_gemm_q6_K", xq, w, M, N, K, out, stream)
+
+
 def gemm(fmt, xq, w, M, N, K, out=None, stream=None):
-    """The GEMM of weight format ``fmt`` (FMT_Q8_0, FMT_Q4_K or FMT_Q5_K)."""
-    f = {FMT_Q8_0: gemm_q8_0, FMT_Q4_K: gemm_q4_K, FMT_Q5_K: gemm_q5_K}[fmt]
+    """The GEMM of weight format ``fmt`` (FMT_Q8_0, FMT_Q4_K, FMT_Q5_K or FMT_Q6_K)."""
+    f = {FMT_Q8_0: gemm_q8_0, FMT_Q4_K: gemm_q4_K, FMT_Q5_K: gemm_q5_K, FMT_Q6_K: gemm_q6_K}[fmt]
     return f(xq, w, M, N, K, out, stream)
 
 
@@ -282,14 +289,16 @@ def moe_gemm_noalloc(fmt, xq, w, n_experts, ids, topk, T, N, K, out, stream=None
 
 
 def debug_block_dots(fmt, xq, w, M, N, K, dots=None, stream=None):
-    """Exact int32 block dots [M, N, K/32] through the GEMM's own staging and MFMA code."""
+    """Exact int32 block dots [M, N, K/32] through the GEMM's own staging and
+    MFMA code (Q6_K: [M, N, K/16], one per 16-element scale group)."""
     import torch
+    per = K // 16 if fmt == FMT_Q6_K else K // 32
     if dots is None:
-        dots = torch.empty((M, N, K // 32), dtype=torch.int32, device=xq.device)
+        dots = torch.empty((M, N, per), dtype=torch.int32, device=xq.device)
     if _dims_ok(M, N, K):
         _need(xq, torch.uint8, M * (K // 32) * Q8_1_BYTES, "xq (q8_1 activations)")
         _need(w, torch.uint8, N * row_bytes(fmt, K), "w (weights)")
-        _need(dots, torch.int32, M * N * (K // 32), "dots")
+        _need(dots, torch.int32, M * N * per, "dots")
     _check(lib().mmq_debug_block_dots(fmt, _ptr(xq), _ptr(w), _ptr(dots, torch.int32), M, N, K,
                                       _stream(stream)), "mmq_debug_block_dots")
     return dots

@@ -230,6 +230,11 @@ int mmq_gemm_q5_K(const void *x_q8_1, const void *w_q5_K, float *out, int64_t M,
     return gemm_common(mmq::FMT_Q5_K, x_q8_1, w_q5_K, out, M, N, K, false, stream);
 }
 
+int mmq_gemm_q6_K(const void *x_q8_1, const void *w_q6_K, float *out, int64_t M, int64_t N, int64_t K,
+                  void *stream) {
+    return gemm_common(mmq::FMT_Q6_K, x_q8_1, w_q6_K, out, M, N, K, false, stream);
+}
+
 int mmq_gemm_multi(int fmt, const void *x_q8_1, int count, const void *const *w, float *const *out,
                    const int64_t *N, int64_t M, int64_t K, void *stream) {
     return gemm_set(fmt, x_q8_1, count, w, reinterpret_cast<void *const *>(out), N, M, K, false, nullptr, 0,

@@ -2,7 +2,7 @@
 //
 //   k_quantize_q8_1   fp32 -> q8_1, one pass over the activations (HBM-bound)
 //   k_mmq<FMT, DOTS, MOE, SKIP, TAIL>
-//                     q8_1 x {Q8_0, Q4_K, Q5_K} -> fp32 (or the raw int32 block
+//                     q8_1 x {Q8_0, Q4_K, Q5_K, Q6_K} -> fp32 (or the raw int32 block
 //                     dots when DOTS), int8 MFMA with the per-block scale
 //                     applied in registers on the MFMA accumulator layout;
 //                     MOE gathers the rows of each expert's routed tokens;
@@ -237,8 +237,9 @@ struct Lds {
     static constexpr int A_CODES = KB * kBlockBytes;
     static constexpr int A_HDR = kTileM * KB * 4;                               // [row][4] (d, s) fp16 pairs
     static constexpr int B_CODES = KB * kBlockBytes;
-    static constexpr int B_SCALE = KB * kTileN * 8;                             // [4][col] (ws, cs) fp32
-    static constexpr int B_MIN = (FMT != FMT_Q8_0) ? kTileN * 2 * KB * 2 : 0;   // [col][g][4] fp16
+    // [4][col] (ws, cs) fp32 pairs; Q6_K: [8][col] ws of its 16-element groups
+    static constexpr int B_SCALE = KB * kTileN * 8;
+    static constexpr int B_MIN = has_min(FMT) ? kTileN * 2 * KB * 2 : 0;     // [col][g][4] fp16
     static constexpr int OFF_A_HDR = A_CODES;
     static constexpr int OFF_B_CODES = OFF_A_HDR + A_HDR;
     static constexpr int OFF_B_SCALE = OFF_B_CODES + B_CODES;
@@ -251,6 +252,7 @@ static_assert(KB == 4 && kTileM == 128 && kTileN == 128 && kThreads == 512 && kN
 static_assert(Lds<FMT_Q8_0>::TOTAL == lds_bytes_for(FMT_Q8_0), "plan and kernel LDS disagree");
 static_assert(Lds<FMT_Q4_K>::TOTAL == lds_bytes_for(FMT_Q4_K), "plan and kernel LDS disagree");
 static_assert(Lds<FMT_Q5_K>::TOTAL == lds_bytes_for(FMT_Q5_K), "plan and kernel LDS disagree");
+static_assert(Lds<FMT_Q6_K>::TOTAL == lds_bytes_for(FMT_Q6_K), "plan and kernel LDS disagree");
 static_assert(Lds<FMT_Q4_K>::OFF_B_CODES % 16 == 0 && Lds<FMT_Q4_K>::OFF_B_MIN % 16 == 0 &&
               Lds<FMT_Q4_K>::STEP % 16 == 0 &&
               Lds<FMT_Q8_0>::OFF_B_SCALE % 16 == 0 && Lds<FMT_Q8_0>::STEP % 16 == 0,
@@ -567,6 +569,75 @@ __device__ __forceinline__ void store_kquant(const Regs &r, uint8_t *buf, int ks
     }
 }
 
+// Q6_K ("When Does a Kernel Win Surface?", section 4.1: 6-bit codes centred
+// at 32, one scale per 16 elements), half `ks & 1` of super-block `ks / 2`:
+// 64 low-bit bytes (two rows of 32), 32 high-bit bytes, 8 scales and d.
+// Thread -> (column tid/4, t = tid%4): element positions l = 8t..8t+7 of all
+// four 32-element quarters q of the half, which take byte l of low-bit row
+// q%2 (its nibble q/2) and bits 2q, 2q+1 of high-bit byte l; and the two
+// scales of quarter t.  A 210-byte super-block starts 2 bytes off the dword
+// grid when its index is odd, so each 8-byte field is loaded as the three
+// dwords around it and realigned with v_perm; the codes are centred to
+// signed int8 (c - 32) at store time, once per workgroup, so the MFMA takes
+// them as they are and the term needs no bias.
+struct Q6KRegs {
+    uint32_t lo0[3], lo1[3], hi[3];   // low-bit rows 0 and 1, high bits: the dword windows
+    uint32_t sc, d;                   // the dwords holding the two scales and d
+};
+
+__device__ __forceinline__ int q6k_base(int wshift, int nsb, int col, int sb) { return wshift + (col * nsb + sb) * 210; }
+
+__device__ __forceinline__ void load_q6_K(__amdgpu_buffer_rsrc_t rw, int wshift, int nsb, int ks, int tid,
+                                          Q6KRegs &r) {
+    const int col = tid >> 2, t = tid & 3, half = ks & 1;
+    const int o = q6k_base(wshift, nsb, col, ks >> 1);
+    typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+    const u32x3 a = __builtin_amdgcn_raw_buffer_load_b96(rw, (o + 64 * half + 8 * t) & ~3, 0, 0);
+    const u32x3 b = __builtin_amdgcn_raw_buffer_load_b96(rw, (o + 64 * half + 32 + 8 * t) & ~3, 0, 0);
+    const u32x3 c = __builtin_amdgcn_raw_buffer_load_b96(rw, (o + 128 + 32 * half + 8 * t) & ~3, 0, 0);
+    r.lo0[0] = a.x; r.lo0[1] = a.y; r.lo0[2] = a.z;
+    r.lo1[0] = b.x; r.lo1[1] = b.y; r.lo1[2] = b.z;
+    r.hi[0] = c.x; r.hi[1] = c.y; r.hi[2] = c.z;
+    r.sc = __builtin_amdgcn_raw_buffer_load_b32(rw, (o + 192 + 8 * half + 2 * t) & ~3, 0, 0);
+    r.d = __builtin_amdgcn_raw_buffer_load_b32(rw, (o + 208) & ~3, 0, 0);
+}
+
+// 8 bytes starting `sh` (0 or 2) bytes into the 3-dword window w.
+__device__ __forceinline__ uint2 q6k_field(const uint32_t *w, int sh) {
+    const uint32_t sel = sh ? 0x05040302u : 0x03020100u;
+    return make_uint2(__builtin_amdgcn_perm(w[1], w[0], sel), __builtin_amdgcn_perm(w[2], w[1], sel));
+}
+
+// c - 32 in every byte of c (6-bit codes 0..63): set bit 7 so that the
+// subtraction cannot borrow across bytes, subtract, then flip bit 7 back.
+__device__ __forceinline__ uint32_t q6k_centre(uint32_t c) { return ((c | 0x80808080u) - 0x20202020u) ^ 0x80808080u; }
+
+__device__ __forceinline__ void store_q6_K(const Q6KRegs &r, uint8_t *buf, int wshift, int nsb, int ks, int tid) {
+    using L = Lds<FMT_Q6_K>;
+    uint8_t *sB = buf + L::OFF_B_CODES;
+    float *sW = reinterpret_cast<float *>(buf + L::OFF_B_SCALE);
+    const int col = tid >> 2, t = tid & 3, half = ks & 1;
+    const int o = q6k_base(wshift, nsb, col, ks >> 1);
+    const int sh = o & 2;   // every 8-byte field sits at o + a multiple of 4
+    const uint2 l0 = q6k_field(r.lo0, sh), l1 = q6k_field(r.lo1, sh), hb = q6k_field(r.hi, sh);
+    // positions 8t..8t+7: k-half t/2 of each block, bytes 8*(t%2).. of it
+    const int off = code_off(0, col, t >> 1) + 8 * (t & 1);
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const uint2 lb = (q & 1) ? l1 : l0;
+        const int ns = 4 * (q >> 1);
+        uint2 c;
+        c.x = ((lb.x >> ns) & 0x0F0F0F0Fu) | (((hb.x >> (2 * q)) & 0x03030303u) << 4);
+        c.y = ((lb.y >> ns) & 0x0F0F0F0Fu) | (((hb.y >> (2 * q)) & 0x03030303u) << 4);
+        *reinterpret_cast<uint2 *>(sB + off + q * kBlockBytes) = make_uint2(q6k_centre(c.x), q6k_centre(c.y));
+    }
+    // scales 2t, 2t+1 of the half: the groups of block t
+    const uint32_t sv = r.sc >> (8 * ((o + 192 + 8 * half + 2 * t) & 2));
+    const float d = h2f(r.d >> (8 * ((o + 208) & 2)));
+    sW[(2 * t) * kTileN + col] = d * (float)(int8_t)(sv & 0xffu);             // exact: 11 x 8 bits
+    sW[(2 * t + 1) * kTileN + col] = d * (float)(int8_t)((sv >> 8) & 0xffu);
+}
+
 template <int FMT>
 struct WRegs;
 template <>
@@ -575,6 +646,8 @@ template <>
 struct WRegs<FMT_Q4_K> { Q4KRegs r; };
 template <>
 struct WRegs<FMT_Q5_K> { Q5KRegs r; };
+template <>
+struct WRegs<FMT_Q6_K> { Q6KRegs r; };
 
 // One int8 MFMA at this point of the program.  The empty asm statements
 // redefine the operands just before it and its result just after it, so the
@@ -584,6 +657,15 @@ struct WRegs<FMT_Q5_K> { Q5KRegs r; };
 __device__ __forceinline__ i32x16 mfma_at(i32x4 &a, i32x4 &b, const i32x16 &c) {
     asm volatile("" : "+v"(a), "+v"(b));
     i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+    asm volatile("" : "+v"(d));
+    return d;
+}
+
+// Q6_K: one 16-element scale group, K = 16 (v_mfma_i32_32x32x16_i8: lane l
+// feeds row/column l%32 with the 8 codes 8*(l/32).. of the group).
+__device__ __forceinline__ i32x16 mfma16_at(long &a, long &b, const i32x16 &c) {
+    asm volatile("" : "+v"(a), "+v"(b));
+    i32x16 d = __builtin_amdgcn_mfma_i32_32x32x16_i8(a, b, c, 0, 0, 0);
     asm volatile("" : "+v"(d));
     return d;
 }
@@ -733,6 +815,11 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     const int b_col0 = kWaveN * wc + l32;            // this lane's B column in sub-tile 0
     const int a_lane = code_off(0, 32 * wr + l32, g); // fragment bases; blocks and sub-tiles
     const int b_lane = code_off(0, b_col0, g);        // are compile-time offsets from here
+    // Q6_K: 8-byte fragments of each 16-element group h (k-half h), lane
+    // group g taking its bytes 8g..8g+7; the two halves of a 32-byte row
+    // differ in bit 4 of the offset only
+    const int a6 = code_off(0, 32 * wr + l32, 0) + 8 * g;
+    const int b6 = code_off(0, b_col0, 0) + 8 * g;
     // the activation row whose scale this lane holds for the row broadcasts
     const int xs_row = 32 * wr + 8 * ((lane & 15) >> 2) + (lane & 3) + 4 * g;
     const ActDma adma = MOE ? act_dma_offsets_gather(kb, wv, lane, moe.sorted, mt.y, mt.z, moe.topk)
@@ -770,6 +857,8 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     auto load_w = [&](int k) {
         if constexpr (FMT == FMT_Q8_0)
             load_q8_0(rw, rwb.shift, kb, k, tid, wr_.r);
+        else if constexpr (FMT == FMT_Q6_K)
+            load_q6_K(rw, rwb.shift, K >> 8, k, tid, wr_.r);
         else if constexpr (FMT == FMT_Q4_K)
             load_q4_K(rw, K >> 8, k, tid, wr_.r);
         else
@@ -778,6 +867,8 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     auto store_w = [&](int k, uint8_t *buf) {
         if constexpr (FMT == FMT_Q8_0)
             store_q8_0(wr_.r, buf, rwb.shift, kb, k, tid);
+        else if constexpr (FMT == FMT_Q6_K)
+            store_q6_K(wr_.r, buf, rwb.shift, K >> 8, k, tid);
         else
             store_kquant<FMT>(wr_.r, buf, k, tid);
     };
@@ -839,7 +930,8 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
         float xsv[2];
         i32x4 fb[kRing];
         // Q8_0 reads the (ws, cs) pair; Q4_K, short of registers, reads ws
-        // alone and forms cs with one multiply (exact)
+        // alone and forms cs with one multiply (exact); Q6_K reads the ws of
+        // each 16-element group just before its MFMA
         using WsT = typename std::conditional<FMT == FMT_Q8_0, float2, float>::type;
         WsT fw[kRing];
         // Blocks of this step that exist (Q8_0 with K % 128 != 0: the last
@@ -849,7 +941,13 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
         // fma(0, 0, acc) = acc whatever those bytes were.
         const int nvalid = kb - ks * KB;   // wave-uniform, >= KB except in that last step
         auto load_a = [&](int b) {
-            fa[b & 1] = *reinterpret_cast<const i32x4 *>(buf + a_lane + b * kBlockBytes);
+            if constexpr (FMT == FMT_Q6_K) {
+                const uint2 f0 = *reinterpret_cast<const uint2 *>(buf + a6 + b * kBlockBytes);
+                const uint2 f1 = *reinterpret_cast<const uint2 *>(buf + (a6 ^ 16) + b * kBlockBytes);
+                fa[b & 1] = i32x4{int(f0.x), int(f0.y), int(f1.x), int(f1.y)};
+            } else {
+                fa[b & 1] = *reinterpret_cast<const i32x4 *>(buf + a_lane + b * kBlockBytes);
+            }
             if constexpr (!DOTS) {
                 const float xs = h2f(sHdr[(xs_row * KB + b) * 2]);
                 if constexpr (TAIL)
@@ -860,12 +958,21 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
         };
         auto load_b = [&](int st) {
             const int b = st / kNSub, c = st % kNSub;
-            fb[st % kRing] = *reinterpret_cast<const i32x4 *>(sB + b_lane + b * kBlockBytes + c * 32 * 32);
+            if constexpr (FMT == FMT_Q6_K) {
+                const uint2 f0 = *reinterpret_cast<const uint2 *>(sB + b6 + b * kBlockBytes + c * 32 * 32);
+                const uint2 f1 = *reinterpret_cast<const uint2 *>(sB + (b6 ^ 16) + b * kBlockBytes + c * 32 * 32);
+                fb[st % kRing] = i32x4{int(f0.x), int(f0.y), int(f1.x), int(f1.y)};
+            } else {
+                fb[st % kRing] = *reinterpret_cast<const i32x4 *>(sB + b_lane + b * kBlockBytes + c * 32 * 32);
+            }
             if constexpr (!DOTS) {
-                if constexpr (FMT == FMT_Q8_0)
+                if constexpr (FMT == FMT_Q8_0) {
                     fw[st % kRing] = sW[b * kTileN + b_col0 + 32 * c];
-                else
+                } else if constexpr (FMT == FMT_Q6_K) {
+                    // read where it is used (registers)
+                } else {
                     fw[st % kRing] = sW[b * kTileN + b_col0 + 32 * c].x;
+                }
             }
         };
         const bool live = !SKIP || FMT == FMT_Q8_0 || wave_live;   // wave-uniform
@@ -892,8 +999,33 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
                 if (st == 6) store_w(ks + 1, nxt);
             }
             if (!live) continue;
-            const i32x16 D = mfma_at(fa[b & 1], fb[st % kRing], srcC);
             const int col = b_col0 + 32 * c;
+            if constexpr (FMT == FMT_Q6_K) {
+                // the block's two 16-element groups, each with its own scale
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    float ws = 0.0f;
+                    if constexpr (!DOTS) ws = reinterpret_cast<const float *>(sW)[(2 * b + h) * kTileN + col];
+                    long fa6 = __builtin_bit_cast(long, make_uint2(uint32_t(fa[b & 1][2 * h]), uint32_t(fa[b & 1][2 * h + 1])));
+                    long fb6 = __builtin_bit_cast(long, make_uint2(uint32_t(fb[st % kRing][2 * h]),
+                                                                   uint32_t(fb[st % kRing][2 * h + 1])));
+                    const i32x16 D6 = mfma16_at(fa6, fb6, srcC);
+                    if constexpr (DOTS) {
+                        int32_t *dots = reinterpret_cast<int32_t *>(outp);
+                        const int n = n0 + col;
+#pragma unroll
+                        for (int r = 0; r < 16; r++) {
+                            const int m = m0 + 32 * wr + 8 * (r >> 2) + 4 * g + (r & 3);
+                            if (m < M && n < N)
+                                dots[(int64_t(m) * N + n) * (2 * kb) + 2 * (int64_t(ks) * KB + b) + h] = D6[r];
+                        }
+                    } else {
+                        scale_epilogue(acc[c], D6, ws, -kMagic * ws, xsv[b & 1]);
+                        asm volatile("" : "+v"(acc[c]));
+                    }
+                }
+            } else {
+            const i32x16 D = mfma_at(fa[b & 1], fb[st % kRing], srcC);
             if constexpr (DEFER) {
                 if (st == kSteps - 1) {   // its epilogue runs after the barrier
                     pendD = D;
@@ -920,8 +1052,9 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
                 // the epilogue happens here, not sunk to the end of the step
                 asm volatile("" : "+v"(acc[c]));
             }
+            }
         }
-        if constexpr (FMT != FMT_Q8_0 && !DOTS) if (live) {
+        if constexpr (has_min(FMT) && !DOTS) if (live) {
             // the min term of this step's four sub-blocks
             const _Float16 *sMin = reinterpret_cast<const _Float16 *>(buf + L::OFF_B_MIN);
             // A = the four block sums s (high halves of the row's headers)
@@ -1495,9 +1628,10 @@ static hipError_t launch_mv(const Plan &p, const GemmSet &set, const uint8_t *xb
             hipLaunchKernelGGL((k_mmv<FMT_Q8_0, MR>), grid, block, 0, stream, xb, set, int(M), int(K));
         else if (p.fmt == FMT_Q4_K)
             hipLaunchKernelGGL((k_mmv<FMT_Q4_K, MR>), grid, block, 0, stream, xb, set, int(M), int(K));
-        else
+        else if (p.fmt == FMT_Q5_K)
             hipLaunchKernelGGL((k_mmv<FMT_Q5_K, MR>), grid, block, 0, stream, xb, set, int(M), int(K));
     };
+    if (p.fmt != FMT_Q8_0 && p.fmt != FMT_Q4_K && p.fmt != FMT_Q5_K) return hipErrorInvalidValue;
     if (M == 1)
         go(std::integral_constant<int, 1>{});
     else if (M == 2)
@@ -1520,6 +1654,7 @@ const void *plan_kernel(const Plan &p, bool dots, bool moe) {
     auto pick = [&](auto fmt) -> const void * {
         constexpr int F = decltype(fmt)::value;
         if (p.kernel == KERNEL_MV) {
+            if constexpr (F == FMT_Q6_K) return nullptr;   // never planned: Q6_K has no matvec kernel
             if (p.tile_m == 1) return reinterpret_cast<const void *>(&k_mmv<F, 1>);
             if (p.tile_m == 2) return reinterpret_cast<const void *>(&k_mmv<F, 2>);
             if (p.tile_m <= 4) return reinterpret_cast<const void *>(&k_mmv<F, 4>);
@@ -1538,7 +1673,8 @@ const void *plan_kernel(const Plan &p, bool dots, bool moe) {
     };
     if (p.fmt == FMT_Q8_0) return pick(std::integral_constant<int, FMT_Q8_0>{});
     if (p.fmt == FMT_Q4_K) return pick(std::integral_constant<int, FMT_Q4_K>{});
-    return pick(std::integral_constant<int, FMT_Q5_K>{});
+    if (p.fmt == FMT_Q5_K) return pick(std::integral_constant<int, FMT_Q5_K>{});
+    return pick(std::integral_constant<int, FMT_Q6_K>{});
 }
 
 hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const void *x, const void *const *w,

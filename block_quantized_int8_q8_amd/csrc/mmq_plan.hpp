@@ -13,12 +13,16 @@
 
 namespace mmq {
 
-enum Fmt : int { FMT_Q8_0 = 0, FMT_Q4_K = 1, FMT_Q5_K = 2 };
+enum Fmt : int { FMT_Q8_0 = 0, FMT_Q4_K = 1, FMT_Q5_K = 2, FMT_Q6_K = 3 };
+
+// Super-block formats with an affine min term (Q4_K, Q5_K); Q6_K's codes are
+// centred instead and it has none.
+constexpr bool has_min(int fmt) { return fmt == FMT_Q4_K || fmt == FMT_Q5_K; }
 
 // Bytes of one weight row of K values (Q8_0: 34-byte blocks of 32; Q4_K /
-// Q5_K: 144- / 176-byte super-blocks of 256).
+// Q5_K / Q6_K: 144- / 176- / 210-byte super-blocks of 256).
 constexpr int64_t weight_row_bytes(int fmt, int64_t K) {
-    return fmt == FMT_Q8_0 ? (K / 32) * 34 : (K / 256) * (fmt == FMT_Q4_K ? 144 : 176);
+    return fmt == FMT_Q8_0 ? (K / 32) * 34 : (K / 256) * (fmt == FMT_Q4_K ? 144 : fmt == FMT_Q5_K ? 176 : 210);
 }
 
 // Geometry of the GEMM kernel (must match the kernel's compile-time tile).
@@ -53,13 +57,14 @@ constexpr int kMaxSplitAtomic = 2;
 
 // LDS bytes for the kernel's layouts: two k-step buffers, each with codes
 // block-major (32 B per block per row, no padding), the activation block
-// headers [row][4] as dwords, and the weight scale pairs [4][col] as two fp32;
-// the K-quants (Q4_K, Q5_K) add the split min operand [col][2][4] fp16 and
-// come to exactly 80 KiB, so two workgroups share a CU's 160 KiB.
+// headers [row][4] as dwords, and the weight scale pairs [4][col] as two fp32
+// (Q6_K: its eight 16-element group scales [8][col], one fp32 each, the same
+// bytes); Q4_K and Q5_K add the split min operand [col][2][4] fp16 and come
+// to exactly 80 KiB, so two workgroups share a CU's 160 KiB.
 constexpr int64_t lds_bytes_for(int fmt) {
     int64_t step = int64_t(kTileM + kTileN) * 32 * kBlocksPerStage + int64_t(kTileM) * kBlocksPerStage * 4 +
                    int64_t(kBlocksPerStage) * kTileN * 8;
-    if (fmt != FMT_Q8_0) step += int64_t(kTileN) * 2 * kBlocksPerStage * 2;
+    if (has_min(fmt)) step += int64_t(kTileN) * 2 * kBlocksPerStage * 2;
     return 2 * step;
 }
 
@@ -135,9 +140,9 @@ struct Plan {
 };
 constexpr int kSkipShare = 4;   // K-quants skip when idle wave rows >= 1/kSkipShare of all
 
-inline bool fmt_ok(int fmt) { return fmt == FMT_Q8_0 || fmt == FMT_Q4_K || fmt == FMT_Q5_K; }
+inline bool fmt_ok(int fmt) { return fmt == FMT_Q8_0 || fmt == FMT_Q4_K || fmt == FMT_Q5_K || fmt == FMT_Q6_K; }
 inline const char *fmt_name(int fmt) {
-    return fmt == FMT_Q8_0 ? "Q8_0" : fmt == FMT_Q4_K ? "Q4_K" : fmt == FMT_Q5_K ? "Q5_K" : "?";
+    return fmt == FMT_Q8_0 ? "Q8_0" : fmt == FMT_Q4_K ? "Q4_K" : fmt == FMT_Q5_K ? "Q5_K" : fmt == FMT_Q6_K ? "Q6_K" : "?";
 }
 
 // Shape checks shared by the quantize pass.  Returns nullptr when fine.
@@ -196,7 +201,8 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
     if (cu_count < 1) return fail("device reports no compute units");
     Plan q;
     q.fmt = fmt;
-    if (allow_mv && M <= kMvMaxM) {
+    // Q6_K has no matrix-vector kernel: its few-row shapes run the tile kernel
+    if (allow_mv && M <= kMvMaxM && fmt != FMT_Q6_K) {
         q.kernel = KERNEL_MV;
         q.tile_m = int(M);
         q.tile_n = 1;
@@ -281,7 +287,7 @@ inline bool make_plan_multi(int fmt, int64_t M, int count, const int64_t *Ns, in
     if (count < 1 || count > kMaxGemms) return fail("count must be 1..8 GEMMs");
     if (!Ns) return fail("null N array");
     // tile units: 128-column tiles for the MMQ kernel, single rows for the matvec kernel
-    const bool mv = allow_mv && M >= 1 && M <= kMvMaxM;
+    const bool mv = allow_mv && M >= 1 && M <= kMvMaxM && fmt != FMT_Q6_K;
     int64_t tiles = 0;
     for (int g = 0; g < count; g++) {
         Plan one;

@@ -64,6 +64,7 @@ extern "C" {
 #define MMQ_FMT_Q8_0 0
 #define MMQ_FMT_Q4_K 1
 #define MMQ_FMT_Q5_K 2
+#define MMQ_FMT_Q6_K 3
 
 /* Quantize fp32 activations to q8_1 ("13 . r7-r8 raw-byte MMQ kernel",
  * section 3.2; q8_1 fields from "When Does a Kernel Win Surface?", 6.2).
@@ -122,12 +123,31 @@ int mmq_gemm_q4_K(const void *x_q8_1, const void *w_q4_K, float *out,
 int mmq_gemm_q5_K(const void *x_q8_1, const void *w_q5_K, float *out,
                   int64_t M, int64_t N, int64_t K, void *stream);
 
+/* q8_1 activations x Q6_K weights -> fp32 (a K-quant the pages name with
+ * 16-element scale groups and 6-bit codes centred at 32: "When Does a Kernel
+ * Win Surface?", section 4.1).
+ *   x_q8_1: M x (K/32) q8_1 blocks; w_q6_K: N x (K/256) super-blocks of
+ *   210 B (128 B of low four bits @0, 64 B of high two bits @128, 16 int8
+ *   scales @192, fp16 d @208; element e, with h = e/128, q = (e%128)/32 and
+ *   l = e%32, takes nibble q/2 of byte 64h + 32(q%2) + l and bits 2q, 2q+1 of
+ *   byte 128 + 32h + l, and the scale byte 192 + e/16); out: M x N fp32
+ *   row-major, fully overwritten.  Requires K % 256 == 0.
+ * Per 16-element group (two per 32-block, in order) the weight scale d*sc
+ * multiplies the exact integer dot of the activation codes with the centred
+ * codes (code - 32) first (one rounding), and the activation scale of the
+ * block is then fused into the running sum: the same arithmetic, in the
+ * same order, as a single pass over the groups, so unsplit shapes are
+ * bit-identical to it.  Every M runs the tile kernel (there is no Q6_K
+ * matrix-vector kernel); split-K as for mmq_gemm_q8_0. */
+int mmq_gemm_q6_K(const void *x_q8_1, const void *w_q6_K, float *out,
+                  int64_t M, int64_t N, int64_t K, void *stream);
+
 /* Several GEMMs of one format that read the same q8_1 activations (the
  * layer pipeline of "13 . r7-r8 raw-byte MMQ kernel": quantize once per
  * distinct input, e.g. the q, k and v projections, or gate and up), computed
  * by one launch whose grid covers the column tiles of all of them (for
  * M <= 8, the output rows of all of them, in the matrix-vector kernel).
- *   fmt: MMQ_FMT_Q8_0, MMQ_FMT_Q4_K or MMQ_FMT_Q5_K; count: 1..8;
+ *   fmt: MMQ_FMT_Q8_0, MMQ_FMT_Q4_K, MMQ_FMT_Q5_K or MMQ_FMT_Q6_K; count: 1..8;
  *   x_q8_1: M x (K/32) q8_1 blocks, shared;
  *   w[g]: N[g] x K weights of format fmt; out[g]: M x N[g] fp32 row-major,
  *   fully overwritten; the arrays w, out and N are host memory (read during
@@ -180,7 +200,7 @@ int64_t mmq_moe_workspace_bytes(int64_t T, int topk, int n_experts);
  * by the weights of each of the topk experts it was routed to, all in one
  * launch, with every 128-row tile holding rows of a single expert.
  *   x_q8_1: T x (K/32) q8_1 blocks (device);
- *   fmt: MMQ_FMT_Q8_0, MMQ_FMT_Q4_K or MMQ_FMT_Q5_K;
+ *   fmt: MMQ_FMT_Q8_0, MMQ_FMT_Q4_K, MMQ_FMT_Q5_K or MMQ_FMT_Q6_K;
  *   w: n_experts weight matrices of format fmt stored one after another,
  *      each N x K (N rows of K/32 Q8_0 blocks or K/256 Q4_K / Q5_K
  *      super-blocks, the layout the dense GEMMs take) (device);
@@ -238,7 +258,9 @@ int mmq_moe_gemm_noalloc(int fmt, const void *x_q8_1, const void *w, int n_exper
 /* Test entry: the exact int32 block dots I[m,n,b] through the same staging
  * and matrix-core code as the tiled GEMM of format `fmt` (MMQ_FMT_Q8_0,
  * MMQ_FMT_Q4_K or MMQ_FMT_Q5_K; always the tile kernel, whatever M),
- * written to dots[(m*N + n)*(K/32) + b].  Same refusal rules as the GEMM. */
+ * written to dots[(m*N + n)*(K/32) + b].  MMQ_FMT_Q6_K gives one dot per
+ * 16-element scale group instead, with the codes centred (code - 32):
+ * dots[(m*N + n)*(K/16) + g].  Same refusal rules as the GEMM. */
 int mmq_debug_block_dots(int fmt, const void *x_q8_1, const void *w, int32_t *dots,
                          int64_t M, int64_t N, int64_t K, void *stream);
 

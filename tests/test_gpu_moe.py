@@ -32,7 +32,7 @@ def _dev(a):
 
 def _weights(fmt, E, N, K, seed):
     f = {mmq.FMT_Q8_0: inputs.q8_0_weights, mmq.FMT_Q4_K: inputs.q4_K_weights,
-         mmq.FMT_Q5_K: inputs.q5_K_weights}[fmt]
+         mmq.FMT_Q5_K: inputs.q5_K_weights, mmq.FMT_Q6_K: inputs.q6_K_weights}[fmt]
     return f(E * N, K, seed)   # E matrices of N rows, one after another
 
 
@@ -49,11 +49,11 @@ def _check(fmt, got, ref):
     rep = metrics.report(got, ref)
     _say(rep)
     assert rep["normalized_max_error"] <= metrics.TOL
-    if fmt == mmq.FMT_Q8_0:
+    if fmt in (mmq.FMT_Q8_0, mmq.FMT_Q6_K):
         assert rep["bit_identical_fraction"] == 1.0
 
 
-@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K, mmq.FMT_Q5_K])
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K, mmq.FMT_Q5_K, mmq.FMT_Q6_K])
 @pytest.mark.parametrize("T,E,topk,N,K,skew", [
     (37, 8, 3, 200, 512, 0.0),      # ragged N, several experts per tile row
     (300, 16, 4, 130, 1024, 2.0),   # skewed: popular experts span several 128-row tiles

@@ -77,11 +77,13 @@ def test_quantize_special_blocks():
 # ------------------------------------------------------------------ block dots
 
 def _weights(fmt, N, K, seed):
-    gen = {mmq.FMT_Q8_0: inputs.q8_0_weights, mmq.FMT_Q4_K: inputs.q4_K_weights, mmq.FMT_Q5_K: inputs.q5_K_weights}
+    gen = {mmq.FMT_Q8_0: inputs.q8_0_weights, mmq.FMT_Q4_K: inputs.q4_K_weights, mmq.FMT_Q5_K: inputs.q5_K_weights,
+           mmq.FMT_Q6_K: inputs.q6_K_weights}
     return gen[fmt](N, K, seed)
 
 
-FMTS = [mmq.FMT_Q8_0, mmq.FMT_Q4_K, mmq.FMT_Q5_K]
+FMTS = [mmq.FMT_Q8_0, mmq.FMT_Q4_K, mmq.FMT_Q5_K, mmq.FMT_Q6_K]
+MV_FMTS = [mmq.FMT_Q8_0, mmq.FMT_Q4_K, mmq.FMT_Q5_K]   # the formats with a matrix-vector kernel
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -90,11 +92,12 @@ def test_block_dots_bit_exact(fmt, M, N, K):
     _say(f"dots fmt={fmt} M={M} N={N} K={K}")
     x = inputs.q8_1_blocks(M, K, 10 + M)
     w = _weights(fmt, N, K, 20 + N)
-    dots = torch.full((M, N, K // 32), -(2 ** 31), dtype=torch.int32, device=DEV)
+    per = K // 16 if fmt == mmq.FMT_Q6_K else K // 32   # Q6_K: one dot per 16-element scale group
+    dots = torch.full((M, N, per), -(2 ** 31), dtype=torch.int32, device=DEV)
     mmq.debug_block_dots(fmt, _to_dev(x), _to_dev(w), M, N, K, dots)
     torch.cuda.synchronize()
     ref = {mmq.FMT_Q8_0: oracle.block_dots_q8_0, mmq.FMT_Q4_K: oracle.block_dots_q4_K,
-           mmq.FMT_Q5_K: oracle.block_dots_q5_K}[fmt](x, w, M, N, K)
+           mmq.FMT_Q5_K: oracle.block_dots_q5_K, mmq.FMT_Q6_K: oracle.group_dots_q6_K}[fmt](x, w, M, N, K)
     assert np.array_equal(dots.cpu().numpy(), ref)
 
 
@@ -110,7 +113,8 @@ def _run_gemm(fmt, xq, w, M, N, K):
 
 
 def _oracle_gemm(fmt, xq, w, M, N, K, rows=None):
-    f = {mmq.FMT_Q8_0: oracle.gemm_q8_0, mmq.FMT_Q4_K: oracle.gemm_q4_K, mmq.FMT_Q5_K: oracle.gemm_q5_K}[fmt]
+    f = {mmq.FMT_Q8_0: oracle.gemm_q8_0, mmq.FMT_Q4_K: oracle.gemm_q4_K, mmq.FMT_Q5_K: oracle.gemm_q5_K,
+         mmq.FMT_Q6_K: oracle.gemm_q6_K}[fmt]
     return f(xq, w, M, N, K, nthreads=16, rows=rows)
 
 
@@ -133,7 +137,7 @@ def test_gemm_matches_oracle(fmt, M, N, K):
     rep = metrics.report(got, ref)
     _say(rep)
     assert rep["normalized_max_error"] <= metrics.TOL
-    if fmt == mmq.FMT_Q8_0 and _split_k(fmt, M, N, K) == 1:
+    if fmt in (mmq.FMT_Q8_0, mmq.FMT_Q6_K) and _split_k(fmt, M, N, K) == 1:
         # one workgroup per output tile: the oracle's arithmetic in its order
         assert rep["bit_identical_fraction"] == 1.0
 
@@ -146,6 +150,15 @@ def _exact_and_scale(fmt, xq, w, M, N, K):
     sum of the absolute block terms, from the independent numpy decoders."""
     kb = K // 32
     xd, xs, xc = npdecode.q8_1_fields(xq.reshape(M, kb, 36))
+    if fmt == mmq.FMT_Q6_K:
+        # one term per 16-element group: weight scale d*sc, centred codes
+        d, sc, codes = npdecode.q6_K_fields(w.reshape(N, K // 256, -1))
+        ng = K // 16
+        I = np.matmul(xc.reshape(M, ng, 16).transpose(1, 0, 2).astype(np.float64),
+                      (codes - 32).reshape(N, ng, 16).transpose(1, 2, 0).astype(np.float64))
+        ws = (d[..., None] * sc).reshape(N, ng)
+        main = np.repeat(xd, 2, axis=1).T[:, :, None] * ws.T[:, None, :] * I
+        return main.sum(0), np.abs(main).sum(0)
     if fmt == mmq.FMT_Q8_0:
         wd, wc = npdecode.q8_0_fields(w.reshape(N, kb, 34))
     else:
@@ -453,7 +466,7 @@ def test_gemm_multi_unsplit_member_equals_single_launch():
     assert torch.equal(outs[0], single)
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", MV_FMTS)
 @pytest.mark.parametrize("M", [1, 2, 3, 8])
 @pytest.mark.parametrize("N,K", [(1, 256), (300, 768), (3584, 3584), (129, 18944)])
 def test_matvec_matches_oracle(fmt, M, N, K):
@@ -482,7 +495,7 @@ def test_matvec_boundary_m8_m9():
         assert rep["normalized_max_error"] <= metrics.TOL
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", MV_FMTS)
 @pytest.mark.parametrize("M,Ns,K", [(8, (257, 130, 33), 512), (5, (3, 1, 2), 256), (6, (1, 129), 18944)])
 def test_matvec_set_rows_straddling_members(fmt, M, Ns, K):
     """M >= 5 runs two output rows per wave, so with odd member widths a
@@ -505,7 +518,7 @@ def test_matvec_set_rows_straddling_members(fmt, M, Ns, K):
         _check_reordered(fmt, o, _oracle_gemm(fmt, xq, w, M, n, K), xq, w, M, n, K)
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", MV_FMTS)
 def test_matvec_layer_set_decode(fmt):
     """The 7B layer's projections at one token: q+k+v and gate+up through
     one matvec launch each, o and down alone; each member equal to its own
@@ -602,8 +615,9 @@ def test_device_plans_read_the_kernels_attributes(fmt):
     workgroups per CU (<= 128 VGPRs, no scratch, or they would be refused),
     the matvec kernels at least one."""
     import re
+    few = "mv" if fmt in MV_FMTS else "mmq"   # Q6_K runs its few-row shapes on the tile kernel
     for M, N, K, kern in [(2048, 3584, 3584, "mmq"), (2048, 18944, 3584, "mmq"), (96, 300, 512, "mmq"),
-                          (1, 3584, 3584, "mv"), (8, 4608, 3584, "mv")]:
+                          (1, 3584, 3584, few), (8, 4608, 3584, few)]:
         ok, desc = mmq.plan_describe(fmt, M, N, K)
         _say(desc)
         assert ok and f"kernel={kern}" in desc, desc
@@ -772,3 +786,42 @@ def test_q8_0_gemm_multi_any_whole_blocks():
         rep = metrics.report(o.cpu().numpy(), _oracle_gemm(mmq.FMT_Q8_0, xq, w, M, n, K))
         _say(rep)
         assert rep["bit_identical_fraction"] == 1.0
+
+
+# ------------------------------------------------------------------ Q6_K
+
+def test_q6_K_hand_case():
+    """The hand-summed fixture (tests/golden/gemm_hand.json, q6_K): one
+    super-block, sixteen scale groups, through the GPU quantize and GEMM."""
+    x, w, K, expect = golden_cases.gemm_q6_K_case()
+    xq = _gpu_quantize(x)
+    assert _run_gemm(mmq.FMT_Q6_K, xq, w, 1, 1, K)[0, 0] == expect
+    x9 = np.repeat(x, 9, axis=0)
+    assert (_run_gemm(mmq.FMT_Q6_K, _gpu_quantize(x9), w, 9, 1, K)[:, 0] == expect).all()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 37888, 3584), (8, 37888, 1024), (1000, 4608, 2304)])
+def test_q6_K_bit_identical(M, N, K):
+    """Unsplit shapes (more than 256 output tiles) apply each 16-element
+    group's scale in the oracle's arithmetic and order: every output
+    bit-identical (few rows included, which run the tile kernel for Q6_K)."""
+    _say(f"q6_K bit-identical M={M} N={N} K={K}")
+    assert _kernel(mmq.FMT_Q6_K, M, N, K) == "mmq" and _split_k(mmq.FMT_Q6_K, M, N, K) == 1
+    xq = oracle.quantize_q8_1(inputs.activations(M, K, 180 + M))
+    w = inputs.q6_K_weights(N, K, 181)
+    got = _run_gemm(mmq.FMT_Q6_K, xq, w, M, N, K)
+    ref = oracle.gemm_q6_K(xq, w, M, N, K, nthreads=16)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_q6_K_full_size_sampled_rows():
+    """Q6_K at the 7B up-projection shape (2048 x 18944 x 3584): sampled rows
+    bit-identical to the oracle, every element written."""
+    M, N, K = 2048, 18944, 3584
+    _say(f"q6_K full size M={M} N={N} K={K}")
+    xq = oracle.quantize_q8_1(inputs.activations(M, K, 190))
+    w = inputs.q6_K_weights(N, K, 191)
+    got = _run_gemm(mmq.FMT_Q6_K, xq, w, M, N, K)
+    rows = sorted(set([0, 1, M - 1, M - 128, M // 2] + list(np.random.default_rng(192).integers(0, M, 3))))
+    ref = oracle.gemm_q6_K(np.ascontiguousarray(xq[rows]), w, len(rows), N, K, nthreads=16)
+    assert np.array_equal(got[rows].view(np.uint32), ref.view(np.uint32))
