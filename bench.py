@@ -654,7 +654,7 @@ def main():
                     help="fmt:MxNxK GEMMs timed in the same run ('' for none)")
     ap.add_argument("--layer-m", default="512,2048,8192",
                     help="token counts at which the 7B layer GEMM set is timed ('' for none)")
-    ap.add_argument("--decode", default="q4_K:1,q8_0:1,q4_K:8",
+    ap.add_argument("--decode", default="q4_K:1,q8_0:1,q4_K:8,q6_K:1",
                     help="format:M pairs of the timed decode-size layer ('' for none)")
     ap.add_argument("--moe", default="q4_K,q8_0",
                     help="weight formats of the timed 128-expert MoE layer ('' for none)")

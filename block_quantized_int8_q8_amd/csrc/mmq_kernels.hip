@@ -1198,6 +1198,13 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
 // oracle's (t = fl(ws * I), then fma(xs, t, acc); Q4_K with its min term
 // per sub-block); only the order of the sum over blocks differs.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int dot4x4(const uint32_t *a, const uint32_t *b) {
+    int acc = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) acc = __builtin_amdgcn_sdot4(int(a[i]), int(b[i]), acc, false);
+    return acc;
+}
+
 __device__ __forceinline__ int dot8(const uint32_t *a, const uint32_t *b) {
     int acc = 0;
 #pragma unroll
@@ -1241,6 +1248,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 struct WUnit {
     uint32_t w0[8], w1[8];
     float ws0, ws1, dm0, dm1;
+    float ws2, ws3;   // Q6_K: ws0..ws3 are the scales of the unit's four 16-element groups
 };
 
 // K-quant unit u of a row: one 32-byte code group of super-block u/4 (low
@@ -1294,6 +1302,53 @@ __device__ __forceinline__ WUnit mv_load_kquant(__amdgpu_buffer_rsrc_t rw, int u
     return r;
 }
 
+// Q6_K unit u of a row (blocks 2u, 2u+1 = quarters 2p, 2p+1 of half n of
+// super-block u/4, p = u%2, n = (u/2)%2): low bits from nibble p of both
+// 32-byte low-bit rows of the half (row 0 for quarter 2p, row 1 for 2p+1),
+// high bits from bit pairs 2q of the half's 32 high-bit bytes, the four
+// group scales 192 + 8n + 4p.. and d.  The super-block starts `sh` (0 or 2)
+// bytes past the dword grid plus 2 bytes per odd index: each 32-byte field
+// is loaded as the 9 dwords around it and realigned with v_perm.
+__device__ __forceinline__ void q6k_window32(__amdgpu_buffer_rsrc_t rw, int f, uint32_t *out) {
+    const int a = f & ~3;
+    const u32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rw, a, 0, 0);
+    const u32x4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rw, a + 16, 0, 0);
+    const uint32_t v8 = __builtin_amdgcn_raw_buffer_load_b32(rw, a + 32, 0, 0);
+    const uint32_t w[9] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w, v8};
+    const uint32_t sel = (f & 2) ? 0x05040302u : 0x03020100u;
+#pragma unroll
+    for (int i = 0; i < 8; i++) out[i] = __builtin_amdgcn_perm(w[i + 1], w[i], sel);
+}
+
+__device__ __forceinline__ WUnit mv_load_q6k(__amdgpu_buffer_rsrc_t rw, int sh, int u) {
+    WUnit r;
+    const int sb = u >> 2, p = u & 1, n = (u >> 1) & 1;
+    const int o = sh + sb * 210;
+    uint32_t l0[8], l1[8], qh[8];
+    q6k_window32(rw, o + 64 * n, l0);
+    q6k_window32(rw, o + 64 * n + 32, l1);
+    q6k_window32(rw, o + 128 + 32 * n, qh);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const int fs = o + 192 + 8 * n + 4 * p, fd = o + 208;
+    const u32x2 sv = __builtin_amdgcn_raw_buffer_load_b64(rw, fs & ~3, 0, 0);
+    const uint32_t scw = __builtin_amdgcn_perm(sv.y, sv.x, (fs & 2) ? 0x05040302u : 0x03020100u);
+    const uint32_t dw = __builtin_amdgcn_raw_buffer_load_b32(rw, fd & ~3, 0, 0);
+    const float d = h2f((fd & 2) ? dw >> 16 : dw);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const uint32_t c0 = ((l0[i] >> (4 * p)) & 0x0F0F0F0Fu) | (((qh[i] >> (4 * p)) & 0x03030303u) << 4);
+        const uint32_t c1 = ((l1[i] >> (4 * p)) & 0x0F0F0F0Fu) | (((qh[i] >> (4 * p + 2)) & 0x03030303u) << 4);
+        r.w0[i] = ((c0 | 0x80808080u) - 0x20202020u) ^ 0x80808080u;   // c - 32 per byte
+        r.w1[i] = ((c1 | 0x80808080u) - 0x20202020u) ^ 0x80808080u;
+    }
+    r.ws0 = d * (float)(int8_t)(scw & 0xffu);           // exact: 11 x 8 bits
+    r.ws1 = d * (float)(int8_t)((scw >> 8) & 0xffu);
+    r.ws2 = d * (float)(int8_t)((scw >> 16) & 0xffu);
+    r.ws3 = d * (float)(int8_t)(scw >> 24);
+    r.dm0 = r.dm1 = 0.0f;
+    return r;
+}
+
 // One Q8_0 block from the 9 dwords at src, starting `off` (0 or 2) bytes in:
 // scale in the low or high half of dword 0, codes realigned by v_perm (bytes
 // 2..5 of each dword pair, or the upper dword whole).
@@ -1332,6 +1387,17 @@ __device__ __forceinline__ void mv_unit_terms(__amdgpu_buffer_rsrc_t rx, int M, 
         if (m < M) {
             const XPair x = load_x_pair(rx, (m * kb + 2 * u) * 36);
             const float xs0 = h2f(x.h0), xs1 = h2f(x.h1);
+            if constexpr (FMT == FMT_Q6_K) {
+                // one term per 16-element group, in order, each with its own scale
+#pragma unroll
+                for (int r = 0; r < RW; r++) {
+                    acc[r][m] = __builtin_fmaf(xs0, wu[r].ws0 * (float)dot4x4(wu[r].w0, x.c0), acc[r][m]);
+                    acc[r][m] = __builtin_fmaf(xs0, wu[r].ws1 * (float)dot4x4(wu[r].w0 + 4, x.c0 + 4), acc[r][m]);
+                    acc[r][m] = __builtin_fmaf(xs1, wu[r].ws2 * (float)dot4x4(wu[r].w1, x.c1), acc[r][m]);
+                    acc[r][m] = __builtin_fmaf(xs1, wu[r].ws3 * (float)dot4x4(wu[r].w1 + 4, x.c1 + 4), acc[r][m]);
+                }
+                continue;
+            }
 #pragma unroll
             for (int r = 0; r < RW; r++) {
                 const float t0 = wu[r].ws0 * (float)dot8(wu[r].w0, x.c0);
@@ -1428,7 +1494,12 @@ __global__ __launch_bounds__(kMvThreads) void k_mmv(const uint8_t *__restrict__ 
             }
         } else if (u < units) {
 #pragma unroll
-            for (int r = 0; r < RW; r++) wu[r] = mv_load_kquant<FMT>(rw[r], u);
+            for (int r = 0; r < RW; r++) {
+                if constexpr (FMT == FMT_Q6_K)
+                    wu[r] = mv_load_q6k(rw[r], sh[r], u);
+                else
+                    wu[r] = mv_load_kquant<FMT>(rw[r], u);
+            }
         }
         if (u < units) mv_unit_terms<FMT, MR, RW>(rx, M, kb, u, wu, acc, pair);
     }
@@ -1630,8 +1701,9 @@ static hipError_t launch_mv(const Plan &p, const GemmSet &set, const uint8_t *xb
             hipLaunchKernelGGL((k_mmv<FMT_Q4_K, MR>), grid, block, 0, stream, xb, set, int(M), int(K));
         else if (p.fmt == FMT_Q5_K)
             hipLaunchKernelGGL((k_mmv<FMT_Q5_K, MR>), grid, block, 0, stream, xb, set, int(M), int(K));
+        else
+            hipLaunchKernelGGL((k_mmv<FMT_Q6_K, MR>), grid, block, 0, stream, xb, set, int(M), int(K));
     };
-    if (p.fmt != FMT_Q8_0 && p.fmt != FMT_Q4_K && p.fmt != FMT_Q5_K) return hipErrorInvalidValue;
     if (M == 1)
         go(std::integral_constant<int, 1>{});
     else if (M == 2)
@@ -1654,7 +1726,6 @@ const void *plan_kernel(const Plan &p, bool dots, bool moe) {
     auto pick = [&](auto fmt) -> const void * {
         constexpr int F = decltype(fmt)::value;
         if (p.kernel == KERNEL_MV) {
-            if constexpr (F == FMT_Q6_K) return nullptr;   // never planned: Q6_K has no matvec kernel
             if (p.tile_m == 1) return reinterpret_cast<const void *>(&k_mmv<F, 1>);
             if (p.tile_m == 2) return reinterpret_cast<const void *>(&k_mmv<F, 2>);
             if (p.tile_m <= 4) return reinterpret_cast<const void *>(&k_mmv<F, 4>);

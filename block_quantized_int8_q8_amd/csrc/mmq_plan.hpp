@@ -201,8 +201,7 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
     if (cu_count < 1) return fail("device reports no compute units");
     Plan q;
     q.fmt = fmt;
-    // Q6_K has no matrix-vector kernel: its few-row shapes run the tile kernel
-    if (allow_mv && M <= kMvMaxM && fmt != FMT_Q6_K) {
+    if (allow_mv && M <= kMvMaxM) {
         q.kernel = KERNEL_MV;
         q.tile_m = int(M);
         q.tile_n = 1;
@@ -287,7 +286,7 @@ inline bool make_plan_multi(int fmt, int64_t M, int count, const int64_t *Ns, in
     if (count < 1 || count > kMaxGemms) return fail("count must be 1..8 GEMMs");
     if (!Ns) return fail("null N array");
     // tile units: 128-column tiles for the MMQ kernel, single rows for the matvec kernel
-    const bool mv = allow_mv && M >= 1 && M <= kMvMaxM && fmt != FMT_Q6_K;
+    const bool mv = allow_mv && M >= 1 && M <= kMvMaxM;
     int64_t tiles = 0;
     for (int g = 0; g < count; g++) {
         Plan one;

@@ -136,9 +136,9 @@ int mmq_gemm_q5_K(const void *x_q8_1, const void *w_q5_K, float *out,
  * multiplies the exact integer dot of the activation codes with the centred
  * codes (code - 32) first (one rounding), and the activation scale of the
  * block is then fused into the running sum: the same arithmetic, in the
- * same order, as a single pass over the groups, so unsplit shapes are
- * bit-identical to it.  Every M runs the tile kernel (there is no Q6_K
- * matrix-vector kernel); split-K as for mmq_gemm_q8_0. */
+ * same order, as a single pass over the groups, so unsplit tile-kernel
+ * shapes are bit-identical to it.  Split-K and M <= 8 (the matrix-vector
+ * kernel, one term per 16-element group) as for mmq_gemm_q8_0. */
 int mmq_gemm_q6_K(const void *x_q8_1, const void *w_q6_K, float *out,
                   int64_t M, int64_t N, int64_t K, void *stream);
 

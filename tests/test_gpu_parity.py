@@ -83,7 +83,6 @@ def _weights(fmt, N, K, seed):
 
 
 FMTS = [mmq.FMT_Q8_0, mmq.FMT_Q4_K, mmq.FMT_Q5_K, mmq.FMT_Q6_K]
-MV_FMTS = [mmq.FMT_Q8_0, mmq.FMT_Q4_K, mmq.FMT_Q5_K]   # the formats with a matrix-vector kernel
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -466,7 +465,7 @@ def test_gemm_multi_unsplit_member_equals_single_launch():
     assert torch.equal(outs[0], single)
 
 
-@pytest.mark.parametrize("fmt", MV_FMTS)
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M", [1, 2, 3, 8])
 @pytest.mark.parametrize("N,K", [(1, 256), (300, 768), (3584, 3584), (129, 18944)])
 def test_matvec_matches_oracle(fmt, M, N, K):
@@ -495,7 +494,7 @@ def test_matvec_boundary_m8_m9():
         assert rep["normalized_max_error"] <= metrics.TOL
 
 
-@pytest.mark.parametrize("fmt", MV_FMTS)
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,Ns,K", [(8, (257, 130, 33), 512), (5, (3, 1, 2), 256), (6, (1, 129), 18944)])
 def test_matvec_set_rows_straddling_members(fmt, M, Ns, K):
     """M >= 5 runs two output rows per wave, so with odd member widths a
@@ -518,7 +517,7 @@ def test_matvec_set_rows_straddling_members(fmt, M, Ns, K):
         _check_reordered(fmt, o, _oracle_gemm(fmt, xq, w, M, n, K), xq, w, M, n, K)
 
 
-@pytest.mark.parametrize("fmt", MV_FMTS)
+@pytest.mark.parametrize("fmt", FMTS)
 def test_matvec_layer_set_decode(fmt):
     """The 7B layer's projections at one token: q+k+v and gate+up through
     one matvec launch each, o and down alone; each member equal to its own
@@ -615,9 +614,8 @@ def test_device_plans_read_the_kernels_attributes(fmt):
     workgroups per CU (<= 128 VGPRs, no scratch, or they would be refused),
     the matvec kernels at least one."""
     import re
-    few = "mv" if fmt in MV_FMTS else "mmq"   # Q6_K runs its few-row shapes on the tile kernel
     for M, N, K, kern in [(2048, 3584, 3584, "mmq"), (2048, 18944, 3584, "mmq"), (96, 300, 512, "mmq"),
-                          (1, 3584, 3584, few), (8, 4608, 3584, few)]:
+                          (1, 3584, 3584, "mv"), (8, 4608, 3584, "mv")]:
         ok, desc = mmq.plan_describe(fmt, M, N, K)
         _say(desc)
         assert ok and f"kernel={kern}" in desc, desc
@@ -800,11 +798,11 @@ def test_q6_K_hand_case():
     assert (_run_gemm(mmq.FMT_Q6_K, _gpu_quantize(x9), w, 9, 1, K)[:, 0] == expect).all()
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 37888, 3584), (8, 37888, 1024), (1000, 4608, 2304)])
+@pytest.mark.parametrize("M,N,K", [(9, 37888, 3584), (100, 37888, 1024), (1000, 4608, 2304)])
 def test_q6_K_bit_identical(M, N, K):
-    """Unsplit shapes (more than 256 output tiles) apply each 16-element
-    group's scale in the oracle's arithmetic and order: every output
-    bit-identical (few rows included, which run the tile kernel for Q6_K)."""
+    """Unsplit tile-kernel shapes (more than 256 output tiles) apply each
+    16-element group's scale in the oracle's arithmetic and order: every
+    output bit-identical."""
     _say(f"q6_K bit-identical M={M} N={N} K={K}")
     assert _kernel(mmq.FMT_Q6_K, M, N, K) == "mmq" and _split_k(mmq.FMT_Q6_K, M, N, K) == 1
     xq = oracle.quantize_q8_1(inputs.activations(M, K, 180 + M))

@@ -324,13 +324,16 @@ def test_guard_refuses_kernels_that_spill(M):
 
 
 @pytest.mark.parametrize("M", [1, 8, 9, 2048])
-def test_q6_K_plans_the_tile_kernel(M):
-    """Q6_K (16-element scale groups, no min term): the Q8_0 LDS layout (the
-    group scales fill the scale area), whole super-blocks, and the tile
-    kernel at every M (it has no matrix-vector kernel)."""
+def test_q6_K_plans(M):
+    """Q6_K (16-element scale groups, no min term): the Q8_0 LDS layout for
+    the tile kernel (the group scales fill the scale area), the matvec for
+    M <= 8, whole super-blocks."""
     ok, desc = mmq.plan_for_limits(mmq.FMT_Q6_K, M, 18944, 3584, LDS_GFX950, 256)
-    assert ok and "kernel=mmq" in desc and "fmt=Q6_K" in desc, desc
-    assert int(re.search(r"lds=(\d+)", desc).group(1)) == 77824
+    assert ok and "fmt=Q6_K" in desc, desc
+    if M <= 8:
+        assert "kernel=mv" in desc, desc
+    else:
+        assert "kernel=mmq" in desc and int(re.search(r"lds=(\d+)", desc).group(1)) == 77824, desc
     ok, why = mmq.plan_for_limits(mmq.FMT_Q6_K, M, 300, 3584 + 32, LDS_GFX950, 256)
     assert not ok and "super-blocks" in why
     assert mmq.row_bytes(mmq.FMT_Q6_K, 3584) == 14 * 210
