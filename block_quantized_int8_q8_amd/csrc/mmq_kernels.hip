@@ -689,9 +689,29 @@ __device__ __forceinline__ void scale_epilogue(f32x16 &acc, const i32x16 &D, flo
 // rectangle of tiles (4 x 14 at 2048 x 3584) whose A rows and B columns its
 // L2 serves to all of them.  Measured: Q4_K 2-3 % faster with it; Q8_0 at
 // 2048 x 3584 x 3584 1.4 % faster, with 29 % fewer bytes fetched past L2.
-// The indexed-MoE launch keeps launch order (its row tiles come from the
-// routing table, spare entries last).
+// The indexed-MoE launch takes the same order over the row tiles its routing
+// filled (tile_in_rows).
 constexpr int kXcds = 8, kGroupRows = 4;
+// The same order over the first `gy` row tiles of the grid (the indexed MoE:
+// the row tiles its routing filled; the table's spare entries follow them).
+// Returns false for a workgroup past them, which has nothing to do: their
+// linear ids are the grid's last, so the real tiles still spread evenly over
+// the XCDs.
+__device__ __forceinline__ bool tile_in_rows(int gy, int &tx, int &ty) {
+    const int gx = gridDim.x, T = gx * gy;
+    const int L = blockIdx.y * gx + blockIdx.x;
+    if (L >= T) return false;
+    const int k = L % kXcds, q = L / kXcds;
+    const int base = T / kXcds, rem = T % kXcds;
+    const int n = k * base + min(k, rem) + q;          // bijective on [0, T)
+    const int group = n / (kGroupRows * gx);
+    const int rows = min(kGroupRows, gy - group * kGroupRows);
+    const int idx = n - group * kGroupRows * gx;
+    ty = group * kGroupRows + idx % rows;
+    tx = idx / rows;
+    return true;
+}
+
 template <bool REMAP>
 __device__ __forceinline__ void tile_of_workgroup(int &tx, int &ty) {
     if constexpr (!REMAP) {
@@ -739,7 +759,7 @@ struct GemmSet {
 // of the tile's expert (expert_bytes apart) and output row i of the tile is
 // routed row sorted[first + i].
 struct MoeArgs {
-    const int4 *header;   // (kMoeMagic, R, E, 0) when the tables below are this launch's
+    const int4 *header;   // (kMoeMagic, R, E, row tiles filled) when the tables below are this launch's
     const int4 *tiles;
     const int32_t *sorted;
     int topk;
@@ -778,8 +798,21 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wr = wv >> 1, wc = wv & 1;          // wave tile: rows 32*wr.., columns 64*wc..
     const int g = lane >> 5, l32 = lane & 31;
-    int tx, ty;
-    tile_of_workgroup<!MOE>(tx, ty);
+    int tx = 0, ty = 0;
+    int4 mh = {0, 0, 0, 0};
+    if constexpr (MOE) {
+        // tables built for other routed rows or experts (or never built):
+        // nothing is computed and nothing written
+        mh = *moe.header;
+        if (mh.x != kMoeMagic || mh.y != moe.R || mh.z != moe.E) return;
+        // XCD-aware order over the row tiles the routing filled (their count
+        // is the header's last field): an XCD's workgroups share the gathered
+        // activation rows of a group of row tiles and the experts' weight
+        // columns in its L2
+        if (!tile_in_rows(min(mh.w, int(gridDim.y)), tx, ty)) return;
+    } else {
+        tile_of_workgroup<true>(tx, ty);
+    }
     // which GEMM of the set this column tile belongs to (workgroup-uniform)
     int gi = 0;
     for (int i = 1; i < set.count; i++)
@@ -789,10 +822,6 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     const int N = set.N[gi];
     int4 mt = {0, 0, 0, 0};   // MoE row tile: expert, first sorted row, end of the expert's rows
     if constexpr (MOE) {
-        // tables built for other routed rows or experts (or never built):
-        // nothing is computed and nothing written
-        const int4 h = *moe.header;
-        if (h.x != kMoeMagic || h.y != moe.R || h.z != moe.E) return;
         mt = moe.tiles[ty];
         if (mt.x < 0) return;   // a spare row tile (workgroup-uniform)
         wq += int64_t(mt.x) * moe.expert_bytes;
@@ -1631,7 +1660,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__re
         for (int j = 0; j < kRouteIds; j++)
             if (valid(e[j])) sorted[atomicAdd(&cursor[e[j]], 1)] = base + j * kRouteThreads + tid;
     }
-    if (tid == 0) *header = make_int4(kMoeMagic, R, E, 0);
+    // last: the header, with the number of row tiles the table fills
+    if (tid == 0) *header = make_int4(kMoeMagic, R, E, tile_off[E]);
 }
 
 // Zero an fp32 array (the output of a split-K launch, before the slices add

@@ -327,7 +327,7 @@ constexpr int kMoeMaxTopk = 64;
 
 constexpr int64_t moe_max_tiles(int64_t R, int64_t E) { return R / kTileM + (E < R ? E : R); }
 
-// Workspace: a 16-byte header (kMoeMagic, R, E, 0) that the routing kernel
+// Workspace: a 16-byte header (kMoeMagic, R, E, row tiles filled) that the routing kernel
 // writes last, so that a later launch can check that the tables it reuses
 // were built for the same routed rows and experts; then the tile table; then
 // the sorted routed-row ids.
