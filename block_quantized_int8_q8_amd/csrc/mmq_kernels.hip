@@ -1548,6 +1548,108 @@ __global__ __launch_bounds__(kMvThreads) void k_mmv(const uint8_t *__restrict__ 
     }
 }
 
+// K-quant decode on the matrix core (the planner's choice for 2 <= M <= 8):
+// the matvec above spends 16 dot instructions per unit and activation row on
+// the VALU, so at M = 8 the VALU, not the weight stream, bounds it.  Here
+// one int8 MFMA per 32-block takes the activation rows as A (rows m, 8 of
+// its 32 used) and 32 weight rows as B: lane l holds weight row l%32 as its
+// D column, so its weight scale and min are single values, and D rows
+// 4(l/32) + r of registers r = 0..3 are the activation rows (the other 12
+// registers hold rows >= 8 and are never read).  The epilogue is the
+// oracle's per block (t = fl(ws * I), fma with the row's activation scale,
+// then the min term), a lane summing its rows' blocks in ascending order.
+// A workgroup of four waves takes 32 weight rows; wave w takes the w-th
+// quarter of the super-blocks, and the four partial sums are added in wave
+// order through LDS.
+template <int FMT>
+__global__ __launch_bounds__(kMvThreads) void k_mmvq(const uint8_t *__restrict__ xq, const GemmSet set, int M,
+                                                     int K) {
+    static_assert(FMT == FMT_Q4_K || FMT == FMT_Q5_K, "K-quant super-blocks with a min term");
+    static_assert(kMvThreads == 64 * kMvqSlices, "one K-slice per wave");
+    __shared__ float part[kMvqSlices][4][64];
+    static_assert(sizeof(part) == kMvqLds, "plan and kernel LDS disagree");
+    const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int total = set.tile_start[set.count];
+    const int row = int(blockIdx.x) * 32 + l32;   // this lane's weight row over the set
+    const bool live = row < total;
+    int gi = 0;
+    for (int i = 1; i < set.count; i++)
+        if (row >= set.tile_start[i]) gi = i;
+    const int n = row - set.tile_start[gi];
+    constexpr int SB = FMT == FMT_Q4_K ? 144 : 176, QS = FMT == FMT_Q4_K ? 16 : 48;
+    const int nsb = K >> 8, kb = K >> 5;
+    const uint8_t *wrow = set.w[gi] + int64_t(live ? n : 0) * nsb * SB;
+    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq, int64_t(M) * kb * 36);   // rows >= M read as zero
+    const int s0 = (nsb * wave) / kMvqSlices, s1 = (nsb * (wave + 1)) / kMvqSlices;
+    i32x16 srcC;
+#pragma unroll
+    for (int r = 0; r < 16; r++) srcC[r] = int(kMagicBits);
+    asm volatile("" : "+v"(srcC));
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const u32x4 zero = {0, 0, 0, 0};
+    for (int sb = s0; sb < s1; sb++) {
+        // every load of the super-block first (8 activation fragments and
+        // headers, 4 weight code chunks), then its 8 MFMAs and epilogues
+        const uint8_t *blk = wrow + int64_t(sb) * SB;
+        const u32x4 hd = live ? *reinterpret_cast<const u32x4 *>(blk) : zero;
+        u32x4 hb = zero;   // Q5_K: high-bit bytes 16h..16h+15 (element positions of this lane's k-half)
+        if constexpr (FMT == FMT_Q5_K) hb = live ? *reinterpret_cast<const u32x4 *>(blk + 16 + 16 * h) : zero;
+        u32x4 v[4];
+#pragma unroll
+        for (int grp = 0; grp < 4; grp++) v[grp] = live ? *reinterpret_cast<const u32x4 *>(blk + QS + 32 * grp + 16 * h) : zero;
+        i32x4 A[8];
+        uint32_t xh[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int b = 8 * sb + j;
+            A[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (l32 * kb + b) * 36 + 4 + 16 * h, 0, 0));
+            xh[j] = __builtin_amdgcn_raw_buffer_load_b32(rx, (l32 * kb + b) * 36, 0, 0);
+        }
+        const float d = h2f(hd.x), dmin = h2f(hd.x >> 16);
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int grp = j >> 1, t = j & 1;
+            i32x4 Bt;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                uint32_t c = t ? (v[grp][i] >> 4) & 0x0F0F0F0Fu : v[grp][i] & 0x0F0F0F0Fu;
+                if constexpr (FMT == FMT_Q5_K) c |= ((hb[i] >> j) & 0x01010101u) << 4;
+                Bt[i] = int(c);
+            }
+            // 6-bit scale and min of sub-block j (the K-quant packing)
+            const int sh = 8 * (j & 3);
+            const uint32_t b0 = (hd.y >> sh) & 0xffu, b1 = (hd.z >> sh) & 0xffu, b2 = (hd.w >> sh) & 0xffu;
+            const uint32_t sc = j < 4 ? (b0 & 63u) : ((b2 & 15u) | ((b0 >> 6) << 4));
+            const uint32_t mn = j < 4 ? (b1 & 63u) : ((b2 >> 4) | ((b1 >> 6) << 4));
+            const float ws = d * (float)sc, dm = dmin * (float)mn;   // exact
+            const i32x16 D = mfma_at(A[j], Bt, srcC);
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const uint32_t hr = uint32_t(__shfl(int(xh[j]), 4 * h + r, 64));   // row 4h + r's header
+                const float tv = __builtin_fmaf(__int_as_float(D[r]), ws, -kMagic * ws);   // fl(ws * I)
+                acc[r] = __builtin_fmaf(h2f(hr), tv, acc[r]);
+                acc[r] = __builtin_fmaf(-dm, h2f(hr >> 16), acc[r]);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; r++) part[wave][r][lane] = acc[r];
+    __syncthreads();
+    if (wave == 0 && live) {
+        float *out = reinterpret_cast<float *>(set.out[gi]);
+        const int N = set.N[gi];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int m = 4 * h + r;
+            float v = part[0][r][lane];
+#pragma unroll
+            for (int w = 1; w < kMvqSlices; w++) v += part[w][r][lane];
+            if (m < M) out[int64_t(m) * N + n] = v;
+        }
+    }
+}
+
 // Routing of the indexed MoE GEMM, one workgroup: count the routed rows of
 // each expert, scan the counts into row and tile offsets, scatter the routed
 // row ids into expert order and write the tile table (spare tiles: expert
@@ -1723,6 +1825,15 @@ static hipError_t launch_mv(const Plan &p, const GemmSet &set, const uint8_t *xb
                             hipStream_t stream) {
     const dim3 grid((unsigned)p.grid_x), block(kMvThreads);
     static_assert(kMvMaxM == 8, "the matvec launches below cover M = 1, 2, 3-4, 5-8");
+    if (p.mv_mfma) {
+        if (p.fmt == FMT_Q4_K)
+            hipLaunchKernelGGL((k_mmvq<FMT_Q4_K>), grid, block, 0, stream, xb, set, int(M), int(K));
+        else if (p.fmt == FMT_Q5_K)
+            hipLaunchKernelGGL((k_mmvq<FMT_Q5_K>), grid, block, 0, stream, xb, set, int(M), int(K));
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     auto go = [&](auto mr) {
         constexpr int MR = decltype(mr)::value;
         if (p.fmt == FMT_Q8_0)
@@ -1756,6 +1867,8 @@ const void *plan_kernel(const Plan &p, bool dots, bool moe) {
     auto pick = [&](auto fmt) -> const void * {
         constexpr int F = decltype(fmt)::value;
         if (p.kernel == KERNEL_MV) {
+            if constexpr (F == FMT_Q4_K || F == FMT_Q5_K)
+                if (p.mv_mfma) return reinterpret_cast<const void *>(&k_mmvq<F>);
             if (p.tile_m == 1) return reinterpret_cast<const void *>(&k_mmv<F, 1>);
             if (p.tile_m == 2) return reinterpret_cast<const void *>(&k_mmv<F, 2>);
             if (p.tile_m <= 4) return reinterpret_cast<const void *>(&k_mmv<F, 4>);

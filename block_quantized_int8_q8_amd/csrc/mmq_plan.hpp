@@ -82,6 +82,25 @@ constexpr int kMvWaves = kMvThreads / 64;
 // 128 us, Q8_0 168 -> 159 us; four or eight rows per wave were slower than
 // one (fewer resident waves), and at M = 3-4 two rows gained nothing.
 constexpr int mv_rows_per_wave(int64_t M) { return M >= 5 ? 2 : 1; }
+// Q4_K and Q5_K few-row shapes on the matrix core (k_mmvq: 32 weight rows
+// per workgroup, one MFMA per block): its time hardly grows with M, the
+// dot-product matvec's does, but it has a latency floor of ~9.5 us.
+// Measured on the 7B decode shapes (Q4_K, us, dot matvec -> matrix core):
+// 37888 rows x 3584 at M = 3: 33.0 -> 28.6, M = 4: 39.6 -> 28.6, M = 8:
+// 55.0 -> 30.8; 4608 rows at M = 5: 9.6 -> 9.7, M = 6: 10.6 -> 9.8; 3584
+// rows at M = 6: 8.6 -> 9.7, M = 8: 10.3 -> 9.6; at M = 2 it lost everywhere
+// (25.9 -> 29.1 on the 37888 rows).  K is capped: four K-slices per 32
+// weight rows leave a long-K launch with few rows too few waves (3584 x
+// 18944 at M = 8: 27.7 -> 30.6).
+constexpr int64_t kMvqMaxK = 8192;
+constexpr int kMvqRows = 32;   // weight rows per k_mmvq workgroup
+constexpr int kMvqSlices = 4;  // its waves, one K-slice each
+constexpr int64_t kMvqLds = int64_t(kMvqSlices) * 4 * 64 * 4;   // the slices' partial sums
+inline bool mv_on_mfma(int fmt, int64_t M, int64_t N, int64_t K) {
+    if (fmt != FMT_Q4_K && fmt != FMT_Q5_K) return false;
+    if (K > kMvqMaxK) return false;
+    return M >= 8 || (M >= 3 && N >= 16384);
+}
 
 // gfx950 register file: 512 registers per lane per SIMD (arch and
 // accumulation VGPRs together), allocated in granules of 8; at most 8 waves
@@ -135,6 +154,7 @@ struct Plan {
     // kBlocksPerStage blocks (a kernel variant of its own)
     bool tail = false;
     int mv_rows_per_wave = 0;   // matvec kernel: output rows per wave
+    bool mv_mfma = false;       // ... on the matrix core (k_mmvq: kMvqRows weight rows per workgroup)
     int wg_per_cu = 0;          // workgroups of the launched kernel resident per CU
     int kernel_vgprs = 0;       // its registers per lane
 };
@@ -207,10 +227,11 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
         q.tile_n = 1;
         q.threads = kMvThreads;
         q.blocks_per_stage = 2;
-        q.lds_bytes = extra_lds;
-        const int64_t rows_per_wg = int64_t(kMvWaves) * mv_rows_per_wave(M);
+        q.mv_mfma = mv_on_mfma(fmt, M, N, K);
+        q.lds_bytes = (q.mv_mfma ? kMvqLds : 0) + extra_lds;
+        const int64_t rows_per_wg = q.mv_mfma ? kMvqRows : int64_t(kMvWaves) * mv_rows_per_wave(M);
         q.grid_x = (N + rows_per_wg - 1) / rows_per_wg;
-        q.mv_rows_per_wave = mv_rows_per_wave(M);
+        q.mv_rows_per_wave = q.mv_mfma ? 0 : mv_rows_per_wave(M);
         q.grid_y = 1;
         q.k_steps = (K / 32 + 1) / 2;   // block pairs per row (an odd last block is a unit of its own)
         q.steps_per_split = q.k_steps;
@@ -376,12 +397,12 @@ inline void describe(const Plan &p, const Plan *ws, char *buf, size_t len) {
     int n = std::snprintf(buf, len,
                           "kernel=%s fmt=%s tile=%dx%d threads=%d blocks_per_stage=%d lds=%lld grid=%lldx%lld "
                           "k_steps=%lld split_k=%lld steps_per_split=%lld skip_idle_waves=%d mv_rows_per_wave=%d "
-                          "wg_per_cu=%d vgprs=%d tail=%d split_ws=%d",
+                          "wg_per_cu=%d vgprs=%d tail=%d split_ws=%d mv_mfma=%d",
                           p.kernel == KERNEL_MV ? "mv" : "mmq", fmt_name(p.fmt), p.tile_m, p.tile_n, p.threads,
                           p.blocks_per_stage, (long long)p.lds_bytes, (long long)p.grid_x, (long long)p.grid_y,
                           (long long)p.k_steps, (long long)p.split_k, (long long)p.steps_per_split,
                           int(p.skip_idle_waves), p.mv_rows_per_wave, p.wg_per_cu, p.kernel_vgprs, int(p.tail),
-                          int(p.split_ws));
+                          int(p.split_ws), int(p.mv_mfma));
     if (ws && n > 0 && size_t(n) < len)
         std::snprintf(buf + n, len - size_t(n), " ws_split_k=%lld ws_steps_per_split=%lld ws_bytes=%lld",
                       (long long)ws->split_k, (long long)ws->steps_per_split, (long long)split_workspace_bytes(*ws));

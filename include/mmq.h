@@ -106,7 +106,12 @@ int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out,
  * through the q8_1 block-sum field).
  *   x_q8_1: M x (K/32) q8_1 blocks; w_q4_K: N x (K/256) super-blocks;
  *   out: M x N fp32 row-major, fully overwritten.  Requires K % 256 == 0.
- * Split-K and M <= 8 shapes behave as for mmq_gemm_q8_0. */
+ * Split-K and M <= 8 shapes behave as for mmq_gemm_q8_0, except that with
+ * K <= 8192 and either M = 8 or 3 <= M and N >= 16384 the few rows run on
+ * the matrix core instead (mmq_plan_describe reports mv_mfma=1): one int8
+ * MFMA per block over 32 weight rows, the activation rows as its other
+ * operand, each output summed by one lane over a quarter of the blocks in
+ * ascending order and the four quarters then added in order. */
 int mmq_gemm_q4_K(const void *x_q8_1, const void *w_q4_K, float *out,
                   int64_t M, int64_t N, int64_t K, void *stream);
 
@@ -152,8 +157,11 @@ int mmq_gemm_q6_K(const void *x_q8_1, const void *w_q6_K, float *out,
  *   w[g]: N[g] x K weights of format fmt; out[g]: M x N[g] fp32 row-major,
  *   fully overwritten; the arrays w, out and N are host memory (read during
  *   the call), the tensors device memory.
- * Each out[g] equals what mmq_gemm_q8_0 / _q4_K / _q5_K would write for
- * (x, w[g], N[g]), except that split-K is decided for the set as a whole.
+ * Each out[g] equals what mmq_gemm_q8_0 / _q4_K / _q5_K / _q6_K would write
+ * for (x, w[g], N[g]), except that split-K, and for M <= 8 the choice between
+ * the two few-row kernels (Q4_K, Q5_K), are decided for the set as a whole
+ * (the summation order, and so the last bits, can then differ from the
+ * member's own launch).
  * Refused (nothing launched) when any member would be refused. */
 int mmq_gemm_multi(int fmt, const void *x_q8_1, int count, const void *const *w, float *const *out,
                    const int64_t *N, int64_t M, int64_t K, void *stream);

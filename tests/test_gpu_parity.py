@@ -823,3 +823,21 @@ def test_q6_K_full_size_sampled_rows():
     rows = sorted(set([0, 1, M - 1, M - 128, M // 2] + list(np.random.default_rng(192).integers(0, M, 3))))
     ref = oracle.gemm_q6_K(np.ascontiguousarray(xq[rows]), w, len(rows), N, K, nthreads=16)
     assert np.array_equal(got[rows].view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q4_K, mmq.FMT_Q5_K])
+@pytest.mark.parametrize("M,N,K", [(3, 16500, 2048), (5, 16417, 768), (7, 20000, 3584), (8, 333, 256)])
+def test_matvec_on_matrix_core(fmt, M, N, K):
+    """Few rows of a K-quant on the matrix core (mv_mfma=1): 32 weight rows
+    per workgroup, the activation rows as the MFMA's other operand, a
+    quarter of the blocks per wave.  Every output written, each within the
+    fp32 bound of the exact value and the 1e-5 normalized error (reading
+    R20); ragged N leaves a partial last group of 32 rows."""
+    import re
+    desc = mmq.plan_describe(fmt, M, N, K)[1]
+    assert "kernel=mv" in desc and "mv_mfma=1" in desc, desc
+    _say(f"matvec on matrix core fmt={fmt} M={M} N={N} K={K}")
+    xq = oracle.quantize_q8_1(inputs.activations(M, K, 200 + M))
+    w = _weights(fmt, N, K, 201)
+    got = _run_gemm(fmt, xq, w, M, N, K)
+    _check_reordered(fmt, got, _oracle_gemm(fmt, xq, w, M, N, K), xq, w, M, N, K)

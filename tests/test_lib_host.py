@@ -173,14 +173,20 @@ def test_moe_workspace_bytes_refuses(T, topk, E):
 def test_decode_sizes_plan_the_matvec_kernel(fmt, M, N, K):
     """M <= 8: the matvec kernel, four waves per 256-thread workgroup, one
     output row per wave for M <= 4 and two for M >= 5 (the wave's rows share
-    each activation load), no LDS, no split."""
+    each activation load), no LDS, no split; Q4_K at M = 8 (K <= 8192) on the
+    matrix core instead: 32 weight rows per workgroup, 4 KiB of LDS for its
+    four K-slices' partial sums."""
     ok, desc = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
     assert ok and "kernel=mv" in desc, desc
-    rows = 1 if M <= 4 else 2
-    assert f"mv_rows_per_wave={rows}" in desc, desc
     gx, gy = map(int, re.search(r"grid=(\d+)x(\d+)", desc).groups())
-    assert (gx, gy) == (-(-N // (4 * rows)), 1)
-    assert "threads=256" in desc and "lds=0" in desc and "split_k=1" in desc
+    assert "threads=256" in desc and "split_k=1" in desc
+    if fmt == mmq.FMT_Q4_K and (M == 8 or (M >= 3 and N >= 16384)) and K <= 8192:
+        assert "mv_mfma=1" in desc and "lds=4096" in desc, desc
+        assert (gx, gy) == (-(-N // 32), 1)
+    else:
+        rows = 1 if M <= 4 else 2
+        assert f"mv_rows_per_wave={rows}" in desc and "mv_mfma=0" in desc and "lds=0" in desc, desc
+        assert (gx, gy) == (-(-N // (4 * rows)), 1)
     # the same shape with one more row is tiled
     assert "kernel=mmq" in mmq.plan_for_limits(fmt, 9, N, K, LDS_GFX950, 256)[1]
 
