@@ -761,6 +761,7 @@ struct GemmSet {
 struct MoeArgs {
     const int4 *header;   // (kMoeMagic, R, E, row tiles filled) when the tables below are this launch's
     const int4 *tiles;
+    const int4 *small;    // small remainders (expert, first and end sorted row), header[1].x of them
     const int32_t *sorted;
     int topk;
     int R, E;
@@ -1650,10 +1651,380 @@ __global__ __launch_bounds__(kMvThreads) void k_mmvq(const uint8_t *__restrict__
     }
 }
 
+// ---------------------------------------------------------------------------
+// Small remainders of the indexed MoE: the routed rows of an expert past its
+// last full 128-row tile when there are at most kMoeSmallRows (32) of them.
+// As a row tile such a remainder holds a workgroup slot about as long as a
+// full tile (the weight staging and barriers of every k-step run for one
+// live wave of eight).  Here a workgroup of four waves takes 128 weight rows
+// of the expert over the whole of K, each wave 32 of them as the B operand
+// of a 32 x 32 x 32 int8 MFMA per block, the remainder's (gathered)
+// activation rows as A.
+//
+// Staging.  A vector load costs about one cycle per cache line its lanes
+// touch (measured on gfx950, cache-resident: ~57 cycles for 64 lanes over 32
+// rows, ~16 for 8 rows x 128 B or 1 KiB contiguous), so operands are not
+// loaded lane = row as the MFMA wants them: every 16-byte load takes 8
+// consecutive lanes along one row, by DMA into LDS (buffer_load ... lds),
+// and the fragments are read back from LDS.
+//   * activations, shared by the four waves: the 16-byte code halves of the
+//     k-chunk's 4 blocks for 32 rows, 8 units per row, unit (block j, half
+//     h) of row r in slot 8r + ((2j + h) xor (r mod 8)) (fragment reads of
+//     consecutive rows hit distinct banks), then the rows' block headers;
+//   * weights, per wave: the raw bytes of each of its 32 rows' k-chunk, as
+//     W_UNITS 16-byte units from the dword below the first byte (Q8_0 and
+//     Q6_K rows start 0 or 2 bytes off the dword grid; the fragment reads
+//     realign them with v_perm), row stride 16 * W_UNITS bytes, the wave's
+//     region padded to whole 64-lane DMA instructions.
+// K is walked in chunks of 4 blocks (128 values); two LDS stages alternate,
+// the next chunk's DMA issued before the current chunk's MFMAs.
+//
+// Grid: x = groups of 128 weight rows, y = the routing's list of small
+// remainders (workgroups past the list's length exit at once).  Listed
+// remainders, not experts, index the grid so that the live workgroups take
+// its first positions and spread evenly over the CUs.
+//
+// Epilogue.  Lane l's output register r holds remainder row 8(r/4) +
+// 4(l/32) + r%4, so register group r/4 holds rows 8(r/4)..8(r/4)+7: only
+// the ceil(cnt/8) groups that hold routed rows get the scale epilogue.
+//
+// The arithmetic and its order are the tile kernel's: t = fl(ws * I), the
+// row-broadcast FMA of the activation scale, blocks in ascending order (Q6_K:
+// a 32 x 32 x 16 MFMA per 16-element group), so Q8_0 and Q6_K rows are
+// bit-identical wherever the routing puts them.  The K-quants add their min
+// term per sub-block as the oracle does (fma(-dm, s, acc), again by row
+// broadcast), where the tile kernel adds it per k-step on a matrix core.
+// ---------------------------------------------------------------------------
+constexpr int kSmallThreads = 256, kSmallRowsPerWg = 128;
+
+template <int FMT>
+struct SmallLds {
+    // 16-byte units of one weight row's k-chunk
+    static constexpr int W_UNITS = FMT == FMT_Q8_0 ? 9 : FMT == FMT_Q4_K ? 5 : FMT == FMT_Q5_K ? 7 : 10;
+    static constexpr int W_ROW = 16 * W_UNITS;
+    static constexpr int W_DMA = (32 * W_UNITS + 63) / 64;   // DMA instructions per wave
+    static constexpr int W_WAVE = 1024 * W_DMA;              // a wave's rows, padded to whole instructions
+    static constexpr int A_CODES = 32 * 4 * 32;   // 32 rows x 4 blocks x 32 code bytes
+    static constexpr int OFF_HDR = A_CODES;       // 32 rows x 4 block headers
+    static constexpr int OFF_W = A_CODES + 32 * 4 * 4;
+    static constexpr int BYTES = OFF_W + 4 * W_WAVE;
+};
+static_assert(2 * SmallLds<FMT_Q6_K>::BYTES * 3 <= 160 * 1024 && 2 * SmallLds<FMT_Q8_0>::BYTES * 3 <= 160 * 1024,
+              "three small-remainder workgroups per CU");
+
+// Byte offset (from the workgroup's weight buffer) of 16-byte unit p of
+// weight row `row`'s k-chunk u, and that row's shift off the dword grid.
+template <int FMT>
+__device__ __forceinline__ int small_w_unit(int wshift, int kb, int row, int u, int p) {
+    if constexpr (FMT == FMT_Q8_0) {
+        return ((wshift + (row * kb + 4 * u) * 34) & ~3) + 16 * p;
+    } else if constexpr (FMT == FMT_Q6_K) {
+        const int a = (wshift + (row * (kb >> 3) + (u >> 1)) * 210) & ~3, hh = u & 1;
+        // low bits (64 B of half hh), high bits (32 B), then scales and d
+        return p < 5 ? a + 64 * hh + 16 * p : p < 8 ? a + 128 + 32 * hh + 16 * (p - 5) : a + 192 + 16 * (p - 8);
+    } else {
+        constexpr int SB = FMT == FMT_Q4_K ? 144 : 176, QS = FMT == FMT_Q4_K ? 16 : 48;
+        const int base = (row * (kb >> 3) + (u >> 1)) * SB, hs = u & 1;
+        if (p == 0) return base;                                            // d, dmin, scales
+        if (FMT == FMT_Q5_K && p < 3) return base + 16 + 16 * (p - 1);      // high bits
+        return base + QS + 64 * hs + 16 * (p - (FMT == FMT_Q5_K ? 3 : 1));  // code groups 2hs, 2hs+1
+    }
+}
+
+// Issue the DMA of k-chunk u into buffer buf: every thread one activation
+// code unit, every wave 64 block headers (waves 2 and 3 repeat waves 0 and
+// 1: the same bytes into the same slots), every wave its 32 weight rows (the
+// lanes past them reload the last unit into the padding).  Every DMA
+// instruction has all lanes active and every wave issues kSmallDmaOps of
+// them: the compiler's wait counts (and the pipeline's) rely on that count.
+// The weight units' source offsets are returned in wo: the caller keeps them
+// live until its compute is issued (a register the compute reused for an
+// LDS read would make the compiler wait for the DMA first).
+template <int FMT>
+struct SmallDmaOffs {
+    static constexpr int N = SmallLds<FMT>::W_DMA;
+    int v[N];
+};
+template <int FMT>
+constexpr int kSmallDmaOps = 2 + SmallDmaOffs<FMT>::N;
+
+
+template <int FMT>
+__device__ __forceinline__ void small_dma(__amdgpu_buffer_rsrc_t rx, int xcode, int xhdr,
+                                          __amdgpu_buffer_rsrc_t rw, int wshift, int kb, int wave, int lane,
+                                          int u, uint8_t *buf, SmallDmaOffs<FMT> &wo) {
+    using L = SmallLds<FMT>;
+    const int soff = u * 4 * 36;   // the chunk's 4 blocks
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + 1024 * wave), 16, xcode, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + L::OFF_HDR + 256 * (wave & 1)), 4, xhdr, soff, 0,
+                                             0);
+    constexpr int kUnits = 32 * L::W_UNITS;
+#pragma unroll
+    for (int i = 0; i < SmallDmaOffs<FMT>::N; i++) {
+        const int f = min(64 * i + lane, kUnits - 1);
+        wo.v[i] = small_w_unit<FMT>(wshift, kb, 32 * wave + f / L::W_UNITS, u, f % L::W_UNITS);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(buf + L::OFF_W + wave * L::W_WAVE + 1024 * i), 16,
+                                                 wo.v[i], 0, 0, 0);
+    }
+}
+
+// acc[R0 + i] += (xsv of lane R0 + i of this lane's 16-lane row) * t_i,
+// i = 0..3: one register group of the row-broadcast FMA (see
+// fmac_row_bcast8; the leading s_nop covers the VALU writes just before).
+#define MMQ_FMAC_BCAST4(R, A, T) "v_fmac_f32_dpp %" #A ", %8, %" #T " row_newbcast:" #R " row_mask:0xf bank_mask:0xf\n"
+template <int R0>
+__device__ __forceinline__ void fmac_row_bcast4(f32x16 &acc, float t0, float t1, float t2, float t3, float xsv) {
+    float a0 = acc[R0 + 0], a1 = acc[R0 + 1], a2 = acc[R0 + 2], a3 = acc[R0 + 3];
+#define MMQ_BCAST4_ASM(R0_, R1_, R2_, R3_)                                                                         \
+    asm volatile("s_nop 1\n" MMQ_FMAC_BCAST4(R0_, 0, 4) MMQ_FMAC_BCAST4(R1_, 1, 5) MMQ_FMAC_BCAST4(R2_, 2, 6)       \
+                     MMQ_FMAC_BCAST4(R3_, 3, 7)                                                                  \
+                 : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)                                                        \
+                 : "v"(t0), "v"(t1), "v"(t2), "v"(t3), "v"(xsv))
+    if constexpr (R0 == 0)
+        MMQ_BCAST4_ASM(0, 1, 2, 3);
+    else if constexpr (R0 == 4)
+        MMQ_BCAST4_ASM(4, 5, 6, 7);
+    else if constexpr (R0 == 8)
+        MMQ_BCAST4_ASM(8, 9, 10, 11);
+    else
+        MMQ_BCAST4_ASM(12, 13, 14, 15);
+#undef MMQ_BCAST4_ASM
+    acc[R0 + 0] = a0; acc[R0 + 1] = a1; acc[R0 + 2] = a2; acc[R0 + 3] = a3;
+}
+#undef MMQ_FMAC_BCAST4
+
+// The scale epilogue (t = fl(ws * I), acc += xs * t) of register group G.
+template <int G>
+__device__ __forceinline__ void small_epi_group(f32x16 &acc, const i32x16 &D, float ws, float cs, float xsv) {
+    fmac_row_bcast4<4 * G>(acc, __builtin_fmaf(__int_as_float(D[4 * G]), ws, cs),
+                           __builtin_fmaf(__int_as_float(D[4 * G + 1]), ws, cs),
+                           __builtin_fmaf(__int_as_float(D[4 * G + 2]), ws, cs),
+                           __builtin_fmaf(__int_as_float(D[4 * G + 3]), ws, cs), xsv);
+}
+
+// The scale epilogue of the first ng register groups (ng wave-uniform).
+__device__ __forceinline__ void small_epilogue(f32x16 &acc, const i32x16 &D, float ws, float cs, float xsv, int ng) {
+    small_epi_group<0>(acc, D, ws, cs, xsv);
+    if (ng > 1) small_epi_group<1>(acc, D, ws, cs, xsv);
+    if (ng > 2) small_epi_group<2>(acc, D, ws, cs, xsv);
+    if (ng > 3) small_epi_group<3>(acc, D, ws, cs, xsv);
+}
+
+// The K-quant min term of the first ng groups: acc[r] += s(row of r) * c,
+// the row's block sum s arriving by the same row broadcast as the scale.
+__device__ __forceinline__ void small_min(f32x16 &acc, float c, float sv, int ng) {
+    fmac_row_bcast4<0>(acc, c, c, c, c, sv);
+    if (ng > 1) fmac_row_bcast4<4>(acc, c, c, c, c, sv);
+    if (ng > 2) fmac_row_bcast4<8>(acc, c, c, c, c, sv);
+    if (ng > 3) fmac_row_bcast4<12>(acc, c, c, c, c, sv);
+}
+
+// LDS reads of the small kernel are written as one byte offset from the
+// buffer's base: the compiler's LDS lowering gives a read the alias scope of
+// its buffer only through a few levels of address arithmetic, and a read
+// without one waits for every LDS DMA in flight (the next chunk's included).
+template <typename T>
+__device__ __forceinline__ T lds_at(const uint8_t *buf, int off) {
+    return *reinterpret_cast<const T *>(buf + off);
+}
+
+// 8 bytes starting at byte b (even) of buf, from the three dwords around them.
+__device__ __forceinline__ uint2 lds_field8(const uint8_t *buf, int b) {
+    const int a = b & ~3;
+    const uint32_t sel = (b & 2) ? 0x05040302u : 0x03020100u;
+    const uint32_t w0 = lds_at<uint32_t>(buf, a), w1 = lds_at<uint32_t>(buf, a + 4), w2 = lds_at<uint32_t>(buf, a + 8);
+    return make_uint2(__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w2, w1, sel));
+}
+
+// The MFMAs and epilogues of k-chunk u from buffer buf, for this wave's 32 weight rows.
+template <int FMT>
+__device__ __forceinline__ void small_compute(const uint8_t *buf, f32x16 &acc, const i32x16 &srcC, int wshift, int kb,
+                                              int wave, int lane, int u, int ng) {
+    using L = SmallLds<FMT>;
+    const int l32 = lane & 31, g = lane >> 5;
+    const int xr = 8 * ((lane & 15) >> 2) + (lane & 3) + 4 * g;   // the row whose header this lane broadcasts
+    const int wr = L::OFF_W + wave * L::W_WAVE + l32 * L::W_ROW;   // this lane's weight row
+    const int hdr = L::OFF_HDR + 16 * xr;                          // its 4 block headers
+    auto a_unit = [&](int j, int h) { return 16 * (8 * l32 + ((2 * j + h) ^ (l32 & 7))); };
+    if constexpr (FMT == FMT_Q8_0) {
+        const int sh = (wshift + (32 * wave + l32) * kb * 34 + u * 4 * 34) & 3;   // the row's chunk start, 0 or 2
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            if (4 * u + j >= kb) break;   // wave-uniform: the row's last chunk may hold 1-3 blocks
+            const int b0 = wr + sh + 34 * j;   // the block's first byte
+            const float ws = h2f(lds_at<unsigned short>(buf, b0));
+            const uint2 c0 = lds_field8(buf, b0 + 2 + 16 * g), c1 = lds_field8(buf, b0 + 10 + 16 * g);
+            i32x4 bf = {int(c0.x), int(c0.y), int(c1.x), int(c1.y)};
+            i32x4 af = lds_at<i32x4>(buf, a_unit(j, g));
+            const i32x16 D = mfma_at(af, bf, srcC);
+            small_epilogue(acc, D, ws, -kMagic * ws, h2f(lds_at<uint32_t>(buf, hdr + 4 * j)), ng);
+            asm volatile("" : "+v"(acc));
+        }
+    } else if constexpr (FMT == FMT_Q6_K) {
+        const int hh = u & 1;
+        const int w6 = wr + ((wshift + ((32 * wave + l32) * (kb >> 3) + (u >> 1)) * 210) & 3);
+        // window offsets: low bits at 0, high bits at 80, scales and d at 128 (each from its dword)
+        const float d = h2f(lds_at<unsigned short>(buf, w6 + 128 + 16));
+        const uint2 hb[2] = {lds_field8(buf, w6 + 80 + 8 * g), lds_field8(buf, w6 + 80 + 16 + 8 * g)};
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const float xs = h2f(lds_at<uint32_t>(buf, hdr + 4 * q));
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const uint2 lb = lds_field8(buf, w6 + 32 * (q & 1) + 16 * h + 8 * g);
+                const int ns = 4 * (q >> 1);
+                const uint32_t c0 = ((lb.x >> ns) & 0x0F0F0F0Fu) | (((hb[h].x >> (2 * q)) & 0x03030303u) << 4);
+                const uint32_t c1 = ((lb.y >> ns) & 0x0F0F0F0Fu) | (((hb[h].y >> (2 * q)) & 0x03030303u) << 4);
+                long b6 = __builtin_bit_cast(long, make_uint2(q6k_centre(c0), q6k_centre(c1)));
+                long a6 = lds_at<long>(buf, a_unit(q, h) + 8 * g);
+                // scale of group 2q + h of the half: byte 192 + 8hh + 2q + h of the super-block
+                const float ws = d * (float)lds_at<int8_t>(buf, w6 + 128 + 8 * hh + 2 * q + h);
+                const i32x16 D6 = mfma16_at(a6, b6, srcC);
+                small_epilogue(acc, D6, ws, -kMagic * ws, xs, ng);
+                asm volatile("" : "+v"(acc));
+            }
+        }
+    } else {
+        const int hs = u & 1;
+        const u32x4 hd = lds_at<u32x4>(buf, wr);
+        const float d = h2f(hd.x), dmin = h2f(hd.x >> 16);
+        constexpr int C0 = FMT == FMT_Q5_K ? 48 : 16;   // the code groups' place in the row's window
+        // this lane's k-half of the row, an opaque offset: the high-bit and
+        // code reads would otherwise share address arithmetic deep enough to
+        // lose their alias scope (Q5_K)
+        int wq = wr + 16 * g;
+        asm volatile("" : "+v"(wq));
+        u32x4 qh = {0, 0, 0, 0};
+        if constexpr (FMT == FMT_Q5_K) qh = lds_at<u32x4>(buf, wq + 16);
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+            const int j = 4 * hs + jj;   // the sub-block within its super-block
+            const u32x4 v = lds_at<u32x4>(buf, wq + C0 + 32 * (jj >> 1));
+            i32x4 bf;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                uint32_t c = (jj & 1) ? (v[i] >> 4) & 0x0F0F0F0Fu : v[i] & 0x0F0F0F0Fu;
+                if constexpr (FMT == FMT_Q5_K) c |= ((qh[i] >> j) & 0x01010101u) << 4;
+                bf[i] = int(c);
+            }
+            // 6-bit scale and min of sub-block j (the K-quant packing)
+            const int s8 = 8 * (j & 3);
+            const uint32_t b0 = (hd.y >> s8) & 0xffu, b1 = (hd.z >> s8) & 0xffu, b2 = (hd.w >> s8) & 0xffu;
+            const uint32_t sc = j < 4 ? (b0 & 63u) : ((b2 & 15u) | ((b0 >> 6) << 4));
+            const uint32_t mn = j < 4 ? (b1 & 63u) : ((b2 >> 4) | ((b1 >> 6) << 4));
+            const float ws = d * (float)sc, dm = dmin * (float)mn;   // exact
+            i32x4 af = lds_at<i32x4>(buf, a_unit(jj, g));
+            const uint32_t xh = lds_at<uint32_t>(buf, hdr + 4 * jj);
+            const i32x16 D = mfma_at(af, bf, srcC);
+            small_epilogue(acc, D, ws, -kMagic * ws, h2f(xh), ng);
+            asm volatile("" : "+v"(acc));
+            small_min(acc, -dm, h2f(xh >> 16), ng);
+            asm volatile("" : "+v"(acc));
+        }
+    }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kSmallThreads) void k_moe_small(const uint8_t *__restrict__ xq,
+                                                             const uint8_t *__restrict__ w, float *__restrict__ out,
+                                                             int T, int N, int K, const MoeArgs moe) {
+    static_assert(kSmallThreads == 64 * (kSmallRowsPerWg / 32) && kMoeSmallRows == 32, "one wave per 32 weight rows");
+    using L = SmallLds<FMT>;
+    // The two stages as two variables, so that the compiler knows the DMA
+    // into one cannot write what the reads of the other return (see k_mmq).
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[L::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[L::BYTES];
+    // tables built for other routed rows or experts (or never built):
+    // nothing is computed and nothing written
+    const int4 mh = moe.header[0];
+    if (mh.x != kMoeMagic || mh.y != moe.R || mh.z != moe.E) return;
+    // the listed remainders take the grid's first rows, so that their
+    // workgroups spread evenly over the CUs; the rest exit (workgroup-
+    // uniform, before any barrier)
+    if (int(blockIdx.y) >= moe.header[1].x) return;
+    const int4 se = moe.small[blockIdx.y];
+    const int e = se.x;
+    const int2 rr = make_int2(se.y, se.z);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n0 = int(blockIdx.x) * kSmallRowsPerWg;   // the workgroup's first weight row
+    const int kb = K >> 5;
+    const int64_t wrow = weight_row_bytes(FMT, K);
+    // weight rows past N read as zero (scale 0) and are never stored
+    const WBuf rwb = weight_rsrc(w + int64_t(e) * moe.expert_bytes + int64_t(n0) * wrow, int64_t(N - n0) * wrow);
+    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq, int64_t(T) * kb * 36);
+    // this thread's activation DMA sources at chunk 0 (rows past the
+    // remainder read token 0 and are never stored)
+    int xcode, xhdr;
+    {
+        const int r = tid >> 3, q = (tid & 7) ^ (r & 7);
+        xcode = gathered_row(moe.sorted, rr.x, rr.y, moe.topk, r) * kb * 36 + (q >> 1) * 36 + 4 + 16 * (q & 1);
+        const int hi = 64 * ((tid >> 6) & 1) + lane;   // header slot: row hi / 4, block hi % 4
+        xhdr = gathered_row(moe.sorted, rr.x, rr.y, moe.topk, hi >> 2) * kb * 36 + (hi & 3) * 36;
+    }
+    const bool live = n0 + 32 * wave < N;   // wave-uniform: the wave has weight rows to compute
+    const int ng = (rr.y - rr.x + 7) >> 3;  // register groups holding routed rows (1..4)
+
+    i32x16 srcC;
+#pragma unroll
+    for (int r = 0; r < 16; r++) srcC[r] = int(kMagicBits);
+    asm volatile("" : "+v"(srcC));
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[r] = 0.0f;
+
+    // Two LDS stages: chunk u computes from stage u % 2 while the DMA of
+    // chunk u + 1 is in flight; at its end the wave waits for that DMA and
+    // the barrier makes every wave's part of it visible and frees stage
+    // u % 2 for chunk u + 2.  Every chunk issues its DMA and the loop runs an
+    // even number of chunks, the DMA index clamped to the last chunk (a
+    // reload from the cache into a stage nothing reads) and the compute
+    // skipped past it: with the DMA behind a branch the compiler's wait
+    // counts, unable to tell how many DMA were in flight, waited for the
+    // next chunk's too before reading the current one.  (Three stages, the
+    // DMA two chunks ahead, measured slower.)
+    const int nunits = (kb + 3) >> 2, last = nunits - 1;
+    {
+        SmallDmaOffs<FMT> wo;
+        small_dma<FMT>(rx, xcode, xhdr, rwb.r, rwb.shift, kb, wave, lane, 0, lds0, wo);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    auto chunk = [&](auto parity, int u) {
+        constexpr int P = decltype(parity)::value;
+        uint8_t *const cur = P ? lds1 : lds0;
+        uint8_t *const nxt = P ? lds0 : lds1;
+        SmallDmaOffs<FMT> wo;
+        small_dma<FMT>(rx, xcode, xhdr, rwb.r, rwb.shift, kb, wave, lane, min(u + 1, last), nxt, wo);
+        if (live && u < nunits) small_compute<FMT>(cur, acc, srcC, rwb.shift, kb, wave, lane, u, ng);
+#pragma unroll
+        for (int i = 0; i < SmallDmaOffs<FMT>::N; i++) asm volatile("" ::"v"(wo.v[i]));
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // chunk u + 1 has landed
+        __syncthreads();                                    // and no wave reads chunk u any more
+    };
+    for (int u = 0; u < nunits; u += 2) {
+        chunk(Parity<0>{}, u);
+        chunk(Parity<1>{}, u + 1);
+    }
+    if (!live) return;
+
+    // scatter: row m of the remainder -> routed row sorted[first + m] (the
+    // 16 ids loaded together, rows past the remainder clamped to its last)
+    const int g = lane >> 5, n = n0 + 32 * wave + (lane & 31), cnt = rr.y - rr.x;
+    int orow[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) orow[r] = moe.sorted[rr.x + min(8 * (r >> 2) + 4 * g + (r & 3), cnt - 1)];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+        const int m = 8 * (r >> 2) + 4 * g + (r & 3);
+        if (m < cnt && n < N) out[int64_t(orow[r]) * N + n] = acc[r];
+    }
+}
+
 // Routing of the indexed MoE GEMM, one workgroup: count the routed rows of
 // each expert, scan the counts into row and tile offsets, scatter the routed
 // row ids into expert order and write the tile table (spare tiles: expert
-// -1).  Rows with an id outside [0, E) join no expert.  Within an expert the
+// -1) and the table of small remainders.  Rows with an id outside [0, E) join no expert.  Within an expert the
 // order of rows depends on atomic timing; the GEMM's result does not (every
 // output row is computed on its own, in the same arithmetic wherever it sits).
 //
@@ -1676,8 +2047,10 @@ __device__ __forceinline__ void load_ids(const int32_t *__restrict__ ids, int R,
 
 __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__restrict__ ids, int R, int E,
                                                              int max_tiles, int4 *__restrict__ header,
-                                                             int4 *__restrict__ tiles, int32_t *__restrict__ sorted) {
+                                                             int4 *__restrict__ tiles, int4 *__restrict__ small,
+                                                             int32_t *__restrict__ sorted) {
     __shared__ int cnt[kMoeMaxExperts];
+    __shared__ int nsmall;
     __shared__ int cursor[kMoeMaxExperts];
     __shared__ int row_off[kMoeMaxExperts + 1];
     __shared__ int tile_off[kMoeMaxExperts + 1];
@@ -1690,6 +2063,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__re
     int e0[kRouteIds];
     load_ids(ids, R, 0, e0);
     for (int e = tid; e < E; e += kRouteThreads) cnt[e] = 0;
+    if (tid == 0) nsmall = 0;
     __syncthreads();
     auto valid = [&](int e) { return e >= 0 && e < E; };
 #pragma unroll
@@ -1703,15 +2077,17 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__re
             if (valid(e[j])) atomicAdd(&cnt[e[j]], 1);
     }
     __syncthreads();
-    // exclusive scan of (rows, tiles) per expert, packed as rows + tiles * 2^32
-    // (rows <= R < 2^31, so the low half never carries); thread t owns
-    // experts 2t and 2t + 1
+    // exclusive scan of (rows, row tiles) per expert, packed as rows + tiles
+    // * 2^32 (rows <= R < 2^31, so the low half never carries); thread t owns
+    // experts 2t and 2t + 1.  A last partial tile of at most kMoeSmallRows
+    // rows is no row tile: it goes to the remainder table.
     long long own[2], v = 0;
 #pragma unroll
     for (int j = 0; j < 2; j++) {
         const int e = 2 * tid + j;
         const int c = e < E ? cnt[e] : 0;
-        own[j] = (long long)c + ((long long)((c + kTileM - 1) / kTileM) << 32);
+        const int nt = c / kTileM + (c % kTileM > kMoeSmallRows ? 1 : 0);
+        own[j] = (long long)c + ((long long)nt << 32);
         v += own[j];
     }
     long long inc = v;   // inclusive scan within the wave
@@ -1741,14 +2117,20 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__re
         row_off[E] = int(ex & 0xffffffffLL);
         tile_off[E] = int(ex >> 32);
     }
-    // the tile table needs only this thread's own offsets and counts
+    // the tile table and the remainder list need only this thread's own
+    // offsets and counts (the list's order follows the LDS atomics; each
+    // entry is computed on its own, so the output does not depend on it)
 #pragma unroll
     for (int j = 0; j < 2; j++) {
         const int e = 2 * tid + j;
         const int c = int(own[j] & 0xffffffffLL), nt = int(own[j] >> 32);
-        if (e < E)
+        if (e < E) {
             for (int t = 0; t < nt; t++)
-                tiles[my_tile[j] + t] = make_int4(e, my_row[j] + kTileM * t, my_row[j] + c, 0);
+                tiles[my_tile[j] + t] =
+                    make_int4(e, my_row[j] + kTileM * t, my_row[j] + min(c, kTileM * (t + 1)), 0);
+            const int rem = c - kTileM * nt;   // 0..kMoeSmallRows rows left over
+            if (rem > 0) small[atomicAdd(&nsmall, 1)] = make_int4(e, my_row[j] + c - rem, my_row[j] + c, 0);
+        }
     }
     __syncthreads();
     for (int t = tile_off[E] + tid; t < max_tiles; t += kRouteThreads) tiles[t] = make_int4(-1, 0, 0, 0);
@@ -1762,8 +2144,12 @@ __global__ __launch_bounds__(kRouteThreads) void k_moe_route(const int32_t *__re
         for (int j = 0; j < kRouteIds; j++)
             if (valid(e[j])) sorted[atomicAdd(&cursor[e[j]], 1)] = base + j * kRouteThreads + tid;
     }
-    // last: the header, with the number of row tiles the table fills
-    if (tid == 0) *header = make_int4(kMoeMagic, R, E, tile_off[E]);
+    // last: the header, with the number of row tiles the table fills and
+    // the number of small remainders listed
+    if (tid == 0) {
+        header[1] = make_int4(nsmall, 0, 0, 0);
+        header[0] = make_int4(kMoeMagic, R, E, tile_off[E]);
+    }
 }
 
 // Zero an fp32 array (the output of a split-K launch, before the slices add
@@ -1891,6 +2277,14 @@ const void *plan_kernel(const Plan &p, bool dots, bool moe) {
     return pick(std::integral_constant<int, FMT_Q6_K>{});
 }
 
+// The small-remainder kernel of the indexed MoE for a weight format.
+const void *small_kernel(int fmt) {
+    if (fmt == FMT_Q8_0) return reinterpret_cast<const void *>(&k_moe_small<FMT_Q8_0>);
+    if (fmt == FMT_Q4_K) return reinterpret_cast<const void *>(&k_moe_small<FMT_Q4_K>);
+    if (fmt == FMT_Q5_K) return reinterpret_cast<const void *>(&k_moe_small<FMT_Q5_K>);
+    return reinterpret_cast<const void *>(&k_moe_small<FMT_Q6_K>);
+}
+
 hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const void *x, const void *const *w,
                        void *const *out, const int64_t *N, int64_t M, int64_t K, bool dots, void *workspace,
                        hipStream_t stream) {
@@ -1941,10 +2335,11 @@ hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t
     const int max_tiles = int(p.grid_y);
     int4 *header = reinterpret_cast<int4 *>(workspace);
     int4 *tiles = reinterpret_cast<int4 *>(reinterpret_cast<uint8_t *>(workspace) + kMoeHeaderBytes);
-    int32_t *sorted = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(tiles) + 16 * int64_t(max_tiles));
+    int4 *small = reinterpret_cast<int4 *>(reinterpret_cast<uint8_t *>(tiles) + 16 * int64_t(max_tiles));
+    int32_t *sorted = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(small) + moe_small_table_bytes(n_experts));
     if (ids)   // else: the tables a previous launch left in the workspace
         hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(kRouteThreads), 0, stream, ids, int(R), n_experts, max_tiles,
-                           header, tiles, sorted);
+                           header, tiles, small, sorted);
     GemmSet set{};
     set.count = 1;
     set.tile_start[0] = 0;
@@ -1957,6 +2352,7 @@ hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t
     MoeArgs moe;
     moe.header = header;
     moe.tiles = tiles;
+    moe.small = small;
     moe.sorted = sorted;
     moe.topk = topk;
     moe.R = int(R);
@@ -1967,7 +2363,14 @@ hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t
     const uint8_t *xb = reinterpret_cast<const uint8_t *>(x);
     int Ti = int(T), Ki = int(K), sps = int(p.steps_per_split);
     void *args[] = {&xb, &set, &Ti, &Ki, &sps, &moe};
-    const hipError_t e = hipLaunchKernel(plan_kernel(p, false, true), grid, block, args, 0, stream);
+    hipError_t e = hipLaunchKernel(plan_kernel(p, false, true), grid, block, args, 0, stream);
+    if (e != hipSuccess) return e;
+    // the small remainders: every expert may hold one
+    const dim3 sgrid((unsigned)((N + kSmallRowsPerWg - 1) / kSmallRowsPerWg), (unsigned)n_experts, 1);
+    const uint8_t *wb = reinterpret_cast<const uint8_t *>(w);
+    int Ni = int(N);
+    void *sargs[] = {&xb, &wb, &out, &Ti, &Ni, &Ki, &moe};
+    e = hipLaunchKernel(small_kernel(p.fmt), sgrid, dim3(kSmallThreads), sargs, 0, stream);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }

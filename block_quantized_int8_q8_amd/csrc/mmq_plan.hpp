@@ -340,29 +340,38 @@ inline int64_t split_workspace_bytes(const Plan &p) {
 // by the weights of expert ids[r].  The routed rows are grouped by expert
 // into 128-row tiles; every non-empty expert leaves at most one partial tile,
 // so floor(R / 128) + min(E, R) row tiles always suffice, and that is the
-// launch's grid y.  The workspace holds a header, the tile table (one int4
-// per row tile: expert, first sorted row, end of the expert's sorted rows,
-// unused) and the routed-row ids sorted by expert (int32 [R]).
+// tile launch's grid y.  An expert's last partial tile of at most
+// kMoeSmallRows rows is not a row tile: those rows go to the small-remainder
+// launch (32 weight rows per wave over the whole of K), whose grid y is E.
+// The workspace holds a header, the tile table (one int4 per row tile:
+// expert, first sorted row, end of the tile's rows, unused), the remainder
+// list (one int4 per expert with a small remainder, in no particular order:
+// expert, first and end sorted row, unused; their count is in the header)
+// and the routed-row ids sorted by expert (int32 [R]).
 constexpr int kMoeMaxExperts = 2048;   // the routing kernel keeps its per-expert tables in LDS
 constexpr int kMoeMaxTopk = 64;
+constexpr int kMoeSmallRows = 32;      // the rows of one MFMA operand
 
 constexpr int64_t moe_max_tiles(int64_t R, int64_t E) { return R / kTileM + (E < R ? E : R); }
 
-// Workspace: a 16-byte header (kMoeMagic, R, E, row tiles filled) that the routing kernel
-// writes last, so that a later launch can check that the tables it reuses
-// were built for the same routed rows and experts; then the tile table; then
-// the sorted routed-row ids.
-constexpr int kMoeMagic = 0x4d6f4531;   // "MoE1"
-constexpr int64_t kMoeHeaderBytes = 16;
+// Workspace: a 32-byte header ((kMoeMagic, R, E, row tiles filled), then
+// (small remainders listed, 0, 0, 0)) that the routing kernel writes last,
+// so that a later launch can check that the tables it reuses were built for
+// the same routed rows and experts; then the tile table; then the remainder
+// list; then the sorted routed-row ids.
+constexpr int kMoeMagic = 0x4d6f4532;   // "MoE2"
+constexpr int64_t kMoeHeaderBytes = 32;
+
+constexpr int64_t moe_small_table_bytes(int64_t E) { return 16 * E; }
 
 constexpr int64_t moe_workspace_bytes(int64_t R, int64_t E) {
     if (R < 0 || E < 0) return -1;
-    return kMoeHeaderBytes + 16 * moe_max_tiles(R, E) + ((4 * R + 15) / 16) * 16;
+    return kMoeHeaderBytes + 16 * moe_max_tiles(R, E) + moe_small_table_bytes(E) + ((4 * R + 15) / 16) * 16;
 }
 
 // The allocation-free MoE entry point keeps its routing tables in a static
 // device array sized for this many routed rows (T * topk) and the most
-// experts: 576 KiB per device.
+// experts: about 592 KiB per device.
 constexpr int64_t kNoAllocMaxRouted = 131072;
 constexpr int64_t kNoAllocScratchBytes = moe_workspace_bytes(kNoAllocMaxRouted, kMoeMaxExperts);
 

@@ -197,10 +197,12 @@ int mmq_gemm_multi_ws(int fmt, const void *x_q8_1, int count, const void *const 
                       void *stream);
 
 /* Bytes of device workspace mmq_moe_gemm needs for T tokens routed to topk
- * experts each among n_experts: a 16-byte header, a tile table (16 B per
+ * experts each among n_experts: a 32-byte header, a tile table (16 B per
  * possible 128-row tile, floor(T*topk/128) + min(n_experts, T*topk) of
- * them) and the routed row ids sorted by expert (4 B each).  -1 for arguments mmq_moe_gemm
- * refuses outright (topk outside 1..64, n_experts outside 1..2048, T < 0). */
+ * them), a list of small remainders (16 B per expert) and the routed row ids
+ * sorted by expert (4 B each, rounded up to 16 B).  -1 for arguments
+ * mmq_moe_gemm refuses outright (topk outside 1..64, n_experts outside
+ * 1..2048, T < 0). */
 int64_t mmq_moe_workspace_bytes(int64_t T, int topk, int n_experts);
 
 /* Indexed-MoE GEMM ("When Does a Kernel Win Surface?", section 4.5, the fused
@@ -218,14 +220,21 @@ int64_t mmq_moe_workspace_bytes(int64_t T, int topk, int n_experts);
  *   workspace: at least mmq_moe_workspace_bytes(T, topk, n_experts) bytes of
  *      16-byte aligned device memory, caller-owned; its contents on entry do
  *      not matter and on return are the routing tables.
- * Row r of out equals the tiled dense GEMM's row for token t and expert
- * ids[r]'s matrix (bit-identical for Q8_0: the same arithmetic in the same
- * order; the MoE launch always uses the 128 x 128 tile kernel, whatever T).  A routed row whose id is outside [0, n_experts) is not
- * computed and its row of out is left as it was.  The routing runs on the
- * device (a kernel on `stream` before the GEMM): the ids never visit the
- * host.  Requires K % 256 == 0, 1 <= topk <= 64, 1 <= n_experts <= 2048,
- * T*topk < 2^31 and x under 2 GiB.  Two calls on one stream may share a
- * workspace; calls that overlap in time may not. */
+ * An expert's routed rows fill 128-row tiles of the tile kernel, except a
+ * last partial tile of at most 32 rows, which a second launch computes one
+ * wave per 32 weight rows over the whole of K (so a decode-sized call, at
+ * most 32 rows per expert, runs on that launch alone).  Both compute every
+ * output element with the tile kernel's per-block arithmetic in ascending
+ * block order, so row r of out equals the tiled dense GEMM's row for token
+ * t and expert ids[r]'s matrix, bit-identical for Q8_0 and Q6_K (for Q4_K
+ * and Q5_K the min term is added per k-step on the matrix core in the
+ * tiles and per sub-block in the second launch: equal within rounding).
+ * A routed row whose id is outside [0, n_experts) is not computed and its
+ * row of out is left as it was.  The routing runs on the device (a kernel
+ * on `stream` before the GEMM launches): the ids never visit the host.
+ * Requires K % 32 == 0 (Q8_0) or K % 256 == 0 (K-quants), 1 <= topk <= 64,
+ * 1 <= n_experts <= 2048, T*topk < 2^31 and x under 2 GiB.  Two calls on
+ * one stream may share a workspace; calls that overlap in time may not. */
 int mmq_moe_gemm(int fmt, const void *x_q8_1, const void *w, int n_experts, const int32_t *ids, int topk,
                  float *out, int64_t T, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,
                  void *stream);
@@ -250,7 +259,7 @@ int mmq_moe_gemm_routed(int fmt, const void *x_q8_1, const void *w, int n_expert
 /* The indexed-MoE GEMM of mmq_moe_gemm for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation): the same routing and GEMM kernels, with the
- * routing tables in a static device array of the library (576 KiB per
+ * routing tables in a static device array of the library (about 592 KiB per
  * device, held until the process ends) instead of a caller workspace.
  * Arguments, layouts and results as for mmq_moe_gemm, without the workspace.
  * Refused when T*topk exceeds MMQ_MOE_NOALLOC_MAX_ROUTED.  Calls no

@@ -2,9 +2,11 @@
 section 4.5): mmq_moe_gemm against the oracle's oracle_moe_gemm on the same
 seeded inputs.
 
-Bars as for the dense GEMM: normalized error <= 1e-5, and Q8_0 bit-identical
-(every routed row is computed by the dense kernel's arithmetic in its order,
-wherever the routing places it).  Outputs start as a NaN sentinel, so a
+Bars as for the dense GEMM: normalized error <= 1e-5, and Q8_0 and Q6_K
+bit-identical (every routed row is computed by the dense kernel's arithmetic
+in its order, wherever the routing places it: in a 128-row tile or in the
+launch for small remainders, whose K-quant rows also follow the oracle's
+order exactly).  Outputs start as a NaN sentinel, so a
 routed row the kernel never wrote fails."""
 import sys
 
@@ -223,6 +225,52 @@ def test_moe_routed_without_matching_tables_is_refused():
     mmq.moe_gemm_routed(fmt, xq, w, E, topk, T, N, K, ws, out4)
     torch.cuda.synchronize()
     assert torch.isnan(out4).all()
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K, mmq.FMT_Q5_K, mmq.FMT_Q6_K])
+def test_moe_remainder_boundaries(fmt):
+    """Experts whose last partial tile holds exactly 32 rows (the largest
+    remainder the small-remainder launch takes), 33 (a row tile of the tile
+    launch), none (a multiple of 128), 17 after two full tiles, and experts
+    of 32 rows and of 1 row in all, plus an empty one; N ragged over the
+    128-row groups and, for Q8_0, K/32 odd (rows off the dword grid, a last
+    unit of one block).  Rows of experts with at most 32 rows are computed by
+    the small-remainder launch alone, in the oracle's order for every format
+    (K-quants too: min term per sub-block), so they match it bit for bit."""
+    counts = [32, 33, 128, 160, 161, 1, 0, 256 + 17]
+    E, topk = len(counts), 1
+    T = sum(counts)
+    ids = np.repeat(np.arange(E, dtype=np.int32), counts)
+    np.random.default_rng(190).shuffle(ids)
+    ids = ids.reshape(T, 1)
+    N = 200
+    K = 288 if fmt == mmq.FMT_Q8_0 else 512
+    _say(f"moe remainder boundaries fmt={fmt} T={T} N={N} K={K}")
+    xq = oracle.quantize_q8_1(inputs.activations(T, K, 191))
+    w = _weights(fmt, E, N, K, 192)
+    got = _run(fmt, xq, w, E, ids, topk, T, N, K)
+    ref = oracle.moe_gemm(fmt, xq, w, ids, topk, T, N, K, E, nthreads=16)
+    _check(fmt, got, ref)
+    small = np.isin(ids[:, 0], [e for e, c in enumerate(counts) if 0 < c <= 32])
+    assert small.sum() == 33
+    assert np.array_equal(got[small].view(np.uint32), ref[small].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K, mmq.FMT_Q5_K, mmq.FMT_Q6_K])
+@pytest.mark.parametrize("T,N,K", [(1, 1536, 2048), (4, 768, 2048), (3, 2048, 768)])
+def test_moe_decode_sized_is_bit_identical(fmt, T, N, K):
+    """A few tokens, 8 of 128 experts each (the Qwen3-30B-A3B router's
+    shape): every expert holds at most T rows, so the small-remainder launch
+    computes everything and the tile launch nothing, and every row is the
+    oracle's bit for bit."""
+    E, topk = 128, 8
+    _say(f"moe decode-sized fmt={fmt} T={T} N={N} K={K}")
+    xq = oracle.quantize_q8_1(inputs.activations(T, K, 200 + T))
+    w = _weights(fmt, E, N, K, 201)
+    ids = inputs.moe_ids(T, E, topk, 202 + T)
+    got = _run(fmt, xq, w, E, ids, topk, T, N, K)
+    ref = oracle.moe_gemm(fmt, xq, w, ids, topk, T, N, K, E, nthreads=16)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
 @pytest.mark.parametrize("fmt,T,E,topk", [(mmq.FMT_Q8_0, 300, 2048, 1),   # the most experts: most of them empty

@@ -153,13 +153,13 @@ def test_guard_refuses_without_compute_units():
 
 
 @pytest.mark.parametrize("T,topk,E,tiles", [(2048, 8, 128, 128 + 128), (1, 8, 128, 0 + 8), (37, 3, 8, 0 + 8),
-                                            (16384, 1, 128, 128 + 128), (0, 2, 4, 0)])
+                                            (16384, 1, 128, 128 + 128), (0, 2, 4, 0), (5, 1, 3, 0 + 3)])
 def test_moe_workspace_bytes(T, topk, E, tiles):
-    """A 16-byte header, the tile table (16 B per possible 128-row tile:
-    floor(R/128) + min(E, R)) and the sorted routed-row ids (4 B each,
-    padded to 16)."""
+    """A 32-byte header, the tile table (16 B per possible 128-row tile:
+    floor(R/128) + min(E, R)), the small-remainder list (16 B per expert)
+    and the sorted routed-row ids (4 B each, padded to 16)."""
     R = T * topk
-    assert mmq.moe_workspace_bytes(T, topk, E) == 16 + 16 * tiles + -(-4 * R // 16) * 16
+    assert mmq.moe_workspace_bytes(T, topk, E) == 32 + 16 * tiles + 16 * E + -(-4 * R // 16) * 16
 
 
 @pytest.mark.parametrize("T,topk,E", [(-1, 2, 4), (4, 0, 4), (4, 65, 128), (4, 2, 0), (4, 2, 2049),
