@@ -11,6 +11,9 @@
 //   k_moe_route       expert routing for the MOE launch (counts, scan, scatter)
 //   k_mmv<FMT>        the same contraction for a few activation rows
 //                     (decode): VALU int8 dot products at the HBM roofline
+//   k_mmvq<FMT>       K-quant decode (M <= 8) on the matrix core
+//   k_mmsm<FMT, AR>   batch decode (9 <= M <= 32) on the matrix core
+//   k_moe_small<FMT>  the indexed MoE's small expert remainders
 //
 // The operation is the block-scaled contraction of "When the Product Won't
 // Collapse" (section 2) and, for Q4_K, the affine identity of "When Does a
@@ -1828,6 +1831,8 @@ __device__ __forceinline__ T lds_at(const uint8_t *buf, int off) {
     return *reinterpret_cast<const T *>(buf + off);
 }
 
+__device__ __forceinline__ void lds_at_store(uint8_t *buf, int off, float v) { *reinterpret_cast<float *>(buf + off) = v; }
+
 // 8 bytes starting at byte b (even) of buf, from the three dwords around them.
 __device__ __forceinline__ uint2 lds_field8(const uint8_t *buf, int b) {
     const int a = b & ~3;
@@ -1836,18 +1841,25 @@ __device__ __forceinline__ uint2 lds_field8(const uint8_t *buf, int b) {
     return make_uint2(__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w2, w1, sel));
 }
 
-// The MFMAs and epilogues of k-chunk u from buffer buf, for this wave's 32 weight rows.
-template <int FMT>
-__device__ __forceinline__ void small_compute(const uint8_t *buf, f32x16 &acc, const i32x16 &srcC, int wshift, int kb,
-                                              int wave, int lane, int u, int ng) {
+// The MFMAs and epilogues of k-chunk u from buffer buf, for one wave's 32
+// weight rows: activation code units at a0 (AR rows staged, 16 or 32),
+// their block headers at h0 (16 bytes per row), the weight rows' windows at
+// w0; wrow is this lane's weight row counted from the weight buffer's start.
+// With AR = 16 the lanes of rows 16-31 read rows 0-15 again: their D rows lie
+// in register groups 2 and 3, which the epilogue of ng <= 2 never reads.
+template <int FMT, int AR = 32>
+__device__ __forceinline__ void small_compute(const uint8_t *buf, int a0, int h0, int w0, int wrow, f32x16 &acc,
+                                              const i32x16 &srcC, int wshift, int kb, int lane, int u, int ng) {
+    static_assert(AR == 16 || AR == 32, "16 or 32 staged activation rows");
     using L = SmallLds<FMT>;
-    const int l32 = lane & 31, g = lane >> 5;
-    const int xr = 8 * ((lane & 15) >> 2) + (lane & 3) + 4 * g;   // the row whose header this lane broadcasts
-    const int wr = L::OFF_W + wave * L::W_WAVE + l32 * L::W_ROW;   // this lane's weight row
-    const int hdr = L::OFF_HDR + 16 * xr;                          // its 4 block headers
-    auto a_unit = [&](int j, int h) { return 16 * (8 * l32 + ((2 * j + h) ^ (l32 & 7))); };
+    const int l32 = lane & 31, g = lane >> 5, ar = l32 & (AR - 1);
+    // the row whose header this lane broadcasts
+    const int xr = (8 * ((lane & 15) >> 2) + (lane & 3) + 4 * g) & (AR - 1);
+    const int wr = w0 + l32 * L::W_ROW;   // this lane's weight row
+    const int hdr = h0 + 16 * xr;         // its 4 block headers
+    auto a_unit = [&](int j, int h) { return a0 + 16 * (8 * ar + ((2 * j + h) ^ (ar & 7))); };
     if constexpr (FMT == FMT_Q8_0) {
-        const int sh = (wshift + (32 * wave + l32) * kb * 34 + u * 4 * 34) & 3;   // the row's chunk start, 0 or 2
+        const int sh = (wshift + wrow * kb * 34 + u * 4 * 34) & 3;   // the row's chunk start, 0 or 2
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             if (4 * u + j >= kb) break;   // wave-uniform: the row's last chunk may hold 1-3 blocks
@@ -1862,7 +1874,7 @@ __device__ __forceinline__ void small_compute(const uint8_t *buf, f32x16 &acc, c
         }
     } else if constexpr (FMT == FMT_Q6_K) {
         const int hh = u & 1;
-        const int w6 = wr + ((wshift + ((32 * wave + l32) * (kb >> 3) + (u >> 1)) * 210) & 3);
+        const int w6 = wr + ((wshift + (wrow * (kb >> 3) + (u >> 1)) * 210) & 3);
         // window offsets: low bits at 0, high bits at 80, scales and d at 128 (each from its dword)
         const float d = h2f(lds_at<unsigned short>(buf, w6 + 128 + 16));
         const uint2 hb[2] = {lds_field8(buf, w6 + 80 + 8 * g), lds_field8(buf, w6 + 80 + 16 + 8 * g)};
@@ -1996,7 +2008,9 @@ __global__ __launch_bounds__(kSmallThreads) void k_moe_small(const uint8_t *__re
         uint8_t *const nxt = P ? lds0 : lds1;
         SmallDmaOffs<FMT> wo;
         small_dma<FMT>(rx, xcode, xhdr, rwb.r, rwb.shift, kb, wave, lane, min(u + 1, last), nxt, wo);
-        if (live && u < nunits) small_compute<FMT>(cur, acc, srcC, rwb.shift, kb, wave, lane, u, ng);
+        if (live && u < nunits)
+            small_compute<FMT>(cur, 0, L::OFF_HDR, L::OFF_W + wave * L::W_WAVE, 32 * wave + (lane & 31), acc, srcC,
+                               rwb.shift, kb, lane, u, ng);
 #pragma unroll
         for (int i = 0; i < SmallDmaOffs<FMT>::N; i++) asm volatile("" ::"v"(wo.v[i]));
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // chunk u + 1 has landed
@@ -2018,6 +2032,207 @@ __global__ __launch_bounds__(kSmallThreads) void k_moe_small(const uint8_t *__re
     for (int r = 0; r < 16; r++) {
         const int m = 8 * (r >> 2) + 4 * g + (r & 3);
         if (m < cnt && n < N) out[int64_t(orow[r]) * N + n] = acc[r];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Batch decode (9 <= M <= 32 activation rows): the matrix-core step of the
+// small-remainder kernel above, for dense GEMMs and GEMM sets.  A workgroup
+// takes 32 weight rows (one set member's: the grid's x counts 32-row groups
+// per member) as the B operand of a 32 x 32 x 32 int8 MFMA per block, the
+// activation rows as A (AR = 16 or 32 staged; rows past M read as zero
+// through the buffer's range check and are never stored).  A 128-row tile
+// kernel would leave 3 of its 4 wave rows idle at these sizes and give
+// narrow GEMMs (N = 3584 at K = 18944: 28 tiles) a small fraction of the
+// CUs; here the same GEMM has 112 workgroups of four waves.
+//
+// Each wave takes a K-slice of the 32 rows: slice q = 4 * blockIdx.z + wave
+// of S = 4 * gridDim.z holds chunks [nunits * q / S, nunits * (q + 1) / S) of
+// 4 blocks.  The waves share nothing while they run: each stages its own
+// activation codes and headers and its rows' weight windows (the layouts of
+// the small-remainder kernel) into LDS of its own by DMA, two stages deep,
+// with no barrier.  At the end the four partial sums are added in wave
+// order through LDS (wave w adds register group w, the output rows
+// 8w..8w+7) and stored; with gridDim.z = 2 the two workgroups of a row group
+// add theirs into the zeroed output with fp32 atomics (two terms onto an
+// exact zero: the same result in either order).
+//
+// Every DMA offset is in the lane's offset register, never the scalar one,
+// so that the buffer's range check sees the whole offset (the last chunk of
+// a Q8_0 row with K % 128 != 0 reaches past the row's end).
+// ---------------------------------------------------------------------------
+template <int FMT, int AR>
+struct SmLds {
+    static_assert(SmallLds<FMT>::W_UNITS == sm_w_units(FMT), "plan and kernel weight windows disagree");
+    static constexpr int A = 0;                             // AR rows x 8 code units of 16 bytes
+    static constexpr int H = AR * 128;                      // AR rows x 4 block headers
+    static constexpr int W = AR * 144;                      // the 32 weight rows' windows
+    static constexpr int WAVE = W + SmallLds<FMT>::W_WAVE;  // one wave's stage
+    static constexpr int STAGE = kSmWaves * WAVE;
+};
+static_assert(kSmStages * SmLds<FMT_Q8_0, 32>::STAGE == sm_lds_bytes(FMT_Q8_0, 32) &&
+                  kSmStages * SmLds<FMT_Q4_K, 16>::STAGE == sm_lds_bytes(FMT_Q4_K, 16) &&
+                  kSmStages * SmLds<FMT_Q5_K, 32>::STAGE == sm_lds_bytes(FMT_Q5_K, 32) &&
+                  kSmStages * SmLds<FMT_Q6_K, 16>::STAGE == sm_lds_bytes(FMT_Q6_K, 16) && kSmStages >= 2 &&
+                  kSmStages <= 4,
+              "plan and kernel LDS disagree");
+
+// A lane's activation DMA sources at chunk 0: code unit f = 64 i + lane is
+// slot f of the stage (row f / 8, unit (2j + h) = (f % 8) xor (row % 8)),
+// header slot 64 i + lane is row (64 i + lane) / 4, block lane % 4.
+template <int AR>
+struct SmActOffs {
+    int code[AR / 8];
+    int hdr[AR / 16];
+};
+
+template <int FMT, int AR>
+__device__ __forceinline__ void sm_dma(__amdgpu_buffer_rsrc_t rx, const SmActOffs<AR> &xo, __amdgpu_buffer_rsrc_t rw,
+                                       int wshift, int kb, int lane, int u, uint8_t *buf, int base,
+                                       SmallDmaOffs<FMT> &wo) {
+    using S = SmLds<FMT, AR>;
+    using L = SmallLds<FMT>;
+    const int cu = u * 4 * 36;   // the chunk's 4 blocks
+#pragma unroll
+    for (int i = 0; i < AR / 8; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + base + S::A + 1024 * i), 16, xo.code[i] + cu,
+                                                 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < AR / 16; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + base + S::H + 256 * i), 4, xo.hdr[i] + cu, 0,
+                                                 0, 0);
+    constexpr int kUnits = 32 * L::W_UNITS;
+#pragma unroll
+    for (int i = 0; i < SmallDmaOffs<FMT>::N; i++) {
+        const int f = min(64 * i + lane, kUnits - 1);
+        wo.v[i] = small_w_unit<FMT>(wshift, kb, f / L::W_UNITS, u, f % L::W_UNITS);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(buf + base + S::W + 1024 * i), 16, wo.v[i], 0, 0,
+                                                 0);
+    }
+}
+
+template <int FMT, int AR>
+__global__ __launch_bounds__(kSmThreads) void k_mmsm(const uint8_t *__restrict__ xq, const GemmSet set, int M,
+                                                     int K) {
+    static_assert(kSmRows == 32 && kSmThreads == 256, "four waves over 32 weight rows");
+    using S = SmLds<FMT, AR>;
+    static_assert(S::STAGE >= kSmWaves * 16 * 64 * 4, "the partial sums fit one stage");
+    // the stages as variables of their own (see k_moe_small), each holding
+    // the four waves' regions
+    constexpr int NST = kSmStages;
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[S::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[S::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds2[NST > 2 ? S::STAGE : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t lds3[NST > 3 ? S::STAGE : 16];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bx = int(blockIdx.x);
+    int gi = 0;
+    for (int i = 1; i < set.count; i++)
+        if (bx >= set.tile_start[i]) gi = i;
+    const int N = set.N[gi], n0 = (bx - set.tile_start[gi]) * kSmRows;
+    const int kb = K >> 5;
+    const int64_t wrow = weight_row_bytes(FMT, K);
+    // weight rows past N read as zero (scale 0) and are never stored
+    const WBuf rwb = weight_rsrc(set.w[gi] + int64_t(n0) * wrow, int64_t(N - n0) * wrow);
+    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq, int64_t(M) * kb * 36);
+    SmActOffs<AR> xo;
+#pragma unroll
+    for (int i = 0; i < AR / 8; i++) {
+        const int f = 64 * i + lane, r = f >> 3, q = (f & 7) ^ (r & 7);
+        xo.code[i] = r * kb * 36 + (q >> 1) * 36 + 4 + 16 * (q & 1);
+    }
+#pragma unroll
+    for (int i = 0; i < AR / 16; i++) {
+        const int hi = 64 * i + lane;
+        xo.hdr[i] = (hi >> 2) * kb * 36 + (hi & 3) * 36;
+    }
+    // register groups holding activation rows: 2 (M <= 16), else 3 or 4 (a
+    // select of constants, so the epilogue's group tests fold)
+    const int ng = AR == 16 ? 2 : (M > 24 ? 4 : 3);
+    const int nunits = (kb + 3) >> 2, slices = kSmWaves * int(gridDim.z);
+    const int sq = int(blockIdx.z) * kSmWaves + wave;
+    const int c0 = nunits * sq / slices, c1 = nunits * (sq + 1) / slices;
+    const int base = wave * S::WAVE;
+
+    i32x16 srcC;
+#pragma unroll
+    for (int r = 0; r < 16; r++) srcC[r] = int(kMagicBits);
+    asm volatile("" : "+v"(srcC));
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[r] = 0.0f;
+
+    auto stage = [&](auto p) -> uint8_t * {
+        constexpr int P = decltype(p)::value % NST;
+        if constexpr (P == 0) return lds0;
+        else if constexpr (P == 1) return lds1;
+        else if constexpr (P == 2) return lds2;
+        else return lds3;
+    };
+    if (c1 > c0) {   // wave-uniform: a K-slice with chunks
+        // the first NST - 1 chunks (clamped to the slice)
+        {
+            SmallDmaOffs<FMT> wo;
+            sm_dma<FMT, AR>(rx, xo, rwb.r, rwb.shift, kb, lane, c0, stage(Parity<0>{}), base, wo);
+            if constexpr (NST > 2) sm_dma<FMT, AR>(rx, xo, rwb.r, rwb.shift, kb, lane, min(c0 + 1, c1 - 1),
+                                                   stage(Parity<1>{}), base, wo);
+            if constexpr (NST > 3) sm_dma<FMT, AR>(rx, xo, rwb.r, rwb.shift, kb, lane, min(c0 + 2, c1 - 1),
+                                                   stage(Parity<2>{}), base, wo);
+        }
+        // Chunk u computes from stage u % NST while the DMA of chunks up to
+        // u + NST - 1 fill the others (the compiler's wait before the first
+        // read of a stage leaves the later DMA in flight).  Every chunk
+        // issues its DMA, the index clamped to the slice's last chunk, and
+        // the loop runs a multiple of NST chunks with the compute skipped
+        // past the slice: the wait counts rely on every iteration issuing
+        // the same DMA instructions.
+        auto chunk = [&](auto parity, int u) {
+            constexpr int P = decltype(parity)::value;
+            SmallDmaOffs<FMT> wo;
+            // the reads of chunk u - 1 from the stage refilled here have returned
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            sm_dma<FMT, AR>(rx, xo, rwb.r, rwb.shift, kb, lane, min(u + NST - 1, c1 - 1),
+                            stage(Parity<P + NST - 1>{}), base, wo);
+            if (u < c1)
+                small_compute<FMT, AR>(stage(parity), base + S::A, base + S::H, base + S::W, lane & 31, acc, srcC,
+                                       rwb.shift, kb, lane, u, ng);
+#pragma unroll
+            for (int i = 0; i < SmallDmaOffs<FMT>::N; i++) asm volatile("" ::"v"(wo.v[i]));
+        };
+        for (int u = c0; u < c1; u += NST) {
+            chunk(Parity<0>{}, u);
+            chunk(Parity<1>{}, u + 1);
+            if constexpr (NST > 2) chunk(Parity<2>{}, u + 2);
+            if constexpr (NST > 3) chunk(Parity<3>{}, u + 3);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();   // every wave is done with both stages
+    // partial sums [wave][register][lane] in stage 0
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+        if (r < 4 * ng) lds_at_store(lds0, 4 * ((wave * 16 + r) * 64 + lane), acc[r]);
+    __syncthreads();
+    if (wave >= ng) return;
+    // wave w: register group w (output rows 8w + 4(l/32) + i), the slices
+    // added in order
+    float *out = reinterpret_cast<float *>(set.out[gi]);
+    const int n = n0 + (lane & 31), g = lane >> 5;
+    const bool split = gridDim.z > 1;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int r = 4 * wave + i;
+        float v = lds_at<float>(lds0, 4 * (r * 64 + lane));
+#pragma unroll
+        for (int w = 1; w < kSmWaves; w++) v += lds_at<float>(lds0, 4 * ((w * 16 + r) * 64 + lane));
+        const int m = 8 * wave + 4 * g + i;
+        if (m < M && n < N) {
+            if (split)
+                unsafeAtomicAdd(out + int64_t(m) * N + n, v);
+            else
+                out[int64_t(m) * N + n] = v;
+        }
     }
 }
 
@@ -2260,6 +2475,9 @@ const void *plan_kernel(const Plan &p, bool dots, bool moe) {
             if (p.tile_m <= 4) return reinterpret_cast<const void *>(&k_mmv<F, 4>);
             return reinterpret_cast<const void *>(&k_mmv<F, 8>);
         }
+        if (p.kernel == KERNEL_SM && !dots)
+            return p.tile_m == 16 ? reinterpret_cast<const void *>(&k_mmsm<F, 16>)
+                                  : reinterpret_cast<const void *>(&k_mmsm<F, 32>);
         if (dots) return kmmq<F, true, false, false, false>();   // partial steps: the store mask
         if constexpr (F == FMT_Q8_0) {
             if (moe) return p.tail ? kmmq<F, false, true, true, true>() : kmmq<F, false, true, true, false>();
@@ -2319,12 +2537,14 @@ hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const vo
     const dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.split_k);
     const dim3 block(p.threads);
     // the kernel the plan names (the one whose attributes the guard read);
-    // its LDS is static (lds_bytes_for() bytes, checked by the plan)
+    // its LDS is static (checked by the plan)
     const uint8_t *xb = reinterpret_cast<const uint8_t *>(x);
     int Mi = int(M), Ki = int(K), sps = int(p.steps_per_split);
     MoeArgs noMoe{};
     void *args[] = {&xb, &set, &Mi, &Ki, &sps, &noMoe};
-    const hipError_t e = hipLaunchKernel(plan_kernel(p, dots, false), grid, block, args, 0, stream);
+    void *sm_args[] = {&xb, &set, &Mi, &Ki};
+    const hipError_t e = hipLaunchKernel(plan_kernel(p, dots, false), grid, block,
+                                         p.kernel == KERNEL_SM ? sm_args : args, 0, stream);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }

@@ -71,7 +71,7 @@ constexpr int64_t lds_bytes_for(int fmt) {
 // Few activation rows (decode): a matrix-vector kernel streams each weight
 // row once for all of them (mv_rows_per_wave(M) output rows per wave, four
 // waves per workgroup) instead of a 128-row tile that would be almost empty.
-enum Kernel : int { KERNEL_MMQ = 0, KERNEL_MV = 1 };
+enum Kernel : int { KERNEL_MMQ = 0, KERNEL_MV = 1, KERNEL_SM = 2 };
 constexpr int kMvMaxM = 8;          // activation rows the matvec kernel takes at most
 constexpr int kMvThreads = 256;
 constexpr int kMvWaves = kMvThreads / 64;
@@ -101,6 +101,40 @@ inline bool mv_on_mfma(int fmt, int64_t M, int64_t N, int64_t K) {
     if (K > kMvqMaxK) return false;
     return M >= 8 || (M >= 3 && N >= 16384);
 }
+
+// Batch-decode sizes (kMvMaxM < M <= kSmMaxM): k_mmsm, the matrix-core
+// kernel of 32 weight rows per workgroup, one int8 MFMA per block with the
+// activation rows as A (16 or 32 of them staged, sm_act_rows).  Its four
+// waves take a K-slice each, staging their operands into LDS of their own by
+// DMA in chunks of 4 blocks, two stages deep, and add their partial sums in
+// wave order at the end.  A 128-row tile would leave 3 of its 4 wave rows
+// idle here and give too few workgroups for the narrow GEMMs.
+constexpr int kSmMaxM = 32;
+constexpr int kSmRows = 32;      // weight rows per workgroup
+constexpr int kSmWaves = 4;      // its waves, one K-slice each
+constexpr int kSmThreads = 64 * kSmWaves;
+// Two stages: three (92 KiB of LDS at Q4_K, 16 rows) or four measured
+// slower on the 7B layer at M = 16 and 32 (gate+up, Q4_K at M = 16: 38.2 us
+// with two, 41.9 with three, 54.6 with four): the workgroups a CU holds
+// fall with the LDS, and the extra chunk in flight per wave does not make
+// up for the waves lost.
+constexpr int kSmStages = 2;
+constexpr int sm_act_rows(int64_t M) { return M <= 16 ? 16 : 32; }
+// 16-byte units of one weight row's 4-block chunk (Q8_0: 136 bytes from the
+// dword below the first; K-quants: the super-block header and the chunk's
+// code half; Q6_K: low bits, high bits, scales and d of the half)
+constexpr int sm_w_units(int fmt) { return fmt == FMT_Q8_0 ? 9 : fmt == FMT_Q4_K ? 5 : fmt == FMT_Q5_K ? 7 : 10; }
+// one wave's stage: activation codes (128 B per row) and headers (16 B per
+// row), then the 32 weight rows' units padded to whole 64-lane DMA
+// instructions of 16 bytes
+constexpr int64_t sm_wave_stage_bytes(int fmt, int ar) {
+    return int64_t(ar) * 144 + 1024 * ((32 * sm_w_units(fmt) + 63) / 64);
+}
+constexpr int64_t sm_lds_bytes(int fmt, int ar) { return int64_t(kSmStages) * kSmWaves * sm_wave_stage_bytes(fmt, ar); }
+// Split K over two workgroups (grid z, fp32 atomics into a zeroed output)
+// when the 32-row groups fill at most half of the resident slots and every
+// wave keeps at least kSmMinChunksPerWave chunks.
+constexpr int kSmMinChunksPerWave = 2;
 
 // gfx950 register file: 512 registers per lane per SIMD (arch and
 // accumulation VGPRs together), allocated in granules of 8; at most 8 waves
@@ -193,7 +227,8 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
         if (fit.scratch > 0) {
             if (why && why_len)
                 std::snprintf(why, why_len, "the %s kernel uses %lld B of scratch per lane (register spills): refused",
-                              q.kernel == KERNEL_MV ? "matvec" : "GEMM", (long long)fit.scratch);
+                              q.kernel == KERNEL_MV ? "matvec" : q.kernel == KERNEL_SM ? "batch-decode" : "GEMM",
+                              (long long)fit.scratch);
             return false;
         }
         if (q.wg_per_cu < 1) {
@@ -238,6 +273,27 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
         if (q.grid_x > INT32_MAX) return fail("too many output rows");
         if (q.lds_bytes > lds_limit) return fail("plan needs more LDS per workgroup than the device allows: refused");
         if (!check_fit(q)) return false;
+        *p = q;
+        return true;
+    }
+    if (allow_mv && M <= kSmMaxM) {
+        q.kernel = KERNEL_SM;
+        q.tile_m = sm_act_rows(M);
+        q.tile_n = kSmRows;
+        q.threads = kSmThreads;
+        q.blocks_per_stage = 4;
+        q.lds_bytes = sm_lds_bytes(fmt, q.tile_m) + extra_lds;
+        q.grid_x = (N + kSmRows - 1) / kSmRows;
+        q.grid_y = 1;
+        q.k_steps = (K / 32 + 3) / 4;   // chunks of 4 blocks (the last may be partial: Q8_0)
+        q.steps_per_split = q.k_steps;
+        if (q.grid_x > INT32_MAX) return fail("too many output rows");
+        if (q.lds_bytes > lds_limit) return fail("plan needs more LDS per workgroup than the device allows: refused");
+        if (!check_fit(q)) return false;
+        if (2 * q.grid_x <= int64_t(q.wg_per_cu) * cu_count && q.k_steps >= 2 * kSmWaves * kSmMinChunksPerWave) {
+            q.split_k = 2;
+            q.steps_per_split = (q.k_steps + 1) / 2;
+        }
         *p = q;
         return true;
     }
@@ -306,20 +362,23 @@ inline bool make_plan_multi(int fmt, int64_t M, int count, const int64_t *Ns, in
     };
     if (count < 1 || count > kMaxGemms) return fail("count must be 1..8 GEMMs");
     if (!Ns) return fail("null N array");
-    // tile units: 128-column tiles for the MMQ kernel, single rows for the matvec kernel
+    // tile units: 128-column tiles for the MMQ kernel, single rows for the
+    // matvec kernel, 32-row groups for the batch-decode kernel (a group never
+    // holds rows of two GEMMs)
     const bool mv = allow_mv && M >= 1 && M <= kMvMaxM;
+    const bool sm = allow_mv && M > kMvMaxM && M <= kSmMaxM;
     int64_t tiles = 0;
     for (int g = 0; g < count; g++) {
         Plan one;
         if (!make_plan(fmt, M, Ns[g], K, lds_limit, cu_count, extra_lds, &one, why, why_len, allow_mv, fit))
             return false;
         tile_start[g] = int(tiles);
-        tiles += mv ? Ns[g] : one.grid_x;
+        tiles += mv ? Ns[g] : sm ? (Ns[g] + kSmRows - 1) / kSmRows : one.grid_x;
         if (tiles > (int64_t(1) << 30)) return fail("too many output columns in the GEMM set");
     }
     tile_start[count] = int(tiles);
-    return make_plan(fmt, M, mv ? tiles : tiles * kTileN, K, lds_limit, cu_count, extra_lds, p, why, why_len,
-                     allow_mv, fit, workspace);
+    return make_plan(fmt, M, mv ? tiles : tiles * (sm ? kSmRows : kTileN), K, lds_limit, cu_count, extra_lds, p, why,
+                     why_len, allow_mv, fit, workspace);
 }
 
 // Split-K workspace of a plan: one 32-bit arrival counter per output tile
@@ -407,7 +466,7 @@ inline void describe(const Plan &p, const Plan *ws, char *buf, size_t len) {
                           "kernel=%s fmt=%s tile=%dx%d threads=%d blocks_per_stage=%d lds=%lld grid=%lldx%lld "
                           "k_steps=%lld split_k=%lld steps_per_split=%lld skip_idle_waves=%d mv_rows_per_wave=%d "
                           "wg_per_cu=%d vgprs=%d tail=%d split_ws=%d mv_mfma=%d",
-                          p.kernel == KERNEL_MV ? "mv" : "mmq", fmt_name(p.fmt), p.tile_m, p.tile_n, p.threads,
+                          p.kernel == KERNEL_MV ? "mv" : p.kernel == KERNEL_SM ? "sm" : "mmq", fmt_name(p.fmt), p.tile_m, p.tile_n, p.threads,
                           p.blocks_per_stage, (long long)p.lds_bytes, (long long)p.grid_x, (long long)p.grid_y,
                           (long long)p.k_steps, (long long)p.split_k, (long long)p.steps_per_split,
                           int(p.skip_idle_waves), p.mv_rows_per_wave, p.wg_per_cu, p.kernel_vgprs, int(p.tail),

@@ -97,7 +97,14 @@ int mmq_quantize_q8_1(const float *x, void *y, int64_t M, int64_t K, void *strea
  * kernel instead: each weight row is read once for all M activation rows
  * and its blocks are summed per lane and then across the 64 lanes of a
  * wave, a fixed order (the same on every run) other than ascending.
- * mmq_plan_describe reports kernel=mv for such shapes. */
+ * mmq_plan_describe reports kernel=mv for such shapes.
+ * 9 <= M <= 32 (batched decode) runs a matrix-core kernel of 32 weight rows
+ * per workgroup instead (kernel=sm): one int8 MFMA per block with the
+ * activation rows as its other operand, the per-block scale arithmetic
+ * above, four K-slices each summed in ascending order and then added in
+ * slice order; narrow shapes split K over two workgroups more, added into
+ * the zeroed output by fp32 atomics as above.  The result is the same on
+ * every run. */
 int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out,
                   int64_t M, int64_t N, int64_t K, void *stream);
 
@@ -111,7 +118,8 @@ int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out,
  * the matrix core instead (mmq_plan_describe reports mv_mfma=1): one int8
  * MFMA per block over 32 weight rows, the activation rows as its other
  * operand, each output summed by one lane over a quarter of the blocks in
- * ascending order and the four quarters then added in order. */
+ * ascending order and the four quarters then added in order.  9 <= M <= 32
+ * as for mmq_gemm_q8_0. */
 int mmq_gemm_q4_K(const void *x_q8_1, const void *w_q4_K, float *out,
                   int64_t M, int64_t N, int64_t K, void *stream);
 
@@ -123,8 +131,8 @@ int mmq_gemm_q4_K(const void *x_q8_1, const void *w_q4_K, float *out,
  *   for Q4_K, 32 B of high bits @16, 128 B of low nibbles @48 in the Q4_K
  *   order; the code of element e is its nibble + 16 * bit (e/32) of
  *   high-bit byte e%32); out: M x N fp32 row-major, fully overwritten.
- *   Requires K % 256 == 0.  Split-K and M <= 8 shapes behave as for
- *   mmq_gemm_q8_0. */
+ *   Requires K % 256 == 0.  Split-K, M <= 8 and 9 <= M <= 32 shapes behave
+ *   as for mmq_gemm_q8_0. */
 int mmq_gemm_q5_K(const void *x_q8_1, const void *w_q5_K, float *out,
                   int64_t M, int64_t N, int64_t K, void *stream);
 
@@ -142,8 +150,9 @@ int mmq_gemm_q5_K(const void *x_q8_1, const void *w_q5_K, float *out,
  * codes (code - 32) first (one rounding), and the activation scale of the
  * block is then fused into the running sum: the same arithmetic, in the
  * same order, as a single pass over the groups, so unsplit tile-kernel
- * shapes are bit-identical to it.  Split-K and M <= 8 (the matrix-vector
- * kernel, one term per 16-element group) as for mmq_gemm_q8_0. */
+ * shapes are bit-identical to it.  Split-K, M <= 8 (the matrix-vector
+ * kernel, one term per 16-element group) and 9 <= M <= 32 (one term per
+ * 16-element group as here, in four K-slices) as for mmq_gemm_q8_0. */
 int mmq_gemm_q6_K(const void *x_q8_1, const void *w_q6_K, float *out,
                   int64_t M, int64_t N, int64_t K, void *stream);
 
@@ -151,7 +160,9 @@ int mmq_gemm_q6_K(const void *x_q8_1, const void *w_q6_K, float *out,
  * layer pipeline of "13 . r7-r8 raw-byte MMQ kernel": quantize once per
  * distinct input, e.g. the q, k and v projections, or gate and up), computed
  * by one launch whose grid covers the column tiles of all of them (for
- * M <= 8, the output rows of all of them, in the matrix-vector kernel).
+ * M <= 8, the output rows of all of them, in the matrix-vector kernel; for
+ * 9 <= M <= 32, their groups of 32 output rows, a group never holding rows
+ * of two of them).
  *   fmt: MMQ_FMT_Q8_0, MMQ_FMT_Q4_K, MMQ_FMT_Q5_K or MMQ_FMT_Q6_K; count: 1..8;
  *   x_q8_1: M x (K/32) q8_1 blocks, shared;
  *   w[g]: N[g] x K weights of format fmt; out[g]: M x N[g] fp32 row-major,

@@ -130,7 +130,7 @@ def test_gemm_matches_oracle(fmt, M, N, K):
     w = _weights(fmt, N, K, 40 + N)
     got = _run_gemm(fmt, xq, w, M, N, K)
     ref = _oracle_gemm(fmt, xq, w, M, N, K)
-    if _kernel(fmt, M, N, K) == "mv":
+    if _kernel(fmt, M, N, K) in ("mv", "sm"):
         _check_reordered(fmt, got, ref, xq, w, M, N, K)
         return
     rep = metrics.report(got, ref)
@@ -321,19 +321,23 @@ def test_gemm_hand_cases():
     # K = 64: two blocks, half a k-step of the tile kernel
     xq = _gpu_quantize(x)
     assert _run_gemm(mmq.FMT_Q8_0, xq, w, 1, 1, K)[0, 0] == expect
-    x9 = np.repeat(x, 9, axis=0)   # the tiled kernel (M > 8) as well
-    assert (_run_gemm(mmq.FMT_Q8_0, _gpu_quantize(x9), w, 9, 1, K)[:, 0] == expect).all()
+    # the batch-decode (9 <= M <= 32) and tile (M > 32) kernels as well: the
+    # same row repeated
+    for m in (9, 33):
+        xm = np.repeat(x, m, axis=0)
+        assert (_run_gemm(mmq.FMT_Q8_0, _gpu_quantize(xm), w, m, 1, K)[:, 0] == expect).all()
     x, w, K, expect = golden_cases.gemm_q4_K_case()
     xq = _gpu_quantize(x)
     assert _run_gemm(mmq.FMT_Q4_K, xq, w, 1, 1, K)[0, 0] == expect
-    x9 = np.repeat(x, 9, axis=0)
-    assert (_run_gemm(mmq.FMT_Q4_K, _gpu_quantize(x9), w, 9, 1, K)[:, 0] == expect).all()
+    for m in (9, 33):
+        xm = np.repeat(x, m, axis=0)
+        assert (_run_gemm(mmq.FMT_Q4_K, _gpu_quantize(xm), w, m, 1, K)[:, 0] == expect).all()
     x, w, K, expect = golden_cases.gemm_q5_K_case()
     xq = _gpu_quantize(x)
     assert _run_gemm(mmq.FMT_Q5_K, xq, w, 1, 1, K)[0, 0] == expect
-    # the tiled kernel too: the same row in a 9-row input (M > 8)
-    x9 = np.repeat(x, 9, axis=0)
-    assert (_run_gemm(mmq.FMT_Q5_K, _gpu_quantize(x9), w, 9, 1, K)[:, 0] == expect).all()
+    for m in (9, 33):
+        xm = np.repeat(x, m, axis=0)
+        assert (_run_gemm(mmq.FMT_Q5_K, _gpu_quantize(xm), w, m, 1, K)[:, 0] == expect).all()
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4])
@@ -481,12 +485,13 @@ def test_matvec_matches_oracle(fmt, M, N, K):
     _check_reordered(fmt, got, _oracle_gemm(fmt, xq, w, M, N, K), xq, w, M, N, K)
 
 
-def test_matvec_boundary_m8_m9():
-    """M = 8 is the last matvec size and M = 9 the first tiled one; both agree
-    with the oracle on the same weights."""
+def test_kernel_boundaries_m8_m9_m32_m33():
+    """M = 8 is the last matvec size, 9 and 32 the first and last
+    batch-decode sizes, 33 the first tiled one; all agree with the oracle on
+    the same weights."""
     fmt, N, K = mmq.FMT_Q4_K, 640, 2048
     w = _weights(fmt, N, K, 130)
-    for M, kern in ((8, "mv"), (9, "mmq")):
+    for M, kern in ((8, "mv"), (9, "sm"), (32, "sm"), (33, "mmq")):
         assert _kernel(fmt, M, N, K) == kern
         xq = oracle.quantize_q8_1(inputs.activations(M, K, 131))
         rep = metrics.report(_run_gemm(fmt, xq, w, M, N, K), _oracle_gemm(fmt, xq, w, M, N, K))
@@ -634,7 +639,8 @@ def test_quantize_refusals():
 
 @pytest.mark.parametrize("fmt,M,N,K", [(mmq.FMT_Q4_K, 1, 4608, 3584),      # matvec
                                        (mmq.FMT_Q8_0, 512, 512, 3584),     # split-K: zero fill + atomics
-                                       (mmq.FMT_Q5_K, 300, 640, 1024)])    # tiled
+                                       (mmq.FMT_Q5_K, 300, 640, 1024),     # tiled
+                                       (mmq.FMT_Q4_K, 16, 3584, 18944)])   # batch decode, split-K
 def test_graph_capture_replays_match_eager(fmt, M, N, K):
     """The library's launches captured in a HIP graph (quantize + GEMM on the
     capture stream): every replay, with eager work and synchronizations in
@@ -786,6 +792,87 @@ def test_q8_0_gemm_multi_any_whole_blocks():
         assert rep["bit_identical_fraction"] == 1.0
 
 
+# ------------------------------------------------------------------ batch decode (9 <= M <= 32)
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [9, 16, 17, 31, 32])
+@pytest.mark.parametrize("N,K", [(300, 768), (37, 2048), (3584, 18944)])
+def test_batch_decode_matches_oracle(fmt, M, N, K):
+    """Batch-decode sizes run the small-M kernel (32 weight rows per
+    workgroup, four K-slices added in order, split over two workgroups for
+    the narrow long-K shape): every element written and each within the
+    fp32 bound of the exact value and the 1e-5 normalized error (a reordered
+    sum); ragged N leaves a partial last group of 32 rows, 300 x 768 an odd
+    chunk count per K-slice."""
+    assert _kernel(fmt, M, N, K) == "sm"
+    _say(f"batch decode fmt={fmt} M={M} N={N} K={K} split={_split_k(fmt, M, N, K)}")
+    xq = oracle.quantize_q8_1(inputs.activations(M, K, 300 + M))
+    w = _weights(fmt, N, K, 310 + N)
+    got = _run_gemm(fmt, xq, w, M, N, K)
+    _check_reordered(fmt, got, _oracle_gemm(fmt, xq, w, M, N, K), xq, w, M, N, K)
+
+
+@pytest.mark.parametrize("M", [12, 32])
+@pytest.mark.parametrize("K", [32, 96, 288, 3616])
+def test_batch_decode_q8_0_any_whole_blocks(M, K):
+    """Q8_0 at batch-decode sizes with K % 128 != 0: the last chunk of 4
+    blocks holds 1-3 (K = 32: a single block, three of the four K-slices
+    empty)."""
+    N = 130
+    assert _kernel(mmq.FMT_Q8_0, M, N, K) == "sm"
+    _say(f"batch decode q8_0 any K: M={M} N={N} K={K}")
+    xq = oracle.quantize_q8_1(inputs.activations(M, K, 320 + K))
+    w = inputs.q8_0_weights(N, K, 330 + K)
+    got = _run_gemm(mmq.FMT_Q8_0, xq, w, M, N, K)
+    _check_reordered(mmq.FMT_Q8_0, got, _oracle_gemm(mmq.FMT_Q8_0, xq, w, M, N, K), xq, w, M, N, K)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_batch_decode_set_members_equal_single_launches(fmt):
+    """A GEMM set at M = 20 with member widths that are not multiples of 32:
+    each member owns whole 32-row groups, equals its own launch bit for bit
+    and passes the reordered-sum check."""
+    M, Ns, K = 20, (257, 130, 33), 512
+    _say(f"batch decode set fmt={fmt} M={M} Ns={Ns} K={K}")
+    xq = oracle.quantize_q8_1(inputs.activations(M, K, 340))
+    ws = [_weights(fmt, n, K, 350 + g) for g, n in enumerate(Ns)]
+    outs = [_nan_out(M, n) for n in Ns]
+    mmq.gemm_multi(fmt, _to_dev(xq), [_to_dev(w) for w in ws], list(Ns), M, K, outs)
+    torch.cuda.synchronize()
+    for n, w, o in zip(Ns, ws, outs):
+        o = o.cpu().numpy()
+        assert not np.isnan(o).any(), "output element left unwritten"
+        single = _run_gemm(fmt, xq, w, M, n, K)
+        assert np.array_equal(o.view(np.uint32), single.view(np.uint32))
+        _check_reordered(fmt, o, _oracle_gemm(fmt, xq, w, M, n, K), xq, w, M, n, K)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_batch_decode_layer_set(fmt):
+    """The 7B layer's projections at 16 tokens through the batch-decode
+    kernel (q+k+v and gate+up as sets, down split over two workgroups):
+    every member equal to its own launch, all within tolerance of the
+    oracle."""
+    M = 16
+    shapes = {g: (n, k) for g, n, k in inputs.LAYER_7B}
+    for name, K, gemms in inputs.LAYER_INPUTS:
+        _say(f"batch decode layer fmt={fmt} {name} {gemms}")
+        xq = oracle.quantize_q8_1(inputs.activations(M, K, inputs.layer_activation_seed(2048, name)))
+        ws = [_weights(fmt, shapes[g][0], K, inputs.layer_weight_seed(g)) for g in gemms]
+        Ns = [shapes[g][0] for g in gemms]
+        assert _kernel(fmt, M, Ns[0], K) == "sm"
+        outs = mmq.gemm_multi(fmt, _to_dev(xq), [_to_dev(w) for w in ws], Ns, M, K)
+        torch.cuda.synchronize()
+        for g, (n, w) in enumerate(zip(Ns, ws)):
+            o = outs[g].cpu().numpy()
+            single = mmq.gemm(fmt, _to_dev(xq), _to_dev(w), M, n, K)
+            torch.cuda.synchronize()
+            assert np.array_equal(o.view(np.uint32), single.cpu().numpy().view(np.uint32))
+            rep = metrics.report(o, _oracle_gemm(fmt, xq, w, M, n, K))
+            _say(gemms[g], rep)
+            assert rep["normalized_max_error"] <= metrics.TOL
+
+
 # ------------------------------------------------------------------ Q6_K
 
 def test_q6_K_hand_case():
@@ -794,11 +881,12 @@ def test_q6_K_hand_case():
     x, w, K, expect = golden_cases.gemm_q6_K_case()
     xq = _gpu_quantize(x)
     assert _run_gemm(mmq.FMT_Q6_K, xq, w, 1, 1, K)[0, 0] == expect
-    x9 = np.repeat(x, 9, axis=0)
-    assert (_run_gemm(mmq.FMT_Q6_K, _gpu_quantize(x9), w, 9, 1, K)[:, 0] == expect).all()
+    for m in (9, 33):
+        xm = np.repeat(x, m, axis=0)
+        assert (_run_gemm(mmq.FMT_Q6_K, _gpu_quantize(xm), w, m, 1, K)[:, 0] == expect).all()
 
 
-@pytest.mark.parametrize("M,N,K", [(9, 37888, 3584), (100, 37888, 1024), (1000, 4608, 2304)])
+@pytest.mark.parametrize("M,N,K", [(33, 37888, 3584), (100, 37888, 1024), (1000, 4608, 2304)])
 def test_q6_K_bit_identical(M, N, K):
     """Unsplit tile-kernel shapes (more than 256 output tiles) apply each
     16-element group's scale in the oracle's arithmetic and order: every

@@ -38,7 +38,7 @@ def test_library_carries_gfx950_code_only():
 @pytest.mark.parametrize("fmt,M,N,K", [
     (mmq.FMT_Q8_0, 64, 256, 512), (mmq.FMT_Q8_0, 2048, 3584, 3584),
     (mmq.FMT_Q4_K, 2048, 18944, 3584), (mmq.FMT_Q4_K, 2048, 3584, 18944),
-    (mmq.FMT_Q4_K, 8192, 512, 3584), (mmq.FMT_Q8_0, 9, 1, 256),
+    (mmq.FMT_Q4_K, 8192, 512, 3584), (mmq.FMT_Q8_0, 33, 1, 256),
 ])
 def test_plans_for_benchmark_shapes_fit(fmt, M, N, K):
     ok, desc = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
@@ -187,12 +187,52 @@ def test_decode_sizes_plan_the_matvec_kernel(fmt, M, N, K):
         rows = 1 if M <= 4 else 2
         assert f"mv_rows_per_wave={rows}" in desc and "mv_mfma=0" in desc and "lds=0" in desc, desc
         assert (gx, gy) == (-(-N // (4 * rows)), 1)
-    # the same shape with one more row is tiled
-    assert "kernel=mmq" in mmq.plan_for_limits(fmt, 9, N, K, LDS_GFX950, 256)[1]
+    # the same shape with one more row runs the batch-decode kernel, and
+    # from M = 33 on the tile kernel
+    assert "kernel=sm" in mmq.plan_for_limits(fmt, 9, N, K, LDS_GFX950, 256)[1]
+    assert "kernel=mmq" in mmq.plan_for_limits(fmt, 33, N, K, LDS_GFX950, 256)[1]
+
+
+W_UNITS = {mmq.FMT_Q8_0: 9, mmq.FMT_Q4_K: 5, mmq.FMT_Q5_K: 7, mmq.FMT_Q6_K: 10}
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K, mmq.FMT_Q5_K, mmq.FMT_Q6_K])
+@pytest.mark.parametrize("M", [9, 16, 17, 24, 25, 32])
+@pytest.mark.parametrize("N,K", [(3584, 18944), (37888, 3584), (4608, 3584), (300, 256), (1, 2048)])
+def test_batch_decode_sizes_plan_the_small_m_kernel(fmt, M, N, K):
+    """9 <= M <= 32: the batch-decode kernel, one 256-thread workgroup per
+    32 weight rows, 16 activation rows staged up to M = 16 and 32 above; two
+    LDS stages per wave of activation codes and headers (144 B per row) and
+    the 32 weight rows' 16-byte units padded to whole 64-lane DMA
+    instructions; K in chunks of 4 blocks, split over two workgroups when
+    the row groups fill at most half of the resident slots and each of the
+    eight waves keeps two chunks."""
+    ok, desc = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
+    assert ok and "kernel=sm" in desc and "threads=256" in desc, desc
+    ar = 16 if M <= 16 else 32
+    assert f"tile={ar}x32" in desc, desc
+    gx, gy = map(int, re.search(r"grid=(\d+)x(\d+)", desc).groups())
+    assert (gx, gy) == (-(-N // 32), 1)
+    lds = int(re.search(r"lds=(\d+)", desc).group(1))
+    assert lds == 2 * 4 * (ar * 144 + 1024 * -(-32 * W_UNITS[fmt] // 64))
+    chunks = int(re.search(r"k_steps=(\d+)", desc).group(1))
+    assert chunks == -(-(K // 32) // 4)
+    wg = int(re.search(r"wg_per_cu=(\d+)", desc).group(1))
+    assert wg == min(4, (160 * 1024) // lds)   # one wave per SIMD each, 128 registers
+    split = int(re.search(r"split_k=(\d+)", desc).group(1))
+    assert split == (2 if 2 * gx <= wg * 256 and chunks >= 16 else 1)
+    assert "ws_bytes=0" in desc
+
+
+def test_batch_decode_set_counts_32_row_groups():
+    """A GEMM set at batch-decode sizes: each member takes whole 32-row
+    groups (a workgroup never holds rows of two members)."""
+    ok, desc = mmq.plan_for_limits(mmq.FMT_Q4_K, 16, 3584 + 33, 3584, LDS_GFX950, 256)
+    assert ok and "grid=114x1" in desc, desc
 
 
 @pytest.mark.parametrize("M,q8_skips,kquant_skips", [
-    (9, True, True), (64, True, True), (96, True, True),   # one row tile, 1-3 of its 4 wave rows past M
+    (33, True, True), (64, True, True), (96, True, True),  # one row tile, 1-2 of its 4 wave rows past M
     (97, False, False), (128, False, False),               # every wave row holds rows
     (192, True, True),                                     # 2 of 8 wave rows idle: the 1/4 share
     (200, True, False), (2000, True, False),               # 1 idle wave row
@@ -320,24 +360,26 @@ def test_guard_plans_with_the_kernels_registers():
     assert ok and "wg_per_cu=1" in desc, desc
 
 
-@pytest.mark.parametrize("M", [1, 8, 9, 2048])
+@pytest.mark.parametrize("M", [1, 8, 9, 32, 33, 2048])
 def test_guard_refuses_kernels_that_spill(M):
     """A kernel that needs scratch missed its register budget: refused
     before launch, for the tile and the matvec kernel alike."""
     ok, why = mmq.plan_for_limits(mmq.FMT_Q4_K, M, 3584, 3584, LDS_GFX950, 256, vgprs=128, scratch=16)
     assert not ok and "scratch" in why and "refused" in why, why
-    assert ("matvec" in why) == (M <= 8)
+    assert ("matvec" in why) == (M <= 8) and ("batch-decode" in why) == (9 <= M <= 32)
 
 
-@pytest.mark.parametrize("M", [1, 8, 9, 2048])
+@pytest.mark.parametrize("M", [1, 8, 9, 32, 33, 2048])
 def test_q6_K_plans(M):
     """Q6_K (16-element scale groups, no min term): the Q8_0 LDS layout for
     the tile kernel (the group scales fill the scale area), the matvec for
-    M <= 8, whole super-blocks."""
+    M <= 8, the batch-decode kernel for 9 <= M <= 32, whole super-blocks."""
     ok, desc = mmq.plan_for_limits(mmq.FMT_Q6_K, M, 18944, 3584, LDS_GFX950, 256)
     assert ok and "fmt=Q6_K" in desc, desc
     if M <= 8:
         assert "kernel=mv" in desc, desc
+    elif M <= 32:
+        assert "kernel=sm" in desc, desc
     else:
         assert "kernel=mmq" in desc and int(re.search(r"lds=(\d+)", desc).group(1)) == 77824, desc
     ok, why = mmq.plan_for_limits(mmq.FMT_Q6_K, M, 300, 3584 + 32, LDS_GFX950, 256)
