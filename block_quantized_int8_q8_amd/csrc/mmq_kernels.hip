@@ -346,20 +346,25 @@ __device__ __forceinline__ ActDma act_dma_offsets_gather(int kb, int wv, int lan
     return o;
 }
 
-template <int FMT>
+// VOFF: the k-step's offset goes into the lane offset instead of the scalar
+// one, so that the buffer's range check covers it: kernels whose last k-step
+// may hold fewer than KB blocks (the bytes past a row's last block then lie
+// past the activations' end for the last row, and read as zero).
+template <int FMT, bool VOFF = false>
 __device__ __forceinline__ void dma_activations(__amdgpu_buffer_rsrc_t rx, const ActDma &o, int ks, uint8_t *buf,
                                                 int wv, int piece) {
     // piece 0, 1: the wave's two code slices; 2: its header slice; -1: all
     using L = Lds<FMT>;
-    const int soff = ks * KB * 36;
+    const int koff = ks * KB * 36;
+    const int soff = VOFF ? 0 : koff, voff = VOFF ? koff : 0;
 #pragma unroll
     for (int i = 0; i < 2; i++)
         if (piece < 0 || piece == i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + (2 * wv + i) * 1024), 16, o.code_off[i],
-                                                     soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + (2 * wv + i) * 1024), 16,
+                                                     o.code_off[i] + voff, soff, 0, 0);
     if (piece < 0 || piece == 2)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + L::OFF_A_HDR + wv * 256), 4, o.hdr_off, soff,
-                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + L::OFF_A_HDR + wv * 256), 4, o.hdr_off + voff,
+                                                 soff, 0, 0);
 }
 
 // Weights pass through registers instead (fetched one k-step ahead, stored
@@ -912,7 +917,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     // barrier they fetch step ks+2.
     // Buffer (ks+1)%2 was last read by step ks-1, which every wave finished
     // before the previous barrier.
-    dma_activations<FMT>(rx, adma, ks0, lds0, wv, -1);
+    dma_activations<FMT, TAIL || DOTS>(rx, adma, ks0, lds0, wv, -1);
     load_w(ks0);
     store_w(ks0, lds0);
     if (nloc > 1) load_w(ks0 + 1);
@@ -942,7 +947,8 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
             if (!wave_live) {
                 if (j + 1 < nloc) {
 #pragma unroll
-                    for (int piece = 0; piece < 3; piece++) dma_activations<FMT>(rx, adma, ks + 1, nxt, wv, piece);
+                    for (int piece = 0; piece < 3; piece++)
+                        dma_activations<FMT, TAIL || DOTS>(rx, adma, ks + 1, nxt, wv, piece);
                     store_w(ks + 1, nxt);
                 }
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1028,7 +1034,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
             // together at the top or bottom of the step they were measured to
             // cost 8-10 % more.
             if (j + 1 < nloc) {
-                if ((st & 1) && st < 6) dma_activations<FMT>(rx, adma, ks + 1, nxt, wv, st >> 1);
+                if ((st & 1) && st < 6) dma_activations<FMT, TAIL || DOTS>(rx, adma, ks + 1, nxt, wv, st >> 1);
                 if (st == 6) store_w(ks + 1, nxt);
             }
             if (!live) continue;
@@ -1757,10 +1763,12 @@ __device__ __forceinline__ void small_dma(__amdgpu_buffer_rsrc_t rx, int xcode, 
                                           __amdgpu_buffer_rsrc_t rw, int wshift, int kb, int wave, int lane,
                                           int u, uint8_t *buf, SmallDmaOffs<FMT> &wo) {
     using L = SmallLds<FMT>;
-    const int soff = u * 4 * 36;   // the chunk's 4 blocks
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + 1024 * wave), 16, xcode, soff, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + L::OFF_HDR + 256 * (wave & 1)), 4, xhdr, soff, 0,
-                                             0);
+    // the chunk's 4 blocks, in the lane offset: the buffer's range check
+    // covers it (a Q8_0 row's last chunk may reach past the last token)
+    const int cu = u * 4 * 36;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + 1024 * wave), 16, xcode + cu, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + L::OFF_HDR + 256 * (wave & 1)), 4, xhdr + cu, 0,
+                                             0, 0);
     constexpr int kUnits = 32 * L::W_UNITS;
 #pragma unroll
     for (int i = 0; i < SmallDmaOffs<FMT>::N; i++) {
