@@ -364,8 +364,9 @@ def graph_time(fn, n: int, reps: int = 4) -> float:
 
 
 def time_decode(M: int, fmt_name: str, steps: int, warmup: int, check: bool = True):
-    """The 7B layer's projections at decode size (M <= 32 tokens: the matvec
-    kernels up to 8, the batch-decode kernel above), one format: one
+    """The 7B layer's projections at decode size (the matvec kernels up to 8
+    tokens, the batch-decode kernel above: up to 32 for every GEMM, up to 128
+    for the narrow ones), one format: one
     quantize per distinct input and one GEMM launch per input group (q+k+v,
     o, gate+up, down).  These kernels stream every weight byte once, so
     their roofline is HBM: `weight_gbs` is weight bytes / GEMM time.  The
@@ -655,7 +656,7 @@ def main():
                     help="fmt:MxNxK GEMMs timed in the same run ('' for none)")
     ap.add_argument("--layer-m", default="512,2048,8192",
                     help="token counts at which the 7B layer GEMM set is timed ('' for none)")
-    ap.add_argument("--decode", default="q4_K:1,q8_0:1,q4_K:8,q6_K:1,q4_K:16,q4_K:32",
+    ap.add_argument("--decode", default="q4_K:1,q8_0:1,q4_K:8,q6_K:1,q4_K:16,q4_K:32,q4_K:64",
                     help="format:M pairs of the timed decode-size layer ('' for none)")
     ap.add_argument("--moe", default="q4_K,q8_0",
                     help="weight formats of the timed 128-expert MoE layer ('' for none)")

@@ -2134,7 +2134,19 @@ __global__ __launch_bounds__(kSmThreads) void k_mmsm(const uint8_t *__restrict__
     __shared__ __attribute__((aligned(16))) uint8_t lds3[NST > 3 ? S::STAGE : 16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int bx = int(blockIdx.x);
+    // M > 32: the workgroup's 32-row group bx and activation row block yb
+    // (rows 32 yb .. 32 yb + 31).  The Y row blocks of a group are 8 ids
+    // apart, so that they run on one XCD at about the same time and the
+    // later ones find the weight rows in its L2 (ids go to the XCDs in turn);
+    // ids past the last group (the grid is padded to whole groups of 8) exit.
+    static_assert(kSmRowBlock == 32, "row blocks of one MFMA operand");
+    int bx = int(blockIdx.x), yb = 0;
+    if (AR == 32 && M > kSmRowBlock) {
+        const int Y = (M + 31) >> 5, r = bx % (8 * Y);
+        bx = bx / (8 * Y) * 8 + (r & 7);
+        yb = r >> 3;
+        if (bx >= set.tile_start[set.count]) return;
+    }
     int gi = 0;
     for (int i = 1; i < set.count; i++)
         if (bx >= set.tile_start[i]) gi = i;
@@ -2143,7 +2155,8 @@ __global__ __launch_bounds__(kSmThreads) void k_mmsm(const uint8_t *__restrict__
     const int64_t wrow = weight_row_bytes(FMT, K);
     // weight rows past N read as zero (scale 0) and are never stored
     const WBuf rwb = weight_rsrc(set.w[gi] + int64_t(n0) * wrow, int64_t(N - n0) * wrow);
-    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq, int64_t(M) * kb * 36);
+    const int m0 = 32 * yb, Mb = min(M - m0, AR);   // the block's activation rows
+    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq + int64_t(m0) * kb * 36, int64_t(Mb) * kb * 36);
     SmActOffs<AR> xo;
 #pragma unroll
     for (int i = 0; i < AR / 8; i++) {
@@ -2155,9 +2168,9 @@ __global__ __launch_bounds__(kSmThreads) void k_mmsm(const uint8_t *__restrict__
         const int hi = 64 * i + lane;
         xo.hdr[i] = (hi >> 2) * kb * 36 + (hi & 3) * 36;
     }
-    // register groups holding activation rows: 2 (M <= 16), else 3 or 4 (a
-    // select of constants, so the epilogue's group tests fold)
-    const int ng = AR == 16 ? 2 : (M > 24 ? 4 : 3);
+    // register groups holding activation rows: 2 (M <= 16), else 2-4 (a
+    // select of constants, so the epilogue's first group tests fold)
+    const int ng = AR == 16 ? 2 : (Mb > 24 ? 4 : Mb > 16 ? 3 : 2);
     const int nunits = (kb + 3) >> 2, slices = kSmWaves * int(gridDim.z);
     const int sq = int(blockIdx.z) * kSmWaves + wave;
     const int c0 = nunits * sq / slices, c1 = nunits * (sq + 1) / slices;
@@ -2235,11 +2248,11 @@ __global__ __launch_bounds__(kSmThreads) void k_mmsm(const uint8_t *__restrict__
 #pragma unroll
         for (int w = 1; w < kSmWaves; w++) v += lds_at<float>(lds0, 4 * ((w * 16 + r) * 64 + lane));
         const int m = 8 * wave + 4 * g + i;
-        if (m < M && n < N) {
+        if (m < Mb && n < N) {
             if (split)
-                unsafeAtomicAdd(out + int64_t(m) * N + n, v);
+                unsafeAtomicAdd(out + int64_t(m0 + m) * N + n, v);
             else
-                out[int64_t(m) * N + n] = v;
+                out[int64_t(m0 + m) * N + n] = v;
         }
     }
 }

@@ -109,7 +109,18 @@ inline bool mv_on_mfma(int fmt, int64_t M, int64_t N, int64_t K) {
 // DMA in chunks of 4 blocks, two stages deep, and add their partial sums in
 // wave order at the end.  A 128-row tile would leave 3 of its 4 wave rows
 // idle here and give too few workgroups for the narrow GEMMs.
-constexpr int kSmMaxM = 32;
+// Above 32 rows the kernel takes the activations in blocks of 32 rows, one
+// workgroup per (32 weight rows, row block), up to kSmMaxM rows, for GEMMs
+// (sets) whose 128-column tiles would be fewer than the CUs: there the tile
+// kernel has too few workgroups, while on wider GEMMs it is faster (the 7B
+// layer at M = 64, Q4_K, us, tile kernel -> this one: gate+up 78.0 -> 85.3;
+// q+k+v 34.4 -> 18.8, o 31.1 -> 15.4, down 128.7 -> 42.8; at M = 128 gate+up
+// 94.4 -> 150.7, down 123.8 -> 72.6).
+constexpr int kSmMaxM = 128;
+constexpr int kSmRowBlock = 32;
+inline bool sm_takes(int64_t M, int64_t N, int cu_count) {
+    return M > kMvMaxM && M <= kSmMaxM && (M <= kSmRowBlock || (N + kTileN - 1) / kTileN < cu_count);
+}
 constexpr int kSmRows = 32;      // weight rows per workgroup
 constexpr int kSmWaves = 4;      // its waves, one K-slice each
 constexpr int kSmThreads = 64 * kSmWaves;
@@ -276,7 +287,7 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
         *p = q;
         return true;
     }
-    if (allow_mv && M <= kSmMaxM) {
+    if (allow_mv && sm_takes(M, N, cu_count)) {
         q.kernel = KERNEL_SM;
         q.tile_m = sm_act_rows(M);
         q.tile_n = kSmRows;
@@ -284,6 +295,8 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
         q.blocks_per_stage = 4;
         q.lds_bytes = sm_lds_bytes(fmt, q.tile_m) + extra_lds;
         q.grid_x = (N + kSmRows - 1) / kSmRows;
+        if (M > kSmRowBlock)   // row blocks of 32; the groups padded to whole groups of 8
+            q.grid_x = (q.grid_x + 7) / 8 * 8 * ((M + kSmRowBlock - 1) / kSmRowBlock);
         q.grid_y = 1;
         q.k_steps = (K / 32 + 3) / 4;   // chunks of 4 blocks (the last may be partial: Q8_0)
         q.steps_per_split = q.k_steps;
@@ -366,14 +379,18 @@ inline bool make_plan_multi(int fmt, int64_t M, int count, const int64_t *Ns, in
     // matvec kernel, 32-row groups for the batch-decode kernel (a group never
     // holds rows of two GEMMs)
     const bool mv = allow_mv && M >= 1 && M <= kMvMaxM;
-    const bool sm = allow_mv && M > kMvMaxM && M <= kSmMaxM;
+    // the batch-decode kernel's choice for the set as a whole, on the N the
+    // final plan below receives (whole 32-row groups per member)
+    int64_t rows32 = 0;
+    for (int g = 0; g < count; g++) rows32 += (Ns[g] > 0 ? (Ns[g] + kSmRows - 1) / kSmRows : 0) * kSmRows;
+    const bool sm = allow_mv && sm_takes(M, rows32, cu_count);
     int64_t tiles = 0;
     for (int g = 0; g < count; g++) {
         Plan one;
         if (!make_plan(fmt, M, Ns[g], K, lds_limit, cu_count, extra_lds, &one, why, why_len, allow_mv, fit))
             return false;
         tile_start[g] = int(tiles);
-        tiles += mv ? Ns[g] : sm ? (Ns[g] + kSmRows - 1) / kSmRows : one.grid_x;
+        tiles += mv ? Ns[g] : sm ? (Ns[g] + kSmRows - 1) / kSmRows : (Ns[g] + kTileN - 1) / kTileN;
         if (tiles > (int64_t(1) << 30)) return fail("too many output columns in the GEMM set");
     }
     tile_start[count] = int(tiles);

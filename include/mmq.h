@@ -103,8 +103,10 @@ int mmq_quantize_q8_1(const float *x, void *y, int64_t M, int64_t K, void *strea
  * activation rows as its other operand, the per-block scale arithmetic
  * above, four K-slices each summed in ascending order and then added in
  * slice order; narrow shapes split K over two workgroups more, added into
- * the zeroed output by fp32 atomics as above.  The result is the same on
- * every run. */
+ * the zeroed output by fp32 atomics as above.  The same kernel takes
+ * 33 <= M <= 128 in blocks of 32 activation rows when N has fewer 128-wide
+ * tiles than the device has compute units.  The result is the same on every
+ * run. */
 int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out,
                   int64_t M, int64_t N, int64_t K, void *stream);
 
@@ -160,19 +162,20 @@ int mmq_gemm_q6_K(const void *x_q8_1, const void *w_q6_K, float *out,
  * layer pipeline of "13 . r7-r8 raw-byte MMQ kernel": quantize once per
  * distinct input, e.g. the q, k and v projections, or gate and up), computed
  * by one launch whose grid covers the column tiles of all of them (for
- * M <= 8, the output rows of all of them, in the matrix-vector kernel; for
- * 9 <= M <= 32, their groups of 32 output rows, a group never holding rows
- * of two of them).
+ * M <= 8, the output rows of all of them, in the matrix-vector kernel; in
+ * the batch-decode kernel, their groups of 32 output rows, a group never
+ * holding rows of two of them).
  *   fmt: MMQ_FMT_Q8_0, MMQ_FMT_Q4_K, MMQ_FMT_Q5_K or MMQ_FMT_Q6_K; count: 1..8;
  *   x_q8_1: M x (K/32) q8_1 blocks, shared;
  *   w[g]: N[g] x K weights of format fmt; out[g]: M x N[g] fp32 row-major,
  *   fully overwritten; the arrays w, out and N are host memory (read during
  *   the call), the tensors device memory.
  * Each out[g] equals what mmq_gemm_q8_0 / _q4_K / _q5_K / _q6_K would write
- * for (x, w[g], N[g]), except that split-K, and for M <= 8 the choice between
- * the two few-row kernels (Q4_K, Q5_K), are decided for the set as a whole
- * (the summation order, and so the last bits, can then differ from the
- * member's own launch).
+ * for (x, w[g], N[g]), except that split-K, for M <= 8 the choice between
+ * the two few-row kernels (Q4_K, Q5_K), and for 33 <= M <= 128 the choice
+ * between the batch-decode and the tile kernel, are decided for the set as
+ * a whole (the summation order, and so the last bits, can then differ from
+ * the member's own launch).
  * Refused (nothing launched) when any member would be refused. */
 int mmq_gemm_multi(int fmt, const void *x_q8_1, int count, const void *const *w, float *const *out,
                    const int64_t *N, int64_t M, int64_t K, void *stream);
