@@ -2168,9 +2168,10 @@ __global__ __launch_bounds__(kSmThreads) void k_mmsm(const uint8_t *__restrict__
         const int hi = 64 * i + lane;
         xo.hdr[i] = (hi >> 2) * kb * 36 + (hi & 3) * 36;
     }
-    // register groups holding activation rows: 2 (M <= 16), else 2-4 (a
-    // select of constants, so the epilogue's first group tests fold)
-    const int ng = AR == 16 ? 2 : (Mb > 24 ? 4 : Mb > 16 ? 3 : 2);
+    // register groups holding activation rows: 2 (M <= 16), else 3 or 4 (a
+    // select of constants, so the epilogue's first two group tests fold; a
+    // last row block of at most 16 rows computes one group of zero rows)
+    const int ng = AR == 16 ? 2 : (Mb > 24 ? 4 : 3);
     const int nunits = (kb + 3) >> 2, slices = kSmWaves * int(gridDim.z);
     const int sq = int(blockIdx.z) * kSmWaves + wave;
     const int c0 = nunits * sq / slices, c1 = nunits * (sq + 1) / slices;
