@@ -1855,17 +1855,27 @@ __device__ __forceinline__ uint2 lds_field8(const uint8_t *buf, int b) {
 // w0; wrow is this lane's weight row counted from the weight buffer's start.
 // With AR = 16 the lanes of rows 16-31 read rows 0-15 again: their D rows lie
 // in register groups 2 and 3, which the epilogue of ng <= 2 never reads.
-template <int FMT, int AR = 32>
+//
+// CB = 8 (K-quants only): the stage holds 8-block chunks (whole
+// super-blocks), the weight window of a row is its raw super-block and the
+// activation rows hold 16 code units (XOR-swizzled by row % 16) and 8
+// headers; `sub` picks the chunk's half computed here and u is the 4-block
+// unit index of that half.
+template <int FMT, int AR = 32, int CB = 4>
 __device__ __forceinline__ void small_compute(const uint8_t *buf, int a0, int h0, int w0, int wrow, f32x16 &acc,
-                                              const i32x16 &srcC, int wshift, int kb, int lane, int u, int ng) {
+                                              const i32x16 &srcC, int wshift, int kb, int lane, int u, int ng,
+                                              int sub = 0) {
     static_assert(AR == 16 || AR == 32, "16 or 32 staged activation rows");
-    using L = SmallLds<FMT>;
+    static_assert(CB == 4 || (CB == 8 && FMT != FMT_Q8_0), "4-block chunks, or whole super-blocks");
+    constexpr int W_ROW = CB == 4 ? SmallLds<FMT>::W_ROW : 16 * sm_w_units_sb(FMT);
     const int l32 = lane & 31, g = lane >> 5, ar = l32 & (AR - 1);
     // the row whose header this lane broadcasts
     const int xr = (8 * ((lane & 15) >> 2) + (lane & 3) + 4 * g) & (AR - 1);
-    const int wr = w0 + l32 * L::W_ROW;   // this lane's weight row
-    const int hdr = h0 + 16 * xr;         // its 4 block headers
-    auto a_unit = [&](int j, int h) { return a0 + 16 * (8 * ar + ((2 * j + h) ^ (ar & 7))); };
+    const int wr = w0 + l32 * W_ROW;                // this lane's weight row
+    const int hdr = h0 + 4 * CB * xr + 16 * sub;    // its 4 block headers of the half
+    auto a_unit = [&](int j, int h) {
+        return a0 + 16 * (2 * CB * ar + ((2 * (4 * sub + j) + h) ^ (ar & (2 * CB - 1))));
+    };
     if constexpr (FMT == FMT_Q8_0) {
         const int sh = (wshift + wrow * kb * 34 + u * 4 * 34) & 3;   // the row's chunk start, 0 or 2
 #pragma unroll
@@ -1883,22 +1893,27 @@ __device__ __forceinline__ void small_compute(const uint8_t *buf, int a0, int h0
     } else if constexpr (FMT == FMT_Q6_K) {
         const int hh = u & 1;
         const int w6 = wr + ((wshift + (wrow * (kb >> 3) + (u >> 1)) * 210) & 3);
-        // window offsets: low bits at 0, high bits at 80, scales and d at 128 (each from its dword)
-        const float d = h2f(lds_at<unsigned short>(buf, w6 + 128 + 16));
-        const uint2 hb[2] = {lds_field8(buf, w6 + 80 + 8 * g), lds_field8(buf, w6 + 80 + 16 + 8 * g)};
+        // window offsets (CB = 4): low bits at 0, high bits at 80, scales at
+        // 128, d at 144 (each from its dword); the raw super-block (CB = 8):
+        // low bits of the half at 64 hh, its high bits at 128 + 32 hh,
+        // scales at 192, d at 208
+        constexpr int SC = CB == 4 ? 128 : 192, DO = CB == 4 ? 144 : 208;
+        const int LO = CB == 4 ? 0 : 64 * hh, HI = CB == 4 ? 80 : 128 + 32 * hh;
+        const float d = h2f(lds_at<unsigned short>(buf, w6 + DO));
+        const uint2 hb[2] = {lds_field8(buf, w6 + HI + 8 * g), lds_field8(buf, w6 + HI + 16 + 8 * g)};
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             const float xs = h2f(lds_at<uint32_t>(buf, hdr + 4 * q));
 #pragma unroll
             for (int h = 0; h < 2; h++) {
-                const uint2 lb = lds_field8(buf, w6 + 32 * (q & 1) + 16 * h + 8 * g);
+                const uint2 lb = lds_field8(buf, w6 + LO + 32 * (q & 1) + 16 * h + 8 * g);
                 const int ns = 4 * (q >> 1);
                 const uint32_t c0 = ((lb.x >> ns) & 0x0F0F0F0Fu) | (((hb[h].x >> (2 * q)) & 0x03030303u) << 4);
                 const uint32_t c1 = ((lb.y >> ns) & 0x0F0F0F0Fu) | (((hb[h].y >> (2 * q)) & 0x03030303u) << 4);
                 long b6 = __builtin_bit_cast(long, make_uint2(q6k_centre(c0), q6k_centre(c1)));
                 long a6 = lds_at<long>(buf, a_unit(q, h) + 8 * g);
                 // scale of group 2q + h of the half: byte 192 + 8hh + 2q + h of the super-block
-                const float ws = d * (float)lds_at<int8_t>(buf, w6 + 128 + 8 * hh + 2 * q + h);
+                const float ws = d * (float)lds_at<int8_t>(buf, w6 + SC + 8 * hh + 2 * q + h);
                 const i32x16 D6 = mfma16_at(a6, b6, srcC);
                 small_epilogue(acc, D6, ws, -kMagic * ws, xs, ng);
                 asm volatile("" : "+v"(acc));
@@ -1908,7 +1923,9 @@ __device__ __forceinline__ void small_compute(const uint8_t *buf, int a0, int h0
         const int hs = u & 1;
         const u32x4 hd = lds_at<u32x4>(buf, wr);
         const float d = h2f(hd.x), dmin = h2f(hd.x >> 16);
-        constexpr int C0 = FMT == FMT_Q5_K ? 48 : 16;   // the code groups' place in the row's window
+        // the code groups' place in the row's window (the raw super-block:
+        // those of half hs)
+        const int C0 = (FMT == FMT_Q5_K ? 48 : 16) + (CB == 8 ? 64 * hs : 0);
         // this lane's k-half of the row, an opaque offset: the high-bit and
         // code reads would otherwise share address arithmetic deep enough to
         // lose their alias scope (Q5_K)
@@ -2056,7 +2073,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_moe_small(const uint8_t *__re
 //
 // Each wave takes a K-slice of the 32 rows: slice q = 4 * blockIdx.z + wave
 // of S = 4 * gridDim.z holds chunks [nunits * q / S, nunits * (q + 1) / S) of
-// 4 blocks.  The waves share nothing while they run: each stages its own
+// CB blocks (4, or a whole super-block for Q4_K with 16 staged rows: one
+// contiguous span per weight row).  The waves share nothing while they run: each stages its own
 // activation codes and headers and its rows' weight windows (the layouts of
 // the small-remainder kernel) into LDS of its own by DMA, two stages deep,
 // with no barrier.  At the end the four partial sums are added in wave
@@ -2069,14 +2087,17 @@ __global__ __launch_bounds__(kSmallThreads) void k_moe_small(const uint8_t *__re
 // so that the buffer's range check sees the whole offset (the last chunk of
 // a Q8_0 row with K % 128 != 0 reaches past the row's end).
 // ---------------------------------------------------------------------------
-template <int FMT, int AR>
+template <int FMT, int AR, int CB = sm_cb(FMT, AR)>
 struct SmLds {
     static_assert(SmallLds<FMT>::W_UNITS == sm_w_units(FMT), "plan and kernel weight windows disagree");
-    static constexpr int A = 0;                             // AR rows x 8 code units of 16 bytes
-    static constexpr int H = AR * 128;                      // AR rows x 4 block headers
-    static constexpr int W = AR * 144;                      // the 32 weight rows' windows
-    static constexpr int WAVE = W + SmallLds<FMT>::W_WAVE;  // one wave's stage
+    static constexpr int W_UNITS = CB == 4 ? sm_w_units(FMT) : sm_w_units_sb(FMT);
+    static constexpr int W_DMA = (32 * W_UNITS + 63) / 64;   // weight DMA instructions per wave
+    static constexpr int A = 0;                      // AR rows x 2 CB code units of 16 bytes
+    static constexpr int H = AR * CB * 32;           // AR rows x CB block headers
+    static constexpr int W = H + AR * CB * 4;        // the 32 weight rows' windows
+    static constexpr int WAVE = W + 1024 * W_DMA;    // one wave's stage
     static constexpr int STAGE = kSmWaves * WAVE;
+    static constexpr int NC = AR * CB * 2 / 64, NH = AR * CB / 64;   // activation DMA instructions
 };
 static_assert(kSmStages * SmLds<FMT_Q8_0, 32>::STAGE == sm_lds_bytes(FMT_Q8_0, 32) &&
                   kSmStages * SmLds<FMT_Q4_K, 16>::STAGE == sm_lds_bytes(FMT_Q4_K, 16) &&
@@ -2085,35 +2106,53 @@ static_assert(kSmStages * SmLds<FMT_Q8_0, 32>::STAGE == sm_lds_bytes(FMT_Q8_0, 3
                   kSmStages <= 4,
               "plan and kernel LDS disagree");
 
+template <int N>
+struct DmaOffs {
+    int v[N];
+};
+
 // A lane's activation DMA sources at chunk 0: code unit f = 64 i + lane is
 // slot f of the stage (row f / 8, unit (2j + h) = (f % 8) xor (row % 8)),
 // header slot 64 i + lane is row (64 i + lane) / 4, block lane % 4.
-template <int AR>
+template <int FMT, int AR>
 struct SmActOffs {
-    int code[AR / 8];
-    int hdr[AR / 16];
+    int code[SmLds<FMT, AR>::NC];
+    int hdr[SmLds<FMT, AR>::NH];
 };
 
+// Source offset of 16-byte unit p of weight row `row`'s chunk u (CB = 8: its
+// super-block u, from the dword below its first byte).
+template <int FMT, int CB>
+__device__ __forceinline__ int sm_w_unit(int wshift, int kb, int row, int u, int p) {
+    if constexpr (CB == 4) {
+        return small_w_unit<FMT>(wshift, kb, row, u, p);
+    } else if constexpr (FMT == FMT_Q6_K) {
+        return ((wshift + (row * (kb >> 3) + u) * 210) & ~3) + 16 * p;
+    } else {
+        return (row * (kb >> 3) + u) * (FMT == FMT_Q4_K ? 144 : 176) + 16 * p;
+    }
+}
+
 template <int FMT, int AR>
-__device__ __forceinline__ void sm_dma(__amdgpu_buffer_rsrc_t rx, const SmActOffs<AR> &xo, __amdgpu_buffer_rsrc_t rw,
-                                       int wshift, int kb, int lane, int u, uint8_t *buf, int base,
-                                       SmallDmaOffs<FMT> &wo) {
+__device__ __forceinline__ void sm_dma(__amdgpu_buffer_rsrc_t rx, const SmActOffs<FMT, AR> &xo,
+                                       __amdgpu_buffer_rsrc_t rw, int wshift, int kb, int lane, int u, uint8_t *buf,
+                                       int base, DmaOffs<SmLds<FMT, AR>::W_DMA> &wo) {
     using S = SmLds<FMT, AR>;
-    using L = SmallLds<FMT>;
-    const int cu = u * 4 * 36;   // the chunk's 4 blocks
+    constexpr int CB = sm_cb(FMT, AR);
+    const int cu = u * CB * 36;   // the chunk's CB blocks
 #pragma unroll
-    for (int i = 0; i < AR / 8; i++)
+    for (int i = 0; i < S::NC; i++)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + base + S::A + 1024 * i), 16, xo.code[i] + cu,
                                                  0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < AR / 16; i++)
+    for (int i = 0; i < S::NH; i++)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + base + S::H + 256 * i), 4, xo.hdr[i] + cu, 0,
                                                  0, 0);
-    constexpr int kUnits = 32 * L::W_UNITS;
+    constexpr int kUnits = 32 * S::W_UNITS;
 #pragma unroll
-    for (int i = 0; i < SmallDmaOffs<FMT>::N; i++) {
+    for (int i = 0; i < S::W_DMA; i++) {
         const int f = min(64 * i + lane, kUnits - 1);
-        wo.v[i] = small_w_unit<FMT>(wshift, kb, f / L::W_UNITS, u, f % L::W_UNITS);
+        wo.v[i] = sm_w_unit<FMT, CB>(wshift, kb, f / S::W_UNITS, u, f % S::W_UNITS);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(buf + base + S::W + 1024 * i), 16, wo.v[i], 0, 0,
                                                  0);
     }
@@ -2157,22 +2196,23 @@ __global__ __launch_bounds__(kSmThreads) void k_mmsm(const uint8_t *__restrict__
     const WBuf rwb = weight_rsrc(set.w[gi] + int64_t(n0) * wrow, int64_t(N - n0) * wrow);
     const int m0 = 32 * yb, Mb = min(M - m0, AR);   // the block's activation rows
     const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq + int64_t(m0) * kb * 36, int64_t(Mb) * kb * 36);
-    SmActOffs<AR> xo;
+    constexpr int CB = sm_cb(FMT, AR);
+    SmActOffs<FMT, AR> xo;
 #pragma unroll
-    for (int i = 0; i < AR / 8; i++) {
-        const int f = 64 * i + lane, r = f >> 3, q = (f & 7) ^ (r & 7);
+    for (int i = 0; i < S::NC; i++) {
+        const int f = 64 * i + lane, r = f / (2 * CB), q = (f % (2 * CB)) ^ (r & (2 * CB - 1));
         xo.code[i] = r * kb * 36 + (q >> 1) * 36 + 4 + 16 * (q & 1);
     }
 #pragma unroll
-    for (int i = 0; i < AR / 16; i++) {
+    for (int i = 0; i < S::NH; i++) {
         const int hi = 64 * i + lane;
-        xo.hdr[i] = (hi >> 2) * kb * 36 + (hi & 3) * 36;
+        xo.hdr[i] = (hi / CB) * kb * 36 + (hi % CB) * 36;
     }
     // register groups holding activation rows: 2 (M <= 16), else 3 or 4 (a
     // select of constants, so the epilogue's first two group tests fold; a
     // last row block of at most 16 rows computes one group of zero rows)
     const int ng = AR == 16 ? 2 : (Mb > 24 ? 4 : 3);
-    const int nunits = (kb + 3) >> 2, slices = kSmWaves * int(gridDim.z);
+    const int nunits = CB == 4 ? (kb + 3) >> 2 : kb >> 3, slices = kSmWaves * int(gridDim.z);
     const int sq = int(blockIdx.z) * kSmWaves + wave;
     const int c0 = nunits * sq / slices, c1 = nunits * (sq + 1) / slices;
     const int base = wave * S::WAVE;
@@ -2195,7 +2235,7 @@ __global__ __launch_bounds__(kSmThreads) void k_mmsm(const uint8_t *__restrict__
     if (c1 > c0) {   // wave-uniform: a K-slice with chunks
         // the first NST - 1 chunks (clamped to the slice)
         {
-            SmallDmaOffs<FMT> wo;
+            DmaOffs<S::W_DMA> wo;
             sm_dma<FMT, AR>(rx, xo, rwb.r, rwb.shift, kb, lane, c0, stage(Parity<0>{}), base, wo);
             if constexpr (NST > 2) sm_dma<FMT, AR>(rx, xo, rwb.r, rwb.shift, kb, lane, min(c0 + 1, c1 - 1),
                                                    stage(Parity<1>{}), base, wo);
@@ -2211,16 +2251,19 @@ __global__ __launch_bounds__(kSmThreads) void k_mmsm(const uint8_t *__restrict__
         // the same DMA instructions.
         auto chunk = [&](auto parity, int u) {
             constexpr int P = decltype(parity)::value;
-            SmallDmaOffs<FMT> wo;
+            DmaOffs<S::W_DMA> wo;
             // the reads of chunk u - 1 from the stage refilled here have returned
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             sm_dma<FMT, AR>(rx, xo, rwb.r, rwb.shift, kb, lane, min(u + NST - 1, c1 - 1),
                             stage(Parity<P + NST - 1>{}), base, wo);
-            if (u < c1)
-                small_compute<FMT, AR>(stage(parity), base + S::A, base + S::H, base + S::W, lane & 31, acc, srcC,
-                                       rwb.shift, kb, lane, u, ng);
+            if (u < c1) {
 #pragma unroll
-            for (int i = 0; i < SmallDmaOffs<FMT>::N; i++) asm volatile("" ::"v"(wo.v[i]));
+                for (int sub = 0; sub < CB / 4; sub++)
+                    small_compute<FMT, AR, CB>(stage(parity), base + S::A, base + S::H, base + S::W, lane & 31, acc,
+                                               srcC, rwb.shift, kb, lane, (CB / 4) * u + sub, ng, sub);
+            }
+#pragma unroll
+            for (int i = 0; i < S::W_DMA; i++) asm volatile("" ::"v"(wo.v[i]));
         };
         for (int u = c0; u < c1; u += NST) {
             chunk(Parity<0>{}, u);

@@ -106,8 +106,8 @@ inline bool mv_on_mfma(int fmt, int64_t M, int64_t N, int64_t K) {
 // kernel of 32 weight rows per workgroup, one int8 MFMA per block with the
 // activation rows as A (16 or 32 of them staged, sm_act_rows).  Its four
 // waves take a K-slice each, staging their operands into LDS of their own by
-// DMA in chunks of 4 blocks, two stages deep, and add their partial sums in
-// wave order at the end.  A 128-row tile would leave 3 of its 4 wave rows
+// DMA in chunks of 4 blocks (or whole super-blocks, sm_cb), two stages deep,
+// and add their partial sums in wave order at the end.  A 128-row tile would leave 3 of its 4 wave rows
 // idle here and give too few workgroups for the narrow GEMMs.
 // Above 32 rows the kernel takes the activations in blocks of 32 rows, one
 // workgroup per (32 weight rows, row block), up to kSmMaxM rows, for GEMMs
@@ -135,11 +135,23 @@ constexpr int sm_act_rows(int64_t M) { return M <= 16 ? 16 : 32; }
 // dword below the first; K-quants: the super-block header and the chunk's
 // code half; Q6_K: low bits, high bits, scales and d of the half)
 constexpr int sm_w_units(int fmt) { return fmt == FMT_Q8_0 ? 9 : fmt == FMT_Q4_K ? 5 : fmt == FMT_Q5_K ? 7 : 10; }
-// one wave's stage: activation codes (128 B per row) and headers (16 B per
-// row), then the 32 weight rows' units padded to whole 64-lane DMA
-// instructions of 16 bytes
+// ... of a whole K-quant super-block (Q6_K: 210 bytes from the dword below
+// the first)
+constexpr int sm_w_units_sb(int fmt) { return fmt == FMT_Q4_K ? 9 : fmt == FMT_Q5_K ? 11 : 14; }
+// Blocks per chunk: 4, or whole super-blocks (one contiguous 144-byte span
+// per weight row, ~1.6 times the bytes per cache line the two half chunks
+// touch) for Q4_K with 16 staged rows.  Measured on the 7B layer (us per
+// layer, 4 -> 8 blocks): Q4_K M = 16 96.4 -> 89.9 (gate+up 38.1 -> 33.2);
+// slower wherever the larger stage costs workgroups per CU: Q4_K M = 32
+// 126.5 -> 146.7, Q5_K M = 16 gate+up 42.5 -> 49.0, Q6_K M = 16 122.8 ->
+// 140.5.
+constexpr int sm_cb(int fmt, int ar) { return fmt == FMT_Q4_K && ar == 16 ? 8 : 4; }
+// one wave's stage: activation codes (32 B per row and block) and headers
+// (4 B per row and block), then the 32 weight rows' units padded to whole
+// 64-lane DMA instructions of 16 bytes
 constexpr int64_t sm_wave_stage_bytes(int fmt, int ar) {
-    return int64_t(ar) * 144 + 1024 * ((32 * sm_w_units(fmt) + 63) / 64);
+    return int64_t(ar) * sm_cb(fmt, ar) * 36 +
+           1024 * ((32 * (sm_cb(fmt, ar) == 8 ? sm_w_units_sb(fmt) : sm_w_units(fmt)) + 63) / 64);
 }
 constexpr int64_t sm_lds_bytes(int fmt, int ar) { return int64_t(kSmStages) * kSmWaves * sm_wave_stage_bytes(fmt, ar); }
 // Split K over two workgroups (grid z, fp32 atomics into a zeroed output)
@@ -292,18 +304,19 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
         q.tile_m = sm_act_rows(M);
         q.tile_n = kSmRows;
         q.threads = kSmThreads;
-        q.blocks_per_stage = 4;
+        q.blocks_per_stage = sm_cb(fmt, q.tile_m);
         q.lds_bytes = sm_lds_bytes(fmt, q.tile_m) + extra_lds;
         q.grid_x = (N + kSmRows - 1) / kSmRows;
         if (M > kSmRowBlock)   // row blocks of 32; the groups padded to whole groups of 8
             q.grid_x = (q.grid_x + 7) / 8 * 8 * ((M + kSmRowBlock - 1) / kSmRowBlock);
         q.grid_y = 1;
-        q.k_steps = (K / 32 + 3) / 4;   // chunks of 4 blocks (the last may be partial: Q8_0)
+        q.k_steps = (K / 32 + q.blocks_per_stage - 1) / q.blocks_per_stage;   // chunks (Q8_0: the last may be partial)
         q.steps_per_split = q.k_steps;
         if (q.grid_x > INT32_MAX) return fail("too many output rows");
         if (q.lds_bytes > lds_limit) return fail("plan needs more LDS per workgroup than the device allows: refused");
         if (!check_fit(q)) return false;
-        if (2 * q.grid_x <= int64_t(q.wg_per_cu) * cu_count && q.k_steps >= 2 * kSmWaves * kSmMinChunksPerWave) {
+        if (2 * q.grid_x <= int64_t(q.wg_per_cu) * cu_count &&
+            K / 32 >= 4 * 2 * kSmWaves * kSmMinChunksPerWave) {
             q.split_k = 2;
             q.steps_per_split = (q.k_steps + 1) / 2;
         }

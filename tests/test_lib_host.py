@@ -211,8 +211,9 @@ def test_batch_decode_sizes_plan_the_small_m_kernel(fmt, M, N, K):
     LDS stages per wave of activation codes and headers (144 B per row) and
     the 32 weight rows' 16-byte units padded to whole 64-lane DMA
     instructions; K in chunks of 4 blocks, split over two workgroups when
-    the row groups fill at most half of the resident slots and each of the
-    eight waves keeps two chunks."""
+    the row groups fill at most half of the resident slots and K holds at
+    least 64 blocks (two 4-block chunks for each of eight waves); Q4_K with
+    16 staged rows takes whole super-blocks per chunk instead."""
     ok, desc = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
     if M > 32 and -(-N // 128) >= 256:   # a wide GEMM above 32 rows: the tile kernel
         assert ok and "kernel=mmq" in desc, desc
@@ -225,14 +226,18 @@ def test_batch_decode_sizes_plan_the_small_m_kernel(fmt, M, N, K):
     # above 32 rows: one workgroup per (group, row block of 32), the groups
     # padded to whole groups of 8
     assert (gx, gy) == ((groups if M <= 32 else -(-groups // 8) * 8 * -(-M // 32)), 1)
+    # chunks of 4 blocks, or of whole super-blocks (Q4_K, 16 staged rows)
+    cb = 8 if fmt == mmq.FMT_Q4_K and ar == 16 else 4
+    units = 9 if cb == 8 else W_UNITS[fmt]
+    assert f"blocks_per_stage={cb}" in desc, desc
     lds = int(re.search(r"lds=(\d+)", desc).group(1))
-    assert lds == 2 * 4 * (ar * 144 + 1024 * -(-32 * W_UNITS[fmt] // 64))
+    assert lds == 2 * 4 * (ar * cb * 36 + 1024 * -(-32 * units // 64))
     chunks = int(re.search(r"k_steps=(\d+)", desc).group(1))
-    assert chunks == -(-(K // 32) // 4)
+    assert chunks == -(-(K // 32) // cb)
     wg = int(re.search(r"wg_per_cu=(\d+)", desc).group(1))
     assert wg == min(4, (160 * 1024) // lds)   # one wave per SIMD each, 128 registers
     split = int(re.search(r"split_k=(\d+)", desc).group(1))
-    assert split == (2 if 2 * gx <= wg * 256 and chunks >= 16 else 1)
+    assert split == (2 if 2 * gx <= wg * 256 and K // 32 >= 64 else 1)
     assert "ws_bytes=0" in desc
 
 
