@@ -118,8 +118,25 @@ inline bool mv_on_mfma(int fmt, int64_t M, int64_t N, int64_t K) {
 // 94.4 -> 150.7, down 123.8 -> 72.6).
 constexpr int kSmMaxM = 128;
 constexpr int kSmRowBlock = 32;
-inline bool sm_takes(int64_t M, int64_t N, int cu_count) {
-    return M > kMvMaxM && M <= kSmMaxM && (M <= kSmRowBlock || (N + kTileN - 1) / kTileN < cu_count);
+// At decode sizes (M <= 8) the batch-decode kernel also replaces the
+// matvecs on the large launches where it was measured faster (the 7B layer,
+// µs, matvec -> batch decode): Q8_0 from M = 4 on the wide (N >= 16384) and
+// long-K launches (gate+up at M = 4 47.8 -> 39.7, M = 8 69.7 -> 42.4; down
+// at M = 8 37.7 -> 23.1; at M = 3 down lost, 22.1 -> 24.4); Q6_K gate+up from
+// M = 4 (52.7 -> 46.5) and its long-K down from M = 7 (M = 6 31.0 -> 33.0,
+// M = 8 36.0 -> 32.5); Q4_K and Q5_K long-K launches (where the matrix-core
+// matvec does not go) from M = 6 (Q4_K down at M = 8 27.6 -> 21.6, Q5_K 30.2
+// -> 27.1).  The narrow launches (q+k+v, o) stay on the matvecs, which win
+// there (Q8_0 q+k+v at M = 5 13.1 against 16.1).
+inline bool sm_few_rows(int fmt, int64_t M, int64_t N, int64_t K) {
+    const bool wide = N >= 16384, long_k = K > kMvqMaxK;
+    if (fmt == FMT_Q8_0) return M >= 4 && (wide || long_k);
+    if (fmt == FMT_Q6_K) return (M >= 4 && wide) || (M >= 7 && long_k);
+    return M >= 6 && long_k;
+}
+inline bool sm_takes(int fmt, int64_t M, int64_t N, int64_t K, int cu_count) {
+    if (M <= kMvMaxM) return M >= 1 && sm_few_rows(fmt, M, N, K);
+    return M <= kSmMaxM && (M <= kSmRowBlock || (N + kTileN - 1) / kTileN < cu_count);
 }
 constexpr int kSmRows = 32;      // weight rows per workgroup
 constexpr int kSmWaves = 4;      // its waves, one K-slice each
@@ -279,27 +296,7 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
     if (cu_count < 1) return fail("device reports no compute units");
     Plan q;
     q.fmt = fmt;
-    if (allow_mv && M <= kMvMaxM) {
-        q.kernel = KERNEL_MV;
-        q.tile_m = int(M);
-        q.tile_n = 1;
-        q.threads = kMvThreads;
-        q.blocks_per_stage = 2;
-        q.mv_mfma = mv_on_mfma(fmt, M, N, K);
-        q.lds_bytes = (q.mv_mfma ? kMvqLds : 0) + extra_lds;
-        const int64_t rows_per_wg = q.mv_mfma ? kMvqRows : int64_t(kMvWaves) * mv_rows_per_wave(M);
-        q.grid_x = (N + rows_per_wg - 1) / rows_per_wg;
-        q.mv_rows_per_wave = q.mv_mfma ? 0 : mv_rows_per_wave(M);
-        q.grid_y = 1;
-        q.k_steps = (K / 32 + 1) / 2;   // block pairs per row (an odd last block is a unit of its own)
-        q.steps_per_split = q.k_steps;
-        if (q.grid_x > INT32_MAX) return fail("too many output rows");
-        if (q.lds_bytes > lds_limit) return fail("plan needs more LDS per workgroup than the device allows: refused");
-        if (!check_fit(q)) return false;
-        *p = q;
-        return true;
-    }
-    if (allow_mv && sm_takes(M, N, cu_count)) {
+    if (allow_mv && sm_takes(fmt, M, N, K, cu_count)) {
         q.kernel = KERNEL_SM;
         q.tile_m = sm_act_rows(M);
         q.tile_n = kSmRows;
@@ -320,6 +317,26 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
             q.split_k = 2;
             q.steps_per_split = (q.k_steps + 1) / 2;
         }
+        *p = q;
+        return true;
+    }
+    if (allow_mv && M <= kMvMaxM) {
+        q.kernel = KERNEL_MV;
+        q.tile_m = int(M);
+        q.tile_n = 1;
+        q.threads = kMvThreads;
+        q.blocks_per_stage = 2;
+        q.mv_mfma = mv_on_mfma(fmt, M, N, K);
+        q.lds_bytes = (q.mv_mfma ? kMvqLds : 0) + extra_lds;
+        const int64_t rows_per_wg = q.mv_mfma ? kMvqRows : int64_t(kMvWaves) * mv_rows_per_wave(M);
+        q.grid_x = (N + rows_per_wg - 1) / rows_per_wg;
+        q.mv_rows_per_wave = q.mv_mfma ? 0 : mv_rows_per_wave(M);
+        q.grid_y = 1;
+        q.k_steps = (K / 32 + 1) / 2;   // block pairs per row (an odd last block is a unit of its own)
+        q.steps_per_split = q.k_steps;
+        if (q.grid_x > INT32_MAX) return fail("too many output rows");
+        if (q.lds_bytes > lds_limit) return fail("plan needs more LDS per workgroup than the device allows: refused");
+        if (!check_fit(q)) return false;
         *p = q;
         return true;
     }
@@ -391,12 +408,12 @@ inline bool make_plan_multi(int fmt, int64_t M, int count, const int64_t *Ns, in
     // tile units: 128-column tiles for the MMQ kernel, single rows for the
     // matvec kernel, 32-row groups for the batch-decode kernel (a group never
     // holds rows of two GEMMs)
-    const bool mv = allow_mv && M >= 1 && M <= kMvMaxM;
     // the batch-decode kernel's choice for the set as a whole, on the N the
     // final plan below receives (whole 32-row groups per member)
     int64_t rows32 = 0;
     for (int g = 0; g < count; g++) rows32 += (Ns[g] > 0 ? (Ns[g] + kSmRows - 1) / kSmRows : 0) * kSmRows;
-    const bool sm = allow_mv && sm_takes(M, rows32, cu_count);
+    const bool sm = allow_mv && sm_takes(fmt, M, rows32, K, cu_count);
+    const bool mv = allow_mv && !sm && M >= 1 && M <= kMvMaxM;
     int64_t tiles = 0;
     for (int g = 0; g < count; g++) {
         Plan one;

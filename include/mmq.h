@@ -97,7 +97,10 @@ int mmq_quantize_q8_1(const float *x, void *y, int64_t M, int64_t K, void *strea
  * kernel instead: each weight row is read once for all M activation rows
  * and its blocks are summed per lane and then across the 64 lanes of a
  * wave, a fixed order (the same on every run) other than ascending.
- * mmq_plan_describe reports kernel=mv for such shapes.
+ * mmq_plan_describe reports kernel=mv for such shapes.  The large decode
+ * launches (N >= 16384 or K > 8192) take the batch-decode kernel below from
+ * the M where it measured faster: M >= 4 for Q8_0, M >= 4 (wide) or 7
+ * (long K) for Q6_K, M >= 6 for the long-K launches of Q4_K and Q5_K.
  * 9 <= M <= 32 (batched decode) runs a matrix-core kernel of 32 weight rows
  * per workgroup instead (kernel=sm): one int8 MFMA per block with the
  * activation rows as its other operand, the per-block scale arithmetic

@@ -474,10 +474,11 @@ def test_gemm_multi_unsplit_member_equals_single_launch():
 @pytest.mark.parametrize("M", [1, 2, 3, 8])
 @pytest.mark.parametrize("N,K", [(1, 256), (300, 768), (3584, 3584), (129, 18944)])
 def test_matvec_matches_oracle(fmt, M, N, K):
-    """Decode-sized inputs (M <= 8) run the matrix-vector kernel: every
-    element written and checked as a reordered sum (the blocks of a row are
-    split over 64 lanes, so bit identity is not expected)."""
-    assert _kernel(fmt, M, N, K) == "mv"
+    """Decode-sized inputs (M <= 8) run the matrix-vector kernel (the
+    long-K shape at M = 8: the batch-decode kernel): every element written
+    and checked as a reordered sum (the blocks of a row are split over 64
+    lanes, so bit identity is not expected)."""
+    assert _kernel(fmt, M, N, K) == ("sm" if M == 8 and K > 8192 else "mv")
     _say(f"matvec fmt={fmt} M={M} N={N} K={K}")
     x = inputs.activations(M, K, 110 + M)
     xq = oracle.quantize_q8_1(x)
@@ -502,7 +503,7 @@ def test_kernel_boundaries():
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M,Ns,K", [(8, (257, 130, 33), 512), (5, (3, 1, 2), 256), (6, (1, 129), 18944)])
+@pytest.mark.parametrize("M,Ns,K", [(8, (257, 130, 33), 512), (5, (3, 1, 2), 256), (6, (1, 129), 8192)])
 def test_matvec_set_rows_straddling_members(fmt, M, Ns, K):
     """M >= 5 runs two output rows per wave, so with odd member widths a
     wave's two rows belong to different GEMMs of the set (and the last wave

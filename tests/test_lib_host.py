@@ -172,7 +172,8 @@ def test_moe_workspace_bytes_refuses(T, topk, E):
 
 
 @pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K])
-@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (1, 3584, 3584), (2, 4608, 3584), (5, 7, 512), (8, 18944, 3584), (3, 5, 18944)])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (1, 3584, 3584), (2, 4608, 3584), (5, 7, 512), (8, 18944, 3584), (3, 5, 18944),
+                                   (3, 18944, 3584)])
 def test_decode_sizes_plan_the_matvec_kernel(fmt, M, N, K):
     """M <= 8: the matvec kernel, four waves per 256-thread workgroup, one
     output row per wave for M <= 4 and two for M >= 5 (the wave's rows share
@@ -180,6 +181,9 @@ def test_decode_sizes_plan_the_matvec_kernel(fmt, M, N, K):
     matrix core instead: 32 weight rows per workgroup, 4 KiB of LDS for its
     four K-slices' partial sums."""
     ok, desc = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
+    if fmt == mmq.FMT_Q8_0 and M >= 4 and N >= 16384:   # the batch-decode kernel (below)
+        assert ok and "kernel=sm" in desc, desc
+        return
     assert ok and "kernel=mv" in desc, desc
     gx, gy = map(int, re.search(r"grid=(\d+)x(\d+)", desc).groups())
     assert "threads=256" in desc and "split_k=1" in desc
@@ -239,6 +243,21 @@ def test_batch_decode_sizes_plan_the_small_m_kernel(fmt, M, N, K):
     split = int(re.search(r"split_k=(\d+)", desc).group(1))
     assert split == (2 if 2 * gx <= wg * 256 and K // 32 >= 64 else 1)
     assert "ws_bytes=0" in desc
+
+
+@pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K, mmq.FMT_Q5_K, mmq.FMT_Q6_K])
+@pytest.mark.parametrize("M", range(1, 9))
+@pytest.mark.parametrize("N,K", [(37888, 3584), (3584, 18944), (4608, 3584), (3584, 3584)])
+def test_decode_sizes_take_the_batch_decode_kernel_where_measured_faster(fmt, M, N, K):
+    """M <= 8: the batch-decode kernel on the wide and long-K launches where
+    it measured faster than the matvecs (Q8_0 from M = 4; Q6_K wide from
+    M = 4, long-K from M = 7; Q4_K and Q5_K long-K from M = 6), the
+    matvecs everywhere else."""
+    wide, long_k = N >= 16384, K > 8192
+    want = {mmq.FMT_Q8_0: M >= 4 and (wide or long_k),
+            mmq.FMT_Q6_K: (M >= 4 and wide) or (M >= 7 and long_k)}.get(fmt, M >= 6 and long_k)
+    ok, desc = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
+    assert ok and f"kernel={'sm' if want else 'mv'}" in desc, desc
 
 
 def test_batch_decode_set_counts_32_row_groups():
@@ -389,15 +408,16 @@ def test_guard_refuses_kernels_that_spill(M):
     assert ("matvec" in why) == (M <= 8) and ("batch-decode" in why) == (9 <= M <= 128)
 
 
-@pytest.mark.parametrize("M", [1, 8, 9, 32, 33, 128, 129, 2048])
+@pytest.mark.parametrize("M", [1, 3, 4, 8, 9, 32, 33, 128, 129, 2048])
 def test_q6_K_plans(M):
     """Q6_K (16-element scale groups, no min term): the Q8_0 LDS layout for
     the tile kernel (the group scales fill the scale area), the matvec for
-    M <= 8, the batch-decode kernel for 9 <= M <= 128 (148 column tiles:
-    fewer than the CUs), whole super-blocks."""
+    M <= 3, the batch-decode kernel for 4 <= M <= 128 at this width
+    (18944 rows; 148 column tiles, fewer than the CUs), whole
+    super-blocks."""
     ok, desc = mmq.plan_for_limits(mmq.FMT_Q6_K, M, 18944, 3584, LDS_GFX950, 256)
     assert ok and "fmt=Q6_K" in desc, desc
-    if M <= 8:
+    if M <= 3:
         assert "kernel=mv" in desc, desc
     elif M <= 128:
         assert "kernel=sm" in desc, desc
