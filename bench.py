@@ -365,7 +365,7 @@ def graph_time(fn, n: int, reps: int = 4) -> float:
 
 def time_decode(M: int, fmt_name: str, steps: int, warmup: int, check: bool = True):
     """The 7B layer's projections at decode size (the matvec kernels up to 8
-    tokens, the batch-decode kernel above: up to 32 for every GEMM, up to 128
+    tokens, the batch-decode kernel above: up to 32 for every GEMM, up to 192
     for the narrow ones), one format: one
     quantize per distinct input and one GEMM launch per input group (q+k+v,
     o, gate+up, down).  These kernels stream every weight byte once, so

@@ -115,8 +115,10 @@ inline bool mv_on_mfma(int fmt, int64_t M, int64_t N, int64_t K) {
 // kernel has too few workgroups, while on wider GEMMs it is faster (the 7B
 // layer at M = 64, Q4_K, us, tile kernel -> this one: gate+up 78.0 -> 85.3;
 // q+k+v 34.4 -> 18.8, o 31.1 -> 15.4, down 128.7 -> 42.8; at M = 128 gate+up
-// 94.4 -> 150.7, down 123.8 -> 72.6).
-constexpr int kSmMaxM = 128;
+// 94.4 -> 150.7, down 123.8 -> 72.6).  The layer with the narrow GEMMs on
+// this kernel: M = 160 347 -> 311 us, M = 192 352 -> 320, M = 256 351 ->
+// 353 (Q4_K); Q8_0 M = 192 333 -> 306.
+constexpr int kSmMaxM = 192;
 constexpr int kSmRowBlock = 32;
 // At decode sizes (M <= 8) the batch-decode kernel also replaces the
 // matvecs on the large launches where it was measured faster (the 7B layer,

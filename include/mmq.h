@@ -107,7 +107,7 @@ int mmq_quantize_q8_1(const float *x, void *y, int64_t M, int64_t K, void *strea
  * above, four K-slices each summed in ascending order and then added in
  * slice order; narrow shapes split K over two workgroups more, added into
  * the zeroed output by fp32 atomics as above.  The same kernel takes
- * 33 <= M <= 128 in blocks of 32 activation rows when N has fewer 128-wide
+ * 33 <= M <= 192 in blocks of 32 activation rows when N has fewer 128-wide
  * tiles than the device has compute units.  The result is the same on every
  * run. */
 int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out,
@@ -175,7 +175,7 @@ int mmq_gemm_q6_K(const void *x_q8_1, const void *w_q6_K, float *out,
  *   the call), the tensors device memory.
  * Each out[g] equals what mmq_gemm_q8_0 / _q4_K / _q5_K / _q6_K would write
  * for (x, w[g], N[g]), except that split-K, for M <= 8 the choice between
- * the two few-row kernels (Q4_K, Q5_K), and for 33 <= M <= 128 the choice
+ * the two few-row kernels (Q4_K, Q5_K), and for 33 <= M <= 192 the choice
  * between the batch-decode and the tile kernel, are decided for the set as
  * a whole (the summation order, and so the last bits, can then differ from
  * the member's own launch).

@@ -203,7 +203,7 @@ def _split_k(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M,N,K", [(160, 64, 3584), (129, 257, 1024), (200, 300, 2048), (200, 100, 18944),
+@pytest.mark.parametrize("M,N,K", [(200, 64, 3584), (250, 257, 1024), (200, 300, 2048), (200, 100, 18944),
                                    (512, 512, 3584)])
 def test_split_k_gemm_matches_oracle(fmt, M, N, K):
     """Shapes with too few output tiles for the device run split-K: without
@@ -240,7 +240,7 @@ def _run_multi(fmt, xq_dev, w_dev, Ns, M, K, workspace=None):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M,Ns,K", [(160, (64,), 3584), (200, (100,), 18944), (200, (300,), 2048),
+@pytest.mark.parametrize("M,Ns,K", [(200, (64,), 3584), (200, (100,), 18944), (200, (300,), 2048),
                                     (512, (512,), 3584), (512, (3584,), 18944), (512, (3584, 512, 512), 3584),
                                     (300, (600,), 3616)])
 def test_split_workspace_matches_oracle_and_repeats(fmt, M, Ns, K):
@@ -323,20 +323,20 @@ def test_gemm_hand_cases():
     xq = _gpu_quantize(x)
     assert _run_gemm(mmq.FMT_Q8_0, xq, w, 1, 1, K)[0, 0] == expect
     # the batch-decode kernel (9 <= M <= 32 in one row block, 33 in two) and
-    # the tile kernel (M = 129) as well: the same row repeated
-    for m in (9, 33, 129):
+    # the tile kernel (M = 193) as well: the same row repeated
+    for m in (9, 33, 193):
         xm = np.repeat(x, m, axis=0)
         assert (_run_gemm(mmq.FMT_Q8_0, _gpu_quantize(xm), w, m, 1, K)[:, 0] == expect).all()
     x, w, K, expect = golden_cases.gemm_q4_K_case()
     xq = _gpu_quantize(x)
     assert _run_gemm(mmq.FMT_Q4_K, xq, w, 1, 1, K)[0, 0] == expect
-    for m in (9, 33, 129):
+    for m in (9, 33, 193):
         xm = np.repeat(x, m, axis=0)
         assert (_run_gemm(mmq.FMT_Q4_K, _gpu_quantize(xm), w, m, 1, K)[:, 0] == expect).all()
     x, w, K, expect = golden_cases.gemm_q5_K_case()
     xq = _gpu_quantize(x)
     assert _run_gemm(mmq.FMT_Q5_K, xq, w, 1, 1, K)[0, 0] == expect
-    for m in (9, 33, 129):
+    for m in (9, 33, 193):
         xm = np.repeat(x, m, axis=0)
         assert (_run_gemm(mmq.FMT_Q5_K, _gpu_quantize(xm), w, m, 1, K)[:, 0] == expect).all()
 
@@ -489,12 +489,12 @@ def test_matvec_matches_oracle(fmt, M, N, K):
 
 def test_kernel_boundaries():
     """M = 8 is the last matvec size, 9 and 32 the first and last
-    batch-decode sizes in one row block, 33 and 128 the first and last in
-    row blocks of 32 (a narrow GEMM: 5 column tiles), 129 the first tiled
+    batch-decode sizes in one row block, 33 and 192 the first and last in
+    row blocks of 32 (a narrow GEMM: 5 column tiles), 193 the first tiled
     one; all agree with the oracle on the same weights."""
     fmt, N, K = mmq.FMT_Q4_K, 640, 2048
     w = _weights(fmt, N, K, 130)
-    for M, kern in ((8, "mv"), (9, "sm"), (32, "sm"), (33, "sm"), (128, "sm"), (129, "mmq")):
+    for M, kern in ((8, "mv"), (9, "sm"), (32, "sm"), (33, "sm"), (192, "sm"), (193, "mmq")):
         assert _kernel(fmt, M, N, K) == kern
         xq = oracle.quantize_q8_1(inputs.activations(M, K, 131))
         rep = metrics.report(_run_gemm(fmt, xq, w, M, N, K), _oracle_gemm(fmt, xq, w, M, N, K))
@@ -758,7 +758,7 @@ def test_q8_0_gemm_any_whole_blocks_bit_identical(K):
     assert rep["bit_identical_fraction"] == 1.0
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 100, 3616), (160, 130, 2080)])
+@pytest.mark.parametrize("M,N,K", [(200, 100, 3616), (250, 130, 2080)])
 def test_q8_0_split_k_any_whole_blocks(M, N, K):
     assert _split_k(mmq.FMT_Q8_0, M, N, K) > 1 and _kernel(mmq.FMT_Q8_0, M, N, K) == "mmq"
     _say(f"q8_0 split-K any K: M={M} N={N} K={K}")
@@ -782,7 +782,9 @@ def test_q8_0_matvec_any_whole_blocks(M, N, K):
 
 
 def test_q8_0_gemm_multi_any_whole_blocks():
-    M, Ns, K = 129, (257, 130), 288
+    """A Q8_0 set on the tile kernel (M > 192) with K % 128 != 0, unsplit:
+    every member bit-identical to the oracle."""
+    M, Ns, K = 250, (257, 130), 288
     _say(f"q8_0 gemm multi any K: M={M} Ns={Ns} K={K}")
     xq = oracle.quantize_q8_1(inputs.activations(M, K, 280))
     ws = [inputs.q8_0_weights(n, K, 281 + g) for g, n in enumerate(Ns)]
@@ -795,7 +797,7 @@ def test_q8_0_gemm_multi_any_whole_blocks():
         assert rep["bit_identical_fraction"] == 1.0
 
 
-# ------------------------------------------------------------------ batch decode (9 <= M <= 32)
+# ------------------------------------------------------------------ batch decode
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M", [9, 16, 17, 31, 32])
@@ -922,7 +924,7 @@ def test_q6_K_hand_case():
     x, w, K, expect = golden_cases.gemm_q6_K_case()
     xq = _gpu_quantize(x)
     assert _run_gemm(mmq.FMT_Q6_K, xq, w, 1, 1, K)[0, 0] == expect
-    for m in (9, 33, 129):
+    for m in (9, 33, 193):
         xm = np.repeat(x, m, axis=0)
         assert (_run_gemm(mmq.FMT_Q6_K, _gpu_quantize(xm), w, m, 1, K)[:, 0] == expect).all()
 

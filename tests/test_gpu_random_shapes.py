@@ -1,6 +1,6 @@
 """Seeded random shapes through whichever kernel the planner picks for them:
 the matvecs (M <= 8), the batch-decode kernel (9 <= M <= 32, and row blocks
-of 32 up to M = 128 for narrow GEMMs), the tile kernel (with and without
+of 32 up to M = 192 for narrow GEMMs), the tile kernel (with and without
 split-K) and GEMM sets mixing member widths.  Every output element must be
 written and lie within the fp32 accumulation bound of the exact value (the
 bound the oracle itself is pinned to), and within the 1e-5 normalized error

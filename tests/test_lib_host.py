@@ -38,7 +38,7 @@ def test_library_carries_gfx950_code_only():
 @pytest.mark.parametrize("fmt,M,N,K", [
     (mmq.FMT_Q8_0, 2048, 3584, 3584),
     (mmq.FMT_Q4_K, 2048, 18944, 3584), (mmq.FMT_Q4_K, 2048, 3584, 18944),
-    (mmq.FMT_Q4_K, 8192, 512, 3584), (mmq.FMT_Q8_0, 129, 1, 256),
+    (mmq.FMT_Q4_K, 8192, 512, 3584), (mmq.FMT_Q8_0, 193, 1, 256),
 ])
 def test_plans_for_benchmark_shapes_fit(fmt, M, N, K):
     ok, desc = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
@@ -59,7 +59,7 @@ def test_plans_for_benchmark_shapes_fit(fmt, M, N, K):
     (512, 4608, 3584, 3, 10),       # the q+k+v set (144 tiles): 3 slices of >= 8 k-steps
     (2048, 512, 3584, 4, 7),        # 64 tiles
     (8192, 512, 3584, 1, 28),       # 256 tiles: one per CU already
-    (160, 256, 512, 1, 4),          # 4 k-steps: too short to split
+    (200, 256, 512, 1, 4),          # 4 k-steps: too short to split
     (200, 100, 18944, 37, 4),       # two tiles, 148 k-steps
 ])
 def test_split_k_planning(M, N, K, split, steps):
@@ -128,7 +128,7 @@ def test_guard_refuses_bad_shapes(fmt, M, N, K, needle):
 
 
 @pytest.mark.parametrize("M,K", [(64, 32), (200, 96), (2048, 288), (2048, 3616), (5, 3616), (100, 3616),
-                                 (160, 3616)])
+                                 (160, 3616), (193, 3616)])
 def test_q8_0_plans_any_whole_number_of_blocks(M, K):
     """Q8_0 contracts over any whole number of 32-blocks ("When the Product
     Won't Collapse", section 2): the tile kernel's last k-step may hold 1-3
@@ -137,11 +137,11 @@ def test_q8_0_plans_any_whole_number_of_blocks(M, K):
     ok, desc = mmq.plan_for_limits(mmq.FMT_Q8_0, M, 300, K, LDS_GFX950, 256)
     assert ok, desc
     kb = K // 32
-    assert f"tail={int(kb % 4 != 0 and M > 128)}" in desc, desc
+    assert f"tail={int(kb % 4 != 0 and M > 192)}" in desc, desc
     steps = int(re.search(r"k_steps=(\d+)", desc).group(1))
     if M <= 8:
         assert "kernel=mv" in desc and steps == (kb + 1) // 2
-    elif M <= 128:   # N = 300: a narrow GEMM, the batch-decode kernel
+    elif M <= 192:   # N = 300: a narrow GEMM, the batch-decode kernel
         assert "kernel=sm" in desc and steps == -(-kb // 4)
     else:
         assert "kernel=mmq" in desc and steps == -(-kb // 4)
@@ -195,20 +195,20 @@ def test_decode_sizes_plan_the_matvec_kernel(fmt, M, N, K):
         assert f"mv_rows_per_wave={rows}" in desc and "mv_mfma=0" in desc and "lds=0" in desc, desc
         assert (gx, gy) == (-(-N // (4 * rows)), 1)
     # the same shape with one more row runs the batch-decode kernel, up to
-    # M = 128 for these narrow GEMMs, and from M = 129 on the tile kernel
+    # M = 192 for these narrow GEMMs, and from M = 193 on the tile kernel
     assert "kernel=sm" in mmq.plan_for_limits(fmt, 9, N, K, LDS_GFX950, 256)[1]
-    assert "kernel=sm" in mmq.plan_for_limits(fmt, 128, N, K, LDS_GFX950, 256)[1]
-    assert "kernel=mmq" in mmq.plan_for_limits(fmt, 129, N, K, LDS_GFX950, 256)[1]
+    assert "kernel=sm" in mmq.plan_for_limits(fmt, 192, N, K, LDS_GFX950, 256)[1]
+    assert "kernel=mmq" in mmq.plan_for_limits(fmt, 193, N, K, LDS_GFX950, 256)[1]
 
 
 W_UNITS = {mmq.FMT_Q8_0: 9, mmq.FMT_Q4_K: 5, mmq.FMT_Q5_K: 7, mmq.FMT_Q6_K: 10}
 
 
 @pytest.mark.parametrize("fmt", [mmq.FMT_Q8_0, mmq.FMT_Q4_K, mmq.FMT_Q5_K, mmq.FMT_Q6_K])
-@pytest.mark.parametrize("M", [9, 16, 17, 24, 25, 32, 33, 64, 100, 128])
+@pytest.mark.parametrize("M", [9, 16, 17, 24, 25, 32, 33, 64, 100, 128, 192])
 @pytest.mark.parametrize("N,K", [(3584, 18944), (37888, 3584), (4608, 3584), (300, 256), (1, 2048)])
 def test_batch_decode_sizes_plan_the_small_m_kernel(fmt, M, N, K):
-    """9 <= M <= 32, and up to 128 for GEMMs of fewer 128-column tiles than
+    """9 <= M <= 32, and up to 192 for GEMMs of fewer 128-column tiles than
     CUs: the batch-decode kernel, one 256-thread workgroup per 32 weight
     rows (and row block of 32 activation rows above M = 32), 16 activation
     rows staged up to M = 16 and 32 above; two
@@ -405,21 +405,21 @@ def test_guard_refuses_kernels_that_spill(M):
     before launch, for the tile and the matvec kernel alike."""
     ok, why = mmq.plan_for_limits(mmq.FMT_Q4_K, M, 3584, 3584, LDS_GFX950, 256, vgprs=128, scratch=16)
     assert not ok and "scratch" in why and "refused" in why, why
-    assert ("matvec" in why) == (M <= 8) and ("batch-decode" in why) == (9 <= M <= 128)
+    assert ("matvec" in why) == (M <= 8) and ("batch-decode" in why) == (9 <= M <= 192)
 
 
-@pytest.mark.parametrize("M", [1, 3, 4, 8, 9, 32, 33, 128, 129, 2048])
+@pytest.mark.parametrize("M", [1, 3, 4, 8, 9, 32, 33, 192, 193, 2048])
 def test_q6_K_plans(M):
     """Q6_K (16-element scale groups, no min term): the Q8_0 LDS layout for
     the tile kernel (the group scales fill the scale area), the matvec for
-    M <= 3, the batch-decode kernel for 4 <= M <= 128 at this width
+    M <= 3, the batch-decode kernel for 4 <= M <= 192 at this width
     (18944 rows; 148 column tiles, fewer than the CUs), whole
     super-blocks."""
     ok, desc = mmq.plan_for_limits(mmq.FMT_Q6_K, M, 18944, 3584, LDS_GFX950, 256)
     assert ok and "fmt=Q6_K" in desc, desc
     if M <= 3:
         assert "kernel=mv" in desc, desc
-    elif M <= 128:
+    elif M <= 192:
         assert "kernel=sm" in desc, desc
     else:
         assert "kernel=mmq" in desc and int(re.search(r"lds=(\d+)", desc).group(1)) == 77824, desc
