@@ -142,7 +142,10 @@ def time_config(cfg, steps: int, warmup: int, check: bool = True, cold: bool = F
 
     step_ms = graph_time(step_in_graph, steps)
     g_avg = span(lambda: gemm(xq, wd, M, N, K, out, stream=stream))
-    q_avg = span(lambda: mmq.quantize_q8_1(xd, xq, stream=stream))
+    # the quantize pass (~6 us at 2048 x 3584) is shorter than the host takes
+    # to issue a launch, so back-to-back eager launches would time the host:
+    # ten launches captured in a HIP graph, replayed (as the step above)
+    q_avg = graph_time(lambda: mmq.quantize_q8_1(xd, xq), steps, reps=10)
     # per launch, evented (median and minimum; each includes the record gap)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
