@@ -2440,6 +2440,16 @@ __global__ __launch_bounds__(256) void k_zero_fill(float *__restrict__ p, int64_
     for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) p[i] = 0.0f;
 }
 
+// The same for the M x N[g] outputs of every GEMM of a set, in one launch
+// (grid y = the set's members): a launch per member costs more than the
+// zeroing itself on the short launches of decode-sized sets.
+__global__ __launch_bounds__(256) void k_zero_fill_set(const GemmSet set, int64_t M) {
+    const int g = int(blockIdx.y);
+    float *__restrict__ p = reinterpret_cast<float *>(set.out[g]);
+    const int64_t n = M * set.N[g];
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) p[i] = 0.0f;
+}
+
 // ---------------------------------------------------------------------------
 // Scratch of the allocation-free MoE entry point: the routing tables of one
 // call (header, tile table, sorted routed-row ids: kNoAllocScratchBytes for
@@ -2592,12 +2602,10 @@ hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const vo
         hipLaunchKernelGGL(k_zero_fill, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
                            reinterpret_cast<float *>(workspace), words);
     } else if (p.split_k > 1 && !dots) {
-        for (int g = 0; g < count; g++) {
-            const int64_t n = M * N[g];
-            const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
-            hipLaunchKernelGGL(k_zero_fill, dim3((unsigned)blocks), dim3(256), 0, stream,
-                               reinterpret_cast<float *>(out[g]), n);
-        }
+        int64_t nmax = 0;
+        for (int g = 0; g < count; g++) nmax = std::max<int64_t>(nmax, M * N[g]);
+        const int64_t blocks = std::min<int64_t>((nmax + 255) / 256, 8192);
+        hipLaunchKernelGGL(k_zero_fill_set, dim3((unsigned)blocks, (unsigned)count), dim3(256), 0, stream, set, M);
     }
     const dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.split_k);
     const dim3 block(p.threads);

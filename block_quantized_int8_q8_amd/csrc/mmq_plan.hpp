@@ -174,9 +174,15 @@ constexpr int64_t sm_wave_stage_bytes(int fmt, int ar) {
 }
 constexpr int64_t sm_lds_bytes(int fmt, int ar) { return int64_t(kSmStages) * kSmWaves * sm_wave_stage_bytes(fmt, ar); }
 // Split K over two workgroups (grid z, fp32 atomics into a zeroed output)
-// when the 32-row groups fill at most half of the resident slots and every
-// wave keeps at least kSmMinChunksPerWave chunks.
+// when the workgroups fill at most half of the resident slots, and K is
+// long (at least kSmSplitLongKb blocks) or the workgroups are fewer than
+// half the CUs with every wave keeping two 4-block chunks.  Measured on the
+// 7B layer's K = 3584 launches (us, split -> not): q+k+v (144 workgroups)
+// at M = 16 11.5 -> 10.4, at M = 32 15.2 -> 14.2; o (112) at M = 16 9.7 ->
+// 10.0, at M = 32 12.4 -> 13.9; at M = 64 (224 and 288 workgroups in two
+// row blocks) o 14.8 -> 14.2.
 constexpr int kSmMinChunksPerWave = 2;
+constexpr int kSmSplitLongKb = 256;
 
 // gfx950 register file: 512 registers per lane per SIMD (arch and
 // accumulation VGPRs together), allocated in granules of 8; at most 8 waves
@@ -315,7 +321,8 @@ inline bool make_plan(int fmt, int64_t M, int64_t N, int64_t K, int64_t lds_limi
         if (q.lds_bytes > lds_limit) return fail("plan needs more LDS per workgroup than the device allows: refused");
         if (!check_fit(q)) return false;
         if (2 * q.grid_x <= int64_t(q.wg_per_cu) * cu_count &&
-            K / 32 >= 4 * 2 * kSmWaves * kSmMinChunksPerWave) {
+            (K / 32 >= kSmSplitLongKb ||
+             (2 * q.grid_x <= cu_count && K / 32 >= 4 * 2 * kSmWaves * kSmMinChunksPerWave))) {
             q.split_k = 2;
             q.steps_per_split = (q.k_steps + 1) / 2;
         }

@@ -894,8 +894,9 @@ def test_batch_decode_set_members_equal_single_launches(fmt):
 def test_batch_decode_layer_set(fmt):
     """The 7B layer's projections at 16 tokens through the batch-decode
     kernel (q+k+v and gate+up as sets, down split over two workgroups):
-    every member equal to its own launch, all within tolerance of the
-    oracle."""
+    every member equal to its own launch wherever the two plans split K
+    alike (the split is decided for the set as a whole), all within
+    tolerance of the oracle."""
     M = 16
     shapes = {g: (n, k) for g, n, k in inputs.LAYER_7B}
     for name, K, gemms in inputs.LAYER_INPUTS:
@@ -904,13 +905,16 @@ def test_batch_decode_layer_set(fmt):
         ws = [_weights(fmt, shapes[g][0], K, inputs.layer_weight_seed(g)) for g in gemms]
         Ns = [shapes[g][0] for g in gemms]
         assert _kernel(fmt, M, Ns[0], K) == "sm"
+        # the set's plan is the plan of one GEMM over its whole 32-row groups
+        set_split = _split_k(fmt, M, sum(-(-n // 32) * 32 for n in Ns), K)
         outs = mmq.gemm_multi(fmt, _to_dev(xq), [_to_dev(w) for w in ws], Ns, M, K)
         torch.cuda.synchronize()
         for g, (n, w) in enumerate(zip(Ns, ws)):
             o = outs[g].cpu().numpy()
             single = mmq.gemm(fmt, _to_dev(xq), _to_dev(w), M, n, K)
             torch.cuda.synchronize()
-            assert np.array_equal(o.view(np.uint32), single.cpu().numpy().view(np.uint32))
+            if _split_k(fmt, M, n, K) == set_split:
+                assert np.array_equal(o.view(np.uint32), single.cpu().numpy().view(np.uint32))
             rep = metrics.report(o, _oracle_gemm(fmt, xq, w, M, n, K))
             _say(gemms[g], rep)
             assert rep["normalized_max_error"] <= metrics.TOL

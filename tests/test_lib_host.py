@@ -215,9 +215,10 @@ def test_batch_decode_sizes_plan_the_small_m_kernel(fmt, M, N, K):
     LDS stages per wave of activation codes and headers (144 B per row) and
     the 32 weight rows' 16-byte units padded to whole 64-lane DMA
     instructions; K in chunks of 4 blocks, split over two workgroups when
-    the row groups fill at most half of the resident slots and K holds at
-    least 64 blocks (two 4-block chunks for each of eight waves); Q4_K with
-    16 staged rows takes whole super-blocks per chunk instead."""
+    the workgroups fill at most half of the resident slots and K is long
+    (256 blocks and more) or the workgroups are fewer than half the CUs
+    (with 64 blocks and more); Q4_K with 16 staged rows takes whole
+    super-blocks per chunk instead."""
     ok, desc = mmq.plan_for_limits(fmt, M, N, K, LDS_GFX950, 256)
     if M > 32 and -(-N // 128) >= 256:   # a wide GEMM above 32 rows: the tile kernel
         assert ok and "kernel=mmq" in desc, desc
@@ -241,7 +242,7 @@ def test_batch_decode_sizes_plan_the_small_m_kernel(fmt, M, N, K):
     wg = int(re.search(r"wg_per_cu=(\d+)", desc).group(1))
     assert wg == min(4, (160 * 1024) // lds)   # one wave per SIMD each, 128 registers
     split = int(re.search(r"split_k=(\d+)", desc).group(1))
-    assert split == (2 if 2 * gx <= wg * 256 and K // 32 >= 64 else 1)
+    assert split == (2 if 2 * gx <= wg * 256 and (K // 32 >= 256 or (2 * gx <= 256 and K // 32 >= 64)) else 1)
     assert "ws_bytes=0" in desc
 
 
