@@ -1861,7 +1861,13 @@ __device__ __forceinline__ uint2 lds_field8(const uint8_t *buf, int b) {
 // activation rows hold 16 code units (XOR-swizzled by row % 16) and 8
 // headers; `sub` picks the chunk's half computed here and u is the 4-block
 // unit index of that half.
-template <int FMT, int AR = 32, int CB = 4>
+//
+// MINMFMA (K-quants): the min term of the half chunk as two fp32 MFMAs
+// (32 x 32 x 2, two blocks each: A = the activation rows' block sums, B =
+// -dmin * m of the weight rows' sub-blocks) into the accumulator, instead of
+// one row-broadcast FMA per register group and block; its sums are then in
+// the matrix core's order, not the oracle's.
+template <int FMT, int AR = 32, int CB = 4, bool MINMFMA = false>
 __device__ __forceinline__ void small_compute(const uint8_t *buf, int a0, int h0, int w0, int wrow, f32x16 &acc,
                                               const i32x16 &srcC, int wshift, int kb, int lane, int u, int ng,
                                               int sub = 0) {
@@ -1955,7 +1961,26 @@ __device__ __forceinline__ void small_compute(const uint8_t *buf, int a0, int h0
             const i32x16 D = mfma_at(af, bf, srcC);
             small_epilogue(acc, D, ws, -kMagic * ws, h2f(xh), ng);
             asm volatile("" : "+v"(acc));
-            small_min(acc, -dm, h2f(xh >> 16), ng);
+            if constexpr (!MINMFMA) {
+                small_min(acc, -dm, h2f(xh >> 16), ng);
+                asm volatile("" : "+v"(acc));
+            }
+        }
+        if constexpr (MINMFMA) {
+            // lane l: A row l % 32 (activation row ar) and B column l % 32
+            // (weight row l32) at k = l / 32 = g: blocks g and 2 + g of the
+            // half chunk, one MFMA each pair
+            const int xrow = h0 + 4 * CB * ar + 16 * sub;
+            const float sa0 = h2f(lds_at<uint32_t>(buf, xrow + 4 * g) >> 16);
+            const float sa1 = h2f(lds_at<uint32_t>(buf, xrow + 8 + 4 * g) >> 16);
+            auto neg_dm = [&](int jj) {
+                const int j = 4 * hs + jj, s8 = 8 * (j & 3);
+                const uint32_t b0 = (hd.y >> s8) & 0xffu, b1 = (hd.z >> s8) & 0xffu, b2 = (hd.w >> s8) & 0xffu;
+                const uint32_t mn = j < 4 ? (b1 & 63u) : ((b2 >> 4) | ((b1 >> 6) << 4));
+                return -(dmin * (float)mn);
+            };
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sa0, neg_dm(g), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sa1, neg_dm(2 + g), acc, 0, 0, 0);
             asm volatile("" : "+v"(acc));
         }
     }
@@ -2259,8 +2284,9 @@ __global__ __launch_bounds__(kSmThreads) void k_mmsm(const uint8_t *__restrict__
             if (u < c1) {
 #pragma unroll
                 for (int sub = 0; sub < CB / 4; sub++)
-                    small_compute<FMT, AR, CB>(stage(parity), base + S::A, base + S::H, base + S::W, lane & 31, acc,
-                                               srcC, rwb.shift, kb, lane, (CB / 4) * u + sub, ng, sub);
+                    small_compute<FMT, AR, CB, kSmMinMfma>(stage(parity), base + S::A, base + S::H, base + S::W,
+                                                           lane & 31, acc, srcC, rwb.shift, kb, lane,
+                                                           (CB / 4) * u + sub, ng, sub);
             }
 #pragma unroll
             for (int i = 0; i < S::W_DMA; i++) asm volatile("" ::"v"(wo.v[i]));

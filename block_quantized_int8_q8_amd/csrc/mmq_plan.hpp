@@ -183,6 +183,10 @@ constexpr int64_t sm_lds_bytes(int fmt, int ar) { return int64_t(kSmStages) * kS
 // row blocks) o 14.8 -> 14.2.
 constexpr int kSmMinChunksPerWave = 2;
 constexpr int kSmSplitLongKb = 256;
+#ifndef MMQ_SM_MIN_MFMA
+#define MMQ_SM_MIN_MFMA 1
+#endif
+constexpr bool kSmMinMfma = MMQ_SM_MIN_MFMA;
 
 // gfx950 register file: 512 registers per lane per SIMD (arch and
 // accumulation VGPRs together), allocated in granules of 8; at most 8 waves

@@ -104,7 +104,8 @@ int mmq_quantize_q8_1(const float *x, void *y, int64_t M, int64_t K, void *strea
  * 9 <= M <= 32 (batched decode) runs a matrix-core kernel of 32 weight rows
  * per workgroup instead (kernel=sm): one int8 MFMA per block with the
  * activation rows as its other operand, the per-block scale arithmetic
- * above, four K-slices each summed in ascending order and then added in
+ * above (the K-quant min term on the matrix core too: two blocks per fp32
+ * MFMA), four K-slices each summed in ascending order and then added in
  * slice order; narrow shapes split K over two workgroups more, added into
  * the zeroed output by fp32 atomics as above.  The same kernel takes
  * 33 <= M <= 192 in blocks of 32 activation rows when N has fewer 128-wide
