@@ -43,6 +43,22 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
     return __half2float(__ushort_as_half((unsigned short)(bits16 & 0xffffu)));
 }
 
+// Lane exchanges inside a 16-lane row by DPP (a VALU operand modifier; no LDS
+// round trip as with ds_bpermute): every lane reads the lane the pattern
+// names, which is always a lane of its own row.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppHalfMirror = 0x141; // lane i of each 8 <-> lane 7 - i
+constexpr int kDppMirror = 0x140;     // lane i of each 16 <-> lane 15 - i
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+
 // ---------------------------------------------------------------------------
 // Quantize: fp32 -> q8_1 ("13 . r7-r8 raw-byte MMQ kernel", section 3.2).
 //
@@ -760,6 +776,21 @@ struct GemmSet {
     uint32_t *cnt;
 };
 
+// The GEMM of the set that holds grid unit t (column tile, 32-row group or
+// row), and the units of the whole set.  The launcher pads tile_start past
+// the set's count with the set's total, so both read fixed entries: one
+// scalar load brings them all, where a loop up to the count (or an index by
+// it) waits for each load in turn before the kernel's first memory access.
+// A unit past the total maps to the last GEMM of the set.
+__device__ __forceinline__ int set_member(const GemmSet &set, int t) {
+    int g = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxGemms; i++)
+        if (t >= set.tile_start[i]) g = i;
+    return min(g, set.count - 1);
+}
+__device__ __forceinline__ int set_total(const GemmSet &set) { return set.tile_start[kMaxGemms]; }
+
 // Indexed MoE: the row tiles come from the routing kernel's table instead of
 // from blockIdx.y alone (row tile y = tiles[y]: expert, first sorted row, end
 // of the expert's sorted rows; expert -1 marks a spare tile), the activation
@@ -823,6 +854,9 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
         tile_of_workgroup<true>(tx, ty);
     }
     // which GEMM of the set this column tile belongs to (workgroup-uniform)
+    // (a loop, not set_member: the workgroup runs long enough that its
+    // load latency does not matter, and the eight boundaries set_member
+    // holds in scalar registers made the Q6_K kernel spill)
     int gi = 0;
     for (int i = 1; i < set.count; i++)
         if (tx >= set.tile_start[i]) gi = i;
@@ -1275,10 +1309,22 @@ __device__ __forceinline__ XPair load_x_pair(__amdgpu_buffer_rsrc_t rx, int off)
     return x;
 }
 
+// The sum over a wave (all 64 lanes active).  Measured on the decode layers
+// against a six-step xor butterfly through ds_bpermute: 3 % faster at M = 1
+// (Q4_K 51.5 -> 49.8 us, Q8_0 71.6 -> 69.2), 5 % at M = 8 (Q8_0 107 -> 101.6,
+// Q6_K 119.5 -> 113.5).  (The quantize pass's four-lane reductions measured
+// 2 % slower through DPP and keep the shuffles.)
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    // butterfly inside each 16-lane row (every lane ends with its row's sum),
+    // then the four row sums, read as wave-uniform values
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppMirror>(v);
+    return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
 }
 
 // One weight unit (two 32-blocks) of one output row, ready for the dot
@@ -1464,7 +1510,7 @@ __global__ __launch_bounds__(kMvThreads) void k_mmv(const uint8_t *__restrict__ 
     // makes every load a loop over the lanes' distinct values)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row0 = (blockIdx.x * kMvWaves + wave) * RW;
-    const int total = set.tile_start[set.count];
+    const int total = set_total(set);
     if (row0 >= total) return;
     const int kb = K >> 5;
     const int64_t wrow = weight_row_bytes(FMT, K);
@@ -1477,9 +1523,7 @@ __global__ __launch_bounds__(kMvThreads) void k_mmv(const uint8_t *__restrict__ 
 #pragma unroll
     for (int r = 0; r < RW; r++) {
         const int row = row0 + r;
-        int g = 0;
-        for (int i = 1; i < set.count; i++)
-            if (row >= set.tile_start[i]) g = i;
+        const int g = set_member(set, row);
         gi[r] = g;
         n[r] = row - set.tile_start[g];
         const WBuf b = weight_rsrc(set.w[g] + int64_t(n[r]) * wrow, row < total ? wrow : 0);
@@ -1580,12 +1624,10 @@ __global__ __launch_bounds__(kMvThreads) void k_mmvq(const uint8_t *__restrict__
     static_assert(sizeof(part) == kMvqLds, "plan and kernel LDS disagree");
     const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int total = set.tile_start[set.count];
+    const int total = set_total(set);
     const int row = int(blockIdx.x) * 32 + l32;   // this lane's weight row over the set
     const bool live = row < total;
-    int gi = 0;
-    for (int i = 1; i < set.count; i++)
-        if (row >= set.tile_start[i]) gi = i;
+    const int gi = set_member(set, row);
     const int n = row - set.tile_start[gi];
     constexpr int SB = FMT == FMT_Q4_K ? 144 : 176, QS = FMT == FMT_Q4_K ? 16 : 48;
     const int nsb = K >> 8, kb = K >> 5;
@@ -2209,11 +2251,9 @@ __global__ __launch_bounds__(kSmThreads) void k_mmsm(const uint8_t *__restrict__
         const int Y = (M + 31) >> 5, r = bx % (8 * Y);
         bx = bx / (8 * Y) * 8 + (r & 7);
         yb = r >> 3;
-        if (bx >= set.tile_start[set.count]) return;
+        if (bx >= set_total(set)) return;
     }
-    int gi = 0;
-    for (int i = 1; i < set.count; i++)
-        if (bx >= set.tile_start[i]) gi = i;
+    const int gi = set_member(set, bx);
     const int N = set.N[gi], n0 = (bx - set.tile_start[gi]) * kSmRows;
     const int kb = K >> 5;
     const int64_t wrow = weight_row_bytes(FMT, K);
@@ -2615,7 +2655,7 @@ hipError_t launch_gemm(const Plan &p, const int *tile_start, int count, const vo
         set.w[g] = reinterpret_cast<const uint8_t *>(w[g]);
         set.out[g] = out[g];
     }
-    set.tile_start[count] = tile_start[count];
+    for (int g = count; g <= kMaxGemms; g++) set.tile_start[g] = tile_start[count];   // set_member, set_total
     if (p.kernel == KERNEL_MV) return launch_mv(p, set, reinterpret_cast<const uint8_t *>(x), M, K, stream);
     set.part = nullptr;
     set.cnt = nullptr;
@@ -2662,7 +2702,7 @@ hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t
     GemmSet set{};
     set.count = 1;
     set.tile_start[0] = 0;
-    set.tile_start[1] = int(p.grid_x);
+    for (int g = 1; g <= kMaxGemms; g++) set.tile_start[g] = int(p.grid_x);   // set_member, set_total
     set.N[0] = int(N);
     set.w[0] = reinterpret_cast<const uint8_t *>(w);
     set.out[0] = out;
