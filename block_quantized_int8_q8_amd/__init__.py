@@ -20,7 +20,8 @@ FMT_Q6_K = 3
 Q8_1_BYTES, Q8_0_BYTES, Q4_K_BYTES, Q5_K_BYTES, Q6_K_BYTES = 36, 34, 144, 176, 210
 
 EXPORTS = (
-    "mmq_quantize_q8_1", "mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_q5_K", "mmq_gemm_q6_K", "mmq_gemm_multi", "mmq_gemm_workspace_bytes",
+    "mmq_quantize_q8_1", "mmq_gemm_q8_0", "mmq_packed_bytes_q8_0", "mmq_pack_q8_0", "mmq_gemm_q8_0_packed",
+    "mmq_gemm_q4_K", "mmq_gemm_q5_K", "mmq_gemm_q6_K", "mmq_gemm_multi", "mmq_gemm_workspace_bytes",
     "mmq_gemm_multi_ws", "mmq_moe_workspace_bytes",
     "mmq_moe_gemm", "mmq_moe_gemm_routed", "mmq_moe_gemm_noalloc", "mmq_debug_block_dots",
     "mmq_last_error", "mmq_plan_describe", "mmq_plan_for_limits",
@@ -48,6 +49,12 @@ def lib() -> ctypes.CDLL:
         for name in ("mmq_gemm_q8_0", "mmq_gemm_q4_K", "mmq_gemm_q5_K", "mmq_gemm_q6_K"):
             getattr(L, name).argtypes = [p, p, p, i64, i64, i64, p]
             getattr(L, name).restype = i32
+        L.mmq_packed_bytes_q8_0.argtypes = [i64, i64]
+        L.mmq_packed_bytes_q8_0.restype = i64
+        L.mmq_pack_q8_0.argtypes = [p, i64, i64, p, i64, p]
+        L.mmq_pack_q8_0.restype = i32
+        L.mmq_gemm_q8_0_packed.argtypes = [p, p, p, i64, i64, i64, p]
+        L.mmq_gemm_q8_0_packed.restype = i32
         L.mmq_gemm_multi.argtypes = [i32, p, i32, p, p, p, i64, i64, p]
         L.mmq_gemm_multi.restype = i32
         L.mmq_gemm_workspace_bytes.argtypes = [i32, i32, p, i64, i64]
@@ -166,6 +173,42 @@ _FN_FMT = {"mmq_gemm_q8_0": FMT_Q8_0, "mmq_gemm_q4_K": FMT_Q4_K, "mmq_gemm_q5_K"
 def gemm_q8_0(xq, w, M, N, K, out=None, stream=None):
     """q8_1 [M, K/32, 36] x Q8_0 [N, K/32, 34] -> fp32 [M, N]."""
     return _gemm("mmq_gemm_q8_0", "mmq_gemm_q8_0", xq, w, M, N, K, out, stream)
+
+
+def packed_bytes_q8_0(N, K) -> int:
+    """Bytes of the tile-packed form of an N x K Q8_0 matrix."""
+    b = int(lib().mmq_packed_bytes_q8_0(N, K))
+    if b < 0:
+        raise MMQError(f"mmq_packed_bytes_q8_0: {last_error()}")
+    return b
+
+
+def pack_q8_0(w, N, K, packed=None, stream=None):
+    """Q8_0 [N, K/32, 34] -> the tile-packed form (uint8, packed_bytes_q8_0(N, K)),
+    reordered on the device; gemm_q8_0_packed reads it."""
+    import torch
+    nbytes = packed_bytes_q8_0(N, K)
+    if packed is None:
+        packed = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    _need(w, torch.uint8, N * row_bytes(FMT_Q8_0, K), "w (Q8_0 weights)")
+    _need(packed, torch.uint8, nbytes, "packed")
+    _check(lib().mmq_pack_q8_0(_ptr(w, torch.uint8), N, K, _ptr(packed, torch.uint8), packed.numel(),
+                               _stream(stream)), "mmq_pack_q8_0")
+    return packed
+
+
+def gemm_q8_0_packed(xq, packed, M, N, K, out=None, stream=None):
+    """q8_1 [M, K/32, 36] x tile-packed Q8_0 (pack_q8_0) -> fp32 [M, N]."""
+    import torch
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    if _dims_ok(M, N, K):
+        _need(xq, torch.uint8, M * (K // 32) * Q8_1_BYTES, "xq (q8_1 activations)")
+        _need(packed, torch.uint8, packed_bytes_q8_0(N, K) if K % 32 == 0 else 0, "packed (Q8_0 weights)")
+        _need(out, torch.float32, M * N, "out")
+    _check(lib().mmq_gemm_q8_0_packed(_ptr(xq), _ptr(packed), _ptr(out, torch.float32), M, N, K, _stream(stream)),
+           "mmq_gemm_q8_0_packed")
+    return out
 
 
 def gemm_q4_K(xq, w, M, N, K, out=None, stream=None):

@@ -31,6 +31,7 @@ hipError_t launch_moe(const Plan &p, const void *x, const void *w, const int32_t
                       float *out, int64_t T, int64_t N, int64_t K, void *workspace, hipStream_t stream);
 const void *plan_kernel(const Plan &p, bool dots, bool moe);
 hipError_t noalloc_scratch(void **ptr);
+hipError_t launch_pack_q8_0(const void *w, int64_t N, int64_t K, void *packed, int cu_count, hipStream_t stream);
 }  // namespace mmq
 
 namespace {
@@ -142,12 +143,16 @@ bool plan_with_kernel_fit(MakePlan make, bool dots, bool moe, mmq::Plan *p, char
 }
 
 // Plan a GEMM set on the current device (with the launched kernel's
-// attributes); `workspace`: plan for a split-K workspace.
+// attributes); `workspace`: plan for a split-K workspace; `packed`: Q8_0
+// weights in the tile-packed form, which only the tile kernel reads.
 bool plan_set(int fmt, int count, const int64_t *N, int64_t M, int64_t K, bool dots, bool workspace,
-              const DeviceLimits &L, mmq::Plan *p, int *tile_start, char *why, size_t why_len) {
+              const DeviceLimits &L, mmq::Plan *p, int *tile_start, char *why, size_t why_len, bool packed = false) {
     auto make = [&](const mmq::KernelFit &fit, mmq::Plan *q, char *w, size_t wl) {
-        return mmq::make_plan_multi(fmt, M, count, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), q,
-                                    tile_start, w, wl, !dots, fit, workspace);
+        if (!mmq::make_plan_multi(fmt, M, count, N, K, L.lds_per_block, L.cu_count, g_extra_lds.load(), q,
+                                  tile_start, w, wl, !dots && !packed, fit, workspace))
+            return false;
+        q->packed = packed;
+        return true;
     };
     return plan_with_kernel_fit(make, dots, false, p, why, why_len);
 }
@@ -155,7 +160,8 @@ bool plan_set(int fmt, int count, const int64_t *N, int64_t M, int64_t K, bool d
 // `workspace`: null, or `workspace_bytes` bytes of device memory for a
 // split-K plan (mmq_gemm_multi_ws).
 int gemm_set(int fmt, const void *x, int count, const void *const *w, void *const *out, const int64_t *N,
-             int64_t M, int64_t K, bool dots, void *workspace, int64_t workspace_bytes, void *stream) {
+             int64_t M, int64_t K, bool dots, void *workspace, int64_t workspace_bytes, void *stream,
+             bool packed = false) {
     g_err[0] = '\0';
     if (!mmq::fmt_ok(fmt)) return refuse("unknown weight format %d", fmt);
     if (count < 1 || count > mmq::kMaxGemms) return refuse("count must be 1..%d GEMMs", mmq::kMaxGemms);
@@ -176,9 +182,10 @@ int gemm_set(int fmt, const void *x, int count, const void *const *w, void *cons
     char why[256];
     // the block-dot output exists for the MMQ kernel only (planned without
     // a workspace: it never splits)
-    if (!plan_set(fmt, count, N, M, K, dots, workspace != nullptr && !dots, L, &p, tile_start, why, sizeof(why)))
-        return refuse("%s GEMM M=%lld N=%lld K=%lld%s: %s", mmq::fmt_name(fmt), (long long)M, (long long)N[0],
-                      (long long)K, count > 1 ? " (first of a set)" : "", why);
+    if (!plan_set(fmt, count, N, M, K, dots, workspace != nullptr && !dots, L, &p, tile_start, why, sizeof(why),
+                  packed))
+        return refuse("%s%s GEMM M=%lld N=%lld K=%lld%s: %s", mmq::fmt_name(fmt), packed ? " (packed)" : "",
+                      (long long)M, (long long)N[0], (long long)K, count > 1 ? " (first of a set)" : "", why);
     const int64_t need = mmq::split_workspace_bytes(p);
     if (need > workspace_bytes)
         return refuse("%s GEMM M=%lld N=%lld K=%lld: the split-K workspace holds %lld bytes, the plan needs %lld",
@@ -218,6 +225,41 @@ int mmq_quantize_q8_1(const float *x, void *y, int64_t M, int64_t K, void *strea
 int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out, int64_t M, int64_t N, int64_t K,
                   void *stream) {
     return gemm_common(mmq::FMT_Q8_0, x_q8_1, w_q8_0, out, M, N, K, false, stream);
+}
+
+int64_t mmq_packed_bytes_q8_0(int64_t N, int64_t K) {
+    g_err[0] = '\0';
+    const int64_t b = mmq::packed_bytes_q8_0(N, K);
+    if (b < 0)
+        refuse("packed Q8_0 N=%lld K=%lld: N must be 1..2^31-1 and K a multiple of 32 in 32..8388608", (long long)N,
+               (long long)K);
+    return b;
+}
+
+int mmq_pack_q8_0(const void *w_q8_0, int64_t N, int64_t K, void *packed, int64_t packed_bytes, void *stream) {
+    g_err[0] = '\0';
+    if (!w_q8_0 || !packed) return refuse("null pointer argument");
+    if (!aligned(w_q8_0, 16) || !aligned(packed, 16)) return refuse("weight and packed pointers must be 16-byte aligned");
+    const int64_t need = mmq::packed_bytes_q8_0(N, K);
+    if (need < 0)
+        return refuse("pack Q8_0 N=%lld K=%lld: N must be 1..2^31-1 and K a multiple of 32 in 32..8388608",
+                      (long long)N, (long long)K);
+    if (packed_bytes < need)
+        return refuse("pack Q8_0 N=%lld K=%lld: the packed buffer holds %lld bytes, the packed form needs %lld",
+                      (long long)N, (long long)K, (long long)packed_bytes, (long long)need);
+    DeviceLimits L;
+    if (!current_limits(&L)) return 0;
+    if (!L.is_gfx950) return refuse("device is %s; this library is built for gfx950 only", L.arch);
+    (void)hipGetLastError();
+    const hipError_t e = mmq::launch_pack_q8_0(w_q8_0, N, K, packed, L.cu_count, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return refuse("pack launch failed: %s", hipGetErrorString(e));
+    return 1;
+}
+
+int mmq_gemm_q8_0_packed(const void *x_q8_1, const void *w_packed, float *out, int64_t M, int64_t N, int64_t K,
+                         void *stream) {
+    void *o = out;
+    return gemm_set(mmq::FMT_Q8_0, x_q8_1, 1, &w_packed, &o, &N, M, K, false, nullptr, 0, stream, true);
 }
 
 int mmq_gemm_q4_K(const void *x_q8_1, const void *w_q4_K, float *out, int64_t M, int64_t N, int64_t K,

@@ -819,9 +819,15 @@ struct MoeArgs {
 // below): the next step's first fragment reads are issued first, so their
 // LDS latency is spent on that epilogue instead of stalling the step's
 // first MFMA, and the last MFMA's latency is spent at the barrier.
-template <int FMT, bool DOTS, bool MOE, bool SKIP, bool TAIL>
+// PK: Q8_0 weights in the tile-packed form (kPackImg images, mmq_pack_q8_0).
+// Their codes are already in the LDS order, so they go to LDS by DMA like
+// the activations (no registers, no VALU); each thread fetches one fp16
+// scale a k-step ahead and stores its fp32 pair, the same values as the
+// unpacked staging, so the output is bit-identical to it.
+template <int FMT, bool DOTS, bool MOE, bool SKIP, bool TAIL, bool PK = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DOTS ? 2 : 4)))
 void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int steps_per_split, const MoeArgs moe) {
+    static_assert(!PK || (FMT == FMT_Q8_0 && !DOTS && !MOE), "the packed form is a Q8_0 GEMM layout");
     static_assert(!(MOE && DOTS), "the block-dot output exists for plain GEMMs only");
     static_assert(!(DOTS && SKIP) && (!MOE || SKIP), "block dots never skip; the MoE launch always does");
     static_assert(!TAIL || FMT == FMT_Q8_0, "only Q8_0 k-steps can be partial");
@@ -883,6 +889,9 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     const __amdgpu_buffer_rsrc_t rx = tile_rsrc(xq + int64_t(m0) * xrow, int64_t(M - m0) * xrow);
     const WBuf rwb = weight_rsrc(wq + int64_t(n0) * wrow, int64_t(N - n0) * wrow);
     const __amdgpu_buffer_rsrc_t rw = rwb.r;
+    // PK: this column tile's images, one per k-step
+    const __amdgpu_buffer_rsrc_t rpk =
+        PK ? tile_rsrc(wq + int64_t(n0 / kTileN) * nsteps * kPackImg, int64_t(nsteps) * kPackImg) : rw;
 
     const int b_col0 = kWaveN * wc + l32;            // this lane's B column in sub-tile 0
     const int a_lane = code_off(0, 32 * wr + l32, g); // fragment bases; blocks and sub-tiles
@@ -926,8 +935,11 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     };
 
     WRegs<FMT> wr_;
+    uint32_t pk_d = 0;   // PK: the fp16 scale of (block tid / 128, column tid % 128) of a k-step
     auto load_w = [&](int k) {
-        if constexpr (FMT == FMT_Q8_0)
+        if constexpr (PK)
+            pk_d = __builtin_amdgcn_raw_buffer_load_b16(rpk, k * int(kPackImg) + int(kPackCodes) + 2 * tid, 0, 0);
+        else if constexpr (FMT == FMT_Q8_0)
             load_q8_0(rw, rwb.shift, kb, k, tid, wr_.r);
         else if constexpr (FMT == FMT_Q6_K)
             load_q6_K(rw, rwb.shift, K >> 8, k, tid, wr_.r);
@@ -937,7 +949,17 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
             load_q5_K(rw, K >> 8, k, tid, wr_.r);
     };
     auto store_w = [&](int k, uint8_t *buf) {
-        if constexpr (FMT == FMT_Q8_0)
+        if constexpr (PK) {
+            // the 16 KiB of codes: two 1 KiB DMA pieces per wave
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int c = wv + 8 * i;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rpk, (lds_void *)(buf + L::OFF_B_CODES + 1024 * c), 16,
+                                                         k * int(kPackImg) + 1024 * c + 16 * lane, 0, 0, 0);
+            }
+            const float ws = h2f(pk_d);
+            reinterpret_cast<float2 *>(buf + L::OFF_B_SCALE)[tid] = make_float2(ws, -kMagic * ws);   // exact
+        } else if constexpr (FMT == FMT_Q8_0)
             store_q8_0(wr_.r, buf, rwb.shift, kb, k, tid);
         else if constexpr (FMT == FMT_Q6_K)
             store_q6_K(wr_.r, buf, rwb.shift, K >> 8, k, tid);
@@ -1069,7 +1091,9 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
             // cost 8-10 % more.
             if (j + 1 < nloc) {
                 if ((st & 1) && st < 6) dma_activations<FMT, TAIL || DOTS>(rx, adma, ks + 1, nxt, wv, st >> 1);
-                if (st == 6) store_w(ks + 1, nxt);
+                // (PK: the weight DMA at sub-step 2, measured 10 % faster
+                // than at 6 and 7 % faster than at 3)
+                if (st == (PK ? 2 : 6)) store_w(ks + 1, nxt);
             }
             if (!live) continue;
             const int col = b_col0 + 32 * c;
@@ -2517,6 +2541,56 @@ __global__ __launch_bounds__(256) void k_zero_fill_set(const GemmSet set, int64_
 }
 
 // ---------------------------------------------------------------------------
+// Tile-packed Q8_0 weights (mmq_pack_q8_0): a permutation of the Q8_0 bytes
+// into the order the tile kernel stages them, kPackImg bytes per 128-column
+// tile and k-step (layout at kPackCodes).  One thread per output dword; a
+// Q8_0 block is 17 16-bit units (the scale, then the codes), so the dword's
+// four code bytes, or its two scales, are read as 16-bit values.  Columns
+// past N and blocks past K/32 are written as zero.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pack_q8_0(const uint16_t *__restrict__ w, int N, int kb, int nsteps,
+                                                   uint32_t *__restrict__ packed, int64_t ndw) {
+    constexpr int kImgDw = int(kPackImg / 4), kCodeDw = int(kPackCodes / 4), kBlockDw = kBlockBytes / 4;
+    const int64_t stride = int64_t(gridDim.x) * 256;
+    for (int64_t d = int64_t(blockIdx.x) * 256 + threadIdx.x; d < ndw; d += stride) {
+        const int64_t img = d / kImgDw;   // image = (column tile, k-step)
+        const int o = int(d - img * kImgDw);
+        const int t = int(img / nsteps), s = int(img - int64_t(t) * nsteps);
+        uint32_t v = 0;
+        if (o < kCodeDw) {
+            // the inverse of code_off: block b, column col, stored half, dword i of the half
+            const int b = o / kBlockDw, r = o - b * kBlockDw;
+            const int col = r >> 3, half = ((r >> 2) & 1) ^ half_swz(col);
+            const int byte0 = 16 * half + 4 * (r & 3);
+            const int n = t * kTileN + col, blk = s * KB + b;
+            if (n < N && blk < kb) {
+                const int64_t h = (int64_t(n) * kb + blk) * 17 + 1 + byte0 / 2;
+                v = uint32_t(w[h]) | (uint32_t(w[h + 1]) << 16);
+            }
+        } else {
+            // scales [block][column], two per dword
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const int u = 2 * (o - kCodeDw) + j, b = u / kTileN, col = u - b * kTileN;
+                const int n = t * kTileN + col, blk = s * KB + b;
+                if (n < N && blk < kb) v |= uint32_t(w[(int64_t(n) * kb + blk) * 17]) << (16 * j);
+            }
+        }
+        packed[d] = v;
+    }
+}
+
+hipError_t launch_pack_q8_0(const void *w, int64_t N, int64_t K, void *packed, int cu_count, hipStream_t stream) {
+    const int kb = int(K / 32), nsteps = (kb + KB - 1) / KB;
+    const int64_t ndw = packed_bytes_q8_0(N, K) / 4;
+    int64_t grid = (ndw + 255) / 256;
+    if (grid > int64_t(cu_count) * 32) grid = int64_t(cu_count) * 32;   // the kernel strides over the rest
+    hipLaunchKernelGGL(k_pack_q8_0, dim3((unsigned)grid), dim3(256), 0, stream, reinterpret_cast<const uint16_t *>(w),
+                       int(N), kb, nsteps, reinterpret_cast<uint32_t *>(packed), ndw);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Scratch of the allocation-free MoE entry point: the routing tables of one
 // call (header, tile table, sorted routed-row ids: kNoAllocScratchBytes for
 // up to kNoAllocMaxRouted routed rows and kMoeMaxExperts experts) in a
@@ -2600,9 +2674,9 @@ static hipError_t launch_mv(const Plan &p, const GemmSet &set, const uint8_t *xb
 
 // The kernel a plan launches: launch_gemm and launch_moe below launch
 // exactly this one, and the capacity guard reads its attributes.
-template <int F, bool DOTS, bool MOE, bool SKIP, bool TAIL>
+template <int F, bool DOTS, bool MOE, bool SKIP, bool TAIL, bool PK = false>
 static const void *kmmq() {
-    return reinterpret_cast<const void *>(&k_mmq<F, DOTS, MOE, SKIP, TAIL>);
+    return reinterpret_cast<const void *>(&k_mmq<F, DOTS, MOE, SKIP, TAIL, PK>);
 }
 
 const void *plan_kernel(const Plan &p, bool dots, bool moe) {
@@ -2621,6 +2695,11 @@ const void *plan_kernel(const Plan &p, bool dots, bool moe) {
                                   : reinterpret_cast<const void *>(&k_mmsm<F, 32>);
         if (dots) return kmmq<F, true, false, false, false>();   // partial steps: the store mask
         if constexpr (F == FMT_Q8_0) {
+            if (p.packed) {
+                if (p.skip_idle_waves)
+                    return p.tail ? kmmq<F, false, false, true, true, true>() : kmmq<F, false, false, true, false, true>();
+                return p.tail ? kmmq<F, false, false, false, true, true>() : kmmq<F, false, false, false, false, true>();
+            }
             if (moe) return p.tail ? kmmq<F, false, true, true, true>() : kmmq<F, false, true, true, false>();
             if (p.skip_idle_waves)
                 return p.tail ? kmmq<F, false, false, true, true>() : kmmq<F, false, false, true, false>();

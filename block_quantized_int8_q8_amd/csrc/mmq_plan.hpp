@@ -30,6 +30,25 @@ constexpr int kTileM = 128;        // output rows per workgroup
 constexpr int kTileN = 128;        // output columns per workgroup
 constexpr int kThreads = 512;      // eight wave64s, a 4 x 2 grid of 32 x 64 wave tiles
 constexpr int kBlocksPerStage = 4; // 32-blocks staged per k-step (half a Q4_K super-block)
+// Tile-packed Q8_0 weights (mmq_pack_q8_0): the same bytes as the Q8_0
+// blocks, ordered as the tile kernel stages them.  For every 128-column tile
+// and every k-step of kBlocksPerStage blocks, one image of kPackImg bytes:
+// the 4 x 128 blocks' 32 code bytes in the kernel's LDS order (kPackCodes
+// bytes: [block][column][32 bytes], the two 16-byte halves of a column
+// swapped where the LDS swizzle swaps them), then their fp16 scales as
+// [block][column].  Columns past N and blocks past K/32 are zero (scale 0).
+constexpr int64_t kPackCodes = int64_t(kBlocksPerStage) * kTileN * 32;
+constexpr int64_t kPackImg = kPackCodes + int64_t(kBlocksPerStage) * kTileN * 2;
+// Bytes of the packed form of an N x K Q8_0 matrix (K a multiple of 32), or
+// -1 for a shape the GEMMs refuse.
+inline int64_t packed_bytes_q8_0(int64_t N, int64_t K) {
+    if (N < 1 || K < 32 || K % 32 != 0 || N > INT32_MAX || K > (int64_t(1) << 23)) return -1;
+    const int64_t tiles = (N + kTileN - 1) / kTileN, steps = (K / 32 + kBlocksPerStage - 1) / kBlocksPerStage;
+    // a tile's images are addressed with 32-bit offsets
+    if (steps * kPackImg > INT32_MAX) return -1;
+    return tiles * steps * kPackImg;
+}
+
 // Workgroups resident per CU are derived from the launched kernel's own
 // register and LDS use (kernel_wg_per_cu below); the kernels are built for
 // two (at most 128 VGPRs, four waves per SIMD).
@@ -219,6 +238,7 @@ inline int kernel_wg_per_cu(int vgprs, int64_t lds, int64_t lds_per_cu, int thre
 struct Plan {
     int fmt = 0;
     int kernel = KERNEL_MMQ;
+    bool packed = false;   // Q8_0 weights in the tile-packed form (kPackImg images)
     int tile_m = kTileM, tile_n = kTileN, threads = kThreads, blocks_per_stage = kBlocksPerStage;
     int64_t lds_bytes = 0;
     int64_t grid_x = 0, grid_y = 0;   // x: column tiles, y: row tiles
@@ -525,12 +545,12 @@ inline void describe(const Plan &p, const Plan *ws, char *buf, size_t len) {
     int n = std::snprintf(buf, len,
                           "kernel=%s fmt=%s tile=%dx%d threads=%d blocks_per_stage=%d lds=%lld grid=%lldx%lld "
                           "k_steps=%lld split_k=%lld steps_per_split=%lld skip_idle_waves=%d mv_rows_per_wave=%d "
-                          "wg_per_cu=%d vgprs=%d tail=%d split_ws=%d mv_mfma=%d",
+                          "wg_per_cu=%d vgprs=%d tail=%d split_ws=%d mv_mfma=%d packed=%d",
                           p.kernel == KERNEL_MV ? "mv" : p.kernel == KERNEL_SM ? "sm" : "mmq", fmt_name(p.fmt), p.tile_m, p.tile_n, p.threads,
                           p.blocks_per_stage, (long long)p.lds_bytes, (long long)p.grid_x, (long long)p.grid_y,
                           (long long)p.k_steps, (long long)p.split_k, (long long)p.steps_per_split,
                           int(p.skip_idle_waves), p.mv_rows_per_wave, p.wg_per_cu, p.kernel_vgprs, int(p.tail),
-                          int(p.split_ws), int(p.mv_mfma));
+                          int(p.split_ws), int(p.mv_mfma), int(p.packed));
     if (ws && n > 0 && size_t(n) < len)
         std::snprintf(buf + n, len - size_t(n), " ws_split_k=%lld ws_steps_per_split=%lld ws_bytes=%lld",
                       (long long)ws->split_k, (long long)ws->steps_per_split, (long long)split_workspace_bytes(*ws));

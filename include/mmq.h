@@ -114,6 +114,38 @@ int mmq_quantize_q8_1(const float *x, void *y, int64_t M, int64_t K, void *strea
 int mmq_gemm_q8_0(const void *x_q8_1, const void *w_q8_0, float *out,
                   int64_t M, int64_t N, int64_t K, void *stream);
 
+/* Tile-packed Q8_0 weights: the bytes of an N x K Q8_0 matrix (the
+ * contraction's weight operand, "When the Product Won't Collapse", section
+ * 2) reordered once, on the device, into the order in which the GEMM kernel
+ * stages them, so that each k-step's weight codes reach LDS by DMA with no
+ * register or VALU work.  The layout is this library's own: for every
+ * 128-column tile and every step of 4 blocks, 17408 bytes -- the 4 x 128
+ * blocks' 32 code bytes as [block][column][32 bytes], the two 16-byte
+ * halves swapped for the columns c (within the tile) whose bits 2 and 3
+ * differ, then their fp16 scales [block][column] -- with columns past N
+ * and blocks past K/32 zero.  No
+ * byte of the weights is converted; the scales are decoded in the GEMM, as
+ * for the row-major form.
+ * mmq_packed_bytes_q8_0: the packed size for N x K (N >= 1, K a multiple of
+ * 32 in 32..8388608), or -1 (reason in mmq_last_error).
+ * mmq_pack_q8_0: w_q8_0 (N x (K/32) Q8_0 blocks, 16-byte aligned, caller
+ * owned, read only) -> packed (at least mmq_packed_bytes_q8_0(N, K) bytes,
+ * 16-byte aligned, caller owned, every byte of the packed form written),
+ * one kernel on `stream`.  Refuses (0) a short buffer or a bad shape. */
+int64_t mmq_packed_bytes_q8_0(int64_t N, int64_t K);
+int mmq_pack_q8_0(const void *w_q8_0, int64_t N, int64_t K, void *packed, int64_t packed_bytes,
+                  void *stream);
+
+/* mmq_gemm_q8_0 on weights packed by mmq_pack_q8_0 for the same N and K:
+ * the same arithmetic in the same order, so out is bit-identical to
+ * mmq_gemm_q8_0's on every shape the tile kernel runs.  Every M runs the
+ * tile kernel (the decode kernels read the row-major form), with the same
+ * split-K rule and its atomics.  w_packed: mmq_packed_bytes_q8_0(N, K)
+ * bytes, 16-byte aligned; x_q8_1, out and the refusals as for
+ * mmq_gemm_q8_0. */
+int mmq_gemm_q8_0_packed(const void *x_q8_1, const void *w_packed, float *out,
+                         int64_t M, int64_t N, int64_t K, void *stream);
+
 /* q8_1 activations x Q4_K weights -> fp32 ("When Does a Kernel Win
  * Surface?", section 6.2, affine identity with the min term folded in
  * through the q8_1 block-sum field).
