@@ -4,6 +4,10 @@
 One step = one pass of the whole path over one batch: quantize the fp32
 activations to q8_1, then the MMQ GEMM against the block-quantized weights.
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
+The Q8_0 headline reads its weights in the tile-packed form (the same Q8_0
+bytes reordered once, before timing, by mmq_pack_q8_0; the time that takes
+is reported as `pack_ms`), and the same configuration on row-major weights
+is timed beside it (`--row-major` puts that one in the headline instead).
 
 Prints ONE JSON line.  `value` is effective int8 TOPS of the whole step,
 2*M*N*K / (quantize + GEMM time); the roofline object reports the GEMM
@@ -82,12 +86,21 @@ def make_inputs(cfg):
     return fmt, M, N, K, x, gen(N, K, sw)
 
 
+def make_inputs_fmt(cfg) -> str:
+    """The weight format of a configuration (without generating its inputs)."""
+    from block_quantized_int8_q8_amd import inputs
+    return inputs.CONFIGS[cfg][0] if isinstance(cfg, int) else cfg.split(":")[0]
+
+
 def _fmt_code(fmt: str) -> int:
     import block_quantized_int8_q8_amd as mmq
     return {"q8_0": mmq.FMT_Q8_0, "q4_K": mmq.FMT_Q4_K, "q5_K": mmq.FMT_Q5_K, "q6_K": mmq.FMT_Q6_K}[fmt]
 
 
-def time_config(cfg, steps: int, warmup: int, check: bool = True, cold: bool = False):
+def time_config(cfg, steps: int, warmup: int, check: bool = True, cold: bool = False, packed: bool = False):
+    """Time one configuration.  `packed` (Q8_0): the weights are reordered
+    once into the tile-packed form (mmq_pack_q8_0, timed on its own as
+    `pack_ms`) before anything is timed, and every GEMM reads that form."""
     import torch
     import block_quantized_int8_q8_amd as mmq
 
@@ -98,9 +111,20 @@ def time_config(cfg, steps: int, warmup: int, check: bool = True, cold: bool = F
     xq = torch.empty((M, K // 32, 36), dtype=torch.uint8, device=dev)
     out = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
     code = _fmt_code(fmt)
+    pack_ms = None
+    if packed:
+        assert fmt == "q8_0", "the packed form is a Q8_0 layout"
+        wpk = mmq.pack_q8_0(wd, N, K)
+        torch.cuda.synchronize()
+        pack_ms = graph_time(lambda: mmq.pack_q8_0(wd, N, K, wpk), 20, reps=5)
+        del wd
+        wd = wpk
 
-    def gemm(*a, **k):
-        return mmq.gemm(code, *a, **k)
+        def gemm(xq_, w_, M_, N_, K_, out_, stream=None):
+            return mmq.gemm_q8_0_packed(xq_, w_, M_, N_, K_, out_, stream=stream)
+    else:
+        def gemm(*a, **k):
+            return mmq.gemm(code, *a, **k)
 
     stream = torch.cuda.current_stream()
 
@@ -182,6 +206,8 @@ def time_config(cfg, steps: int, warmup: int, check: bool = True, cold: bool = F
         "quant_ms_avg": q_avg,
         "quant_gbs": (4.0 + 36.0 / 32.0) * M * K / (q_avg * 1e-3) / 1e9,
         "parity": parity,
+        "packed": packed,
+        "pack_ms": pack_ms,
     }
 
 
@@ -663,6 +689,8 @@ def main():
                     help="format:M pairs of the timed decode-size layer ('' for none)")
     ap.add_argument("--moe", default="q4_K,q8_0",
                     help="weight formats of the timed 128-expert MoE layer ('' for none)")
+    ap.add_argument("--row-major", action="store_true",
+                    help="time the headline Q8_0 GEMM on row-major weights instead of the tile-packed form")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -694,9 +722,19 @@ def main():
     def progress(what):
         print(f"bench.py: {what} done", file=sys.stderr, flush=True)
 
-    main_rec = time_config(args.config, args.steps, args.warmup, check=not args.no_check, cold=True)
+    packed = not args.row_major and make_inputs_fmt(args.config) == "q8_0"
+    main_rec = time_config(args.config, args.steps, args.warmup, check=not args.no_check, cold=True,
+                           packed=packed)
     progress(f"config {args.config}")
     extra = {}
+    if packed:
+        # the same configuration on row-major weights (mmq_gemm_q8_0), for comparison
+        r = time_config(args.config, args.steps, args.warmup, check=not args.no_check)
+        extra[f"config{args.config}_row_major"] = {
+            k: r[k] for k in ("fmt", "M", "N", "K", "ms_per_step", "tops_step", "gemm_ms_avg", "gemm_tops",
+                              "quant_gbs", "parity")}
+        extra[f"config{args.config}_row_major"]["gemm_frac_of_int8_peak"] = r["gemm_tops"] / PEAK_INT8_TOPS
+        progress(f"config {args.config} row-major")
     for c in [int(v) for v in args.extra_configs.split(",") if v.strip()]:
         if c != args.config:
             r = time_config(c, max(5, args.steps // 5), 2, check=not args.no_check)
@@ -727,7 +765,7 @@ def main():
         extra[f"moe_{f}"] = time_moe(f, max(3, args.steps // 5), 1, check=not args.no_check)
         progress(f"moe {f}")
 
-    kname = "k_mmq<Q8_0>" if main_rec["fmt"] == "q8_0" else "k_mmq<Q4_K>"
+    kname = ("k_mmq<Q8_0,packed>" if packed else "k_mmq<Q8_0>") if main_rec["fmt"] == "q8_0" else "k_mmq<Q4_K>"
     achieved = main_rec["gemm_tops"]
     # The per-block scale costs 32 VALU operations per 32x32x32 MFMA; measured
     # alone (registers only, 4 waves per SIMD) that epilogue takes 159 cycles
@@ -763,8 +801,11 @@ def main():
         "config": {
             "workload": f"{main_rec['fmt'].upper()} x q8_1 MMQ M={M} N={N} K={K} (quantize + GEMM)",
             "M": M, "N": N, "K": K, "format": main_rec["fmt"].upper(),
+            "weights": ("Q8_0 in the tile-packed form: the same bytes reordered once before timing "
+                        "(mmq_pack_q8_0, pack_ms); row-major figures under extra" if packed else "row-major"),
             "parallelism": "single GPU",
         },
+        "pack_ms": main_rec["pack_ms"],
         "frac_of_int8_peak_step": main_rec["tops_step"] / PEAK_INT8_TOPS,
         "step_timing": "quantize + GEMM captured once as a HIP graph, replayed; eager launches: "
                        f"{main_rec['ms_per_step_eager'] * 1e3:.1f} us per step",

@@ -838,8 +838,16 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     // write what the fragment reads of the other return, and does not make
     // every LDS read wait for the DMA in flight.  The step loop is unrolled
     // by two so that each copy names its buffers at compile time.
-    __shared__ __attribute__((aligned(16))) uint8_t lds0[L::STEP];
-    __shared__ __attribute__((aligned(16))) uint8_t lds1[L::STEP];
+    // PK: the weight scale pairs of each buffer are LDS variables of their
+    // own as well (the same bytes, taken off the end of the step buffers), so
+    // that storing them does not wait for the codes' DMA into the same step
+    // buffer (the compiler orders an LDS store after an LDS DMA it may alias)
+    static_assert(FMT != FMT_Q8_0 || L::OFF_B_SCALE + L::B_SCALE == L::STEP, "Q8_0 scale pairs end the step");
+    constexpr int kStepBytes = PK ? L::OFF_B_SCALE : L::STEP;
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[kStepBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[kStepBytes];
+    __shared__ __attribute__((aligned(16))) float2 pks0[PK ? KB * kTileN : 1];
+    __shared__ __attribute__((aligned(16))) float2 pks1[PK ? KB * kTileN : 1];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wr = wv >> 1, wc = wv & 1;          // wave tile: rows 32*wr.., columns 64*wc..
@@ -935,7 +943,10 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     };
 
     WRegs<FMT> wr_;
-    uint32_t pk_d = 0;   // PK: the fp16 scale of (block tid / 128, column tid % 128) of a k-step
+    // PK: the fp16 scale of (block tid / 128, column tid % 128) of a k-step,
+    // kept as the loaded 16-bit value (widened where it is used, so the load
+    // is not waited for when it is issued)
+    unsigned short pk_d = 0;
     auto load_w = [&](int k) {
         if constexpr (PK)
             pk_d = __builtin_amdgcn_raw_buffer_load_b16(rpk, k * int(kPackImg) + int(kPackCodes) + 2 * tid, 0, 0);
@@ -948,17 +959,24 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
         else
             load_q5_K(rw, K >> 8, k, tid, wr_.r);
     };
+    // PK: the 16 KiB of codes, two 1 KiB DMA pieces per wave, and the
+    // thread's scale pair (from the fp16 scale load_w fetched)
+    auto pk_codes = [&](int k, uint8_t *buf) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int c = wv + 8 * i;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rpk, (lds_void *)(buf + L::OFF_B_CODES + 1024 * c), 16,
+                                                     k * int(kPackImg) + 1024 * c + 16 * lane, 0, 0, 0);
+        }
+    };
+    auto pk_scale = [&](uint8_t *buf) {
+        const float ws = __half2float(__ushort_as_half(pk_d));
+        (buf == lds0 ? pks0 : pks1)[tid] = make_float2(ws, -kMagic * ws);   // exact
+    };
     auto store_w = [&](int k, uint8_t *buf) {
         if constexpr (PK) {
-            // the 16 KiB of codes: two 1 KiB DMA pieces per wave
-#pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const int c = wv + 8 * i;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rpk, (lds_void *)(buf + L::OFF_B_CODES + 1024 * c), 16,
-                                                         k * int(kPackImg) + 1024 * c + 16 * lane, 0, 0, 0);
-            }
-            const float ws = h2f(pk_d);
-            reinterpret_cast<float2 *>(buf + L::OFF_B_SCALE)[tid] = make_float2(ws, -kMagic * ws);   // exact
+            pk_codes(k, buf);
+            pk_scale(buf);
         } else if constexpr (FMT == FMT_Q8_0)
             store_q8_0(wr_.r, buf, rwb.shift, kb, k, tid);
         else if constexpr (FMT == FMT_Q6_K)
@@ -1015,7 +1033,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
         }
         const unsigned short *sHdr = reinterpret_cast<const unsigned short *>(buf + L::OFF_A_HDR);
         const uint8_t *sB = buf + L::OFF_B_CODES;
-        const float2 *sW = reinterpret_cast<const float2 *>(buf + L::OFF_B_SCALE);
+        const float2 *sW = PK ? (P ? pks1 : pks0) : reinterpret_cast<const float2 *>(buf + L::OFF_B_SCALE);
 
         // Sub-step st = (block b = st/2, sub-tile c = st%2).  B fragments are
         // read from LDS kPfB sub-steps ahead, A fragments one block ahead.
@@ -1091,9 +1109,14 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
             // cost 8-10 % more.
             if (j + 1 < nloc) {
                 if ((st & 1) && st < 6) dma_activations<FMT, TAIL || DOTS>(rx, adma, ks + 1, nxt, wv, st >> 1);
-                // (PK: the weight DMA at sub-step 2, measured 10 % faster
-                // than at 6 and 7 % faster than at 3)
-                if (st == (PK ? 2 : 6)) store_w(ks + 1, nxt);
+                // PK: the codes' DMA at sub-step 2 (measured 10 % faster
+                // than at 6 and 7 % faster than at 3); the scale pairs are
+                // stored after the step, below
+                if constexpr (PK) {
+                    if (st == 2) pk_codes(ks + 1, nxt);
+                } else {
+                    if (st == 6) store_w(ks + 1, nxt);
+                }
             }
             if (!live) continue;
             const int col = b_col0 + 32 * c;
@@ -1170,6 +1193,11 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
             }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // step ks+1's DMA has landed
+        // PK: the scale pairs of step ks+1, stored where every load has
+        // landed anyway (anywhere inside the step the compiler makes the
+        // store wait for all loads in flight, the DMA pieces included)
+        if constexpr (PK)
+            if (j + 1 < nloc) pk_scale(nxt);
         __syncthreads();
         if (j + 2 < nloc) load_w(ks + 2);
     };
