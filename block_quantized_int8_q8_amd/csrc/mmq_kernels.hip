@@ -251,8 +251,14 @@ __device__ __forceinline__ void fmac_row_bcast8(f32x16 &acc, const f32x16 &t, fl
 }
 #undef MMQ_FMAC_BCAST
 
+// One k-step buffer of the tile kernel is two LDS variables: A, the
+// activation codes and headers (written by DMA), and B, the weight codes,
+// scales and mins (written by the threads' stores); offsets are within each
+// variable.  Q6_K keeps one variable per buffer (B after A): split, its
+// kernel spilled.
 template <int FMT>
 struct Lds {
+    static constexpr bool SPLIT = FMT != FMT_Q6_K;
     static constexpr int A_CODES = KB * kBlockBytes;
     static constexpr int A_HDR = kTileM * KB * 4;                               // [row][4] (d, s) fp16 pairs
     static constexpr int B_CODES = KB * kBlockBytes;
@@ -260,10 +266,12 @@ struct Lds {
     static constexpr int B_SCALE = KB * kTileN * 8;
     static constexpr int B_MIN = has_min(FMT) ? kTileN * 2 * KB * 2 : 0;     // [col][g][4] fp16
     static constexpr int OFF_A_HDR = A_CODES;
-    static constexpr int OFF_B_CODES = OFF_A_HDR + A_HDR;
+    static constexpr int A_BYTES = OFF_A_HDR + A_HDR;
+    static constexpr int OFF_B_CODES = SPLIT ? 0 : A_BYTES;
     static constexpr int OFF_B_SCALE = OFF_B_CODES + B_CODES;
     static constexpr int OFF_B_MIN = OFF_B_SCALE + B_SCALE;
-    static constexpr int STEP = OFF_B_MIN + B_MIN;     // one k-step buffer
+    static constexpr int B_BYTES = OFF_B_MIN + B_MIN - OFF_B_CODES;
+    static constexpr int STEP = A_BYTES + B_BYTES;     // one k-step buffer
     static constexpr int TOTAL = 2 * STEP;
 };
 static_assert(KB == 4 && kTileM == 128 && kTileN == 128 && kThreads == 512 && kNSub == 2 && kBlockBytes == 4096,
@@ -272,9 +280,9 @@ static_assert(Lds<FMT_Q8_0>::TOTAL == lds_bytes_for(FMT_Q8_0), "plan and kernel 
 static_assert(Lds<FMT_Q4_K>::TOTAL == lds_bytes_for(FMT_Q4_K), "plan and kernel LDS disagree");
 static_assert(Lds<FMT_Q5_K>::TOTAL == lds_bytes_for(FMT_Q5_K), "plan and kernel LDS disagree");
 static_assert(Lds<FMT_Q6_K>::TOTAL == lds_bytes_for(FMT_Q6_K), "plan and kernel LDS disagree");
-static_assert(Lds<FMT_Q4_K>::OFF_B_CODES % 16 == 0 && Lds<FMT_Q4_K>::OFF_B_MIN % 16 == 0 &&
-              Lds<FMT_Q4_K>::STEP % 16 == 0 &&
-              Lds<FMT_Q8_0>::OFF_B_SCALE % 16 == 0 && Lds<FMT_Q8_0>::STEP % 16 == 0,
+static_assert(Lds<FMT_Q4_K>::A_BYTES % 16 == 0 && Lds<FMT_Q4_K>::OFF_B_MIN % 16 == 0 &&
+              Lds<FMT_Q4_K>::B_BYTES % 16 == 0 && Lds<FMT_Q8_0>::OFF_B_SCALE % 16 == 0 &&
+              Lds<FMT_Q8_0>::B_BYTES % 16 == 0 && Lds<FMT_Q6_K>::B_BYTES % 16 == 0,
               "LDS regions must stay 16-byte aligned");
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -833,21 +841,25 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     static_assert(!TAIL || FMT == FMT_Q8_0, "only Q8_0 k-steps can be partial");
     constexpr bool DEFER = FMT == FMT_Q8_0 && !DOTS;
     using L = Lds<FMT>;
-    // The two k-step buffers are two LDS variables, not offsets into one
-    // array: the compiler then knows that the DMA into one buffer cannot
-    // write what the fragment reads of the other return, and does not make
-    // every LDS read wait for the DMA in flight.  The step loop is unrolled
-    // by two so that each copy names its buffers at compile time.
-    // PK: the weight scale pairs of each buffer are LDS variables of their
-    // own as well (the same bytes, taken off the end of the step buffers), so
-    // that storing them does not wait for the codes' DMA into the same step
-    // buffer (the compiler orders an LDS store after an LDS DMA it may alias)
-    static_assert(FMT != FMT_Q8_0 || L::OFF_B_SCALE + L::B_SCALE == L::STEP, "Q8_0 scale pairs end the step");
-    constexpr int kStepBytes = PK ? L::OFF_B_SCALE : L::STEP;
-    __shared__ __attribute__((aligned(16))) uint8_t lds0[kStepBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t lds1[kStepBytes];
+    // The two k-step buffers are LDS variables of their own, each in two
+    // (A: activations, B: weights), not offsets into one array: the compiler
+    // then knows that the DMA into one buffer cannot write what the fragment
+    // reads of the other return (it would make every LDS read wait for the
+    // DMA in flight), and that the weight stores into B cannot write what the
+    // activation DMA into A writes (it orders an LDS store after an LDS DMA
+    // it may alias: with one variable per buffer the weight stores waited for
+    // every DMA piece of the step).  The step loop is unrolled by two so that
+    // each copy names its buffers at compile time.  PK: the weight scale
+    // pairs are variables of their own as well, apart from the codes' DMA.
+    static_assert(FMT != FMT_Q8_0 || L::OFF_B_SCALE + L::B_SCALE == L::B_BYTES, "Q8_0 scale pairs end B");
+    constexpr bool kSplitAB = L::SPLIT;
+    constexpr int kBBytes = PK ? L::OFF_B_SCALE : L::B_BYTES;
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[kSplitAB ? L::A_BYTES : L::STEP];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[kSplitAB ? L::A_BYTES : L::STEP];
     __shared__ __attribute__((aligned(16))) float2 pks0[PK ? KB * kTileN : 1];
     __shared__ __attribute__((aligned(16))) float2 pks1[PK ? KB * kTileN : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t ldsb0_[kSplitAB ? kBBytes : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t ldsb1_[kSplitAB ? kBBytes : 1];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wr = wv >> 1, wc = wv & 1;          // wave tile: rows 32*wr.., columns 64*wc..
@@ -971,7 +983,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     };
     auto pk_scale = [&](uint8_t *buf) {
         const float ws = __half2float(__ushort_as_half(pk_d));
-        (buf == lds0 ? pks0 : pks1)[tid] = make_float2(ws, -kMagic * ws);   // exact
+        (buf == ldsb0_ ? pks0 : pks1)[tid] = make_float2(ws, -kMagic * ws);   // exact
     };
     auto store_w = [&](int k, uint8_t *buf) {
         if constexpr (PK) {
@@ -985,7 +997,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
             store_kquant<FMT>(wr_.r, buf, k, tid);
     };
 
-    // Pipeline: step ks computes from buffer ks%2 (lds0 or lds1).  Meanwhile the DMA fills
+    // Pipeline: step ks computes from buffer ks%2 (lds0/ldsb0 or lds1/ldsb1).  Meanwhile the DMA fills
     // the other buffer with step ks+1's activations, and the weight
     // registers, fetched one step earlier, are stored into it; after the
     // barrier they fetch step ks+2.
@@ -993,7 +1005,10 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     // before the previous barrier.
     dma_activations<FMT, TAIL || DOTS>(rx, adma, ks0, lds0, wv, -1);
     load_w(ks0);
-    store_w(ks0, lds0);
+    if constexpr (kSplitAB)
+        store_w(ks0, ldsb0_);
+    else
+        store_w(ks0, lds0);   // B offsets count from the buffer's start
     if (nloc > 1) load_w(ks0 + 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the DMA has landed in LDS
     __syncthreads();
@@ -1011,8 +1026,17 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
     auto step = [&](auto parity, int j) {
         constexpr int P = decltype(parity)::value;
         const int ks = ks0 + j;                   // the k-step; j is its place in this workgroup's range
-        uint8_t *const buf = P ? lds1 : lds0;     // local step j (j % 2 == P)
+        uint8_t *const buf = P ? lds1 : lds0;     // local step j (j % 2 == P): activations
         uint8_t *const nxt = P ? lds0 : lds1;     // local step j + 1
+        // the same steps' weights (B offsets count from here)
+        uint8_t *const bufb = [&]() -> uint8_t * {
+            if constexpr (kSplitAB) return P ? ldsb1_ : ldsb0_;
+            else return buf;
+        }();
+        uint8_t *const nxtb = [&]() -> uint8_t * {
+            if constexpr (kSplitAB) return P ? ldsb0_ : ldsb1_;
+            else return nxt;
+        }();
         // Q8_0: an idle wave takes this path of its own (staging only).  The
         // K-quants skip the same work by guarding the fragment reads, MFMAs
         // and epilogues below instead: with a second copy of the staging code
@@ -1023,7 +1047,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
 #pragma unroll
                     for (int piece = 0; piece < 3; piece++)
                         dma_activations<FMT, TAIL || DOTS>(rx, adma, ks + 1, nxt, wv, piece);
-                    store_w(ks + 1, nxt);
+                    store_w(ks + 1, nxtb);
                 }
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
@@ -1032,8 +1056,8 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
             }
         }
         const unsigned short *sHdr = reinterpret_cast<const unsigned short *>(buf + L::OFF_A_HDR);
-        const uint8_t *sB = buf + L::OFF_B_CODES;
-        const float2 *sW = PK ? (P ? pks1 : pks0) : reinterpret_cast<const float2 *>(buf + L::OFF_B_SCALE);
+        const uint8_t *sB = bufb + L::OFF_B_CODES;
+        const float2 *sW = PK ? (P ? pks1 : pks0) : reinterpret_cast<const float2 *>(bufb + L::OFF_B_SCALE);
 
         // Sub-step st = (block b = st/2, sub-tile c = st%2).  B fragments are
         // read from LDS kPfB sub-steps ahead, A fragments one block ahead.
@@ -1107,16 +1131,30 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
             // three DMA pieces at 1, 3 and 5, the weight stores at 6): issued
             // together at the top or bottom of the step they were measured to
             // cost 8-10 % more.
-            if (j + 1 < nloc) {
-                if ((st & 1) && st < 6) dma_activations<FMT, TAIL || DOTS>(rx, adma, ks + 1, nxt, wv, st >> 1);
-                // PK: the codes' DMA at sub-step 2 (measured 10 % faster
-                // than at 6 and 7 % faster than at 3); the scale pairs are
-                // stored after the step, below
-                if constexpr (PK) {
-                    if (st == 2) pk_codes(ks + 1, nxt);
-                } else {
-                    if (st == 6) store_w(ks + 1, nxt);
+            // The DMA pieces are issued on every step, the last one included
+            // (it copies its own k-step again into the buffer no one reads
+            // any more): issued on some paths only, they leave the compiler
+            // unable to count them, and the weight registers' wait at the
+            // stores then drains every load in flight (Q8_0 2048 x 3584 x
+            // 18944: 429 -> 398 us).  Q6_K keeps the guarded form (unguarded,
+            // its kernel spilled), and so does PK, which has no weight
+            // registers to wait for (1.7 % slower unguarded).
+            // PK: the codes' DMA at sub-step 2 (measured 10 % faster than at
+            // 6 and 7 % faster than at 3); the scale pairs are stored after
+            // the step, below.
+            if constexpr (FMT == FMT_Q6_K || PK) {
+                if (j + 1 < nloc) {
+                    if ((st & 1) && st < 6) dma_activations<FMT, TAIL || DOTS>(rx, adma, ks + 1, nxt, wv, st >> 1);
+                    if constexpr (PK) {
+                        if (st == 2) pk_codes(ks + 1, nxtb);
+                    } else {
+                        if (st == 6) store_w(ks + 1, nxtb);
+                    }
                 }
+            } else {
+                const int kn = j + 1 < nloc ? ks + 1 : ks;   // the k-step the DMA stages into the other buffer
+                if ((st & 1) && st < 6) dma_activations<FMT, TAIL || DOTS>(rx, adma, kn, nxt, wv, st >> 1);
+                if (st == 6 && j + 1 < nloc) store_w(ks + 1, nxtb);
             }
             if (!live) continue;
             const int col = b_col0 + 32 * c;
@@ -1176,7 +1214,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
         }
         if constexpr (has_min(FMT) && !DOTS) if (live) {
             // the min term of this step's four sub-blocks
-            const _Float16 *sMin = reinterpret_cast<const _Float16 *>(buf + L::OFF_B_MIN);
+            const _Float16 *sMin = reinterpret_cast<const _Float16 *>(bufb + L::OFF_B_MIN);
             // A = the four block sums s (high halves of the row's headers)
             const u32x4 h = *reinterpret_cast<const u32x4 *>(buf + L::OFF_A_HDR + (32 * wr + l32) * KB * 4);
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -1197,7 +1235,7 @@ void k_mmq(const uint8_t *__restrict__ xq, const GemmSet set, int M, int K, int 
         // landed anyway (anywhere inside the step the compiler makes the
         // store wait for all loads in flight, the DMA pieces included)
         if constexpr (PK)
-            if (j + 1 < nloc) pk_scale(nxt);
+            if (j + 1 < nloc) pk_scale(nxtb);
         __syncthreads();
         if (j + 2 < nloc) load_w(ks + 2);
     };
